@@ -1,0 +1,63 @@
+"""Plain single-token decode attention over a (dequantized) KV cache (oracle).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Pages cited
+  [KV-opt]  "AI 推理性能调优：KV Cache 优化与显存管理的工程实践"
+            (bxzpzcl.cn/news/2871434), section 3.2 ``SlidingWindowAttention``:
+            window ``[max(0, i - W + 1), i]``, GQA by repeating each KV head
+            ``n_rep = Hq // Hkv`` times (query head h reads KV head ``h // n_rep``),
+            ``scale = head_dim ** -0.5``, masked softmax, then weights times V.
+  [KV-4bit] lpnh.cn/news/2042373, section 1.1: at decode each new token's query
+            attends over every cached key/value, the new token's own K/V included.
+  [INT4-SM] "LLM长上下文推理优化：用INT4状态机管理KV Cache" (pwwt.cn/news/4219524),
+            section 5 step 5: the operator reads INT4 data and dequantizes inside.
+
+Readings: the window is inclusive of the current token and holds W positions, so the
+attended positions are ``[max(0, len - W), len)`` (``W = 0`` means global).
+Attention sinks (the page's default of 4) are not part of this path.  Everything is
+fp64; the dequantized values passed in are exact (``q * s`` in fp64).
+"""
+
+import numpy as np
+
+
+def attended_positions(length, window):
+    """Positions a decode query at sequence length ``length`` attends ([KV-opt] §3.2)."""
+    if length <= 0:
+        raise ValueError("length must be positive")
+    lo = max(0, length - window) if window > 0 else 0
+    return np.arange(lo, length)
+
+
+def decode_attention(q, k_hat, v_hat, lens, window=0, scale=None):
+    """out[b, h] = sum_t softmax_t(scale * q[b,h] . k_hat[b,kv,t]) * v_hat[b,kv,t].
+
+    q:      [B, Hq, D] (any float; taken as exact values)
+    k_hat:  [B, Hkv, N, D] dequantized keys indexed by *position* (fp64)
+    v_hat:  [B, Hkv, N, D] dequantized values indexed by position (fp64)
+    lens:   [B] valid lengths (positions 0..len-1, the just-appended one included)
+    window: 0 for global attention, else the horizon W
+    scale:  softmax scale; None -> 1/sqrt(D)
+    Returns fp64 [B, Hq, D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k_hat.shape[1]
+    if Hq % Hkv != 0:
+        raise ValueError("q heads must be a multiple of kv heads")
+    n_rep = Hq // Hkv
+    if scale is None:
+        scale = D ** -0.5
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        T = attended_positions(int(lens[b]), window)
+        for h in range(Hq):
+            kv = h // n_rep
+            K = np.asarray(k_hat[b, kv, T], dtype=np.float64)
+            V = np.asarray(v_hat[b, kv, T], dtype=np.float64)
+            z = scale * (K @ q[b, h])
+            e = np.exp(z - z.max())
+            p = e / e.sum()
+            out[b, h] = p @ V
+    return out

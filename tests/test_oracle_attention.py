@@ -1,0 +1,90 @@
+"""Pins of oracle/attention.py (CPU only): closed forms, invariants, a library routine.
+
+Semantics ([KV-opt] bxzpzcl.cn/news/2871434 §3.2): window [max(0, i-W+1), i],
+query head h reads KV head h // (Hq // Hkv), scale head_dim ** -0.5, softmax, P V.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import attended_positions, decode_attention
+
+
+def _rand(rng, B=2, Hq=4, Hkv=2, N=37, D=16):
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, Hkv, N, D)) * 2
+    v = rng.standard_normal((B, Hkv, N, D))
+    return q, k, v
+
+
+def test_two_position_closed_form():
+    # q = (1, 0), scale 1: z = (0, ln 3) -> p = (1/4, 3/4)
+    q = np.array([[[1.0, 0.0]]])
+    k = np.array([[[[0.0, 0.0], [math.log(3.0), 5.0]]]])
+    v = np.array([[[[4.0, -8.0], [8.0, 4.0]]]])
+    o = decode_attention(q, k, v, [2], scale=1.0)
+    assert np.allclose(o[0, 0], [0.25 * 4 + 0.75 * 8, 0.25 * -8 + 0.75 * 4], atol=1e-15)
+
+
+def test_single_position_returns_value_row():
+    rng = np.random.default_rng(1)
+    q, k, v = _rand(rng)
+    o = decode_attention(q, k, v, [1, 1])
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(o[b, h], v[b, h // 2, 0])
+
+
+def test_zero_query_is_mean_of_window():
+    rng = np.random.default_rng(2)
+    q, k, v = _rand(rng)
+    q[:] = 0
+    o = decode_attention(q, k, v, [37, 20], window=8)
+    assert np.allclose(o[0, 3], v[0, 1, 29:37].mean(0), atol=1e-14)
+    assert np.allclose(o[1, 0], v[1, 0, 12:20].mean(0), atol=1e-14)
+
+
+def test_window_bounds():
+    assert list(attended_positions(10, 0)) == list(range(10))
+    assert list(attended_positions(10, 4)) == [6, 7, 8, 9]
+    assert list(attended_positions(3, 4)) == [0, 1, 2]
+    with pytest.raises(ValueError):
+        attended_positions(0, 0)
+    rng = np.random.default_rng(3)
+    q, k, v = _rand(rng)
+    # W >= len is global attention; W < len equals global attention over the last W rows
+    assert np.allclose(decode_attention(q, k, v, [37, 30], window=37),
+                       decode_attention(q, k, v, [37, 30], window=0), atol=1e-14)
+    o = decode_attention(q, k, v, [37, 30], window=5)
+    o2 = decode_attention(q, k[:, :, 32:37], v[:, :, 32:37], [5, 5])
+    assert np.allclose(o[0], o2[0], atol=1e-14)
+
+
+def test_permutation_invariance_and_gqa_equals_repeated_mha():
+    rng = np.random.default_rng(4)
+    q, k, v = _rand(rng)
+    perm = rng.permutation(37)
+    o = decode_attention(q, k, v, [37, 37])
+    op = decode_attention(q, k[:, :, perm], v[:, :, perm], [37, 37])
+    assert np.allclose(o, op, atol=1e-13)
+    k_rep = np.repeat(k, 2, axis=1)
+    v_rep = np.repeat(v, 2, axis=1)
+    assert np.allclose(o, decode_attention(q, k_rep, v_rep, [37, 37]), atol=1e-14)
+
+
+@pytest.mark.parametrize("lens,window", [([37, 11], 0), ([37, 30], 7), ([5, 37], 40)])
+def test_matches_torch_sdpa_fp64(lens, window):
+    """torch's scaled_dot_product_attention in float64 on the CPU, fed the window's rows
+    with the KV heads expanded by repeat_interleave."""
+    rng = np.random.default_rng(5)
+    q, k, v = _rand(rng)
+    o = decode_attention(q, k, v, lens, window=window)
+    for b, L in enumerate(lens):
+        lo = max(0, L - window) if window else 0
+        kt = torch.from_numpy(k[b, :, lo:L]).repeat_interleave(2, dim=0)
+        vt = torch.from_numpy(v[b, :, lo:L]).repeat_interleave(2, dim=0)
+        qt = torch.from_numpy(q[b])[:, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, 0]
+        assert np.allclose(o[b], ref.numpy(), rtol=1e-12, atol=1e-13)

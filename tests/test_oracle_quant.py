@@ -1,0 +1,179 @@
+"""Pins of oracle/quant.py against what the pages and the arithmetic fix (CPU only).
+
+The INT4 rule ([KV-4bit] lpnh.cn/news/2042373 §2.1): per group of g head_dim
+elements, s = amax/7 (1 for an all-zero group), q = clamp(round(x/s), -7, 7), with
+round-half-to-even and fp32 scales.  The INT8 rule ([KV-opt] bxzpzcl.cn/news/2871434
+§3.1): per (token, head), s = max(amax/127, 1e-8), q = clamp(round(x/s), -128, 127).
+"""
+import numpy as np
+import pytest
+
+from oracle import quant
+
+F16_ALL = np.arange(1 << 16, dtype=np.uint16).view(np.float16)
+F16_FINITE = F16_ALL[np.isfinite(F16_ALL)]
+
+
+def _fp64_route_int4(x16, g):
+    """Same definition in fp64 then one rounding to fp32.  Division is one of the
+    operations for which rounding through a format with >= 2p+2 bits first is
+    innocuous (53 >= 2*24 + 2), so fl32(fl64(a/b)) == fl32(a/b) exactly."""
+    x = np.asarray(x16, dtype=np.float16).astype(np.float64)
+    D = x.shape[-1]
+    xg = x.reshape(x.shape[:-1] + (D // g, g))
+    a = np.abs(xg).max(-1)
+    s = np.float32(a / 7.0) if np.ndim(a) == 0 else (a / 7.0).astype(np.float32)
+    s = np.where(s == 0, np.float32(1), s).astype(np.float32)
+    y = (xg / s.astype(np.float64)[..., None]).astype(np.float32)
+    q = np.clip(np.rint(y.astype(np.float64)), -7, 7).astype(np.int8)
+    return q.reshape(x.shape), s
+
+
+def test_hand_example_groups_along_head_dim():
+    # One row, D = 128, g = 64: the first 64 elements hold 7 and 3.5, the next 64 hold 14.
+    x = np.zeros((1, 128), np.float16)
+    x[0, 0] = 7.0
+    x[0, 1] = 3.5        # 3.5 / 1 -> tie -> 4 (even)
+    x[0, 2] = -0.5       # tie -> 0
+    x[0, 64] = 14.0
+    x[0, 65] = 3.0       # 3 / 2 = 1.5 -> tie -> 2
+    x[0, 66] = -5.0      # -2.5 -> -2
+    q, s = quant.quantize_int4(x, 64)
+    assert s.dtype == np.float32 and s.shape == (1, 2)
+    assert s[0, 0] == np.float32(1.0) and s[0, 1] == np.float32(2.0)
+    assert list(q[0, :3]) == [7, 4, 0]
+    assert list(q[0, 64:67]) == [7, 2, -2]
+    assert not q[0, 3:64].any() and not q[0, 67:].any()
+    # With g = 128 the whole row is one group: s = 14/7 = 2.
+    q2, s2 = quant.quantize_int4(x, 128)
+    assert s2.shape == (1, 1) and s2[0, 0] == np.float32(2.0)
+    assert list(q2[0, :3]) == [4, 2, 0]   # 7/2=3.5->4, 3.5/2=1.75->2, -0.25->0
+
+
+@pytest.mark.parametrize("v,expect", [(0.5, 0), (1.5, 2), (2.5, 2), (3.5, 4), (4.5, 4),
+                                      (5.5, 6), (6.5, 6), (0.49951171875, 0), (1.4990234375, 1)])
+def test_ties_round_half_to_even(v, expect):
+    # amax 7 -> s = 1 exactly, so x / s = x and only the integer rounding acts.
+    x = np.zeros((64,), np.float16)
+    x[0] = 7.0
+    x[1] = v
+    x[2] = -v
+    q, s = quant.quantize_int4(x, 64)
+    assert s[0] == 1.0
+    assert q[1] == expect and q[2] == -expect
+
+
+def test_zero_group_gets_scale_one():
+    x = np.zeros((3, 128), np.float16)
+    x[1, 70] = 2.0
+    q, s = quant.quantize_int4(x, 64)
+    assert np.all(s[0] == 1.0) and np.all(s[2] == 1.0) and s[1, 0] == 1.0
+    assert s[1, 1] == np.float32(2.0) / np.float32(7.0)
+    assert not q[0].any() and not q[2].any()
+
+
+def _rand_rows(rng, n, D, outliers=True):
+    x = rng.standard_normal((n, D)).astype(np.float32)
+    if outliers:
+        x[:, rng.choice(D, 3, replace=False)] *= 20
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_invariants_random(g):
+    rng = np.random.default_rng(7)
+    x = _rand_rows(rng, 2000, 128)
+    q, s = quant.quantize_int4(x, g)
+    xg = x.astype(np.float64).reshape(2000, 128 // g, g)
+    qg = q.astype(np.float64).reshape(2000, 128 // g, g)
+    sg = s.astype(np.float64)[..., None]
+    # |x - q s| <= s (1/2 + 2^-21): rounding to an integer plus one fp32 rounding of x/s
+    assert np.all(np.abs(xg - qg * sg) <= sg * (0.5 + 2.0 ** -21))
+    # the amax element of every non-zero group maps to +-7, and codes stay in [-7, 7]
+    am = np.abs(xg).argmax(-1)
+    top = np.take_along_axis(qg, am[..., None], -1)[..., 0]
+    assert np.all(np.abs(top) == 7)
+    assert q.min() >= -7 and q.max() <= 7
+    # odd symmetry
+    qn, sn = quant.quantize_int4(-x, g)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    # same as the fp64 route (double rounding through fp64 is innocuous for division)
+    q64, s64 = _fp64_route_int4(x, g)
+    assert np.array_equal(q, q64) and np.array_equal(s, s64)
+
+
+def test_exhaustive_fp16_sweep():
+    """Every finite fp16 value x, inside groups whose amax is a spread of fp16 values."""
+    pos = F16_FINITE[(F16_FINITE > 0)]
+    rng = np.random.default_rng(11)
+    amaxes = np.concatenate([pos[[0, 1, 100, 1023, 1024, 5000, 15000, 15360, 20000, 30000, -1]],
+                             rng.choice(pos, 40, replace=False)]).astype(np.float16)
+    for a in amaxes:
+        xs = F16_FINITE[np.abs(F16_FINITE.astype(np.float64)) <= float(a)]
+        n = -(-len(xs) // 63) * 63
+        pad = np.zeros(n, np.float16)
+        pad[:len(xs)] = xs
+        rows = np.empty((n // 63, 64), np.float16)
+        rows[:, 0] = a
+        rows[:, 1:] = pad.reshape(-1, 63)
+        q, s = quant.quantize_int4(rows, 64)
+        assert np.all(s == (np.float32(a) / np.float32(7.0)))
+        q64, s64 = _fp64_route_int4(rows, 64)
+        assert np.array_equal(q, q64)
+        xr = rows.astype(np.float64)
+        assert np.all(np.abs(xr - q * s.astype(np.float64)) <= s.astype(np.float64) * (0.5 + 2.0 ** -21))
+
+
+def test_pack_layout():
+    codes = np.array([1, -1, -7, 7, 0, -8, 3, 4], np.int8)
+    p = quant.pack_nibbles(codes)
+    assert list(p) == [0xF1, 0x79, 0x80, 0x43]
+    assert np.array_equal(quant.unpack_nibbles(p), codes)
+    u = np.array([0, 15, 7, 8], np.uint8)
+    assert list(quant.pack_nibbles(u)) == [0xF0, 0x87]
+    assert np.array_equal(quant.unpack_nibbles(quant.pack_nibbles(u), signed=False), u)
+    rng = np.random.default_rng(3)
+    c = rng.integers(-7, 8, size=(5, 6, 128)).astype(np.int8)
+    assert np.array_equal(quant.unpack_nibbles(quant.pack_nibbles(c)), c)
+
+
+def test_dequant_is_fl32_of_exact_product():
+    rng = np.random.default_rng(5)
+    x = _rand_rows(rng, 300, 128)
+    q, s = quant.quantize_int4(x, 64)
+    d = quant.dequantize_int4(q, s, 64)
+    exact = quant.dequantize_int4_exact(q, s, 64)
+    # q (3 bits) * s (24 bits) is exact in fp64; fl32 of it is one rounding
+    assert np.array_equal(d, exact.astype(np.float32))
+    # and exact product is q*s by hand for a few entries
+    assert exact[0, 0] == float(q[0, 0]) * float(s[0, 0])
+
+
+# ---------------------------------------------------------------- INT8 per-token
+
+
+def test_int8_rules():
+    rng = np.random.default_rng(9)
+    x = _rand_rows(rng, 500, 128)
+    x[17] = 0
+    q, s = quant.quantize_int8(x)
+    assert s.shape == (500,) and s.dtype == np.float32
+    assert s[17] == np.float32(1e-8) and not q[17].any()
+    xd = x.astype(np.float64)
+    am = np.abs(xd).argmax(-1)
+    nz = np.abs(xd).max(-1) > 0
+    assert np.all(np.abs(q[np.arange(500), am][nz]) == 127)
+    assert np.all(np.abs(xd - q * s.astype(np.float64)[:, None]) <= s.astype(np.float64)[:, None] * (0.5 + 2.0 ** -17))
+    # fp64 route
+    a = np.abs(xd).max(-1)
+    s64 = np.maximum((a / 127.0).astype(np.float32), np.float32(1e-8))
+    y = (xd / s64.astype(np.float64)[:, None]).astype(np.float32)
+    q64 = np.clip(np.rint(y.astype(np.float64)), -128, 127).astype(np.int8)
+    assert np.array_equal(s, s64) and np.array_equal(q, q64)
+    # tiny rows hit the 1e-8 floor: amax below 127e-8
+    t = np.zeros((1, 128), np.float16)
+    t[0, 0] = np.float16(6e-8)   # smallest fp16 subnormal ~5.96e-8
+    qt, st = quant.quantize_int8(t)
+    assert st[0] == np.float32(1e-8) and qt[0, 0] == 6
+    dq = quant.dequantize_int8(q, s)
+    assert np.array_equal(dq, quant.dequantize_int8_exact(q, s).astype(np.float32))
