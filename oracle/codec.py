@@ -84,6 +84,7 @@ def lloyd_max_gaussian(bits, tol=1e-14, max_iter=200000):
         c = c_new
         if done:
             break
+    c = 0.5 * (c - c[::-1])  # the N(0,1) quantizer is odd-symmetric; remove rounding asymmetry
     t = 0.5 * (c[:-1] + c[1:])
     lo = np.concatenate(([-np.inf], t))
     hi = np.concatenate((t, [np.inf]))
