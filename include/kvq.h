@@ -1,0 +1,190 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) INT4 KV-cache library.
+ *
+ * The library stores an attention layer's key/value cache in packed low-precision
+ * form and runs single-token decode attention directly on the packed data.  All
+ * entry points take plain pointers and sizes; no C++ or PyTorch types cross this
+ * boundary.
+ *
+ * Pages the operations follow (cited by title/address and section):
+ *   [KV-4bit]  lpnh.cn/news/2042373, article on compressing the KV cache from FP16 to
+ *              4 bits.  Section 1.1: the decode loop appends each new token's K/V to a
+ *              per-layer cache and attends over all of it.  Section 2.1: group-wise
+ *              symmetric INT4, scale = amax/7, an all-zero group gets scale 1,
+ *              round then clamp to [-7, 7].  Section 2.2: K groups of 64, V of 128.
+ *   [KV-opt]   "AI 推理性能调优：KV Cache 优化与显存管理的工程实践"
+ *              (bxzpzcl.cn/news/2871434).  Section 3.1: per-token INT8 variant and the
+ *              [batch, heads, seq, head_dim] layout.  Section 3.2: sliding window,
+ *              GQA head mapping, softmax scale head_dim^-1/2.
+ *   [INT4-SM]  "LLM长上下文推理优化：用INT4状态机管理KV Cache" (pwwt.cn/news/4219524),
+ *              section 5 step 5: attention reads the INT4 data and dequantizes it
+ *              inside the operator.
+ *   [LARQL]    "长上下文内存大瘦身：LARQL 四大 KV 缓存引擎原理与横向对比"
+ *              (pwwt.cn/news/5725003): window engine (keep only rows inside the
+ *              attention horizon) and codec engine (per-head Walsh-Hadamard rotation
+ *              plus Lloyd-Max 4-bit codes; head_dim must be a power of two).
+ *
+ * Conventions shared by every call
+ *   - Device pointers point to HIP device memory of the GPU that is current on the
+ *     calling thread; host pointers are ordinary CPU memory read before the call
+ *     returns.  The caller owns every buffer.  The library allocates nothing,
+ *     keeps no pointer after returning and has no mutable global state (it is
+ *     re-entrant; calls on different streams touching different buffers may overlap).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Nothing synchronizes the host.
+ *   - Every argument is validated before any work is enqueued.  On error a negative
+ *     kvq_status is returned and nothing has been launched or written.
+ *     KVQ_ERR_LAUNCH reports a launch failure seen right after enqueueing.
+ *   - fp16 tensors are IEEE binary16 (`_Float16` / torch.float16), row-major,
+ *     contiguous, 16-byte aligned.  fp32 outputs are IEEE binary32.
+ *
+ * Cache layout ([KV-opt] §3.1: [batch, kv_heads, seq, head_dim]) for capacity C:
+ *   KVQ_INT4_G    codes  [B, Hkv, C, D/2] uint8: element 2i in the low nibble of byte
+ *                        i, element 2i+1 in the high nibble, 4-bit two's complement
+ *                        (values -7..7);
+ *                 scales [B, Hkv, C, D/g] fp32, g = group_k for K and group_v for V.
+ *   KVQ_INT8_TOKEN codes [B, Hkv, C, D] int8; scales [B, Hkv, C] fp32.
+ *   KVQ_WHT_LM4   codes  [B, Hkv, C, D/2] uint8, unsigned 4-bit Lloyd-Max indices
+ *                        (0..15) of the rotated row, same nibble order as INT4;
+ *                 scales [B, Hkv, C] fp32 (the row's RMS).
+ *   Position p of a sequence lives in slot p % C (a ring once p >= C).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_VERSION 1
+/* Largest batch the decode/append calls accept (per-sequence lengths and positions
+ * travel in the kernel argument block). */
+#define KVQ_MAX_BATCH 256
+
+typedef enum {
+  KVQ_INT4_G = 0,      /* group-wise symmetric INT4 ([KV-4bit] §2.1) */
+  KVQ_INT8_TOKEN = 1,  /* per-token symmetric INT8 ([KV-opt] §3.1) */
+  KVQ_WHT_LM4 = 2      /* Walsh-Hadamard rotation + 4-bit Lloyd-Max codec ([LARQL]) */
+} kvq_format;
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,          /* null pointer, non-positive size, bad kv selector, len 0 */
+  KVQ_ERR_UNSUPPORTED = -2,  /* shape the kernels do not implement (see kvq_check_desc) */
+  KVQ_ERR_CAPACITY = -3,     /* positions that do not fit the cache / window */
+  KVQ_ERR_WORKSPACE = -4,    /* workspace missing or smaller than required */
+  KVQ_ERR_LAUNCH = -5        /* the HIP runtime reported an error when enqueueing */
+} kvq_status;
+
+/* Shape and format of one layer's cache. */
+typedef struct {
+  int32_t format;    /* kvq_format */
+  int32_t batch;     /* B, 1..KVQ_MAX_BATCH */
+  int32_t kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;  /* D: 64, 128 or 256 */
+  int32_t capacity;  /* C: slots per (b, kv head) >= 1 */
+  int32_t group_k;   /* INT4 only: K group size (default 64); power of two, 32 <= g <= D */
+  int32_t group_v;   /* INT4 only: V group size (default 128); same rule */
+} kvq_cache_desc;
+
+/* Device pointers of one layer's cache (layout above). */
+typedef struct {
+  void* k_codes;
+  void* k_scales;
+  void* v_codes;
+  void* v_scales;
+} kvq_cache;
+
+/* A hipStream_t, passed as an opaque pointer; NULL is the null stream. */
+typedef void* kvq_stream;
+
+/* KVQ_VERSION of the built library. */
+int32_t kvq_version(void);
+
+/* Static, human-readable name of a kvq_status value ("unknown status" otherwise). */
+const char* kvq_status_str(int32_t status);
+
+/* Validate a descriptor without touching the GPU.  Returns KVQ_OK, KVQ_ERR_ARG (null,
+ * non-positive sizes, unknown format) or KVQ_ERR_UNSUPPORTED (D not in {64,128,256};
+ * INT4 group not a power of two in [32, D]; batch > KVQ_MAX_BATCH). */
+int32_t kvq_check_desc(const kvq_cache_desc* desc);
+
+/* Bytes of the codes (or scales) buffer of K (kv = 0) or V (kv = 1) for `desc`;
+ * 0 if the descriptor is invalid or kv is not 0/1.  INT4: B*Hkv*C*D/2 and
+ * B*Hkv*C*(D/g)*4; INT8: B*Hkv*C*D and B*Hkv*C*4; codec: B*Hkv*C*D/2 and B*Hkv*C*4. */
+size_t kvq_codes_bytes(const kvq_cache_desc* desc, int32_t kv);
+size_t kvq_scales_bytes(const kvq_cache_desc* desc, int32_t kv);
+
+/* Number of sequence splits kvq_decode_attn uses when called with num_splits = 0 for
+ * a longest attended span of `span` positions and `q_heads` query heads; 0 if invalid. */
+int32_t kvq_plan_splits(const kvq_cache_desc* desc, int32_t q_heads, int32_t span);
+
+/* Workspace bytes kvq_decode_attn needs for these arguments (num_splits = 0: the
+ * library's own plan for a longest span of min(max_len, window or max_len));
+ * 0 if invalid.  Equal to B * q_heads * nsplit * (D + 2) * 4. */
+size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t q_heads,
+                                  int32_t max_len, int32_t window, int32_t num_splits);
+
+/* The library's own 4-bit Lloyd-Max quantizer of a unit Gaussian ([LARQL] codec):
+ * 16 ascending output levels and the 15 midpoint decision thresholds, rounded to
+ * fp32 from a double-precision fixed-point iteration.  Host pointers.  KVQ_ERR_ARG on
+ * null. */
+int32_t kvq_codec_codebook(float* levels16, float* thresholds15);
+
+/* Bulk quantize `n` consecutive positions [start_pos, start_pos + n) of every
+ * (b, kv head) into the cache ([KV-4bit] §2.1 applied to the prefill rows).
+ *   k_f16, v_f16: device, [B, Hkv, n, D] fp16 contiguous (the prompt's K and V).
+ *   Position p goes to slot p % C.  Requires 0 <= start_pos, 1 <= n <= C
+ *   (KVQ_ERR_CAPACITY otherwise: more rows than slots would overwrite each other
+ *   within one call).
+ * INT4: per group, s = fl32(amax/7) (1 if 0), code = clamp(rne(fl32(x/s)), -7, 7).
+ * INT8: s = max(fl32(amax/127), 1e-8), code = clamp(rne(fl32(x/s)), -128, 127).
+ * Codec: y = H x / sqrt(D), s = ||x||_2 / sqrt(D), index = #{thresholds < y/s}. */
+int32_t kvq_quantize_prefill(const kvq_cache_desc* desc, const kvq_cache* cache,
+                             const void* k_f16, const void* v_f16,
+                             int32_t start_pos, int32_t n, kvq_stream stream);
+
+/* Quantize one new token's K/V row per (b, kv head) into slot pos[b] % C
+ * ([KV-4bit] §1.1 decode step: append the new token's K/V to the cache).
+ *   k_f16, v_f16: device, [B, Hkv, D] fp16 contiguous.
+ *   pos: host, [B] positions, each >= 0.
+ * Same arithmetic as kvq_quantize_prefill. */
+int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
+                   const void* k_f16, const void* v_f16, const int32_t* pos,
+                   kvq_stream stream);
+
+/* Single-token decode attention reading the packed cache, dequantizing in registers
+ * ([INT4-SM] §5 step 5; semantics of [KV-opt] §3.2):
+ *   out[b, h] = sum_t softmax_t(scale * q[b,h] . x_K[b,kv,t]) * x_V[b,kv,t]
+ * with kv = h / (q_heads / Hkv) (GQA), t over [max(0, len_b - window), len_b)
+ * (window = 0: [0, len_b)), x = the dequantized cache values.
+ *   q_f16: device, [B, q_heads, D] fp16.  q_heads must be a multiple of Hkv with
+ *          q_heads / Hkv in {1, 2, 4, 8}.
+ *   lens: host, [B], 1 <= len_b; positions 0..len_b-1 must be in the cache
+ *         (len_b <= C, or window in 1..C when len_b > C; KVQ_ERR_CAPACITY otherwise).
+ *   softmax_scale: 0 selects 1/sqrt(D).
+ *   num_splits: sequence splits per (b, kv head); 0 = kvq_plan_splits.
+ *   out: device, [B, q_heads, D] fp32.
+ *   workspace: device scratch of at least kvq_decode_workspace_bytes bytes
+ *              (KVQ_ERR_WORKSPACE otherwise); its contents are clobbered.
+ * Split-K: each split writes an unnormalized partial (running max, sum, weighted V)
+ * and a second kernel merges them with the log-sum-exp rule. */
+int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
+                        const void* q_f16, int32_t q_heads, const int32_t* lens,
+                        int32_t window, float softmax_scale, int32_t num_splits,
+                        float* out, void* workspace, size_t ws_bytes, kvq_stream stream);
+
+/* Dequantize positions [start_pos, start_pos + n) of K (kv = 0) or V (kv = 1)
+ * ([KV-4bit] §2.1 dequantize_4bit_group: code * scale; codec: s * H c[idx] / sqrt(D)).
+ *   out: device, [B, Hkv, n, D] fp32.  Requires 1 <= n <= C, start_pos >= 0. */
+int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t kv,
+                    int32_t start_pos, int32_t n, float* out, kvq_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

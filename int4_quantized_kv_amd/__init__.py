@@ -1,0 +1,14 @@
+"""INT4 KV-cache quantization and INT4 decode attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in the HIP library ``libkvq.so`` (C ABI: ``include/kvq.h``); this
+package is its Python binding.  Importing it fails if the library has not been built
+(``python -m int4_quantized_kv_amd.build``): there is no CPU fallback.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS, FORMATS, KVQ_ERR_ARG, KVQ_ERR_CAPACITY, KVQ_ERR_LAUNCH, KVQ_ERR_UNSUPPORTED,
+    KVQ_ERR_WORKSPACE, KVQ_INT4_G, KVQ_INT8_TOKEN, KVQ_MAX_BATCH, KVQ_OK, KVQ_WHT_LM4, LIB,
+    LIB_PATH, DeviceCache, KvqError, kvq_append, kvq_cache, kvq_cache_desc, kvq_check_desc,
+    kvq_codec_codebook, kvq_codes_bytes, kvq_decode_attn, kvq_decode_workspace_bytes,
+    kvq_dequant, kvq_plan_splits, kvq_quantize_prefill, kvq_scales_bytes, kvq_version,
+    make_desc, status_str,
+)

@@ -1,0 +1,255 @@
+// api.hip -- the C ABI declared in include/kvq.h: argument validation, size queries,
+// split planning and kernel dispatch.  Every check runs before anything is enqueued.
+#include <cmath>
+#include <cstring>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int32_t check_desc(const kvq_cache_desc* d) {
+  if (!d) return KVQ_ERR_ARG;
+  if (d->format < KVQ_INT4_G || d->format > KVQ_WHT_LM4) return KVQ_ERR_ARG;
+  if (d->batch < 1 || d->kv_heads < 1 || d->head_dim < 1 || d->capacity < 1)
+    return KVQ_ERR_ARG;
+  if (d->batch > KVQ_MAX_BATCH) return KVQ_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (d->format == KVQ_INT4_G) {
+    for (int32_t g : {d->group_k, d->group_v}) {
+      if (g < 1) return KVQ_ERR_ARG;
+      if (!pow2(g) || g < 32 || g > d->head_dim) return KVQ_ERR_UNSUPPORTED;
+    }
+  }
+  // 32-bit lane indexing inside the kernels
+  const uint64_t rows = (uint64_t)d->batch * d->kv_heads * d->capacity;
+  if (rows * (uint64_t)(d->head_dim / 8) >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+bool cache_ok(const kvq_cache* c) {
+  return c && c->k_codes && c->k_scales && c->v_codes && c->v_scales;
+}
+
+int32_t scales_per_row(const kvq_cache_desc* d, int32_t kv) {
+  if (d->format == KVQ_INT4_G) return d->head_dim / (kv ? d->group_v : d->group_k);
+  return 1;
+}
+
+int32_t launch_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH; }
+
+int32_t quant_common(const kvq_cache_desc* desc, const kvq_cache* cache, const void* k,
+                     const void* v, const SlotMap& map, int32_t n, hipStream_t stream) {
+  QuantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.k_codes = cache->k_codes;
+  a.k_scales = static_cast<float*>(cache->k_scales);
+  a.v_codes = cache->v_codes;
+  a.v_scales = static_cast<float*>(cache->v_scales);
+  a.B = desc->batch;
+  a.Hkv = desc->kv_heads;
+  a.D = desc->head_dim;
+  a.gk = desc->group_k;
+  a.gv = desc->group_v;
+  a.rows = desc->batch * desc->kv_heads * n;
+  a.map = map;
+  if (desc->format == KVQ_WHT_LM4) {
+    float lv[16];
+    codec_codebook(lv, a.thr);
+    return launch_status(launch_codec_encode(a, stream));
+  }
+  return launch_status(launch_quant_intq(desc->format, a, stream));
+}
+
+// Longest attended span over the batch; KVQ_ERR_* (negative) if a length is invalid.
+int32_t check_lens(const kvq_cache_desc* d, const int32_t* lens, int32_t window) {
+  int32_t span = 0;
+  for (int32_t b = 0; b < d->batch; ++b) {
+    const int32_t L = lens[b];
+    if (L < 1) return KVQ_ERR_ARG;
+    if (window == 0) {
+      if (L > d->capacity) return KVQ_ERR_CAPACITY;
+    } else if (L > d->capacity && window > d->capacity) {
+      return KVQ_ERR_CAPACITY;
+    }
+    const int32_t s = window > 0 && window < L ? window : L;
+    if (s > span) span = s;
+  }
+  return span;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_version(void) { return KVQ_VERSION; }
+
+const char* kvq_status_str(int32_t status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case KVQ_ERR_CAPACITY: return "positions do not fit the cache";
+    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t kvq_check_desc(const kvq_cache_desc* desc) { return check_desc(desc); }
+
+size_t kvq_codes_bytes(const kvq_cache_desc* d, int32_t kv) {
+  if (check_desc(d) != KVQ_OK || (kv != 0 && kv != 1)) return 0;
+  const size_t rows = (size_t)d->batch * d->kv_heads * d->capacity;
+  return d->format == KVQ_INT8_TOKEN ? rows * d->head_dim : rows * (d->head_dim / 2);
+}
+
+size_t kvq_scales_bytes(const kvq_cache_desc* d, int32_t kv) {
+  if (check_desc(d) != KVQ_OK || (kv != 0 && kv != 1)) return 0;
+  const size_t rows = (size_t)d->batch * d->kv_heads * d->capacity;
+  return rows * scales_per_row(d, kv) * sizeof(float);
+}
+
+int32_t kvq_plan_splits(const kvq_cache_desc* d, int32_t q_heads, int32_t span) {
+  if (check_desc(d) != KVQ_OK || q_heads < 1 || q_heads % d->kv_heads || span < 1) return 0;
+  return plan_splits(d->format, d->batch * d->kv_heads, q_heads / d->kv_heads, d->head_dim,
+                     span);
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache_desc* d, int32_t q_heads, int32_t max_len,
+                                  int32_t window, int32_t num_splits) {
+  if (check_desc(d) != KVQ_OK || q_heads < 1 || q_heads % d->kv_heads || max_len < 1 ||
+      window < 0 || num_splits < 0)
+    return 0;
+  const int32_t span = window > 0 && window < max_len ? window : max_len;
+  const int32_t ns = num_splits ? num_splits : kvq_plan_splits(d, q_heads, span);
+  return (size_t)d->batch * q_heads * ns * (d->head_dim + 2) * sizeof(float);
+}
+
+int32_t kvq_codec_codebook(float* levels16, float* thresholds15) {
+  if (!levels16 || !thresholds15) return KVQ_ERR_ARG;
+  codec_codebook(levels16, thresholds15);
+  return KVQ_OK;
+}
+
+int32_t kvq_quantize_prefill(const kvq_cache_desc* desc, const kvq_cache* cache,
+                             const void* k_f16, const void* v_f16, int32_t start_pos,
+                             int32_t n, kvq_stream stream) {
+  const int32_t st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (!cache_ok(cache) || !k_f16 || !v_f16 || start_pos < 0 || n < 1) return KVQ_ERR_ARG;
+  if (n > desc->capacity) return KVQ_ERR_CAPACITY;
+  if ((uint64_t)desc->batch * desc->kv_heads * n * (desc->head_dim / 8) >= (1ull << 31))
+    return KVQ_ERR_UNSUPPORTED;
+  if ((int64_t)start_pos + n - 1 > INT32_MAX) return KVQ_ERR_ARG;
+  SlotMap map;
+  std::memset(&map, 0, sizeof(map));
+  map.append = 0;
+  map.start = start_pos;
+  map.n = n;
+  map.cap = desc->capacity;
+  return quant_common(desc, cache, k_f16, v_f16, map, n, static_cast<hipStream_t>(stream));
+}
+
+int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache, const void* k_f16,
+                   const void* v_f16, const int32_t* pos, kvq_stream stream) {
+  const int32_t st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (!cache_ok(cache) || !k_f16 || !v_f16 || !pos) return KVQ_ERR_ARG;
+  SlotMap map;
+  std::memset(&map, 0, sizeof(map));
+  for (int32_t b = 0; b < desc->batch; ++b) {
+    if (pos[b] < 0) return KVQ_ERR_ARG;
+    map.pos[b] = pos[b];
+  }
+  map.append = 1;
+  map.n = 1;
+  map.cap = desc->capacity;
+  return quant_common(desc, cache, k_f16, v_f16, map, 1, static_cast<hipStream_t>(stream));
+}
+
+int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache, const void* q_f16,
+                        int32_t q_heads, const int32_t* lens, int32_t window,
+                        float softmax_scale, int32_t num_splits, float* out, void* workspace,
+                        size_t ws_bytes, kvq_stream stream) {
+  const int32_t st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (!cache_ok(cache) || !q_f16 || !lens || !out || window < 0 || num_splits < 0 ||
+      q_heads < 1 || !std::isfinite(softmax_scale))
+    return KVQ_ERR_ARG;
+  if (q_heads % desc->kv_heads) return KVQ_ERR_ARG;
+  const int32_t G = q_heads / desc->kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
+  const int32_t span = check_lens(desc, lens, window);
+  if (span < 0) return span;
+  const int32_t ns = num_splits ? num_splits : kvq_plan_splits(desc, q_heads, span);
+  if (ns < 1 || ns > 65535) return KVQ_ERR_ARG;
+  const size_t need = (size_t)desc->batch * q_heads * ns * (desc->head_dim + 2) * sizeof(float);
+  if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k_codes = cache->k_codes;
+  a.k_scales = static_cast<const float*>(cache->k_scales);
+  a.v_codes = cache->v_codes;
+  a.v_scales = static_cast<const float*>(cache->v_scales);
+  a.q = static_cast<const uint16_t*>(q_f16);
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = a.ws_acc + (size_t)desc->batch * q_heads * ns * desc->head_dim;
+  a.out = out;
+  a.B = desc->batch;
+  a.Hkv = desc->kv_heads;
+  a.Hq = q_heads;
+  a.D = desc->head_dim;
+  a.cap = desc->capacity;
+  a.gk = desc->group_k;
+  a.gv = desc->group_v;
+  a.window = window;
+  a.nsplit = ns;
+  const float scale = softmax_scale != 0.0f ? softmax_scale
+                                            : 1.0f / std::sqrt((float)desc->head_dim);
+  a.qscale = scale * 1.4426950408889634f;  // log2(e): scores in base-2 units
+  if (desc->format == KVQ_WHT_LM4) {
+    float thr[15];
+    codec_codebook(a.levels, thr);
+  }
+  for (int32_t b = 0; b < desc->batch; ++b) a.lens[b] = lens[b];
+  return launch_status(launch_decode(desc->format, a, G, static_cast<hipStream_t>(stream)));
+}
+
+int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t kv,
+                    int32_t start_pos, int32_t n, float* out, kvq_stream stream) {
+  const int32_t st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (!cache_ok(cache) || !out || (kv != 0 && kv != 1) || start_pos < 0 || n < 1)
+    return KVQ_ERR_ARG;
+  if (n > desc->capacity) return KVQ_ERR_CAPACITY;
+  if ((uint64_t)desc->batch * desc->kv_heads * n * (desc->head_dim / 8) >= (1ull << 31))
+    return KVQ_ERR_UNSUPPORTED;
+  DequantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.codes = kv ? cache->v_codes : cache->k_codes;
+  a.scales = static_cast<const float*>(kv ? cache->v_scales : cache->k_scales);
+  a.out = out;
+  a.B = desc->batch;
+  a.Hkv = desc->kv_heads;
+  a.D = desc->head_dim;
+  a.g = kv ? desc->group_v : desc->group_k;
+  a.cap = desc->capacity;
+  a.start = start_pos;
+  a.n = n;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (desc->format == KVQ_WHT_LM4) {
+    float thr[15];
+    codec_codebook(a.levels, thr);
+    return launch_status(launch_codec_dequant(a, s));
+  }
+  return launch_status(launch_dequant_intq(desc->format, a, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// codec.hip -- Walsh-Hadamard rotation + 4-bit Lloyd-Max KV codec: encode (prefill and
+// append), dequantize, and the library's own codebook.
+//
+// Page: "长上下文内存大瘦身：LARQL 四大 KV 缓存引擎原理与横向对比" (pwwt.cn/news/5725003),
+// engine three (codec): every K/V row is coded per head by a Walsh-Hadamard rotation
+// followed by Lloyd-Max quantization at 3 or 4 bits; head_dim must be a power of two.
+// The page gives no further detail; this library takes the plainest algorithm that
+// fits it: y = H x / sqrt(D) (Sylvester order, orthonormal, no sign flips),
+// s = ||x||_2 / sqrt(D), index = number of Lloyd-Max decision thresholds of N(0,1)
+// strictly below y / s (a zero row is coded as y / 1), decode x = s * H c[index] / sqrt(D).
+//
+// Mapping: as for INT4, a row of D elements spans D/8 lanes of 8 elements; three
+// butterfly stages run inside a lane, log2(D/8) across lanes with xor shuffles.
+#include <cmath>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+template <int D>
+__global__ void __launch_bounds__(256) codec_encode_kernel(QuantArgs a) {
+  constexpr int LPR = D / 8;
+  const int isv = blockIdx.y;
+  const uint16_t* src = isv ? a.v : a.k;
+  uint32_t* codes = reinterpret_cast<uint32_t*>(isv ? a.v_codes : a.k_codes);
+  float* scales = isv ? a.v_scales : a.k_scales;
+  const uint32_t total = (uint32_t)a.rows * LPR;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const uint32_t row = i / LPR;
+    const int c = (int)(i - row * LPR);
+    float x[8];
+    load8_f16(src + (size_t)i * 8, x);
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(x[j], x[j], ss);
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
+    wht_row<LPR>(x, c);
+    const float s = sqrtf(ss / (float)D);
+    const float inv = inv_sqrt_d / (s == 0.0f ? 1.0f : s);  // u = (H x / sqrt(D)) / s
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float u = x[j] * inv;
+      int idx = 0;
+#pragma unroll
+      for (int k = 0; k < 15; ++k) idx += (a.thr[k] < u) ? 1 : 0;
+      w |= (uint32_t)idx << (4 * j);
+    }
+    const uint32_t bh = row / (uint32_t)a.map.n;
+    const int t = (int)(row - bh * a.map.n);
+    const int b = (int)(bh / (uint32_t)a.Hkv);
+    const int p = a.map.append ? a.map.pos[b] : a.map.start + t;
+    const size_t drow = (size_t)bh * a.map.cap + p % a.map.cap;
+    codes[drow * LPR + c] = w;
+    if (c == 0) scales[drow] = s;
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) codec_dequant_kernel(DequantArgs a) {
+  constexpr int LPR = D / 8;
+  __shared__ float lv[16];
+  if (threadIdx.x < 16) lv[threadIdx.x] = a.levels[threadIdx.x];
+  __syncthreads();
+  const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.codes);
+  const uint32_t total = (uint32_t)a.B * a.Hkv * a.n * LPR;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  // a row's LPR lanes are aligned and consecutive, so they enter and leave the loop
+  // together and the butterfly shuffles never read a lane outside the row
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const uint32_t row = i / LPR;
+    const int c = (int)(i - row * LPR);
+    const uint32_t bh = row / (uint32_t)a.n;
+    const int t = (int)(row - bh * a.n);
+    const size_t drow = (size_t)bh * a.cap + (a.start + t) % a.cap;
+    const uint32_t w = codes[drow * LPR + c];
+    const float s = a.scales[drow];
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = lv[nib_u(w, j)];
+    wht_row<LPR>(v, c);
+    const float f = s * inv_sqrt_d;
+    float4* out = reinterpret_cast<float4*>(a.out + (size_t)i * 8);
+    out[0] = make_float4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+    out[1] = make_float4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
+  }
+}
+
+inline int grid_for(uint64_t lanes) {
+  uint64_t blocks = (lanes + 255) / 256;
+  const uint64_t cap = 256ull * 16;
+  return (int)(blocks < cap ? (blocks ? blocks : 1) : cap);
+}
+
+struct Book {
+  float levels[16];
+  float thresholds[15];
+};
+
+double phi(double t) { return std::exp(-0.5 * t * t) / std::sqrt(2.0 * M_PI); }
+double Phi(double t) { return 0.5 * std::erfc(-t / std::sqrt(2.0)); }
+
+// Lloyd's two optimality conditions for N(0,1), iterated to a fixed point in double:
+// thresholds are midpoints of adjacent levels; each level is the mean of its cell,
+// (phi(lo) - phi(hi)) / (Phi(hi) - Phi(lo)).
+Book compute_book() {
+  double c[16];
+  for (int i = 0; i < 16; ++i) c[i] = -2.5 + 5.0 * i / 15.0;
+  for (int it = 0; it < 200000; ++it) {
+    double t[15];
+    for (int j = 0; j < 15; ++j) t[j] = 0.5 * (c[j] + c[j + 1]);
+    double delta = 0.0;
+    for (int j = 0; j < 16; ++j) {
+      const double plo = j == 0 ? 0.0 : phi(t[j - 1]);
+      const double phi_hi = j == 15 ? 0.0 : phi(t[j]);
+      const double Plo = j == 0 ? 0.0 : Phi(t[j - 1]);
+      const double Phi_hi = j == 15 ? 1.0 : Phi(t[j]);
+      const double cn = (plo - phi_hi) / (Phi_hi - Plo);
+      delta = std::fmax(delta, std::fabs(cn - c[j]));
+      c[j] = cn;
+    }
+    if (delta < 1e-14) break;
+  }
+  // N(0,1) is symmetric, so is its optimal quantizer: make the levels exactly odd so
+  // that the middle threshold is exactly 0
+  double cs[16];
+  for (int j = 0; j < 16; ++j) cs[j] = 0.5 * (c[j] - c[15 - j]);
+  for (int j = 0; j < 16; ++j) c[j] = cs[j];
+  Book b;
+  for (int j = 0; j < 16; ++j) b.levels[j] = (float)c[j];
+  for (int j = 0; j < 15; ++j) b.thresholds[j] = (float)(0.5 * (c[j] + c[j + 1]));
+  return b;
+}
+
+}  // namespace
+
+void codec_codebook(float levels[16], float thresholds[15]) {
+  static const Book book = compute_book();  // computed once, constant afterwards
+  for (int j = 0; j < 16; ++j) levels[j] = book.levels[j];
+  for (int j = 0; j < 15; ++j) thresholds[j] = book.thresholds[j];
+}
+
+hipError_t launch_codec_encode(const QuantArgs& a, hipStream_t s) {
+  const uint64_t lanes = (uint64_t)a.rows * (a.D / 8);
+  dim3 grid(grid_for(lanes), 2);
+  switch (a.D) {
+    case 64: return launch_kernel(codec_encode_kernel<64>, grid, dim3(256), a, s);
+    case 128: return launch_kernel(codec_encode_kernel<128>, grid, dim3(256), a, s);
+    case 256: return launch_kernel(codec_encode_kernel<256>, grid, dim3(256), a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_codec_dequant(const DequantArgs& a, hipStream_t s) {
+  const uint64_t lanes = (uint64_t)a.B * a.Hkv * a.n * (a.D / 8);
+  const dim3 grid(grid_for(lanes));
+  switch (a.D) {
+    case 64: return launch_kernel(codec_dequant_kernel<64>, grid, dim3(256), a, s);
+    case 128: return launch_kernel(codec_dequant_kernel<128>, grid, dim3(256), a, s);
+    case 256: return launch_kernel(codec_dequant_kernel<256>, grid, dim3(256), a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

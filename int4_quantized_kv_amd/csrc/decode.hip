@@ -1,0 +1,251 @@
+// decode.hip -- split-K single-token decode attention over the packed cache (all three
+// formats, any supported GQA group), plus the log-sum-exp merge of the splits.
+//
+// Semantics: bxzpzcl.cn/news/2871434 section 3.2 (window [len - W, len), query head h
+// reads KV head h / (Hq / Hkv), softmax scale head_dim^-1/2); lpnh.cn/news/2042373
+// section 1.1 (each decode step attends over the whole cache); the operator reads the
+// packed data and dequantizes inside ("LLM长上下文推理优化：用INT4状态机管理KV Cache",
+// pwwt.cn/news/4219524, section 5 step 5).
+//
+// Stage 1 (decode_splitk_kernel): one workgroup per (split, kv head, batch).  A row of
+// D values spans D/8 lanes (8 values per lane), so a 256-lane workgroup walks 2048/D
+// positions at a time; the G query heads of the KV head share every K/V load.  Scores
+// are kept in log2 units (q is pre-scaled by scale * log2 e) with an online softmax per
+// lane row; the rows are combined through LDS and the workgroup writes one unnormalized
+// partial (max, sum, weighted V) per query head.
+// Stage 2 (merge_kernel): out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
+// Codec: keys/values stay in the rotated domain.  Since H/sqrt(D) is orthonormal and
+// symmetric, q . x_hat = (H q / sqrt(D)) . (s c[idx]); q is rotated once per workgroup
+// and the merged output is rotated back once per (b, h).
+#include <cmath>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+// Dequantize the 8 values lane c owns of row `row` (cache row index b*Hkv*C + slot).
+template <int D, int FMT>
+__device__ __forceinline__ void load_row(const void* codes, const float* scales, int g,
+                                         size_t row, int c, const float* lv, float x[8]) {
+  constexpr int LPR = D / 8;
+  if (FMT == KVQ_INT4_G) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[row * LPR + c];
+    const float s = scales[row * (D / g) + (8 * c) / g];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (float)nib_s(w, j) * s;
+  } else if (FMT == KVQ_INT8_TOKEN) {
+    const uint2 w = reinterpret_cast<const uint2*>(codes)[row * LPR + c];
+    const float s = scales[row];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = (float)(int8_t)((w.x >> (8 * j)) & 255u) * s;
+      x[j + 4] = (float)(int8_t)((w.y >> (8 * j)) & 255u) * s;
+    }
+  } else {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[row * LPR + c];
+    const float s = scales[row];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = lv[nib_u(w, j)] * s;
+  }
+}
+
+template <int D, int G, int FMT>
+__global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
+  constexpr int LPR = D / 8;
+  constexpr int NGRP = 256 / LPR;
+  __shared__ float s_m[NGRP][G];
+  __shared__ float s_l[NGRP][G];
+  __shared__ float s_acc[NGRP][G][D];
+  __shared__ float lv[16];
+  if (FMT == KVQ_WHT_LM4) {
+    if (threadIdx.x < 16) lv[threadIdx.x] = a.levels[threadIdx.x];
+    __syncthreads();
+  }
+
+  const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, grp = tid / LPR, c = tid % LPR;
+  const int len = a.lens[b];
+  const int lo = a.window > 0 ? max(0, len - a.window) : 0;
+  const int span = len - lo;
+  const int chunk = (span + a.nsplit - 1) / a.nsplit;
+  const int ps = min(len, lo + sp * chunk);
+  const int pe = min(len, ps + chunk);
+
+  float q[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    load8_f16(a.q + ((size_t)(b * a.Hq + kvh * G + h) * D + 8 * c), q[h]);
+    if (FMT == KVQ_WHT_LM4) {
+      wht_row<LPR>(q[h], c);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[h][j] *= 1.0f / sqrtf((float)D);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[h][j] *= a.qscale;
+  }
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = NEG_INF;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
+  }
+
+  const size_t bh = (size_t)b * a.Hkv + kvh;
+  for (int t = ps + grp; t < pe; t += NGRP) {
+    const size_t row = bh * a.cap + (t % a.cap);
+    float kx[8], vx[8];
+    load_row<D, FMT>(a.k_codes, a.k_scales, a.gk, row, c, lv, kx);
+    load_row<D, FMT>(a.v_codes, a.v_scales, a.gv, row, c, lv, vx);
+    float z[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float d = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) d = __builtin_fmaf(q[h][j], kx[j], d);
+      z[h] = d;
+    }
+    // the LPR lanes of a row share the trip count, so the row's shuffles are complete
+#pragma unroll
+    for (int msk = 1; msk < LPR; msk <<= 1) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) z[h] += __shfl_xor(z[h], msk);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mn = fmaxf(m[h], z[h]);
+      const float corr = fast_exp2(m[h] - mn);
+      const float p = fast_exp2(z[h] - mn);
+      l[h] = __builtin_fmaf(l[h], corr, p);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[h][j] = __builtin_fmaf(acc[h][j], corr, p * vx[j]);
+      m[h] = mn;
+    }
+  }
+
+  if (c == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_m[grp][h] = m[h];
+      s_l[grp][h] = l[h];
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_acc[grp][h][8 * c + j] = acc[h][j];
+  __syncthreads();
+
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx % D;
+    float M = NEG_INF;
+    for (int gi = 0; gi < NGRP; ++gi) M = fmaxf(M, s_m[gi][h]);
+    float A = 0.0f, L = 0.0f;
+    if (M != NEG_INF) {
+      for (int gi = 0; gi < NGRP; ++gi) {
+        const float mg = s_m[gi][h];
+        if (mg != NEG_INF) {
+          const float w = fast_exp2(mg - M);
+          A = __builtin_fmaf(s_acc[gi][h][d], w, A);
+          L = __builtin_fmaf(s_l[gi][h], w, L);
+        }
+      }
+    }
+    const size_t o = (size_t)(b * a.Hq + kvh * G + h) * a.nsplit + sp;
+    a.ws_acc[o * D + d] = A;
+    if (d == 0) {
+      a.ws_ml[2 * o] = M;
+      a.ws_ml[2 * o + 1] = L;
+    }
+  }
+}
+
+template <int D, bool CODEC>
+__global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
+  __shared__ float sh[D];
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const size_t base = (size_t)(b * a.Hq + h) * a.nsplit;
+  float M = NEG_INF;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_ml[2 * (base + s)]);
+  float A = 0.0f, L = 0.0f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float ms = a.ws_ml[2 * (base + s)];
+    if (ms != NEG_INF) {
+      const float w = fast_exp2(ms - M);
+      A = __builtin_fmaf(a.ws_acc[(base + s) * D + d], w, A);
+      L = __builtin_fmaf(a.ws_ml[2 * (base + s) + 1], w, L);
+    }
+  }
+  float o = A / L;
+  if (CODEC) {
+    sh[d] = o;
+    __syncthreads();
+    for (int hh = 1; hh < D; hh <<= 1) {
+      const float mine = sh[d], other = sh[d ^ hh];
+      __syncthreads();
+      sh[d] = (d & hh) ? other - mine : mine + other;
+      __syncthreads();
+    }
+    o = sh[d] * (1.0f / sqrtf((float)D));
+  }
+  a.out[(size_t)(b * a.Hq + h) * D + d] = o;
+}
+
+template <int D, int FMT>
+hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
+  const dim3 grid(a.nsplit, a.Hkv, a.B);
+  hipError_t e;
+  switch (G) {
+    case 1: e = launch_kernel(decode_splitk_kernel<D, 1, FMT>, grid, dim3(256), a, s); break;
+    case 2: e = launch_kernel(decode_splitk_kernel<D, 2, FMT>, grid, dim3(256), a, s); break;
+    case 4: e = launch_kernel(decode_splitk_kernel<D, 4, FMT>, grid, dim3(256), a, s); break;
+    case 8: e = launch_kernel(decode_splitk_kernel<D, 8, FMT>, grid, dim3(256), a, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  return launch_kernel(merge_kernel<D, FMT == KVQ_WHT_LM4>, dim3(a.Hq, a.B), dim3(D), a, s);
+}
+
+template <int D>
+hipError_t launch_fmt(int32_t format, const DecodeArgs& a, int G, hipStream_t s) {
+  switch (format) {
+    case KVQ_INT4_G: return launch_d<D, KVQ_INT4_G>(a, G, s);
+    case KVQ_INT8_TOKEN: return launch_d<D, KVQ_INT8_TOKEN>(a, G, s);
+    case KVQ_WHT_LM4: return launch_d<D, KVQ_WHT_LM4>(a, G, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int32_t plan_splits(int32_t format, int32_t units, int32_t q_group, int32_t head_dim,
+                    int32_t span) {
+  (void)format;
+  (void)q_group;
+  (void)head_dim;
+  if (units <= 0 || span <= 0) return 0;
+  const int32_t target = 2048;       // workgroups: 8 per CU on 256 CUs
+  const int32_t min_rows = 256;      // positions per split worth a workgroup
+  int32_t n = (target + units - 1) / units;
+  const int32_t by_span = (span + min_rows - 1) / min_rows;
+  if (n > by_span) n = by_span;
+  if (n > 1024) n = 1024;
+  return n < 1 ? 1 : n;
+}
+
+hipError_t launch_decode(int32_t format, const DecodeArgs& a, int32_t q_group, hipStream_t s) {
+  switch (a.D) {
+    case 64: return launch_fmt<64>(format, a, q_group, s);
+    case 128: return launch_fmt<128>(format, a, q_group, s);
+    case 256: return launch_fmt<256>(format, a, q_group, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

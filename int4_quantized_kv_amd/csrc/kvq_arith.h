@@ -1,0 +1,44 @@
+// kvq_arith.h -- scalar arithmetic of the quantizers, shared by the gfx950 kernels and
+// by a host-compiled exhaustive check of the same instruction sequence.
+//
+// The INT4 rule (lpnh.cn/news/2042373, section 2.1) and the INT8 rule
+// (bxzpzcl.cn/news/2871434, section 3.1) both need q = round_half_even(fl32(x / s)).
+// A correctly rounded IEEE divide costs ~10 VALU instructions on gfx950.  Here the
+// quotient is formed from one reciprocal per group instead:
+//   r  = fl32(1 / s)                 (one IEEE divide per group)
+//   y0 = fl32(x * r)
+//   e  = fma(-y0, s, x)              (exact residual x - y0 * s)
+//   y1 = fma(e, r, y0)               (Markstein-style correction)
+// For every fp16 x and every scale s the quantizers can produce from an fp16 amax
+// with |x| <= amax (s = fl32(amax/7), and s = max(fl32(amax/127), 1e-8)), y1 equals
+// fl32(x / s) bit for bit; the host test enumerates all ~1e9 such pairs per rule.
+#ifndef KVQ_ARITH_H
+#define KVQ_ARITH_H
+
+#if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
+#define KVQ_HD __host__ __device__ inline __attribute__((always_inline))
+#else
+#define KVQ_HD static inline
+#endif
+
+// fl32(x / s) given r = fl32(1 / s), for the (x, s) domain described above.
+KVQ_HD float kvq_div_exact(float x, float s, float r) {
+  float y0 = x * r;
+  float e = __builtin_fmaf(-y0, s, x);
+  return __builtin_fmaf(e, r, y0);
+}
+
+// INT4 group scale from the group's amax: fl32(amax / 7), 1 for an all-zero group.
+KVQ_HD float kvq_int4_scale(float amax) {
+  float s = amax / 7.0f;
+  return s == 0.0f ? 1.0f : s;
+}
+
+// INT8 per-token scale: max(fl32(amax / 127), 1e-8f).
+KVQ_HD float kvq_int8_scale(float amax) {
+  float s = amax / 127.0f;
+  return s < 1e-8f ? 1e-8f : s;
+}
+
+#endif  // KVQ_ARITH_H

@@ -1,0 +1,73 @@
+// kvq_device.h -- small device helpers shared by the gfx950 kernels.
+#ifndef KVQ_DEVICE_H
+#define KVQ_DEVICE_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Eight consecutive fp16 values (one 16-byte load) widened to fp32 (exact).
+__device__ __forceinline__ void load8_f16(const uint16_t* p, float x[8]) {
+  const uint4 r = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+    x[2 * i] = (float)h.x;
+    x[2 * i + 1] = (float)h.y;
+  }
+}
+
+// Signed 4-bit field j (0..7) of a packed word, as an int in -8..7.
+__device__ __forceinline__ int nib_s(uint32_t w, int j) {
+  return (int32_t)(w << (28 - 4 * j)) >> 28;
+}
+
+// Unsigned 4-bit field j of a packed word.
+__device__ __forceinline__ int nib_u(uint32_t w, int j) { return (w >> (4 * j)) & 15; }
+
+// Unnormalized Sylvester Walsh-Hadamard transform of one row spread over `lpr`
+// consecutive lanes, each holding 8 consecutive elements (element 8*c + i in lane c).
+// Butterflies (a, b) -> (a + b, a - b) over every bit of the element index; the
+// three low bits are inside a lane, the others pair lane c with lane c ^ m.
+template <int LPR>
+__device__ __forceinline__ void wht_row(float v[8], int c) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __shfl_xor(v[i], m);
+      v[i] = (c & m) ? (p - v[i]) : (v[i] + p);
+    }
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Enqueue `kernel(args)` and return the runtime's status for this launch only (the
+// thread's last-error slot may hold an unrelated earlier status, e.g. a not-ready
+// query made by the caller, so it is never consulted).
+template <typename Args>
+inline hipError_t launch_kernel(void (*kernel)(Args), dim3 grid, dim3 block, const Args& a,
+                                hipStream_t s) {
+  void* params[] = {const_cast<Args*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, params, 0, s);
+}
+
+}  // namespace kvq
+
+#endif  // KVQ_DEVICE_H

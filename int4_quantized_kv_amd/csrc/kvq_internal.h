@@ -1,0 +1,75 @@
+// kvq_internal.h -- launch interfaces between the C-ABI layer (api.hip) and the kernel
+// translation units.  Not installed; not part of the ABI.
+#ifndef KVQ_INTERNAL_H
+#define KVQ_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+// Where row (b, h, t) of a quantize call lands: slot (start + t) % cap for a prefill,
+// slot pos[b] % cap for an append (n == 1).
+struct SlotMap {
+  int32_t append;   // 0: prefill, 1: append
+  int32_t start;
+  int32_t n;        // rows per (b, h) in the source tensor
+  int32_t cap;
+  int32_t pos[KVQ_MAX_BATCH];
+};
+
+struct QuantArgs {
+  const uint16_t* k;     // fp16 source [B, Hkv, n, D]
+  const uint16_t* v;
+  void* k_codes;
+  float* k_scales;
+  void* v_codes;
+  float* v_scales;
+  int32_t B, Hkv, D, gk, gv;
+  int32_t rows;          // B * Hkv * n
+  float thr[15];         // codec decision thresholds (codec format only)
+  SlotMap map;
+};
+
+struct DequantArgs {
+  const void* codes;
+  const float* scales;
+  float* out;            // [B, Hkv, n, D]
+  int32_t B, Hkv, D, g, cap, start, n;
+  float levels[16];      // codec output levels (codec format only)
+};
+
+struct DecodeArgs {
+  const void* k_codes;
+  const float* k_scales;
+  const void* v_codes;
+  const float* v_scales;
+  const uint16_t* q;     // [B, Hq, D] fp16
+  float* ws_acc;         // [B, Hq, nsplit, D]
+  float* ws_ml;          // [B, Hq, nsplit, 2] (running max in log2 units, sum)
+  float* out;            // [B, Hq, D]
+  int32_t B, Hkv, Hq, D, cap, gk, gv, window, nsplit;
+  float qscale;          // softmax scale * log2(e)
+  float levels[16];
+  int32_t lens[KVQ_MAX_BATCH];
+};
+
+hipError_t launch_quant_intq(int32_t format, const QuantArgs& a, hipStream_t s);
+hipError_t launch_dequant_intq(int32_t format, const DequantArgs& a, hipStream_t s);
+hipError_t launch_codec_encode(const QuantArgs& a, hipStream_t s);
+hipError_t launch_codec_dequant(const DequantArgs& a, hipStream_t s);
+hipError_t launch_decode(int32_t format, const DecodeArgs& a, int32_t q_group, hipStream_t s);
+
+// Split plan of the decode kernels for `units` (b, kv head) pairs and a longest
+// attended span of `span` positions.
+int32_t plan_splits(int32_t format, int32_t units, int32_t q_group, int32_t head_dim,
+                    int32_t span);
+
+// The library's own 4-bit Lloyd-Max codebook of N(0,1) (computed once, then constant).
+void codec_codebook(float levels[16], float thresholds[15]);
+
+}  // namespace kvq
+
+#endif  // KVQ_INTERNAL_H

@@ -1,0 +1,161 @@
+"""Host-side tests of the C ABI (no GPU work): exports, size queries, validation errors,
+the library's codebook against the oracle's, and an exhaustive check of the quantizers'
+scalar arithmetic compiled for the host."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import int4_quantized_kv_amd as kvq
+from oracle import codec, memory
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 12
+    assert sorted(kvq.EXPORTS) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (kvq_\w+)", out))
+    for n in names:
+        assert n in exported, n
+    assert kvq.kvq_version() == 1
+
+
+def test_status_strings():
+    assert kvq.status_str(0) == "ok"
+    assert kvq.status_str(-4) == "workspace too small"
+    assert kvq.status_str(12345) == "unknown status"
+
+
+def test_size_queries_match_closed_forms():
+    for fmt in ("int4", "int8", "codec"):
+        for (B, H, D, C, gk, gv) in [(8, 8, 128, 8193, 64, 128), (1, 4, 256, 1024, 64, 128),
+                                     (3, 2, 64, 17, 32, 64)]:
+            d = kvq.make_desc(fmt, B, H, D, C, gk, gv)
+            assert kvq.kvq_check_desc(d) == 0
+            if fmt == "int4":
+                assert kvq.kvq_codes_bytes(d, 0) + kvq.kvq_scales_bytes(d, 0) == \
+                    memory.int4_cache_bytes(B, H, C, D, gk)
+                assert kvq.kvq_codes_bytes(d, 1) + kvq.kvq_scales_bytes(d, 1) == \
+                    memory.int4_cache_bytes(B, H, C, D, gv)
+            elif fmt == "int8":
+                assert kvq.kvq_codes_bytes(d, 0) == B * H * C * D
+                assert kvq.kvq_scales_bytes(d, 1) == B * H * C * 4
+            else:
+                assert kvq.kvq_codes_bytes(d, 1) == B * H * C * D // 2
+                assert kvq.kvq_scales_bytes(d, 0) == B * H * C * 4
+            assert kvq.kvq_codes_bytes(d, 2) == 0
+    # effective bits with fp32 scales: K (g=64) 4.5 bits, V (g=128) 4.25 bits per element
+    d = kvq.make_desc("int4", 1, 1, 128, 1000)
+    kb = (kvq.kvq_codes_bytes(d, 0) + kvq.kvq_scales_bytes(d, 0)) * 8 / (1000 * 128)
+    vb = (kvq.kvq_codes_bytes(d, 1) + kvq.kvq_scales_bytes(d, 1)) * 8 / (1000 * 128)
+    assert kb == memory.effective_bits(64, scale_bits=32) == 4.5
+    assert vb == memory.effective_bits(128, scale_bits=32) == 4.25
+
+
+@pytest.mark.parametrize("fields,status", [
+    (dict(format=7), kvq.KVQ_ERR_ARG),
+    (dict(batch=0), kvq.KVQ_ERR_ARG),
+    (dict(batch=257), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(head_dim=96), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(group_k=48), kvq.KVQ_ERR_UNSUPPORTED),     # not a power of two / D % g != 0
+    (dict(group_k=16), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(group_v=256), kvq.KVQ_ERR_UNSUPPORTED),    # g > D
+    (dict(capacity=0), kvq.KVQ_ERR_ARG),
+    (dict(kv_heads=-1), kvq.KVQ_ERR_ARG),
+])
+def test_descriptor_validation(fields, status):
+    base = dict(format=0, batch=2, kv_heads=4, head_dim=128, capacity=64, group_k=64, group_v=128)
+    base.update(fields)
+    d = kvq.kvq_cache_desc(*[base[k] for k in ("format", "batch", "kv_heads", "head_dim",
+                                               "capacity", "group_k", "group_v")])
+    assert kvq.kvq_check_desc(d) == status
+    assert kvq.kvq_codes_bytes(d, 0) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation before any launch
+
+
+def _cache():
+    return kvq.kvq_cache(FAKE, FAKE, FAKE, FAKE)
+
+
+def _expect(status, fn, *args):
+    with pytest.raises(kvq.KvqError) as e:
+        fn(*args)
+    assert e.value.status == status
+
+
+def test_error_paths_enqueue_nothing():
+    d = kvq.make_desc("int4", 2, 4, 128, 64)
+    c = _cache()
+    # prefill: n > capacity, n < 1, negative start, null source
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_quantize_prefill, d, c, FAKE, FAKE, 0, 65, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_quantize_prefill, d, c, FAKE, FAKE, 0, 0, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_quantize_prefill, d, c, FAKE, FAKE, -1, 4, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_quantize_prefill, d, c, 0, FAKE, 0, 4, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_quantize_prefill, d, kvq.kvq_cache(FAKE, 0, FAKE, FAKE),
+            FAKE, FAKE, 0, 4, 0)
+    # append: negative position
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_append, d, c, FAKE, FAKE, [3, -1], 0)
+    # decode: Hq % Hkv, unsupported group, len 0, len > capacity without window,
+    # window > capacity with len > capacity, too-small / missing workspace
+    ws = kvq.kvq_decode_workspace_bytes(d, 8, 64)
+    assert ws == 2 * 8 * kvq.kvq_plan_splits(d, 8, 64) * 130 * 4
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 6, [10, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
+    _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_decode_attn, d, c, FAKE, 64, [10, 10], 0, 0.0, 0, FAKE, FAKE, 1 << 30, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [10, 0], 0, 0.0, 0, FAKE, FAKE, ws, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_decode_attn, d, c, FAKE, 8, [65, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_decode_attn, d, c, FAKE, 8, [100, 10], 65, 0.0, 0, FAKE, FAKE, ws, 0)
+    _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, FAKE, ws - 1, 0)
+    _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, 0, ws, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], -1, 0.0, 0, FAKE, FAKE, ws, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, float("nan"), 0, FAKE, FAKE, ws, 0)
+    # dequant: bad kv selector, n > capacity
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_dequant, d, c, 2, 0, 4, FAKE, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_dequant, d, c, 0, 0, 65, FAKE, 0)
+    # an invalid descriptor is reported by every call
+    bad = kvq.make_desc("codec", 2, 4, 96, 64)
+    _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_quantize_prefill, bad, c, FAKE, FAKE, 0, 4, 0)
+    _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_dequant, bad, c, 0, 0, 4, FAKE, 0)
+
+
+def test_split_plan():
+    d2 = kvq.make_desc("int4", 8, 8, 128, 8193)
+    n2 = kvq.kvq_plan_splits(d2, 32, 8193)
+    assert 1 <= n2 <= 64
+    d5 = kvq.make_desc("int4", 1, 8, 128, 131072)
+    assert kvq.kvq_plan_splits(d5, 32, 131072) >= 64     # 8 natural units need splitting
+    assert kvq.kvq_plan_splits(d5, 32, 1) == 1
+    assert kvq.kvq_plan_splits(d5, 31, 100) == 0
+
+
+def test_library_codebook_matches_oracle():
+    lv, th = kvq.kvq_codec_codebook()
+    c, t, _ = codec.codebook(4)
+    assert np.allclose(lv, c, atol=1e-6) and np.allclose(th, t, atol=1e-6)
+    assert th[7] == 0.0 and lv[7] == -lv[8]
+
+
+@pytest.mark.parametrize("rule", ["int4", "int8"])
+def test_quantizer_arithmetic_exhaustive_on_host(tmp_path, rule):
+    exe = tmp_path / "arith_exhaustive"
+    src = os.path.join(ROOT, "tests", "host", "arith_exhaustive.c")
+    inc = os.path.join(ROOT, "int4_quantized_kv_amd", "csrc")
+    subprocess.run(["gcc", "-O2", "-mfma", "-ffp-contract=off", "-I", inc, src, "-o", str(exe),
+                    "-lm"], check=True)
+    r = subprocess.run([str(exe), rule], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout
+    assert "quotient_mismatches=0" in r.stdout and "scale_mismatches=0" in r.stdout

@@ -1,0 +1,160 @@
+"""GPU parity of split-K decode attention over the packed cache against the fp64 oracle.
+
+Bar (over the same dequantized values): max abs error <= 2e-3 and relative L2 error
+<= 1e-4 of the fp32 output.  Semantics: bxzpzcl.cn/news/2871434 §3.2 (window, GQA,
+scale), lpnh.cn/news/2042373 §1.1 (append then attend over the whole cache).
+"""
+import numpy as np
+import pytest
+import torch
+
+import int4_quantized_kv_amd as kvq
+import synth
+from oracle import attention, quant
+from tests.kvq_testutil import assert_attn_close, decode, np16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _fill(fmt, k, v, cap, gk=64, gv=128):
+    B, H, S, D = k.shape
+    gk, gv = min(gk, D), min(gv, D)
+    desc = kvq.make_desc(fmt, B, H, D, cap, gk, gv)
+    dc = kvq.DeviceCache(desc, DEV)
+    kvq.kvq_quantize_prefill(desc, dc.c, k, v, 0, S)
+    return desc, dc
+
+
+def _oracle_hat(fmt, k16, v16, gk=64, gv=128):
+    D = k16.shape[-1]
+    gk, gv = min(gk, D), min(gv, D)
+    if fmt == "int4":
+        qk, sk = quant.quantize_int4(k16, gk)
+        qv, sv = quant.quantize_int4(v16, gv)
+        return quant.dequantize_int4_exact(qk, sk, gk), quant.dequantize_int4_exact(qv, sv, gv)
+    qk, sk = quant.quantize_int8(k16)
+    qv, sv = quant.quantize_int8(v16)
+    return quant.dequantize_int8_exact(qk, sk), quant.dequantize_int8_exact(qv, sv)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8"])
+def test_tiny_workload(fmt):
+    w = synth.WORKLOADS[1]
+    k, v, q, _, _ = synth.layer_inputs(w, 0, DEV)
+    desc, dc = _fill(fmt, k, v, w.context)
+    out = decode(desc, dc, q, w.q_heads, [w.context])
+    kh, vh = _oracle_hat(fmt, np16(k), np16(v))
+    ref = attention.decode_attention(np16(q), kh, vh, [w.context])
+    assert_attn_close(out.cpu().numpy(), ref, f"tiny {fmt}")
+
+
+CASES = [
+    # B, Hkv, G, D, lens, window, nsplit
+    (2, 2, 1, 128, [1, 2], 0, 0),
+    (3, 2, 2, 64, [37, 300, 129], 0, 0),
+    (2, 3, 4, 128, [513, 77], 0, 3),
+    (2, 1, 8, 128, [600, 64], 0, 7),
+    (2, 2, 4, 256, [257, 1000], 0, 0),
+    (2, 2, 4, 128, [700, 700], 100, 0),
+    (1, 2, 2, 128, [1000], 999, 5),
+    (2, 2, 4, 128, [50, 1000], 0, 64),     # more splits than positions of sequence 0
+    (4, 1, 1, 64, [5, 17, 33, 65], 16, 0),
+]
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8"])
+@pytest.mark.parametrize("case", CASES, ids=[f"case{i}" for i in range(len(CASES))])
+def test_shapes_lengths_windows_splits(fmt, case):
+    B, Hkv, G, D, lens, window, nsplit = case
+    S = max(lens)
+    k = synth.kv_source((B, Hkv, S, D), 100 + S, DEV, outlier_channels=3)
+    v = synth.kv_source((B, Hkv, S, D), 200 + S, DEV, outlier_channels=3)
+    q = synth.query((B, Hkv * G, D), 300 + S, DEV)
+    desc, dc = _fill(fmt, k, v, S)
+    out = decode(desc, dc, q, Hkv * G, lens, window, 0.0, nsplit)
+    kh, vh = _oracle_hat(fmt, np16(k), np16(v))
+    ref = attention.decode_attention(np16(q), kh, vh, lens, window)
+    assert_attn_close(out.cpu().numpy(), ref, f"{fmt} {case}")
+
+
+def test_split_count_invariance_and_scale():
+    B, Hkv, G, D, S = 2, 2, 4, 128, 2000
+    k = synth.kv_source((B, Hkv, S, D), 5, DEV, outlier_channels=3)
+    v = synth.kv_source((B, Hkv, S, D), 6, DEV, outlier_channels=3)
+    q = synth.query((B, Hkv * G, D), 7, DEV)
+    desc, dc = _fill("int4", k, v, S)
+    kh, vh = _oracle_hat("int4", np16(k), np16(v))
+    for ns in (1, 2, 9, 31, 0):
+        out = decode(desc, dc, q, Hkv * G, [S, 1500], 0, 0.0, ns)
+        ref = attention.decode_attention(np16(q), kh, vh, [S, 1500])
+        assert_attn_close(out.cpu().numpy(), ref, f"nsplit={ns}")
+    out = decode(desc, dc, q, Hkv * G, [S, 1500], 0, 0.25)
+    ref = attention.decode_attention(np16(q), kh, vh, [S, 1500], scale=0.25)
+    assert_attn_close(out.cpu().numpy(), ref, "scale=0.25")
+
+
+def test_ring_window_equals_unwrapped():
+    """A window layer whose ring (capacity W) has wrapped attends exactly like the
+    unwrapped cache restricted to the last W positions."""
+    B, Hkv, G, D, W, L = 2, 2, 2, 128, 256, 1000
+    k = synth.kv_source((B, Hkv, L, D), 8, DEV, outlier_channels=3)
+    v = synth.kv_source((B, Hkv, L, D), 9, DEV, outlier_channels=3)
+    q = synth.query((B, Hkv * G, D), 10, DEV)
+    desc = kvq.make_desc("int4", B, Hkv, D, W)
+    dc = kvq.DeviceCache(desc, DEV)
+    for start in range(0, L, W):        # prefill in W-sized chunks through the ring
+        n = min(W, L - start)
+        kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, start:start + n].contiguous(),
+                                 v[:, :, start:start + n].contiguous(), start, n)
+    out = decode(desc, dc, q, Hkv * G, [L, L], W)
+    kh, vh = _oracle_hat("int4", np16(k), np16(v))
+    ref = attention.decode_attention(np16(q), kh, vh, [L, L], W)
+    assert_attn_close(out.cpu().numpy(), ref, "ring")
+
+
+def test_llama8b_shape_full_layer_with_append():
+    """One full layer of the Llama-3-8B-shaped decode step: prefill 8192 positions,
+    append the new token (position 8192), attend over 8193 with GQA 4:1, batch 8."""
+    w = synth.WORKLOADS[2]
+    layer = 5
+    k, v, q, kn, vn = synth.layer_inputs(w, layer, DEV)
+    desc, dc = _fill("int4", k, v, w.context + 1)
+    kvq.kvq_append(desc, dc.c, kn, vn, [w.context] * w.batch)
+    L = w.context + 1
+    out = decode(desc, dc, q, w.q_heads, [L] * w.batch)
+    kall = np.concatenate([np16(k), np16(kn)[:, :, None]], axis=2)
+    vall = np.concatenate([np16(v), np16(vn)[:, :, None]], axis=2)
+    del k, v
+    kh, vh = _oracle_hat("int4", kall, vall)
+    ref = attention.decode_attention(np16(q), kh, vh, [L] * w.batch)
+    assert_attn_close(out.cpu().numpy(), ref, "llama8b layer")
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8"])
+def test_128k_single_sequence(fmt):
+    """The 128K-context, batch-1 split-K workload (one layer), INT4 and INT8."""
+    w = synth.WORKLOADS[5]
+    k, v, q, _, _ = synth.layer_inputs(w, 0, DEV)
+    desc, dc = _fill(fmt, k, v, w.context)
+    out = decode(desc, dc, q, w.q_heads, [w.context])
+    kn, vn = np16(k), np16(v)
+    del k, v
+    kh, vh = _oracle_hat(fmt, kn, vn)
+    ref = attention.decode_attention(np16(q), kh, vh, [w.context])
+    assert_attn_close(out.cpu().numpy(), ref, f"128k {fmt}")
+
+
+def test_mha7b_shape_sampled_heads():
+    """The MHA-7B-shaped 20K x 8 workload (G = 1): full launch, oracle on sampled
+    (batch, head) pairs."""
+    w = synth.WORKLOADS[3]
+    k, v, q, _, _ = synth.layer_inputs(w, 0, DEV)
+    desc, dc = _fill("int4", k, v, w.context)
+    out = decode(desc, dc, q, w.q_heads, [w.context] * w.batch).cpu().numpy()
+    for (b, h) in [(0, 0), (3, 17), (7, 31)]:
+        kn = k[b:b + 1, h:h + 1].cpu().numpy()
+        vn = v[b:b + 1, h:h + 1].cpu().numpy()
+        kh, vh = _oracle_hat("int4", kn, vn)
+        ref = attention.decode_attention(np16(q[b:b + 1, h:h + 1]), kh, vh, [w.context])
+        assert_attn_close(out[b:b + 1, h:h + 1], ref, f"mha7b b={b} h={h}")
