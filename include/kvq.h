@@ -165,8 +165,8 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
  *          q_heads / Hkv in {1, 2, 4, 8}.
  *   lens: host, [B], 1 <= len_b; positions 0..len_b-1 must be in the cache
  *         (len_b <= C, or window in 1..C when len_b > C; KVQ_ERR_CAPACITY otherwise).
- *   softmax_scale: 0 selects 1/sqrt(D).
- *   num_splits: sequence splits per (b, kv head); 0 = kvq_plan_splits.
+ *   softmax_scale: > 0, or 0 to select 1/sqrt(D); negative values are rejected.
+ *   num_splits: sequence splits per (b, kv head), at most 1024; 0 = kvq_plan_splits.
  *   out: device, [B, q_heads, D] fp32.
  *   workspace: device scratch of at least kvq_decode_workspace_bytes bytes
  *              (KVQ_ERR_WORKSPACE otherwise); its contents are clobbered.

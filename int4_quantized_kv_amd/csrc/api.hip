@@ -117,8 +117,7 @@ size_t kvq_scales_bytes(const kvq_cache_desc* d, int32_t kv) {
 
 int32_t kvq_plan_splits(const kvq_cache_desc* d, int32_t q_heads, int32_t span) {
   if (check_desc(d) != KVQ_OK || q_heads < 1 || q_heads % d->kv_heads || span < 1) return 0;
-  return plan_splits(d->format, d->batch * d->kv_heads, q_heads / d->kv_heads, d->head_dim,
-                     span);
+  return plan_splits(d, q_heads / d->kv_heads, span);
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc* d, int32_t q_heads, int32_t max_len,
@@ -180,7 +179,7 @@ int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache, cons
   const int32_t st = check_desc(desc);
   if (st != KVQ_OK) return st;
   if (!cache_ok(cache) || !q_f16 || !lens || !out || window < 0 || num_splits < 0 ||
-      q_heads < 1 || !std::isfinite(softmax_scale))
+      q_heads < 1 || !std::isfinite(softmax_scale) || softmax_scale < 0.0f)
     return KVQ_ERR_ARG;
   if (q_heads % desc->kv_heads) return KVQ_ERR_ARG;
   const int32_t G = q_heads / desc->kv_heads;
@@ -188,7 +187,7 @@ int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache, cons
   const int32_t span = check_lens(desc, lens, window);
   if (span < 0) return span;
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(desc, q_heads, span);
-  if (ns < 1 || ns > 65535) return KVQ_ERR_ARG;
+  if (ns < 1 || ns > MAX_SPLITS) return KVQ_ERR_ARG;
   const size_t need = (size_t)desc->batch * q_heads * ns * (desc->head_dim + 2) * sizeof(float);
   if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
 

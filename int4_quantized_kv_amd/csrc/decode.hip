@@ -166,23 +166,60 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   }
 }
 
+// Block-wide max / sum for blockDim.x = D threads (1, 2 or 4 waves).
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float v, float* tmp) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float u = __shfl_xor(v, o);
+    v = MAX ? fmaxf(v, u) : v + u;
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) tmp[w] = v;
+  __syncthreads();
+  float r = tmp[0];
+  const int nw = (blockDim.x + 63) >> 6;
+  for (int i = 1; i < nw; ++i) r = MAX ? fmaxf(r, tmp[i]) : r + tmp[i];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup of D threads per (query head, batch): the split maxima and sums are
+// staged in LDS, then thread d accumulates dim d over the splits.
 template <int D, bool CODEC>
 __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
+  __shared__ float s_w[MAX_SPLITS];
+  __shared__ float s_tmp[4];
   __shared__ float sh[D];
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const size_t base = (size_t)(b * a.Hq + h) * a.nsplit;
+  const int ns = a.nsplit;
+  const size_t base = (size_t)(b * a.Hq + h) * ns;
   float M = NEG_INF;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_ml[2 * (base + s)]);
-  float A = 0.0f, L = 0.0f;
-  for (int s = 0; s < a.nsplit; ++s) {
+  for (int s = d; s < ns; s += D) {
     const float ms = a.ws_ml[2 * (base + s)];
-    if (ms != NEG_INF) {
-      const float w = fast_exp2(ms - M);
-      A = __builtin_fmaf(a.ws_acc[(base + s) * D + d], w, A);
-      L = __builtin_fmaf(a.ws_ml[2 * (base + s) + 1], w, L);
-    }
+    s_w[s] = ms;
+    M = fmaxf(M, ms);
   }
-  float o = A / L;
+  M = block_reduce<true>(M, s_tmp);
+  float L = 0.0f;
+  for (int s = d; s < ns; s += D) {
+    const float ms = s_w[s];
+    const float w = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
+    s_w[s] = w;
+    L = __builtin_fmaf(w, a.ws_ml[2 * (base + s) + 1], L);
+  }
+  L = block_reduce<false>(L, s_tmp);   // its barrier also publishes s_w
+  const float* acc = a.ws_acc + base * D + d;
+  float A0 = 0.0f, A1 = 0.0f, A2 = 0.0f, A3 = 0.0f;
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {
+    A0 = __builtin_fmaf(acc[(size_t)s * D], s_w[s], A0);
+    A1 = __builtin_fmaf(acc[(size_t)(s + 1) * D], s_w[s + 1], A1);
+    A2 = __builtin_fmaf(acc[(size_t)(s + 2) * D], s_w[s + 2], A2);
+    A3 = __builtin_fmaf(acc[(size_t)(s + 3) * D], s_w[s + 3], A3);
+  }
+  for (; s < ns; ++s) A0 = __builtin_fmaf(acc[(size_t)s * D], s_w[s], A0);
+  float o = ((A0 + A1) + (A2 + A3)) / L;
   if (CODEC) {
     sh[d] = o;
     __syncthreads();
@@ -201,6 +238,11 @@ template <int D, int FMT>
 hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   hipError_t e;
+  if (FMT == KVQ_INT4_G && mfma_int4_eligible(D, a.gk, a.gv, a.cap, G)) {
+    e = launch_decode_int4_mfma(a, G, s);
+    if (e != hipSuccess) return e;
+    return launch_kernel(merge_kernel<D, false>, dim3(a.Hq, a.B), dim3(D), a, s);
+  }
   switch (G) {
     case 1: e = launch_kernel(decode_splitk_kernel<D, 1, FMT>, grid, dim3(256), a, s); break;
     case 2: e = launch_kernel(decode_splitk_kernel<D, 2, FMT>, grid, dim3(256), a, s); break;
@@ -224,12 +266,12 @@ hipError_t launch_fmt(int32_t format, const DecodeArgs& a, int G, hipStream_t s)
 
 }  // namespace
 
-int32_t plan_splits(int32_t format, int32_t units, int32_t q_group, int32_t head_dim,
-                    int32_t span) {
-  (void)format;
-  (void)q_group;
-  (void)head_dim;
+int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
+  const int32_t units = d->batch * d->kv_heads;
   if (units <= 0 || span <= 0) return 0;
+  if (d->format == KVQ_INT4_G &&
+      mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group))
+    return plan_splits_mfma(units, span);
   const int32_t target = 2048;       // workgroups: 8 per CU on 256 CUs
   const int32_t min_rows = 256;      // positions per split worth a workgroup
   int32_t n = (target + units - 1) / units;

@@ -1,0 +1,547 @@
+// decode_mfma.hip -- split-K decode attention over the packed INT4 cache on the gfx950
+// matrix cores, for head_dim 128, one V scale per row (V group 128), any K group that is
+// a multiple of 32, and GQA groups of 1, 2, 4 or 8 query heads per KV head.
+//
+// Semantics as decode.hip (bxzpzcl.cn/news/2871434 section 3.2; lpnh.cn/news/2042373
+// sections 1.1 and 2.1; in-operator dequantization, pwwt.cn/news/4219524 section 5).
+//
+// Why MFMA: one decode step reads every cached position once; with the G query heads
+// of a KV head sharing that read, q.K and P.V are G x 128 contractions per position.
+// Done with fp32 FMAs they cost ~8 VALU ops per cached byte, above what the vector ALUs
+// sustain at HBM speed (~5 per byte), so both contractions go to v_mfma_f32_16x16x32_f16
+// and the VALU only unpacks nibbles and runs the softmax.
+//
+// Per wave, per tile of 32 positions (two 16-position halves T = 0, 1):
+//   q.K   A = K codes (rows = 16 positions, k = 32 head dims), B = q.  Lane (r, j) =
+//         (lane % 16, lane / 16) holds the 16-byte chunk j (dims 32j .. 32j + 31) of
+//         position r and feeds dword c of it to MFMA c.  The K group scale differs per
+//         group, so the 16 B columns are (query head, K group) pairs: column
+//         head * NGK + g carries q only on the lanes whose dims lie in group g.  Each
+//         column's result is scaled by its group's scale and the NGK adjacent columns
+//         are summed with a lane shuffle: z = sum_g sK[t, g] * (q . codes_g).
+//   P.V   computed transposed: A = V codes (rows = 16 head dims, k = 32 positions),
+//         B = P (k = positions, columns = heads).  Lane (r, j) loads dword r of the 8
+//         positions {4j..4j+3, 16+4j..16+4j+3} whose scores it already holds from q.K, so
+//         P needs no data movement.  MFMA e (e = 0..7) covers dims {8r + e}.  The V row
+//         scale is folded into P (p' = p * sV[t]); p' is split into fp16 hi + lo and both
+//         go through the MFMA, so P.V keeps ~22 bits (fp16 P alone would lose ~1e-4).
+// Nibbles become fp16 exactly: flipping bit 3 turns a two's complement nibble into
+// u = q + 8, (u | 0x6400) is the fp16 1024 + u, and a packed subtract of 1032 leaves q;
+// the first two steps are one v_bitop3 per nibble pair.
+// The online softmax keeps the running maximum of the unscaled scores and forms
+// p = 2^(s * (z - m)) with s = softmax scale * log2 e (one fma + exp per score); it
+// rescales the accumulators only when some head's running maximum grows.
+// The four waves of a workgroup take interleaved tiles of the split and merge their
+// (max, sum, weighted V) through LDS; the merge kernel of decode.hip combines splits.
+// Tiles are staged through LDS by direct global->LDS transfers (see "LDS staging").
+#include <cmath>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr int HD = 128;     // head_dim of this kernel
+constexpr int TILE = 32;    // positions per wave iteration
+constexpr int WAVES = 4;
+
+union H8 {
+  half8 h;
+  uint32_t u[4];
+};
+
+// fp16 pair (1024 + a, 1024 + b) -> (a - 8, b - 8), exact.
+__device__ __forceinline__ uint32_t sub1032(uint32_t x) {
+  f16x2 v = __builtin_bit_cast(f16x2, x);
+  const f16x2 k = {(_Float16)1032.0f, (_Float16)1032.0f};
+  v = v - k;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Nibble pair -> fp16 pair: for x holding two's-complement nibbles at bits 0..3 and
+// 16..19, (x & 0x000F000F) ^ 0x64086408 flips the nibble sign bit (u = q + 8) and sets
+// the fp16 exponent of 1024, i.e. the fp16 pair (1024 + u, 1024 + u'); one v_bitop3.
+// The immediate is the truth table f(0xF0, 0xCC, 0xAA) of f(a, b, c) = (a & b) ^ c.
+__device__ __forceinline__ uint32_t nib_pair_f16(uint32_t x) {
+  return sub1032(__builtin_amdgcn_bitop3_b32(x, 0x000F000Fu, 0x64086408u, 0x6A));
+}
+
+// Eight two's-complement nibbles of `w` as an MFMA operand holding u * 2^-24 (u = q + 8,
+// fp16 subnormals, which the matrix cores take exactly): slot 2p = nibble p, slot
+// 2p + 1 = nibble p + 4.  One v_bitop3 (mask, then flip the sign bit) per pair; the
+// + 8 offset is removed after the MFMA: sum q_k (u_k - 8) = 2^24 C - 8 sum q_k.
+__device__ __forceinline__ half8 unpack_word_u(uint32_t w) {
+  H8 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    r.u[p] = __builtin_amdgcn_bitop3_b32(w >> (4 * p), 0x000F000Fu, 0x00080008u, 0x6A);
+  return r.h;
+}
+
+// Max / sum over the 4 lanes j (lane, lane ^ 16, lane ^ 32, lane ^ 48) that share a
+// column, with the gfx950 row-swap permutes (VALU, no LDS round trip).  Swapping a
+// register with a copy of itself leaves [r0, r0, r2, r2] / [r1, r1, r3, r3] (16-lane
+// rows) for v_permlane16_swap and [r0, r1, r0, r1] / [r2, r3, r2, r3] for
+// v_permlane32_swap.  The swaps are written as inline assembly with both registers
+// read-write (the compiler builtin returns its first result for both elements of the
+// pair); the s_nop covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_over_j(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap16(a, b);
+  uint32_t c = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, a),
+                                                  __builtin_bit_cast(float, b)));
+  uint32_t d = c;
+  swap32(c, d);
+  return fmaxf(__builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
+}
+__device__ __forceinline__ float sum_over_j(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap16(a, b);
+  uint32_t c = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) +
+                                                __builtin_bit_cast(float, b));
+  uint32_t d = c;
+  swap32(c, d);
+  return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
+}
+// x + x[lane ^ 1] / x[lane ^ 2] within quads (DPP, one VALU op each).
+__device__ __forceinline__ float add_xor1(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                 0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float add_xor2(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                 0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+}
+
+typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef __attribute__((address_space(1))) void* gbl_vptr;
+
+// ---------------------------------------------------------------------------------------
+// LDS staging.  Each wave owns a ring of NB tile slots and keeps NB - 1 tiles in flight:
+// tiles arrive by global_load_lds (HBM -> LDS without passing through VGPRs), so the
+// prefetch depth does not cost registers.  The compiler does not track these transfers,
+// so the pipeline waits on them explicitly with s_waitcnt vmcnt (every tile issues the
+// same number of transfers, and no other vector-memory load is issued inside the loop).
+//
+// Slot layout (bytes): K codes [0, 2048), V codes [2048, 4096), K scales [4096, +SKB),
+// V scales [.., +256).  A 16-row half of K or V is 1 KB: LDS row position P holds tile
+// row rowperm(P) of the half, and its 16-byte chunk slot S holds chunk S ^ f(P).  The
+// row permutation and the chunk swizzle make the q.K reads (lane (r, j): chunk j of row
+// r, ds_read_b128) and the P.V reads (lane (r, j): dword r of row 4j + i, ds_read_b32)
+// free of bank conflicts for 32- and for 64-bank LDS.  K scales are stored group-major
+// ([g][32 rows]) so a lane reads its 4 rows of its group with one ds_read_b128.
+constexpr int NB = 3;
+
+__device__ __forceinline__ int rowinv(int rho) { return 4 * (rho >> 2) + ((rho + (rho >> 2)) & 3); }
+__device__ __forceinline__ int rowperm(int P) { return 4 * (P >> 2) + (((P & 3) - (P >> 2)) & 3); }
+__device__ __forceinline__ int chunk_swz(int P) { return ((P >> 1) ^ (P >> 3)) & 3; }
+
+template <int NGK>
+struct Slot {
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 2048;
+  static constexpr int SK_OFF = 4096;
+  static constexpr int SK_BYTES = NGK <= 2 ? 256 : 512;
+  static constexpr int SV_OFF = SK_OFF + SK_BYTES;
+  static constexpr int BYTES = SV_OFF + 256;
+  static constexpr int DMA = 4 + (NGK <= 2 ? 1 : 2) + 1;   // transfers per tile
+};
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds((gbl_vptr)g, (lds_vptr)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds((gbl_vptr)g, (lds_vptr)l, 4, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Per-lane byte offsets of the transfers, fixed for the whole kernel: lane l fills LDS
+// row position P = l / 4, chunk slot l % 4 with chunk (l % 4) ^ f(P) of tile row
+// rowperm(P) (+16 for the second half); scale transfers take row l % 32.
+struct DmaOffs {
+  int kv[2];    // K / V codes, half T: row (16T + rowperm(P)) * 64 + 16 * chunk
+  int rho[2];   // the tile rows behind kv[T] (for the clamped path)
+  int kap16;    // 16 * chunk
+  int sk[2];    // K scale h: (l % 32) * NGK * 4 + g * 4
+  int sv;       // V scale: (l % 32) * 4
+};
+
+template <int NGK>
+__device__ __forceinline__ DmaOffs dma_offsets(int lane) {
+  DmaOffs o;
+  const int P = lane >> 2;
+  o.kap16 = 16 * ((lane & 3) ^ chunk_swz(P));
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    o.rho[T] = 16 * T + rowperm(P);
+    o.kv[T] = o.rho[T] * (HD / 2) + o.kap16;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) o.sk[h] = ((lane & 31) * NGK + min((lane >> 5) + 2 * h, NGK - 1)) * 4;
+  o.sv = (lane & 31) * 4;
+  return o;
+}
+
+// Issue the transfers of tile t0 (positions t0 .. t0 + 31 of a split ending at pe) into
+// the LDS slot `lb`.  A full tile whose 32 slots are contiguous is addressed from one
+// scalar base row plus the fixed lane offsets; otherwise each row is clamped to pe - 1
+// (masked positions read a valid row) and wrapped around the ring.
+template <int NGK>
+__device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int t0, int pe,
+                                           uint8_t* lb, int lane, const DmaOffs& o) {
+  using L = Slot<NGK>;
+  const int cap = a.cap;
+  const int sbase = t0 % cap;
+  const uint8_t* kc = static_cast<const uint8_t*>(a.k_codes);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.v_codes);
+  const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k_scales);
+  const uint8_t* vs = reinterpret_cast<const uint8_t*>(a.v_scales);
+  if (t0 + TILE <= pe && sbase + TILE <= cap) {
+    const size_t rb = row0 + (size_t)sbase;
+    const uint8_t* kb = kc + rb * (HD / 2);
+    const uint8_t* vb = vc + rb * (HD / 2);
+    const uint8_t* ksb = ks + rb * (NGK * 4);
+    const uint8_t* vsb = vs + rb * 4;
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      dma16(kb + o.kv[T], lb + L::K_OFF + 1024 * T);
+      dma16(vb + o.kv[T], lb + L::V_OFF + 1024 * T);
+    }
+#pragma unroll
+    for (int h = 0; h < (NGK <= 2 ? 1 : 2); ++h) dma4(ksb + o.sk[h], lb + L::SK_OFF + 256 * h);
+    dma4(vsb + o.sv, lb + L::SV_OFF);
+    return;
+  }
+  auto row_of = [&](int rho) -> size_t {
+    int off = rho;
+    if (t0 + off > pe - 1) off = pe - 1 - t0;
+    int sl = sbase + off;
+    if (sl >= cap) sl -= cap;
+    return row0 + (size_t)sl;
+  };
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    const size_t row = row_of(o.rho[T]);
+    dma16(kc + row * (HD / 2) + o.kap16, lb + L::K_OFF + 1024 * T);
+    dma16(vc + row * (HD / 2) + o.kap16, lb + L::V_OFF + 1024 * T);
+  }
+  const size_t srow = row_of(lane & 31);
+#pragma unroll
+  for (int h = 0; h < (NGK <= 2 ? 1 : 2); ++h)
+    dma4(ks + srow * (NGK * 4) + (o.sk[h] - (lane & 31) * NGK * 4), lb + L::SK_OFF + 256 * h);
+  dma4(vs + srow * 4, lb + L::SV_OFF);
+}
+
+// Online-softmax state of one wave (per lane: query head of column r).
+struct State {
+  floatx4 oacc[8];
+  float m, l;
+};
+
+// Per-lane LDS offsets, fixed for the whole kernel.
+struct LaneOffs {
+  int k;        // q.K: chunk j of row r (half 0)
+  int v[4];     // P.V: dword r of row 4j + i (half 0)
+  int sk;       // K scales of group g, rows 4j .. 4j+3 (half 0)
+  int sv;       // V scales, rows 4j .. 4j+3 (half 0)
+};
+
+// State::m is the running maximum of the unscaled scores z = q . k; since the scale
+// (softmax scale * log2 e) is positive, p = 2^(scale * (z - m)).
+template <int G, int NGK, bool MASK>
+__device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& lo, State& st,
+                                             const half8 (&qb)[4], float qbias, int t0, int pe,
+                                             int j, float qscale) {
+  using L = Slot<NGK>;
+  // ---- q.K: lane (r, j) gets rows 4j + i of half T for column r = (head, group)
+  float z[2][4];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    const uint4 kw = *reinterpret_cast<const uint4*>(lb + L::K_OFF + 1024 * T + lo.k);
+    const f4u sk = *reinterpret_cast<const f4u*>(lb + L::SK_OFF + 64 * T + lo.sk);
+    const uint32_t kw4[4] = {kw.x, kw.y, kw.z, kw.w};
+    floatx4 cg = (floatx4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_word_u(kw4[c]), qb[c], cg, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // q . codes_g = 2^24 C - 8 sum_g(q); then the group scale
+      float s = __builtin_fmaf(cg[i], 16777216.0f, qbias) * sk[i];
+      // the NGK columns of a head are adjacent (column = head * NGK + group)
+      if (NGK >= 2) s = add_xor1(s);
+      if (NGK >= 4) s = add_xor2(s);
+      if (MASK) s = t0 + 16 * T + 4 * j + i < pe ? s : NEG_INF;
+      z[T][i] = s;
+    }
+  }
+
+  // ---- online softmax (the 4 lanes j of a column share a head)
+  float mx = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                   fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+  mx = max_over_j(mx);
+  const float m_new = fmaxf(st.m, mx);
+  if (__any(m_new > st.m)) {
+    const float corr = fast_exp2((st.m - m_new) * qscale);
+    st.l *= corr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.oacc[e] *= corr;
+    st.m = m_new;
+  }
+  const float mq = st.m * qscale;
+
+  // ---- P' = P * sV as fp16 hi + lo, in the B layout (k = 4T + i)
+  H8 phi, plo;
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    const f4u sv = *reinterpret_cast<const f4u*>(lb + L::SV_OFF + 64 * T + lo.sv);
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      const float p0 = fast_exp2(__builtin_fmaf(z[T][i], qscale, -mq));
+      const float p1 = fast_exp2(__builtin_fmaf(z[T][i + 1], qscale, -mq));
+      st.l += p0 + p1;
+      const float q0 = p0 * sv[i];
+      const float q1 = p1 * sv[i + 1];
+      const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(q0, q1));
+      const float r0 = __builtin_fmaf((float)h.x, -1.0f, q0);
+      const float r1 = __builtin_fmaf((float)h.y, -1.0f, q1);
+      phi.u[2 * T + i / 2] = __builtin_bit_cast(uint32_t, h);
+      plo.u[2 * T + i / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    }
+  }
+
+  // ---- P.V: byte halves of two rows' dwords give the (row, row + 1) pairs of 4 dims
+  uint32_t xlo[4], xhi[4];
+#pragma unroll
+  for (int pr = 0; pr < 4; ++pr) {
+    const int T = pr >> 1, i = 2 * (pr & 1);
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(lb + L::V_OFF + 1024 * T + lo.v[i]);
+    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(lb + L::V_OFF + 1024 * T + lo.v[i + 1]);
+    xlo[pr] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);   // w0.b0 w0.b1 w1.b0 w1.b1
+    xhi[pr] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);   // w0.b2 w0.b3 w1.b2 w1.b3
+  }
+  // V codes as exact fp16 (q, via the 1024 bias and a packed subtract): the matrix
+  // cores do not keep full fp32 precision when adding a 32-term dot product whose terms
+  // carry a common +8 offset, so V (unlike K) is not fed as biased subnormals.
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    H8 va;
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      const uint32_t x = e < 4 ? xlo[pr] : xhi[pr];
+      va.u[pr] = nib_pair_f16(x >> (4 * (e & 3)));
+    }
+    st.oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, phi.h, st.oacc[e], 0, 0, 0);
+    st.oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, plo.h, st.oacc[e], 0, 0, 0);
+  }
+}
+
+template <int G, int NGK>
+__global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
+  using L = Slot<NGK>;
+  constexpr int DMA = L::DMA;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[WAVES * NB * L::BYTES];
+
+  const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform: keeps tile positions, ring addresses and base pointers in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  // q.K column r = (head r / NGK, group r % NGK); junk columns beyond G * NGK
+  const int qhead = (r / NGK) % G;
+  const int qgrp = r % NGK;
+  const int len = a.lens[b];
+  const int lo_pos = a.window > 0 ? max(0, len - a.window) : 0;
+  const int span = len - lo_pos;
+  const int chunk = (span + a.nsplit - 1) / a.nsplit;
+  const int ps = min(len, lo_pos + sp * chunk);
+  const int pe = min(len, ps + chunk);
+
+  // q as the B operand of dim chunk c: lane quarter j holds dims 8(4j + c) + {p, p + 4}
+  // in slots {2p, 2p + 1} (the order unpack_word produces) when quarter j lies in the
+  // column's K group, zeros otherwise; q is pre-scaled by scale * log2 e in fp32 later.
+  half8 qb[4];
+  {
+    constexpr int QPG = 4 / NGK;   // lane quarters (32 dims) per K group
+    const bool live = r < G * NGK && j / QPG == qgrp;
+    const uint16_t* qh = a.q + (size_t)(b * a.Hq + kvh * G + qhead) * HD;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qh + 8 * (4 * j + c));
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      H8 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        // element p is half (p&1) of word p/2; element p+4 is half (p&1) of word 2+p/2
+        const uint32_t lo16 = (w[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
+        const uint32_t hi16 = (w[2 + (p >> 1)] >> (16 * (p & 1))) & 0xFFFFu;
+        o.u[p] = live ? (lo16 | (hi16 << 16)) : 0u;
+      }
+      qb[c] = o.h;
+    }
+  }
+  // -8 * (sum of the q entries this column carries), summed over the 4 lanes j
+  float qbias;
+  {
+    float qs = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      H8 o;
+      o.h = qb[c];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const f16x2 h2 = __builtin_bit_cast(f16x2, o.u[p]);
+        qs += (float)h2.x + (float)h2.y;
+      }
+    }
+    qbias = -8.0f * sum_over_j(qs);
+  }
+
+  LaneOffs lo;
+  {
+    const int P = rowinv(r);
+    lo.k = P * 64 + 16 * (j ^ chunk_swz(P));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int Pv = rowinv(4 * j + i);
+      lo.v[i] = Pv * 64 + 16 * ((r >> 2) ^ chunk_swz(Pv)) + 4 * (r & 3);
+    }
+    lo.sk = (min(qgrp, NGK - 1) * 32 + 4 * j) * 4;
+    lo.sv = 4 * j * 4;
+  }
+
+  State st;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st.oacc[e] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  st.m = NEG_INF;
+  st.l = 0.0f;
+
+  const size_t row0 = ((size_t)b * a.Hkv + kvh) * a.cap;
+  constexpr int STRIDE = TILE * WAVES;
+  const int tfirst = ps + TILE * wave;
+  const int ntiles = tfirst < pe ? (pe - tfirst + STRIDE - 1) / STRIDE : 0;
+  uint8_t* ring = smem + wave * NB * L::BYTES;
+  const DmaOffs dof = dma_offsets<NGK>(lane);
+  if (ntiles > 0) issue_tile<NGK>(a, row0, tfirst, pe, ring, lane, dof);
+  if (ntiles > 1) issue_tile<NGK>(a, row0, tfirst + STRIDE, pe, ring + L::BYTES, lane, dof);
+  for (int k = 0; k < ntiles; ++k) {
+    const int t0 = tfirst + k * STRIDE;
+    if (k + 2 < ntiles) {
+      issue_tile<NGK>(a, row0, t0 + 2 * STRIDE, pe, ring + ((k + 2) % NB) * L::BYTES, lane, dof);
+      wait_vmcnt<2 * DMA>();
+    } else if (k + 1 < ntiles) {
+      wait_vmcnt<DMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    const uint8_t* lb = ring + (k % NB) * L::BYTES;
+    if (t0 + TILE <= pe)
+      process_tile<G, NGK, false>(lb, lo, st, qb, qbias, t0, pe, j, a.qscale);
+    else
+      process_tile<G, NGK, true>(lb, lo, st, qb, qbias, t0, pe, j, a.qscale);
+  }
+
+  // ---- combine the 4 waves through LDS (reusing the ring): lane (r, j) holds
+  // O[column r][8(4j + i) + e] in oacc[e][i]; the head's value sits in column head * NGK.
+  __syncthreads();
+  float* s_o = reinterpret_cast<float*>(smem);                 // [WAVES][G][HD]
+  float* s_m = s_o + WAVES * G * HD;                            // [WAVES][G]
+  float* s_l = s_m + WAVES * G;                                 // [WAVES][G]
+  const float l_run = sum_over_j(st.l);
+  if (r < G * NGK && qgrp == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s_o[(wave * G + qhead) * HD + 8 * (4 * j + i) + e] = st.oacc[e][i];
+    if (j == 0) {
+      s_m[wave * G + qhead] = st.m * a.qscale;   // base-2 units, as the merge expects
+      s_l[wave * G + qhead] = l_run;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
+    const int h = idx / HD, d = idx % HD;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w * G + h]);
+    float Acc = 0.0f, Lsum = 0.0f;
+    if (M != NEG_INF) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float mw = s_m[w * G + h];
+        if (mw != NEG_INF) {
+          const float f = fast_exp2(mw - M);
+          Acc = __builtin_fmaf(s_o[(w * G + h) * HD + d], f, Acc);
+          Lsum = __builtin_fmaf(s_l[w * G + h], f, Lsum);
+        }
+      }
+    }
+    const size_t o = (size_t)(b * a.Hq + kvh * G + h) * a.nsplit + sp;
+    a.ws_acc[o * HD + d] = Acc;
+    if (d == 0) {
+      a.ws_ml[2 * o] = M;
+      a.ws_ml[2 * o + 1] = Lsum;
+    }
+  }
+}
+
+template <int G>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.nsplit, a.Hkv, a.B);
+  switch (HD / a.gk) {
+    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1>, grid, dim3(256), a, s);
+    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2>, grid, dim3(256), a, s);
+    case 4:
+      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4>, grid, dim3(256), a, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool mfma_int4_eligible(int32_t head_dim, int32_t group_k, int32_t group_v, int32_t cap,
+                        int32_t q_group) {
+  if (head_dim != HD || group_v != HD || group_k < 32 || group_k > HD || cap < TILE) return false;
+  if (q_group != 1 && q_group != 2 && q_group != 4 && q_group != 8) return false;
+  return q_group * (HD / group_k) <= 16;   // (K group, head) pairs fit the 16 MFMA columns
+}
+
+int32_t plan_splits_mfma(int32_t units, int32_t span) {
+  const int32_t target_wg = 512;        // x 4 waves = 8 waves per CU on 256 CUs
+  const int32_t min_rows = 512;         // >= 4 tiles per wave
+  int32_t n = (target_wg + units - 1) / units;
+  const int32_t by_span = (span + min_rows - 1) / min_rows;
+  if (n > by_span) n = by_span;
+  if (n > 1024) n = 1024;
+  return n < 1 ? 1 : n;
+}
+
+hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
+  switch (q_group) {
+    case 1: return launch_g<1>(a, s);
+    case 2: return launch_g<2>(a, s);
+    case 4: return launch_g<4>(a, s);
+    case 8: return launch_g<8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

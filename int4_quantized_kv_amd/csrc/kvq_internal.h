@@ -62,10 +62,20 @@ hipError_t launch_codec_encode(const QuantArgs& a, hipStream_t s);
 hipError_t launch_codec_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_decode(int32_t format, const DecodeArgs& a, int32_t q_group, hipStream_t s);
 
-// Split plan of the decode kernels for `units` (b, kv head) pairs and a longest
-// attended span of `span` positions.
-int32_t plan_splits(int32_t format, int32_t units, int32_t q_group, int32_t head_dim,
-                    int32_t span);
+// Split plan of the decode kernels for the cache `d`, `q_group` query heads per KV
+// head and a longest attended span of `span` positions (the kernel that will run
+// decides the plan, so the workspace query and the launch always agree).
+int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span);
+
+// The INT4 matrix-core kernel (decode_mfma.hip) and when it applies.
+bool mfma_int4_eligible(int32_t head_dim, int32_t group_k, int32_t group_v, int32_t cap,
+                        int32_t q_group);
+int32_t plan_splits_mfma(int32_t units, int32_t span);
+hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
+
+// Largest split count a decode call accepts (the merge kernel keeps one weight per
+// split in LDS).
+constexpr int32_t MAX_SPLITS = 1024;
 
 // The library's own 4-bit Lloyd-Max codebook of N(0,1) (computed once, then constant).
 void codec_codebook(float levels[16], float thresholds[15]);

@@ -158,3 +158,59 @@ def test_mha7b_shape_sampled_heads():
         kh, vh = _oracle_hat("int4", kn, vn)
         ref = attention.decode_attention(np16(q[b:b + 1, h:h + 1]), kh, vh, [w.context])
         assert_attn_close(out[b:b + 1, h:h + 1], ref, f"mha7b b={b} h={h}")
+
+
+MFMA_CASES = [
+    # gk, G, lens, window, cap    (head_dim 128, V group 128: the matrix-core kernel)
+    (32, 1, [33, 1000], 0, None),
+    (64, 2, [511, 97], 0, None),
+    (128, 4, [700, 1], 0, None),
+    (32, 8, [1025, 640], 0, None),
+    (64, 4, [1500, 1500], 300, 512),    # window ring, capacity 512 (wraps)
+    (128, 8, [2049, 40], 0, None),
+]
+
+
+@pytest.mark.parametrize("case", MFMA_CASES, ids=[f"mfma{i}" for i in range(len(MFMA_CASES))])
+def test_int4_matrix_core_path(case):
+    gk, G, lens, window, cap = case
+    B, Hkv, D = len(lens), 2, 128
+    S = max(lens)
+    k = synth.kv_source((B, Hkv, S, D), 400 + gk + G, DEV, outlier_channels=3)
+    v = synth.kv_source((B, Hkv, S, D), 500 + gk + G, DEV, outlier_channels=3,
+                        zero_groups=((0, 1, 0, 0, D),))
+    q = synth.query((B, Hkv * G, D), 600 + gk + G, DEV)
+    C = cap or S
+    desc = kvq.make_desc("int4", B, Hkv, D, C, gk, 128)
+    dc = kvq.DeviceCache(desc, DEV)
+    for start in range(0, S, C):
+        n = min(C, S - start)
+        kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, start:start + n].contiguous(),
+                                 v[:, :, start:start + n].contiguous(), start, n)
+    for ns in (0, 1, 5):
+        out = decode(desc, dc, q, Hkv * G, lens, window, 0.0, ns)
+        kh, vh = _oracle_hat("int4", np16(k), np16(v), gk, 128)
+        ref = attention.decode_attention(np16(q), kh, vh, lens, window)
+        assert_attn_close(out.cpu().numpy(), ref, f"mfma {case} nsplit={ns}")
+
+
+@pytest.mark.parametrize("gv,cap", [(64, None), (128, 16)])
+def test_int4_generic_fallback(gv, cap):
+    """INT4 shapes the matrix-core kernel does not take (V group < head_dim, capacity
+    below one tile) run on the generic kernel."""
+    B, Hkv, G, D, L = 2, 2, 4, 128, 300
+    k = synth.kv_source((B, Hkv, L, D), 71, DEV, outlier_channels=3)
+    v = synth.kv_source((B, Hkv, L, D), 72, DEV, outlier_channels=3)
+    q = synth.query((B, Hkv * G, D), 73, DEV)
+    C = cap or L
+    desc = kvq.make_desc("int4", B, Hkv, D, C, 64, gv)
+    dc = kvq.DeviceCache(desc, DEV)
+    for start in range(0, L, C):
+        n = min(C, L - start)
+        kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, start:start + n].contiguous(),
+                                 v[:, :, start:start + n].contiguous(), start, n)
+    W = C if cap else 0
+    out = decode(desc, dc, q, Hkv * G, [L, L], W)
+    kh, vh = _oracle_hat("int4", np16(k), np16(v), 64, gv)
+    ref = attention.decode_attention(np16(q), kh, vh, [L, L], W)
+    assert_attn_close(out.cpu().numpy(), ref, f"generic gv={gv} cap={cap}")
