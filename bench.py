@@ -3,11 +3,12 @@
 
 Workload (the headline): Llama-3-8B-shaped decode, 32 layers, 32 query heads over 8 KV
 heads (GQA 4:1), head_dim 128, batch 8, 8192 cached positions per sequence.  One step =
-for every layer: kvq_append (quantize the new token's K/V into slot 8192) then
-kvq_decode_attn over the 8193 positions (split-K kernel + merge kernel).  The 32 layers
-have distinct caches (2.36 GB of packed K/V in total), so the 256 MB Infinity Cache
-cannot serve a step.  Inputs are seeded synthetic fp16 N(0,1) K/V with 3 of 128
-channels x20 (synth.py), quantized into the caches before timing.
+for every layer, kvq_append_decode_attn: quantize the new token's K/V into slot 8192 and
+attend over the 8193 positions (one kernel per layer on this shape; --unfused runs
+kvq_append then kvq_decode_attn instead).  The 32 layers have distinct caches (2.36 GB
+of packed K/V in total), so the 256 MB Infinity Cache cannot serve a step.  Inputs are
+seeded synthetic fp16 N(0,1) K/V with 3 of 128 channels x20 (synth.py), quantized into
+the caches before timing.
 
 Prints ONE JSON line: effective KV GB/s (algorithmic bytes per step / step time), the
 roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
@@ -32,9 +33,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=None, help="override the layer count (debug only)")
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    p.add_argument("--unfused", action="store_true",
+                   help="kvq_append + kvq_decode_attn per layer instead of kvq_append_decode_attn")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-units", type=int, default=8,
-                   help="(batch, kv head) units of one layer the CPU oracle is timed on")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="timed CPU work of the oracle baseline (whole (batch, kv head) units)")
     return p.parse_args()
 
 
@@ -77,14 +80,21 @@ def main():
 
     lens = (ctypes.c_int32 * B)(*([L] * B))
     pos = (ctypes.c_int32 * B)(*([S] * B))
-    ws_bytes = kvq.kvq_decode_workspace_bytes(desc, Hq, L)
-    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=dev)
+    ws = kvq.decode_workspace(desc, Hq, L, device=dev)
+    ws_bytes = ws.numel() * 4
     nsplit = kvq.kvq_plan_splits(desc, Hq, L)
     LIB = kvq.LIB
 
     def step(stream, append=True, attend=True):
         sp = ctypes.c_void_p(stream)
         for lay in layers:
+            if not args.unfused:
+                st = LIB.kvq_append_decode_attn(dref, lay.cref, lay.kn.data_ptr(), lay.vn.data_ptr(),
+                                                lay.q.data_ptr(), Hq, lens, 0, 0.0, 0,
+                                                lay.out.data_ptr(), ws.data_ptr(), ws_bytes, sp)
+                if st:
+                    raise kvq.KvqError(st, "kvq_append_decode_attn")
+                continue
             if append:
                 st = LIB.kvq_append(dref, lay.cref, lay.kn.data_ptr(), lay.vn.data_ptr(), pos, sp)
                 if st:
@@ -122,7 +132,8 @@ def main():
         if not torch.equal(layers[-1].out, eager_out):
             raise RuntimeError("graph replay differs from the eager result")
 
-    # ---- timed region: exactly K steps, synchronized on both sides
+    # ---- timed region: exactly K steps, synchronized on both sides; the events are
+    # recorded on the stream the kernels run on (the graph replays on the current stream)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -135,33 +146,41 @@ def main():
     wall_s = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- dominant kernel: kvq_decode_attn alone (split-K + merge), all layers, graph
-    if args.eager:
-        attn_run = lambda: step(torch.cuda.current_stream().cuda_stream, append=False)  # noqa: E731
-    else:
-        g_attn = capture(append=False)
-        attn_run = g_attn.replay
-    attn_run()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
+    if args.unfused:
+        # dominant kernel: kvq_decode_attn alone, all layers, timed in its own pass
+        if args.eager:
+            attn_run = lambda: step(torch.cuda.current_stream().cuda_stream, append=False)  # noqa: E731
+        else:
+            g_attn = capture(append=False)
+            attn_run = g_attn.replay
         attn_run()
-    e1.record()
-    torch.cuda.synchronize()
-    attn_ms = e0.elapsed_time(e1) / (args.steps * nl)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            attn_run()
+        e1.record()
+        torch.cuda.synchronize()
+        kern_ms = e0.elapsed_time(e1) / (args.steps * nl)
+        kern_name = "kvq_decode_attn (decode_int4_mfma_kernel, splits merged in-kernel)"
+    else:
+        # one kernel per layer: the timed region is that kernel's launches back to back
+        kern_ms = ms_step / nl
+        kern_name = "kvq_append_decode_attn (decode_int4_mfma_kernel with the append fused)"
 
-    # ---- algorithmic bytes
+    # ---- algorithmic bytes of one layer's step: read the 8192 cached rows, write the
+    # new row (codes + scales), read its fp16 K/V, read q, write the fp32 output
     row_bytes = (D // 2 + 4 * (D // w.group_k)) + (D // 2 + 4 * (D // w.group_v))  # K + V, 140 B
-    cache_read = B * Hkv * L * row_bytes
-    q_bytes = B * Hq * D * 2
-    out_bytes = B * Hq * D * 4
-    append_bytes = B * Hkv * D * 2 * 2 + B * Hkv * row_bytes
-    attn_bytes = cache_read + q_bytes + out_bytes
-    step_bytes = nl * (attn_bytes + append_bytes)
+    layer_bytes = (B * Hkv * S * row_bytes + B * Hkv * row_bytes + B * Hkv * D * 2 * 2
+                   + B * Hq * D * 2 + B * Hq * D * 4)
+    step_bytes = nl * layer_bytes
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    attn_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
+    if args.unfused:   # the attention kernel alone also reads the appended row back
+        kern_bytes = B * Hkv * L * row_bytes + B * Hq * D * 2 + B * Hq * D * 4
+    else:
+        kern_bytes = layer_bytes
+    kern_gbs = kern_bytes / (kern_ms * 1e-3) / 1e9
 
     result = {
         "metric": "INT4-KV decode attn: effective KV GB/s, % HBM peak, tok/s (8B-shape, 8K ctx)",
@@ -178,70 +197,77 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "layers": nl, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "context": L, "format": "int4 K g64 / V g128, fp32 scales",
-                   "launch": "eager" if args.eager else "hip-graph", "num_splits": nsplit},
+                   "launch": "eager" if args.eager else "hip-graph", "num_splits": nsplit,
+                   "entry": "kvq_append + kvq_decode_attn" if args.unfused else "kvq_append_decode_attn"},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tok_per_s": round(B / (ms_step * 1e-3), 1),
         "bytes_per_step": step_bytes,
         "wall_s_timed": round(wall_s, 4),
         "roofline": {
-            "kernel": "kvq_decode_attn (decode_splitk_kernel + merge_kernel)",
+            "kernel": kern_name,
             "bound": "hbm",
-            "achieved": round(attn_gbs, 1),
+            "achieved": round(kern_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "bytes_per_launch": attn_bytes,
-            "avg_launch_us": round(attn_ms * 1e3, 2),
+            "bytes_per_launch": kern_bytes,
+            "avg_launch_us": round(kern_ms * 1e3, 2),
         },
         "cpu_baseline": None,
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, layers[0], desc, args.cpu_units, L)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, L)
 
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, lay, desc, units, L):
-    """The oracle (never tuned) timed on host cores for `units` (batch, kv head) pairs of
-    one layer's decode step: quantize the new row, dequantize the cache exactly, fp64
-    softmax attention for the pair's G query heads.  Single-threaded BLAS."""
+def cpu_baseline(w, seconds, L):
+    """The oracle (never tuned) timed on host cores, one (batch, kv head) unit of a layer
+    at a time, layer after layer, until `seconds` of timed work: quantize the new row,
+    dequantize the cache exactly, fp64 softmax attention for the unit's G query heads.
+    The cache state a unit starts from (the prefill) is built outside the timer.
+    Single-threaded BLAS."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import synth
     from oracle import attention, quant
 
-    S = w.context
     G = w.q_heads // w.kv_heads
-    k, v, q, kn, vn = synth.layer_inputs(w, 0, "cuda:0")
-    pairs = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)][:units]
-    kk = [k[b, h].cpu().numpy() for b, h in pairs]
-    vv = [v[b, h].cpu().numpy() for b, h in pairs]
-    qq = [q[b, h * G:(h + 1) * G].cpu().numpy() for b, h in pairs]
-    kr = [kn[b, h].cpu().numpy() for b, h in pairs]
-    vr = [vn[b, h].cpu().numpy() for b, h in pairs]
-    del k, v
-    # the cache state the step starts from (prefill, not timed)
-    pre = [(quant.quantize_int4(a, 64), quant.quantize_int4(b_, 128)) for a, b_ in zip(kk, vv)]
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        for i in range(len(pairs)):
-            (ck, sk), (cv, sv) = pre[i]
-            nk, nsk = quant.quantize_int4(kr[i][None], 64)         # append the new row
-            nv, nsv = quant.quantize_int4(vr[i][None], 128)
-            ck = np.concatenate([ck, nk]); sk = np.concatenate([sk, nsk])
-            cv = np.concatenate([cv, nv]); sv = np.concatenate([sv, nsv])
-            kh = quant.dequantize_int4_exact(ck, sk, 64)
-            vh = quant.dequantize_int4_exact(cv, sv, 128)
-            attention.decode_attention(qq[i][None], kh[None, None], vh[None, None], [L])
-        dt = time.perf_counter() - t0
+    units = 0
+    dt = 0.0
+    layer = 0
+    while dt < seconds and layer < w.layers:
+        k, v, q, kn, vn = (t.cpu().numpy() for t in synth.layer_inputs(w, layer, "cuda:0"))
+        for b in range(w.batch):
+            for h in range(w.kv_heads):
+                if dt >= seconds:
+                    break
+                (ck, sk), (cv, sv) = quant.quantize_int4(k[b, h], 64), quant.quantize_int4(v[b, h], 128)
+                qq = q[b, h * G:(h + 1) * G]
+                with threadpool_limits(1):
+                    t0 = time.perf_counter()
+                    nk, nsk = quant.quantize_int4(kn[b, h][None], 64)     # append the new row
+                    nv, nsv = quant.quantize_int4(vn[b, h][None], 128)
+                    ck2 = np.concatenate([ck, nk]); sk2 = np.concatenate([sk, nsk])
+                    cv2 = np.concatenate([cv, nv]); sv2 = np.concatenate([sv, nsv])
+                    kh = quant.dequantize_int4_exact(ck2, sk2, 64)
+                    vh = quant.dequantize_int4_exact(cv2, sv2, 128)
+                    attention.decode_attention(qq[None], kh[None, None], vh[None, None], [L])
+                    dt += time.perf_counter() - t0
+                units += 1
+        layer += 1
+        del k, v
+    S = L - 1
     row = 140
-    bytes_sample = len(pairs) * (L * row + G * 128 * 2 + G * 128 * 4)
-    return {"value": round(bytes_sample / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(pairs)} of {w.batch * w.kv_heads} (batch, kv head) units of 1 of "
-                      f"{w.layers} layers (append + exact dequant + fp64 attention), "
-                      f"{dt:.2f} s; full step extrapolates to {dt * w.batch * w.kv_heads / len(pairs) * w.layers:.1f} s"}
+    unit_bytes = S * row + row + 2 * 128 * 2 + G * 128 * 2 + G * 128 * 4
+    full = w.batch * w.kv_heads * w.layers
+    return {"value": round(units * unit_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{units} of the step's {full} (layer, batch, kv head) units "
+                      f"(append + exact dequant + fp64 attention over {L} positions), "
+                      f"{dt:.2f} s timed; a full step extrapolates to {dt * full / units:.1f} s"}
 
 
 if __name__ == "__main__":

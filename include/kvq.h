@@ -59,10 +59,15 @@
 extern "C" {
 #endif
 
-#define KVQ_VERSION 1
+#define KVQ_VERSION 2
 /* Largest batch the decode/append calls accept (per-sequence lengths and positions
  * travel in the kernel argument block). */
 #define KVQ_MAX_BATCH 256
+/* Bytes at the start of a decode workspace that hold split-arrival counters: one
+ * uint32 per (sequence, kv head), so the decode calls take batch * kv_heads <= 16384
+ * (KVQ_ERR_UNSUPPORTED otherwise).  They must read zero when a decode call starts;
+ * every decode call leaves them zero again. */
+#define KVQ_WS_COUNTER_BYTES 65536
 
 typedef enum {
   KVQ_INT4_G = 0,      /* group-wise symmetric INT4 ([KV-4bit] §2.1) */
@@ -122,9 +127,10 @@ size_t kvq_scales_bytes(const kvq_cache_desc* desc, int32_t kv);
  * a longest attended span of `span` positions and `q_heads` query heads; 0 if invalid. */
 int32_t kvq_plan_splits(const kvq_cache_desc* desc, int32_t q_heads, int32_t span);
 
-/* Workspace bytes kvq_decode_attn needs for these arguments (num_splits = 0: the
- * library's own plan for a longest span of min(max_len, window or max_len));
- * 0 if invalid.  Equal to B * q_heads * nsplit * (D + 2) * 4. */
+/* Workspace bytes kvq_decode_attn / kvq_append_decode_attn need for these arguments
+ * (num_splits = 0: the library's own plan for a longest span of min(max_len, window or
+ * max_len)); 0 if invalid.  Equal to KVQ_WS_COUNTER_BYTES + B * q_heads *
+ * (nsplit + 1) * (D + 2) * 4. */
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t q_heads,
                                   int32_t max_len, int32_t window, int32_t num_splits);
 
@@ -169,13 +175,35 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
  *   num_splits: sequence splits per (b, kv head), at most 1024; 0 = kvq_plan_splits.
  *   out: device, [B, q_heads, D] fp32.
  *   workspace: device scratch of at least kvq_decode_workspace_bytes bytes
- *              (KVQ_ERR_WORKSPACE otherwise); its contents are clobbered.
- * Split-K: each split writes an unnormalized partial (running max, sum, weighted V)
- * and a second kernel merges them with the log-sum-exp rule. */
+ *              (KVQ_ERR_WORKSPACE otherwise).  Zero-fill it once before its first use
+ *              (hipMemset of the whole buffer, or of its first KVQ_WS_COUNTER_BYTES):
+ *              the counters there must read zero when a call starts, and each call
+ *              leaves them zero; the rest is clobbered.  Calls that may run at the same
+ *              time need separate workspaces.
+ * Split-K: each split writes an unnormalized partial (running max, sum, weighted V) to
+ * the workspace; the partials are merged with the log-sum-exp rule, for INT4 with
+ * head_dim 128 and V group 128 by the last split to finish (no second launch),
+ * otherwise by a second kernel. */
 int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
                         const void* q_f16, int32_t q_heads, const int32_t* lens,
                         int32_t window, float softmax_scale, int32_t num_splits,
                         float* out, void* workspace, size_t ws_bytes, kvq_stream stream);
+
+/* One whole decode step of a layer ([KV-4bit] §1.1: append the new token's K/V, then
+ * attend over the cache including it): the same result as kvq_append with
+ * pos[b] = lens[b] - 1 followed by kvq_decode_attn with the same arguments.
+ *   k_f16, v_f16: device, [B, Hkv, D] fp16, the new token's rows (position lens[b] - 1).
+ * Every other argument, the workspace rule and the errors are those of kvq_decode_attn
+ * (KVQ_ERR_ARG also for null k_f16 / v_f16).  For INT4 with head_dim 128 and V group
+ * 128 the new row is quantized inside the attention kernel by the first split to finish
+ * its share of the cache, which writes it to the cache and adds it to the softmax from
+ * registers (one launch per step); other formats and shapes run the append kernel
+ * first. */
+int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
+                               const void* k_f16, const void* v_f16, const void* q_f16,
+                               int32_t q_heads, const int32_t* lens, int32_t window,
+                               float softmax_scale, int32_t num_splits, float* out,
+                               void* workspace, size_t ws_bytes, kvq_stream stream);
 
 /* Dequantize positions [start_pos, start_pos + n) of K (kv = 0) or V (kv = 1)
  * ([KV-4bit] §2.1 dequantize_4bit_group: code * scale; codec: s * H c[idx] / sqrt(D)).

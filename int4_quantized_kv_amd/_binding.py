@@ -29,12 +29,14 @@ FORMATS = {"int4": KVQ_INT4_G, "int8": KVQ_INT8_TOKEN, "codec": KVQ_WHT_LM4}
 KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = \
     0, -1, -2, -3, -4, -5
 KVQ_MAX_BATCH = 256
+KVQ_WS_COUNTER_BYTES = 65536
 
 # Every symbol include/kvq.h declares.
 EXPORTS = (
     "kvq_version", "kvq_status_str", "kvq_check_desc", "kvq_codes_bytes", "kvq_scales_bytes",
     "kvq_plan_splits", "kvq_decode_workspace_bytes", "kvq_codec_codebook",
-    "kvq_quantize_prefill", "kvq_append", "kvq_decode_attn", "kvq_dequant",
+    "kvq_quantize_prefill", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
+    "kvq_dequant",
 )
 
 
@@ -77,6 +79,8 @@ def _load():
         "kvq_quantize_prefill": (i32, [D, C, vp, vp, i32, i32, vp]),
         "kvq_append": (i32, [D, C, vp, vp, P(i32), vp]),
         "kvq_decode_attn": (i32, [D, C, vp, i32, P(i32), i32, f32, i32, vp, vp, sz, vp]),
+        "kvq_append_decode_attn": (i32, [D, C, vp, vp, vp, i32, P(i32), i32, f32, i32, vp, vp,
+                                         sz, vp]),
         "kvq_dequant": (i32, [D, C, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -191,6 +195,30 @@ def kvq_decode_attn(desc, cache, q, q_heads, lens, window, softmax_scale, num_sp
                              int(num_splits), _ptr(out, torch.float32, "out"),
                              _ptr(workspace, None, "workspace"), int(ws_bytes), _stream(stream))
     return _check(st, "kvq_decode_attn")
+
+
+def kvq_append_decode_attn(desc, cache, k, v, q, q_heads, lens, window, softmax_scale,
+                           num_splits, out, workspace, ws_bytes=None, stream=None):
+    import torch
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = LIB.kvq_append_decode_attn(
+        ctypes.byref(desc), ctypes.byref(cache), _ptr(k, torch.float16, "k"),
+        _ptr(v, torch.float16, "v"), _ptr(q, torch.float16, "q"), int(q_heads),
+        _i32_array(lens), int(window), float(softmax_scale), int(num_splits),
+        _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"), int(ws_bytes),
+        _stream(stream))
+    return _check(st, "kvq_append_decode_attn")
+
+
+def decode_workspace(desc, q_heads, max_len, window=0, num_splits=0, device="cuda"):
+    """A zero-filled decode workspace (the split counters at its start must read zero
+    before the first call; the library keeps them zero afterwards)."""
+    import torch
+    nbytes = kvq_decode_workspace_bytes(desc, q_heads, max_len, window, num_splits)
+    if nbytes == 0:
+        raise KvqError(KVQ_ERR_ARG, "kvq_decode_workspace_bytes")
+    return torch.zeros((nbytes + 3) // 4, dtype=torch.float32, device=device)
 
 
 def kvq_dequant(desc, cache, kv, start_pos, n, out, stream=None):

@@ -66,6 +66,14 @@ int32_t quant_common(const kvq_cache_desc* desc, const kvq_cache* cache, const v
   return launch_status(launch_quant_intq(desc->format, a, stream));
 }
 
+// Workspace: the split-arrival counters first (KVQ_WS_COUNTER_BYTES, zero between
+// calls), then nsplit + 1 partial slots (weighted V sums, then (max, sum) pairs) per
+// query head; the extra slot holds the fused append's new row.
+constexpr size_t partials_offset() { return KVQ_WS_COUNTER_BYTES; }
+size_t partials_bytes(int32_t batch, int32_t q_heads, int32_t ns, int32_t head_dim) {
+  return (size_t)batch * q_heads * (ns + 1) * (head_dim + 2) * sizeof(float);
+}
+
 // Longest attended span over the batch; KVQ_ERR_* (negative) if a length is invalid.
 int32_t check_lens(const kvq_cache_desc* d, const int32_t* lens, int32_t window) {
   int32_t span = 0;
@@ -127,7 +135,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* d, int32_t q_heads, int3
     return 0;
   const int32_t span = window > 0 && window < max_len ? window : max_len;
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(d, q_heads, span);
-  return (size_t)d->batch * q_heads * ns * (d->head_dim + 2) * sizeof(float);
+  return partials_offset() + partials_bytes(d->batch, q_heads, ns, d->head_dim);
 }
 
 int32_t kvq_codec_codebook(float* levels16, float* thresholds15) {
@@ -172,10 +180,15 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache, const voi
   return quant_common(desc, cache, k_f16, v_f16, map, 1, static_cast<hipStream_t>(stream));
 }
 
-int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache, const void* q_f16,
-                        int32_t q_heads, const int32_t* lens, int32_t window,
-                        float softmax_scale, int32_t num_splits, float* out, void* workspace,
-                        size_t ws_bytes, kvq_stream stream) {
+namespace {
+
+// Shared by kvq_decode_attn and kvq_append_decode_attn: validate, then append (when
+// k_new is set) and attend.
+int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const void* k_new,
+                      const void* v_new, const void* q_f16, int32_t q_heads,
+                      const int32_t* lens, int32_t window, float softmax_scale,
+                      int32_t num_splits, float* out, void* workspace, size_t ws_bytes,
+                      hipStream_t stream) {
   const int32_t st = check_desc(desc);
   if (st != KVQ_OK) return st;
   if (!cache_ok(cache) || !q_f16 || !lens || !out || window < 0 || num_splits < 0 ||
@@ -184,11 +197,13 @@ int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache, cons
   if (q_heads % desc->kv_heads) return KVQ_ERR_ARG;
   const int32_t G = q_heads / desc->kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
+  if ((int64_t)desc->batch * desc->kv_heads > (int64_t)(KVQ_WS_COUNTER_BYTES / 4))
+    return KVQ_ERR_UNSUPPORTED;
   const int32_t span = check_lens(desc, lens, window);
   if (span < 0) return span;
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(desc, q_heads, span);
   if (ns < 1 || ns > MAX_SPLITS) return KVQ_ERR_ARG;
-  const size_t need = (size_t)desc->batch * q_heads * ns * (desc->head_dim + 2) * sizeof(float);
+  const size_t need = partials_offset() + partials_bytes(desc->batch, q_heads, ns, desc->head_dim);
   if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
 
   DecodeArgs a;
@@ -198,8 +213,9 @@ int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache, cons
   a.v_codes = cache->v_codes;
   a.v_scales = static_cast<const float*>(cache->v_scales);
   a.q = static_cast<const uint16_t*>(q_f16);
-  a.ws_acc = static_cast<float*>(workspace);
-  a.ws_ml = a.ws_acc + (size_t)desc->batch * q_heads * ns * desc->head_dim;
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + partials_offset());
+  a.ws_ml = a.ws_acc + (size_t)desc->batch * q_heads * (ns + 1) * desc->head_dim;
   a.out = out;
   a.B = desc->batch;
   a.Hkv = desc->kv_heads;
@@ -218,7 +234,46 @@ int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache, cons
     codec_codebook(a.levels, thr);
   }
   for (int32_t b = 0; b < desc->batch; ++b) a.lens[b] = lens[b];
-  return launch_status(launch_decode(desc->format, a, G, static_cast<hipStream_t>(stream)));
+
+  if (k_new) {
+    if (fused_append_supported(desc, G)) {
+      a.k_new = static_cast<const uint16_t*>(k_new);
+      a.v_new = static_cast<const uint16_t*>(v_new);
+    } else {
+      // the other kernels attend over the cache only: append first
+      SlotMap map;
+      std::memset(&map, 0, sizeof(map));
+      for (int32_t b = 0; b < desc->batch; ++b) map.pos[b] = lens[b] - 1;
+      map.append = 1;
+      map.n = 1;
+      map.cap = desc->capacity;
+      const int32_t r = quant_common(desc, cache, k_new, v_new, map, 1, stream);
+      if (r != KVQ_OK) return r;
+    }
+  }
+  return launch_status(launch_decode(desc->format, a, G, stream));
+}
+
+}  // namespace
+
+int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache, const void* q_f16,
+                        int32_t q_heads, const int32_t* lens, int32_t window,
+                        float softmax_scale, int32_t num_splits, float* out, void* workspace,
+                        size_t ws_bytes, kvq_stream stream) {
+  return decode_common(desc, cache, nullptr, nullptr, q_f16, q_heads, lens, window,
+                       softmax_scale, num_splits, out, workspace, ws_bytes,
+                       static_cast<hipStream_t>(stream));
+}
+
+int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
+                               const void* k_f16, const void* v_f16, const void* q_f16,
+                               int32_t q_heads, const int32_t* lens, int32_t window,
+                               float softmax_scale, int32_t num_splits, float* out,
+                               void* workspace, size_t ws_bytes, kvq_stream stream) {
+  if (!k_f16 || !v_f16) return KVQ_ERR_ARG;
+  return decode_common(desc, cache, k_f16, v_f16, q_f16, q_heads, lens, window,
+                       softmax_scale, num_splits, out, workspace, ws_bytes,
+                       static_cast<hipStream_t>(stream));
 }
 
 int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t kv,

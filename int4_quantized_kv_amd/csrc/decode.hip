@@ -238,11 +238,8 @@ template <int D, int FMT>
 hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   hipError_t e;
-  if (FMT == KVQ_INT4_G && mfma_int4_eligible(D, a.gk, a.gv, a.cap, G)) {
-    e = launch_decode_int4_mfma(a, G, s);
-    if (e != hipSuccess) return e;
-    return launch_kernel(merge_kernel<D, false>, dim3(a.Hq, a.B), dim3(D), a, s);
-  }
+  if (FMT == KVQ_INT4_G && mfma_int4_eligible(D, a.gk, a.gv, a.cap, G))
+    return launch_decode_int4_mfma(a, G, s);   // merges the splits itself
   switch (G) {
     case 1: e = launch_kernel(decode_splitk_kernel<D, 1, FMT>, grid, dim3(256), a, s); break;
     case 2: e = launch_kernel(decode_splitk_kernel<D, 2, FMT>, grid, dim3(256), a, s); break;

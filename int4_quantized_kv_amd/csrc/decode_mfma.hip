@@ -32,10 +32,12 @@
 // p = 2^(s * (z - m)) with s = softmax scale * log2 e (one fma + exp per score); it
 // rescales the accumulators only when some head's running maximum grows.
 // The four waves of a workgroup take interleaved tiles of the split and merge their
-// (max, sum, weighted V) through LDS; the merge kernel of decode.hip combines splits.
+// (max, sum, weighted V) through LDS; the workgroup that finishes last for a (sequence,
+// KV head) then combines the splits' partials (no separate merge launch).
 // Tiles are staged through LDS by direct global->LDS transfers (see "LDS staging").
 #include <cmath>
 
+#include "kvq_arith.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -352,11 +354,110 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
   }
 }
 
+// Device-scope (all XCDs) store / load of one float of the split partials.
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fetch(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The new token's row when the append is fused into the attention.  Wave 0 of every
+// workgroup copies the fp16 K and V rows and the G query rows into LDS (s_new) at the
+// start, so the workgroup that ends up doing the append reads them without a trip to
+// memory.  Lanes 0..15 of wave 0 quantize K dims 8c .. 8c+7 (c = lane), lanes 16..31
+// V, with the arithmetic of the append kernel; the codes and scales go to the cache for
+// later steps and the row enters this step's softmax as one extra partial, so no tile
+// has to read it back from memory.
+template <int G>
+struct NewLds {
+  uint16_t k[HD], v[HD], q[G][HD];
+};
+
+template <int G>
+__device__ __forceinline__ void stage_new_row(const DecodeArgs& a, int b, int kvh, NewLds<G>* s,
+                                              int lane) {
+  const size_t r = ((size_t)b * a.Hkv + kvh) * HD;
+  uint8_t* base = reinterpret_cast<uint8_t*>(s);
+  dma4(a.k_new + r + 2 * lane, base);
+  dma4(a.v_new + r + 2 * lane, base + 2 * HD);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    dma4(a.q + ((size_t)b * a.Hq + kvh * G + h) * HD + 2 * lane, base + (2 + h) * 2 * HD);
+}
+
+struct NewRow {
+  float z[8];     // unscaled score per query head (K lanes)
+  float v[8];     // dequantized V values of dims 8c .. 8c+7 (V lanes)
+  uint32_t w;     // the 8 packed codes of this lane
+  float sc;       // the group scale of this lane
+};
+
+template <int G, int NGK>
+__device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds<G>* s, int lane) {
+  NewRow nr;
+  const bool isv = lane >= 16;
+  const int c = lane & 15;
+  const int lpg = (isv ? HD : a.gk) >> 3;               // lanes per quantization group
+  float x[8];
+  load8_f16((isv ? s->v : s->k) + 8 * c, x);
+  float am = 0.0f;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) am = fmaxf(am, fabsf(x[jj]));
+  for (int m = 1; m < lpg; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+  const float sc = kvq_int4_scale(am);
+  const float rc = 1.0f / sc;
+  uint32_t w = 0;
+  float code[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const float q = fminf(fmaxf(rintf(kvq_div_exact(x[jj], sc, rc)), -7.0f), 7.0f);
+    code[jj] = q;
+    w |= ((uint32_t)(int)q & 15u) << (4 * jj);
+  }
+  nr.w = w;
+  nr.sc = sc;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) nr.v[jj] = code[jj] * sc;
+  // score of every query head: sum over K groups of (group scale) * (q . codes)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float qv[8];
+    load8_f16(s->q[h] + 8 * c, qv);
+    float d = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) d = __builtin_fmaf(qv[jj], code[jj], d);
+    for (int m = 1; m < lpg; m <<= 1) d += __shfl_xor(d, m);   // within the K group
+    d *= sc;
+    for (int m = lpg; m < 16; m <<= 1) d += __shfl_xor(d, m);  // over the K groups
+    nr.z[h] = d;
+  }
+  return nr;
+}
+
+// Write the lane's codes and scale of the new row to cache row `row`.
+template <int NGK>
+__device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewRow& nr, size_t row,
+                                              int lane) {
+  const bool isv = lane >= 16;
+  const int c = lane & 15;
+  if (isv) {
+    static_cast<uint32_t*>(const_cast<void*>(a.v_codes))[row * (HD / 8) + c] = nr.w;
+    if (c == 0) const_cast<float*>(a.v_scales)[row] = nr.sc;
+  } else {
+    const int lpg = a.gk >> 3;
+    static_cast<uint32_t*>(const_cast<void*>(a.k_codes))[row * (HD / 8) + c] = nr.w;
+    if ((c & (lpg - 1)) == 0) const_cast<float*>(a.k_scales)[row * NGK + c / lpg] = nr.sc;
+  }
+}
+
 template <int G, int NGK>
 __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   using L = Slot<NGK>;
   constexpr int DMA = L::DMA;
   __shared__ __attribute__((aligned(16))) uint8_t smem[WAVES * NB * L::BYTES];
+  __shared__ __attribute__((aligned(16))) NewLds<G> s_new;
+  __shared__ int s_last;
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -372,10 +473,26 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   const int chunk = (span + a.nsplit - 1) / a.nsplit;
   const int ps = min(len, lo_pos + sp * chunk);
   const int pe = min(len, ps + chunk);
+  // with the append fused, the split holding position len - 1 takes that row from the
+  // new token instead of from a tile
+  const bool appending = a.k_new != nullptr && ps < len && pe == len;
+  const int pt = appending ? len - 1 : pe;     // tiles cover [ps, pt)
+
+  // ---- start the first two tiles' transfers before anything else
+  const size_t row0 = ((size_t)b * a.Hkv + kvh) * a.cap;
+  constexpr int STRIDE = TILE * WAVES;
+  const int tfirst = ps + TILE * wave;
+  const int ntiles = tfirst < pt ? (pt - tfirst + STRIDE - 1) / STRIDE : 0;
+  uint8_t* ring = smem + wave * NB * L::BYTES;
+  const DmaOffs dof = dma_offsets<NGK>(lane);
+  // (issued before the tiles: the loop's in-order transfer waits then cover them too)
+  if (a.k_new != nullptr && wave == 0) stage_new_row<G>(a, b, kvh, &s_new, lane);
+  if (ntiles > 0) issue_tile<NGK>(a, row0, tfirst, pt, ring, lane, dof);
+  if (ntiles > 1) issue_tile<NGK>(a, row0, tfirst + STRIDE, pt, ring + L::BYTES, lane, dof);
 
   // q as the B operand of dim chunk c: lane quarter j holds dims 8(4j + c) + {p, p + 4}
-  // in slots {2p, 2p + 1} (the order unpack_word produces) when quarter j lies in the
-  // column's K group, zeros otherwise; q is pre-scaled by scale * log2 e in fp32 later.
+  // in slots {2p, 2p + 1} (the order unpack_word_u produces) when quarter j lies in the
+  // column's K group, zeros otherwise.
   half8 qb[4];
   {
     constexpr int QPG = 4 / NGK;   // lane quarters (32 dims) per K group
@@ -432,18 +549,10 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   st.m = NEG_INF;
   st.l = 0.0f;
 
-  const size_t row0 = ((size_t)b * a.Hkv + kvh) * a.cap;
-  constexpr int STRIDE = TILE * WAVES;
-  const int tfirst = ps + TILE * wave;
-  const int ntiles = tfirst < pe ? (pe - tfirst + STRIDE - 1) / STRIDE : 0;
-  uint8_t* ring = smem + wave * NB * L::BYTES;
-  const DmaOffs dof = dma_offsets<NGK>(lane);
-  if (ntiles > 0) issue_tile<NGK>(a, row0, tfirst, pe, ring, lane, dof);
-  if (ntiles > 1) issue_tile<NGK>(a, row0, tfirst + STRIDE, pe, ring + L::BYTES, lane, dof);
   for (int k = 0; k < ntiles; ++k) {
     const int t0 = tfirst + k * STRIDE;
     if (k + 2 < ntiles) {
-      issue_tile<NGK>(a, row0, t0 + 2 * STRIDE, pe, ring + ((k + 2) % NB) * L::BYTES, lane, dof);
+      issue_tile<NGK>(a, row0, t0 + 2 * STRIDE, pt, ring + ((k + 2) % NB) * L::BYTES, lane, dof);
       wait_vmcnt<2 * DMA>();
     } else if (k + 1 < ntiles) {
       wait_vmcnt<DMA>();
@@ -451,14 +560,14 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
       wait_vmcnt<0>();
     }
     const uint8_t* lb = ring + (k % NB) * L::BYTES;
-    if (t0 + TILE <= pe)
-      process_tile<G, NGK, false>(lb, lo, st, qb, qbias, t0, pe, j, a.qscale);
+    if (t0 + TILE <= pt)
+      process_tile<G, NGK, false>(lb, lo, st, qb, qbias, t0, pt, j, a.qscale);
     else
-      process_tile<G, NGK, true>(lb, lo, st, qb, qbias, t0, pe, j, a.qscale);
+      process_tile<G, NGK, true>(lb, lo, st, qb, qbias, t0, pt, j, a.qscale);
   }
 
-  // ---- combine the 4 waves through LDS (reusing the ring): lane (r, j) holds
-  // O[column r][8(4j + i) + e] in oacc[e][i]; the head's value sits in column head * NGK.
+  // ---- combine the 4 waves through LDS, reusing the ring: lane (r, j) holds
+  // O[column r][8(4j + i) + e] in oacc[e][i]; a head sits in column head * NGK
   __syncthreads();
   float* s_o = reinterpret_cast<float*>(smem);                 // [WAVES][G][HD]
   float* s_m = s_o + WAVES * G * HD;                            // [WAVES][G]
@@ -471,11 +580,13 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
       for (int i = 0; i < 4; ++i)
         s_o[(wave * G + qhead) * HD + 8 * (4 * j + i) + e] = st.oacc[e][i];
     if (j == 0) {
-      s_m[wave * G + qhead] = st.m * a.qscale;   // base-2 units, as the merge expects
+      s_m[wave * G + qhead] = st.m * a.qscale;   // base-2 units
       s_l[wave * G + qhead] = l_run;
     }
   }
   __syncthreads();
+  const int nps = a.nsplit + 1;                         // partial slots per query head
+  const size_t pbase = (size_t)(b * a.Hq + kvh * G) * nps;   // slot of (head 0, split 0)
   for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
     const int h = idx / HD, d = idx % HD;
     float M = NEG_INF;
@@ -493,13 +604,119 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
         }
       }
     }
-    const size_t o = (size_t)(b * a.Hq + kvh * G + h) * a.nsplit + sp;
-    a.ws_acc[o * HD + d] = Acc;
+    const size_t o = pbase + (size_t)h * nps + sp;
+    publish(a.ws_acc + o * HD + d, Acc);
     if (d == 0) {
-      a.ws_ml[2 * o] = M;
-      a.ws_ml[2 * o + 1] = Lsum;
+      publish(a.ws_ml + 2 * o, M);
+      publish(a.ws_ml + 2 * o + 1, Lsum);
     }
   }
+
+  // ---- arrivals.  The partials are device-scope stores (written through to the point
+  // where every XCD sees them); each wave waits until its own have completed before the
+  // barrier, so when the counting thread bumps the (device-scope) arrival counter the
+  // whole partial is visible.  This avoids a release fence, which on this chip writes
+  // back the XCD's whole L2 and costs microseconds per workgroup.
+  uint32_t* cnt = a.counters + b * a.Hkv + kvh;
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int arrived = s_last;
+  const bool fused = a.k_new != nullptr;
+  if (fused && arrived == 0) {
+    // The first workgroup to arrive (the one with the most slack) quantizes the new
+    // token's row and publishes that one position as an extra partial (slot nsplit:
+    // max = its score, sum = 1, value = its dequantized V row), counts itself a second
+    // time, then writes the row to the cache (nothing in this launch reads it there).
+    // Every transfer of wave 0, s_new's included, completed before the barrier above.
+    NewRow nr;
+    if (wave == 0 && lane < 32) {
+      nr = append_row<G, NGK>(a, &s_new, lane);
+      const size_t o = pbase + a.nsplit;
+      if (lane >= 16) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj)
+            publish(a.ws_acc + (o + (size_t)h * nps) * HD + 8 * (lane - 16) + jj, nr.v[jj]);
+      } else if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          publish(a.ws_ml + 2 * (o + (size_t)h * nps), nr.z[h] * a.qscale);
+          publish(a.ws_ml + 2 * (o + (size_t)h * nps) + 1, 1.0f);
+        }
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_last = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave == 0 && lane < 32) store_new_row<NGK>(a, nr, row0 + (size_t)((len - 1) % a.cap), lane);
+    __syncthreads();
+    arrived = s_last;
+  }
+  const int np = fused ? nps : a.nsplit;                // partials to merge
+  if (arrived != np - 1) return;
+
+  // ---- the last arrival merges the np partials of its G heads with the log-sum-exp
+  // rule (device-scope loads: the partials come from other XCDs) and resets the counter.
+  // Each thread first issues the loads of its outputs' first PF partials, so their
+  // latency overlaps the maxima's.
+  constexpr int PF = 8;
+  constexpr int OPT = (G * HD + 255) / 256;             // outputs per thread
+  float pre[OPT][PF];
+#pragma unroll
+  for (int u = 0; u < OPT; ++u) {
+    const int idx = threadIdx.x + 256 * u;
+    const int h = idx / HD, d = idx % HD;
+#pragma unroll
+    for (int sI = 0; sI < PF; ++sI)
+      pre[u][sI] = idx < G * HD && sI < np ? fetch(a.ws_acc + (pbase + (size_t)h * nps + sI) * HD + d)
+                                           : 0.0f;
+  }
+  float* s_w = reinterpret_cast<float*>(smem);          // [G][np] split weights
+  float* s_L = s_w + G * np;                            // [G]
+  for (int idx = threadIdx.x; idx < G * np; idx += 256) {
+    const int h = idx / np, sI = idx % np;
+    s_w[idx] = fetch(a.ws_ml + 2 * (pbase + (size_t)h * nps + sI));
+  }
+  __syncthreads();
+  // one wave per head: maximum, weights 2^(m_s - M), weighted sum of the partial sums
+  for (int h = wave; h < G; h += WAVES) {
+    float M = NEG_INF;
+    for (int sI = lane; sI < np; sI += 64) M = fmaxf(M, s_w[h * np + sI]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+    float Ls = 0.0f;
+    for (int sI = lane; sI < np; sI += 64) {
+      const float ms = s_w[h * np + sI];
+      const float wgt = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
+      s_w[h * np + sI] = wgt;
+      Ls = __builtin_fmaf(wgt, fetch(a.ws_ml + 2 * (pbase + (size_t)h * nps + sI) + 1), Ls);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) Ls += __shfl_xor(Ls, m);
+    if (lane == 0) s_L[h] = Ls;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < OPT; ++u) {
+    const int idx = threadIdx.x + 256 * u;
+    if (idx < G * HD) {
+      const int h = idx / HD, d = idx % HD;
+      float A = 0.0f;
+#pragma unroll
+      for (int sI = 0; sI < PF; ++sI)
+        if (sI < np) A = __builtin_fmaf(pre[u][sI], s_w[h * np + sI], A);
+      for (int sI = PF; sI < np; ++sI)
+        A = __builtin_fmaf(fetch(a.ws_acc + (pbase + (size_t)h * nps + sI) * HD + d),
+                           s_w[h * np + sI], A);
+      a.out[(size_t)(b * a.Hq + kvh * G + h) * HD + d] = A / s_L[h];
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int G>
@@ -532,6 +749,11 @@ int32_t plan_splits_mfma(int32_t units, int32_t span) {
   if (n > by_span) n = by_span;
   if (n > 1024) n = 1024;
   return n < 1 ? 1 : n;
+}
+
+bool fused_append_supported(const kvq_cache_desc* d, int32_t q_group) {
+  return d->format == KVQ_INT4_G &&
+         mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group);
 }
 
 hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s) {

@@ -50,6 +50,9 @@ struct DecodeArgs {
   float* ws_acc;         // [B, Hq, nsplit, D]
   float* ws_ml;          // [B, Hq, nsplit, 2] (running max in log2 units, sum)
   float* out;            // [B, Hq, D]
+  uint32_t* counters;    // [B, Hkv] split arrival counters (zero between calls)
+  const uint16_t* k_new; // [B, Hkv, D] fp16 rows appended at position lens[b] - 1, or null
+  const uint16_t* v_new;
   int32_t B, Hkv, Hq, D, cap, gk, gv, window, nsplit;
   float qscale;          // softmax scale * log2(e)
   float levels[16];
@@ -60,6 +63,11 @@ hipError_t launch_quant_intq(int32_t format, const QuantArgs& a, hipStream_t s);
 hipError_t launch_dequant_intq(int32_t format, const DequantArgs& a, hipStream_t s);
 hipError_t launch_codec_encode(const QuantArgs& a, hipStream_t s);
 hipError_t launch_codec_dequant(const DequantArgs& a, hipStream_t s);
+// Decode attention.  When the matrix-core kernel applies, the splits are merged inside
+// it (a.counters must then point at zeroed counters) and a.k_new / a.v_new, if set,
+// fuse the append of position lens[b] - 1 into it; the other kernels ignore both
+// (callers launch the append separately, see fused_append_supported) and run the
+// merge kernel.
 hipError_t launch_decode(int32_t format, const DecodeArgs& a, int32_t q_group, hipStream_t s);
 
 // Split plan of the decode kernels for the cache `d`, `q_group` query heads per KV
@@ -71,6 +79,7 @@ int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span);
 bool mfma_int4_eligible(int32_t head_dim, int32_t group_k, int32_t group_v, int32_t cap,
                         int32_t q_group);
 int32_t plan_splits_mfma(int32_t units, int32_t span);
+bool fused_append_supported(const kvq_cache_desc* d, int32_t q_group);
 hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
 
 // Largest split count a decode call accepts (the merge kernel keeps one weight per

@@ -48,11 +48,24 @@ def assert_attn_close(got, ref, what=""):
     return max_abs, rel
 
 
-def decode(desc, dc, q, q_heads, lens, window=0, scale=0.0, num_splits=0):
-    """Run kvq_decode_attn with a fresh workspace; returns the fp32 output tensor."""
-    ws_bytes = kvq.kvq_decode_workspace_bytes(desc, q_heads, max(lens), window, num_splits)
-    ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device=q.device)
+def decode(desc, dc, q, q_heads, lens, window=0, scale=0.0, num_splits=0, ws=None):
+    """Run kvq_decode_attn (with a fresh zeroed workspace unless one is given); returns
+    the fp32 output tensor."""
+    if ws is None:
+        ws = kvq.decode_workspace(desc, q_heads, max(lens), window, num_splits, q.device)
     out = torch.empty((desc.batch, q_heads, desc.head_dim), dtype=torch.float32, device=q.device)
     kvq.kvq_decode_attn(desc, dc.c, q, q_heads, lens, window, scale, num_splits, out, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def append_decode(desc, dc, k_new, v_new, q, q_heads, lens, window=0, scale=0.0,
+                  num_splits=0, ws=None):
+    """Run kvq_append_decode_attn (fresh zeroed workspace unless one is given)."""
+    if ws is None:
+        ws = kvq.decode_workspace(desc, q_heads, max(lens), window, num_splits, q.device)
+    out = torch.empty((desc.batch, q_heads, desc.head_dim), dtype=torch.float32, device=q.device)
+    kvq.kvq_append_decode_attn(desc, dc.c, k_new, v_new, q, q_heads, lens, window, scale,
+                               num_splits, out, ws)
     torch.cuda.synchronize()
     return out

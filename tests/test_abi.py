@@ -23,14 +23,14 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert sorted(kvq.EXPORTS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (kvq_\w+)", out))
     for n in names:
         assert n in exported, n
-    assert kvq.kvq_version() == 1
+    assert kvq.kvq_version() == 2
 
 
 def test_status_strings():
@@ -113,7 +113,7 @@ def test_error_paths_enqueue_nothing():
     # decode: Hq % Hkv, unsupported group, len 0, len > capacity without window,
     # window > capacity with len > capacity, too-small / missing workspace
     ws = kvq.kvq_decode_workspace_bytes(d, 8, 64)
-    assert ws == 2 * 8 * kvq.kvq_plan_splits(d, 8, 64) * 130 * 4
+    assert ws == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * (kvq.kvq_plan_splits(d, 8, 64) + 1) * 130 * 4
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 6, [10, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_decode_attn, d, c, FAKE, 64, [10, 10], 0, 0.0, 0, FAKE, FAKE, 1 << 30, 0)
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [10, 0], 0, 0.0, 0, FAKE, FAKE, ws, 0)
@@ -123,6 +123,14 @@ def test_error_paths_enqueue_nothing():
     _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, 0, ws, 0)
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], -1, 0.0, 0, FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, float("nan"), 0, FAKE, FAKE, ws, 0)
+    # fused append + decode: null new rows, then the decode checks
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_append_decode_attn, d, c, 0, FAKE, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_append_decode_attn, d, c, FAKE, 0, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_append_decode_attn, d, c, FAKE, FAKE, FAKE, 8, [65, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
+    _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_append_decode_attn, d, c, FAKE, FAKE, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, FAKE, ws - 1, 0)
+    # the split counters bound batch * kv_heads
+    big = kvq.make_desc("int4", 256, 128, 128, 64)
+    _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_decode_attn, big, c, FAKE, 128, [10] * 256, 0, 0.0, 1, FAKE, FAKE, 1 << 40, 0)
     # dequant: bad kv selector, n > capacity
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_dequant, d, c, 2, 0, 4, FAKE, 0)
     _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_dequant, d, c, 0, 0, 65, FAKE, 0)

@@ -11,7 +11,7 @@ import torch
 import int4_quantized_kv_amd as kvq
 import synth
 from oracle import attention, quant
-from tests.kvq_testutil import assert_attn_close, decode, np16
+from tests.kvq_testutil import append_decode, assert_attn_close, decode, np16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -214,3 +214,94 @@ def test_int4_generic_fallback(gv, cap):
     kh, vh = _oracle_hat("int4", np16(k), np16(v), 64, gv)
     ref = attention.decode_attention(np16(q), kh, vh, [L, L], W)
     assert_attn_close(out.cpu().numpy(), ref, f"generic gv={gv} cap={cap}")
+
+
+FUSED_CASES = [
+    # fmt, gk, gv, G, D, lens, window, cap, nsplit   (the first four: matrix-core kernel)
+    ("int4", 64, 128, 4, 128, [300, 45], 0, None, 0),
+    ("int4", 32, 128, 8, 128, [1100, 1], 0, None, 5),     # a sequence of length 1
+    ("int4", 128, 128, 1, 128, [97, 640], 0, None, 64),   # more splits than positions
+    ("int4", 64, 128, 2, 128, [900, 900], 256, 256, 0),   # ring of 256 slots, wrapped
+    ("int4", 64, 64, 4, 128, [300, 45], 0, None, 0),      # V group 64: append kernel first
+    ("int8", 64, 128, 4, 128, [300, 45], 0, None, 3),
+    ("codec", 64, 128, 4, 128, [300, 45], 0, None, 0),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[f"fused{i}" for i in range(len(FUSED_CASES))])
+def test_append_decode_step(case):
+    """kvq_append_decode_attn: the new token lands in the cache exactly as kvq_append
+    stores it, and the attention covers it (lpnh.cn/news/2042373 section 1.1)."""
+    fmt, gk, gv, G, D, lens, window, cap, ns = case
+    B, Hkv = len(lens), 2
+    L = max(lens)
+    C = cap or L
+    k = synth.kv_source((B, Hkv, L, D), 700 + L, DEV, outlier_channels=3)
+    v = synth.kv_source((B, Hkv, L, D), 800 + L, DEV, outlier_channels=3,
+                        zero_groups=((1, 0, 0, 0, D),))
+    q = synth.query((B, Hkv * G, D), 900 + L, DEV)
+    desc = kvq.make_desc(fmt, B, Hkv, D, C, gk, gv)
+    ref_cache = kvq.DeviceCache(desc, DEV)
+    dc = kvq.DeviceCache(desc, DEV)
+    # positions 0 .. len_b - 2 from the prefill (ring-chunked), position len_b - 1 new
+    for start in range(0, L, C):
+        n = min(C, L - start)
+        for cache in (dc, ref_cache):
+            kvq.kvq_quantize_prefill(desc, cache.c, k[:, :, start:start + n].contiguous(),
+                                     v[:, :, start:start + n].contiguous(), start, n)
+    idx = torch.tensor([ln - 1 for ln in lens], device=DEV)
+    ar = torch.arange(B, device=DEV)
+    kn = k[ar, :, idx].contiguous()           # [B, Hkv, D]
+    vn = v[ar, :, idx].contiguous()
+    # clobber slot len_b - 1 of the fused cache so the call must write it
+    for b, ln in enumerate(lens):
+        s = (ln - 1) % C
+        dc.k_codes.view(B, Hkv, C, -1)[b, :, s] = 0x5A
+        dc.v_codes.view(B, Hkv, C, -1)[b, :, s] = 0xA5
+        dc.k_scales.view(B, Hkv, C, -1)[b, :, s] = -1.0
+        dc.v_scales.view(B, Hkv, C, -1)[b, :, s] = -1.0
+    kvq.kvq_append(desc, ref_cache.c, kn, vn, [ln - 1 for ln in lens])
+    out = append_decode(desc, dc, kn, vn, q, Hkv * G, lens, window, 0.0, ns)
+    for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
+        assert torch.equal(getattr(dc, name), getattr(ref_cache, name)), name
+    if fmt == "codec":
+        # the codec's attention parity lives in test_gpu_codec.py; here: same result as
+        # the separate calls
+        ref = decode(desc, ref_cache, q, Hkv * G, lens, window, 0.0, ns).cpu().numpy()
+        assert_attn_close(out.cpu().numpy(), ref.astype(np.float64), f"fused {case}")
+        return
+    kh, vh = _oracle_hat(fmt, np16(k), np16(v), gk, gv)
+    ref = attention.decode_attention(np16(q), kh, vh, lens, window)
+    assert_attn_close(out.cpu().numpy(), ref, f"fused {case}")
+
+
+def test_append_decode_loop_reuses_workspace():
+    """Eight consecutive decode steps through one workspace (split counters are reset by
+    each call), the split count changing between calls; each step matches the oracle."""
+    B, Hkv, G, D, P, steps = 2, 2, 4, 128, 500, 8
+    L = P + steps
+    k = synth.kv_source((B, Hkv, L, D), 31, DEV, outlier_channels=3)
+    v = synth.kv_source((B, Hkv, L, D), 32, DEV, outlier_channels=3)
+    qs = synth.query((steps, B, Hkv * G, D), 33, DEV)
+    desc = kvq.make_desc("int4", B, Hkv, D, L)
+    dc = kvq.DeviceCache(desc, DEV)
+    kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, :P].contiguous(), v[:, :, :P].contiguous(), 0, P)
+    ws = kvq.decode_workspace(desc, Hkv * G, L, 0, 64, DEV)
+    kh, vh = _oracle_hat("int4", np16(k), np16(v))
+    for t in range(steps):
+        pos = P + t
+        q = qs[t].contiguous()
+        ns = (0, 1, 7, 64)[t % 4]
+        out = append_decode(desc, dc, k[:, :, pos].contiguous(), v[:, :, pos].contiguous(), q,
+                            Hkv * G, [pos + 1, pos + 1], 0, 0.0, ns, ws=ws)
+        ref = attention.decode_attention(np16(q), kh, vh, [pos + 1, pos + 1])
+        assert_attn_close(out.cpu().numpy(), ref, f"step {t} nsplit={ns}")
+        counters = ws[: B * Hkv].view(torch.int32)
+        assert int(counters.abs().sum()) == 0, "split counters not reset"
+    # a smaller batch through the same workspace
+    desc1 = kvq.make_desc("int4", 1, Hkv, D, L)
+    dc1 = kvq.DeviceCache(desc1, DEV)
+    kvq.kvq_quantize_prefill(desc1, dc1.c, k[:1].contiguous(), v[:1].contiguous(), 0, L)
+    out = decode(desc1, dc1, qs[0, :1].contiguous(), Hkv * G, [L], 0, 0.0, 9, ws=ws)
+    ref = attention.decode_attention(np16(qs[0, :1]), kh[:1], vh[:1], [L])
+    assert_attn_close(out.cpu().numpy(), ref, "batch 1 after batch 2")
