@@ -24,6 +24,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+# Sources of the dominant kernel (and its build flags): HBM-traffic counters recorded in
+# profiles/ are reported only while these files hash to the value recorded with them.
+KERNEL_SOURCES = ["int4_quantized_kv_amd/csrc/decode_mfma.hip", "int4_quantized_kv_amd/csrc/kvq_device.h",
+                  "int4_quantized_kv_amd/csrc/kvq_internal.h", "int4_quantized_kv_amd/csrc/kvq_arith.h",
+                  "int4_quantized_kv_amd/build.py"]
+TRAFFIC_FILE = "profiles/decode_int4_mfma_llama8b_ctx8k_b8_traffic.md"
 
 
 def parse():
@@ -38,6 +44,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="timed CPU work of the oracle baseline (whole (batch, kv head) units)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="time a plain 1 GiB device copy and a 1 GiB read-only reduction instead "
+                        "(attainable bandwidth; the known-size reference for the HBM counters)")
     return p.parse_args()
 
 
@@ -53,6 +62,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        calibrate_copy(args)
+        return
     import int4_quantized_kv_amd as kvq
     import synth
 
@@ -210,7 +222,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(),
             "bytes_per_launch": kern_bytes,
             "avg_launch_us": round(kern_ms * 1e3, 2),
         },
@@ -221,6 +233,61 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, L)
 
     print(json.dumps(result), flush=True)
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel from the rocprofv3 FETCH_SIZE and
+    WRITE_SIZE passes recorded in TRAFFIC_FILE (each scaled by the factor the same
+    counter shows on a copy of known size), or None if there is no record or the kernel
+    has changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        line = line.strip().strip("`")
+        if ":" in line and line.split(":", 1)[0] in ("source_sha256", "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            rec[k] = v.strip()
+    if rec.get("source_sha256") != kernel_source_hash() or "traffic_bytes_per_launch" not in rec:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def calibrate_copy(args):
+    """A plain device copy of 1 GiB (1 GiB read + 1 GiB written per launch) and a
+    read-only sum over 1 GiB, timed with events; one JSON line."""
+    import torch
+    n = 1 << 28                                   # fp32 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.float32, device="cuda:0")
+    res = {}
+    for name, fn in (("copy", lambda: dst.copy_(src)), ("sum", lambda: torch.sum(src, 0, out=acc))):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        moved = (2 if name == "copy" else 1) * n * 4
+        res[name] = {"bytes_read": n * 4, "bytes_written": n * 4 if name == "copy" else 4,
+                     "ms": round(ms, 4), "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
+    print(json.dumps({"calibration": res, "steps": args.steps}), flush=True)
 
 
 def cpu_baseline(w, seconds, L):
