@@ -141,7 +141,9 @@ def main():
         for _ in range(args.warmup):
             run()
         torch.cuda.synchronize()
-        if not torch.equal(layers[-1].out, eager_out):
+        # (tiles are shared out dynamically, so the fp32 sums may differ in their last
+        # bits from run to run; anything beyond rounding is an error)
+        if not torch.allclose(layers[-1].out, eager_out, rtol=1e-4, atol=1e-5):
             raise RuntimeError("graph replay differs from the eager result")
 
     # ---- timed region: exactly K steps, synchronized on both sides; the events are

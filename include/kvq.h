@@ -129,8 +129,8 @@ int32_t kvq_plan_splits(const kvq_cache_desc* desc, int32_t q_heads, int32_t spa
 
 /* Workspace bytes kvq_decode_attn / kvq_append_decode_attn need for these arguments
  * (num_splits = 0: the library's own plan for a longest span of min(max_len, window or
- * max_len)); 0 if invalid.  Equal to KVQ_WS_COUNTER_BYTES + B * q_heads *
- * (nsplit + 1) * (D + 2) * 4. */
+ * max_len)); 0 if invalid.  Equal to KVQ_WS_COUNTER_BYTES + B * q_heads * nsplit *
+ * (D + 2) * 4. */
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t q_heads,
                                   int32_t max_len, int32_t window, int32_t num_splits);
 
@@ -195,10 +195,9 @@ int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
  *   k_f16, v_f16: device, [B, Hkv, D] fp16, the new token's rows (position lens[b] - 1).
  * Every other argument, the workspace rule and the errors are those of kvq_decode_attn
  * (KVQ_ERR_ARG also for null k_f16 / v_f16).  For INT4 with head_dim 128 and V group
- * 128 the new row is quantized inside the attention kernel by the first split to finish
- * its share of the cache, which writes it to the cache and adds it to the softmax from
- * registers (one launch per step); other formats and shapes run the append kernel
- * first. */
+ * 128 the new row is quantized inside the attention kernel, which writes it to the
+ * cache and adds it to the softmax without reading it back (one launch per step); other
+ * formats and shapes run the append kernel first. */
 int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
                                const void* k_f16, const void* v_f16, const void* q_f16,
                                int32_t q_heads, const int32_t* lens, int32_t window,

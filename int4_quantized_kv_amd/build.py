@@ -29,6 +29,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators in ordinary VGPRs (no AGPR copies around the softmax rescale)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # atomics stay single-lane as written (the optimizer's wave-combining rewrite reads
+    # each result back at once, which waits for every transfer in flight)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
     "-Wno-unused-function",
 ]

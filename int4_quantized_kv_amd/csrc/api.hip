@@ -66,12 +66,13 @@ int32_t quant_common(const kvq_cache_desc* desc, const kvq_cache* cache, const v
   return launch_status(launch_quant_intq(desc->format, a, stream));
 }
 
-// Workspace: the split-arrival counters first (KVQ_WS_COUNTER_BYTES, zero between
-// calls), then nsplit + 1 partial slots (weighted V sums, then (max, sum) pairs) per
-// query head; the extra slot holds the fused append's new row.
+// Workspace: the split-arrival counters first (KVQ_WS_COUNTER_BYTES, [B, Hkv] uint32,
+// zero between calls), then nsplit partial slots per query head (weighted V sums
+// [B, Hq, nsplit, D], then (max, sum) pairs [B, Hq, nsplit, 2]).
 constexpr size_t partials_offset() { return KVQ_WS_COUNTER_BYTES; }
+constexpr int64_t max_units() { return KVQ_WS_COUNTER_BYTES / sizeof(uint32_t); }
 size_t partials_bytes(int32_t batch, int32_t q_heads, int32_t ns, int32_t head_dim) {
-  return (size_t)batch * q_heads * (ns + 1) * (head_dim + 2) * sizeof(float);
+  return (size_t)batch * q_heads * ns * (head_dim + 2) * sizeof(float);
 }
 
 // Longest attended span over the batch; KVQ_ERR_* (negative) if a length is invalid.
@@ -197,8 +198,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   if (q_heads % desc->kv_heads) return KVQ_ERR_ARG;
   const int32_t G = q_heads / desc->kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
-  if ((int64_t)desc->batch * desc->kv_heads > (int64_t)(KVQ_WS_COUNTER_BYTES / 4))
-    return KVQ_ERR_UNSUPPORTED;
+  if ((int64_t)desc->batch * desc->kv_heads > max_units()) return KVQ_ERR_UNSUPPORTED;
   const int32_t span = check_lens(desc, lens, window);
   if (span < 0) return span;
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(desc, q_heads, span);
@@ -215,7 +215,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   a.q = static_cast<const uint16_t*>(q_f16);
   a.counters = static_cast<uint32_t*>(workspace);
   a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + partials_offset());
-  a.ws_ml = a.ws_acc + (size_t)desc->batch * q_heads * (ns + 1) * desc->head_dim;
+  a.ws_ml = a.ws_acc + (size_t)desc->batch * q_heads * ns * desc->head_dim;
   a.out = out;
   a.B = desc->batch;
   a.Hkv = desc->kv_heads;

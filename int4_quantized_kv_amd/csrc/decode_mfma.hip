@@ -46,6 +46,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr int HD = 128;     // head_dim of this kernel
@@ -264,19 +265,67 @@ struct LaneOffs {
   int sv;       // V scales, rows 4j .. 4j+3 (half 0)
 };
 
+// The LDS reads of one tile for one lane: K codes (chunk j of row r, both halves), the
+// K and V scales of rows 4j .. 4j+3 (both halves) and the V dwords of rows 4j + i.
+struct TileData {
+  u32x4 k[2], sk[2], sv[2];
+  uint32_t v[2][4];
+};
+
+// All 14 reads are issued in one asm statement that ends by waiting for them.  Written
+// this way the compiler sees no LDS read here, so it does not add a wait for every
+// transfer in flight before the tile (it cannot tell which LDS bytes a global->LDS
+// transfer writes); the caller's vmcnt wait is what orders this tile's own transfers
+// before the reads.
+template <int NGK>
+__device__ __forceinline__ TileData read_tile(const uint8_t* lb, const LaneOffs& lo) {
+  using L = Slot<NGK>;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_vptr)lb;
+  const uint32_t ak = base + L::K_OFF + lo.k, ask = base + L::SK_OFF + lo.sk;
+  const uint32_t asv = base + L::SV_OFF + lo.sv;
+  const uint32_t av0 = base + L::V_OFF + lo.v[0], av1 = base + L::V_OFF + lo.v[1];
+  const uint32_t av2 = base + L::V_OFF + lo.v[2], av3 = base + L::V_OFF + lo.v[3];
+  TileData d;
+  asm volatile(
+      "ds_read_b128 %0, %14\n\t"
+      "ds_read_b128 %1, %14 offset:1024\n\t"
+      "ds_read_b128 %2, %15\n\t"
+      "ds_read_b128 %3, %15 offset:64\n\t"
+      "ds_read_b128 %4, %16\n\t"
+      "ds_read_b128 %5, %16 offset:64\n\t"
+      "ds_read_b32 %6, %17\n\t"
+      "ds_read_b32 %7, %18\n\t"
+      "ds_read_b32 %8, %19\n\t"
+      "ds_read_b32 %9, %20\n\t"
+      "ds_read_b32 %10, %17 offset:1024\n\t"
+      "ds_read_b32 %11, %18 offset:1024\n\t"
+      "ds_read_b32 %12, %19 offset:1024\n\t"
+      "ds_read_b32 %13, %20 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d.k[0]), "=&v"(d.k[1]), "=&v"(d.sk[0]), "=&v"(d.sk[1]), "=&v"(d.sv[0]),
+        "=&v"(d.sv[1]), "=&v"(d.v[0][0]), "=&v"(d.v[0][1]), "=&v"(d.v[0][2]),
+        "=&v"(d.v[0][3]), "=&v"(d.v[1][0]), "=&v"(d.v[1][1]), "=&v"(d.v[1][2]),
+        "=&v"(d.v[1][3])
+      : "v"(ak), "v"(ask), "v"(asv), "v"(av0), "v"(av1), "v"(av2), "v"(av3)
+      : "memory");
+  return d;
+}
+
 // State::m is the running maximum of the unscaled scores z = q . k; since the scale
 // (softmax scale * log2 e) is positive, p = 2^(scale * (z - m)).
-template <int G, int NGK, bool MASK>
+template <int G, int NGK>
 __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& lo, State& st,
                                              const half8 (&qb)[4], float qbias, int t0, int pe,
                                              int j, float qscale) {
-  using L = Slot<NGK>;
+  // positions at or past pe (only in a split's last tile) get score -inf
+  const bool mask = t0 + TILE > pe;
+  const TileData td = read_tile<NGK>(lb, lo);
   // ---- q.K: lane (r, j) gets rows 4j + i of half T for column r = (head, group)
   float z[2][4];
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
-    const uint4 kw = *reinterpret_cast<const uint4*>(lb + L::K_OFF + 1024 * T + lo.k);
-    const f4u sk = *reinterpret_cast<const f4u*>(lb + L::SK_OFF + 64 * T + lo.sk);
+    const u32x4 kw = td.k[T];
+    const floatx4 sk = __builtin_bit_cast(floatx4, td.sk[T]);
     const uint32_t kw4[4] = {kw.x, kw.y, kw.z, kw.w};
     floatx4 cg = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -289,7 +338,7 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
       // the NGK columns of a head are adjacent (column = head * NGK + group)
       if (NGK >= 2) s = add_xor1(s);
       if (NGK >= 4) s = add_xor2(s);
-      if (MASK) s = t0 + 16 * T + 4 * j + i < pe ? s : NEG_INF;
+      if (mask) s = t0 + 16 * T + 4 * j + i < pe ? s : NEG_INF;
       z[T][i] = s;
     }
   }
@@ -312,7 +361,7 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
   H8 phi, plo;
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
-    const f4u sv = *reinterpret_cast<const f4u*>(lb + L::SV_OFF + 64 * T + lo.sv);
+    const floatx4 sv = __builtin_bit_cast(floatx4, td.sv[T]);
 #pragma unroll
     for (int i = 0; i < 4; i += 2) {
       const float p0 = fast_exp2(__builtin_fmaf(z[T][i], qscale, -mq));
@@ -333,8 +382,8 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
 #pragma unroll
   for (int pr = 0; pr < 4; ++pr) {
     const int T = pr >> 1, i = 2 * (pr & 1);
-    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(lb + L::V_OFF + 1024 * T + lo.v[i]);
-    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(lb + L::V_OFF + 1024 * T + lo.v[i + 1]);
+    const uint32_t w0 = td.v[T][i];
+    const uint32_t w1 = td.v[T][i + 1];
     xlo[pr] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);   // w0.b0 w0.b1 w1.b0 w1.b1
     xhi[pr] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);   // w0.b2 w0.b3 w1.b2 w1.b3
   }
@@ -362,29 +411,21 @@ __device__ __forceinline__ float fetch(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The new token's row when the append is fused into the attention.  Wave 0 of every
-// workgroup copies the fp16 K and V rows and the G query rows into LDS (s_new) at the
-// start, so the workgroup that ends up doing the append reads them without a trip to
-// memory.  Lanes 0..15 of wave 0 quantize K dims 8c .. 8c+7 (c = lane), lanes 16..31
-// V, with the arithmetic of the append kernel; the codes and scales go to the cache for
-// later steps and the row enters this step's softmax as one extra partial, so no tile
-// has to read it back from memory.
-template <int G>
+// The new token's row when the append is fused into the attention.  Wave 0 of the
+// first workgroup of each (sequence, KV head) copies the fp16 K and V rows into LDS at
+// the start (the G query rows are staged by every wave anyway), quantizes them with
+// the arithmetic of the append kernel while its first tiles are in flight (lanes 0..15:
+// K dims 8c .. 8c+7, c = lane; lanes 16..31: V), and keeps the result in LDS: the row
+// enters this step's softmax as one more entry of the workgroup's combine (no tile
+// reads it back from memory), and its codes and scales are written to the cache at the
+// end.
 struct NewLds {
-  uint16_t k[HD], v[HD], q[G][HD];
+  uint16_t k[HD], v[HD];  // the new token's fp16 K and V rows (staged by transfers)
+  float m[8];          // the new row's score per head (base-2 units)
+  float o[HD];         // its dequantized V row
+  uint32_t w[32];      // packed codes of lanes 0..31 (K dims 8c.., then V dims 8c..)
+  float sc[32];        // the group scale each of those lanes holds
 };
-
-template <int G>
-__device__ __forceinline__ void stage_new_row(const DecodeArgs& a, int b, int kvh, NewLds<G>* s,
-                                              int lane) {
-  const size_t r = ((size_t)b * a.Hkv + kvh) * HD;
-  uint8_t* base = reinterpret_cast<uint8_t*>(s);
-  dma4(a.k_new + r + 2 * lane, base);
-  dma4(a.v_new + r + 2 * lane, base + 2 * HD);
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    dma4(a.q + ((size_t)b * a.Hq + kvh * G + h) * HD + 2 * lane, base + (2 + h) * 2 * HD);
-}
 
 struct NewRow {
   float z[8];     // unscaled score per query head (K lanes)
@@ -393,14 +434,25 @@ struct NewRow {
   float sc;       // the group scale of this lane
 };
 
+__device__ __forceinline__ void f16x8_to_f32(const u32x4& r, float x[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+    x[2 * i] = (float)h.x;
+    x[2 * i + 1] = (float)h.y;
+  }
+}
+
 template <int G, int NGK>
-__device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds<G>* s, int lane) {
+__device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds* s,
+                                             const uint8_t* qrows, int lane) {
   NewRow nr;
   const bool isv = lane >= 16;
   const int c = lane & 15;
   const int lpg = (isv ? HD : a.gk) >> 3;               // lanes per quantization group
   float x[8];
-  load8_f16((isv ? s->v : s->k) + 8 * c, x);
+  f16x8_to_f32(*reinterpret_cast<const u32x4*>((isv ? s->v : s->k) + 8 * c), x);
   float am = 0.0f;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) am = fmaxf(am, fabsf(x[jj]));
@@ -423,7 +475,7 @@ __device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds<G
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float qv[8];
-    load8_f16(s->q[h] + 8 * c, qv);
+    f16x8_to_f32(*reinterpret_cast<const u32x4*>(qrows + h * 2 * HD + 16 * c), qv);
     float d = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) d = __builtin_fmaf(qv[jj], code[jj], d);
@@ -435,19 +487,21 @@ __device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds<G
   return nr;
 }
 
-// Write the lane's codes and scale of the new row to cache row `row`.
+// Write the new row's codes and scales (kept in LDS by lanes 0..31) to cache row `row`.
 template <int NGK>
-__device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewRow& nr, size_t row,
+__device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewLds* s, size_t row,
                                               int lane) {
   const bool isv = lane >= 16;
   const int c = lane & 15;
+  const uint32_t w = s->w[lane];
+  const float sc = s->sc[lane];
   if (isv) {
-    static_cast<uint32_t*>(const_cast<void*>(a.v_codes))[row * (HD / 8) + c] = nr.w;
-    if (c == 0) const_cast<float*>(a.v_scales)[row] = nr.sc;
+    static_cast<uint32_t*>(const_cast<void*>(a.v_codes))[row * (HD / 8) + c] = w;
+    if (c == 0) const_cast<float*>(a.v_scales)[row] = sc;
   } else {
     const int lpg = a.gk >> 3;
-    static_cast<uint32_t*>(const_cast<void*>(a.k_codes))[row * (HD / 8) + c] = nr.w;
-    if ((c & (lpg - 1)) == 0) const_cast<float*>(a.k_scales)[row * NGK + c / lpg] = nr.sc;
+    static_cast<uint32_t*>(const_cast<void*>(a.k_codes))[row * (HD / 8) + c] = w;
+    if ((c & (lpg - 1)) == 0) const_cast<float*>(a.k_scales)[row * NGK + c / lpg] = sc;
   }
 }
 
@@ -456,7 +510,7 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   using L = Slot<NGK>;
   constexpr int DMA = L::DMA;
   __shared__ __attribute__((aligned(16))) uint8_t smem[WAVES * NB * L::BYTES];
-  __shared__ __attribute__((aligned(16))) NewLds<G> s_new;
+  __shared__ __attribute__((aligned(16))) NewLds s_new;
   __shared__ int s_last;
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -467,67 +521,43 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   // q.K column r = (head r / NGK, group r % NGK); junk columns beyond G * NGK
   const int qhead = (r / NGK) % G;
   const int qgrp = r % NGK;
+  const int unit = b * a.Hkv + kvh;
   const int len = a.lens[b];
   const int lo_pos = a.window > 0 ? max(0, len - a.window) : 0;
-  const int span = len - lo_pos;
-  const int chunk = (span + a.nsplit - 1) / a.nsplit;
-  const int ps = min(len, lo_pos + sp * chunk);
-  const int pe = min(len, ps + chunk);
-  // with the append fused, the split holding position len - 1 takes that row from the
-  // new token instead of from a tile
-  const bool appending = a.k_new != nullptr && ps < len && pe == len;
-  const int pt = appending ? len - 1 : pe;     // tiles cover [ps, pt)
+  // with the append fused, position len - 1 comes from the new token, not from a tile
+  const bool fused = a.k_new != nullptr;
+  const bool appender = fused && sp == 0;
+  const int pt = fused ? len - 1 : len;                 // tiles cover [lo_pos, pt)
 
-  // ---- start the first two tiles' transfers before anything else
-  const size_t row0 = ((size_t)b * a.Hkv + kvh) * a.cap;
+  // ---- tile schedule: split sp covers positions [ps, pe) of [lo_pos, pt); its 4 waves
+  // take interleaved tiles of 32 positions (wave w: tiles w, w + 4, ...).  (Sharing the
+  // tiles of a (sequence, KV head) dynamically through a device-scope counter was
+  // measured 4x slower: each claim is a round trip to the memory side behind the
+  // streaming traffic.)
+  const int span = pt - lo_pos;
+  const int chunk = span > 0 ? (span + a.nsplit - 1) / a.nsplit : 0;
+  const int ps = min(pt, lo_pos + sp * chunk);
+  const int pe = min(pt, ps + chunk);
   constexpr int STRIDE = TILE * WAVES;
   const int tfirst = ps + TILE * wave;
-  const int ntiles = tfirst < pt ? (pt - tfirst + STRIDE - 1) / STRIDE : 0;
+  const int ntiles = tfirst < pe ? (pe - tfirst + STRIDE - 1) / STRIDE : 0;
+  const size_t row0 = (size_t)unit * a.cap;
   uint8_t* ring = smem + wave * NB * L::BYTES;
   const DmaOffs dof = dma_offsets<NGK>(lane);
-  // (issued before the tiles: the loop's in-order transfer waits then cover them too)
-  if (a.k_new != nullptr && wave == 0) stage_new_row<G>(a, b, kvh, &s_new, lane);
-  if (ntiles > 0) issue_tile<NGK>(a, row0, tfirst, pt, ring, lane, dof);
-  if (ntiles > 1) issue_tile<NGK>(a, row0, tfirst + STRIDE, pt, ring + L::BYTES, lane, dof);
 
-  // q as the B operand of dim chunk c: lane quarter j holds dims 8(4j + c) + {p, p + 4}
-  // in slots {2p, 2p + 1} (the order unpack_word_u produces) when quarter j lies in the
-  // column's K group, zeros otherwise.
-  half8 qb[4];
-  {
-    constexpr int QPG = 4 / NGK;   // lane quarters (32 dims) per K group
-    const bool live = r < G * NGK && j / QPG == qgrp;
-    const uint16_t* qh = a.q + (size_t)(b * a.Hq + kvh * G + qhead) * HD;
+  // fp16 inputs, copied into LDS by transfers before the first tile: the G query rows
+  // into ring slot 2 (free until step 0 starts tile 2 there, after reading them) and,
+  // in the appending wave, the new K/V rows into s_new.  (Loading them into registers
+  // inside the loop would make the compiler wait for them wherever it reuses those
+  // registers; a load before the loop would make it wait ahead of every transfer.)
+  const bool app_wave = appender && wave == 0;
+  uint8_t* qstage = ring + 2 * L::BYTES;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(qh + 8 * (4 * j + c));
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-      H8 o;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        // element p is half (p&1) of word p/2; element p+4 is half (p&1) of word 2+p/2
-        const uint32_t lo16 = (w[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
-        const uint32_t hi16 = (w[2 + (p >> 1)] >> (16 * (p & 1))) & 0xFFFFu;
-        o.u[p] = live ? (lo16 | (hi16 << 16)) : 0u;
-      }
-      qb[c] = o.h;
-    }
-  }
-  // -8 * (sum of the q entries this column carries), summed over the 4 lanes j
-  float qbias;
-  {
-    float qs = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      H8 o;
-      o.h = qb[c];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const f16x2 h2 = __builtin_bit_cast(f16x2, o.u[p]);
-        qs += (float)h2.x + (float)h2.y;
-      }
-    }
-    qbias = -8.0f * sum_over_j(qs);
+  for (int h = 0; h < G; ++h)
+    dma4(a.q + ((size_t)b * a.Hq + kvh * G + h) * HD + 2 * lane, qstage + h * 2 * HD);
+  if (app_wave) {
+    dma4(a.k_new + (size_t)unit * HD + 2 * lane, reinterpret_cast<uint8_t*>(s_new.k));
+    dma4(a.v_new + (size_t)unit * HD + 2 * lane, reinterpret_cast<uint8_t*>(s_new.v));
   }
 
   LaneOffs lo;
@@ -548,26 +578,75 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   for (int e = 0; e < 8; ++e) st.oacc[e] = (floatx4){0.f, 0.f, 0.f, 0.f};
   st.m = NEG_INF;
   st.l = 0.0f;
+  half8 qb[4];
+  float qbias = 0.0f;
+
+  // The pipeline: tiles 0 and 1 start before the loop; step k starts tile k + 2 into
+  // slot (k + 2) % NB (while there is one) and processes tile k from slot k % NB, so two
+  // tiles stay in flight behind the one being processed.
+  if (ntiles > 0) issue_tile<NGK>(a, row0, tfirst, pe, ring, lane, dof);
+  if (ntiles > 1) issue_tile<NGK>(a, row0, tfirst + STRIDE, pe, ring + L::BYTES, lane, dof);
+
+  // q into MFMA layout (and the appending wave's quantization of the new row) while
+  // tiles 0 and 1 are in flight
+  u32x4 qraw[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    qraw[c] = *reinterpret_cast<const u32x4*>(qstage + qhead * 2 * HD + 16 * (4 * j + c));
+  // q as the B operand of dim chunk c: lane quarter j holds dims 8(4j + c) + {p, p+4}
+  // in slots {2p, 2p + 1} (the order unpack_word_u produces) when quarter j lies in
+  // the column's K group, zeros otherwise; qbias = -8 * (sum of those q entries)
+  constexpr int QPG = 4 / NGK;   // lane quarters (32 dims) per K group
+  const bool live = r < G * NGK && j / QPG == qgrp;
+  float qs = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t w[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+    H8 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      // element p is half (p&1) of word p/2; element p+4 is half (p&1) of word 2+p/2
+      const uint32_t lo16 = (w[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
+      const uint32_t hi16 = (w[2 + (p >> 1)] >> (16 * (p & 1))) & 0xFFFFu;
+      o.u[p] = live ? (lo16 | (hi16 << 16)) : 0u;
+      const f16x2 h2 = __builtin_bit_cast(f16x2, o.u[p]);
+      qs += (float)h2.x + (float)h2.y;
+    }
+    qb[c] = o.h;
+  }
+  qbias = -8.0f * sum_over_j(qs);
+  if (app_wave && lane < 32) {
+    const NewRow nr = append_row<G, NGK>(a, &s_new, qstage, lane);
+    s_new.w[lane] = nr.w;
+    s_new.sc[lane] = nr.sc;
+    if (lane >= 16) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) s_new.o[8 * (lane - 16) + jj] = nr.v[jj];
+    } else if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) s_new.m[h] = nr.z[h] * a.qscale;
+    }
+  }
 
   for (int k = 0; k < ntiles; ++k) {
-    const int t0 = tfirst + k * STRIDE;
     if (k + 2 < ntiles) {
-      issue_tile<NGK>(a, row0, t0 + 2 * STRIDE, pt, ring + ((k + 2) % NB) * L::BYTES, lane, dof);
-      wait_vmcnt<2 * DMA>();
+      issue_tile<NGK>(a, row0, tfirst + (k + 2) * STRIDE, pe, ring + ((k + 2) % NB) * L::BYTES,
+                      lane, dof);
+      wait_vmcnt<2 * DMA>();   // after tile k: the transfers of tiles k + 1 and k + 2
     } else if (k + 1 < ntiles) {
       wait_vmcnt<DMA>();
     } else {
       wait_vmcnt<0>();
     }
-    const uint8_t* lb = ring + (k % NB) * L::BYTES;
-    if (t0 + TILE <= pt)
-      process_tile<G, NGK, false>(lb, lo, st, qb, qbias, t0, pt, j, a.qscale);
-    else
-      process_tile<G, NGK, true>(lb, lo, st, qb, qbias, t0, pt, j, a.qscale);
+    process_tile<G, NGK>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, tfirst + k * STRIDE, pe,
+                         j, a.qscale);
   }
+  wait_vmcnt<0>();   // (also the q staging, when this wave had no tile)
+  if (app_wave && lane < 32) store_new_row<NGK>(a, &s_new, row0 + (size_t)((len - 1) % a.cap), lane);
 
-  // ---- combine the 4 waves through LDS, reusing the ring: lane (r, j) holds
-  // O[column r][8(4j + i) + e] in oacc[e][i]; a head sits in column head * NGK
+  // ---- combine the 4 waves (and, in the appending workgroup, the new row) through
+  // LDS, reusing the ring: lane (r, j) holds O[column r][8(4j + i) + e] in oacc[e][i];
+  // a head sits in column head * NGK
   __syncthreads();
   float* s_o = reinterpret_cast<float*>(smem);                 // [WAVES][G][HD]
   float* s_m = s_o + WAVES * G * HD;                            // [WAVES][G]
@@ -585,11 +664,12 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  const int nps = a.nsplit + 1;                         // partial slots per query head
-  const size_t pbase = (size_t)(b * a.Hq + kvh * G) * nps;   // slot of (head 0, split 0)
+  const int nps = a.nsplit;                                     // partials per query head
+  const size_t pbase = (size_t)(b * a.Hq + kvh * G) * nps;     // slot of (head 0, split 0)
   for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
     const int h = idx / HD, d = idx % HD;
-    float M = NEG_INF;
+    const float mn = appender ? s_new.m[h] : NEG_INF;
+    float M = mn;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w * G + h]);
     float Acc = 0.0f, Lsum = 0.0f;
@@ -602,6 +682,11 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
           Acc = __builtin_fmaf(s_o[(w * G + h) * HD + d], f, Acc);
           Lsum = __builtin_fmaf(s_l[w * G + h], f, Lsum);
         }
+      }
+      if (mn != NEG_INF) {
+        const float f = fast_exp2(mn - M);
+        Acc = __builtin_fmaf(s_new.o[d], f, Acc);
+        Lsum += f;
       }
     }
     const size_t o = pbase + (size_t)h * nps + sp;
@@ -617,53 +702,19 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   // barrier, so when the counting thread bumps the (device-scope) arrival counter the
   // whole partial is visible.  This avoids a release fence, which on this chip writes
   // back the XCD's whole L2 and costs microseconds per workgroup.
-  uint32_t* cnt = a.counters + b * a.Hkv + kvh;
+  uint32_t* cnt = a.counters + unit;
   wait_vmcnt<0>();
   __syncthreads();
   if (threadIdx.x == 0)
     s_last = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  int arrived = s_last;
-  const bool fused = a.k_new != nullptr;
-  if (fused && arrived == 0) {
-    // The first workgroup to arrive (the one with the most slack) quantizes the new
-    // token's row and publishes that one position as an extra partial (slot nsplit:
-    // max = its score, sum = 1, value = its dequantized V row), counts itself a second
-    // time, then writes the row to the cache (nothing in this launch reads it there).
-    // Every transfer of wave 0, s_new's included, completed before the barrier above.
-    NewRow nr;
-    if (wave == 0 && lane < 32) {
-      nr = append_row<G, NGK>(a, &s_new, lane);
-      const size_t o = pbase + a.nsplit;
-      if (lane >= 16) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            publish(a.ws_acc + (o + (size_t)h * nps) * HD + 8 * (lane - 16) + jj, nr.v[jj]);
-      } else if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          publish(a.ws_ml + 2 * (o + (size_t)h * nps), nr.z[h] * a.qscale);
-          publish(a.ws_ml + 2 * (o + (size_t)h * nps) + 1, 1.0f);
-        }
-      }
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (threadIdx.x == 0)
-      s_last = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (wave == 0 && lane < 32) store_new_row<NGK>(a, nr, row0 + (size_t)((len - 1) % a.cap), lane);
-    __syncthreads();
-    arrived = s_last;
-  }
-  const int np = fused ? nps : a.nsplit;                // partials to merge
-  if (arrived != np - 1) return;
+  const int np = a.nsplit;                               // partials to merge
+  if (s_last != np - 1) return;
 
   // ---- the last arrival merges the np partials of its G heads with the log-sum-exp
-  // rule (device-scope loads: the partials come from other XCDs) and resets the counter.
-  // Each thread first issues the loads of its outputs' first PF partials, so their
-  // latency overlaps the maxima's.
+  // rule (device-scope loads: the partials come from other XCDs) and resets the arrival
+  // counter.  Each thread first issues the loads of its outputs' first PF partials, so
+  // their latency overlaps the maxima's.
   constexpr int PF = 8;
   constexpr int OPT = (G * HD + 255) / 256;             // outputs per thread
   float pre[OPT][PF];

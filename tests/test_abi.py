@@ -113,7 +113,7 @@ def test_error_paths_enqueue_nothing():
     # decode: Hq % Hkv, unsupported group, len 0, len > capacity without window,
     # window > capacity with len > capacity, too-small / missing workspace
     ws = kvq.kvq_decode_workspace_bytes(d, 8, 64)
-    assert ws == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * (kvq.kvq_plan_splits(d, 8, 64) + 1) * 130 * 4
+    assert ws == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * kvq.kvq_plan_splits(d, 8, 64) * 130 * 4
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 6, [10, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_decode_attn, d, c, FAKE, 64, [10, 10], 0, 0.0, 0, FAKE, FAKE, 1 << 30, 0)
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [10, 0], 0, 0.0, 0, FAKE, FAKE, ws, 0)
