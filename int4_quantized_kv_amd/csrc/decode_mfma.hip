@@ -51,7 +51,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr int HD = 128;     // head_dim of this kernel
 constexpr int TILE = 32;    // positions per wave iteration
-constexpr int WAVES = 4;
+constexpr int WAVES = 8;    // one workgroup per CU (see the tile schedule below)
+constexpr int NT = WAVES * 64;
 
 union H8 {
   half8 h;
@@ -264,6 +265,19 @@ struct LaneOffs {
   int sk;       // K scales of group g, rows 4j .. 4j+3 (half 0)
   int sv;       // V scales, rows 4j .. 4j+3 (half 0)
 };
+
+// Next value of a workgroup's LDS tile counter (lane 0 adds, the wave reads its result).
+// Written in asm that waits for its own result, for the same reason as read_tile.
+__device__ __forceinline__ uint32_t lds_claim(uint32_t* ctr, int lane) {
+  uint32_t old = 0;
+  const uint32_t addr = (uint32_t)(uintptr_t)(lds_vptr)ctr;
+  if (lane == 0)
+    asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(old)
+                 : "v"(addr), "v"(1u)
+                 : "memory");
+  return __builtin_amdgcn_readfirstlane(old);
+}
 
 // The LDS reads of one tile for one lane: K codes (chunk j of row r, both halves), the
 // K and V scales of rows 4j .. 4j+3 (both halves) and the V dwords of rows 4j + i.
@@ -506,12 +520,13 @@ __device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewLds*
 }
 
 template <int G, int NGK>
-__global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   using L = Slot<NGK>;
   constexpr int DMA = L::DMA;
   __shared__ __attribute__((aligned(16))) uint8_t smem[WAVES * NB * L::BYTES];
   __shared__ __attribute__((aligned(16))) NewLds s_new;
   __shared__ int s_last;
+  __shared__ uint32_t s_claim;
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -529,21 +544,21 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   const bool appender = fused && sp == 0;
   const int pt = fused ? len - 1 : len;                 // tiles cover [lo_pos, pt)
 
-  // ---- tile schedule: split sp covers positions [ps, pe) of [lo_pos, pt); its 4 waves
-  // take interleaved tiles of 32 positions (wave w: tiles w, w + 4, ...).  (Sharing the
-  // tiles of a (sequence, KV head) dynamically through a device-scope counter was
-  // measured 4x slower: each claim is a round trip to the memory side behind the
-  // streaming traffic.)
+  // ---- tile schedule: split sp covers positions [ps, pe) of [lo_pos, pt), nts tiles
+  // of 32 positions.  Wave w starts with tiles w and w + WAVES; every further tile is
+  // claimed from the workgroup's LDS counter, so faster waves take more tiles.  One
+  // workgroup of 8 waves per CU: with two workgroups of 4 waves sharing a CU, one of the
+  // pair was measured to lag the other by up to a third of the kernel, a split no LDS
+  // counter can rebalance.
   const int span = pt - lo_pos;
   const int chunk = span > 0 ? (span + a.nsplit - 1) / a.nsplit : 0;
   const int ps = min(pt, lo_pos + sp * chunk);
   const int pe = min(pt, ps + chunk);
-  constexpr int STRIDE = TILE * WAVES;
-  const int tfirst = ps + TILE * wave;
-  const int ntiles = tfirst < pe ? (pe - tfirst + STRIDE - 1) / STRIDE : 0;
+  const int nts = (pe - ps + TILE - 1) / TILE;
   const size_t row0 = (size_t)unit * a.cap;
   uint8_t* ring = smem + wave * NB * L::BYTES;
   const DmaOffs dof = dma_offsets<NGK>(lane);
+  if (threadIdx.x == 0) s_claim = 0;   // ordered before the first claim by a barrier
 
   // fp16 inputs, copied into LDS by transfers before the first tile: the G query rows
   // into ring slot 2 (free until step 0 starts tile 2 there, after reading them) and,
@@ -581,11 +596,16 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   half8 qb[4];
   float qbias = 0.0f;
 
-  // The pipeline: tiles 0 and 1 start before the loop; step k starts tile k + 2 into
-  // slot (k + 2) % NB (while there is one) and processes tile k from slot k % NB, so two
-  // tiles stay in flight behind the one being processed.
-  if (ntiles > 0) issue_tile<NGK>(a, row0, tfirst, pe, ring, lane, dof);
-  if (ntiles > 1) issue_tile<NGK>(a, row0, tfirst + STRIDE, pe, ring + L::BYTES, lane, dof);
+  // The pipeline: the first two tiles start before the loop; step k claims tile k + 2,
+  // starts it into slot (k + 2) % NB and processes tile k from slot k % NB, so two tiles
+  // stay in flight behind the one being processed.  `cur` / `nxt` are the tiles of
+  // steps k and k + 1 (NONE past the end; claims only grow, so once a claim is past the
+  // end every later one is too).
+  constexpr int NONE = -1;
+  int cur = wave < nts ? wave : NONE;
+  int nxt = wave + WAVES < nts ? wave + WAVES : NONE;
+  if (cur != NONE) issue_tile<NGK>(a, row0, ps + TILE * cur, pe, ring, lane, dof);
+  if (nxt != NONE) issue_tile<NGK>(a, row0, ps + TILE * nxt, pe, ring + L::BYTES, lane, dof);
 
   // q into MFMA layout (and the appending wave's quantization of the new row) while
   // tiles 0 and 1 are in flight
@@ -628,23 +648,30 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  for (int k = 0; k < ntiles; ++k) {
-    if (k + 2 < ntiles) {
-      issue_tile<NGK>(a, row0, tfirst + (k + 2) * STRIDE, pe, ring + ((k + 2) % NB) * L::BYTES,
-                      lane, dof);
+  __syncthreads();   // s_claim is zero
+  for (int k = 0; cur != NONE; ++k) {
+    int nn = NONE;
+    if (nxt != NONE) {
+      const int id = 2 * WAVES + (int)lds_claim(&s_claim, lane);
+      nn = id < nts ? id : NONE;
+    }
+    if (nn != NONE) {
+      issue_tile<NGK>(a, row0, ps + TILE * nn, pe, ring + ((k + 2) % NB) * L::BYTES, lane, dof);
       wait_vmcnt<2 * DMA>();   // after tile k: the transfers of tiles k + 1 and k + 2
-    } else if (k + 1 < ntiles) {
+    } else if (nxt != NONE) {
       wait_vmcnt<DMA>();
     } else {
       wait_vmcnt<0>();
     }
-    process_tile<G, NGK>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, tfirst + k * STRIDE, pe,
-                         j, a.qscale);
+    process_tile<G, NGK>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, ps + TILE * cur, pe, j,
+                         a.qscale);
+    cur = nxt;
+    nxt = nn;
   }
   wait_vmcnt<0>();   // (also the q staging, when this wave had no tile)
   if (app_wave && lane < 32) store_new_row<NGK>(a, &s_new, row0 + (size_t)((len - 1) % a.cap), lane);
 
-  // ---- combine the 4 waves (and, in the appending workgroup, the new row) through
+  // ---- combine the waves (and, in the appending workgroup, the new row) through
   // LDS, reusing the ring: lane (r, j) holds O[column r][8(4j + i) + e] in oacc[e][i];
   // a head sits in column head * NGK
   __syncthreads();
@@ -666,7 +693,7 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   __syncthreads();
   const int nps = a.nsplit;                                     // partials per query head
   const size_t pbase = (size_t)(b * a.Hq + kvh * G) * nps;     // slot of (head 0, split 0)
-  for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * HD; idx += NT) {
     const int h = idx / HD, d = idx % HD;
     const float mn = appender ? s_new.m[h] : NEG_INF;
     float M = mn;
@@ -716,11 +743,11 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   // counter.  Each thread first issues the loads of its outputs' first PF partials, so
   // their latency overlaps the maxima's.
   constexpr int PF = 8;
-  constexpr int OPT = (G * HD + 255) / 256;             // outputs per thread
+  constexpr int OPT = (G * HD + NT - 1) / NT;           // outputs per thread
   float pre[OPT][PF];
 #pragma unroll
   for (int u = 0; u < OPT; ++u) {
-    const int idx = threadIdx.x + 256 * u;
+    const int idx = threadIdx.x + NT * u;
     const int h = idx / HD, d = idx % HD;
 #pragma unroll
     for (int sI = 0; sI < PF; ++sI)
@@ -729,7 +756,7 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   }
   float* s_w = reinterpret_cast<float*>(smem);          // [G][np] split weights
   float* s_L = s_w + G * np;                            // [G]
-  for (int idx = threadIdx.x; idx < G * np; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * np; idx += NT) {
     const int h = idx / np, sI = idx % np;
     s_w[idx] = fetch(a.ws_ml + 2 * (pbase + (size_t)h * nps + sI));
   }
@@ -754,7 +781,7 @@ __global__ void __launch_bounds__(256) decode_int4_mfma_kernel(DecodeArgs a) {
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < OPT; ++u) {
-    const int idx = threadIdx.x + 256 * u;
+    const int idx = threadIdx.x + NT * u;
     if (idx < G * HD) {
       const int h = idx / HD, d = idx % HD;
       float A = 0.0f;
@@ -774,10 +801,10 @@ template <int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   switch (HD / a.gk) {
-    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1>, grid, dim3(256), a, s);
-    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2>, grid, dim3(256), a, s);
+    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1>, grid, dim3(NT), a, s);
+    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2>, grid, dim3(NT), a, s);
     case 4:
-      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4>, grid, dim3(256), a, s);
+      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4>, grid, dim3(NT), a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -793,8 +820,8 @@ bool mfma_int4_eligible(int32_t head_dim, int32_t group_k, int32_t group_v, int3
 }
 
 int32_t plan_splits_mfma(int32_t units, int32_t span) {
-  const int32_t target_wg = 512;        // x 4 waves = 8 waves per CU on 256 CUs
-  const int32_t min_rows = 512;         // >= 4 tiles per wave
+  const int32_t target_wg = 256;        // one 8-wave workgroup per CU on 256 CUs
+  const int32_t min_rows = 1024;        // >= 4 tiles per wave
   int32_t n = (target_wg + units - 1) / units;
   const int32_t by_span = (span + min_rows - 1) / min_rows;
   if (n > by_span) n = by_span;

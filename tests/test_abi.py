@@ -145,7 +145,9 @@ def test_split_plan():
     n2 = kvq.kvq_plan_splits(d2, 32, 8193)
     assert 1 <= n2 <= 64
     d5 = kvq.make_desc("int4", 1, 8, 128, 131072)
-    assert kvq.kvq_plan_splits(d5, 32, 131072) >= 64     # 8 natural units need splitting
+    # only 8 natural (batch, kv head) units: the splits must give every one of the 256
+    # CUs a workgroup
+    assert 8 * kvq.kvq_plan_splits(d5, 32, 131072) >= 256
     assert kvq.kvq_plan_splits(d5, 32, 1) == 1
     assert kvq.kvq_plan_splits(d5, 31, 100) == 0
 
