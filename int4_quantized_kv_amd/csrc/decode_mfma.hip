@@ -59,31 +59,43 @@ union H8 {
   uint32_t u[4];
 };
 
-// fp16 pair (1024 + a, 1024 + b) -> (a - 8, b - 8), exact.
-__device__ __forceinline__ uint32_t sub1032(uint32_t x) {
+// Nibble pairs -> MFMA operands.  A dword holds two 16-bit halves of four
+// two's-complement nibbles each (nibble p at bits 4p .. 4p+3 of a half).  Nibbles 0 and
+// 1 of both halves are taken in place and nibbles 2 and 3 after one shift by 8, so each
+// dword costs one shift.  A nibble taken at bits 4..7 lands in the fp16 encoding 16
+// times larger than one at bits 0..3; the caller compensates with exact powers of two
+// (q scaled by 1/16 in those MFMA slots for K, the V accumulators of those dims by
+// 1/16 at the end).  In every bitop3, the immediate 0x6A is the truth table
+// f(0xF0, 0xCC, 0xAA) of f(a, b, c) = (a & b) ^ c: keep the nibble, flip its sign bit
+// (u = q + 8) and set the bits of c outside the nibble.
+
+// V: (1024 + u) or (1024 + 16 u) as fp16 (exponent bits set by c), then a packed
+// subtract of 1032 (or 1152) leaves q (or 16 q) exactly.
+__device__ __forceinline__ uint32_t pk_sub_f16(uint32_t x, float k) {
   f16x2 v = __builtin_bit_cast(f16x2, x);
-  const f16x2 k = {(_Float16)1032.0f, (_Float16)1032.0f};
-  v = v - k;
+  const f16x2 kk = {(_Float16)k, (_Float16)k};
+  v = v - kk;
   return __builtin_bit_cast(uint32_t, v);
 }
-
-// Nibble pair -> fp16 pair: for x holding two's-complement nibbles at bits 0..3 and
-// 16..19, (x & 0x000F000F) ^ 0x64086408 flips the nibble sign bit (u = q + 8) and sets
-// the fp16 exponent of 1024, i.e. the fp16 pair (1024 + u, 1024 + u'); one v_bitop3.
-// The immediate is the truth table f(0xF0, 0xCC, 0xAA) of f(a, b, c) = (a & b) ^ c.
-__device__ __forceinline__ uint32_t nib_pair_f16(uint32_t x) {
-  return sub1032(__builtin_amdgcn_bitop3_b32(x, 0x000F000Fu, 0x64086408u, 0x6A));
+template <int P>   // nibble P (0..3) of both halves of x
+__device__ __forceinline__ uint32_t v_pair_f16(uint32_t x, uint32_t x8) {
+  if (P == 0) return pk_sub_f16(__builtin_amdgcn_bitop3_b32(x, 0x000F000Fu, 0x64086408u, 0x6A), 1032.0f);
+  if (P == 1) return pk_sub_f16(__builtin_amdgcn_bitop3_b32(x, 0x00F000F0u, 0x64806480u, 0x6A), 1152.0f);
+  if (P == 2) return pk_sub_f16(__builtin_amdgcn_bitop3_b32(x8, 0x000F000Fu, 0x64086408u, 0x6A), 1032.0f);
+  return pk_sub_f16(__builtin_amdgcn_bitop3_b32(x8, 0x00F000F0u, 0x64806480u, 0x6A), 1152.0f);
 }
 
-// Eight two's-complement nibbles of `w` as an MFMA operand holding u * 2^-24 (u = q + 8,
-// fp16 subnormals, which the matrix cores take exactly): slot 2p = nibble p, slot
-// 2p + 1 = nibble p + 4.  One v_bitop3 (mask, then flip the sign bit) per pair; the
-// + 8 offset is removed after the MFMA: sum q_k (u_k - 8) = 2^24 C - 8 sum q_k.
+// K: the eight nibbles of `w` as fp16 subnormals u * 2^-24 (slots 0, 1, 4, 5) or
+// 16 u * 2^-24 (slots 2, 3, 6, 7), which the matrix cores take exactly; slot 2p holds
+// nibble p of the low half, slot 2p + 1 nibble p of the high half.  The + 8 offset is
+// removed after the MFMA: sum q_k (u_k - 8) = 2^24 C - 8 sum q_k.
 __device__ __forceinline__ half8 unpack_word_u(uint32_t w) {
   H8 r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-    r.u[p] = __builtin_amdgcn_bitop3_b32(w >> (4 * p), 0x000F000Fu, 0x00080008u, 0x6A);
+  const uint32_t w8 = w >> 8;
+  r.u[0] = __builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x00080008u, 0x6A);
+  r.u[1] = __builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, 0x00800080u, 0x6A);
+  r.u[2] = __builtin_amdgcn_bitop3_b32(w8, 0x000F000Fu, 0x00080008u, 0x6A);
+  r.u[3] = __builtin_amdgcn_bitop3_b32(w8, 0x00F000F0u, 0x00800080u, 0x6A);
   return r.h;
 }
 
@@ -327,12 +339,11 @@ __device__ __forceinline__ TileData read_tile(const uint8_t* lb, const LaneOffs&
 
 // State::m is the running maximum of the unscaled scores z = q . k; since the scale
 // (softmax scale * log2 e) is positive, p = 2^(scale * (z - m)).
-template <int G, int NGK>
+// MASK: the tile reaches past pe (a split's last tile); those positions get score -inf.
+template <int G, int NGK, bool MASK>
 __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& lo, State& st,
                                              const half8 (&qb)[4], float qbias, int t0, int pe,
                                              int j, float qscale) {
-  // positions at or past pe (only in a split's last tile) get score -inf
-  const bool mask = t0 + TILE > pe;
   const TileData td = read_tile<NGK>(lb, lo);
   // ---- q.K: lane (r, j) gets rows 4j + i of half T for column r = (head, group)
   float z[2][4];
@@ -352,7 +363,7 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
       // the NGK columns of a head are adjacent (column = head * NGK + group)
       if (NGK >= 2) s = add_xor1(s);
       if (NGK >= 4) s = add_xor2(s);
-      if (mask) s = t0 + 16 * T + 4 * j + i < pe ? s : NEG_INF;
+      if (MASK) s = t0 + 16 * T + 4 * j + i < pe ? s : NEG_INF;
       z[T][i] = s;
     }
   }
@@ -404,13 +415,26 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
   // V codes as exact fp16 (q, via the 1024 bias and a packed subtract): the matrix
   // cores do not keep full fp32 precision when adding a 32-term dot product whose terms
   // carry a common +8 offset, so V (unlike K) is not fed as biased subnormals.
+  uint32_t xlo8[4], xhi8[4];
+#pragma unroll
+  for (int pr = 0; pr < 4; ++pr) {
+    xlo8[pr] = xlo[pr] >> 8;
+    xhi8[pr] = xhi[pr] >> 8;
+  }
+  // (dims with e & 3 in {1, 3} accumulate 16 times their value; see v_pair_f16)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     H8 va;
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {
       const uint32_t x = e < 4 ? xlo[pr] : xhi[pr];
-      va.u[pr] = nib_pair_f16(x >> (4 * (e & 3)));
+      const uint32_t x8 = e < 4 ? xlo8[pr] : xhi8[pr];
+      switch (e & 3) {
+        case 0: va.u[pr] = v_pair_f16<0>(x, x8); break;
+        case 1: va.u[pr] = v_pair_f16<1>(x, x8); break;
+        case 2: va.u[pr] = v_pair_f16<2>(x, x8); break;
+        default: va.u[pr] = v_pair_f16<3>(x, x8); break;
+      }
     }
     st.oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, phi.h, st.oacc[e], 0, 0, 0);
     st.oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, plo.h, st.oacc[e], 0, 0, 0);
@@ -629,8 +653,13 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       const uint32_t lo16 = (w[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
       const uint32_t hi16 = (w[2 + (p >> 1)] >> (16 * (p & 1))) & 0xFFFFu;
       o.u[p] = live ? (lo16 | (hi16 << 16)) : 0u;
-      const f16x2 h2 = __builtin_bit_cast(f16x2, o.u[p]);
+      f16x2 h2 = __builtin_bit_cast(f16x2, o.u[p]);
       qs += (float)h2.x + (float)h2.y;
+      if (p & 1) {   // slots of nibbles taken at bits 4..7 (16 times larger): q / 16
+        const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+        h2 = h2 * sixteenth;
+        o.u[p] = __builtin_bit_cast(uint32_t, h2);
+      }
     }
     qb[c] = o.h;
   }
@@ -663,8 +692,11 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     } else {
       wait_vmcnt<0>();
     }
-    process_tile<G, NGK>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, ps + TILE * cur, pe, j,
-                         a.qscale);
+    const int t0 = ps + TILE * cur;
+    if (t0 + TILE <= pe)
+      process_tile<G, NGK, false>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j, a.qscale);
+    else
+      process_tile<G, NGK, true>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j, a.qscale);
     cur = nxt;
     nxt = nn;
   }
@@ -678,6 +710,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   float* s_o = reinterpret_cast<float*>(smem);                 // [WAVES][G][HD]
   float* s_m = s_o + WAVES * G * HD;                            // [WAVES][G]
   float* s_l = s_m + WAVES * G;                                 // [WAVES][G]
+#pragma unroll
+  for (int e = 1; e < 8; e += 2) st.oacc[e] *= 0.0625f;   // see v_pair_f16
   const float l_run = sum_over_j(st.l);
   if (r < G * NGK && qgrp == 0) {
 #pragma unroll
