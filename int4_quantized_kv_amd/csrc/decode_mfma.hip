@@ -343,7 +343,7 @@ __device__ __forceinline__ TileData read_tile(const uint8_t* lb, const LaneOffs&
 template <int G, int NGK, bool MASK>
 __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& lo, State& st,
                                              const half8 (&qb)[4], float qbias, int t0, int pe,
-                                             int j, float qscale) {
+                                             int j, float qscale, bool lo_col) {
   const TileData td = read_tile<NGK>(lb, lo);
   // ---- q.K: lane (r, j) gets rows 4j + i of half T for column r = (head, group)
   float z[2][4];
@@ -402,6 +402,12 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
     }
   }
 
+  H8 pb;
+  if (NGK >= 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pb.u[w] = lo_col ? plo.u[w] : phi.u[w];
+  }
+
   // ---- P.V: byte halves of two rows' dwords give the (row, row + 1) pairs of 4 dims
   uint32_t xlo[4], xhi[4];
 #pragma unroll
@@ -436,8 +442,14 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
         default: va.u[pr] = v_pair_f16<3>(x, x8); break;
       }
     }
-    st.oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, phi.h, st.oacc[e], 0, 0, 0);
-    st.oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, plo.h, st.oacc[e], 0, 0, 0);
+    if (NGK >= 2) {
+      // a head's NGK columns carry the same P: columns g = 0, 2 take P'_hi and g = 1, 3
+      // take P'_lo, so one MFMA gives both parts (summed over columns g = 0, 1 at the end)
+      st.oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, pb.h, st.oacc[e], 0, 0, 0);
+    } else {
+      st.oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, phi.h, st.oacc[e], 0, 0, 0);
+      st.oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, plo.h, st.oacc[e], 0, 0, 0);
+    }
   }
 }
 
@@ -560,6 +572,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // q.K column r = (head r / NGK, group r % NGK); junk columns beyond G * NGK
   const int qhead = (r / NGK) % G;
   const int qgrp = r % NGK;
+  const bool lo_col = (qgrp & 1) != 0;   // column carries P'_lo in P.V (NGK >= 2)
   const int unit = b * a.Hkv + kvh;
   const int len = a.lens[b];
   const int lo_pos = a.window > 0 ? max(0, len - a.window) : 0;
@@ -633,10 +646,24 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 
   // q into MFMA layout (and the appending wave's quantization of the new row) while
   // tiles 0 and 1 are in flight
+  // (asm reads after a wait for the q transfers alone, which are older than the tiles';
+  // plain reads would make the compiler wait for the first tiles as well)
+  if (nxt != NONE) wait_vmcnt<2 * DMA>();
+  else if (cur != NONE) wait_vmcnt<DMA>();
+  else wait_vmcnt<0>();
   u32x4 qraw[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    qraw[c] = *reinterpret_cast<const u32x4*>(qstage + qhead * 2 * HD + 16 * (4 * j + c));
+  {
+    const uint32_t aq = (uint32_t)(uintptr_t)(lds_vptr)(qstage + qhead * 2 * HD + 16 * 4 * j);
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:16\n\t"
+        "ds_read_b128 %2, %4 offset:32\n\t"
+        "ds_read_b128 %3, %4 offset:48\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(qraw[0]), "=&v"(qraw[1]), "=&v"(qraw[2]), "=&v"(qraw[3])
+        : "v"(aq)
+        : "memory");
+  }
   // q as the B operand of dim chunk c: lane quarter j holds dims 8(4j + c) + {p, p+4}
   // in slots {2p, 2p + 1} (the order unpack_word_u produces) when quarter j lies in
   // the column's K group, zeros otherwise; qbias = -8 * (sum of those q entries)
@@ -694,9 +721,11 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     }
     const int t0 = ps + TILE * cur;
     if (t0 + TILE <= pe)
-      process_tile<G, NGK, false>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j, a.qscale);
+      process_tile<G, NGK, false>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j,
+                                  a.qscale, lo_col);
     else
-      process_tile<G, NGK, true>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j, a.qscale);
+      process_tile<G, NGK, true>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j,
+                                 a.qscale, lo_col);
     cur = nxt;
     nxt = nn;
   }
@@ -712,6 +741,12 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   float* s_l = s_m + WAVES * G;                                 // [WAVES][G]
 #pragma unroll
   for (int e = 1; e < 8; e += 2) st.oacc[e] *= 0.0625f;   // see v_pair_f16
+  if (NGK >= 2) {   // column g = 0 of a head: P'_hi part + (column g = 1) P'_lo part
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.oacc[e][i] = add_xor1(st.oacc[e][i]);
+  }
   const float l_run = sum_over_j(st.l);
   if (r < G * NGK && qgrp == 0) {
 #pragma unroll
