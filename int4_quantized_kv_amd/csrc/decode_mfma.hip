@@ -494,19 +494,38 @@ __device__ __forceinline__ void f16x8_to_f32(const u32x4& r, float x[8]) {
   }
 }
 
+// Reductions within aligned groups of 2^n lanes of a 16-lane row, by DPP (VALU, no LDS
+// round trip): quad swaps for partners 1 and 2, then the half-row and row mirrors, each
+// of which pairs a lane with one in the other half of its group of 8 / 16.
+template <bool MAX, int CTRL>
+__device__ __forceinline__ float dpp_step(float x) {
+  const float y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  return MAX ? fmaxf(x, y) : x + y;
+}
+template <bool MAX, int LANES>   // LANES: 1, 2, 4, 8 or 16
+__device__ __forceinline__ float row_reduce(float x) {
+  if (LANES >= 2) x = dpp_step<MAX, 0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  if (LANES >= 4) x = dpp_step<MAX, 0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  if (LANES >= 8) x = dpp_step<MAX, 0x141>(x);   // row_half_mirror
+  if (LANES >= 16) x = dpp_step<MAX, 0x140>(x);  // row_mirror
+  return x;
+}
+
 template <int G, int NGK>
 __device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds* s,
                                              const uint8_t* qrows, int lane) {
   NewRow nr;
   const bool isv = lane >= 16;
   const int c = lane & 15;
-  const int lpg = (isv ? HD : a.gk) >> 3;               // lanes per quantization group
+  constexpr int LPG_K = 16 / NGK;                       // lanes per K group (V: 16)
   float x[8];
   f16x8_to_f32(*reinterpret_cast<const u32x4*>((isv ? s->v : s->k) + 8 * c), x);
   float am = 0.0f;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) am = fmaxf(am, fabsf(x[jj]));
-  for (int m = 1; m < lpg; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+  const float am_row = row_reduce<true, 16>(am);
+  am = isv ? am_row : row_reduce<true, LPG_K>(am);
   const float sc = kvq_int4_scale(am);
   const float rc = 1.0f / sc;
   uint32_t w = 0;
@@ -521,7 +540,7 @@ __device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds* 
   nr.sc = sc;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) nr.v[jj] = code[jj] * sc;
-  // score of every query head: sum over K groups of (group scale) * (q . codes)
+  // score of every query head (K lanes): sum over K groups of (group scale) * (q . codes)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float qv[8];
@@ -529,9 +548,11 @@ __device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds* 
     float d = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) d = __builtin_fmaf(qv[jj], code[jj], d);
-    for (int m = 1; m < lpg; m <<= 1) d += __shfl_xor(d, m);   // within the K group
-    d *= sc;
-    for (int m = lpg; m < 16; m <<= 1) d += __shfl_xor(d, m);  // over the K groups
+    d = row_reduce<false, LPG_K>(d) * sc;               // within the K group, scaled
+    if (LPG_K < 2) d = dpp_step<false, 0xB1>(d);         // then over the K groups
+    if (LPG_K < 4) d = dpp_step<false, 0x4E>(d);
+    if (LPG_K < 8) d = dpp_step<false, 0x141>(d);
+    if (LPG_K < 16) d = dpp_step<false, 0x140>(d);
     nr.z[h] = d;
   }
   return nr;
