@@ -339,11 +339,14 @@ __device__ __forceinline__ TileData read_tile(const uint8_t* lb, const LaneOffs&
 
 // State::m is the running maximum of the unscaled scores z = q . k; since the scale
 // (softmax scale * log2 e) is positive, p = 2^(scale * (z - m)).
-// MASK: the tile reaches past pe (a split's last tile); those positions get score -inf.
-template <int G, int NGK, bool MASK>
+// masked (uniform): the tile reaches past pe (a split's last tile); those positions get
+// score -inf.  One code path serves both kinds of tile, and the masking only rewrites
+// the 8 scores in place: with two instances of the tile in the loop, the compiler gave
+// the accumulators of each its own registers and copied all 32 of them twice per tile.
+template <int G, int NGK>
 __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& lo, State& st,
                                              const half8 (&qb)[4], float qbias, int t0, int pe,
-                                             int j, float qscale, bool lo_col) {
+                                             int j, float qscale, bool lo_col, bool masked) {
   const TileData td = read_tile<NGK>(lb, lo);
   // ---- q.K: lane (r, j) gets rows 4j + i of half T for column r = (head, group)
   float z[2][4];
@@ -363,9 +366,15 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
       // the NGK columns of a head are adjacent (column = head * NGK + group)
       if (NGK >= 2) s = add_xor1(s);
       if (NGK >= 4) s = add_xor2(s);
-      if (MASK) s = t0 + 16 * T + 4 * j + i < pe ? s : NEG_INF;
       z[T][i] = s;
     }
+  }
+  if (masked) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (t0 + 16 * T + 4 * j + i >= pe) z[T][i] = NEG_INF;
   }
 
   // ---- online softmax (the 4 lanes j of a column share a head)
@@ -741,12 +750,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       wait_vmcnt<0>();
     }
     const int t0 = ps + TILE * cur;
-    if (t0 + TILE <= pe)
-      process_tile<G, NGK, false>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j,
-                                  a.qscale, lo_col);
-    else
-      process_tile<G, NGK, true>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j,
-                                 a.qscale, lo_col);
+    process_tile<G, NGK>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j, a.qscale,
+                         lo_col, t0 + TILE > pe);
     cur = nxt;
     nxt = nn;
   }
