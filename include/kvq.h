@@ -174,8 +174,8 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
  *   softmax_scale: > 0, or 0 to select 1/sqrt(D); negative values are rejected.
  *   num_splits: sequence splits per (b, kv head), at most 1024; 0 = kvq_plan_splits.
  *   out: device, [B, q_heads, D] fp32.
- *   workspace: device scratch of at least kvq_decode_workspace_bytes bytes
- *              (KVQ_ERR_WORKSPACE otherwise).  Zero-fill it once before its first use
+ *   workspace: device scratch of at least kvq_decode_workspace_bytes bytes, 16-byte
+ *              aligned (KVQ_ERR_WORKSPACE otherwise).  Zero-fill it once before its first use
  *              (hipMemset of the whole buffer, or of its first KVQ_WS_COUNTER_BYTES):
  *              the counters there must read zero when a call starts, and each call
  *              leaves them zero; the rest is clobbered.  Calls that may run at the same

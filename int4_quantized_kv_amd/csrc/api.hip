@@ -204,7 +204,8 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(desc, q_heads, span);
   if (ns < 1 || ns > MAX_SPLITS) return KVQ_ERR_ARG;
   const size_t need = partials_offset() + partials_bytes(desc->batch, q_heads, ns, desc->head_dim);
-  if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16)
+    return KVQ_ERR_WORKSPACE;
 
   DecodeArgs a;
   std::memset(&a, 0, sizeof(a));

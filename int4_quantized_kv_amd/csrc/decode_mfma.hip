@@ -49,6 +49,13 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float NEG_INF = -__builtin_huge_valf();
+// Initial running maximum: finite and below every score (|q . k| < 128 * 65504^2 for fp16
+// q and K values), so a column that sees only masked positions keeps p = 2^-inf = 0,
+// a zero sum and zero accumulators (with -inf it would form 2^(-inf + inf) = NaN), and
+// enters the combine with weight 0.  Raised for very large softmax scales so that
+// M_EMPTY * scale stays finite.
+constexpr float M_EMPTY = -1.0e30f;
+__device__ __forceinline__ float empty_max(float qscale) { return fmaxf(M_EMPTY, -1.0e37f / qscale); }
 constexpr int HD = 128;     // head_dim of this kernel
 constexpr int TILE = 32;    // positions per wave iteration
 constexpr int WAVES = 8;    // one workgroup per CU (see the tile schedule below)
@@ -264,18 +271,29 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int
   dma4(vs + srow * 4, lb + L::SV_OFF);
 }
 
+// Position sets.  A head's q.K needs G * NGK of the 16 MFMA columns.  When that is at
+// most 8 (S = 2), the other 8 columns score the second 16-position half of the tile in
+// the same MFMAs: A row r then carries position r of half 0 in the k slots of lane
+// quarters j = 0, 1 and position 16 + r in those of quarters 2, 3 (two chunks of K
+// codes per lane instead of one chunk of each half), and the q of columns 8 .. 15 sits
+// in quarters 2, 3 (columns 0 .. 7: quarters 0, 1).  Column r then scores positions
+// 16 (r / 8) + 4j + i in lane (r, j): each lane holds 4 scores instead of 8 (the same 8
+// MFMAs per tile, half the softmax arithmetic), and P.V keeps its layout: a column's B
+// is its 4 values of P' in its set's k slots and zeros in the other set's.
+__host__ __device__ constexpr int position_sets(int g, int ngk) { return g * ngk <= 8 ? 2 : 1; }
+
 // Online-softmax state of one wave (per lane: query head of column r).
 struct State {
   floatx4 oacc[8];
   float m, l;
 };
 
-// Per-lane LDS offsets, fixed for the whole kernel.
+// Per-lane LDS offsets, fixed for the whole kernel (see position_sets).
 struct LaneOffs {
-  int k;        // q.K: chunk j of row r (half 0)
+  int k[2];     // q.K: the lane's two 16-byte chunks of K codes
   int v[4];     // P.V: dword r of row 4j + i (half 0)
-  int sk;       // K scales of group g, rows 4j .. 4j+3 (half 0)
-  int sv;       // V scales, rows 4j .. 4j+3 (half 0)
+  int sk;       // K scales of the lane's group and first 4 rows
+  int sv;       // V scales of the lane's first 4 rows
 };
 
 // Next value of a workgroup's LDS tile counter (lane 0 adds, the wave reads its result).
@@ -291,95 +309,124 @@ __device__ __forceinline__ uint32_t lds_claim(uint32_t* ctr, int lane) {
   return __builtin_amdgcn_readfirstlane(old);
 }
 
-// The LDS reads of one tile for one lane: K codes (chunk j of row r, both halves), the
-// K and V scales of rows 4j .. 4j+3 (both halves) and the V dwords of rows 4j + i.
+// The LDS reads of one tile for one lane: two chunks of K codes, the K and V scales of
+// the rows whose scores the lane holds (S = 1: rows 4j .. 4j+3 of both halves; S = 2:
+// of its column's half only) and the V dwords of rows 4j + i of both halves.
 struct TileData {
   u32x4 k[2], sk[2], sv[2];
   uint32_t v[2][4];
 };
 
-// All 14 reads are issued in one asm statement that ends by waiting for them.  Written
+// All 14 (S = 2: 12) reads are issued in one asm statement that ends by waiting for them.  Written
 // this way the compiler sees no LDS read here, so it does not add a wait for every
 // transfer in flight before the tile (it cannot tell which LDS bytes a global->LDS
 // transfer writes); the caller's vmcnt wait is what orders this tile's own transfers
 // before the reads.
-template <int NGK>
+template <int NGK, int S>
 __device__ __forceinline__ TileData read_tile(const uint8_t* lb, const LaneOffs& lo) {
   using L = Slot<NGK>;
   const uint32_t base = (uint32_t)(uintptr_t)(lds_vptr)lb;
-  const uint32_t ak = base + L::K_OFF + lo.k, ask = base + L::SK_OFF + lo.sk;
-  const uint32_t asv = base + L::SV_OFF + lo.sv;
+  const uint32_t ak0 = base + L::K_OFF + lo.k[0], ak1 = base + L::K_OFF + lo.k[1];
+  const uint32_t ask = base + L::SK_OFF + lo.sk, asv = base + L::SV_OFF + lo.sv;
   const uint32_t av0 = base + L::V_OFF + lo.v[0], av1 = base + L::V_OFF + lo.v[1];
   const uint32_t av2 = base + L::V_OFF + lo.v[2], av3 = base + L::V_OFF + lo.v[3];
   TileData d;
-  asm volatile(
-      "ds_read_b128 %0, %14\n\t"
-      "ds_read_b128 %1, %14 offset:1024\n\t"
-      "ds_read_b128 %2, %15\n\t"
-      "ds_read_b128 %3, %15 offset:64\n\t"
-      "ds_read_b128 %4, %16\n\t"
-      "ds_read_b128 %5, %16 offset:64\n\t"
-      "ds_read_b32 %6, %17\n\t"
-      "ds_read_b32 %7, %18\n\t"
-      "ds_read_b32 %8, %19\n\t"
-      "ds_read_b32 %9, %20\n\t"
-      "ds_read_b32 %10, %17 offset:1024\n\t"
-      "ds_read_b32 %11, %18 offset:1024\n\t"
-      "ds_read_b32 %12, %19 offset:1024\n\t"
-      "ds_read_b32 %13, %20 offset:1024\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(d.k[0]), "=&v"(d.k[1]), "=&v"(d.sk[0]), "=&v"(d.sk[1]), "=&v"(d.sv[0]),
-        "=&v"(d.sv[1]), "=&v"(d.v[0][0]), "=&v"(d.v[0][1]), "=&v"(d.v[0][2]),
-        "=&v"(d.v[0][3]), "=&v"(d.v[1][0]), "=&v"(d.v[1][1]), "=&v"(d.v[1][2]),
-        "=&v"(d.v[1][3])
-      : "v"(ak), "v"(ask), "v"(asv), "v"(av0), "v"(av1), "v"(av2), "v"(av3)
-      : "memory");
+  if (S == 1) {
+    asm volatile(
+        "ds_read_b128 %0, %14\n\t"
+        "ds_read_b128 %1, %15\n\t"
+        "ds_read_b128 %2, %16\n\t"
+        "ds_read_b128 %3, %16 offset:64\n\t"
+        "ds_read_b128 %4, %17\n\t"
+        "ds_read_b128 %5, %17 offset:64\n\t"
+        "ds_read_b32 %6, %18\n\t"
+        "ds_read_b32 %7, %19\n\t"
+        "ds_read_b32 %8, %20\n\t"
+        "ds_read_b32 %9, %21\n\t"
+        "ds_read_b32 %10, %18 offset:1024\n\t"
+        "ds_read_b32 %11, %19 offset:1024\n\t"
+        "ds_read_b32 %12, %20 offset:1024\n\t"
+        "ds_read_b32 %13, %21 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(d.k[0]), "=&v"(d.k[1]), "=&v"(d.sk[0]), "=&v"(d.sk[1]), "=&v"(d.sv[0]),
+          "=&v"(d.sv[1]), "=&v"(d.v[0][0]), "=&v"(d.v[0][1]), "=&v"(d.v[0][2]),
+          "=&v"(d.v[0][3]), "=&v"(d.v[1][0]), "=&v"(d.v[1][1]), "=&v"(d.v[1][2]),
+          "=&v"(d.v[1][3])
+        : "v"(ak0), "v"(ak1), "v"(ask), "v"(asv), "v"(av0), "v"(av1), "v"(av2), "v"(av3)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %13\n\t"
+        "ds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %3, %15\n\t"
+        "ds_read_b32 %4, %16\n\t"
+        "ds_read_b32 %5, %17\n\t"
+        "ds_read_b32 %6, %18\n\t"
+        "ds_read_b32 %7, %19\n\t"
+        "ds_read_b32 %8, %16 offset:1024\n\t"
+        "ds_read_b32 %9, %17 offset:1024\n\t"
+        "ds_read_b32 %10, %18 offset:1024\n\t"
+        "ds_read_b32 %11, %19 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(d.k[0]), "=&v"(d.k[1]), "=&v"(d.sk[0]), "=&v"(d.sv[0]), "=&v"(d.v[0][0]),
+          "=&v"(d.v[0][1]), "=&v"(d.v[0][2]), "=&v"(d.v[0][3]), "=&v"(d.v[1][0]),
+          "=&v"(d.v[1][1]), "=&v"(d.v[1][2]), "=&v"(d.v[1][3])
+        : "v"(ak0), "v"(ak1), "v"(ask), "v"(asv), "v"(av0), "v"(av1), "v"(av2), "v"(av3)
+        : "memory");
+  }
   return d;
 }
 
 // State::m is the running maximum of the unscaled scores z = q . k; since the scale
 // (softmax scale * log2 e) is positive, p = 2^(scale * (z - m)).
+// S = 1: the lane's scores are positions 16T + 4j + i (T = 0, 1); S = 2: positions
+// soff + 4j + i, soff = 16 * (the half of the lane's column set), see position_sets.
 // masked (uniform): the tile reaches past pe (a split's last tile); those positions get
 // score -inf.  One code path serves both kinds of tile, and the masking only rewrites
-// the 8 scores in place: with two instances of the tile in the loop, the compiler gave
+// the scores in place: with two instances of the tile in the loop, the compiler gave
 // the accumulators of each its own registers and copied all 32 of them twice per tile.
-template <int G, int NGK>
+template <int G, int NGK, int S>
 __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& lo, State& st,
-                                             const half8 (&qb)[4], float qbias, int t0, int pe,
-                                             int j, float qscale, bool lo_col, bool masked) {
-  const TileData td = read_tile<NGK>(lb, lo);
-  // ---- q.K: lane (r, j) gets rows 4j + i of half T for column r = (head, group)
-  float z[2][4];
+                                             const half8 (&qb)[4 * S], float qbias, int t0,
+                                             int pe, int j, float qscale, bool lo_col,
+                                             int soff, bool masked) {
+  constexpr int NTB = 2 / S;   // 16-row blocks of q.K results per lane
+  const TileData td = read_tile<NGK, S>(lb, lo);
+  // ---- q.K: lane (r, j) gets rows 4j + i of block T for column r = (set, head, group)
+  const uint32_t kw8[8] = {td.k[0].x, td.k[0].y, td.k[0].z, td.k[0].w,
+                           td.k[1].x, td.k[1].y, td.k[1].z, td.k[1].w};
+  float z[NTB][4];
 #pragma unroll
-  for (int T = 0; T < 2; ++T) {
-    const u32x4 kw = td.k[T];
+  for (int T = 0; T < NTB; ++T) {
     const floatx4 sk = __builtin_bit_cast(floatx4, td.sk[T]);
-    const uint32_t kw4[4] = {kw.x, kw.y, kw.z, kw.w};
     floatx4 cg = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_word_u(kw4[c]), qb[c], cg, 0, 0, 0);
+    for (int c = 0; c < 4 * S; ++c)
+      cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_word_u(kw8[4 * S * T + c]), qb[c], cg,
+                                                  0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // q . codes_g = 2^24 C - 8 sum_g(q); then the group scale
-      float s = __builtin_fmaf(cg[i], 16777216.0f, qbias) * sk[i];
+      float sc = __builtin_fmaf(cg[i], 16777216.0f, qbias) * sk[i];
       // the NGK columns of a head are adjacent (column = head * NGK + group)
-      if (NGK >= 2) s = add_xor1(s);
-      if (NGK >= 4) s = add_xor2(s);
-      z[T][i] = s;
+      if (NGK >= 2) sc = add_xor1(sc);
+      if (NGK >= 4) sc = add_xor2(sc);
+      z[T][i] = sc;
     }
   }
   if (masked) {
 #pragma unroll
-    for (int T = 0; T < 2; ++T)
+    for (int T = 0; T < NTB; ++T)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (t0 + 16 * T + 4 * j + i >= pe) z[T][i] = NEG_INF;
+        if (t0 + 16 * T + soff + 4 * j + i >= pe) z[T][i] = NEG_INF;
   }
 
   // ---- online softmax (the 4 lanes j of a column share a head)
-  float mx = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
-                   fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+  float mx = fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3]));
+  if (NTB == 2) mx = fmaxf(mx, fmaxf(fmaxf(z[NTB - 1][0], z[NTB - 1][1]),
+                                     fmaxf(z[NTB - 1][2], z[NTB - 1][3])));
   mx = max_over_j(mx);
   const float m_new = fmaxf(st.m, mx);
   if (__any(m_new > st.m)) {
@@ -391,10 +438,11 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
   }
   const float mq = st.m * qscale;
 
-  // ---- P' = P * sV as fp16 hi + lo, in the B layout (k = 4T + i)
+  // ---- P' = P * sV as fp16 hi + lo, in the B layout: k slot 4T + i (S = 1) or
+  // 4 * set + i (S = 2, zeros in the other set's four slots)
   H8 phi, plo;
 #pragma unroll
-  for (int T = 0; T < 2; ++T) {
+  for (int T = 0; T < NTB; ++T) {
     const floatx4 sv = __builtin_bit_cast(floatx4, td.sv[T]);
 #pragma unroll
     for (int i = 0; i < 4; i += 2) {
@@ -410,11 +458,22 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
       plo.u[2 * T + i / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
     }
   }
-
+  // S = 2: the lane's two dwords go to its set's slots (the other two are zero)
+  auto place = [&](H8& x) {
+    const bool s1 = soff != 0;
+    x.u[2] = s1 ? x.u[0] : 0u;
+    x.u[3] = s1 ? x.u[1] : 0u;
+    x.u[0] = s1 ? 0u : x.u[0];
+    x.u[1] = s1 ? 0u : x.u[1];
+  };
   H8 pb;
   if (NGK >= 2) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) pb.u[w] = lo_col ? plo.u[w] : phi.u[w];
+    for (int w = 0; w < 2 * NTB; ++w) pb.u[w] = lo_col ? plo.u[w] : phi.u[w];
+    if (S == 2) place(pb);
+  } else if (S == 2) {
+    place(phi);
+    place(plo);
   }
 
   // ---- P.V: byte halves of two rows' dwords give the (row, row + 1) pairs of 4 dims
@@ -468,6 +527,11 @@ __device__ __forceinline__ void publish(float* p, float v) {
 }
 __device__ __forceinline__ float fetch(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// an 8-byte-aligned (max, sum) pair in one load
+__device__ __forceinline__ uint64_t fetch_pair(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The new token's row when the append is fused into the attention.  Wave 0 of the
@@ -588,6 +652,7 @@ __device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewLds*
 template <int G, int NGK>
 __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   using L = Slot<NGK>;
+  constexpr int S = position_sets(G, NGK);
   constexpr int DMA = L::DMA;
   __shared__ __attribute__((aligned(16))) uint8_t smem[WAVES * NB * L::BYTES];
   __shared__ __attribute__((aligned(16))) NewLds s_new;
@@ -599,9 +664,12 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // wave-uniform: keeps tile positions, ring addresses and base pointers in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, j = lane >> 4;
-  // q.K column r = (head r / NGK, group r % NGK); junk columns beyond G * NGK
-  const int qhead = (r / NGK) % G;
-  const int qgrp = r % NGK;
+  // q.K column r = (set r / 8 when S = 2, head, group) with head = rr / NGK and
+  // group = rr % NGK for rr = r % (16 / S); junk columns beyond G * NGK
+  const int rr = S == 2 ? (r & 7) : r;
+  const int cset = S == 2 ? (r >> 3) : 0;   // the half whose positions the column scores
+  const int qhead = (rr / NGK) % G;
+  const int qgrp = rr % NGK;
   const bool lo_col = (qgrp & 1) != 0;   // column carries P'_lo in P.V (NGK >= 2)
   const int unit = b * a.Hkv + kvh;
   const int len = a.lens[b];
@@ -645,22 +713,28 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   LaneOffs lo;
   {
     const int P = rowinv(r);
-    lo.k = P * 64 + 16 * (j ^ chunk_swz(P));
+    if (S == 1) {   // chunk j of row r in both halves
+      lo.k[0] = P * 64 + 16 * (j ^ chunk_swz(P));
+      lo.k[1] = lo.k[0] + 1024;
+    } else {        // chunks j % 2 and j % 2 + 2 of row r in half j / 2
+      lo.k[0] = (j >> 1) * 1024 + P * 64 + 16 * ((j & 1) ^ chunk_swz(P));
+      lo.k[1] = (j >> 1) * 1024 + P * 64 + 16 * (((j & 1) + 2) ^ chunk_swz(P));
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int Pv = rowinv(4 * j + i);
       lo.v[i] = Pv * 64 + 16 * ((r >> 2) ^ chunk_swz(Pv)) + 4 * (r & 3);
     }
-    lo.sk = (min(qgrp, NGK - 1) * 32 + 4 * j) * 4;
-    lo.sv = 4 * j * 4;
+    lo.sk = (min(qgrp, NGK - 1) * 32 + 16 * cset + 4 * j) * 4;
+    lo.sv = (16 * cset + 4 * j) * 4;
   }
 
   State st;
 #pragma unroll
   for (int e = 0; e < 8; ++e) st.oacc[e] = (floatx4){0.f, 0.f, 0.f, 0.f};
-  st.m = NEG_INF;
+  st.m = empty_max(a.qscale);
   st.l = 0.0f;
-  half8 qb[4];
+  half8 qb[4 * S];
   float qbias = 0.0f;
 
   // The pipeline: the first two tiles start before the loop; step k claims tile k + 2,
@@ -681,9 +755,11 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   if (nxt != NONE) wait_vmcnt<2 * DMA>();
   else if (cur != NONE) wait_vmcnt<DMA>();
   else wait_vmcnt<0>();
-  u32x4 qraw[4];
+  // the chunk of q feeding MFMA c: S = 1: chunk j (all c); S = 2: chunk j % 2 + 2 (c / 4)
+  u32x4 qraw[4 * S];
   {
-    const uint32_t aq = (uint32_t)(uintptr_t)(lds_vptr)(qstage + qhead * 2 * HD + 16 * 4 * j);
+    const int ch0 = S == 1 ? j : (j & 1);
+    const uint32_t aq = (uint32_t)(uintptr_t)(lds_vptr)(qstage + qhead * 2 * HD + 64 * ch0);
     asm volatile(
         "ds_read_b128 %0, %4\n\t"
         "ds_read_b128 %1, %4 offset:16\n\t"
@@ -693,15 +769,27 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
         : "=&v"(qraw[0]), "=&v"(qraw[1]), "=&v"(qraw[2]), "=&v"(qraw[3])
         : "v"(aq)
         : "memory");
+    if constexpr (S == 2)
+      asm volatile(
+          "ds_read_b128 %0, %4 offset:128\n\t"
+          "ds_read_b128 %1, %4 offset:144\n\t"
+          "ds_read_b128 %2, %4 offset:160\n\t"
+          "ds_read_b128 %3, %4 offset:176\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(qraw[4]), "=&v"(qraw[5]), "=&v"(qraw[6]), "=&v"(qraw[7])
+          : "v"(aq)
+          : "memory");
   }
-  // q as the B operand of dim chunk c: lane quarter j holds dims 8(4j + c) + {p, p+4}
-  // in slots {2p, 2p + 1} (the order unpack_word_u produces) when quarter j lies in
-  // the column's K group, zeros otherwise; qbias = -8 * (sum of those q entries)
-  constexpr int QPG = 4 / NGK;   // lane quarters (32 dims) per K group
-  const bool live = r < G * NGK && j / QPG == qgrp;
+  // q as the B operand of MFMA c: lane quarter j holds dims 32 ch + 8 (c % 4) + {p, p+4}
+  // (ch its chunk for c) in slots {2p, 2p + 1} (the order unpack_word_u produces) when
+  // those dims lie in the column's K group and (S = 2) quarter j feeds the column's
+  // set, zeros otherwise; qbias = -8 * (sum of those q entries)
+  constexpr int QPG = 4 / NGK;   // chunks (32 dims) per K group
   float qs = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < 4 * S; ++c) {
+    const int ch = S == 1 ? j : (j & 1) + 2 * (c >> 2);
+    const bool live = rr < G * NGK && ch / QPG == qgrp && (S == 1 || (j >> 1) == cset);
     const uint32_t w[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
     H8 o;
 #pragma unroll
@@ -750,21 +838,29 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       wait_vmcnt<0>();
     }
     const int t0 = ps + TILE * cur;
-    process_tile<G, NGK>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j, a.qscale,
-                         lo_col, t0 + TILE > pe);
+    process_tile<G, NGK, S>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j,
+                            a.qscale, lo_col, 16 * cset, t0 + TILE > pe);
     cur = nxt;
     nxt = nn;
   }
   wait_vmcnt<0>();   // (also the q staging, when this wave had no tile)
-  if (app_wave && lane < 32) store_new_row<NGK>(a, &s_new, row0 + (size_t)((len - 1) % a.cap), lane);
 
-  // ---- combine the waves (and, in the appending workgroup, the new row) through
-  // LDS, reusing the ring: lane (r, j) holds O[column r][8(4j + i) + e] in oacc[e][i];
-  // a head sits in column head * NGK
+  // ---- combine the waves' column sets (and, in the appending workgroup, the new row)
+  // through LDS, reusing the ring: lane (r, j) holds O[column r][8(4j + i) + e] in
+  // oacc[e][i]; a head sits in column head * NGK of each set, and each set has its own
+  // running maximum, so it enters the combine as an entry of its own
+  // s_o rows of 132 words (a pad word after every 32 dims): one write instruction stores
+  // dims 32j + const of up to 8 (entry, head) rows, which then fall in 32 distinct banks
+  // (unpadded they all share one bank)
+  constexpr int NE = WAVES * S;                                 // combine entries
+  constexpr int ORS = HD + HD / 32;                             // padded row stride
+  auto opad = [](int d) { return d + (d >> 5); };
+  static_assert((NE * G * ORS + 2 * NE * G) * sizeof(float) <= sizeof(smem),
+                "the combine reuses the tile rings");
   __syncthreads();
-  float* s_o = reinterpret_cast<float*>(smem);                 // [WAVES][G][HD]
-  float* s_m = s_o + WAVES * G * HD;                            // [WAVES][G]
-  float* s_l = s_m + WAVES * G;                                 // [WAVES][G]
+  float* s_o = reinterpret_cast<float*>(smem);                 // [NE][G][ORS]
+  float* s_m = s_o + NE * G * ORS;                              // [G][NE]
+  float* s_l = s_m + NE * G;                                    // [G][NE]
 #pragma unroll
   for (int e = 1; e < 8; e += 2) st.oacc[e] *= 0.0625f;   // see v_pair_f16
   if (NGK >= 2) {   // column g = 0 of a head: P'_hi part + (column g = 1) P'_lo part
@@ -774,15 +870,16 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       for (int i = 0; i < 4; ++i) st.oacc[e][i] = add_xor1(st.oacc[e][i]);
   }
   const float l_run = sum_over_j(st.l);
-  if (r < G * NGK && qgrp == 0) {
+  if (rr < G * NGK && qgrp == 0) {
+    const int ent = wave * S + cset;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        s_o[(wave * G + qhead) * HD + 8 * (4 * j + i) + e] = st.oacc[e][i];
+        s_o[(ent * G + qhead) * ORS + opad(8 * (4 * j + i) + e)] = st.oacc[e][i];
     if (j == 0) {
-      s_m[wave * G + qhead] = st.m * a.qscale;   // base-2 units
-      s_l[wave * G + qhead] = l_run;
+      s_m[qhead * NE + ent] = st.m * a.qscale;   // base-2 units
+      s_l[qhead * NE + ent] = l_run;
     }
   }
   __syncthreads();
@@ -790,26 +887,38 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   const size_t pbase = (size_t)(b * a.Hq + kvh * G) * nps;     // slot of (head 0, split 0)
   for (int idx = threadIdx.x; idx < G * HD; idx += NT) {
     const int h = idx / HD, d = idx % HD;
+    // every entry's (max, sum, value) first, so the reads issue together (the per-head
+    // max and sum are 16-byte broadcast reads); an entry that saw no position has max
+    // empty_max * scale and zero sum and value, so it adds nothing whatever its weight
+    float mw[NE], lw[NE], ow[NE];
+#pragma unroll
+    for (int w = 0; w < NE; w += 4) {
+      const floatx4 m4 = *reinterpret_cast<const floatx4*>(s_m + h * NE + w);
+      const floatx4 l4 = *reinterpret_cast<const floatx4*>(s_l + h * NE + w);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        mw[w + u] = m4[u];
+        lw[w + u] = l4[u];
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < NE; ++w) ow[w] = s_o[(w * G + h) * ORS + opad(d)];
     const float mn = appender ? s_new.m[h] : NEG_INF;
+    const float on = appender ? s_new.o[d] : 0.0f;
     float M = mn;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w * G + h]);
+    for (int w = 0; w < NE; ++w) M = fmaxf(M, mw[w]);
     float Acc = 0.0f, Lsum = 0.0f;
-    if (M != NEG_INF) {
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) {
-        const float mw = s_m[w * G + h];
-        if (mw != NEG_INF) {
-          const float f = fast_exp2(mw - M);
-          Acc = __builtin_fmaf(s_o[(w * G + h) * HD + d], f, Acc);
-          Lsum = __builtin_fmaf(s_l[w * G + h], f, Lsum);
-        }
-      }
-      if (mn != NEG_INF) {
-        const float f = fast_exp2(mn - M);
-        Acc = __builtin_fmaf(s_new.o[d], f, Acc);
-        Lsum += f;
-      }
+    for (int w = 0; w < NE; ++w) {
+      const float f = fast_exp2(mw[w] - M);
+      Acc = __builtin_fmaf(ow[w], f, Acc);
+      Lsum = __builtin_fmaf(lw[w], f, Lsum);
+    }
+    if (mn != NEG_INF) {
+      const float f = fast_exp2(mn - M);
+      Acc = __builtin_fmaf(on, f, Acc);
+      Lsum += f;
     }
     const size_t o = pbase + (size_t)h * nps + sp;
     publish(a.ws_acc + o * HD + d, Acc);
@@ -824,6 +933,10 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // barrier, so when the counting thread bumps the (device-scope) arrival counter the
   // whole partial is visible.  This avoids a release fence, which on this chip writes
   // back the XCD's whole L2 and costs microseconds per workgroup.
+  // the new row's codes and scales go to the cache here, so that the wait below covers
+  // them together with the partials (a barrier right after the loop would wait for them
+  // alone); no tile of this step reads that row
+  if (app_wave && lane < 32) store_new_row<NGK>(a, &s_new, row0 + (size_t)((len - 1) % a.cap), lane);
   uint32_t* cnt = a.counters + unit;
   wait_vmcnt<0>();
   __syncthreads();
@@ -849,11 +962,14 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       pre[u][sI] = idx < G * HD && sI < np ? fetch(a.ws_acc + (pbase + (size_t)h * nps + sI) * HD + d)
                                            : 0.0f;
   }
-  float* s_w = reinterpret_cast<float*>(smem);          // [G][np] split weights
-  float* s_L = s_w + G * np;                            // [G]
+  float* s_w = reinterpret_cast<float*>(smem);          // [G][np] split maxima, then weights
+  float* s_ls = s_w + G * np;                           // [G][np] split sums
+  float* s_L = s_ls + G * np;                           // [G]
   for (int idx = threadIdx.x; idx < G * np; idx += NT) {
     const int h = idx / np, sI = idx % np;
-    s_w[idx] = fetch(a.ws_ml + 2 * (pbase + (size_t)h * nps + sI));
+    const uint64_t ml = fetch_pair(a.ws_ml + 2 * (pbase + (size_t)h * nps + sI));
+    s_w[idx] = __builtin_bit_cast(float, (uint32_t)ml);
+    s_ls[idx] = __builtin_bit_cast(float, (uint32_t)(ml >> 32));
   }
   __syncthreads();
   // one wave per head: maximum, weights 2^(m_s - M), weighted sum of the partial sums
@@ -867,7 +983,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       const float ms = s_w[h * np + sI];
       const float wgt = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
       s_w[h * np + sI] = wgt;
-      Ls = __builtin_fmaf(wgt, fetch(a.ws_ml + 2 * (pbase + (size_t)h * nps + sI) + 1), Ls);
+      Ls = __builtin_fmaf(wgt, s_ls[h * np + sI], Ls);
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) Ls += __shfl_xor(Ls, m);

@@ -121,6 +121,7 @@ def test_error_paths_enqueue_nothing():
     _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_decode_attn, d, c, FAKE, 8, [100, 10], 65, 0.0, 0, FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, FAKE, ws - 1, 0)
     _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, 0, ws, 0)
+    _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, FAKE + 8, ws, 0)
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], -1, 0.0, 0, FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, float("nan"), 0, FAKE, FAKE, ws, 0)
     # fused append + decode: null new rows, then the decode checks

@@ -168,6 +168,8 @@ MFMA_CASES = [
     (32, 8, [1025, 640], 0, None),
     (64, 4, [1500, 1500], 300, 512),    # window ring, capacity 512 (wraps)
     (128, 8, [2049, 40], 0, None),
+    (64, 8, [1300, 33], 0, None),       # 16 (head, group) columns: one position set
+    (32, 4, [777, 1024], 0, None),      # 16 columns, K group 32
 ]
 
 
@@ -217,7 +219,7 @@ def test_int4_generic_fallback(gv, cap):
 
 
 FUSED_CASES = [
-    # fmt, gk, gv, G, D, lens, window, cap, nsplit   (the first four: matrix-core kernel)
+    # fmt, gk, gv, G, D, lens, window, cap, nsplit   (cases 0, 2, 3: matrix-core kernel)
     ("int4", 64, 128, 4, 128, [300, 45], 0, None, 0),
     ("int4", 32, 128, 8, 128, [1100, 1], 0, None, 5),     # a sequence of length 1
     ("int4", 128, 128, 1, 128, [97, 640], 0, None, 64),   # more splits than positions
