@@ -12,6 +12,17 @@ the caches before timing.
 
 Prints ONE JSON line: effective KV GB/s (algorithmic bytes per step / step time), the
 roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
+
+--workload selects one of the other workloads instead (each prints its own JSON line of
+the same form; the default run is the headline above):
+  mha7b-prefill  kvq_quantize_prefill of one MHA-7B-shaped layer (B 8, 32 heads x 128,
+                 20480 positions): pure streaming, 3.42 GB per layer
+  mha7b-decode   32 layers of decode over 20480 positions, one query head per KV head
+  ctx128k-int4   32 layers of batch-1 decode over 131072 positions, INT4 K g64 / V g128
+  ctx128k-int8   the same with the INT8 per-token format
+  gemma-codec    Gemma-3-4B-shaped step of the WHT + Lloyd-Max codec: 34 layers (29 with a
+                 1024-row window ring, 5 global), append at position 4096 then attend
+  dequant        kvq_dequant of K and V of 8 Llama-3-8B-shaped layer caches to fp32
 """
 import argparse
 import ctypes
@@ -35,6 +46,9 @@ TRAFFIC_FILE = "profiles/decode_int4_mfma_llama8b_ctx8k_b8_traffic.md"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--workload", default="llama8b",
+                   choices=["llama8b", "mha7b-prefill", "mha7b-decode", "ctx128k-int4",
+                            "ctx128k-int8", "gemma-codec", "dequant"])
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=None, help="override the layer count (debug only)")
@@ -70,6 +84,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.workload != "llama8b":
+        print(json.dumps(OTHER[args.workload](args)), flush=True)
+        return
     w = synth.WORKLOADS[2]
     nl = args.layers or w.layers
     B, Hq, Hkv, D, S = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.context
@@ -337,6 +354,367 @@ def cpu_baseline(w, seconds, L):
             "sample": f"{units} of the step's {full} (layer, batch, kv head) units "
                       f"(append + exact dequant + fp64 attention over {L} positions), "
                       f"{dt:.2f} s timed; a full step extrapolates to {dt * full / units:.1f} s"}
+
+
+# ---------------------------------------------------------------------------------------
+# The other workloads (--workload).  Each returns the JSON object of its line.
+
+def row_bytes(fmt, D, gk, gv):
+    """Bytes of K + V codes and scales per (position, kv head)."""
+    if fmt == "int4":
+        return (D // 2 + 4 * (D // gk)) + (D // 2 + 4 * (D // gv))
+    if fmt == "int8":
+        return 2 * (D + 4)
+    return 2 * (D // 2 + 4)                               # codec: indices + one scale
+
+
+def _timed(run, steps):
+    """ms per call of `run` over exactly `steps` calls, events on the current stream
+    (torch.cuda.synchronize on both sides), and the wall seconds of the region."""
+    import torch
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+
+def _runner(args, fn):
+    """A HIP-graph replay of fn(stream) (or eager calls with --eager), warmed up."""
+    import torch
+    cur = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        fn(cur.cuda_stream)
+    torch.cuda.synchronize()
+    if args.eager:
+        return lambda: fn(torch.cuda.current_stream().cuda_stream)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        fn(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    return g.replay
+
+
+def _line(args, metric, value, ms, config, roofline, cpu, extra, dtype="f32"):
+    out = {"metric": metric, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+           "data": "synthetic", "config": config, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)}
+    out.update(extra)
+    out["roofline"] = roofline
+    out["cpu_baseline"] = cpu
+    return out
+
+
+def _roofline(kernel, nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": int(nbytes), "avg_launch_us": round(us, 2)}
+
+
+DECODE_MODES = {   # workload id, cache format
+    "mha7b-decode": (3, "int4"),
+    "ctx128k-int4": (5, "int4"),
+    "ctx128k-int8": (5, "int8"),
+    "gemma-codec": (4, "codec"),
+}
+
+
+def bench_decode(args):
+    """One decode step over every layer of a workload: for appending workloads
+    kvq_append_decode_attn per layer (append at position `context`, attend over
+    context + 1), otherwise kvq_decode_attn.  Window layers keep a ring of `window` rows."""
+    import torch
+    import int4_quantized_kv_amd as kvq
+    import synth
+    wid, fmt = DECODE_MODES[args.workload]
+    w = synth.WORKLOADS[wid]
+    dev = "cuda:0"
+    nl = args.layers or w.layers
+    B, Hq, Hkv, D, S = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.context
+    L = S + 1 if w.append else S
+    rb = row_bytes(fmt, D, w.group_k, w.group_v)
+    LIB = kvq.LIB
+    layers, ws_need = [], 0
+    attend_bytes = step_bytes = 0
+    for li in range(nl):
+        lay = Layer()
+        lay.W = w.layer_window(li)
+        cap = lay.W if lay.W else L
+        lay.desc = kvq.make_desc(fmt, B, Hkv, D, cap, w.group_k, w.group_v)
+        k, v, q, kn, vn = synth.layer_inputs(w, li, dev)
+        lay.dc = kvq.DeviceCache(lay.desc, dev)
+        lo = max(0, S - cap)          # the rows a ring of `cap` slots still holds
+        kvq.kvq_quantize_prefill(lay.desc, lay.dc.c, k[:, :, lo:].contiguous(),
+                                 v[:, :, lo:].contiguous(), lo, S - lo)
+        del k, v
+        lay.q, lay.kn, lay.vn = q, kn, vn
+        lay.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        lay.dref, lay.cref = ctypes.byref(lay.desc), ctypes.byref(lay.dc.c)
+        ws_need = max(ws_need, kvq.kvq_decode_workspace_bytes(lay.desc, Hq, L, lay.W))
+        # the step reads the cached rows of the horizon (all but the new one when it
+        # appends), the new row's fp16 K/V, q; writes the new row's codes and the output.
+        # The attention call alone (for the roofline) reads every row of the horizon.
+        rows = min(L, lay.W) if lay.W else L
+        qo = B * Hq * D * 2 + B * Hq * D * 4
+        attend_bytes += B * Hkv * rows * rb + qo
+        if w.append:
+            step_bytes += B * Hkv * ((rows - 1) * rb + rb + 2 * D * 2) + qo
+        else:
+            step_bytes += B * Hkv * rows * rb + qo
+        layers.append(lay)
+    torch.cuda.synchronize()
+    ws = torch.zeros(ws_need // 4 + 4, dtype=torch.float32, device=dev)
+    ws_bytes = ws.numel() * 4
+    lens = (ctypes.c_int32 * B)(*([L] * B))
+
+    def step(stream, attend_only=False):
+        sp = ctypes.c_void_p(stream)
+        for lay in layers:
+            if w.append and not attend_only:
+                st = LIB.kvq_append_decode_attn(lay.dref, lay.cref, lay.kn.data_ptr(), lay.vn.data_ptr(),
+                                                lay.q.data_ptr(), Hq, lens, lay.W, 0.0, 0,
+                                                lay.out.data_ptr(), ws.data_ptr(), ws_bytes, sp)
+            else:
+                st = LIB.kvq_decode_attn(lay.dref, lay.cref, lay.q.data_ptr(), Hq, lens, lay.W, 0.0, 0,
+                                         lay.out.data_ptr(), ws.data_ptr(), ws_bytes, sp)
+            if st:
+                raise kvq.KvqError(st, "decode step")
+
+    run = _runner(args, step)
+    ms_step, wall = _timed(run, args.steps)
+    if w.append:     # the attention calls alone, in their own pass
+        attn = _runner(args, lambda st: step(st, attend_only=True))
+        attn_ms, _ = _timed(attn, args.steps)
+    else:
+        attn_ms = ms_step
+    mfma = fmt == "int4" and D == 128 and w.group_v == 128
+    kern = ("kvq_decode_attn: decode_int4_mfma_kernel (splits merged in-kernel)" if mfma else
+            f"kvq_decode_attn: decode_splitk_kernel<{D}, {Hq // Hkv}, {fmt}> + merge_kernel")
+    roof = _roofline(kern, attend_bytes / nl, attn_ms * 1e3 / nl)
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    cfg = {"workload": w.name, "format": fmt, "layers": nl, "batch": B, "q_heads": Hq,
+           "kv_heads": Hkv, "head_dim": D, "context": L, "append": w.append,
+           "window_layers": min(nl, w.window_layers), "window": w.window,
+           "launch": "eager" if args.eager else "hip-graph",
+           "num_splits": kvq.kvq_plan_splits(layers[-1].desc, Hq, min(L, layers[-1].W or L))}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_decode(w, fmt, args.cpu_seconds, L)
+    names = {"mha7b-decode": "MHA-7B shape, 20K ctx, B 8", "ctx128k-int4": "128K ctx, B 1, INT4",
+             "ctx128k-int8": "128K ctx, B 1, INT8 per-token",
+             "gemma-codec": "Gemma-3-4B shape, WHT+Lloyd-Max codec, window 1024 x29 + global x5"}
+    return _line(args, f"decode step: effective KV GB/s ({names[args.workload]})", gbs, ms_step, cfg,
+                 roof, cpu, {"tok_per_s": round(B / (ms_step * 1e-3), 1), "bytes_per_step": step_bytes,
+                             "wall_s_timed": round(wall, 4)})
+
+
+def bench_prefill(args):
+    """kvq_quantize_prefill of one MHA-7B-shaped layer (K and V [8, 32, 20480, 128] fp16
+    into the INT4 cache), the same call repeated; the inputs (2.68 GB) do not fit the
+    Infinity Cache, so every call streams from HBM."""
+    import torch
+    import int4_quantized_kv_amd as kvq
+    import synth
+    w = synth.WORKLOADS[3]
+    dev = "cuda:0"
+    B, Hkv, D, S = w.batch, w.kv_heads, w.head_dim, w.context
+    desc = kvq.make_desc("int4", B, Hkv, D, S, w.group_k, w.group_v)
+    dc = kvq.DeviceCache(desc, dev)
+    k, v, _, _, _ = synth.layer_inputs(w, 0, dev)
+    dref, cref = ctypes.byref(desc), ctypes.byref(dc.c)
+
+    def step(stream):
+        st = kvq.LIB.kvq_quantize_prefill(dref, cref, k.data_ptr(), v.data_ptr(), 0, S,
+                                          ctypes.c_void_p(stream))
+        if st:
+            raise kvq.KvqError(st, "kvq_quantize_prefill")
+
+    run = _runner(args, step)
+    ms, wall = _timed(run, args.steps)
+    rb = row_bytes("int4", D, w.group_k, w.group_v)
+    nbytes = B * Hkv * S * (2 * D * 2 + rb)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cfg = {"workload": w.name + "-prefill", "format": "int4", "layers_timed": 1, "batch": B,
+           "kv_heads": Hkv, "head_dim": D, "positions": S, "launch": "eager" if args.eager else "hip-graph"}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_seconds)
+    return _line(args, "prefill quantize: effective GB/s (fp16 read + codes/scales written, MHA-7B shape, 20K ctx)",
+                 gbs, ms, cfg, _roofline("kvq_quantize_prefill: quant_int4_kernel", nbytes, ms * 1e3), cpu,
+                 {"bytes_per_layer": nbytes, "ms_32_layers": round(32 * ms, 3), "wall_s_timed": round(wall, 4)})
+
+
+def bench_dequant(args):
+    """kvq_dequant of K and V (all 8192 positions) of 8 distinct Llama-3-8B-shaped layer
+    caches into one fp32 buffer: 16 calls per step."""
+    import torch
+    import int4_quantized_kv_amd as kvq
+    import synth
+    w = synth.WORKLOADS[2]
+    dev = "cuda:0"
+    nl = args.layers or 8
+    B, Hkv, D, S = w.batch, w.kv_heads, w.head_dim, w.context
+    desc = kvq.make_desc("int4", B, Hkv, D, S, w.group_k, w.group_v)
+    caches = []
+    for li in range(nl):
+        k, v, _, _, _ = synth.layer_inputs(w, li, dev)
+        dc = kvq.DeviceCache(desc, dev)
+        kvq.kvq_quantize_prefill(desc, dc.c, k, v, 0, S)
+        del k, v
+        caches.append(dc)
+    out = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=dev)
+    dref = ctypes.byref(desc)
+    crefs = [ctypes.byref(dc.c) for dc in caches]
+
+    def step(stream):
+        for cref in crefs:
+            for kv in (0, 1):
+                st = kvq.LIB.kvq_dequant(dref, cref, kv, 0, S, out.data_ptr(), ctypes.c_void_p(stream))
+                if st:
+                    raise kvq.KvqError(st, "kvq_dequant")
+
+    run = _runner(args, step)
+    ms, wall = _timed(run, args.steps)
+    per_k = B * Hkv * S * (D // 2 + 4 * (D // w.group_k) + 4 * D)
+    per_v = B * Hkv * S * (D // 2 + 4 * (D // w.group_v) + 4 * D)
+    nbytes = nl * (per_k + per_v)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cfg = {"workload": w.name + "-dequant", "format": "int4", "layer_caches": nl, "batch": B,
+           "kv_heads": Hkv, "head_dim": D, "positions": S, "launch": "eager" if args.eager else "hip-graph"}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_dequant(w, args.cpu_seconds)
+    return _line(args, "dequant: effective GB/s (codes + scales read, fp32 written; Llama-3-8B shape, 8K)",
+                 gbs, ms, cfg, _roofline("kvq_dequant: dequant_int4_kernel", nbytes / (2 * nl),
+                                         ms * 1e3 / (2 * nl)), cpu,
+                 {"bytes_per_step": nbytes, "wall_s_timed": round(wall, 4)})
+
+
+OTHER = {"mha7b-prefill": bench_prefill, "mha7b-decode": bench_decode, "ctx128k-int4": bench_decode,
+         "ctx128k-int8": bench_decode, "gemma-codec": bench_decode, "dequant": bench_dequant}
+
+
+def _oracle_rows(fmt, x16, gk, gv, kv):
+    """Oracle quantization of rows [N, D] and their exact dequantization (fp64)."""
+    from oracle import codec, quant
+    if fmt == "int4":
+        g = gk if kv == 0 else gv
+        c, s = quant.quantize_int4(x16, g)
+        return (c, s), lambda cs: quant.dequantize_int4_exact(cs[0], cs[1], g)
+    if fmt == "int8":
+        return quant.quantize_int8(x16), lambda cs: quant.dequantize_int8_exact(cs[0], cs[1])
+    idx, s, _ = codec.encode(x16)
+    return (idx, s), lambda cs: codec.decode(cs[0], cs[1])
+
+
+def cpu_baseline_decode(w, fmt, seconds, L):
+    """The oracle (never tuned) on one host core, one (layer, batch, kv head) unit at a
+    time until `seconds` of timed work: (append the new row,) exact dequantization of
+    the attended rows, fp64 attention for the unit's query heads.  The unit's cache (the
+    prefill) is quantized outside the timer."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import synth
+    from oracle import attention
+    G = w.q_heads // w.kv_heads
+    D = w.head_dim
+    rb = row_bytes(fmt, D, w.group_k, w.group_v)
+    units = 0
+    nbytes = 0
+    dt = 0.0
+    layer = 0
+    while dt < seconds and layer < w.layers:
+        W = w.layer_window(layer)
+        rows = min(L, W) if W else L
+        k, v, q, kn, vn = (None if t is None else t.cpu().numpy()
+                           for t in synth.layer_inputs(w, layer, "cuda:0"))
+        lo = L - rows                                   # first attended position
+        for b in range(w.batch):
+            for h in range(w.kv_heads):
+                if dt >= seconds:
+                    break
+                kr, vr = k[b, h, lo:], v[b, h, lo:]
+                (kc, kdq), (vc, vdq) = _oracle_rows(fmt, kr, w.group_k, w.group_v, 0), \
+                    _oracle_rows(fmt, vr, w.group_k, w.group_v, 1)
+                qq = q[b, h * G:(h + 1) * G]
+                with threadpool_limits(1):
+                    t0 = time.perf_counter()
+                    kh, vh = kdq(kc), vdq(vc)
+                    if w.append:
+                        (nkc, nkdq), (nvc, nvdq) = _oracle_rows(fmt, kn[b, h][None], w.group_k, w.group_v, 0), \
+                            _oracle_rows(fmt, vn[b, h][None], w.group_k, w.group_v, 1)
+                        kh = np.concatenate([kh, nkdq(nkc)])
+                        vh = np.concatenate([vh, nvdq(nvc)])
+                    attention.decode_attention(qq[None], kh[None, None], vh[None, None], [kh.shape[0]])
+                    dt += time.perf_counter() - t0
+                units += 1
+                nbytes += rows * rb + G * D * 6 + (4 * D if w.append else 0)
+        layer += 1
+        del k, v
+    full = w.batch * w.kv_heads * w.layers
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} of the step's {full} (layer, batch, kv head) units "
+                      f"({'append + ' if w.append else ''}exact dequant + fp64 attention), "
+                      f"{dt:.2f} s timed"}
+
+
+def cpu_baseline_prefill(w, seconds):
+    """The oracle's INT4 quantization of the K and V rows of one (batch, kv head) at a
+    time, on one host core, until `seconds` of timed work."""
+    import synth
+    from threadpoolctl import threadpool_limits
+    from oracle import quant
+    D, S = w.head_dim, w.context
+    k, v, _, _, _ = synth.layer_inputs(w, 0, "cuda:0")
+    units, dt = 0, 0.0
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            if dt >= seconds:
+                break
+            kr, vr = k[b, h].cpu().numpy(), v[b, h].cpu().numpy()
+            with threadpool_limits(1):
+                t0 = time.perf_counter()
+                quant.quantize_int4(kr, w.group_k)
+                quant.quantize_int4(vr, w.group_v)
+                dt += time.perf_counter() - t0
+            units += 1
+    nbytes = units * S * (2 * D * 2 + row_bytes("int4", D, w.group_k, w.group_v))
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} of the layer's {w.batch * w.kv_heads} (batch, kv head) units "
+                      f"({S} K and V rows each), {dt:.2f} s timed"}
+
+
+def cpu_baseline_dequant(w, seconds):
+    """The oracle's fp32 dequantization of the K and V rows of one (batch, kv head) at a
+    time, on one host core, until `seconds` of timed work."""
+    import synth
+    from threadpoolctl import threadpool_limits
+    from oracle import quant
+    D, S = w.head_dim, w.context
+    k, v, _, _, _ = synth.layer_inputs(w, 0, "cuda:0")
+    units, dt = 0, 0.0
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            if dt >= seconds:
+                break
+            kc, ks = quant.quantize_int4(k[b, h].cpu().numpy(), w.group_k)
+            vc, vs = quant.quantize_int4(v[b, h].cpu().numpy(), w.group_v)
+            with threadpool_limits(1):
+                t0 = time.perf_counter()
+                quant.dequantize_int4(kc, ks, w.group_k)
+                quant.dequantize_int4(vc, vs, w.group_v)
+                dt += time.perf_counter() - t0
+            units += 1
+    per = S * ((D // 2 + 4 * (D // w.group_k) + 4 * D) + (D // 2 + 4 * (D // w.group_v) + 4 * D))
+    return {"value": round(units * per / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} of a layer's {w.batch * w.kv_heads} (batch, kv head) units "
+                      f"({S} K and V rows each), {dt:.2f} s timed"}
 
 
 if __name__ == "__main__":
