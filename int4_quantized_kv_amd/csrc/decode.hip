@@ -27,29 +27,56 @@ namespace {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 
-// Dequantize the 8 values lane c owns of row `row` (cache row index b*Hkv*C + slot).
+// The packed bytes lane c owns of one row (cache row index b*Hkv*C + slot): its code
+// word(s) and the scale of its group, for K and V.  Loaded for several rows before any
+// of them is used, so that a lane keeps several rows' transfers in flight.
+struct RawRow {
+  uint32_t k[2], v[2];   // INT4 / codec: k[0], v[0] (8 nibbles); INT8: both (8 bytes)
+  float sk, sv;
+};
+
 template <int D, int FMT>
-__device__ __forceinline__ void load_row(const void* codes, const float* scales, int g,
-                                         size_t row, int c, const float* lv, float x[8]) {
+__device__ __forceinline__ RawRow load_raw(const DecodeArgs& a, size_t row, int c) {
   constexpr int LPR = D / 8;
+  RawRow r;
+  if (FMT == KVQ_INT8_TOKEN) {
+    const uint2 kw = reinterpret_cast<const uint2*>(a.k_codes)[row * LPR + c];
+    const uint2 vw = reinterpret_cast<const uint2*>(a.v_codes)[row * LPR + c];
+    r.k[0] = kw.x; r.k[1] = kw.y; r.v[0] = vw.x; r.v[1] = vw.y;
+    r.sk = a.k_scales[row];
+    r.sv = a.v_scales[row];
+  } else {
+    r.k[0] = reinterpret_cast<const uint32_t*>(a.k_codes)[row * LPR + c];
+    r.v[0] = reinterpret_cast<const uint32_t*>(a.v_codes)[row * LPR + c];
+    r.k[1] = r.v[1] = 0u;
+    if (FMT == KVQ_INT4_G) {
+      r.sk = a.k_scales[row * (D / a.gk) + (8 * c) / a.gk];
+      r.sv = a.v_scales[row * (D / a.gv) + (8 * c) / a.gv];
+    } else {
+      r.sk = a.k_scales[row];
+      r.sv = a.v_scales[row];
+    }
+  }
+  return r;
+}
+
+// The 8 code values of a code word pair as floats, before the scale (integers for INT4
+// and INT8, codebook levels for the codec).  A lane's 8 values share one scale (groups
+// are powers of two of at least 32), which is applied once per dot product instead.
+template <int FMT>
+__device__ __forceinline__ void codes_f32(const uint32_t w[2], const float* lv, float x[8]) {
   if (FMT == KVQ_INT4_G) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[row * LPR + c];
-    const float s = scales[row * (D / g) + (8 * c) / g];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = (float)nib_s(w, j) * s;
+    for (int j = 0; j < 8; ++j) x[j] = (float)nib_s(w[0], j);
   } else if (FMT == KVQ_INT8_TOKEN) {
-    const uint2 w = reinterpret_cast<const uint2*>(codes)[row * LPR + c];
-    const float s = scales[row];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[j] = (float)(int8_t)((w.x >> (8 * j)) & 255u) * s;
-      x[j + 4] = (float)(int8_t)((w.y >> (8 * j)) & 255u) * s;
+      x[j] = (float)(int8_t)((w[0] >> (8 * j)) & 255u);
+      x[j + 4] = (float)(int8_t)((w[1] >> (8 * j)) & 255u);
     }
   } else {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[row * LPR + c];
-    const float s = scales[row];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = lv[nib_u(w, j)] * s;
+    for (int j = 0; j < 8; ++j) x[j] = lv[nib_u(w[0], j)];
   }
 }
 
@@ -97,36 +124,71 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
   }
 
+  // U rows per lane group per step, their loads issued before any is used.  The step
+  // scores its U rows, rescales the accumulators once by 2^(m - m_new) (1 when no
+  // head's maximum grew; 0 for the first rows, m being -inf before them: a multiply
+  // costs less than the register copies the compiler adds around a conditional
+  // rescale), then adds the U rows.  Rows past pe (last step only) are loaded clamped to pe - 1 and scored
+  // -inf; they are the same rows for the LPR lanes of a row, and every lane of a row
+  // takes part in the row's lane sums.
+  constexpr int U = 4;
   const size_t bh = (size_t)b * a.Hkv + kvh;
-  for (int t = ps + grp; t < pe; t += NGRP) {
-    const size_t row = bh * a.cap + (t % a.cap);
-    float kx[8], vx[8];
-    load_row<D, FMT>(a.k_codes, a.k_scales, a.gk, row, c, lv, kx);
-    load_row<D, FMT>(a.v_codes, a.v_scales, a.gv, row, c, lv, vx);
-    float z[G];
+  auto do_step = [&](const RawRow (&raw)[U], int nvalid) {
+    float z[U][G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float d = 0.0f;
+    for (int u = 0; u < U; ++u) {
+      float kc[8];
+      codes_f32<FMT>(raw[u].k, lv, kc);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) d = __builtin_fmaf(q[h][j], kx[j], d);
-      z[h] = d;
-    }
-    // the LPR lanes of a row share the trip count, so the row's shuffles are complete
+      for (int h = 0; h < G; ++h) {
+        float d = 0.0f;
 #pragma unroll
-    for (int msk = 1; msk < LPR; msk <<= 1) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) z[h] += __shfl_xor(z[h], msk);
+        for (int j = 0; j < 8; ++j) d = __builtin_fmaf(q[h][j], kc[j], d);
+        // the lane's partial dot product times its K scale, summed over the row
+        const float zz = lane_group_sum<LPR>(d * raw[u].sk);
+        z[u][h] = u < nvalid ? zz : NEG_INF;
+      }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mn = fmaxf(m[h], z[h]);
-      const float corr = fast_exp2(m[h] - mn);
-      const float p = fast_exp2(z[h] - mn);
-      l[h] = __builtin_fmaf(l[h], corr, p);
+      float mn = m[h];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[h][j] = __builtin_fmaf(acc[h][j], corr, p * vx[j]);
+      for (int u = 0; u < U; ++u) mn = fmaxf(mn, z[u][h]);
+      const float corr = fast_exp2(m[h] - mn);   // (row 0 is valid: mn > -inf)
+      l[h] *= corr;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[h][j] *= corr;
       m[h] = mn;
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vc[8];
+      codes_f32<FMT>(raw[u].v, lv, vc);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = fast_exp2(z[u][h] - m[h]);
+        l[h] += p;
+        const float pv = p * raw[u].sv;   // the V scale folded into the weight
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[h][j] = __builtin_fmaf(vc[j], pv, acc[h][j]);
+      }
+    }
+  };
+  int t0 = ps + grp;
+  for (; t0 + (U - 1) * NGRP < pe; t0 += U * NGRP) {
+    RawRow raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = load_raw<D, FMT>(a, bh * a.cap + ((t0 + u * NGRP) % a.cap), c);
+    do_step(raw, U);
+  }
+  if (t0 < pe) {
+    RawRow raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(t0 + u * NGRP, pe - 1);
+      raw[u] = load_raw<D, FMT>(a, bh * a.cap + (t % a.cap), c);
+    }
+    do_step(raw, (pe - t0 + NGRP - 1) / NGRP);
   }
 
   if (c == 0) {
@@ -270,7 +332,8 @@ int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
       mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group))
     return plan_splits_mfma(units, span);
   const int32_t target = 2048;       // workgroups: 8 per CU on 256 CUs
-  const int32_t min_rows = 256;      // positions per split worth a workgroup
+  const int32_t min_rows = 64;       // positions per split worth a workgroup (short
+                                     // contexts need many splits to fill the chip)
   int32_t n = (target + units - 1) / units;
   const int32_t by_span = (span + min_rows - 1) / min_rows;
   if (n > by_span) n = by_span;

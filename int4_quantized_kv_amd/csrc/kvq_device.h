@@ -58,6 +58,31 @@ __device__ __forceinline__ void wht_row(float v[8], int c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum over aligned groups of LANES (2, 4, 8, 16 or 32) lanes, left in every lane of the
+// group, without an LDS round trip: quad swaps for partners 1 and 2, the half-row and
+// row mirrors (each pairs a lane with one in the other half of its group of 8 / 16)
+// and, for 32 lanes, the gfx950 row-pair swap (v_permlane16_swap of a register with a
+// copy of itself leaves row r in one and row r ^ 1 in the other; written in assembly,
+// with the s_nop covering the VALU-write -> permlane-read hazard).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                 0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int LANES>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  if (LANES >= 2) x = dpp_add<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  if (LANES >= 4) x = dpp_add<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  if (LANES >= 8) x = dpp_add<0x141>(x);   // row_half_mirror
+  if (LANES >= 16) x = dpp_add<0x140>(x);  // row_mirror
+  if (LANES >= 32) {
+    uint32_t p = __builtin_bit_cast(uint32_t, x), q = p;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(p), "+v"(q));
+    x = __builtin_bit_cast(float, p) + __builtin_bit_cast(float, q);
+  }
+  return x;
+}
+
 // Enqueue `kernel(args)` and return the runtime's status for this launch only (the
 // thread's last-error slot may hold an unrelated earlier status, e.g. a not-ready
 // query made by the caller, so it is never consulted).
