@@ -30,14 +30,17 @@ KVQ_HD float kvq_div_exact(float x, float s, float r) {
 }
 
 // INT4 group scale from the group's amax: fl32(amax / 7), 1 for an all-zero group.
+// The quotient by the constant is the corrected product above with r = fl32(1/7)
+// (constant-folded); for every fp16 amax it equals the IEEE quotient (checked
+// exhaustively on the host), at 3 instructions instead of a full divide.
 KVQ_HD float kvq_int4_scale(float amax) {
-  float s = amax / 7.0f;
+  float s = kvq_div_exact(amax, 7.0f, 1.0f / 7.0f);
   return s == 0.0f ? 1.0f : s;
 }
 
-// INT8 per-token scale: max(fl32(amax / 127), 1e-8f).
+// INT8 per-token scale: max(fl32(amax / 127), 1e-8f), the quotient formed as above.
 KVQ_HD float kvq_int8_scale(float amax) {
-  float s = amax / 127.0f;
+  float s = kvq_div_exact(amax, 127.0f, 1.0f / 127.0f);
   return s < 1e-8f ? 1e-8f : s;
 }
 

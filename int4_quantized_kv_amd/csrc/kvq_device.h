@@ -21,6 +21,17 @@ __device__ __forceinline__ void load8_f16(const uint16_t* p, float x[8]) {
   }
 }
 
+// Eight fp16 values already loaded as one 16-byte word, widened to fp32 (exact).
+__device__ __forceinline__ void f16x8_unpack(const uint4& r, float x[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+    x[2 * i] = (float)h.x;
+    x[2 * i + 1] = (float)h.y;
+  }
+}
+
 // Signed 4-bit field j (0..7) of a packed word, as an int in -8..7.
 __device__ __forceinline__ int nib_s(uint32_t w, int j) {
   return (int32_t)(w << (28 - 4 * j)) >> 28;

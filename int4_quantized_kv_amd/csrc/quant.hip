@@ -10,7 +10,12 @@
 // D elements spans D/8 consecutive lanes, a group of g elements g/8 lanes, so the
 // group amax is an xor-shuffle reduction inside the wave.  Each lane writes its 8
 // codes as one 32-bit word (INT4) or one 64-bit word (INT8).  K and V are the two
-// grid rows (blockIdx.y) of one launch.  Streaming kernel: HBM bound.
+// grid rows (blockIdx.y) of one launch.  Streaming kernel: HBM bound.  Each lane takes
+// U chunks of the grid-stride sequence per iteration and issues their loads before
+// using any, so that enough bytes are in flight to cover the memory latency (a row's
+// lanes are consecutive and the stride is a multiple of 256, so the lanes of a row or
+// group are all in or all out of an iteration's chunk u).
+constexpr int U = 4;
 #include "kvq_arith.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -18,153 +23,171 @@
 namespace kvq {
 namespace {
 
-__device__ __forceinline__ int slot_of(const SlotMap& m, int b, int t) {
-  const int p = m.append ? m.pos[b] : m.start + t;
-  return p % m.cap;
+// Grid: (chunks of a (b, h) pair, K or V (quantizers), pairs bh = blockIdx.z + k *
+// gridDim.z; gridDim.z is capped at 65535).  A pair's
+// rows are n consecutive source rows of D/8 16-byte chunks; chunk ci is row ci / lpr,
+// lane-chunk ci % lpr (lpr a power of two: shifts).  The cache slot of row t is
+// (base + t) mod cap with base < cap and t < n <= cap: one conditional subtract.
+__device__ __forceinline__ int log2i(int x) { return 31 - __builtin_clz(x); }
+
+template <bool INT8>
+__device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
+  const int isv = blockIdx.y;
+  const int b = bh / a.Hkv;
+  const uint16_t* src = (isv ? a.v : a.k);
+  float* scales = isv ? a.v_scales : a.k_scales;
+  const int g = INT8 ? a.D : (isv ? a.gv : a.gk);
+  // lpr, lpg and gpr are powers of two (D in {64, 128, 256}, g a power of two >= 32)
+  const int lpr = a.D >> 3, lsh = log2i(lpr), lpg = g >> 3, gsh = log2i(lpg);
+  const int gprsh = log2i(a.D / g);
+  const int cap = a.map.cap;
+  const int base = (a.map.append ? a.map.pos[b] : a.map.start) % cap;
+  const uint32_t npair = (uint32_t)a.map.n * (uint32_t)lpr;
+  const uint4* srcp = reinterpret_cast<const uint4*>(src) + (size_t)bh * npair;
+  const size_t row0 = (size_t)bh * cap;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i0 = blockIdx.x * blockDim.x + threadIdx.x; i0 < npair; i0 += U * stride) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = i0 + u * stride;
+      if (i < npair) raw[u] = srcp[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = i0 + u * stride;
+      if (i >= npair) break;
+      const int t = (int)(i >> lsh), c = (int)(i & (lpr - 1));
+      float x[8];
+      f16x8_unpack(raw[u], x);
+      float am = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+      // a group is lpg aligned consecutive lanes, all of which take this chunk
+      for (int m = 1; m < lpg; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+      const float sc = INT8 ? kvq_int8_scale(am) : kvq_int4_scale(am);
+      const float r = 1.0f / sc;
+      int slot = base + t;
+      if (slot >= cap) slot -= cap;
+      const size_t drow = row0 + slot;
+      if (INT8) {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float q = fminf(fmaxf(rintf(kvq_div_exact(x[j], sc, r)), -128.0f), 127.0f);
+          const uint32_t byte = (uint32_t)(int)q & 255u;
+          if (j < 4) w0 |= byte << (8 * j); else w1 |= byte << (8 * (j - 4));
+        }
+        reinterpret_cast<uint2*>(isv ? a.v_codes : a.k_codes)[(drow << lsh) + c] = make_uint2(w0, w1);
+        if (c == 0) scales[drow] = sc;
+      } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float q = fminf(fmaxf(rintf(kvq_div_exact(x[j], sc, r)), -7.0f), 7.0f);
+          w |= ((uint32_t)(int)q & 15u) << (4 * j);
+        }
+        reinterpret_cast<uint32_t*>(isv ? a.v_codes : a.k_codes)[(drow << lsh) + c] = w;
+        if ((c & (lpg - 1)) == 0) scales[(drow << gprsh) + (c >> gsh)] = sc;
+      }
+    }
+  }
 }
 
 __global__ void __launch_bounds__(256) quant_int4_kernel(QuantArgs a) {
-  const int isv = blockIdx.y;
-  const uint16_t* src = isv ? a.v : a.k;
-  uint32_t* codes = reinterpret_cast<uint32_t*>(isv ? a.v_codes : a.k_codes);
-  float* scales = isv ? a.v_scales : a.k_scales;
-  const int g = isv ? a.gv : a.gk;
-  const int lpg = g >> 3, lpr = a.D >> 3, gpr = a.D / g;
-  const uint32_t total = (uint32_t)a.rows * (uint32_t)lpr;
-  const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const uint32_t row = i / lpr;
-    const int c = (int)(i - row * lpr);
-    float x[8];
-    load8_f16(src + (size_t)i * 8, x);
-    float am = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
-    // groups are lpg aligned consecutive lanes, entirely inside or outside the loop
-    for (int m = 1; m < lpg; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
-    const float s = kvq_int4_scale(am);
-    const float r = 1.0f / s;
-    uint32_t w = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float y = kvq_div_exact(x[j], s, r);
-      const float q = fminf(fmaxf(rintf(y), -7.0f), 7.0f);
-      w |= ((uint32_t)(int)q & 15u) << (4 * j);
-    }
-    const uint32_t bh = row / (uint32_t)a.map.n;
-    const int t = (int)(row - bh * a.map.n);
-    const int b = (int)(bh / (uint32_t)a.Hkv);
-    const size_t drow = (size_t)bh * a.map.cap + slot_of(a.map, b, t);
-    codes[drow * lpr + c] = w;
-    if ((c & (lpg - 1)) == 0) scales[drow * gpr + c / lpg] = s;
-  }
+  for (int bh = blockIdx.z; bh < a.B * a.Hkv; bh += gridDim.z) quant_pair<false>(a, bh);
 }
-
 __global__ void __launch_bounds__(256) quant_int8_kernel(QuantArgs a) {
-  const int isv = blockIdx.y;
-  const uint16_t* src = isv ? a.v : a.k;
-  uint2* codes = reinterpret_cast<uint2*>(isv ? a.v_codes : a.k_codes);
-  float* scales = isv ? a.v_scales : a.k_scales;
-  const int lpr = a.D >> 3;
-  const uint32_t total = (uint32_t)a.rows * (uint32_t)lpr;
+  for (int bh = blockIdx.z; bh < a.B * a.Hkv; bh += gridDim.z) quant_pair<true>(a, bh);
+}
+
+// out[b, h, t, :] = fl32(code * scale) for positions start + t, t < n; one (b, h) pair
+// per blockIdx.z, mapped as the quantizers.
+template <bool INT8>
+__device__ __forceinline__ void dequant_pair(const DequantArgs& a, int bh) {
+  const int g = INT8 ? a.D : a.g;
+  const int lpr = a.D >> 3, lsh = log2i(lpr), gsh = log2i(g >> 3), gprsh = log2i(a.D / g);
+  const int cap = a.cap;
+  const int base = a.start % cap;
+  const uint32_t npair = (uint32_t)a.n * (uint32_t)lpr;
+  const size_t row0 = (size_t)bh * cap;
+  float4* outp = reinterpret_cast<float4*>(a.out) + (size_t)bh * npair * 2;
   const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const uint32_t row = i / lpr;
-    const int c = (int)(i - row * lpr);
-    float x[8];
-    load8_f16(src + (size_t)i * 8, x);
-    float am = 0.0f;
+  for (uint32_t i0 = blockIdx.x * blockDim.x + threadIdx.x; i0 < npair; i0 += U * stride) {
+    uint2 wr[U];
+    float sr[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
-    for (int m = 1; m < lpr; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
-    const float s = kvq_int8_scale(am);
-    const float r = 1.0f / s;
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float y = kvq_div_exact(x[j], s, r);
-      const float q = fminf(fmaxf(rintf(y), -128.0f), 127.0f);
-      const uint32_t byte = (uint32_t)(int)q & 255u;
-      if (j < 4) w0 |= byte << (8 * j); else w1 |= byte << (8 * (j - 4));
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = i0 + u * stride;
+      if (i < npair) {
+        const int t = (int)(i >> lsh), c = (int)(i & (lpr - 1));
+        int slot = base + t;
+        if (slot >= cap) slot -= cap;
+        const size_t drow = row0 + slot;
+        if (INT8) {
+          wr[u] = reinterpret_cast<const uint2*>(a.codes)[(drow << lsh) + c];
+          sr[u] = a.scales[drow];
+        } else {
+          wr[u].x = reinterpret_cast<const uint32_t*>(a.codes)[(drow << lsh) + c];
+          wr[u].y = 0u;
+          sr[u] = a.scales[(drow << gprsh) + (c >> gsh)];
+        }
+      }
     }
-    const uint32_t bh = row / (uint32_t)a.map.n;
-    const int t = (int)(row - bh * a.map.n);
-    const int b = (int)(bh / (uint32_t)a.Hkv);
-    const size_t drow = (size_t)bh * a.map.cap + slot_of(a.map, b, t);
-    codes[drow * lpr + c] = make_uint2(w0, w1);
-    if (c == 0) scales[drow] = s;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = i0 + u * stride;
+      if (i >= npair) break;
+      const float s = sr[u];
+      float v[8];
+      if (INT8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = (float)(int8_t)((wr[u].x >> (8 * j)) & 255u) * s;
+          v[j + 4] = (float)(int8_t)((wr[u].y >> (8 * j)) & 255u) * s;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (float)nib_s(wr[u].x, j) * s;
+      }
+      outp[2 * (size_t)i] = make_float4(v[0], v[1], v[2], v[3]);
+      outp[2 * (size_t)i + 1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
   }
 }
 
-// out[b, h, t, :] = fl32(code * scale) for positions start + t, t < n.
 __global__ void __launch_bounds__(256) dequant_int4_kernel(DequantArgs a) {
-  const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.codes);
-  const int lpr = a.D >> 3, lpg = a.g >> 3, gpr = a.D / a.g;
-  const uint32_t total = (uint32_t)a.B * a.Hkv * a.n * lpr;
-  const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const uint32_t row = i / lpr;
-    const int c = (int)(i - row * lpr);
-    const uint32_t bh = row / (uint32_t)a.n;
-    const int t = (int)(row - bh * a.n);
-    const size_t drow = (size_t)bh * a.cap + (a.start + t) % a.cap;
-    const uint32_t w = codes[drow * lpr + c];
-    const float s = a.scales[drow * gpr + c / lpg];
-    float4 o0, o1;
-    o0.x = (float)nib_s(w, 0) * s; o0.y = (float)nib_s(w, 1) * s;
-    o0.z = (float)nib_s(w, 2) * s; o0.w = (float)nib_s(w, 3) * s;
-    o1.x = (float)nib_s(w, 4) * s; o1.y = (float)nib_s(w, 5) * s;
-    o1.z = (float)nib_s(w, 6) * s; o1.w = (float)nib_s(w, 7) * s;
-    float4* out = reinterpret_cast<float4*>(a.out + (size_t)i * 8);
-    out[0] = o0;
-    out[1] = o1;
-  }
+  for (int bh = blockIdx.z; bh < a.B * a.Hkv; bh += gridDim.z) dequant_pair<false>(a, bh);
 }
-
 __global__ void __launch_bounds__(256) dequant_int8_kernel(DequantArgs a) {
-  const uint2* codes = reinterpret_cast<const uint2*>(a.codes);
-  const int lpr = a.D >> 3;
-  const uint32_t total = (uint32_t)a.B * a.Hkv * a.n * lpr;
-  const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const uint32_t row = i / lpr;
-    const int c = (int)(i - row * lpr);
-    const uint32_t bh = row / (uint32_t)a.n;
-    const int t = (int)(row - bh * a.n);
-    const size_t drow = (size_t)bh * a.cap + (a.start + t) % a.cap;
-    const uint2 w = codes[drow * lpr + c];
-    const float s = a.scales[drow];
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[j] = (float)(int8_t)((w.x >> (8 * j)) & 255u) * s;
-      v[j + 4] = (float)(int8_t)((w.y >> (8 * j)) & 255u) * s;
-    }
-    float4* out = reinterpret_cast<float4*>(a.out + (size_t)i * 8);
-    out[0] = make_float4(v[0], v[1], v[2], v[3]);
-    out[1] = make_float4(v[4], v[5], v[6], v[7]);
-  }
+  for (int bh = blockIdx.z; bh < a.B * a.Hkv; bh += gridDim.z) dequant_pair<true>(a, bh);
 }
 
-inline int grid_for(uint64_t lanes) {
-  uint64_t blocks = (lanes + 255) / 256;
-  const uint64_t cap = 256ull * 16;  // enough resident waves to cover HBM latency
-  return (int)(blocks < cap ? (blocks ? blocks : 1) : cap);
+// Chunk blocks per (b, h) pair: about 4096 workgroups in all (16 per CU), at least
+// one per pair, no more than a pair's chunks need.
+inline int blocks_per_pair(uint64_t pairs, uint64_t chunks_per_pair) {
+  const uint64_t want = (4096 + pairs - 1) / pairs;
+  const uint64_t need = (chunks_per_pair + 255) / 256;
+  const uint64_t n = want < need ? want : need;
+  return (int)(n ? n : 1);
 }
 
 }  // namespace
 
 hipError_t launch_quant_intq(int32_t format, const QuantArgs& a, hipStream_t s) {
-  const uint64_t lanes = (uint64_t)a.rows * (a.D / 8);
-  dim3 grid(grid_for(lanes), 2);
+  const uint64_t pairs = (uint64_t)a.B * a.Hkv;
+  const dim3 grid(blocks_per_pair(2 * pairs, (uint64_t)a.map.n * (a.D / 8)), 2,
+                  (uint32_t)(pairs < 65535 ? pairs : 65535));
   return launch_kernel(format == KVQ_INT4_G ? quant_int4_kernel : quant_int8_kernel, grid,
                        dim3(256), a, s);
 }
 
 hipError_t launch_dequant_intq(int32_t format, const DequantArgs& a, hipStream_t s) {
-  const uint64_t lanes = (uint64_t)a.B * a.Hkv * a.n * (a.D / 8);
-  return launch_kernel(format == KVQ_INT4_G ? dequant_int4_kernel : dequant_int8_kernel,
-                       dim3(grid_for(lanes)), dim3(256), a, s);
+  const uint64_t pairs = (uint64_t)a.B * a.Hkv;
+  const dim3 grid(blocks_per_pair(pairs, (uint64_t)a.n * (a.D / 8)), 1,
+                  (uint32_t)(pairs < 65535 ? pairs : 65535));
+  return launch_kernel(format == KVQ_INT4_G ? dequant_int4_kernel : dequant_int8_kernel, grid,
+                       dim3(256), a, s);
 }
 
 }  // namespace kvq
