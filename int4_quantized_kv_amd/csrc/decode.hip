@@ -271,17 +271,26 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
     L = __builtin_fmaf(w, a.ws_ml[2 * (base + s) + 1], L);
   }
   L = block_reduce<false>(L, s_tmp);   // its barrier also publishes s_w
+  // 16 partials per step, their loads issued together (the merge is latency-bound)
   const float* acc = a.ws_acc + base * D + d;
-  float A0 = 0.0f, A1 = 0.0f, A2 = 0.0f, A3 = 0.0f;
+  constexpr int MU = 16;
+  float A[MU];
+#pragma unroll
+  for (int u = 0; u < MU; ++u) A[u] = 0.0f;
   int s = 0;
-  for (; s + 4 <= ns; s += 4) {
-    A0 = __builtin_fmaf(acc[(size_t)s * D], s_w[s], A0);
-    A1 = __builtin_fmaf(acc[(size_t)(s + 1) * D], s_w[s + 1], A1);
-    A2 = __builtin_fmaf(acc[(size_t)(s + 2) * D], s_w[s + 2], A2);
-    A3 = __builtin_fmaf(acc[(size_t)(s + 3) * D], s_w[s + 3], A3);
+  for (; s + MU <= ns; s += MU) {
+    float x[MU];
+#pragma unroll
+    for (int u = 0; u < MU; ++u) x[u] = acc[(size_t)(s + u) * D];
+#pragma unroll
+    for (int u = 0; u < MU; ++u) A[u] = __builtin_fmaf(x[u], s_w[s + u], A[u]);
   }
-  for (; s < ns; ++s) A0 = __builtin_fmaf(acc[(size_t)s * D], s_w[s], A0);
-  float o = ((A0 + A1) + (A2 + A3)) / L;
+  for (; s < ns; ++s) A[0] = __builtin_fmaf(acc[(size_t)s * D], s_w[s], A[0]);
+#pragma unroll
+  for (int w = MU / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int u = 0; u < w; ++u) A[u] += A[u + w];
+  float o = A[0] / L;
   if (CODEC) {
     sh[d] = o;
     __syncthreads();
@@ -331,7 +340,7 @@ int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
   if (d->format == KVQ_INT4_G &&
       mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group))
     return plan_splits_mfma(units, span);
-  const int32_t target = 2048;       // workgroups: 8 per CU on 256 CUs
+  const int32_t target = 1024;       // workgroups: 4 per CU on 256 CUs (all resident)
   const int32_t min_rows = 64;       // positions per split worth a workgroup (short
                                      // contexts need many splits to fill the chip)
   int32_t n = (target + units - 1) / units;

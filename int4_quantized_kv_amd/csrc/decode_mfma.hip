@@ -864,10 +864,21 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int e = 1; e < 8; e += 2) st.oacc[e] *= 0.0625f;   // see v_pair_f16
   if (NGK >= 2) {   // column g = 0 of a head: P'_hi part + (column g = 1) P'_lo part
+    // (one DPP add per value, in assembly: written with the builtin, the compiler moved
+    // the adds below the branch that follows and kept a zeroed copy per value; each
+    // block starts with the two wait states a DPP read needs after a VALU write)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.oacc[e][i] = add_xor1(st.oacc[e][i]);
+    for (int e = 0; e < 8; ++e) {
+      float x0 = st.oacc[e][0], x1 = st.oacc[e][1], x2 = st.oacc[e][2], x3 = st.oacc[e][3];
+      asm volatile(
+          "s_nop 1\n\t"
+          "v_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+          "v_add_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+          "v_add_f32_dpp %2, %2, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+          "v_add_f32_dpp %3, %3, %3 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+          : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
+      st.oacc[e] = (floatx4){x0, x1, x2, x3};
+    }
   }
   const float l_run = sum_over_j(st.l);
   if (rr < G * NGK && qgrp == 0) {
