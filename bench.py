@@ -37,10 +37,23 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 # Sources of the dominant kernel (and its build flags): HBM-traffic counters recorded in
 # profiles/ are reported only while these files hash to the value recorded with them.
-KERNEL_SOURCES = ["int4_quantized_kv_amd/csrc/decode_mfma.hip", "int4_quantized_kv_amd/csrc/kvq_device.h",
-                  "int4_quantized_kv_amd/csrc/kvq_internal.h", "int4_quantized_kv_amd/csrc/kvq_arith.h",
-                  "int4_quantized_kv_amd/build.py"]
+_COMMON = ["int4_quantized_kv_amd/csrc/kvq_device.h", "int4_quantized_kv_amd/csrc/kvq_internal.h",
+           "int4_quantized_kv_amd/csrc/kvq_arith.h", "int4_quantized_kv_amd/build.py"]
+KERNEL_SOURCES = ["int4_quantized_kv_amd/csrc/decode_mfma.hip"] + _COMMON
 TRAFFIC_FILE = "profiles/decode_int4_mfma_llama8b_ctx8k_b8_traffic.md"
+# the other workloads: (traffic record, sources of the kernels it covers)
+OTHER_TRAFFIC = {
+    "mha7b-prefill": ("profiles/quant_int4_mha7b_ctx20k_b8_traffic.md",
+                      ["int4_quantized_kv_amd/csrc/quant.hip"] + _COMMON),
+    "dequant": ("profiles/dequant_int4_llama8b_ctx8k_b8_traffic.md",
+                ["int4_quantized_kv_amd/csrc/quant.hip"] + _COMMON),
+    "mha7b-decode": ("profiles/decode_int4_mfma_mha7b_ctx20k_b8_traffic.md", KERNEL_SOURCES),
+    "ctx128k-int4": ("profiles/decode_int4_mfma_ctx128k_b1_traffic.md", KERNEL_SOURCES),
+    "ctx128k-int8": ("profiles/decode_splitk_int8_ctx128k_b1_traffic.md",
+                     ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
+    "gemma-codec": ("profiles/decode_splitk_codec_gemma3_4b_b4_traffic.md",
+                    ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
+}
 
 
 def parse():
@@ -85,7 +98,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     if args.workload != "llama8b":
-        print(json.dumps(OTHER[args.workload](args)), flush=True)
+        line = OTHER[args.workload](args)
+        line["roofline"]["traffic"] = recorded_traffic(*OTHER_TRAFFIC[args.workload])
+        print(json.dumps(line), flush=True)
         return
     w = synth.WORKLOADS[2]
     nl = args.layers or w.layers
@@ -254,21 +269,21 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
+def recorded_traffic(traffic_file=None, sources=None):
     """HBM bytes per launch of the dominant kernel from the rocprofv3 FETCH_SIZE and
-    WRITE_SIZE passes recorded in TRAFFIC_FILE (each scaled by the factor the same
+    WRITE_SIZE passes recorded in the traffic file (each scaled by the factor the same
     counter shows on a copy of known size), or None if there is no record or the kernel
     has changed since it was taken."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
+    path = os.path.join(ROOT, traffic_file or TRAFFIC_FILE)
     if not os.path.exists(path):
         return None
     rec = {}
@@ -277,7 +292,7 @@ def recorded_traffic():
         if ":" in line and line.split(":", 1)[0] in ("source_sha256", "traffic_bytes_per_launch"):
             k, v = line.split(":", 1)
             rec[k] = v.strip()
-    if rec.get("source_sha256") != kernel_source_hash() or "traffic_bytes_per_launch" not in rec:
+    if rec.get("source_sha256") != kernel_source_hash(sources) or "traffic_bytes_per_launch" not in rec:
         return None
     return int(rec["traffic_bytes_per_launch"])
 
