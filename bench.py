@@ -49,8 +49,7 @@ OTHER_TRAFFIC = {
                 ["int4_quantized_kv_amd/csrc/quant.hip"] + _COMMON),
     "mha7b-decode": ("profiles/decode_int4_mfma_mha7b_ctx20k_b8_traffic.md", KERNEL_SOURCES),
     "ctx128k-int4": ("profiles/decode_int4_mfma_ctx128k_b1_traffic.md", KERNEL_SOURCES),
-    "ctx128k-int8": ("profiles/decode_splitk_int8_ctx128k_b1_traffic.md",
-                     ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
+    "ctx128k-int8": ("profiles/decode_mfma_int8_ctx128k_b1_traffic.md", KERNEL_SOURCES),
     "gemma-codec": ("profiles/decode_splitk_codec_gemma3_4b_b4_traffic.md",
                     ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
 }
@@ -514,9 +513,12 @@ def bench_decode(args):
         attn_ms, _ = _timed(attn, args.steps)
     else:
         attn_ms = ms_step
-    mfma = fmt == "int4" and D == 128 and w.group_v == 128
-    kern = ("kvq_decode_attn: decode_int4_mfma_kernel (splits merged in-kernel)" if mfma else
-            f"kvq_decode_attn: decode_splitk_kernel<{D}, {Hq // Hkv}, {fmt}> + merge_kernel")
+    if fmt == "int4" and D == 128 and w.group_v == 128:
+        kern = "kvq_decode_attn: decode_int4_mfma_kernel (splits merged in-kernel)"
+    elif fmt == "int8" and D == 128:
+        kern = "kvq_decode_attn: decode_int4_mfma_kernel, INT8 tiles (splits merged in-kernel)"
+    else:
+        kern = f"kvq_decode_attn: decode_splitk_kernel<{D}, {Hq // Hkv}, {fmt}> + merge_kernel"
     roof = _roofline(kern, attend_bytes / nl, attn_ms * 1e3 / nl)
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     cfg = {"workload": w.name, "format": fmt, "layers": nl, "batch": B, "q_heads": Hq,

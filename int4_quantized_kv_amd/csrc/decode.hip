@@ -311,6 +311,8 @@ hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
   hipError_t e;
   if (FMT == KVQ_INT4_G && mfma_int4_eligible(D, a.gk, a.gv, a.cap, G))
     return launch_decode_int4_mfma(a, G, s);   // merges the splits itself
+  if (FMT == KVQ_INT8_TOKEN && mfma_int8_eligible(D, a.cap, G))
+    return launch_decode_int8_mfma(a, G, s);
   switch (G) {
     case 1: e = launch_kernel(decode_splitk_kernel<D, 1, FMT>, grid, dim3(256), a, s); break;
     case 2: e = launch_kernel(decode_splitk_kernel<D, 2, FMT>, grid, dim3(256), a, s); break;
@@ -339,6 +341,8 @@ int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
   if (units <= 0 || span <= 0) return 0;
   if (d->format == KVQ_INT4_G &&
       mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group))
+    return plan_splits_mfma(units, span);
+  if (d->format == KVQ_INT8_TOKEN && mfma_int8_eligible(d->head_dim, d->capacity, q_group))
     return plan_splits_mfma(units, span);
   const int32_t target = 1024;       // workgroups: 4 per CU on 256 CUs (all resident)
   const int32_t min_rows = 64;       // positions per split worth a workgroup (short

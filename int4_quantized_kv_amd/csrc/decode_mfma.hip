@@ -36,6 +36,7 @@
 // KV head) then combines the splits' partials (no separate merge launch).
 // Tiles are staged through LDS by direct global->LDS transfers (see "LDS staging").
 #include <cmath>
+#include <type_traits>
 
 #include "kvq_arith.h"
 #include "kvq_device.h"
@@ -521,6 +522,241 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// INT8 per-token tiles (bxzpzcl.cn/news/2871434 section 3.1: one scale per row and head).
+// A row is 128 bytes of codes for K and for V, so a tile is 16 positions (4352 bytes
+// with the scales: the same LDS ring and the same bytes in flight as the INT4 tiles).
+//   q.K   A = K codes (rows = 16 positions, k = 32 dims) in 4 MFMAs; lane (r, j) holds
+//         dims 32j .. 32j + 31 of position r (two 16-byte chunks) and feeds dims
+//         32j + 8c .. + 7 to MFMA c.  Columns are (head, part) pairs: both carry the
+//         whole q of the head (there are no K groups), so lane (column, j) gets the
+//         score of positions 4j + i of its head directly, times the row scale.
+//   P.V   A = V codes (rows = 16 dims, k = 4 positions per lane quarter) in 8
+//         v_mfma_f32_16x16x16_f16; lane (r, j) feeds dim 8r + e of positions 4j .. 4j+3,
+//         which are the positions of the 4 scores the lane holds, so B is the lane's own
+//         4 values of P'_hi (part 0) or P'_lo (part 1); the two parts are summed at
+//         the end as for INT4.
+// Codes become exact fp16 integers with the 1024 bias: byte b with its sign bit
+// flipped is q + 128; (0x64 << 8 | (q + 128)) is the fp16 1152 + q; a packed subtract of
+// 1152 leaves q.  (Fed as biased subnormals like the INT4 keys, the +128 offset would
+// cost ~16 times the INT4 keys' accumulation error.)
+// LDS: tile row rho lives in row slot P = rho ^ ((rho >> 2) & 1) and its 16-byte chunk c
+// in chunk slot c ^ g(P), g(P) = ((P >> 1) ^ ((P & 1) << 2)) & 7: the K reads (16 rows,
+// one chunk) and the V reads (the 16 eight-byte pieces of a row; two rows an XOR 4 apart
+// per 32 lanes) are then free of bank conflicts for 32- and 64-bank LDS.
+struct Slot8 {
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 2048;
+  static constexpr int SK_OFF = 4096;   // 16 K scales, then 16 V scales, then 128 spare
+  static constexpr int SV_OFF = 4160;
+  static constexpr int BYTES = 4352;
+  static constexpr int DMA = 5;
+};
+constexpr int TILE8 = 16;
+__device__ __forceinline__ int rowslot8(int rho) { return rho ^ ((rho >> 2) & 1); }
+__device__ __forceinline__ int chunk_swz8(int P) { return ((P >> 1) ^ ((P & 1) << 2)) & 7; }
+
+struct DmaOffs8 {
+  int kv[2];    // K / V codes, transfer T: tile row rho_T, chunk (byte offset)
+  int rho[2];
+  int ch16[2];  // 16 * logical chunk of transfer T
+  int srow;     // the tile row whose scale this lane moves
+  bool sv;      // lanes 16..31 move V scales, the others K scales
+};
+
+__device__ __forceinline__ DmaOffs8 dma_offsets8(int lane) {
+  DmaOffs8 o;
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    const int P = 8 * T + (lane >> 3), pc = lane & 7;
+    o.rho[T] = rowslot8(P);                   // (an involution)
+    o.ch16[T] = 16 * (pc ^ chunk_swz8(P));
+    o.kv[T] = o.rho[T] * 128 + o.ch16[T];
+  }
+  o.srow = lane & 15;
+  o.sv = (lane >> 4) == 1;
+  return o;
+}
+
+__device__ __forceinline__ void issue_tile8(const DecodeArgs& a, size_t row0, int t0, int pe,
+                                            uint8_t* lb, const DmaOffs8& o) {
+  using L = Slot8;
+  const int cap = a.cap;
+  const int sbase = t0 % cap;
+  const uint8_t* kc = static_cast<const uint8_t*>(a.k_codes);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.v_codes);
+  if (t0 + TILE8 <= pe && sbase + TILE8 <= cap) {
+    const size_t rb = row0 + (size_t)sbase;
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      dma16(kc + rb * HD + o.kv[T], lb + L::K_OFF + 1024 * T);
+      dma16(vc + rb * HD + o.kv[T], lb + L::V_OFF + 1024 * T);
+    }
+    const float* sc = o.sv ? a.v_scales : a.k_scales;
+    dma4(sc + rb + o.srow, lb + L::SK_OFF);
+    return;
+  }
+  auto row_of = [&](int rho) -> size_t {
+    int off = rho;
+    if (t0 + off > pe - 1) off = pe - 1 - t0;
+    int sl = sbase + off;
+    if (sl >= cap) sl -= cap;
+    return row0 + (size_t)sl;
+  };
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    const size_t row = row_of(o.rho[T]);
+    dma16(kc + row * HD + o.ch16[T], lb + L::K_OFF + 1024 * T);
+    dma16(vc + row * HD + o.ch16[T], lb + L::V_OFF + 1024 * T);
+  }
+  const float* sc = o.sv ? a.v_scales : a.k_scales;
+  dma4(sc + row_of(o.srow), lb + L::SK_OFF);
+}
+
+struct LaneOffs8 {
+  int k[2];     // chunks 2j, 2j + 1 of row r
+  int v[4];     // bytes 8r .. 8r + 7 of rows 4j + i
+  int sk, sv;   // scales of rows 4j .. 4j + 3
+};
+
+__device__ __forceinline__ LaneOffs8 lane_offsets8(int r, int j) {
+  LaneOffs8 lo;
+  const int P = rowslot8(r);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) lo.k[h] = P * 128 + 16 * ((2 * j + h) ^ chunk_swz8(P));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int Pv = rowslot8(4 * j + i);
+    lo.v[i] = Pv * 128 + 16 * ((r >> 1) ^ chunk_swz8(Pv)) + 8 * (r & 1);
+  }
+  lo.sk = 16 * j;
+  lo.sv = 16 * j;
+  return lo;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+struct TileData8 {
+  u32x4 k[2];
+  u32x4 sk, sv;
+  u32x2 v[4];
+};
+
+// The 8 LDS reads of an INT8 tile, in one asm statement that waits for them (see
+// read_tile).
+__device__ __forceinline__ TileData8 read_tile8(const uint8_t* lb, const LaneOffs8& lo) {
+  using L = Slot8;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_vptr)lb;
+  const uint32_t ak0 = base + L::K_OFF + lo.k[0], ak1 = base + L::K_OFF + lo.k[1];
+  const uint32_t ask = base + L::SK_OFF + lo.sk, asv = base + L::SV_OFF + lo.sv;
+  const uint32_t av0 = base + L::V_OFF + lo.v[0], av1 = base + L::V_OFF + lo.v[1];
+  const uint32_t av2 = base + L::V_OFF + lo.v[2], av3 = base + L::V_OFF + lo.v[3];
+  TileData8 d;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b64 %4, %12\n\t"
+      "ds_read_b64 %5, %13\n\t"
+      "ds_read_b64 %6, %14\n\t"
+      "ds_read_b64 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d.k[0]), "=&v"(d.k[1]), "=&v"(d.sk), "=&v"(d.sv), "=&v"(d.v[0]), "=&v"(d.v[1]),
+        "=&v"(d.v[2]), "=&v"(d.v[3])
+      : "v"(ak0), "v"(ak1), "v"(ask), "v"(asv), "v"(av0), "v"(av1), "v"(av2), "v"(av3)
+      : "memory");
+  return d;
+}
+
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+union H4 {
+  half4 h;
+  uint32_t u[2];
+};
+
+// Bytes 0, 1 (SEL = 0x04010400) or 2, 3 (0x04030402) of a sign-flipped code word with
+// 0x64 above each: the fp16 pair (1152 + q0, 1152 + q1), then q0, q1 exactly.
+template <uint32_t SEL>
+__device__ __forceinline__ uint32_t k8_pair(uint32_t xflip) {
+  return pk_sub_f16(__builtin_amdgcn_perm(0x64646464u, xflip, SEL), 1152.0f);
+}
+// Byte e of two rows' code words (positions p, p + 1) as the fp16 pair (q_p, q_p+1).
+__device__ __forceinline__ uint32_t v8_pair(uint32_t w0, uint32_t w1, uint32_t sel) {
+  return pk_sub_f16(__builtin_amdgcn_perm(w1, w0, sel) ^ 0x64806480u, 1152.0f);
+}
+
+template <int G>
+__device__ __forceinline__ void process_tile8(const uint8_t* lb, const LaneOffs8& lo, State& st,
+                                              const half8 (&qb)[4], int t0, int pe, int j,
+                                              float qscale, bool lo_col, bool masked) {
+  const TileData8 td = read_tile8(lb, lo);
+  // ---- q.K: the lane's 32 dims in 4 MFMAs, 8 dims each
+  const uint32_t kw[8] = {td.k[0].x, td.k[0].y, td.k[0].z, td.k[0].w,
+                          td.k[1].x, td.k[1].y, td.k[1].z, td.k[1].w};
+  floatx4 cg = (floatx4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t x0 = kw[2 * c] ^ 0x80808080u, x1 = kw[2 * c + 1] ^ 0x80808080u;
+    H8 ka;
+    ka.u[0] = k8_pair<0x04010400u>(x0);
+    ka.u[1] = k8_pair<0x04030402u>(x0);
+    ka.u[2] = k8_pair<0x04010400u>(x1);
+    ka.u[3] = k8_pair<0x04030402u>(x1);
+    cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.h, qb[c], cg, 0, 0, 0);
+  }
+  const floatx4 sk = __builtin_bit_cast(floatx4, td.sk);
+  float z[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = cg[i] * sk[i];
+  if (masked) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (t0 + 4 * j + i >= pe) z[i] = NEG_INF;
+  }
+
+  // ---- online softmax (the 4 lanes j of a column share a head)
+  float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+  mx = max_over_j(mx);
+  const float m_new = fmaxf(st.m, mx);
+  if (__any(m_new > st.m)) {
+    const float corr = fast_exp2((st.m - m_new) * qscale);
+    st.l *= corr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.oacc[e] *= corr;
+    st.m = m_new;
+  }
+  const float mq = st.m * qscale;
+
+  // ---- P' = P * sV as fp16 hi + lo; the column's part goes to B
+  const floatx4 sv = __builtin_bit_cast(floatx4, td.sv);
+  H4 pb;
+#pragma unroll
+  for (int i = 0; i < 4; i += 2) {
+    const float p0 = fast_exp2(__builtin_fmaf(z[i], qscale, -mq));
+    const float p1 = fast_exp2(__builtin_fmaf(z[i + 1], qscale, -mq));
+    st.l += p0 + p1;
+    const float q0 = p0 * sv[i];
+    const float q1 = p1 * sv[i + 1];
+    const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(q0, q1));
+    const float r0 = __builtin_fmaf((float)h.x, -1.0f, q0);
+    const float r1 = __builtin_fmaf((float)h.y, -1.0f, q1);
+    const uint32_t hi = __builtin_bit_cast(uint32_t, h);
+    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    pb.u[i / 2] = lo_col ? lo : hi;
+  }
+
+  // ---- P.V: dim 8r + e of positions 4j .. 4j + 3
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int wsel = e >> 2, b = e & 3;
+    const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + b) << 16) | (uint32_t)b;
+    H4 va;
+    va.u[0] = v8_pair(td.v[0][wsel], td.v[1][wsel], sel);
+    va.u[1] = v8_pair(td.v[2][wsel], td.v[3][wsel], sel);
+    st.oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(va.h, pb.h, st.oacc[e], 0, 0, 0);
+  }
+}
+
 // Device-scope (all XCDs) store / load of one float of the split partials.
 __device__ __forceinline__ void publish(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -649,10 +885,13 @@ __device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewLds*
   }
 }
 
-template <int G, int NGK>
+// I8: the INT8 per-token format (NGK = 2 then counts the (head, part) columns of a head,
+// both carrying the whole q; 16-position tiles, one position set).
+template <int G, int NGK, bool I8>
 __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
-  using L = Slot<NGK>;
-  constexpr int S = position_sets(G, NGK);
+  using L = std::conditional_t<I8, Slot8, Slot<NGK>>;
+  constexpr int TL = I8 ? TILE8 : TILE;       // positions per tile
+  constexpr int S = I8 ? 1 : position_sets(G, NGK);
   constexpr int DMA = L::DMA;
   __shared__ __attribute__((aligned(16))) uint8_t smem[WAVES * NB * L::BYTES];
   __shared__ __attribute__((aligned(16))) NewLds s_new;
@@ -675,7 +914,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   const int len = a.lens[b];
   const int lo_pos = a.window > 0 ? max(0, len - a.window) : 0;
   // with the append fused, position len - 1 comes from the new token, not from a tile
-  const bool fused = a.k_new != nullptr;
+  // (INT4 only: the INT8 step is appended by the quantize kernel first)
+  const bool fused = !I8 && a.k_new != nullptr;
   const bool appender = fused && sp == 0;
   const int pt = fused ? len - 1 : len;                 // tiles cover [lo_pos, pt)
 
@@ -689,10 +929,17 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   const int chunk = span > 0 ? (span + a.nsplit - 1) / a.nsplit : 0;
   const int ps = min(pt, lo_pos + sp * chunk);
   const int pe = min(pt, ps + chunk);
-  const int nts = (pe - ps + TILE - 1) / TILE;
+  const int nts = (pe - ps + TL - 1) / TL;
   const size_t row0 = (size_t)unit * a.cap;
   uint8_t* ring = smem + wave * NB * L::BYTES;
-  const DmaOffs dof = dma_offsets<NGK>(lane);
+  const auto dof = [&] {
+    if constexpr (I8) return dma_offsets8(lane);
+    else return dma_offsets<NGK>(lane);
+  }();
+  auto issue = [&](int t0, uint8_t* lb) {
+    if constexpr (I8) issue_tile8(a, row0, t0, pe, lb, dof);
+    else issue_tile<NGK>(a, row0, t0, pe, lb, lane, dof);
+  };
   if (threadIdx.x == 0) s_claim = 0;   // ordered before the first claim by a barrier
 
   // fp16 inputs, copied into LDS by transfers before the first tile: the G query rows
@@ -710,6 +957,10 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     dma4(a.v_new + (size_t)unit * HD + 2 * lane, reinterpret_cast<uint8_t*>(s_new.v));
   }
 
+  const auto lo = [&] {
+  if constexpr (I8) {
+    return lane_offsets8(r, j);
+  } else {
   LaneOffs lo;
   {
     const int P = rowinv(r);
@@ -728,6 +979,9 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     lo.sk = (min(qgrp, NGK - 1) * 32 + 16 * cset + 4 * j) * 4;
     lo.sv = (16 * cset + 4 * j) * 4;
   }
+  return lo;
+  }
+  }();
 
   State st;
 #pragma unroll
@@ -745,8 +999,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   constexpr int NONE = -1;
   int cur = wave < nts ? wave : NONE;
   int nxt = wave + WAVES < nts ? wave + WAVES : NONE;
-  if (cur != NONE) issue_tile<NGK>(a, row0, ps + TILE * cur, pe, ring, lane, dof);
-  if (nxt != NONE) issue_tile<NGK>(a, row0, ps + TILE * nxt, pe, ring + L::BYTES, lane, dof);
+  if (cur != NONE) issue(ps + TL * cur, ring);
+  if (nxt != NONE) issue(ps + TL * nxt, ring + L::BYTES);
 
   // q into MFMA layout (and the appending wave's quantization of the new row) while
   // tiles 0 and 1 are in flight
@@ -786,6 +1040,16 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // set, zeros otherwise; qbias = -8 * (sum of those q entries)
   constexpr int QPG = 4 / NGK;   // chunks (32 dims) per K group
   float qs = 0.0f;
+  if constexpr (I8) {   // INT8: dims 32j + 8c .. + 7 in order, every column of a head
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      H8 o;
+      const uint32_t w[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) o.u[p] = rr < G * NGK ? w[p] : 0u;
+      qb[c] = o.h;
+    }
+  } else {
 #pragma unroll
   for (int c = 0; c < 4 * S; ++c) {
     const int ch = S == 1 ? j : (j & 1) + 2 * (c >> 2);
@@ -809,7 +1073,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     qb[c] = o.h;
   }
   qbias = -8.0f * sum_over_j(qs);
-  if (app_wave && lane < 32) {
+  }
+  if constexpr (!I8) if (app_wave && lane < 32) {
     const NewRow nr = append_row<G, NGK>(a, &s_new, qstage, lane);
     s_new.w[lane] = nr.w;
     s_new.sc[lane] = nr.sc;
@@ -830,16 +1095,20 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       nn = id < nts ? id : NONE;
     }
     if (nn != NONE) {
-      issue_tile<NGK>(a, row0, ps + TILE * nn, pe, ring + ((k + 2) % NB) * L::BYTES, lane, dof);
+      issue(ps + TL * nn, ring + ((k + 2) % NB) * L::BYTES);
       wait_vmcnt<2 * DMA>();   // after tile k: the transfers of tiles k + 1 and k + 2
     } else if (nxt != NONE) {
       wait_vmcnt<DMA>();
     } else {
       wait_vmcnt<0>();
     }
-    const int t0 = ps + TILE * cur;
-    process_tile<G, NGK, S>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j,
-                            a.qscale, lo_col, 16 * cset, t0 + TILE > pe);
+    const int t0 = ps + TL * cur;
+    if constexpr (I8)
+      process_tile8<G>(ring + (k % NB) * L::BYTES, lo, st, qb, t0, pe, j, a.qscale, lo_col,
+                       t0 + TL > pe);
+    else
+      process_tile<G, NGK, S>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j,
+                              a.qscale, lo_col, 16 * cset, t0 + TL > pe);
     cur = nxt;
     nxt = nn;
   }
@@ -861,8 +1130,10 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   float* s_o = reinterpret_cast<float*>(smem);                 // [NE][G][ORS]
   float* s_m = s_o + NE * G * ORS;                              // [G][NE]
   float* s_l = s_m + NE * G;                                    // [G][NE]
+  if constexpr (!I8) {
 #pragma unroll
-  for (int e = 1; e < 8; e += 2) st.oacc[e] *= 0.0625f;   // see v_pair_f16
+    for (int e = 1; e < 8; e += 2) st.oacc[e] *= 0.0625f;   // see v_pair_f16
+  }
   if (NGK >= 2) {   // column g = 0 of a head: P'_hi part + (column g = 1) P'_lo part
     // (one DPP add per value, in assembly: written with the builtin, the compiler moved
     // the adds below the branch that follows and kept a zeroed copy per value; each
@@ -1023,10 +1294,10 @@ template <int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   switch (HD / a.gk) {
-    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1>, grid, dim3(NT), a, s);
-    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2>, grid, dim3(NT), a, s);
+    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1, false>, grid, dim3(NT), a, s);
+    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2, false>, grid, dim3(NT), a, s);
     case 4:
-      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4>, grid, dim3(NT), a, s);
+      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4, false>, grid, dim3(NT), a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -1062,6 +1333,22 @@ hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStre
     case 2: return launch_g<2>(a, s);
     case 4: return launch_g<4>(a, s);
     case 8: return launch_g<8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool mfma_int8_eligible(int32_t head_dim, int32_t cap, int32_t q_group) {
+  return head_dim == HD && cap >= TILE8 &&
+         (q_group == 1 || q_group == 2 || q_group == 4 || q_group == 8);
+}
+
+hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
+  const dim3 grid(a.nsplit, a.Hkv, a.B);
+  switch (q_group) {
+    case 1: return launch_kernel(decode_int4_mfma_kernel<1, 2, true>, grid, dim3(NT), a, s);
+    case 2: return launch_kernel(decode_int4_mfma_kernel<2, 2, true>, grid, dim3(NT), a, s);
+    case 4: return launch_kernel(decode_int4_mfma_kernel<4, 2, true>, grid, dim3(NT), a, s);
+    case 8: return launch_kernel(decode_int4_mfma_kernel<8, 2, true>, grid, dim3(NT), a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -81,6 +81,9 @@ bool mfma_int4_eligible(int32_t head_dim, int32_t group_k, int32_t group_v, int3
 int32_t plan_splits_mfma(int32_t units, int32_t span);
 bool fused_append_supported(const kvq_cache_desc* d, int32_t q_group);
 hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
+// The same kernel for the INT8 per-token format (head_dim 128, capacity >= 16).
+bool mfma_int8_eligible(int32_t head_dim, int32_t cap, int32_t q_group);
+hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
 
 // Largest split count a decode call accepts (the merge kernel keeps one weight per
 // split in LDS).

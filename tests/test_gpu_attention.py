@@ -196,6 +196,40 @@ def test_int4_matrix_core_path(case):
         assert_attn_close(out.cpu().numpy(), ref, f"mfma {case} nsplit={ns}")
 
 
+INT8_MFMA_CASES = [
+    # G, lens, window, cap    (head_dim 128: the matrix-core kernel with 16-position tiles)
+    (1, [33, 1000], 0, None),
+    (2, [511, 17], 0, None),
+    (4, [16, 15, 1], 0, None),          # contexts of one tile or less
+    (8, [1025, 640], 0, None),
+    (4, [1500, 1500], 300, 512),        # window ring, capacity 512 (wraps)
+    (4, [700, 300], 0, None),
+]
+
+
+@pytest.mark.parametrize("case", INT8_MFMA_CASES, ids=[f"int8mfma{i}" for i in range(len(INT8_MFMA_CASES))])
+def test_int8_matrix_core_path(case):
+    G, lens, window, cap = case
+    B, Hkv, D = len(lens), 2, 128
+    S = max(lens)
+    k = synth.kv_source((B, Hkv, S, D), 700 + G, DEV, outlier_channels=3)
+    v = synth.kv_source((B, Hkv, S, D), 800 + G, DEV, outlier_channels=3,
+                        zero_groups=((0, 1, 0, 0, D),))
+    q = synth.query((B, Hkv * G, D), 900 + G, DEV)
+    C = cap or S
+    desc = kvq.make_desc("int8", B, Hkv, D, C)
+    dc = kvq.DeviceCache(desc, DEV)
+    for start in range(0, S, C):
+        n = min(C, S - start)
+        kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, start:start + n].contiguous(),
+                                 v[:, :, start:start + n].contiguous(), start, n)
+    kh, vh = _oracle_hat("int8", np16(k), np16(v))
+    ref = attention.decode_attention(np16(q), kh, vh, lens, window)
+    for ns in (0, 1, 5):
+        out = decode(desc, dc, q, Hkv * G, lens, window, 0.0, ns)
+        assert_attn_close(out.cpu().numpy(), ref, f"int8 mfma {case} nsplit={ns}")
+
+
 @pytest.mark.parametrize("gv,cap", [(64, None), (128, 16)])
 def test_int4_generic_fallback(gv, cap):
     """INT4 shapes the matrix-core kernel does not take (V group < head_dim, capacity
