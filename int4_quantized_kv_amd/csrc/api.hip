@@ -230,10 +230,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   const float scale = softmax_scale != 0.0f ? softmax_scale
                                             : 1.0f / std::sqrt((float)desc->head_dim);
   a.qscale = scale * 1.4426950408889634f;  // log2(e): scores in base-2 units
-  if (desc->format == KVQ_WHT_LM4) {
-    float thr[15];
-    codec_codebook(a.levels, thr);
-  }
+  if (desc->format == KVQ_WHT_LM4) codec_codebook(a.levels, a.thr);
   for (int32_t b = 0; b < desc->batch; ++b) a.lens[b] = lens[b];
 
   if (k_new) {

@@ -28,29 +28,14 @@ __global__ void __launch_bounds__(256) codec_encode_kernel(QuantArgs a) {
   float* scales = isv ? a.v_scales : a.k_scales;
   const uint32_t total = (uint32_t)a.rows * LPR;
   const uint32_t stride = gridDim.x * blockDim.x;
-  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
     const uint32_t row = i / LPR;
     const int c = (int)(i - row * LPR);
     float x[8];
     load8_f16(src + (size_t)i * 8, x);
-    float ss = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(x[j], x[j], ss);
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
-    wht_row<LPR>(x, c);
-    const float s = sqrtf(ss / (float)D);
-    const float inv = inv_sqrt_d / (s == 0.0f ? 1.0f : s);  // u = (H x / sqrt(D)) / s
-    uint32_t w = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float u = x[j] * inv;
-      int idx = 0;
-#pragma unroll
-      for (int k = 0; k < 15; ++k) idx += (a.thr[k] < u) ? 1 : 0;
-      w |= (uint32_t)idx << (4 * j);
-    }
+    uint32_t w;
+    float s;
+    codec_encode_row<LPR>(x, c, a.thr, w, s);
     const uint32_t bh = row / (uint32_t)a.map.n;
     const int t = (int)(row - bh * a.map.n);
     const int b = (int)(bh / (uint32_t)a.Hkv);

@@ -27,6 +27,14 @@ namespace {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 
+// Device-scope (every XCD) store / loads of the split partials, for the in-kernel merge.
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fetch(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The packed bytes lane c owns of one row (cache row index b*Hkv*C + slot): its code
 // word(s) and the scale of its group, for K and V.  Loaded for several rows before any
 // of them is used, so that a lane keeps several rows' transfers in flight.
@@ -97,10 +105,30 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, grp = tid / LPR, c = tid % LPR;
   const int len = a.lens[b];
   const int lo = a.window > 0 ? max(0, len - a.window) : 0;
-  const int span = len - lo;
-  const int chunk = (span + a.nsplit - 1) / a.nsplit;
-  const int ps = min(len, lo + sp * chunk);
-  const int pe = min(len, ps + chunk);
+  // codec with the append fused: position len - 1 is the new row, coded in this kernel
+  // by split 0 and attended from registers; the splits cover [lo, len - 1)
+  const bool fused = FMT == KVQ_WHT_LM4 && a.k_new != nullptr;
+  const int pt = fused ? len - 1 : len;
+  const int span = pt - lo;
+  const int chunk = span > 0 ? (span + a.nsplit - 1) / a.nsplit : 0;
+  const int ps = min(pt, lo + sp * chunk);
+  const int pe = min(pt, ps + chunk);
+
+  // the rows of the first step are requested before q is loaded and rotated, so the
+  // two latencies overlap; each later step's rows are requested before the previous
+  // step is computed (see the row loop below)
+  constexpr int U = 4;
+  const size_t bh = (size_t)b * a.Hkv + kvh;
+  auto load_step = [&](int t0, RawRow (&raw)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(t0 + u * NGRP, pe - 1);
+      raw[u] = load_raw<D, FMT>(a, bh * a.cap + (t % a.cap), c);
+    }
+  };
+  int t0 = ps + grp;
+  RawRow cur[U];
+  if (t0 < pe) load_step(t0, cur);
 
   float q[G][8];
 #pragma unroll
@@ -124,15 +152,13 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
   }
 
-  // U rows per lane group per step, their loads issued before any is used.  The step
-  // scores its U rows, rescales the accumulators once by 2^(m - m_new) (1 when no
-  // head's maximum grew; 0 for the first rows, m being -inf before them: a multiply
-  // costs less than the register copies the compiler adds around a conditional
-  // rescale), then adds the U rows.  Rows past pe (last step only) are loaded clamped to pe - 1 and scored
-  // -inf; they are the same rows for the LPR lanes of a row, and every lane of a row
-  // takes part in the row's lane sums.
-  constexpr int U = 4;
-  const size_t bh = (size_t)b * a.Hkv + kvh;
+  // U rows per lane group per step.  The step scores its U rows, rescales the
+  // accumulators once by 2^(m - m_new) (1 when no head's maximum grew; 0 for the first
+  // rows, m being -inf before them: a multiply costs less than the register copies the
+  // compiler adds around a conditional rescale), then adds the U rows.  Rows past pe
+  // (last step only) are loaded clamped to pe - 1 and scored -inf; they are the same
+  // rows for the LPR lanes of a row, and every lane of a row takes part in the row's
+  // lane sums.
   auto do_step = [&](const RawRow (&raw)[U], int nvalid) {
     float z[U][G];
 #pragma unroll
@@ -174,21 +200,36 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
       }
     }
   };
-  int t0 = ps + grp;
-  for (; t0 + (U - 1) * NGRP < pe; t0 += U * NGRP) {
-    RawRow raw[U];
+  while (t0 < pe) {
+    const int t1 = t0 + U * NGRP;
+    RawRow nxt[U];
+    if (t1 < pe) load_step(t1, nxt);   // the next step's rows, in flight during this one
+    do_step(cur, min(U, (pe - t0 + NGRP - 1) / NGRP));
 #pragma unroll
-    for (int u = 0; u < U; ++u) raw[u] = load_raw<D, FMT>(a, bh * a.cap + ((t0 + u * NGRP) % a.cap), c);
-    do_step(raw, U);
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    t0 = t1;
   }
-  if (t0 < pe) {
-    RawRow raw[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = min(t0 + u * NGRP, pe - 1);
-      raw[u] = load_raw<D, FMT>(a, bh * a.cap + (t % a.cap), c);
+  if (FMT == KVQ_WHT_LM4 && fused && sp == 0 && grp == 0) {
+    // the new row: coded as the append kernel codes it, written to its slot (no other
+    // split reads that slot: it is outside [lo, len - 1) and holds no position of the
+    // horizon), and added to this row group's softmax as one more row
+    const size_t unit = (size_t)b * a.Hkv + kvh;
+    RawRow nr;
+    float x[8];
+    load8_f16(a.k_new + unit * D + 8 * c, x);
+    codec_encode_row<LPR>(x, c, a.thr, nr.k[0], nr.sk);
+    load8_f16(a.v_new + unit * D + 8 * c, x);
+    codec_encode_row<LPR>(x, c, a.thr, nr.v[0], nr.sv);
+    nr.k[1] = nr.v[1] = 0u;
+    const size_t row = bh * a.cap + (len - 1) % a.cap;
+    static_cast<uint32_t*>(const_cast<void*>(a.k_codes))[row * LPR + c] = nr.k[0];
+    static_cast<uint32_t*>(const_cast<void*>(a.v_codes))[row * LPR + c] = nr.v[0];
+    if (c == 0) {
+      const_cast<float*>(a.k_scales)[row] = nr.sk;
+      const_cast<float*>(a.v_scales)[row] = nr.sv;
     }
-    do_step(raw, (pe - t0 + NGRP - 1) / NGRP);
+    const RawRow raw[U] = {nr, nr, nr, nr};
+    do_step(raw, 1);
   }
 
   if (c == 0) {
@@ -220,12 +261,88 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
       }
     }
     const size_t o = (size_t)(b * a.Hq + kvh * G + h) * a.nsplit + sp;
-    a.ws_acc[o * D + d] = A;
-    if (d == 0) {
-      a.ws_ml[2 * o] = M;
-      a.ws_ml[2 * o + 1] = L;
+    if (a.merge_inline) {
+      publish(a.ws_acc + o * D + d, A);
+      if (d == 0) {
+        publish(a.ws_ml + 2 * o, M);
+        publish(a.ws_ml + 2 * o + 1, L);
+      }
+    } else {
+      a.ws_acc[o * D + d] = A;
+      if (d == 0) {
+        a.ws_ml[2 * o] = M;
+        a.ws_ml[2 * o + 1] = L;
+      }
     }
   }
+  if (!a.merge_inline) return;
+
+  // ---- in-kernel merge (few splits): every wave waits for its partial stores, the
+  // workgroup counts itself in with a device-scope atomic, and the last split of the
+  // (b, kv head) merges the partials with the log-sum-exp rule (the codec's output is
+  // rotated back), then resets the counter for the next call
+  __shared__ int s_last;
+  uint32_t* cnt = a.counters + (size_t)b * a.Hkv + kvh;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) s_last = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int np = a.nsplit;
+  if (s_last != np - 1) return;
+  const size_t pbase = (size_t)(b * a.Hq + kvh * G) * np;   // partial of (head 0, split 0)
+  float* s_w = &s_acc[0][0][0];       // [G][np] split maxima, then weights
+  float* s_ls = s_w + G * np;         // [G][np] split sums
+  float* s_L = s_ls + G * np;         // [G]
+  float* s_out = s_L + G;             // [G][D] merged output (codec: before the rotation)
+  for (int idx = tid; idx < G * np; idx += 256) {
+    const int h = idx / np, sI = idx % np;
+    s_w[idx] = fetch(a.ws_ml + 2 * (pbase + (size_t)h * np + sI));
+    s_ls[idx] = fetch(a.ws_ml + 2 * (pbase + (size_t)h * np + sI) + 1);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = NEG_INF;
+    for (int sI = 0; sI < np; ++sI) M = fmaxf(M, s_w[tid * np + sI]);
+    float Ls = 0.0f;
+    for (int sI = 0; sI < np; ++sI) {
+      const float ms = s_w[tid * np + sI];
+      const float w = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
+      s_w[tid * np + sI] = w;
+      Ls = __builtin_fmaf(w, s_ls[tid * np + sI], Ls);
+    }
+    s_L[tid] = Ls;
+  }
+  __syncthreads();
+  constexpr int MPF = 16;             // partial loads in flight per output
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx % D;
+    float A = 0.0f;
+    for (int s0 = 0; s0 < np; s0 += MPF) {   // MPF partials per chunk, loads issued together
+      float x[MPF];
+#pragma unroll
+      for (int t = 0; t < MPF; ++t)
+        x[t] = s0 + t < np ? fetch(a.ws_acc + (pbase + (size_t)h * np + s0 + t) * D + d) : 0.0f;
+#pragma unroll
+      for (int t = 0; t < MPF; ++t)
+        if (s0 + t < np) A = __builtin_fmaf(x[t], s_w[h * np + s0 + t], A);
+    }
+    const float o = A / s_L[h];
+    if (FMT == KVQ_WHT_LM4) s_out[h * D + d] = o;
+    else a.out[(size_t)(b * a.Hq + kvh * G + h) * D + d] = o;
+  }
+  if (FMT == KVQ_WHT_LM4) {   // back from the rotated domain: H o / sqrt(D), a row group per head
+    __syncthreads();
+    if (grp < G) {
+      float v[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) v[jj] = s_out[grp * D + 8 * c + jj];
+      wht_row<LPR>(v, c);
+      float* dst = a.out + (size_t)(b * a.Hq + kvh * G + grp) * D + 8 * c;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) dst[jj] = v[jj] * (1.0f / sqrtf((float)D));
+    }
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Block-wide max / sum for blockDim.x = D threads (1, 2 or 4 waves).
@@ -305,6 +422,8 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
   a.out[(size_t)(b * a.Hq + h) * D + d] = o;
 }
 
+constexpr int MERGE_INLINE_MAX = 16;
+
 template <int D, int FMT>
 hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
@@ -313,15 +432,20 @@ hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
     return launch_decode_int4_mfma(a, G, s);   // merges the splits itself
   if (FMT == KVQ_INT8_TOKEN && mfma_int8_eligible(D, a.cap, G))
     return launch_decode_int8_mfma(a, G, s);
+  // up to MERGE_INLINE_MAX splits the last split of a unit merges inside the kernel
+  // (one launch less); more partials are merged by the merge kernel, which spreads
+  // them over one workgroup per query head
+  DecodeArgs k = a;
+  k.merge_inline = a.nsplit <= MERGE_INLINE_MAX;
   switch (G) {
-    case 1: e = launch_kernel(decode_splitk_kernel<D, 1, FMT>, grid, dim3(256), a, s); break;
-    case 2: e = launch_kernel(decode_splitk_kernel<D, 2, FMT>, grid, dim3(256), a, s); break;
-    case 4: e = launch_kernel(decode_splitk_kernel<D, 4, FMT>, grid, dim3(256), a, s); break;
-    case 8: e = launch_kernel(decode_splitk_kernel<D, 8, FMT>, grid, dim3(256), a, s); break;
+    case 1: e = launch_kernel(decode_splitk_kernel<D, 1, FMT>, grid, dim3(256), k, s); break;
+    case 2: e = launch_kernel(decode_splitk_kernel<D, 2, FMT>, grid, dim3(256), k, s); break;
+    case 4: e = launch_kernel(decode_splitk_kernel<D, 4, FMT>, grid, dim3(256), k, s); break;
+    case 8: e = launch_kernel(decode_splitk_kernel<D, 8, FMT>, grid, dim3(256), k, s); break;
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
-  return launch_kernel(merge_kernel<D, FMT == KVQ_WHT_LM4>, dim3(a.Hq, a.B), dim3(D), a, s);
+  if (e != hipSuccess || k.merge_inline) return e;
+  return launch_kernel(merge_kernel<D, FMT == KVQ_WHT_LM4>, dim3(a.Hq, a.B), dim3(D), k, s);
 }
 
 template <int D>

@@ -1232,7 +1232,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // rule (device-scope loads: the partials come from other XCDs) and resets the arrival
   // counter.  Each thread first issues the loads of its outputs' first PF partials, so
   // their latency overlaps the maxima's.
-  constexpr int PF = 8;
+  constexpr int PF = 16;
   constexpr int OPT = (G * HD + NT - 1) / NT;           // outputs per thread
   float pre[OPT][PF];
 #pragma unroll
@@ -1281,9 +1281,16 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int sI = 0; sI < PF; ++sI)
         if (sI < np) A = __builtin_fmaf(pre[u][sI], s_w[h * np + sI], A);
-      for (int sI = PF; sI < np; ++sI)
-        A = __builtin_fmaf(fetch(a.ws_acc + (pbase + (size_t)h * nps + sI) * HD + d),
-                           s_w[h * np + sI], A);
+      // the rest in chunks of PF whose loads are issued together
+      for (int s0 = PF; s0 < np; s0 += PF) {
+        float x[PF];
+#pragma unroll
+        for (int t = 0; t < PF; ++t)
+          x[t] = s0 + t < np ? fetch(a.ws_acc + (pbase + (size_t)h * nps + s0 + t) * HD + d) : 0.0f;
+#pragma unroll
+        for (int t = 0; t < PF; ++t)
+          if (s0 + t < np) A = __builtin_fmaf(x[t], s_w[h * np + s0 + t], A);
+      }
       a.out[(size_t)(b * a.Hq + kvh * G + h) * HD + d] = A / s_L[h];
     }
   }
@@ -1323,6 +1330,7 @@ int32_t plan_splits_mfma(int32_t units, int32_t span) {
 }
 
 bool fused_append_supported(const kvq_cache_desc* d, int32_t q_group) {
+  if (d->format == KVQ_WHT_LM4) return true;   // the codec's split-K kernel codes the row
   return d->format == KVQ_INT4_G &&
          mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group);
 }

@@ -69,6 +69,35 @@ __device__ __forceinline__ void wht_row(float v[8], int c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Codec encode of one row spread over LPR = D/8 lanes (8 elements in lane c) for the
+// WHT + Lloyd-Max codec ("长上下文内存大瘦身：LARQL 四大 KV 缓存引擎原理与横向对比",
+// engine three): s = ||x||_2 / sqrt(D); the index of element i is the number of the
+// 15 decision thresholds strictly below (H x / sqrt(D))_i / s (a zero row: / 1).  Every
+// kernel that codes a row calls this, so all paths write the same codes.  x is
+// overwritten (rotated); w gets the lane's 8 indices (element 8c + i in bits 4i..4i+3).
+template <int LPR>
+__device__ __forceinline__ void codec_encode_row(float x[8], int c, const float* thr,
+                                                 uint32_t& w, float& s) {
+  constexpr int D = LPR * 8;
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(x[j], x[j], ss);
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
+  wht_row<LPR>(x, c);
+  s = sqrtf(ss / (float)D);
+  const float inv = (1.0f / sqrtf((float)D)) / (s == 0.0f ? 1.0f : s);  // u = (H x / sqrt(D)) / s
+  w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float u = x[j] * inv;
+    int idx = 0;
+#pragma unroll
+    for (int k = 0; k < 15; ++k) idx += (thr[k] < u) ? 1 : 0;
+    w |= (uint32_t)idx << (4 * j);
+  }
+}
+
 // Sum over aligned groups of LANES (2, 4, 8, 16 or 32) lanes, left in every lane of the
 // group, without an LDS round trip: quad swaps for partners 1 and 2, the half-row and
 // row mirrors (each pairs a lane with one in the other half of its group of 8 / 16)

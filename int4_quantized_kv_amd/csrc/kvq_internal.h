@@ -55,7 +55,9 @@ struct DecodeArgs {
   const uint16_t* v_new;
   int32_t B, Hkv, Hq, D, cap, gk, gv, window, nsplit;
   float qscale;          // softmax scale * log2(e)
-  float levels[16];
+  float levels[16];      // codec output levels
+  float thr[15];         // codec decision thresholds (the fused codec append)
+  int32_t merge_inline;  // split-K kernel: the last split of a unit merges (no merge kernel)
   int32_t lens[KVQ_MAX_BATCH];
 };
 
@@ -64,10 +66,10 @@ hipError_t launch_dequant_intq(int32_t format, const DequantArgs& a, hipStream_t
 hipError_t launch_codec_encode(const QuantArgs& a, hipStream_t s);
 hipError_t launch_codec_dequant(const DequantArgs& a, hipStream_t s);
 // Decode attention.  When the matrix-core kernel applies, the splits are merged inside
-// it (a.counters must then point at zeroed counters) and a.k_new / a.v_new, if set,
-// fuse the append of position lens[b] - 1 into it; the other kernels ignore both
-// (callers launch the append separately, see fused_append_supported) and run the
-// merge kernel.
+// it (a.counters must then point at zeroed counters).  a.k_new / a.v_new, if set, fuse
+// the append of position lens[b] - 1 into the INT4 matrix-core kernel and into the
+// codec's split-K kernel (see fused_append_supported); the other kernels require the
+// append to have been launched separately.
 hipError_t launch_decode(int32_t format, const DecodeArgs& a, int32_t q_group, hipStream_t s);
 
 // Split plan of the decode kernels for the cache `d`, `q_group` query heads per KV

@@ -261,6 +261,8 @@ FUSED_CASES = [
     ("int4", 64, 64, 4, 128, [300, 45], 0, None, 0),      # V group 64: append kernel first
     ("int8", 64, 128, 4, 128, [300, 45], 0, None, 3),
     ("codec", 64, 128, 4, 128, [300, 45], 0, None, 0),
+    ("codec", 64, 128, 2, 256, [1500, 1], 300, 512, 0),    # codec, ring, a 1-token sequence
+    ("codec", 64, 128, 2, 256, [4097, 1025], 1024, 1024, 3),  # window = capacity
 ]
 
 
