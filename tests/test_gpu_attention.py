@@ -10,7 +10,7 @@ import torch
 
 import int4_quantized_kv_amd as kvq
 import synth
-from oracle import attention, quant
+from oracle import attention, codec, quant
 from tests.kvq_testutil import append_decode, assert_attn_close, decode, np16
 
 pytestmark = pytest.mark.gpu
@@ -343,3 +343,40 @@ def test_append_decode_loop_reuses_workspace():
     out = decode(desc1, dc1, qs[0, :1].contiguous(), Hkv * G, [L], 0, 0.0, 9, ws=ws)
     ref = attention.decode_attention(np16(qs[0, :1]), kh[:1], vh[:1], [L])
     assert_attn_close(out.cpu().numpy(), ref, "batch 1 after batch 2")
+
+
+@pytest.mark.parametrize("fmt,D", [("int8", 128), ("int8", 64), ("codec", 128), ("int4", 256)])
+def test_other_paths_loop_reuse_workspace(fmt, D):
+    """Consecutive append + decode steps through one workspace on the INT8 matrix-core
+    kernel (D = 128) and the split-K kernel (the rest; splits merged in-kernel up to 16,
+    by the merge kernel beyond): the split counters are zero after every call and each
+    step matches the oracle."""
+    B, Hkv, G, P, steps = 2, 2, 2, 300, 6
+    L = P + steps
+    k = synth.kv_source((B, Hkv, L, D), 41, DEV, outlier_channels=2)
+    v = synth.kv_source((B, Hkv, L, D), 42, DEV, outlier_channels=2)
+    qs = synth.query((steps, B, Hkv * G, D), 43, DEV)
+    desc = kvq.make_desc(fmt, B, Hkv, D, L, min(64, D), min(128, D))
+    dc = kvq.DeviceCache(desc, DEV)
+    kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, :P].contiguous(), v[:, :, :P].contiguous(), 0, P)
+    ws = kvq.decode_workspace(desc, Hkv * G, L, 0, 40, DEV)
+    if fmt == "codec":
+        kidx, ksc, _ = codec.encode(np16(k))
+        vidx, vsc, _ = codec.encode(np16(v))
+        kh, vh = codec.decode(kidx, ksc), codec.decode(vidx, vsc)
+    else:
+        kh, vh = _oracle_hat(fmt, np16(k), np16(v), min(64, D), min(128, D))
+    for t in range(steps):
+        pos = P + t
+        q = qs[t].contiguous()
+        ns = (0, 1, 7, 16, 17, 40)[t]
+        out = append_decode(desc, dc, k[:, :, pos].contiguous(), v[:, :, pos].contiguous(), q,
+                            Hkv * G, [pos + 1, pos + 1], 0, 0.0, ns, ws=ws)
+        ref = attention.decode_attention(np16(q), kh, vh, [pos + 1, pos + 1])
+        if fmt == "codec":   # a code that flips at a threshold moves one value by a level gap
+            rel = np.linalg.norm(out.cpu().numpy() - ref) / np.linalg.norm(ref)
+            assert rel < 1e-3, (t, ns, rel)
+        else:
+            assert_attn_close(out.cpu().numpy(), ref, f"{fmt} D={D} step {t} nsplit={ns}")
+        counters = ws[: B * Hkv].view(torch.int32)
+        assert int(counters.abs().sum()) == 0, "split counters not reset"
