@@ -9,14 +9,19 @@
 //
 // Stage 1 (decode_splitk_kernel): one workgroup per (split, kv head, batch).  A row of
 // D values spans D/8 lanes (8 values per lane), so a 256-lane workgroup walks 2048/D
-// positions at a time; the G query heads of the KV head share every K/V load.  Scores
-// are kept in log2 units (q is pre-scaled by scale * log2 e) with an online softmax per
-// lane row; the rows are combined through LDS and the workgroup writes one unnormalized
-// partial (max, sum, weighted V) per query head.
-// Stage 2 (merge_kernel): out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
+// positions at a time, 4 per lane group per step with the next step's rows already in
+// flight; the G query heads of the KV head share every K/V load.  Scores are kept in
+// log2 units (q is pre-scaled by scale * log2 e) with an online softmax per lane row;
+// the rows are combined through LDS and the workgroup writes one unnormalized partial
+// (max, sum, weighted V) per query head.
+// Stage 2: out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i, inside stage 1 by the
+// last split of a (b, kv head) when there are at most 16 splits, otherwise by
+// merge_kernel (one workgroup per query head).
 // Codec: keys/values stay in the rotated domain.  Since H/sqrt(D) is orthonormal and
 // symmetric, q . x_hat = (H q / sqrt(D)) . (s c[idx]); q is rotated once per workgroup
-// and the merged output is rotated back once per (b, h).
+// and the merged output is rotated back once per (b, h).  With the append fused, split
+// 0 codes the new row (the same row encoder as the append kernel) and attends it from
+// registers.
 #include <cmath>
 
 #include "kvq_device.h"

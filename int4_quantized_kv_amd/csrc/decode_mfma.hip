@@ -1,6 +1,7 @@
-// decode_mfma.hip -- split-K decode attention over the packed INT4 cache on the gfx950
-// matrix cores, for head_dim 128, one V scale per row (V group 128), any K group that is
-// a multiple of 32, and GQA groups of 1, 2, 4 or 8 query heads per KV head.
+// decode_mfma.hip -- split-K decode attention over the packed cache on the gfx950 matrix
+// cores, for head_dim 128 and GQA groups of 1, 2, 4 or 8 query heads per KV head: the
+// INT4 format with one V scale per row (V group 128) and any K group that is a multiple
+// of 32, and the INT8 per-token format (see "INT8 per-token tiles").
 //
 // Semantics as decode.hip (bxzpzcl.cn/news/2871434 section 3.2; lpnh.cn/news/2042373
 // sections 1.1 and 2.1; in-operator dequantization, pwwt.cn/news/4219524 section 5).
@@ -8,33 +9,35 @@
 // Why MFMA: one decode step reads every cached position once; with the G query heads
 // of a KV head sharing that read, q.K and P.V are G x 128 contractions per position.
 // Done with fp32 FMAs they cost ~8 VALU ops per cached byte, above what the vector ALUs
-// sustain at HBM speed (~5 per byte), so both contractions go to v_mfma_f32_16x16x32_f16
-// and the VALU only unpacks nibbles and runs the softmax.
+// sustain at HBM speed (~5 per byte), so both contractions go to the matrix cores and
+// the VALU only unpacks codes and runs the softmax.
 //
-// Per wave, per tile of 32 positions (two 16-position halves T = 0, 1):
-//   q.K   A = K codes (rows = 16 positions, k = 32 head dims), B = q.  Lane (r, j) =
-//         (lane % 16, lane / 16) holds the 16-byte chunk j (dims 32j .. 32j + 31) of
-//         position r and feeds dword c of it to MFMA c.  The K group scale differs per
-//         group, so the 16 B columns are (query head, K group) pairs: column
-//         head * NGK + g carries q only on the lanes whose dims lie in group g.  Each
-//         column's result is scaled by its group's scale and the NGK adjacent columns
-//         are summed with a lane shuffle: z = sum_g sK[t, g] * (q . codes_g).
+// INT4, per wave, per tile of 32 positions (two 16-position halves T = 0, 1):
+//   q.K   A = K codes (rows = 16 positions, k = 32 head dims), B = q, v_mfma_f32_16x16x32_f16.
+//         The K group scale differs per group, so the 16 B columns are (query head,
+//         K group) pairs: column head * NGK + g carries q only in the k slots of dims in
+//         group g.  Each column's result is scaled by its group's scale and the NGK
+//         adjacent columns are summed with a lane shuffle: z = sum_g sK[t, g] (q . codes_g).
+//         With at most 8 columns in use, the other 8 score the second half of the tile
+//         in the same MFMAs (see "Position sets").
 //   P.V   computed transposed: A = V codes (rows = 16 head dims, k = 32 positions),
 //         B = P (k = positions, columns = heads).  Lane (r, j) loads dword r of the 8
 //         positions {4j..4j+3, 16+4j..16+4j+3} whose scores it already holds from q.K, so
 //         P needs no data movement.  MFMA e (e = 0..7) covers dims {8r + e}.  The V row
-//         scale is folded into P (p' = p * sV[t]); p' is split into fp16 hi + lo and both
-//         go through the MFMA, so P.V keeps ~22 bits (fp16 P alone would lose ~1e-4).
-// Nibbles become fp16 exactly: flipping bit 3 turns a two's complement nibble into
-// u = q + 8, (u | 0x6400) is the fp16 1024 + u, and a packed subtract of 1032 leaves q;
-// the first two steps are one v_bitop3 per nibble pair.
+//         scale is folded into P (p' = p * sV[t]); p' is split into fp16 hi + lo, which
+//         ride in a head's two columns of one MFMA, so P.V keeps ~22 bits (fp16 P alone
+//         would lose ~1e-4).
+// Codes become exact MFMA operands: K nibbles as biased fp16 subnormals (the bias is
+// removed after the MFMA), V nibbles as fp16 integers via the 1024 exponent bias and a
+// packed subtract (see v_pair_f16 and unpack_word_u).
 // The online softmax keeps the running maximum of the unscaled scores and forms
 // p = 2^(s * (z - m)) with s = softmax scale * log2 e (one fma + exp per score); it
 // rescales the accumulators only when some head's running maximum grows.
-// The four waves of a workgroup take interleaved tiles of the split and merge their
-// (max, sum, weighted V) through LDS; the workgroup that finishes last for a (sequence,
-// KV head) then combines the splits' partials (no separate merge launch).
-// Tiles are staged through LDS by direct global->LDS transfers (see "LDS staging").
+// The eight waves of a workgroup (one per CU) claim tiles of the split from an LDS
+// counter and merge their (max, sum, weighted V) through LDS; the workgroup that
+// finishes last for a (sequence, KV head) then combines the splits' partials (no
+// separate merge launch).  Tiles are staged through LDS by direct global->LDS
+// transfers (see "LDS staging").
 #include <cmath>
 #include <type_traits>
 
