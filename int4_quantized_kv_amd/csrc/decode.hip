@@ -134,6 +134,14 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   int t0 = ps + grp;
   RawRow cur[U];
   if (t0 < pe) load_step(t0, cur);
+  // codec with the append fused: row group 0 of split 0 codes the new row (fp16 K and V
+  // requested here, coded once q is ready) and attends it after its cached rows
+  const bool app_grp = FMT == KVQ_WHT_LM4 && fused && sp == 0 && grp == 0;
+  uint4 newk = make_uint4(0u, 0u, 0u, 0u), newv = newk;
+  if (app_grp) {
+    newk = *reinterpret_cast<const uint4*>(a.k_new + bh * D + 8 * c);
+    newv = *reinterpret_cast<const uint4*>(a.v_new + bh * D + 8 * c);
+  }
 
   float q[G][8];
 #pragma unroll
@@ -146,6 +154,24 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) q[h][j] *= a.qscale;
+  }
+  RawRow nr;
+  if (app_grp) {
+    // coded as the append kernel codes it and written to its slot (no other split reads
+    // that slot: it is outside [lo, len - 1) and holds no position of the horizon)
+    float x[8];
+    f16x8_unpack(newk, x);
+    codec_encode_row<LPR>(x, c, a.thr, nr.k[0], nr.sk);
+    f16x8_unpack(newv, x);
+    codec_encode_row<LPR>(x, c, a.thr, nr.v[0], nr.sv);
+    nr.k[1] = nr.v[1] = 0u;
+    const size_t row = bh * a.cap + (len - 1) % a.cap;
+    static_cast<uint32_t*>(const_cast<void*>(a.k_codes))[row * LPR + c] = nr.k[0];
+    static_cast<uint32_t*>(const_cast<void*>(a.v_codes))[row * LPR + c] = nr.v[0];
+    if (c == 0) {
+      const_cast<float*>(a.k_scales)[row] = nr.sk;
+      const_cast<float*>(a.v_scales)[row] = nr.sv;
+    }
   }
 
   float m[G], l[G], acc[G][8];
@@ -214,25 +240,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     t0 = t1;
   }
-  if (FMT == KVQ_WHT_LM4 && fused && sp == 0 && grp == 0) {
-    // the new row: coded as the append kernel codes it, written to its slot (no other
-    // split reads that slot: it is outside [lo, len - 1) and holds no position of the
-    // horizon), and added to this row group's softmax as one more row
-    const size_t unit = (size_t)b * a.Hkv + kvh;
-    RawRow nr;
-    float x[8];
-    load8_f16(a.k_new + unit * D + 8 * c, x);
-    codec_encode_row<LPR>(x, c, a.thr, nr.k[0], nr.sk);
-    load8_f16(a.v_new + unit * D + 8 * c, x);
-    codec_encode_row<LPR>(x, c, a.thr, nr.v[0], nr.sv);
-    nr.k[1] = nr.v[1] = 0u;
-    const size_t row = bh * a.cap + (len - 1) % a.cap;
-    static_cast<uint32_t*>(const_cast<void*>(a.k_codes))[row * LPR + c] = nr.k[0];
-    static_cast<uint32_t*>(const_cast<void*>(a.v_codes))[row * LPR + c] = nr.v[0];
-    if (c == 0) {
-      const_cast<float*>(a.k_scales)[row] = nr.sk;
-      const_cast<float*>(a.v_scales)[row] = nr.sv;
-    }
+  if (app_grp) {   // the new row: one more row of this group's softmax
     const RawRow raw[U] = {nr, nr, nr, nr};
     do_step(raw, 1);
   }
@@ -299,6 +307,16 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   float* s_ls = s_w + G * np;         // [G][np] split sums
   float* s_L = s_ls + G * np;         // [G]
   float* s_out = s_L + G;             // [G][D] merged output (codec: before the rotation)
+  // the accumulators of this thread's first output are requested together with the
+  // (max, sum) pairs, so the two round trips overlap
+  constexpr int MPF = 16;             // partial loads in flight per output
+  float pre[MPF];
+  {
+    const int h0 = tid / D, d0 = tid % D;
+#pragma unroll
+    for (int t = 0; t < MPF; ++t)
+      pre[t] = tid < G * D && t < np ? fetch(a.ws_acc + (pbase + (size_t)h0 * np + t) * D + d0) : 0.0f;
+  }
   for (int idx = tid; idx < G * np; idx += 256) {
     const int h = idx / np, sI = idx % np;
     s_w[idx] = fetch(a.ws_ml + 2 * (pbase + (size_t)h * np + sI));
@@ -318,11 +336,17 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     s_L[tid] = Ls;
   }
   __syncthreads();
-  constexpr int MPF = 16;             // partial loads in flight per output
   for (int idx = tid; idx < G * D; idx += 256) {
     const int h = idx / D, d = idx % D;
     float A = 0.0f;
-    for (int s0 = 0; s0 < np; s0 += MPF) {   // MPF partials per chunk, loads issued together
+    int s0 = 0;
+    if (idx == tid) {                 // the first output: its first MPF partials are in pre
+#pragma unroll
+      for (int t = 0; t < MPF; ++t)
+        if (t < np) A = __builtin_fmaf(pre[t], s_w[h * np + t], A);
+      s0 = MPF;
+    }
+    for (; s0 < np; s0 += MPF) {      // MPF partials per chunk, loads issued together
       float x[MPF];
 #pragma unroll
       for (int t = 0; t < MPF; ++t)
