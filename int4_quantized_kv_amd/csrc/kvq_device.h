@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kvq {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -40,10 +42,35 @@ __device__ __forceinline__ int nib_s(uint32_t w, int j) {
 // Unsigned 4-bit field j of a packed word.
 __device__ __forceinline__ int nib_u(uint32_t w, int j) { return (w >> (4 * j)) & 15; }
 
+// x from lane (lane ^ M) within aligned groups of 2M lanes (M = 1, 2, 4, 8, 16), by DPP
+// and the gfx950 row-pair swap (VALU, no LDS round trip): partners 1 and 2 are quad
+// permutes, 4 is a quad xor-3 followed by a half-row mirror (lane i ^ 7), 8 is a
+// rotation by 8 within a 16-lane row, 16 is v_permlane16_swap of a register with a copy
+// of itself (one copy then holds row r, the other row r ^ 1) and a select.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               CTRL, 0xF, 0xF, false));
+}
+template <int M>
+__device__ __forceinline__ float xor_lane(float x, int lane_in_group) {
+  if constexpr (M == 1) return dpp_mov<0xB1>(x);            // quad_perm [1, 0, 3, 2]
+  else if constexpr (M == 2) return dpp_mov<0x4E>(x);       // quad_perm [2, 3, 0, 1]
+  else if constexpr (M == 4) return dpp_mov<0x141>(dpp_mov<0x1B>(x));   // xor 3, mirror 8
+  else if constexpr (M == 8) return dpp_mov<0x128>(x);      // row_ror:8
+  else {
+    static_assert(M == 16, "partners 1 .. 16");
+    uint32_t p = __builtin_bit_cast(uint32_t, x), q = p;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(p), "+v"(q));
+    return __builtin_bit_cast(float, (lane_in_group & 16) ? p : q);
+  }
+}
+
 // Unnormalized Sylvester Walsh-Hadamard transform of one row spread over `lpr`
 // consecutive lanes, each holding 8 consecutive elements (element 8*c + i in lane c).
 // Butterflies (a, b) -> (a + b, a - b) over every bit of the element index; the
-// three low bits are inside a lane, the others pair lane c with lane c ^ m.
+// three low bits are inside a lane, the others pair lane c with lane c ^ m.  All the
+// row's lanes must be active.
 template <int LPR>
 __device__ __forceinline__ void wht_row(float v[8], int c) {
 #pragma unroll
@@ -57,14 +84,31 @@ __device__ __forceinline__ void wht_row(float v[8], int c) {
       }
     }
   }
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) {
+  auto stage = [&](auto mtag) {
+    constexpr int M = decltype(mtag)::value;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p = __shfl_xor(v[i], m);
-      v[i] = (c & m) ? (p - v[i]) : (v[i] + p);
+      const float p = xor_lane<M>(v[i], c);
+      v[i] = (c & M) ? (p - v[i]) : (v[i] + p);
     }
-  }
+  };
+  if constexpr (LPR > 1) stage(std::integral_constant<int, 1>{});
+  if constexpr (LPR > 2) stage(std::integral_constant<int, 2>{});
+  if constexpr (LPR > 4) stage(std::integral_constant<int, 4>{});
+  if constexpr (LPR > 8) stage(std::integral_constant<int, 8>{});
+  if constexpr (LPR > 16) stage(std::integral_constant<int, 16>{});
+}
+
+// Sum over the LPR lanes of a row, by the same xor pairings as wht_row (so every path
+// that reduces a row this way gets the same bits).
+template <int LPR>
+__device__ __forceinline__ float row_xor_sum(float x, int c) {
+  if constexpr (LPR > 1) x += xor_lane<1>(x, c);
+  if constexpr (LPR > 2) x += xor_lane<2>(x, c);
+  if constexpr (LPR > 4) x += xor_lane<4>(x, c);
+  if constexpr (LPR > 8) x += xor_lane<8>(x, c);
+  if constexpr (LPR > 16) x += xor_lane<16>(x, c);
+  return x;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -82,8 +126,7 @@ __device__ __forceinline__ void codec_encode_row(float x[8], int c, const float*
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(x[j], x[j], ss);
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
+  ss = row_xor_sum<LPR>(ss, c);
   wht_row<LPR>(x, c);
   s = sqrtf(ss / (float)D);
   const float inv = (1.0f / sqrtf((float)D)) / (s == 0.0f ? 1.0f : s);  // u = (H x / sqrt(D)) / s
