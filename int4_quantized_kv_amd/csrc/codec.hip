@@ -28,6 +28,7 @@ __global__ void __launch_bounds__(256) codec_encode_kernel(QuantArgs a) {
   float* scales = isv ? a.v_scales : a.k_scales;
   const uint32_t total = (uint32_t)a.rows * LPR;
   const uint32_t stride = gridDim.x * blockDim.x;
+  const Thresholds thr = load_thresholds(a.thr);
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
     const uint32_t row = i / LPR;
     const int c = (int)(i - row * LPR);
@@ -35,7 +36,7 @@ __global__ void __launch_bounds__(256) codec_encode_kernel(QuantArgs a) {
     load8_f16(src + (size_t)i * 8, x);
     uint32_t w;
     float s;
-    codec_encode_row<LPR>(x, c, a.thr, w, s);
+    codec_encode_row<LPR>(x, c, thr, w, s);
     const uint32_t bh = row / (uint32_t)a.map.n;
     const int t = (int)(row - bh * a.map.n);
     const int b = (int)(bh / (uint32_t)a.Hkv);

@@ -39,6 +39,11 @@ __device__ __forceinline__ void publish(float* p, float v) {
 __device__ __forceinline__ float fetch(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// an 8-byte-aligned (max, sum) pair in one load
+__device__ __forceinline__ uint64_t fetch_pair(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // The packed bytes lane c owns of one row (cache row index b*Hkv*C + slot): its code
 // word(s) and the scale of its group, for K and V.  Loaded for several rows before any
@@ -93,6 +98,10 @@ __device__ __forceinline__ void codes_f32(const uint32_t w[2], const float* lv, 
   }
 }
 
+// Up to this many splits, the last split of a (sequence, KV head) merges the partials
+// inside the split-K kernel; above, the merge kernel does.
+constexpr int MERGE_INLINE_MAX = 32;
+
 template <int D, int G, int FMT>
 __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   constexpr int LPR = D / 8;
@@ -101,22 +110,21 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   __shared__ float s_l[NGRP][G];
   __shared__ float s_acc[NGRP][G][D];
   __shared__ float lv[16];
-  if (FMT == KVQ_WHT_LM4) {
-    if (threadIdx.x < 16) lv[threadIdx.x] = a.levels[threadIdx.x];
-    __syncthreads();
-  }
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, grp = tid / LPR, c = tid % LPR;
   const int len = a.lens[b];
   const int lo = a.window > 0 ? max(0, len - a.window) : 0;
   // codec with the append fused: position len - 1 is the new row, coded in this kernel
-  // by split 0 and attended from registers; the splits cover [lo, len - 1)
+  // and attended from registers by the last split, which (when there are several) has
+  // no other rows: the other splits cover [lo, len - 1)
   const bool fused = FMT == KVQ_WHT_LM4 && a.k_new != nullptr;
+  const bool app_split = fused && sp == a.nsplit - 1;
+  const int nrs = fused && a.nsplit > 1 ? a.nsplit - 1 : a.nsplit;   // splits with rows
   const int pt = fused ? len - 1 : len;
   const int span = pt - lo;
-  const int chunk = span > 0 ? (span + a.nsplit - 1) / a.nsplit : 0;
-  const int ps = min(pt, lo + sp * chunk);
+  const int chunk = span > 0 ? (span + nrs - 1) / nrs : 0;
+  const int ps = sp < nrs ? min(pt, lo + sp * chunk) : pt;
   const int pe = min(pt, ps + chunk);
 
   // the rows of the first step are requested before q is loaded and rotated, so the
@@ -134,13 +142,16 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   int t0 = ps + grp;
   RawRow cur[U];
   if (t0 < pe) load_step(t0, cur);
-  // codec with the append fused: row group 0 of split 0 codes the new row (fp16 K and V
-  // requested here, coded once q is ready) and attends it after its cached rows
-  const bool app_grp = FMT == KVQ_WHT_LM4 && fused && sp == 0 && grp == 0;
-  uint4 newk = make_uint4(0u, 0u, 0u, 0u), newv = newk;
-  if (app_grp) {
-    newk = *reinterpret_cast<const uint4*>(a.k_new + bh * D + 8 * c);
-    newv = *reinterpret_cast<const uint4*>(a.v_new + bh * D + 8 * c);
+  // the append split: row group 0 codes the new K row and row group 1 the new V row,
+  // side by side in wave 0 (fp16 rows requested here, coded once q is ready); group 0
+  // then attends the new row (after its cached rows, if the split has any)
+  const bool app_wave = app_split && tid < 64;   // wave-uniform
+  const bool app_grp = app_wave && grp == 0;
+  uint4 newx = make_uint4(0u, 0u, 0u, 0u);
+  Thresholds thr;
+  if (app_wave) {
+    if (grp < 2) newx = *reinterpret_cast<const uint4*>((grp ? a.v_new : a.k_new) + bh * D + 8 * c);
+    thr = load_thresholds(a.thr);
   }
 
   float q[G][8];
@@ -156,22 +167,32 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     for (int j = 0; j < 8; ++j) q[h][j] *= a.qscale;
   }
   RawRow nr;
-  if (app_grp) {
-    // coded as the append kernel codes it and written to its slot (no other split reads
-    // that slot: it is outside [lo, len - 1) and holds no position of the horizon)
+  if (app_wave) {
+    // coded as the append kernel codes it (every lane of the wave runs the coder, so
+    // its lane exchanges stay inside active rows) and written to the row's slot, which
+    // no other split reads: it is outside [lo, len - 1) and holds no horizon position
     float x[8];
-    f16x8_unpack(newk, x);
-    codec_encode_row<LPR>(x, c, a.thr, nr.k[0], nr.sk);
-    f16x8_unpack(newv, x);
-    codec_encode_row<LPR>(x, c, a.thr, nr.v[0], nr.sv);
-    nr.k[1] = nr.v[1] = 0u;
-    const size_t row = bh * a.cap + (len - 1) % a.cap;
-    static_cast<uint32_t*>(const_cast<void*>(a.k_codes))[row * LPR + c] = nr.k[0];
-    static_cast<uint32_t*>(const_cast<void*>(a.v_codes))[row * LPR + c] = nr.v[0];
-    if (c == 0) {
-      const_cast<float*>(a.k_scales)[row] = nr.sk;
-      const_cast<float*>(a.v_scales)[row] = nr.sv;
+    f16x8_unpack(newx, x);
+    uint32_t w;
+    float sc;
+    codec_encode_row<LPR>(x, c, thr, w, sc);
+    if (grp < 2) {
+      const size_t row = bh * a.cap + (len - 1) % a.cap;
+      static_cast<uint32_t*>(const_cast<void*>(grp ? a.v_codes : a.k_codes))[row * LPR + c] = w;
+      if (c == 0) const_cast<float*>(grp ? a.v_scales : a.k_scales)[row] = sc;
     }
+    // group 0 takes the V row's word and scale from the lane LPR above it
+    const int src = ((tid + LPR) & 63) << 2;
+    nr.k[0] = w;
+    nr.sk = sc;
+    nr.v[0] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)w);
+    nr.sv = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sc)));
+    nr.k[1] = nr.v[1] = 0u;
+  }
+
+  if (FMT == KVQ_WHT_LM4) {   // the codebook levels (the barrier comes after the loads above)
+    if (tid < 16) lv[tid] = a.levels[tid];
+    __syncthreads();
   }
 
   float m[G], l[G], acc[G][8];
@@ -303,61 +324,82 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   const int np = a.nsplit;
   if (s_last != np - 1) return;
   const size_t pbase = (size_t)(b * a.Hq + kvh * G) * np;   // partial of (head 0, split 0)
-  float* s_w = &s_acc[0][0][0];       // [G][np] split maxima, then weights
-  float* s_ls = s_w + G * np;         // [G][np] split sums
-  float* s_L = s_ls + G * np;         // [G]
+  static_assert(MERGE_INLINE_MAX == 32, "one split per lane of a 32-lane half wave");
+  float* s_w = &s_acc[0][0][0];       // [G][32] split weights (0 past np)
+  float* s_L = s_w + G * 32;          // [G] weighted sums of the split sums
   float* s_out = s_L + G;             // [G][D] merged output (codec: before the rotation)
-  // the accumulators of this thread's first output are requested together with the
-  // (max, sum) pairs, so the two round trips overlap
-  constexpr int MPF = 16;             // partial loads in flight per output
-  float pre[MPF];
-  {
-    const int h0 = tid / D, d0 = tid % D;
+  const int wave = tid >> 6, lane = tid & 63;
+  // every thread first requests its outputs' partials (up to 64 loads), and wave w the
+  // (max, sum) pairs of heads w, w + 4, ... (split = lane), so that all are one round
+  // trip; the partial loads go in groups of 8 under a uniform test, the split index
+  // clamped to np - 1 inside a group (their weight is 0) and the output index to the
+  // last output
+  constexpr int OPT = (G * D + 255) / 256;                 // outputs per thread
+  constexpr int PF = OPT <= 2 ? 32 : 64 / OPT;             // partials prefetched per output
+  float pre[OPT][PF];
 #pragma unroll
-    for (int t = 0; t < MPF; ++t)
-      pre[t] = tid < G * D && t < np ? fetch(a.ws_acc + (pbase + (size_t)h0 * np + t) * D + d0) : 0.0f;
+  for (int u = 0; u < OPT; ++u) {
+    const int idx = min(tid + 256 * u, G * D - 1), h = idx / D, d = idx % D;
+    const float* src = a.ws_acc + (pbase + (size_t)h * np) * D + d;
+#pragma unroll
+    for (int t8 = 0; t8 < PF; t8 += 8) {
+      if (t8 < np) {
+#pragma unroll
+        for (int t = t8; t < t8 + 8; ++t) pre[u][t] = fetch(src + (size_t)min(t, np - 1) * D);
+      } else {
+#pragma unroll
+        for (int t = t8; t < t8 + 8; ++t) pre[u][t] = 0.0f;
+      }
+    }
   }
-  for (int idx = tid; idx < G * np; idx += 256) {
-    const int h = idx / np, sI = idx % np;
-    s_w[idx] = fetch(a.ws_ml + 2 * (pbase + (size_t)h * np + sI));
-    s_ls[idx] = fetch(a.ws_ml + 2 * (pbase + (size_t)h * np + sI) + 1);
+  constexpr int HPW = (G + 3) / 4;                         // heads per wave
+  float mt[HPW], lt[HPW];
+#pragma unroll
+  for (int k = 0; k < HPW; ++k) {
+    const int h = wave + 4 * k;
+    mt[k] = NEG_INF;
+    lt[k] = 0.0f;
+    if (h < G && lane < np) {
+      const uint64_t ml = fetch_pair(a.ws_ml + 2 * (pbase + (size_t)h * np + lane));
+      mt[k] = __builtin_bit_cast(float, (uint32_t)ml);
+      lt[k] = __builtin_bit_cast(float, (uint32_t)(ml >> 32));
+    }
+  }
+  // weights 2^(m_s - M) by DPP reductions over the 32 lanes of the first half wave
+#pragma unroll
+  for (int k = 0; k < HPW; ++k) {
+    const int h = wave + 4 * k;
+    if (h < G) {   // wave-uniform
+      const float M = lane_group_max<32>(mt[k]);
+      const float w = mt[k] != NEG_INF ? fast_exp2(mt[k] - M) : 0.0f;
+      const float L = lane_group_sum<32>(w * lt[k]);
+      if (lane < 32) s_w[h * 32 + lane] = w;
+      if (lane == 0) s_L[h] = L;
+    }
   }
   __syncthreads();
-  if (tid < G) {
-    float M = NEG_INF;
-    for (int sI = 0; sI < np; ++sI) M = fmaxf(M, s_w[tid * np + sI]);
-    float Ls = 0.0f;
-    for (int sI = 0; sI < np; ++sI) {
-      const float ms = s_w[tid * np + sI];
-      const float w = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
-      s_w[tid * np + sI] = w;
-      Ls = __builtin_fmaf(w, s_ls[tid * np + sI], Ls);
-    }
-    s_L[tid] = Ls;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx % D;
-    float A = 0.0f;
-    int s0 = 0;
-    if (idx == tid) {                 // the first output: its first MPF partials are in pre
 #pragma unroll
-      for (int t = 0; t < MPF; ++t)
-        if (t < np) A = __builtin_fmaf(pre[t], s_w[h * np + t], A);
-      s0 = MPF;
-    }
-    for (; s0 < np; s0 += MPF) {      // MPF partials per chunk, loads issued together
-      float x[MPF];
+  for (int u = 0; u < OPT; ++u) {
+    const int idx = tid + 256 * u;
+    if (idx < G * D) {
+      const int h = idx / D, d = idx % D;
+      const float* wh = s_w + h * 32;
+      float A = 0.0f;
 #pragma unroll
-      for (int t = 0; t < MPF; ++t)
-        x[t] = s0 + t < np ? fetch(a.ws_acc + (pbase + (size_t)h * np + s0 + t) * D + d) : 0.0f;
+      for (int t = 0; t < PF; ++t) A = __builtin_fmaf(pre[u][t], wh[t], A);
+      for (int s0 = PF; s0 < np; s0 += PF) {   // the rest: PF loads issued together
+        float x[PF];
 #pragma unroll
-      for (int t = 0; t < MPF; ++t)
-        if (s0 + t < np) A = __builtin_fmaf(x[t], s_w[h * np + s0 + t], A);
+        for (int t = 0; t < PF; ++t)
+          x[t] = s0 + t < np ? fetch(a.ws_acc + (pbase + (size_t)h * np + s0 + t) * D + d) : 0.0f;
+#pragma unroll
+        for (int t = 0; t < PF; ++t)
+          if (s0 + t < np) A = __builtin_fmaf(x[t], wh[s0 + t], A);
+      }
+      const float o = A / s_L[h];
+      if (FMT == KVQ_WHT_LM4) s_out[h * D + d] = o;
+      else a.out[(size_t)(b * a.Hq + kvh * G + h) * D + d] = o;
     }
-    const float o = A / s_L[h];
-    if (FMT == KVQ_WHT_LM4) s_out[h * D + d] = o;
-    else a.out[(size_t)(b * a.Hq + kvh * G + h) * D + d] = o;
   }
   if (FMT == KVQ_WHT_LM4) {   // back from the rotated domain: H o / sqrt(D), a row group per head
     __syncthreads();
@@ -451,7 +493,6 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
   a.out[(size_t)(b * a.Hq + h) * D + d] = o;
 }
 
-constexpr int MERGE_INLINE_MAX = 16;
 
 template <int D, int FMT>
 hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
@@ -497,14 +538,17 @@ int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
     return plan_splits_mfma(units, span);
   if (d->format == KVQ_INT8_TOKEN && mfma_int8_eligible(d->head_dim, d->capacity, q_group))
     return plan_splits_mfma(units, span);
+  // the codec keeps one more split for the new row when its append is fused (planned
+  // for every codec call, so that the workspace query does not depend on the call)
+  const int32_t extra = d->format == KVQ_WHT_LM4 ? 1 : 0;
   const int32_t target = 1024;       // workgroups: 4 per CU on 256 CUs (all resident)
   const int32_t min_rows = 64;       // positions per split worth a workgroup (short
                                      // contexts need many splits to fill the chip)
   int32_t n = (target + units - 1) / units;
   const int32_t by_span = (span + min_rows - 1) / min_rows;
   if (n > by_span) n = by_span;
-  if (n > 1024) n = 1024;
-  return n < 1 ? 1 : n;
+  if (n > 1024 - extra) n = 1024 - extra;
+  return (n < 1 ? 1 : n) + extra;
 }
 
 hipError_t launch_decode(int32_t format, const DecodeArgs& a, int32_t q_group, hipStream_t s) {

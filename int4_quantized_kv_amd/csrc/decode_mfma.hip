@@ -1237,17 +1237,25 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // their latency overlaps the maxima's.
   constexpr int PF = 16;
   constexpr int OPT = (G * HD + NT - 1) / NT;           // outputs per thread
+  // (branch-free: the loads go in groups of 4 under a uniform test, the split index
+  // clamped to np - 1 inside a group and the output index to the last output)
   float pre[OPT][PF];
 #pragma unroll
   for (int u = 0; u < OPT; ++u) {
-    const int idx = threadIdx.x + NT * u;
-    const int h = idx / HD, d = idx % HD;
+    const int idx = min((int)threadIdx.x + NT * u, G * HD - 1);
+    const float* src = a.ws_acc + (pbase + (size_t)(idx / HD) * nps) * HD + idx % HD;
 #pragma unroll
-    for (int sI = 0; sI < PF; ++sI)
-      pre[u][sI] = idx < G * HD && sI < np ? fetch(a.ws_acc + (pbase + (size_t)h * nps + sI) * HD + d)
-                                           : 0.0f;
+    for (int s4 = 0; s4 < PF; s4 += 4) {
+      if (s4 < np) {
+#pragma unroll
+        for (int sI = s4; sI < s4 + 4; ++sI) pre[u][sI] = fetch(src + (size_t)min(sI, np - 1) * HD);
+      } else {
+#pragma unroll
+        for (int sI = s4; sI < s4 + 4; ++sI) pre[u][sI] = 0.0f;
+      }
+    }
   }
-  float* s_w = reinterpret_cast<float*>(smem);          // [G][np] split maxima, then weights
+  float* s_w = reinterpret_cast<float*>(smem);          // [G][np] split maxima (then weights)
   float* s_ls = s_w + G * np;                           // [G][np] split sums
   float* s_L = s_ls + G * np;                           // [G]
   for (int idx = threadIdx.x; idx < G * np; idx += NT) {
@@ -1257,33 +1265,53 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     s_ls[idx] = __builtin_bit_cast(float, (uint32_t)(ml >> 32));
   }
   __syncthreads();
-  // one wave per head: maximum, weights 2^(m_s - M), weighted sum of the partial sums
-  for (int h = wave; h < G; h += WAVES) {
-    float M = NEG_INF;
-    for (int sI = lane; sI < np; sI += 64) M = fmaxf(M, s_w[h * np + sI]);
+  // weights 2^(m_s - M) and the weighted sum of the partial sums: up to 32 splits every
+  // thread computes them for its outputs from broadcast LDS reads (no second barrier);
+  // above, one wave per head does, into s_w and s_L
+  const bool own_weights = np <= 32;   // uniform
+  if (!own_weights) {
+    for (int h = wave; h < G; h += WAVES) {
+      float M = NEG_INF;
+      for (int sI = lane; sI < np; sI += 64) M = fmaxf(M, s_w[h * np + sI]);
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
-    float Ls = 0.0f;
-    for (int sI = lane; sI < np; sI += 64) {
-      const float ms = s_w[h * np + sI];
-      const float wgt = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
-      s_w[h * np + sI] = wgt;
-      Ls = __builtin_fmaf(wgt, s_ls[h * np + sI], Ls);
+      for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+      float Ls = 0.0f;
+      for (int sI = lane; sI < np; sI += 64) {
+        const float ms = s_w[h * np + sI];
+        const float wgt = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
+        s_w[h * np + sI] = wgt;
+        Ls = __builtin_fmaf(wgt, s_ls[h * np + sI], Ls);
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) Ls += __shfl_xor(Ls, m);
+      if (lane == 0) s_L[h] = Ls;
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) Ls += __shfl_xor(Ls, m);
-    if (lane == 0) s_L[h] = Ls;
+    __syncthreads();
   }
-  __syncthreads();
 #pragma unroll
   for (int u = 0; u < OPT; ++u) {
     const int idx = threadIdx.x + NT * u;
     if (idx < G * HD) {
       const int h = idx / HD, d = idx % HD;
-      float A = 0.0f;
+      const float* mh = s_w + h * np;
+      const float* lh = s_ls + h * np;
+      float M = NEG_INF;
+      if (own_weights) {
+#pragma unroll 4
+        for (int sI = 0; sI < np; ++sI) M = fmaxf(M, mh[sI]);
+      }
+      auto weight = [&](int sI) {
+        return own_weights ? (mh[sI] != NEG_INF ? fast_exp2(mh[sI] - M) : 0.0f) : mh[sI];
+      };
+      float A = 0.0f, L = 0.0f;
 #pragma unroll
-      for (int sI = 0; sI < PF; ++sI)
-        if (sI < np) A = __builtin_fmaf(pre[u][sI], s_w[h * np + sI], A);
+      for (int sI = 0; sI < PF; ++sI) {
+        if (sI < np) {
+          const float w = weight(sI);
+          A = __builtin_fmaf(pre[u][sI], w, A);
+          if (own_weights) L = __builtin_fmaf(w, lh[sI], L);
+        }
+      }
       // the rest in chunks of PF whose loads are issued together
       for (int s0 = PF; s0 < np; s0 += PF) {
         float x[PF];
@@ -1291,10 +1319,15 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
         for (int t = 0; t < PF; ++t)
           x[t] = s0 + t < np ? fetch(a.ws_acc + (pbase + (size_t)h * nps + s0 + t) * HD + d) : 0.0f;
 #pragma unroll
-        for (int t = 0; t < PF; ++t)
-          if (s0 + t < np) A = __builtin_fmaf(x[t], s_w[h * np + s0 + t], A);
+        for (int t = 0; t < PF; ++t) {
+          if (s0 + t < np) {
+            const float w = weight(s0 + t);
+            A = __builtin_fmaf(x[t], w, A);
+            if (own_weights) L = __builtin_fmaf(w, lh[s0 + t], L);
+          }
+        }
       }
-      a.out[(size_t)(b * a.Hq + kvh * G + h) * HD + d] = A / s_L[h];
+      a.out[(size_t)(b * a.Hq + kvh * G + h) * HD + d] = A / (own_weights ? L : s_L[h]);
     }
   }
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -84,19 +84,60 @@ __device__ __forceinline__ void wht_row(float v[8], int c) {
       }
     }
   }
+  // the lane with bit M of c set keeps p - v, its partner v + p: both are fma(+-1, v, p),
+  // which rounds the exact sum once, as the add / subtract does
   auto stage = [&](auto mtag) {
     constexpr int M = decltype(mtag)::value;
+    const float sgn = (c & M) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = xor_lane<M>(v[i], c);
-      v[i] = (c & M) ? (p - v[i]) : (v[i] + p);
-    }
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(sgn, v[i], xor_lane<M>(v[i], c));
   };
   if constexpr (LPR > 1) stage(std::integral_constant<int, 1>{});
   if constexpr (LPR > 2) stage(std::integral_constant<int, 2>{});
   if constexpr (LPR > 4) stage(std::integral_constant<int, 4>{});
   if constexpr (LPR > 8) stage(std::integral_constant<int, 8>{});
   if constexpr (LPR > 16) stage(std::integral_constant<int, 16>{});
+}
+
+// The codec's 15 decision thresholds as wave-uniform values, read at the point of the
+// call (a kernel reads them at its start, so that their load is not on the critical path
+// of the coder: the empty asm pins each value to a scalar register there).
+struct Thresholds {
+  float t[15];
+};
+__device__ __forceinline__ Thresholds load_thresholds(const float* thr) {
+  Thresholds r;
+#pragma unroll
+  for (int k = 0; k < 15; ++k) {
+    float x = thr[k];
+    asm volatile("" : "+s"(x));
+    r.t[k] = x;
+  }
+  return r;
+}
+
+// The number of the 15 ascending thresholds strictly below u, by binary search: "t[k] < u"
+// holds for a prefix of k, whose length is found bit by bit (8, 4, 2, 1), each step
+// comparing u with the one threshold that splits what is left.  Equal to counting all
+// 15 comparisons (u = NaN: 0) at about half the instructions.  The selects are bit
+// selects in assembly: as plain selects of array elements the compiler turns them into
+// a per-lane indexed load from a stack copy of the array.
+__device__ __forceinline__ float bit_select(bool b, float x, float y) {   // b ? x : y
+  const int m = b ? -1 : 0;
+  float r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(x), "v"(y));
+  return r;
+}
+__device__ __forceinline__ int count_below15(const Thresholds& th, float u) {
+  const float* t = th.t;
+  const bool b3 = t[7] < u;
+  const bool b2 = bit_select(b3, t[11], t[3]) < u;
+  const float t1a = bit_select(b2, t[13], t[9]), t1b = bit_select(b2, t[5], t[1]);
+  const bool b1 = bit_select(b3, t1a, t1b) < u;
+  const float q3 = bit_select(b1, t[14], t[12]), q2 = bit_select(b1, t[10], t[8]);
+  const float q1 = bit_select(b1, t[6], t[4]), q0 = bit_select(b1, t[2], t[0]);
+  const float t0 = bit_select(b3, bit_select(b2, q3, q2), bit_select(b2, q1, q0));
+  return 8 * b3 + 4 * b2 + 2 * b1 + (t0 < u ? 1 : 0);
 }
 
 // Sum over the LPR lanes of a row, by the same xor pairings as wht_row (so every path
@@ -120,7 +161,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // kernel that codes a row calls this, so all paths write the same codes.  x is
 // overwritten (rotated); w gets the lane's 8 indices (element 8c + i in bits 4i..4i+3).
 template <int LPR>
-__device__ __forceinline__ void codec_encode_row(float x[8], int c, const float* thr,
+__device__ __forceinline__ void codec_encode_row(float x[8], int c, const Thresholds& thr,
                                                  uint32_t& w, float& s) {
   constexpr int D = LPR * 8;
   float ss = 0.0f;
@@ -132,13 +173,7 @@ __device__ __forceinline__ void codec_encode_row(float x[8], int c, const float*
   const float inv = (1.0f / sqrtf((float)D)) / (s == 0.0f ? 1.0f : s);  // u = (H x / sqrt(D)) / s
   w = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float u = x[j] * inv;
-    int idx = 0;
-#pragma unroll
-    for (int k = 0; k < 15; ++k) idx += (thr[k] < u) ? 1 : 0;
-    w |= (uint32_t)idx << (4 * j);
-  }
+  for (int j = 0; j < 8; ++j) w |= (uint32_t)count_below15(thr, x[j] * inv) << (4 * j);
 }
 
 // Sum over aligned groups of LANES (2, 4, 8, 16 or 32) lanes, left in every lane of the
@@ -162,6 +197,26 @@ __device__ __forceinline__ float lane_group_sum(float x) {
     uint32_t p = __builtin_bit_cast(uint32_t, x), q = p;
     asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(p), "+v"(q));
     x = __builtin_bit_cast(float, p) + __builtin_bit_cast(float, q);
+  }
+  return x;
+}
+
+// Maximum over aligned groups of LANES lanes, by the same lane pairings.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float x) {
+  return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                      0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false)));
+}
+template <int LANES>
+__device__ __forceinline__ float lane_group_max(float x) {
+  if (LANES >= 2) x = dpp_max<0xB1>(x);
+  if (LANES >= 4) x = dpp_max<0x4E>(x);
+  if (LANES >= 8) x = dpp_max<0x141>(x);
+  if (LANES >= 16) x = dpp_max<0x140>(x);
+  if (LANES >= 32) {
+    uint32_t p = __builtin_bit_cast(uint32_t, x), q = p;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(p), "+v"(q));
+    x = fmaxf(__builtin_bit_cast(float, p), __builtin_bit_cast(float, q));
   }
   return x;
 }

@@ -158,6 +158,8 @@ def test_library_codebook_matches_oracle():
     c, t, _ = codec.codebook(4)
     assert np.allclose(lv, c, atol=1e-6) and np.allclose(th, t, atol=1e-6)
     assert th[7] == 0.0 and lv[7] == -lv[8]
+    # the kernels code a value by binary search over the thresholds: they must ascend
+    assert np.all(np.diff(th) > 0)
 
 
 @pytest.mark.parametrize("rule", ["int4", "int8"])

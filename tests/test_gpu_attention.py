@@ -348,7 +348,7 @@ def test_append_decode_loop_reuses_workspace():
 @pytest.mark.parametrize("fmt,D", [("int8", 128), ("int8", 64), ("codec", 128), ("int4", 256)])
 def test_other_paths_loop_reuse_workspace(fmt, D):
     """Consecutive append + decode steps through one workspace on the INT8 matrix-core
-    kernel (D = 128) and the split-K kernel (the rest; splits merged in-kernel up to 16,
+    kernel (D = 128) and the split-K kernel (the rest; splits merged in-kernel up to 32,
     by the merge kernel beyond): the split counters are zero after every call and each
     step matches the oracle."""
     B, Hkv, G, P, steps = 2, 2, 2, 300, 6
