@@ -82,7 +82,7 @@ __device__ __forceinline__ RawRow load_raw(const DecodeArgs& a, size_t row, int 
 // and INT8, codebook levels for the codec).  A lane's 8 values share one scale (groups
 // are powers of two of at least 32), which is applied once per dot product instead.
 template <int FMT>
-__device__ __forceinline__ void codes_f32(const uint32_t w[2], const float* lv, float x[8]) {
+__device__ __forceinline__ void codes_f32(const uint32_t w[2], const float2* lv2, float x[8]) {
   if (FMT == KVQ_INT4_G) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = (float)nib_s(w[0], j);
@@ -94,7 +94,11 @@ __device__ __forceinline__ void codes_f32(const uint32_t w[2], const float* lv, 
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = lv[nib_u(w[0], j)];
+    for (int i = 0; i < 4; ++i) {   // one lookup per byte: its two levels (low nibble first)
+      const float2 p = lv2[(w[0] >> (8 * i)) & 255u];
+      x[2 * i] = p.x;
+      x[2 * i + 1] = p.y;
+    }
   }
 }
 
@@ -109,7 +113,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   __shared__ float s_m[NGRP][G];
   __shared__ float s_l[NGRP][G];
   __shared__ float s_acc[NGRP][G][D];
-  __shared__ float lv[16];
+  __shared__ float2 lv2[FMT == KVQ_WHT_LM4 ? 256 : 1];   // codec: the levels of a byte's nibbles
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, grp = tid / LPR, c = tid % LPR;
@@ -127,10 +131,12 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   const int ps = sp < nrs ? min(pt, lo + sp * chunk) : pt;
   const int pe = min(pt, ps + chunk);
 
-  // the rows of the first step are requested before q is loaded and rotated, so the
-  // two latencies overlap; each later step's rows are requested before the previous
-  // step is computed (see the row loop below)
+  // the rows of the first two steps are requested before q is loaded and rotated, so
+  // their latency overlaps it (a split of up to 2 U NGRP rows has all of its rows in
+  // flight at once); each later step's rows are requested one step ahead (see the
+  // row loop below)
   constexpr int U = 4;
+  constexpr int SR = U * NGRP;   // rows per step (all groups)
   const size_t bh = (size_t)b * a.Hkv + kvh;
   auto load_step = [&](int t0, RawRow (&raw)[U]) {
 #pragma unroll
@@ -140,8 +146,9 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     }
   };
   int t0 = ps + grp;
-  RawRow cur[U];
+  RawRow cur[U], nxt[U];
   if (t0 < pe) load_step(t0, cur);
+  if (t0 + SR < pe) load_step(t0 + SR, nxt);
   // the append split: row group 0 codes the new K row and row group 1 the new V row,
   // side by side in wave 0 (fp16 rows requested here, coded once q is ready); group 0
   // then attends the new row (after its cached rows, if the split has any)
@@ -191,7 +198,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   }
 
   if (FMT == KVQ_WHT_LM4) {   // the codebook levels (the barrier comes after the loads above)
-    if (tid < 16) lv[tid] = a.levels[tid];
+    lv2[tid] = make_float2(a.levels[tid & 15], a.levels[tid >> 4]);
     __syncthreads();
   }
 
@@ -216,7 +223,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kc[8];
-      codes_f32<FMT>(raw[u].k, lv, kc);
+      codes_f32<FMT>(raw[u].k, lv2, kc);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.0f;
@@ -241,7 +248,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float vc[8];
-      codes_f32<FMT>(raw[u].v, lv, vc);
+      codes_f32<FMT>(raw[u].v, lv2, vc);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float p = fast_exp2(z[u][h] - m[h]);
@@ -252,9 +259,17 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
       }
     }
   };
+  // the first step (its successor already in flight), then one step per iteration,
+  // each requesting the next step's rows before it computes (a loop that carried both
+  // buffers across iterations would need more registers)
+  if (t0 < pe) {
+    do_step(cur, min(U, (pe - t0 + NGRP - 1) / NGRP));
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    t0 += SR;
+  }
   while (t0 < pe) {
-    const int t1 = t0 + U * NGRP;
-    RawRow nxt[U];
+    const int t1 = t0 + SR;
     if (t1 < pe) load_step(t1, nxt);   // the next step's rows, in flight during this one
     do_step(cur, min(U, (pe - t0 + NGRP - 1) / NGRP));
 #pragma unroll
@@ -544,7 +559,7 @@ int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
   const int32_t target = 1024;       // workgroups: 4 per CU on 256 CUs (all resident)
   const int32_t min_rows = 64;       // positions per split worth a workgroup (short
                                      // contexts need many splits to fill the chip)
-  int32_t n = (target + units - 1) / units;
+  int32_t n = (target + units - 1) / units - extra;
   const int32_t by_span = (span + min_rows - 1) / min_rows;
   if (n > by_span) n = by_span;
   if (n > 1024 - extra) n = 1024 - extra;
