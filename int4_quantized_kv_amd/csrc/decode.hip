@@ -131,8 +131,8 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   const int ps = sp < nrs ? min(pt, lo + sp * chunk) : pt;
   const int pe = min(pt, ps + chunk);
 
-  // the rows of the first two steps are requested before q is loaded and rotated, so
-  // their latency overlaps it (a split of up to 2 U NGRP rows has all of its rows in
+  // the rows of the first two steps are requested before q is rotated, so their
+  // latency overlaps it (a split of up to 2 U NGRP rows has all of its rows in
   // flight at once); each later step's rows are requested one step ahead (see the
   // row loop below)
   constexpr int U = 4;
@@ -145,6 +145,11 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
       raw[u] = load_raw<D, FMT>(a, bh * a.cap + (t % a.cap), c);
     }
   };
+  // q first (it is needed first), then the rows
+  uint4 qraw[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qraw[h] = *reinterpret_cast<const uint4*>(a.q + ((size_t)(b * a.Hq + kvh * G + h) * D + 8 * c));
   int t0 = ps + grp;
   RawRow cur[U], nxt[U];
   if (t0 < pe) load_step(t0, cur);
@@ -164,7 +169,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   float q[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    load8_f16(a.q + ((size_t)(b * a.Hq + kvh * G + h) * D + 8 * c), q[h]);
+    f16x8_unpack(qraw[h], q[h]);
     if (FMT == KVQ_WHT_LM4) {
       wht_row<LPR>(q[h], c);
 #pragma unroll
@@ -297,16 +302,15 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   for (int idx = tid; idx < G * D; idx += 256) {
     const int h = idx / D, d = idx % D;
     float M = NEG_INF;
+#pragma unroll
     for (int gi = 0; gi < NGRP; ++gi) M = fmaxf(M, s_m[gi][h]);
     float A = 0.0f, L = 0.0f;
-    if (M != NEG_INF) {
+    if (M != NEG_INF) {   // (a group that saw no row has max -inf: weight 2^-inf = 0)
+#pragma unroll
       for (int gi = 0; gi < NGRP; ++gi) {
-        const float mg = s_m[gi][h];
-        if (mg != NEG_INF) {
-          const float w = fast_exp2(mg - M);
-          A = __builtin_fmaf(s_acc[gi][h][d], w, A);
-          L = __builtin_fmaf(s_l[gi][h], w, L);
-        }
+        const float w = fast_exp2(s_m[gi][h] - M);
+        A = __builtin_fmaf(s_acc[gi][h][d], w, A);
+        L = __builtin_fmaf(s_l[gi][h], w, L);
       }
     }
     const size_t o = (size_t)(b * a.Hq + kvh * G + h) * a.nsplit + sp;
