@@ -15,6 +15,8 @@
 #ifndef KVQ_ARITH_H
 #define KVQ_ARITH_H
 
+#include <stdint.h>
+
 #if defined(__HIPCC__)
 #include <hip/hip_runtime.h>
 #define KVQ_HD __host__ __device__ inline __attribute__((always_inline))
@@ -42,6 +44,20 @@ KVQ_HD float kvq_int4_scale(float amax) {
 KVQ_HD float kvq_int8_scale(float amax) {
   float s = kvq_div_exact(amax, 127.0f, 1.0f / 127.0f);
   return s < 1e-8f ? 1e-8f : s;
+}
+
+// rint(q) (half to even) as the low bits of a word, for |q| <= 128: the fp32 sum
+// q + 1.5 * 2^23 lies in [2^23, 2^24), where the spacing is 1, so the addition rounds q
+// to an integer (to nearest, ties to even) and leaves 0x400000 + rint(q) in the
+// mantissa; 0x400000 is a multiple of 256, so the low 4 (8) bits are the two's
+// complement nibble (byte) of rint(q).  One add in place of round, convert and mask.
+KVQ_HD uint32_t kvq_round_bits(float q) {
+  union {
+    float f;
+    uint32_t u;
+  } v;
+  v.f = q + 12582912.0f;
+  return v.u;
 }
 
 #endif  // KVQ_ARITH_H

@@ -172,3 +172,4 @@ def test_quantizer_arithmetic_exhaustive_on_host(tmp_path, rule):
     r = subprocess.run([str(exe), rule], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout
     assert "quotient_mismatches=0" in r.stdout and "scale_mismatches=0" in r.stdout
+    assert "code_mismatches=0" in r.stdout
