@@ -1255,79 +1255,67 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       }
     }
   }
-  float* s_w = reinterpret_cast<float*>(smem);          // [G][np] split maxima (then weights)
-  float* s_ls = s_w + G * np;                           // [G][np] split sums
-  float* s_L = s_ls + G * np;                           // [G]
+  const int sws = np > PF ? (np + 3) & ~3 : PF;         // weight row stride (>= PF)
+  static_assert((3 * G * MAX_SPLITS + G) * sizeof(float) <= sizeof(smem),
+                "the merge stages up to MAX_SPLITS partials per head in the tile rings");
+  float* s_mx = reinterpret_cast<float*>(smem);          // [G][np] split maxima
+  float* s_ls = s_mx + G * np;                           // [G][np] split sums
+  float* s_w = s_ls + G * np;                           // [G][sws] weights (0 past np)
+  float* s_L = s_w + G * sws;                           // [G]
   for (int idx = threadIdx.x; idx < G * np; idx += NT) {
     const int h = idx / np, sI = idx % np;
     const uint64_t ml = fetch_pair(a.ws_ml + 2 * (pbase + (size_t)h * nps + sI));
-    s_w[idx] = __builtin_bit_cast(float, (uint32_t)ml);
+    s_mx[idx] = __builtin_bit_cast(float, (uint32_t)ml);
     s_ls[idx] = __builtin_bit_cast(float, (uint32_t)(ml >> 32));
   }
   __syncthreads();
-  // weights 2^(m_s - M) and the weighted sum of the partial sums: up to 32 splits every
-  // thread computes them for its outputs from broadcast LDS reads (no second barrier);
-  // above, one wave per head does, into s_w and s_L
-  const bool own_weights = np <= 32;   // uniform
-  if (!own_weights) {
-    for (int h = wave; h < G; h += WAVES) {
-      float M = NEG_INF;
-      for (int sI = lane; sI < np; sI += 64) M = fmaxf(M, s_w[h * np + sI]);
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
-      float Ls = 0.0f;
-      for (int sI = lane; sI < np; sI += 64) {
-        const float ms = s_w[h * np + sI];
-        const float wgt = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
-        s_w[h * np + sI] = wgt;
-        Ls = __builtin_fmaf(wgt, s_ls[h * np + sI], Ls);
+  // one wave per head: maximum and weighted sum of the split sums by DPP reductions
+  // (splits strided over the lanes), weights 2^(m_s - M) into s_w
+  for (int h = wave; h < G; h += WAVES) {
+    float mx = NEG_INF;
+    for (int sI = lane; sI < np; sI += 64) mx = fmaxf(mx, s_mx[h * np + sI]);
+    mx = lane_group_max<32>(mx);
+    const float M = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 0)),
+                          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 32)));
+    float ls = 0.0f;
+    for (int sI = lane; sI < sws; sI += 64) {
+      float wgt = 0.0f;
+      if (sI < np) {
+        const float ms = s_mx[h * np + sI];
+        wgt = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
+        ls = __builtin_fmaf(wgt, s_ls[h * np + sI], ls);
       }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) Ls += __shfl_xor(Ls, m);
-      if (lane == 0) s_L[h] = Ls;
+      s_w[h * sws + sI] = wgt;
     }
-    __syncthreads();
+    ls = lane_group_sum<32>(ls);
+    // (read by every lane: inside the lane-0 branch the compiler computed the half
+    // sums in lane 0 alone, and lane 32 was read before its own sum)
+    const float L = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 0)) +
+                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 32));
+    if (lane == 0) s_L[h] = L;
   }
+  __syncthreads();
+  // every output: the weighted sum of its partials (the first PF branch-free: weights
+  // past np are 0; the rest, for plans above PF splits, in chunks of PF loads)
 #pragma unroll
   for (int u = 0; u < OPT; ++u) {
     const int idx = threadIdx.x + NT * u;
     if (idx < G * HD) {
       const int h = idx / HD, d = idx % HD;
-      const float* mh = s_w + h * np;
-      const float* lh = s_ls + h * np;
-      float M = NEG_INF;
-      if (own_weights) {
-#pragma unroll 4
-        for (int sI = 0; sI < np; ++sI) M = fmaxf(M, mh[sI]);
-      }
-      auto weight = [&](int sI) {
-        return own_weights ? (mh[sI] != NEG_INF ? fast_exp2(mh[sI] - M) : 0.0f) : mh[sI];
-      };
-      float A = 0.0f, L = 0.0f;
+      const float* wh = s_w + h * sws;
+      float A = 0.0f;
 #pragma unroll
-      for (int sI = 0; sI < PF; ++sI) {
-        if (sI < np) {
-          const float w = weight(sI);
-          A = __builtin_fmaf(pre[u][sI], w, A);
-          if (own_weights) L = __builtin_fmaf(w, lh[sI], L);
-        }
-      }
-      // the rest in chunks of PF whose loads are issued together
+      for (int sI = 0; sI < PF; ++sI) A = __builtin_fmaf(pre[u][sI], wh[sI], A);
       for (int s0 = PF; s0 < np; s0 += PF) {
         float x[PF];
 #pragma unroll
         for (int t = 0; t < PF; ++t)
           x[t] = s0 + t < np ? fetch(a.ws_acc + (pbase + (size_t)h * nps + s0 + t) * HD + d) : 0.0f;
 #pragma unroll
-        for (int t = 0; t < PF; ++t) {
-          if (s0 + t < np) {
-            const float w = weight(s0 + t);
-            A = __builtin_fmaf(x[t], w, A);
-            if (own_weights) L = __builtin_fmaf(w, lh[s0 + t], L);
-          }
-        }
+        for (int t = 0; t < PF; ++t)
+          if (s0 + t < np) A = __builtin_fmaf(x[t], wh[s0 + t], A);
       }
-      a.out[(size_t)(b * a.Hq + kvh * G + h) * HD + d] = A / (own_weights ? L : s_L[h]);
+      a.out[(size_t)(b * a.Hq + kvh * G + h) * HD + d] = A / s_L[h];
     }
   }
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
