@@ -59,6 +59,7 @@ CASES = [
     (2, 2, 4, 128, [700, 700], 100, 0),
     (1, 2, 2, 128, [1000], 999, 5),
     (2, 2, 4, 128, [50, 1000], 0, 64),     # more splits than positions of sequence 0
+    (1, 2, 4, 128, [4000], 0, 130),        # more splits than lanes in the in-kernel merge
     (4, 1, 1, 64, [5, 17, 33, 65], 16, 0),
 ]
 
