@@ -900,6 +900,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) NewLds s_new;
   __shared__ int s_last;
   __shared__ uint32_t s_claim;
+  __shared__ __attribute__((aligned(16))) float s_mlc[2 * WAVES * G];   // combine max / sum
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -1118,21 +1119,22 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   wait_vmcnt<0>();   // (also the q staging, when this wave had no tile)
 
   // ---- combine the waves' column sets (and, in the appending workgroup, the new row)
-  // through LDS, reusing the ring: lane (r, j) holds O[column r][8(4j + i) + e] in
-  // oacc[e][i]; a head sits in column head * NGK of each set, and each set has its own
-  // running maximum, so it enters the combine as an entry of its own
-  // s_o rows of 132 words (a pad word after every 32 dims): one write instruction stores
-  // dims 32j + const of up to 8 (entry, head) rows, which then fall in 32 distinct banks
-  // (unpadded they all share one bank)
-  constexpr int NE = WAVES * S;                                 // combine entries
+  // through LDS: lane (r, j) holds O[column r][8(4j + i) + e] in oacc[e][i]; a head sits
+  // in column head * NGK of each set, and each set has its own running maximum.  A wave
+  // first merges its two sets (S = 2: lanes r and r ^ 8 hold the same head and dims for
+  // the two halves of every tile), so it enters the combine as one entry, and writes that
+  // entry into its own ring as soon as its loop ends (no other wave transfers into that
+  // ring or reads it): only the last wave's writes come after the workgroup barrier.
+  // Entry rows of 132 words (a pad word after every 32 dims): one write instruction
+  // stores dims 32j + const of up to 8 (entry, head) rows, which then fall in 32 distinct
+  // banks (unpadded they all share one bank)
+  constexpr int NE = WAVES;                                     // combine entries
   constexpr int ORS = HD + HD / 32;                             // padded row stride
   auto opad = [](int d) { return d + (d >> 5); };
-  static_assert((NE * G * ORS + 2 * NE * G) * sizeof(float) <= sizeof(smem),
-                "the combine reuses the tile rings");
-  __syncthreads();
-  float* s_o = reinterpret_cast<float*>(smem);                 // [NE][G][ORS]
-  float* s_m = s_o + NE * G * ORS;                              // [G][NE]
-  float* s_l = s_m + NE * G;                                    // [G][NE]
+  static_assert(G * ORS * sizeof(float) <= NB * L::BYTES, "a wave's entry fits its ring");
+  float* s_o = reinterpret_cast<float*>(ring);                 // this wave's [G][ORS]
+  float* s_m = s_mlc;                                           // [G][NE]
+  float* s_l = s_mlc + NE * G;                                  // [G][NE]
   if constexpr (!I8) {
 #pragma unroll
     for (int e = 1; e < 8; e += 2) st.oacc[e] *= 0.0625f;   // see v_pair_f16
@@ -1154,17 +1156,32 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       st.oacc[e] = (floatx4){x0, x1, x2, x3};
     }
   }
-  const float l_run = sum_over_j(st.l);
-  if (rr < G * NGK && qgrp == 0) {
-    const int ent = wave * S + cset;
+  float l_run = sum_over_j(st.l);
+  if constexpr (S == 2) {   // the partner set from lane r ^ 8 (DPP rotation by 8 in the row)
+    const auto partner = [](float x) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                   0x128, 0xF, 0xF, false));
+    };
+    const float mo = partner(st.m), lo_run = partner(l_run);
+    const float mx = fmaxf(st.m, mo);
+    const float f0 = fast_exp2((st.m - mx) * a.qscale), f1 = fast_exp2((mo - mx) * a.qscale);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        s_o[(ent * G + qhead) * ORS + opad(8 * (4 * j + i) + e)] = st.oacc[e][i];
+        st.oacc[e][i] = __builtin_fmaf(st.oacc[e][i], f0, partner(st.oacc[e][i]) * f1);
+    l_run = __builtin_fmaf(l_run, f0, lo_run * f1);
+    st.m = mx;
+  }
+  if (rr < G * NGK && qgrp == 0 && cset == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s_o[qhead * ORS + opad(8 * (4 * j + i) + e)] = st.oacc[e][i];
     if (j == 0) {
-      s_m[qhead * NE + ent] = st.m * a.qscale;   // base-2 units
-      s_l[qhead * NE + ent] = l_run;
+      s_m[qhead * NE + wave] = st.m * a.qscale;   // base-2 units
+      s_l[qhead * NE + wave] = l_run;
     }
   }
   __syncthreads();
@@ -1187,7 +1204,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int w = 0; w < NE; ++w) ow[w] = s_o[(w * G + h) * ORS + opad(d)];
+    for (int w = 0; w < NE; ++w)   // entry w: wave w's, in that wave's ring
+      ow[w] = reinterpret_cast<const float*>(smem + w * NB * L::BYTES)[h * ORS + opad(d)];
     const float mn = appender ? s_new.m[h] : NEG_INF;
     const float on = appender ? s_new.o[d] : 0.0f;
     float M = mn;
