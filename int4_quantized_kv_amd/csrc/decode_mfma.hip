@@ -198,6 +198,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier over LDS data: waits for this wave's LDS operations only.
+// __syncthreads()'s fence also waits for every outstanding global load (vmcnt 0), here
+// the transfers of the first tiles, which held the loop start back by ~1.5 us.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Per-lane byte offsets of the transfers, fixed for the whole kernel: lane l fills LDS
 // row position P = l / 4, chunk slot l % 4 with chunk (l % 4) ^ f(P) of tile row
 // rowperm(P) (+16 for the second half); scale transfers take row l % 32.
@@ -901,11 +908,30 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   __shared__ int s_last;
   __shared__ uint32_t s_claim;
   __shared__ __attribute__((aligned(16))) float s_mlc[2 * WAVES * G];   // combine max / sum
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[G * 2 * HD];      // the G query rows
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   // wave-uniform: keeps tile positions, ring addresses and base pointers in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // fp16 inputs, copied into LDS by wave 0's first transfers, ahead of every tile and
+  // of the kernel arguments the tile schedule needs: the G query rows, one copy shared
+  // by the workgroup, and in the appending workgroup the new K/V rows into s_new.
+  // (Loading them into registers inside the loop would make the compiler wait for them
+  // wherever it reuses those registers; a load before the loop would make it wait ahead
+  // of every transfer.)
+  uint8_t* qstage = s_q;
+  if (wave == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      dma4(a.q + ((size_t)b * a.Hq + kvh * G + h) * HD + 2 * lane, qstage + h * 2 * HD);
+    if (!I8 && sp == 0 && a.k_new != nullptr) {
+      const size_t u = (size_t)b * a.Hkv + kvh;
+      dma4(a.k_new + u * HD + 2 * lane, reinterpret_cast<uint8_t*>(s_new.k));
+      dma4(a.v_new + u * HD + 2 * lane, reinterpret_cast<uint8_t*>(s_new.v));
+    }
+  }
   const int r = lane & 15, j = lane >> 4;
   // q.K column r = (set r / 8 when S = 2, head, group) with head = rr / NGK and
   // group = rr % NGK for rr = r % (16 / S); junk columns beyond G * NGK
@@ -944,22 +970,9 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     if constexpr (I8) issue_tile8(a, row0, t0, pe, lb, dof);
     else issue_tile<NGK>(a, row0, t0, pe, lb, lane, dof);
   };
-  if (threadIdx.x == 0) s_claim = 0;   // ordered before the first claim by a barrier
+  if (threadIdx.x == 0) s_claim = 0;   // ordered before the first claim by the q barrier
 
-  // fp16 inputs, copied into LDS by transfers before the first tile: the G query rows
-  // into ring slot 2 (free until step 0 starts tile 2 there, after reading them) and,
-  // in the appending wave, the new K/V rows into s_new.  (Loading them into registers
-  // inside the loop would make the compiler wait for them wherever it reuses those
-  // registers; a load before the loop would make it wait ahead of every transfer.)
   const bool app_wave = appender && wave == 0;
-  uint8_t* qstage = ring + 2 * L::BYTES;
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    dma4(a.q + ((size_t)b * a.Hq + kvh * G + h) * HD + 2 * lane, qstage + h * 2 * HD);
-  if (app_wave) {
-    dma4(a.k_new + (size_t)unit * HD + 2 * lane, reinterpret_cast<uint8_t*>(s_new.k));
-    dma4(a.v_new + (size_t)unit * HD + 2 * lane, reinterpret_cast<uint8_t*>(s_new.v));
-  }
 
   const auto lo = [&] {
   if constexpr (I8) {
@@ -1006,13 +1019,17 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   if (cur != NONE) issue(ps + TL * cur, ring);
   if (nxt != NONE) issue(ps + TL * nxt, ring + L::BYTES);
 
+  // wave 0 waits for its q (and new-row) transfers alone, which are older than its
+  // tiles'; the barrier then publishes them (and the zeroed claim counter) to every wave
+  if (wave == 0) {
+    if (nxt != NONE) wait_vmcnt<2 * DMA>();
+    else if (cur != NONE) wait_vmcnt<DMA>();
+    else wait_vmcnt<0>();
+  }
+  lds_barrier();
   // q into MFMA layout (and the appending wave's quantization of the new row) while
-  // tiles 0 and 1 are in flight
-  // (asm reads after a wait for the q transfers alone, which are older than the tiles';
-  // plain reads would make the compiler wait for the first tiles as well)
-  if (nxt != NONE) wait_vmcnt<2 * DMA>();
-  else if (cur != NONE) wait_vmcnt<DMA>();
-  else wait_vmcnt<0>();
+  // tiles 0 and 1 are in flight (asm reads: plain reads would make the compiler wait
+  // for the first tiles as well)
   // the chunk of q feeding MFMA c: S = 1: chunk j (all c); S = 2: chunk j % 2 + 2 (c / 4)
   u32x4 qraw[4 * S];
   {
@@ -1067,7 +1084,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       const uint32_t hi16 = (w[2 + (p >> 1)] >> (16 * (p & 1))) & 0xFFFFu;
       o.u[p] = live ? (lo16 | (hi16 << 16)) : 0u;
       f16x2 h2 = __builtin_bit_cast(f16x2, o.u[p]);
-      qs += (float)h2.x + (float)h2.y;
+      const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+      qs = __builtin_amdgcn_fdot2(h2, one2, qs, false);   // qs += h2.x + h2.y (one dot2)
       if (p & 1) {   // slots of nibbles taken at bits 4..7 (16 times larger): q / 16
         const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
         h2 = h2 * sixteenth;
@@ -1091,7 +1109,6 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  __syncthreads();   // s_claim is zero
   for (int k = 0; cur != NONE; ++k) {
     int nn = NONE;
     if (nxt != NONE) {
