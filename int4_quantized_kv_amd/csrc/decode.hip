@@ -103,7 +103,10 @@ __device__ __forceinline__ void codes_f32(const uint32_t w[2], const float2* lv2
 }
 
 // Up to this many splits, the last split of a (sequence, KV head) merges the partials
-// inside the split-K kernel; above, the merge kernel does.
+// inside the split-K kernel; above, the merge kernel does.  (64 measured slower on the
+// Gemma step's 64-split layers: every split then waits for its stores' acknowledgement
+// and for an arrival counter that 64 workgroups update one after another, where
+// otherwise they store and exit.)
 constexpr int MERGE_INLINE_MAX = 32;
 
 template <int D, int G, int FMT>
@@ -343,16 +346,16 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   const int np = a.nsplit;
   if (s_last != np - 1) return;
   const size_t pbase = (size_t)(b * a.Hq + kvh * G) * np;   // partial of (head 0, split 0)
-  static_assert(MERGE_INLINE_MAX == 32, "one split per lane of a 32-lane half wave");
-  float* s_w = &s_acc[0][0][0];       // [G][32] split weights (0 past np)
-  float* s_L = s_w + G * 32;          // [G] weighted sums of the split sums
+  static_assert(MERGE_INLINE_MAX <= 64, "one split per lane");
+  float* s_w = &s_acc[0][0][0];       // [G][64] split weights (0 past np)
+  float* s_L = s_w + G * 64;          // [G] weighted sums of the split sums
   float* s_out = s_L + G;             // [G][D] merged output (codec: before the rotation)
   const int wave = tid >> 6, lane = tid & 63;
-  // every thread first requests its outputs' partials (up to 64 loads), and wave w the
-  // (max, sum) pairs of heads w, w + 4, ... (split = lane), so that all are one round
-  // trip; the partial loads go in groups of 8 under a uniform test, the split index
-  // clamped to np - 1 inside a group (their weight is 0) and the output index to the
-  // last output
+  // every thread first requests its outputs' first partials (up to 64 loads), and wave
+  // w the (max, sum) pairs of heads w, w + 4, ... (split = lane), so that up to PF
+  // splits are one round trip; the partial loads go in groups of 8 under a uniform test,
+  // the split index clamped to np - 1 inside a group (their weight is 0) and the output
+  // index to the last output
   constexpr int OPT = (G * D + 255) / 256;                 // outputs per thread
   constexpr int PF = OPT <= 2 ? 32 : 64 / OPT;             // partials prefetched per output
   float pre[OPT][PF];
@@ -384,15 +387,18 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
       lt[k] = __builtin_bit_cast(float, (uint32_t)(ml >> 32));
     }
   }
-  // weights 2^(m_s - M) by DPP reductions over the 32 lanes of the first half wave
+  // weights 2^(m_s - M) by DPP reductions over each half wave and a read of lanes 0
+  // and 32 (by every lane: the half sums must be formed in both lanes)
 #pragma unroll
   for (int k = 0; k < HPW; ++k) {
     const int h = wave + 4 * k;
     if (h < G) {   // wave-uniform
-      const float M = lane_group_max<32>(mt[k]);
+      const float mh = lane_group_max<32>(mt[k]);
+      const float M = fmaxf(readlane_f(mh, 0), readlane_f(mh, 32));
       const float w = mt[k] != NEG_INF ? fast_exp2(mt[k] - M) : 0.0f;
-      const float L = lane_group_sum<32>(w * lt[k]);
-      if (lane < 32) s_w[h * 32 + lane] = w;
+      const float lh = lane_group_sum<32>(w * lt[k]);
+      const float L = readlane_f(lh, 0) + readlane_f(lh, 32);
+      s_w[h * 64 + lane] = w;
       if (lane == 0) s_L[h] = L;
     }
   }
@@ -402,7 +408,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     const int idx = tid + 256 * u;
     if (idx < G * D) {
       const int h = idx / D, d = idx % D;
-      const float* wh = s_w + h * 32;
+      const float* wh = s_w + h * 64;
       float A = 0.0f;
 #pragma unroll
       for (int t = 0; t < PF; ++t) A = __builtin_fmaf(pre[u][t], wh[t], A);
@@ -453,65 +459,84 @@ __device__ __forceinline__ float block_reduce(float v, float* tmp) {
   return r;
 }
 
-// One workgroup of D threads per (query head, batch): the split maxima and sums are
-// staged in LDS, then thread d accumulates dim d over the splits.
+// One workgroup of D threads per (query head, batch).  Thread d first requests dim d of
+// the first PFM partials (one round trip; groups of 8 under a uniform test with the
+// split index clamped, as in the in-kernel merge), then the (max, sum) pairs, staged in
+// LDS; the weights 2^(m_s - M) follow from two block reductions, and thread d sums its
+// prefetched partials (weights past ns are 0).  The codec's inverse rotation is one
+// row transform by the first D/8 lanes.
 template <int D, bool CODEC>
 __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
-  __shared__ float s_w[MAX_SPLITS];
+  constexpr int PFM = 64;
+  __shared__ float s_w[MAX_SPLITS > PFM ? MAX_SPLITS : PFM];
+  __shared__ float s_l[MAX_SPLITS];
   __shared__ float s_tmp[4];
   __shared__ float sh[D];
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int ns = a.nsplit;
   const size_t base = (size_t)(b * a.Hq + h) * ns;
+  const float* acc = a.ws_acc + base * D + d;
+  float pre[PFM];
+#pragma unroll
+  for (int t8 = 0; t8 < PFM; t8 += 8) {
+    if (t8 < ns) {
+#pragma unroll
+      for (int t = t8; t < t8 + 8; ++t) pre[t] = acc[(size_t)min(t, ns - 1) * D];
+    } else {
+#pragma unroll
+      for (int t = t8; t < t8 + 8; ++t) pre[t] = 0.0f;
+    }
+  }
   float M = NEG_INF;
   for (int s = d; s < ns; s += D) {
-    const float ms = a.ws_ml[2 * (base + s)];
-    s_w[s] = ms;
-    M = fmaxf(M, ms);
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + 2 * (base + s));
+    s_w[s] = ml.x;
+    s_l[s] = ml.y;
+    M = fmaxf(M, ml.x);
   }
   M = block_reduce<true>(M, s_tmp);
   float L = 0.0f;
-  for (int s = d; s < ns; s += D) {
-    const float ms = s_w[s];
-    const float w = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
+  for (int s = d; s < max(ns, PFM); s += D) {
+    float w = 0.0f;
+    if (s < ns) {
+      const float ms = s_w[s];
+      w = ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
+      L = __builtin_fmaf(w, s_l[s], L);
+    }
     s_w[s] = w;
-    L = __builtin_fmaf(w, a.ws_ml[2 * (base + s) + 1], L);
   }
   L = block_reduce<false>(L, s_tmp);   // its barrier also publishes s_w
-  // 16 partials per step, their loads issued together (the merge is latency-bound)
-  const float* acc = a.ws_acc + base * D + d;
-  constexpr int MU = 16;
-  float A[MU];
+  float A = 0.0f;
 #pragma unroll
-  for (int u = 0; u < MU; ++u) A[u] = 0.0f;
-  int s = 0;
-  for (; s + MU <= ns; s += MU) {
+  for (int t = 0; t < PFM; ++t) A = __builtin_fmaf(pre[t], s_w[t], A);
+  // more than PFM splits: 16 partials per step, their loads issued together
+  constexpr int MU = 16;
+  for (int s0 = PFM; s0 < ns; s0 += MU) {
     float x[MU];
 #pragma unroll
-    for (int u = 0; u < MU; ++u) x[u] = acc[(size_t)(s + u) * D];
+    for (int u = 0; u < MU; ++u) x[u] = s0 + u < ns ? acc[(size_t)(s0 + u) * D] : 0.0f;
 #pragma unroll
-    for (int u = 0; u < MU; ++u) A[u] = __builtin_fmaf(x[u], s_w[s + u], A[u]);
+    for (int u = 0; u < MU; ++u)
+      if (s0 + u < ns) A = __builtin_fmaf(x[u], s_w[s0 + u], A);
   }
-  for (; s < ns; ++s) A[0] = __builtin_fmaf(acc[(size_t)s * D], s_w[s], A[0]);
-#pragma unroll
-  for (int w = MU / 2; w >= 1; w >>= 1)
-#pragma unroll
-    for (int u = 0; u < w; ++u) A[u] += A[u + w];
-  float o = A[0] / L;
-  if (CODEC) {
+  const float o = A / L;
+  float* out = a.out + (size_t)(b * a.Hq + h) * D;
+  if (CODEC) {   // back from the rotated domain: H o / sqrt(D), lane c holding dims 8c .. 8c + 7
+    constexpr int LPR = D / 8;
     sh[d] = o;
     __syncthreads();
-    for (int hh = 1; hh < D; hh <<= 1) {
-      const float mine = sh[d], other = sh[d ^ hh];
-      __syncthreads();
-      sh[d] = (d & hh) ? other - mine : mine + other;
-      __syncthreads();
+    if (d < LPR) {   // (LPR <= 32 consecutive lanes of the first wave, all active)
+      float v[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) v[jj] = sh[8 * d + jj];
+      wht_row<LPR>(v, d);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) out[8 * d + jj] = v[jj] * (1.0f / sqrtf((float)D));
     }
-    o = sh[d] * (1.0f / sqrtf((float)D));
+  } else {
+    out[d] = o;
   }
-  a.out[(size_t)(b * a.Hq + h) * D + d] = o;
 }
-
 
 template <int D, int FMT>
 hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {

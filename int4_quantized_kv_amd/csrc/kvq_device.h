@@ -201,6 +201,11 @@ __device__ __forceinline__ float lane_group_sum(float x) {
   return x;
 }
 
+// The value of lane L (a constant) in every lane.
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
 // Maximum over aligned groups of LANES lanes, by the same lane pairings.
 template <int CTRL>
 __device__ __forceinline__ float dpp_max(float x) {

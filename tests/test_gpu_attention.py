@@ -352,7 +352,7 @@ def test_other_paths_loop_reuse_workspace(fmt, D):
     kernel (D = 128) and the split-K kernel (the rest; splits merged in-kernel up to 32,
     by the merge kernel beyond): the split counters are zero after every call and each
     step matches the oracle."""
-    B, Hkv, G, P, steps = 2, 2, 2, 300, 6
+    B, Hkv, G, P, steps = 2, 2, 2, 300, 7
     L = P + steps
     k = synth.kv_source((B, Hkv, L, D), 41, DEV, outlier_channels=2)
     v = synth.kv_source((B, Hkv, L, D), 42, DEV, outlier_channels=2)
@@ -360,7 +360,7 @@ def test_other_paths_loop_reuse_workspace(fmt, D):
     desc = kvq.make_desc(fmt, B, Hkv, D, L, min(64, D), min(128, D))
     dc = kvq.DeviceCache(desc, DEV)
     kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, :P].contiguous(), v[:, :, :P].contiguous(), 0, P)
-    ws = kvq.decode_workspace(desc, Hkv * G, L, 0, 40, DEV)
+    ws = kvq.decode_workspace(desc, Hkv * G, L, 0, 70, DEV)
     if fmt == "codec":
         kidx, ksc, _ = codec.encode(np16(k))
         vidx, vsc, _ = codec.encode(np16(v))
@@ -370,7 +370,7 @@ def test_other_paths_loop_reuse_workspace(fmt, D):
     for t in range(steps):
         pos = P + t
         q = qs[t].contiguous()
-        ns = (0, 1, 7, 16, 17, 40)[t]
+        ns = (0, 1, 7, 16, 17, 40, 70)[t]
         out = append_decode(desc, dc, k[:, :, pos].contiguous(), v[:, :, pos].contiguous(), q,
                             Hkv * G, [pos + 1, pos + 1], 0, 0.0, ns, ws=ws)
         ref = attention.decode_attention(np16(q), kh, vh, [pos + 1, pos + 1])
