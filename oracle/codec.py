@@ -10,7 +10,7 @@ Page cited
            the codec is approximate, with a per-row cosine of about 0.9954 at 4 bits.
 
 The page names the two steps and nothing else.  The plainest algorithm that its
-statement supports, used here (every choice is listed in the design doc):
+statement supports, used here:
   1. rotate:   y = H_d x / sqrt(d), H_d the Sylvester-ordered +-1 Hadamard matrix
                (H_ij = (-1)^popcount(i & j)); orthonormal, no random sign flips;
   2. scale:    s = ||x||_2 / sqrt(d) (the RMS of the row; the codebook is for a

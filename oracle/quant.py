@@ -10,7 +10,7 @@ Pages cited
   [KV-opt]   "AI 推理性能调优：KV Cache 优化与显存管理的工程实践"
              (bxzpzcl.cn/news/2871434), section 3.1 (``KVCacheQuantizer.quantize_int8``).
 
-Readings taken where the text is silent or garbled (each is listed in the design doc):
+Readings taken where the text is silent or garbled:
   * Groups are ``g`` contiguous elements of the last axis (head_dim): the page
     reshapes "the last dim" into groups of ``group_size``.
   * The extraction dropped ``=`` and ``==``: ``scale = torch.where(scale == 0, 1, scale)``.
