@@ -1,0 +1,87 @@
+"""HIP-graph replay of a decode step.
+
+A captured ``kvq_append_decode_attn`` call replays to the eager result, replay after
+replay, with eager library work and synchronizations in between, and leaves the split
+arrival counters at zero each time.  Paths: the INT4 matrix-core kernel (in-kernel
+merge, append fused in the prologue), the codec's split-K kernel with the in-kernel
+merge, and the codec's split-K kernel followed by the merge kernel.  The eager result
+is itself checked against the oracle ("长上下文内存大瘦身" engine three for the codec;
+lpnh.cn/news/2042373 section 2.1 and the plain softmax definition for INT4).
+"""
+import numpy as np
+import pytest
+import torch
+
+import int4_quantized_kv_amd as kvq
+import synth
+from oracle import attention, codec, quant
+from tests.kvq_testutil import assert_attn_close, np16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+CASES = [
+    # fmt, head_dim, q heads per kv head, num_splits (0: planned)
+    ("int4", 128, 4, 0),     # matrix-core kernel, 4 splits merged in-kernel
+    ("codec", 256, 2, 0),    # split-K, in-kernel merge (append in a split of its own)
+    ("codec", 256, 2, 40),   # split-K + merge kernel
+]
+
+
+@pytest.mark.parametrize("fmt,D,G,ns", CASES, ids=[f"{c[0]}-{c[1]}-ns{c[3]}" for c in CASES])
+def test_graph_replay_matches_eager(fmt, D, G, ns):
+    B, Hkv, P = 2, 2, 700
+    L = P + 1
+    Hq = Hkv * G
+    k = synth.kv_source((B, Hkv, L, D), 61, DEV, outlier_channels=2)
+    v = synth.kv_source((B, Hkv, L, D), 62, DEV, outlier_channels=2)
+    q = synth.query((B, Hq, D), 63, DEV)
+    q2 = synth.query((B, Hq, D), 64, DEV)
+    desc = kvq.make_desc(fmt, B, Hkv, D, L, min(64, D), min(128, D))
+    dc = kvq.DeviceCache(desc, DEV)
+    kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, :P].contiguous(), v[:, :, :P].contiguous(), 0, P)
+    kn, vn = k[:, :, P].contiguous(), v[:, :, P].contiguous()
+    ws = kvq.decode_workspace(desc, Hq, L, 0, ns, DEV)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    other = torch.empty_like(out)
+    lens = [L, L]
+
+    def step():
+        kvq.kvq_append_decode_attn(desc, dc.c, kn, vn, q, Hq, lens, 0, 0.0, ns, out, ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    if fmt == "codec":   # a code that flips at a threshold moves one value by a level gap
+        kidx, ksc, _ = codec.encode(np16(k))
+        vidx, vsc, _ = codec.encode(np16(v))
+        ref = attention.decode_attention(np16(q), codec.decode(kidx, ksc), codec.decode(vidx, vsc), lens)
+        rel = np.linalg.norm(eager.cpu().numpy() - ref) / np.linalg.norm(ref)
+        assert rel < 1e-3, rel
+    else:
+        qk, sk = quant.quantize_int4(np16(k), 64)
+        qv, sv = quant.quantize_int4(np16(v), 128)
+        ref = attention.decode_attention(np16(q), quant.dequantize_int4_exact(qk, sk, 64),
+                                         quant.dequantize_int4_exact(qv, sv, 128), lens)
+        assert_attn_close(eager.cpu().numpy(), ref, f"{fmt} eager")
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    counters = ws[: B * Hkv].view(torch.int32)
+    for r in range(4):
+        out.fill_(float("nan"))   # the replay must write every output
+        g.replay()
+        torch.cuda.synchronize()
+        # (tiles and rows are shared out dynamically: the fp32 sums may differ from the
+        # eager call in their last bits)
+        assert torch.allclose(out, eager, rtol=1e-4, atol=1e-5), f"replay {r}"
+        assert int(counters.abs().sum()) == 0, f"split counters after replay {r}"
+        # eager work between replays, through the same workspace
+        kvq.kvq_decode_attn(desc, dc.c, q2, Hq, lens, 0, 0.0, ns, other, ws)
+        torch.cuda.synchronize()
+        assert int(counters.abs().sum()) == 0, f"split counters after eager call {r}"
+        assert torch.isfinite(other).all()
