@@ -782,9 +782,10 @@ __device__ __forceinline__ uint64_t fetch_pair(const float* p) {
 
 // The new token's row when the append is fused into the attention.  Wave 0 of the
 // first workgroup of each (sequence, KV head) copies the fp16 K and V rows into LDS at
-// the start (the G query rows are staged by every wave anyway), quantizes them with
-// the arithmetic of the append kernel while its first tiles are in flight (lanes 0..15:
-// K dims 8c .. 8c+7, c = lane; lanes 16..31: V), and keeps the result in LDS: the row
+// the start (with the workgroup's one copy of the G query rows), quantizes them to the
+// append kernel's codes (the same scale and fp32 quotient, rounded half to even) while
+// its first tiles are in flight (lanes 0..15: K dims 8c .. 8c+7, c = lane; lanes
+// 16..31: V), and keeps the result in LDS: the row
 // enters this step's softmax as one more entry of the workgroup's combine (no tile
 // reads it back from memory), and its codes and scales are written to the cache at the
 // end.
