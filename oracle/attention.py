@@ -14,23 +14,33 @@ Pages cited
             section 5 step 5: the operator reads INT4 data and dequantizes inside.
 
 Readings: the window is inclusive of the current token and holds W positions, so the
-attended positions are ``[max(0, len - W), len)`` (``W = 0`` means global).
-Attention sinks (the page's default of 4) are not part of this path.  Everything is
-fp64; the dequantized values passed in are exact (``q * s`` in fp64).
+attended positions are ``[max(0, len - W), len)`` (``W = 0`` means global).  With
+attention sinks ([KV-opt] §3.2: every position also sees the first
+``num_sink_tokens`` positions, default 4) a windowed query attends
+``[0, min(n_sink, len)) U [max(0, len - W), len)``; the page's mask also marks the
+first n_sink columns for rows i < n_sink, positions after i that a decode step does
+not have yet, so at decode the sinks stop at ``len``.  Everything is fp64; the
+dequantized values passed in are exact (``q * s`` in fp64).
 """
 
 import numpy as np
 
 
-def attended_positions(length, window):
-    """Positions a decode query at sequence length ``length`` attends ([KV-opt] §3.2)."""
+def attended_positions(length, window, sinks=0):
+    """Positions a decode query at sequence length ``length`` attends ([KV-opt] §3.2):
+    the last ``window`` positions (all of them for window 0) and, with a window, the
+    first ``sinks`` positions."""
     if length <= 0:
         raise ValueError("length must be positive")
+    if window < 0 or sinks < 0:
+        raise ValueError("window and sinks must be non-negative")
     lo = max(0, length - window) if window > 0 else 0
+    if window > 0 and sinks > 0:
+        return np.concatenate([np.arange(0, min(sinks, lo)), np.arange(lo, length)])
     return np.arange(lo, length)
 
 
-def decode_attention(q, k_hat, v_hat, lens, window=0, scale=None):
+def decode_attention(q, k_hat, v_hat, lens, window=0, scale=None, sinks=0):
     """out[b, h] = sum_t softmax_t(scale * q[b,h] . k_hat[b,kv,t]) * v_hat[b,kv,t].
 
     q:      [B, Hq, D] (any float; taken as exact values)
@@ -39,6 +49,7 @@ def decode_attention(q, k_hat, v_hat, lens, window=0, scale=None):
     lens:   [B] valid lengths (positions 0..len-1, the just-appended one included)
     window: 0 for global attention, else the horizon W
     scale:  softmax scale; None -> 1/sqrt(D)
+    sinks:  with a window, the number of leading positions also attended
     Returns fp64 [B, Hq, D].
     """
     q = np.asarray(q, dtype=np.float64)
@@ -51,7 +62,7 @@ def decode_attention(q, k_hat, v_hat, lens, window=0, scale=None):
         scale = D ** -0.5
     out = np.zeros((B, Hq, D), dtype=np.float64)
     for b in range(B):
-        T = attended_positions(int(lens[b]), window)
+        T = attended_positions(int(lens[b]), window, sinks)
         for h in range(Hq):
             kv = h // n_rep
             K = np.asarray(k_hat[b, kv, T], dtype=np.float64)

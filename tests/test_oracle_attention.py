@@ -88,3 +88,36 @@ def test_matches_torch_sdpa_fp64(lens, window):
         qt = torch.from_numpy(q[b])[:, None, :]
         ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, 0]
         assert np.allclose(o[b], ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_sink_positions():
+    """Window plus attention sinks ([KV-opt] section 3.2): the first n_sink positions and
+    the last W; contiguous once the window reaches the sinks; window 0 ignores them."""
+    assert list(attended_positions(10, 4, sinks=2)) == [0, 1, 6, 7, 8, 9]
+    assert list(attended_positions(10, 4, sinks=0)) == [6, 7, 8, 9]
+    assert list(attended_positions(7, 4, sinks=4)) == [0, 1, 2, 3, 4, 5, 6]   # lo = 3 < 4
+    assert list(attended_positions(3, 4, sinks=2)) == [0, 1, 2]
+    assert list(attended_positions(2, 1, sinks=4)) == [0, 1]                  # sinks stop at len
+    assert list(attended_positions(10, 0, sinks=3)) == list(range(10))
+    with pytest.raises(ValueError):
+        attended_positions(5, 2, sinks=-1)
+
+
+@pytest.mark.parametrize("lens,window,sinks", [([37, 30], 7, 4), ([37, 6], 5, 4), ([9, 37], 3, 12)])
+def test_sinks_match_torch_sdpa_with_the_pages_mask(lens, window, sinks):
+    """The decode row of the page's mask (window rows [max(0, i - W + 1), i] plus the
+    first n_sink columns, i = len - 1, columns limited to the len positions that exist),
+    applied by torch's scaled_dot_product_attention in float64 over all positions."""
+    rng = np.random.default_rng(6)
+    q, k, v = _rand(rng)
+    o = decode_attention(q, k, v, lens, window=window, sinks=sinks)
+    for b, L in enumerate(lens):
+        i = L - 1
+        mask = torch.zeros(L, dtype=torch.bool)
+        mask[max(0, i - window + 1): i + 1] = True
+        mask[:sinks] = True
+        kt = torch.from_numpy(k[b, :, :L]).repeat_interleave(2, dim=0)
+        vt = torch.from_numpy(v[b, :, :L]).repeat_interleave(2, dim=0)
+        qt = torch.from_numpy(q[b])[:, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask[None, None, :])[:, 0]
+        assert np.allclose(o[b], ref.numpy(), rtol=1e-12, atol=1e-13)
