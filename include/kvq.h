@@ -47,7 +47,9 @@
  *   KVQ_WHT_LM4   codes  [B, Hkv, C, D/2] uint8, unsigned 4-bit Lloyd-Max indices
  *                        (0..15) of the rotated row, same nibble order as INT4;
  *                 scales [B, Hkv, C] fp32 (the row's RMS).
- *   Position p of a sequence lives in slot p % C (a ring once p >= C).
+ *   Position p of a sequence lives in slot p when p < S (S = sinks, the first
+ *   positions kept for attention sinks, [KV-opt] §3.2), else in slot
+ *   S + (p - S) mod (C - S): a ring of C - S slots (S = 0: slot p mod C).
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -59,7 +61,7 @@
 extern "C" {
 #endif
 
-#define KVQ_VERSION 2
+#define KVQ_VERSION 3
 /* Largest batch the decode/append calls accept (per-sequence lengths and positions
  * travel in the kernel argument block). */
 #define KVQ_MAX_BATCH 256
@@ -93,6 +95,7 @@ typedef struct {
   int32_t capacity;  /* C: slots per (b, kv head) >= 1 */
   int32_t group_k;   /* INT4 only: K group size (default 64); power of two, 32 <= g <= D */
   int32_t group_v;   /* INT4 only: V group size (default 128); same rule */
+  int32_t sinks;     /* S: leading positions kept outside the ring, 0 <= S < C (0: none) */
 } kvq_cache_desc;
 
 /* Device pointers of one layer's cache (layout above). */
@@ -128,8 +131,9 @@ size_t kvq_scales_bytes(const kvq_cache_desc* desc, int32_t kv);
 int32_t kvq_plan_splits(const kvq_cache_desc* desc, int32_t q_heads, int32_t span);
 
 /* Workspace bytes kvq_decode_attn / kvq_append_decode_attn need for these arguments
- * (num_splits = 0: the library's own plan for a longest span of min(max_len, window or
- * max_len)); 0 if invalid.  Equal to KVQ_WS_COUNTER_BYTES + B * q_heads * nsplit *
+ * (num_splits = 0: the library's own plan for the longest attended span at max_len:
+ * max_len, or window + min(S, max_len - window) when 0 < window < max_len); 0 if
+ * invalid.  Equal to KVQ_WS_COUNTER_BYTES + B * q_heads * nsplit *
  * (D + 2) * 4. */
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t q_heads,
                                   int32_t max_len, int32_t window, int32_t num_splits);
@@ -143,9 +147,9 @@ int32_t kvq_codec_codebook(float* levels16, float* thresholds15);
 /* Bulk quantize `n` consecutive positions [start_pos, start_pos + n) of every
  * (b, kv head) into the cache ([KV-4bit] §2.1 applied to the prefill rows).
  *   k_f16, v_f16: device, [B, Hkv, n, D] fp16 contiguous (the prompt's K and V).
- *   Position p goes to slot p % C.  Requires 0 <= start_pos, 1 <= n <= C
- *   (KVQ_ERR_CAPACITY otherwise: more rows than slots would overwrite each other
- *   within one call).
+ *   Position p goes to its slot (layout above).  Requires 0 <= start_pos, n >= 1 and
+ *   at most C - S of the positions at or after S (KVQ_ERR_CAPACITY otherwise: more
+ *   rows than ring slots would overwrite each other within one call).
  * INT4: per group, s = fl32(amax/7) (1 if 0), code = clamp(rne(fl32(x/s)), -7, 7).
  * INT8: s = max(fl32(amax/127), 1e-8), code = clamp(rne(fl32(x/s)), -128, 127).
  * Codec: y = H x / sqrt(D), s = ||x||_2 / sqrt(D), index = #{thresholds < y/s}. */
@@ -153,7 +157,7 @@ int32_t kvq_quantize_prefill(const kvq_cache_desc* desc, const kvq_cache* cache,
                              const void* k_f16, const void* v_f16,
                              int32_t start_pos, int32_t n, kvq_stream stream);
 
-/* Quantize one new token's K/V row per (b, kv head) into slot pos[b] % C
+/* Quantize one new token's K/V row per (b, kv head) into the slot of position pos[b]
  * ([KV-4bit] §1.1 decode step: append the new token's K/V to the cache).
  *   k_f16, v_f16: device, [B, Hkv, D] fp16 contiguous.
  *   pos: host, [B] positions, each >= 0.
@@ -165,12 +169,14 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
 /* Single-token decode attention reading the packed cache, dequantizing in registers
  * ([INT4-SM] §5 step 5; semantics of [KV-opt] §3.2):
  *   out[b, h] = sum_t softmax_t(scale * q[b,h] . x_K[b,kv,t]) * x_V[b,kv,t]
- * with kv = h / (q_heads / Hkv) (GQA), t over [max(0, len_b - window), len_b)
- * (window = 0: [0, len_b)), x = the dequantized cache values.
+ * with kv = h / (q_heads / Hkv) (GQA), t over [max(0, len_b - window), len_b) and,
+ * with a window, the attention sinks [0, min(S, len_b - window)) as well (window = 0:
+ * [0, len_b)), x = the dequantized cache values.
  *   q_f16: device, [B, q_heads, D] fp16.  q_heads must be a multiple of Hkv with
  *          q_heads / Hkv in {1, 2, 4, 8}.
  *   lens: host, [B], 1 <= len_b; positions 0..len_b-1 must be in the cache
- *         (len_b <= C, or window in 1..C when len_b > C; KVQ_ERR_CAPACITY otherwise).
+ *         (len_b <= C, or window in 1..C - S when len_b > C; KVQ_ERR_CAPACITY
+ *         otherwise).
  *   softmax_scale: > 0, or 0 to select 1/sqrt(D); negative values are rejected.
  *   num_splits: sequence splits per (b, kv head), at most 1024; 0 = kvq_plan_splits.
  *   out: device, [B, q_heads, D] fp32.
@@ -181,9 +187,10 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
  *              leaves them zero; the rest is clobbered.  Calls that may run at the same
  *              time need separate workspaces.
  * Split-K: each split writes an unnormalized partial (running max, sum, weighted V) to
- * the workspace; the partials are merged with the log-sum-exp rule, for INT4 with
- * head_dim 128 and V group 128 by the last split to finish (no second launch),
- * otherwise by a second kernel. */
+ * the workspace; the partials are merged with the log-sum-exp rule by the last split to
+ * finish (no second launch) on the matrix-core kernels (INT4 with head_dim 128, V group
+ * 128 and no sinks; INT8 with head_dim 128) and, up to 32 splits, on the split-K kernel
+ * (every other case); above that by a second kernel. */
 int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
                         const void* q_f16, int32_t q_heads, const int32_t* lens,
                         int32_t window, float softmax_scale, int32_t num_splits,
@@ -194,10 +201,10 @@ int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
  * pos[b] = lens[b] - 1 followed by kvq_decode_attn with the same arguments.
  *   k_f16, v_f16: device, [B, Hkv, D] fp16, the new token's rows (position lens[b] - 1).
  * Every other argument, the workspace rule and the errors are those of kvq_decode_attn
- * (KVQ_ERR_ARG also for null k_f16 / v_f16).  For INT4 with head_dim 128 and V group
- * 128 the new row is quantized inside the attention kernel, which writes it to the
- * cache and adds it to the softmax without reading it back (one launch per step); other
- * formats and shapes run the append kernel first. */
+ * (KVQ_ERR_ARG also for null k_f16 / v_f16).  On the INT4 matrix-core kernel (head_dim
+ * 128, V group 128, no sinks) and for the codec, the new row is quantized inside the
+ * attention kernel, which writes it to the cache and adds it to the softmax without
+ * reading it back (one launch per step); the other cases run the append kernel first. */
 int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
                                const void* k_f16, const void* v_f16, const void* q_f16,
                                int32_t q_heads, const int32_t* lens, int32_t window,
@@ -206,7 +213,8 @@ int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cach
 
 /* Dequantize positions [start_pos, start_pos + n) of K (kv = 0) or V (kv = 1)
  * ([KV-4bit] §2.1 dequantize_4bit_group: code * scale; codec: s * H c[idx] / sqrt(D)).
- *   out: device, [B, Hkv, n, D] fp32.  Requires 1 <= n <= C, start_pos >= 0. */
+ *   out: device, [B, Hkv, n, D] fp32.  Requires start_pos >= 0, n >= 1 and at most C - S
+ *   of the positions at or after S (the rows must be distinct slots). */
 int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t kv,
                     int32_t start_pos, int32_t n, float* out, kvq_stream stream);
 

@@ -44,7 +44,7 @@ class kvq_cache_desc(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("group_k", ctypes.c_int32),
-                ("group_v", ctypes.c_int32)]
+                ("group_v", ctypes.c_int32), ("sinks", ctypes.c_int32)]
 
 
 class kvq_cache(ctypes.Structure):
@@ -105,9 +105,9 @@ def _check(status, where):
     return status
 
 
-def make_desc(fmt, batch, kv_heads, head_dim, capacity, group_k=64, group_v=128):
+def make_desc(fmt, batch, kv_heads, head_dim, capacity, group_k=64, group_v=128, sinks=0):
     f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
-    return kvq_cache_desc(f, batch, kv_heads, head_dim, capacity, group_k, group_v)
+    return kvq_cache_desc(f, batch, kv_heads, head_dim, capacity, group_k, group_v, sinks)
 
 
 def _ptr(t, dtype=None, name="tensor"):

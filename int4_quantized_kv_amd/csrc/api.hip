@@ -16,6 +16,7 @@ int32_t check_desc(const kvq_cache_desc* d) {
   if (d->format < KVQ_INT4_G || d->format > KVQ_WHT_LM4) return KVQ_ERR_ARG;
   if (d->batch < 1 || d->kv_heads < 1 || d->head_dim < 1 || d->capacity < 1)
     return KVQ_ERR_ARG;
+  if (d->sinks < 0 || d->sinks >= d->capacity) return KVQ_ERR_ARG;
   if (d->batch > KVQ_MAX_BATCH) return KVQ_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   if (d->format == KVQ_INT4_G) {
@@ -75,6 +76,13 @@ size_t partials_bytes(int32_t batch, int32_t q_heads, int32_t ns, int32_t head_d
   return (size_t)batch * q_heads * ns * (head_dim + 2) * sizeof(float);
 }
 
+// Positions a decode step at length L attends: L, or with a window W < L the window
+// and the sinks before it.
+int32_t attended_span(int32_t L, int32_t window, int32_t sinks) {
+  if (window <= 0 || window >= L) return L;
+  return window + (sinks < L - window ? sinks : L - window);
+}
+
 // Longest attended span over the batch; KVQ_ERR_* (negative) if a length is invalid.
 int32_t check_lens(const kvq_cache_desc* d, const int32_t* lens, int32_t window) {
   int32_t span = 0;
@@ -83,13 +91,19 @@ int32_t check_lens(const kvq_cache_desc* d, const int32_t* lens, int32_t window)
     if (L < 1) return KVQ_ERR_ARG;
     if (window == 0) {
       if (L > d->capacity) return KVQ_ERR_CAPACITY;
-    } else if (L > d->capacity && window > d->capacity) {
-      return KVQ_ERR_CAPACITY;
+    } else if (L > d->capacity && window > d->capacity - d->sinks) {
+      return KVQ_ERR_CAPACITY;   // the window's rows would not all be in the ring
     }
-    const int32_t s = window > 0 && window < L ? window : L;
+    const int32_t s = attended_span(L, window, d->sinks);
     if (s > span) span = s;
   }
   return span;
+}
+
+// Positions [start, start + n) map to distinct slots: at most C - S of them at or after S.
+bool rows_fit(const kvq_cache_desc* d, int32_t start, int32_t n) {
+  const int64_t first_ring = start > d->sinks ? start : d->sinks;
+  return (int64_t)start + n - first_ring <= d->capacity - d->sinks;
 }
 
 }  // namespace
@@ -134,7 +148,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* d, int32_t q_heads, int3
   if (check_desc(d) != KVQ_OK || q_heads < 1 || q_heads % d->kv_heads || max_len < 1 ||
       window < 0 || num_splits < 0)
     return 0;
-  const int32_t span = window > 0 && window < max_len ? window : max_len;
+  const int32_t span = attended_span(max_len, window, d->sinks);
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(d, q_heads, span);
   return partials_offset() + partials_bytes(d->batch, q_heads, ns, d->head_dim);
 }
@@ -151,7 +165,7 @@ int32_t kvq_quantize_prefill(const kvq_cache_desc* desc, const kvq_cache* cache,
   const int32_t st = check_desc(desc);
   if (st != KVQ_OK) return st;
   if (!cache_ok(cache) || !k_f16 || !v_f16 || start_pos < 0 || n < 1) return KVQ_ERR_ARG;
-  if (n > desc->capacity) return KVQ_ERR_CAPACITY;
+  if (!rows_fit(desc, start_pos, n)) return KVQ_ERR_CAPACITY;
   if ((uint64_t)desc->batch * desc->kv_heads * n * (desc->head_dim / 8) >= (1ull << 31))
     return KVQ_ERR_UNSUPPORTED;
   if ((int64_t)start_pos + n - 1 > INT32_MAX) return KVQ_ERR_ARG;
@@ -161,6 +175,7 @@ int32_t kvq_quantize_prefill(const kvq_cache_desc* desc, const kvq_cache* cache,
   map.start = start_pos;
   map.n = n;
   map.cap = desc->capacity;
+  map.sinks = desc->sinks;
   return quant_common(desc, cache, k_f16, v_f16, map, n, static_cast<hipStream_t>(stream));
 }
 
@@ -178,6 +193,7 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache, const voi
   map.append = 1;
   map.n = 1;
   map.cap = desc->capacity;
+  map.sinks = desc->sinks;
   return quant_common(desc, cache, k_f16, v_f16, map, 1, static_cast<hipStream_t>(stream));
 }
 
@@ -227,6 +243,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   a.gv = desc->group_v;
   a.window = window;
   a.nsplit = ns;
+  a.sinks = desc->sinks;
   const float scale = softmax_scale != 0.0f ? softmax_scale
                                             : 1.0f / std::sqrt((float)desc->head_dim);
   a.qscale = scale * 1.4426950408889634f;  // log2(e): scores in base-2 units
@@ -245,6 +262,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
       map.append = 1;
       map.n = 1;
       map.cap = desc->capacity;
+      map.sinks = desc->sinks;
       const int32_t r = quant_common(desc, cache, k_new, v_new, map, 1, stream);
       if (r != KVQ_OK) return r;
     }
@@ -280,7 +298,7 @@ int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t 
   if (st != KVQ_OK) return st;
   if (!cache_ok(cache) || !out || (kv != 0 && kv != 1) || start_pos < 0 || n < 1)
     return KVQ_ERR_ARG;
-  if (n > desc->capacity) return KVQ_ERR_CAPACITY;
+  if (!rows_fit(desc, start_pos, n)) return KVQ_ERR_CAPACITY;
   if ((uint64_t)desc->batch * desc->kv_heads * n * (desc->head_dim / 8) >= (1ull << 31))
     return KVQ_ERR_UNSUPPORTED;
   DequantArgs a;
@@ -295,6 +313,7 @@ int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t 
   a.cap = desc->capacity;
   a.start = start_pos;
   a.n = n;
+  a.sinks = desc->sinks;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (desc->format == KVQ_WHT_LM4) {
     float thr[15];

@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(256) codec_encode_kernel(QuantArgs a) {
     const int t = (int)(row - bh * a.map.n);
     const int b = (int)(bh / (uint32_t)a.Hkv);
     const int p = a.map.append ? a.map.pos[b] : a.map.start + t;
-    const size_t drow = (size_t)bh * a.map.cap + p % a.map.cap;
+    const size_t drow = (size_t)bh * a.map.cap + cache_slot(p, a.map.cap, a.map.sinks);
     codes[drow * LPR + c] = w;
     if (c == 0) scales[drow] = s;
   }
@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(256) codec_dequant_kernel(DequantArgs a) {
     const int c = (int)(i - row * LPR);
     const uint32_t bh = row / (uint32_t)a.n;
     const int t = (int)(row - bh * a.n);
-    const size_t drow = (size_t)bh * a.cap + (a.start + t) % a.cap;
+    const size_t drow = (size_t)bh * a.cap + cache_slot(a.start + t, a.cap, a.sinks);
     const uint32_t w = codes[drow * LPR + c];
     const float s = a.scales[drow];
     float v[8];

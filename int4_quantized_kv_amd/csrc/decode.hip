@@ -129,9 +129,13 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   const bool app_split = fused && sp == a.nsplit - 1;
   const int nrs = fused && a.nsplit > 1 ? a.nsplit - 1 : a.nsplit;   // splits with rows
   const int pt = fused ? len - 1 : len;
-  const int span = pt - lo;
+  // with a window, the attention sinks [0, nsk) come first: the splits share out the
+  // virtual range [vlo, pt), where u in [vlo, lo) stands for position u - vlo
+  const int nsk = a.window > 0 ? min(a.sinks, lo) : 0;
+  const int vlo = lo - nsk;
+  const int span = pt - vlo;
   const int chunk = span > 0 ? (span + nrs - 1) / nrs : 0;
-  const int ps = sp < nrs ? min(pt, lo + sp * chunk) : pt;
+  const int ps = sp < nrs ? min(pt, vlo + sp * chunk) : pt;
   const int pe = min(pt, ps + chunk);
 
   // the rows of the first two steps are requested before q is rotated, so their
@@ -142,10 +146,18 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   constexpr int SR = U * NGRP;   // rows per step (all groups)
   const size_t bh = (size_t)b * a.Hkv + kvh;
   auto load_step = [&](int t0, RawRow (&raw)[U]) {
+    if (a.sinks == 0) {   // (uniform) one ring: slot t mod cap
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = min(t0 + u * NGRP, pe - 1);
-      raw[u] = load_raw<D, FMT>(a, bh * a.cap + (t % a.cap), c);
+      for (int u = 0; u < U; ++u) {
+        const int t = min(t0 + u * NGRP, pe - 1);
+        raw[u] = load_raw<D, FMT>(a, bh * a.cap + (t % a.cap), c);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = min(t0 + u * NGRP, pe - 1);
+        raw[u] = load_raw<D, FMT>(a, bh * a.cap + cache_slot(t >= lo ? t : t - vlo, a.cap, a.sinks), c);
+      }
     }
   };
   // q first (it is needed first), then the rows
@@ -192,7 +204,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     float sc;
     codec_encode_row<LPR>(x, c, thr, w, sc);
     if (grp < 2) {
-      const size_t row = bh * a.cap + (len - 1) % a.cap;
+      const size_t row = bh * a.cap + cache_slot(len - 1, a.cap, a.sinks);
       static_cast<uint32_t*>(const_cast<void*>(grp ? a.v_codes : a.k_codes))[row * LPR + c] = w;
       if (c == 0) const_cast<float*>(grp ? a.v_scales : a.k_scales)[row] = sc;
     }
@@ -542,9 +554,10 @@ template <int D, int FMT>
 hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   hipError_t e;
-  if (FMT == KVQ_INT4_G && mfma_int4_eligible(D, a.gk, a.gv, a.cap, G))
+  // (caches with sinks take the split-K kernel: the matrix-core tiles assume one ring)
+  if (FMT == KVQ_INT4_G && a.sinks == 0 && mfma_int4_eligible(D, a.gk, a.gv, a.cap, G))
     return launch_decode_int4_mfma(a, G, s);   // merges the splits itself
-  if (FMT == KVQ_INT8_TOKEN && mfma_int8_eligible(D, a.cap, G))
+  if (FMT == KVQ_INT8_TOKEN && a.sinks == 0 && mfma_int8_eligible(D, a.cap, G))
     return launch_decode_int8_mfma(a, G, s);
   // up to MERGE_INLINE_MAX splits the last split of a unit merges inside the kernel
   // (one launch less); more partials are merged by the merge kernel, which spreads
@@ -577,10 +590,11 @@ hipError_t launch_fmt(int32_t format, const DecodeArgs& a, int G, hipStream_t s)
 int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
   const int32_t units = d->batch * d->kv_heads;
   if (units <= 0 || span <= 0) return 0;
-  if (d->format == KVQ_INT4_G &&
+  if (d->format == KVQ_INT4_G && d->sinks == 0 &&
       mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group))
     return plan_splits_mfma(units, span);
-  if (d->format == KVQ_INT8_TOKEN && mfma_int8_eligible(d->head_dim, d->capacity, q_group))
+  if (d->format == KVQ_INT8_TOKEN && d->sinks == 0 &&
+      mfma_int8_eligible(d->head_dim, d->capacity, q_group))
     return plan_splits_mfma(units, span);
   // the codec keeps one more split for the new row when its append is fused (planned
   // for every codec call, so that the workspace query does not depend on the call)

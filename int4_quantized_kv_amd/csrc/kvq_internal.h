@@ -12,11 +12,19 @@ namespace kvq {
 
 // Where row (b, h, t) of a quantize call lands: slot (start + t) % cap for a prefill,
 // slot pos[b] % cap for an append (n == 1).
+// Slot of position p in a cache of `cap` slots whose first `sinks` slots hold positions
+// 0 .. sinks - 1 and the rest a ring: p below sinks, else sinks + (p - sinks) mod
+// (cap - sinks) (p mod cap without sinks).
+__host__ __device__ inline int32_t cache_slot(int32_t p, int32_t cap, int32_t sinks) {
+  return p < sinks ? p : sinks + (p - sinks) % (cap - sinks);
+}
+
 struct SlotMap {
   int32_t append;   // 0: prefill, 1: append
   int32_t start;
   int32_t n;        // rows per (b, h) in the source tensor
   int32_t cap;
+  int32_t sinks;    // slots ahead of the ring (cache_slot)
   int32_t pos[KVQ_MAX_BATCH];
 };
 
@@ -38,6 +46,7 @@ struct DequantArgs {
   const float* scales;
   float* out;            // [B, Hkv, n, D]
   int32_t B, Hkv, D, g, cap, start, n;
+  int32_t sinks;         // slots ahead of the ring (cache_slot)
   float levels[16];      // codec output levels (codec format only)
 };
 
@@ -54,6 +63,8 @@ struct DecodeArgs {
   const uint16_t* k_new; // [B, Hkv, D] fp16 rows appended at position lens[b] - 1, or null
   const uint16_t* v_new;
   int32_t B, Hkv, Hq, D, cap, gk, gv, window, nsplit;
+  int32_t sinks;         // slots ahead of the ring; with a window, positions 0 .. sinks - 1
+                         // are attended too (before the window)
   float qscale;          // softmax scale * log2(e)
   float levels[16];      // codec output levels
   float thr[15];         // codec decision thresholds (the fused codec append)

@@ -28,7 +28,8 @@ namespace {
 // gridDim.z; gridDim.z is capped at 65535).  A pair's
 // rows are n consecutive source rows of D/8 16-byte chunks; chunk ci is row ci / lpr,
 // lane-chunk ci % lpr (lpr a power of two: shifts).  The cache slot of row t is
-// (base + t) mod cap with base < cap and t < n <= cap: one conditional subtract.
+// (base + t) mod cap with base < cap and t < n <= cap: one conditional subtract
+// (cache_slot when the cache keeps sink slots ahead of its ring).
 __device__ __forceinline__ int log2i(int x) { return 31 - __builtin_clz(x); }
 
 
@@ -42,8 +43,9 @@ __device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
   // lpr, lpg and gpr are powers of two (D in {64, 128, 256}, g a power of two >= 32)
   const int lpr = a.D >> 3, lsh = log2i(lpr), lpg = g >> 3, gsh = log2i(lpg);
   const int gprsh = log2i(a.D / g);
-  const int cap = a.map.cap;
-  const int base = (a.map.append ? a.map.pos[b] : a.map.start) % cap;
+  const int cap = a.map.cap, sinks = a.map.sinks;
+  const int p0 = a.map.append ? a.map.pos[b] : a.map.start;
+  const int base = p0 % cap;
   const uint32_t npair = (uint32_t)a.map.n * (uint32_t)lpr;
   const uint4* srcp = reinterpret_cast<const uint4*>(src) + (size_t)bh * npair;
   const size_t row0 = (size_t)bh * cap;
@@ -74,8 +76,13 @@ __device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
       }
       const float sc = INT8 ? kvq_int8_scale(am) : kvq_int4_scale(am);
       const float r = 1.0f / sc;
-      int slot = base + t;
-      if (slot >= cap) slot -= cap;
+      int slot;
+      if (sinks) {   // (uniform) sink slots ahead of the ring
+        slot = cache_slot(p0 + t, cap, sinks);
+      } else {
+        slot = base + t;
+        if (slot >= cap) slot -= cap;
+      }
       const size_t drow = row0 + slot;
       if (INT8) {
         uint32_t w0 = 0, w1 = 0;
@@ -116,7 +123,7 @@ template <bool INT8>
 __device__ __forceinline__ void dequant_pair(const DequantArgs& a, int bh) {
   const int g = INT8 ? a.D : a.g;
   const int lpr = a.D >> 3, lsh = log2i(lpr), gsh = log2i(g >> 3), gprsh = log2i(a.D / g);
-  const int cap = a.cap;
+  const int cap = a.cap, sinks = a.sinks;
   const int base = a.start % cap;
   const uint32_t nhalf = 2u * (uint32_t)a.n * (uint32_t)lpr;
   const size_t row0 = (size_t)bh * cap;
@@ -131,8 +138,13 @@ __device__ __forceinline__ void dequant_pair(const DequantArgs& a, int bh) {
       if (k < nhalf) {
         const uint32_t i = k >> 1;
         const int t = (int)(i >> lsh), c = (int)(i & (lpr - 1));
-        int slot = base + t;
-        if (slot >= cap) slot -= cap;
+        int slot;
+        if (sinks) {   // (uniform) sink slots ahead of the ring
+          slot = cache_slot(a.start + t, cap, sinks);
+        } else {
+          slot = base + t;
+          if (slot >= cap) slot -= cap;
+        }
         const size_t drow = row0 + slot;
         if (INT8) {   // the half's 4 bytes
           wr[u] = reinterpret_cast<const uint32_t*>(a.codes)[2 * ((drow << lsh) + c) + (k & 1)];

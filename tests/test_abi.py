@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     exported = set(re.findall(r" T (kvq_\w+)", out))
     for n in names:
         assert n in exported, n
-    assert kvq.kvq_version() == 2
+    assert kvq.kvq_version() == 3
 
 
 def test_status_strings():
@@ -75,12 +75,15 @@ def test_size_queries_match_closed_forms():
     (dict(group_v=256), kvq.KVQ_ERR_UNSUPPORTED),    # g > D
     (dict(capacity=0), kvq.KVQ_ERR_ARG),
     (dict(kv_heads=-1), kvq.KVQ_ERR_ARG),
+    (dict(sinks=-1), kvq.KVQ_ERR_ARG),
+    (dict(sinks=64), kvq.KVQ_ERR_ARG),                # no ring slot left
 ])
 def test_descriptor_validation(fields, status):
-    base = dict(format=0, batch=2, kv_heads=4, head_dim=128, capacity=64, group_k=64, group_v=128)
+    base = dict(format=0, batch=2, kv_heads=4, head_dim=128, capacity=64, group_k=64,
+                group_v=128, sinks=0)
     base.update(fields)
     d = kvq.kvq_cache_desc(*[base[k] for k in ("format", "batch", "kv_heads", "head_dim",
-                                               "capacity", "group_k", "group_v")])
+                                               "capacity", "group_k", "group_v", "sinks")])
     assert kvq.kvq_check_desc(d) == status
     assert kvq.kvq_codes_bytes(d, 0) == 0
 
@@ -139,6 +142,24 @@ def test_error_paths_enqueue_nothing():
     bad = kvq.make_desc("codec", 2, 4, 96, 64)
     _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_quantize_prefill, bad, c, FAKE, FAKE, 0, 4, 0)
     _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_dequant, bad, c, 0, 0, 4, FAKE, 0)
+
+
+def test_sinks_validation_and_workspace():
+    """A cache of 20 slots with 4 sink slots: a ring of 16.  Writes of more ring positions
+    than ring slots, and windows longer than the ring over a wrapped cache, are
+    rejected; the workspace covers the window plus the sinks."""
+    d = kvq.make_desc("int4", 2, 4, 128, 20, sinks=4)
+    assert kvq.kvq_check_desc(d) == 0
+    assert kvq.kvq_check_desc(kvq.make_desc("int4", 2, 4, 128, 20, sinks=19)) == 0
+    c = _cache()
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_quantize_prefill, d, c, FAKE, FAKE, 0, 21, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_quantize_prefill, d, c, FAKE, FAKE, 10, 17, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_dequant, d, c, 0, 2, 19, FAKE, 0)   # ring part 17
+    ws = kvq.kvq_decode_workspace_bytes(d, 8, 100, 10)
+    span = 10 + 4
+    assert ws == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * kvq.kvq_plan_splits(d, 8, span) * 130 * 4
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_decode_attn, d, c, FAKE, 8, [30, 10], 17, 0.0, 0, FAKE, FAKE, ws, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_decode_attn, d, c, FAKE, 8, [30, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
 
 
 def test_split_plan():
