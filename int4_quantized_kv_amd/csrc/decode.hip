@@ -554,10 +554,9 @@ template <int D, int FMT>
 hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   hipError_t e;
-  // (caches with sinks take the split-K kernel: the matrix-core tiles assume one ring)
-  if (FMT == KVQ_INT4_G && a.sinks == 0 && mfma_int4_eligible(D, a.gk, a.gv, a.cap, G))
+  if (FMT == KVQ_INT4_G && mfma_int4_eligible(D, a.gk, a.gv, a.cap, G))
     return launch_decode_int4_mfma(a, G, s);   // merges the splits itself
-  if (FMT == KVQ_INT8_TOKEN && a.sinks == 0 && mfma_int8_eligible(D, a.cap, G))
+  if (FMT == KVQ_INT8_TOKEN && mfma_int8_eligible(D, a.cap, G))
     return launch_decode_int8_mfma(a, G, s);
   // up to MERGE_INLINE_MAX splits the last split of a unit merges inside the kernel
   // (one launch less); more partials are merged by the merge kernel, which spreads
@@ -590,11 +589,10 @@ hipError_t launch_fmt(int32_t format, const DecodeArgs& a, int G, hipStream_t s)
 int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
   const int32_t units = d->batch * d->kv_heads;
   if (units <= 0 || span <= 0) return 0;
-  if (d->format == KVQ_INT4_G && d->sinks == 0 &&
+  if (d->format == KVQ_INT4_G &&
       mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group))
     return plan_splits_mfma(units, span);
-  if (d->format == KVQ_INT8_TOKEN && d->sinks == 0 &&
-      mfma_int8_eligible(d->head_dim, d->capacity, q_group))
+  if (d->format == KVQ_INT8_TOKEN && mfma_int8_eligible(d->head_dim, d->capacity, q_group))
     return plan_splits_mfma(units, span);
   // the codec keeps one more split for the new row when its append is fused (planned
   // for every codec call, so that the workspace query does not depend on the call)

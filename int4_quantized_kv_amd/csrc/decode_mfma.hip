@@ -236,9 +236,10 @@ __device__ __forceinline__ DmaOffs dma_offsets(int lane) {
 // the LDS slot `lb`.  A full tile whose 32 slots are contiguous is addressed from one
 // scalar base row plus the fixed lane offsets; otherwise each row is clamped to pe - 1
 // (masked positions read a valid row) and wrapped around the ring.
-template <int NGK>
+template <int NGK, bool SK>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int t0, int pe,
-                                           uint8_t* lb, int lane, const DmaOffs& o) {
+                                           int lo, int vlo, uint8_t* lb, int lane,
+                                           const DmaOffs& o) {
   using L = Slot<NGK>;
   const int cap = a.cap;
   const int sbase = t0 % cap;
@@ -246,7 +247,7 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int
   const uint8_t* vc = static_cast<const uint8_t*>(a.v_codes);
   const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k_scales);
   const uint8_t* vs = reinterpret_cast<const uint8_t*>(a.v_scales);
-  if (t0 + TILE <= pe && sbase + TILE <= cap) {
+  if (!SK && t0 + TILE <= pe && sbase + TILE <= cap) {
     const size_t rb = row0 + (size_t)sbase;
     const uint8_t* kb = kc + rb * (HD / 2);
     const uint8_t* vb = vc + rb * (HD / 2);
@@ -265,6 +266,10 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int
   auto row_of = [&](int rho) -> size_t {
     int off = rho;
     if (t0 + off > pe - 1) off = pe - 1 - t0;
+    if constexpr (SK) {   // virtual index u: [vlo, lo) stands for the sinks 0 .. lo - vlo - 1
+      const int u = t0 + off;
+      return row0 + (size_t)cache_slot(u >= lo ? u : u - vlo, cap, a.sinks);
+    }
     int sl = sbase + off;
     if (sl >= cap) sl -= cap;
     return row0 + (size_t)sl;
@@ -588,14 +593,15 @@ __device__ __forceinline__ DmaOffs8 dma_offsets8(int lane) {
   return o;
 }
 
+template <bool SK>
 __device__ __forceinline__ void issue_tile8(const DecodeArgs& a, size_t row0, int t0, int pe,
-                                            uint8_t* lb, const DmaOffs8& o) {
+                                            int lo, int vlo, uint8_t* lb, const DmaOffs8& o) {
   using L = Slot8;
   const int cap = a.cap;
   const int sbase = t0 % cap;
   const uint8_t* kc = static_cast<const uint8_t*>(a.k_codes);
   const uint8_t* vc = static_cast<const uint8_t*>(a.v_codes);
-  if (t0 + TILE8 <= pe && sbase + TILE8 <= cap) {
+  if (!SK && t0 + TILE8 <= pe && sbase + TILE8 <= cap) {
     const size_t rb = row0 + (size_t)sbase;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
@@ -609,6 +615,10 @@ __device__ __forceinline__ void issue_tile8(const DecodeArgs& a, size_t row0, in
   auto row_of = [&](int rho) -> size_t {
     int off = rho;
     if (t0 + off > pe - 1) off = pe - 1 - t0;
+    if constexpr (SK) {   // as in issue_tile
+      const int u = t0 + off;
+      return row0 + (size_t)cache_slot(u >= lo ? u : u - vlo, cap, a.sinks);
+    }
     int sl = sbase + off;
     if (sl >= cap) sl -= cap;
     return row0 + (size_t)sl;
@@ -898,7 +908,9 @@ __device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewLds*
 
 // I8: the INT8 per-token format (NGK = 2 then counts the (head, part) columns of a head,
 // both carrying the whole q; 16-position tiles, one position set).
-template <int G, int NGK, bool I8>
+// SK: the cache keeps attention-sink slots ahead of its ring (a separate instance, so
+// that the common case carries no sink arithmetic).
+template <int G, int NGK, bool I8, bool SK>
 __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   using L = std::conditional_t<I8, Slot8, Slot<NGK>>;
   constexpr int TL = I8 ? TILE8 : TILE;       // positions per tile
@@ -956,9 +968,13 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // workgroup of 8 waves per CU: with two workgroups of 4 waves sharing a CU, one of the
   // pair was measured to lag the other by up to a third of the kernel, a split no LDS
   // counter can rebalance.
-  const int span = pt - lo_pos;
+  // with a window, the attention sinks [0, nsk) come first: the splits share out the
+  // virtual range [vlo, pt), where u in [vlo, lo_pos) stands for position u - vlo
+  const int nsk = SK && a.window > 0 ? min(a.sinks, lo_pos) : 0;
+  const int vlo = lo_pos - nsk;
+  const int span = pt - vlo;
   const int chunk = span > 0 ? (span + a.nsplit - 1) / a.nsplit : 0;
-  const int ps = min(pt, lo_pos + sp * chunk);
+  const int ps = min(pt, vlo + sp * chunk);
   const int pe = min(pt, ps + chunk);
   const int nts = (pe - ps + TL - 1) / TL;
   const size_t row0 = (size_t)unit * a.cap;
@@ -968,8 +984,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     else return dma_offsets<NGK>(lane);
   }();
   auto issue = [&](int t0, uint8_t* lb) {
-    if constexpr (I8) issue_tile8(a, row0, t0, pe, lb, dof);
-    else issue_tile<NGK>(a, row0, t0, pe, lb, lane, dof);
+    if constexpr (I8) issue_tile8<SK>(a, row0, t0, pe, lo_pos, vlo, lb, dof);
+    else issue_tile<NGK, SK>(a, row0, t0, pe, lo_pos, vlo, lb, lane, dof);
   };
   if (threadIdx.x == 0) s_claim = 0;   // ordered before the first claim by the q barrier
 
@@ -1257,7 +1273,9 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // the new row's codes and scales go to the cache here, so that the wait below covers
   // them together with the partials (a barrier right after the loop would wait for them
   // alone); no tile of this step reads that row
-  if (app_wave && lane < 32) store_new_row<NGK>(a, &s_new, row0 + (size_t)((len - 1) % a.cap), lane);
+  if (app_wave && lane < 32)
+    store_new_row<NGK>(a, &s_new, row0 + (size_t)(SK ? cache_slot(len - 1, a.cap, a.sinks)
+                                                       : (len - 1) % a.cap), lane);
   uint32_t* cnt = a.counters + unit;
   wait_vmcnt<0>();
   __syncthreads();
@@ -1357,15 +1375,32 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int G>
-hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
+template <int G, bool SK>
+hipError_t launch_gs(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   switch (HD / a.gk) {
-    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1, false>, grid, dim3(NT), a, s);
-    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2, false>, grid, dim3(NT), a, s);
+    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1, false, SK>, grid, dim3(NT), a, s);
+    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2, false, SK>, grid, dim3(NT), a, s);
     case 4:
-      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4, false>, grid, dim3(NT), a, s);
+      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4, false, SK>, grid, dim3(NT), a, s);
       return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int G>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
+  return a.sinks ? launch_gs<G, true>(a, s) : launch_gs<G, false>(a, s);
+}
+
+template <bool SK>
+hipError_t launch_i8(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
+  const dim3 grid(a.nsplit, a.Hkv, a.B);
+  switch (q_group) {
+    case 1: return launch_kernel(decode_int4_mfma_kernel<1, 2, true, SK>, grid, dim3(NT), a, s);
+    case 2: return launch_kernel(decode_int4_mfma_kernel<2, 2, true, SK>, grid, dim3(NT), a, s);
+    case 4: return launch_kernel(decode_int4_mfma_kernel<4, 2, true, SK>, grid, dim3(NT), a, s);
+    case 8: return launch_kernel(decode_int4_mfma_kernel<8, 2, true, SK>, grid, dim3(NT), a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1391,7 +1426,7 @@ int32_t plan_splits_mfma(int32_t units, int32_t span) {
 
 bool fused_append_supported(const kvq_cache_desc* d, int32_t q_group) {
   if (d->format == KVQ_WHT_LM4) return true;   // the codec's split-K kernel codes the row
-  return d->format == KVQ_INT4_G && d->sinks == 0 &&
+  return d->format == KVQ_INT4_G &&
          mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group);
 }
 
@@ -1411,14 +1446,7 @@ bool mfma_int8_eligible(int32_t head_dim, int32_t cap, int32_t q_group) {
 }
 
 hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
-  const dim3 grid(a.nsplit, a.Hkv, a.B);
-  switch (q_group) {
-    case 1: return launch_kernel(decode_int4_mfma_kernel<1, 2, true>, grid, dim3(NT), a, s);
-    case 2: return launch_kernel(decode_int4_mfma_kernel<2, 2, true>, grid, dim3(NT), a, s);
-    case 4: return launch_kernel(decode_int4_mfma_kernel<4, 2, true>, grid, dim3(NT), a, s);
-    case 8: return launch_kernel(decode_int4_mfma_kernel<8, 2, true>, grid, dim3(NT), a, s);
-    default: return hipErrorInvalidValue;
-  }
+  return a.sinks ? launch_i8<true>(a, q_group, s) : launch_i8<false>(a, q_group, s);
 }
 
 }  // namespace kvq
