@@ -22,6 +22,8 @@ the same form; the default run is the headline above):
   ctx128k-int8   the same with the INT8 per-token format
   gemma-codec    Gemma-3-4B-shaped step of the WHT + Lloyd-Max codec: 34 layers (29 with a
                  1024-row window ring, 5 global), append at position 4096 then attend
+  llama8b-sinks  the headline shape with every layer windowed: a 4096-row ring plus 4
+                 attention-sink positions, append at position 8192 then attend 4100 rows
   dequant        kvq_dequant of K and V of 8 Llama-3-8B-shaped layer caches to fp32
 """
 import argparse
@@ -52,6 +54,7 @@ OTHER_TRAFFIC = {
     "ctx128k-int8": ("profiles/decode_mfma_int8_ctx128k_b1_traffic.md", KERNEL_SOURCES),
     "gemma-codec": ("profiles/decode_splitk_codec_gemma3_4b_b4_traffic.md",
                     ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
+    "llama8b-sinks": ("profiles/decode_int4_mfma_llama8b_window4k_sinks4_traffic.md", KERNEL_SOURCES),
 }
 
 
@@ -60,7 +63,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--workload", default="llama8b",
                    choices=["llama8b", "mha7b-prefill", "mha7b-decode", "ctx128k-int4",
-                            "ctx128k-int8", "gemma-codec", "dequant"])
+                            "ctx128k-int8", "gemma-codec", "llama8b-sinks", "dequant"])
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=None, help="override the layer count (debug only)")
@@ -442,13 +445,23 @@ DECODE_MODES = {   # workload id, cache format
     "ctx128k-int4": (5, "int4"),
     "ctx128k-int8": (5, "int8"),
     "gemma-codec": (4, "codec"),
+    "llama8b-sinks": (6, "int4"),
 }
+
+
+def attended_rows(L, W, sinks):
+    """Rows a decode step of length L attends: all of them, or the window's W and the
+    sink positions that lie before it."""
+    if not W or W >= L:
+        return L
+    return W + min(sinks, L - W)
 
 
 def bench_decode(args):
     """One decode step over every layer of a workload: for appending workloads
     kvq_append_decode_attn per layer (append at position `context`, attend over
-    context + 1), otherwise kvq_decode_attn.  Window layers keep a ring of `window` rows."""
+    context + 1), otherwise kvq_decode_attn.  Window layers keep a ring of `window` rows
+    (after `sinks` slots for the first positions when the workload keeps sinks)."""
     import torch
     import int4_quantized_kv_amd as kvq
     import synth
@@ -465,11 +478,15 @@ def bench_decode(args):
     for li in range(nl):
         lay = Layer()
         lay.W = w.layer_window(li)
-        cap = lay.W if lay.W else L
-        lay.desc = kvq.make_desc(fmt, B, Hkv, D, cap, w.group_k, w.group_v)
+        ns = w.sinks if lay.W else 0
+        cap = lay.W + ns if lay.W else L
+        lay.desc = kvq.make_desc(fmt, B, Hkv, D, cap, w.group_k, w.group_v, sinks=ns)
         k, v, q, kn, vn = synth.layer_inputs(w, li, dev)
         lay.dc = kvq.DeviceCache(lay.desc, dev)
-        lo = max(0, S - cap)          # the rows a ring of `cap` slots still holds
+        if ns:                        # the sink positions, in their own slots
+            kvq.kvq_quantize_prefill(lay.desc, lay.dc.c, k[:, :, :ns].contiguous(),
+                                     v[:, :, :ns].contiguous(), 0, ns)
+        lo = max(ns, S - (cap - ns))  # the rows a ring of cap - ns slots still holds
         kvq.kvq_quantize_prefill(lay.desc, lay.dc.c, k[:, :, lo:].contiguous(),
                                  v[:, :, lo:].contiguous(), lo, S - lo)
         del k, v
@@ -480,7 +497,7 @@ def bench_decode(args):
         # the step reads the cached rows of the horizon (all but the new one when it
         # appends), the new row's fp16 K/V, q; writes the new row's codes and the output.
         # The attention call alone (for the roofline) reads every row of the horizon.
-        rows = min(L, lay.W) if lay.W else L
+        rows = attended_rows(L, lay.W, ns)
         qo = B * Hq * D * 2 + B * Hq * D * 4
         attend_bytes += B * Hkv * rows * rb + qo
         if w.append:
@@ -515,6 +532,8 @@ def bench_decode(args):
         attn_ms = ms_step
     if fmt == "int4" and D == 128 and w.group_v == 128:
         kern = "kvq_decode_attn: decode_int4_mfma_kernel (splits merged in-kernel)"
+        if w.sinks and w.window_layers:
+            kern = "kvq_decode_attn: decode_int4_mfma_kernel, sink instance (splits merged in-kernel)"
     elif fmt == "int8" and D == 128:
         kern = "kvq_decode_attn: decode_int4_mfma_kernel, INT8 tiles (splits merged in-kernel)"
     else:
@@ -523,13 +542,15 @@ def bench_decode(args):
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     cfg = {"workload": w.name, "format": fmt, "layers": nl, "batch": B, "q_heads": Hq,
            "kv_heads": Hkv, "head_dim": D, "context": L, "append": w.append,
-           "window_layers": min(nl, w.window_layers), "window": w.window,
+           "window_layers": min(nl, w.window_layers), "window": w.window, "sinks": w.sinks,
            "launch": "eager" if args.eager else "hip-graph",
-           "num_splits": kvq.kvq_plan_splits(layers[-1].desc, Hq, min(L, layers[-1].W or L))}
+           "num_splits": kvq.kvq_plan_splits(layers[-1].desc, Hq,
+                                             attended_rows(L, layers[-1].W, layers[-1].desc.sinks))}
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(w, fmt, args.cpu_seconds, L)
     names = {"mha7b-decode": "MHA-7B shape, 20K ctx, B 8", "ctx128k-int4": "128K ctx, B 1, INT4",
              "ctx128k-int8": "128K ctx, B 1, INT8 per-token",
-             "gemma-codec": "Gemma-3-4B shape, WHT+Lloyd-Max codec, window 1024 x29 + global x5"}
+             "gemma-codec": "Gemma-3-4B shape, WHT+Lloyd-Max codec, window 1024 x29 + global x5",
+             "llama8b-sinks": "Llama-3-8B shape, 8K ctx, B 8, window 4096 + 4 sinks"}
     return _line(args, f"decode step: effective KV GB/s ({names[args.workload]})", gbs, ms_step, cfg,
                  roof, cpu, {"tok_per_s": round(B / (ms_step * 1e-3), 1), "bytes_per_step": step_bytes,
                              "wall_s_timed": round(wall, 4)})
@@ -614,7 +635,8 @@ def bench_dequant(args):
 
 
 OTHER = {"mha7b-prefill": bench_prefill, "mha7b-decode": bench_decode, "ctx128k-int4": bench_decode,
-         "ctx128k-int8": bench_decode, "gemma-codec": bench_decode, "dequant": bench_dequant}
+         "ctx128k-int8": bench_decode, "gemma-codec": bench_decode, "llama8b-sinks": bench_decode,
+         "dequant": bench_dequant}
 
 
 def _oracle_rows(fmt, x16, gk, gv, kv):
@@ -648,15 +670,18 @@ def cpu_baseline_decode(w, fmt, seconds, L):
     layer = 0
     while dt < seconds and layer < w.layers:
         W = w.layer_window(layer)
-        rows = min(L, W) if W else L
+        ns = w.sinks if W else 0
+        rows = attended_rows(L, W, ns)
         k, v, q, kn, vn = (None if t is None else t.cpu().numpy()
                            for t in synth.layer_inputs(w, layer, "cuda:0"))
-        lo = L - rows                                   # first attended position
+        nsink = rows - min(L, W) if W else 0            # sink positions before the window
+        lo = L - (rows - nsink)                         # first attended window position
         for b in range(w.batch):
             for h in range(w.kv_heads):
                 if dt >= seconds:
                     break
-                kr, vr = k[b, h, lo:], v[b, h, lo:]
+                kr = np.concatenate([k[b, h, :nsink], k[b, h, lo:]])
+                vr = np.concatenate([v[b, h, :nsink], v[b, h, lo:]])
                 (kc, kdq), (vc, vdq) = _oracle_rows(fmt, kr, w.group_k, w.group_v, 0), \
                     _oracle_rows(fmt, vr, w.group_k, w.group_v, 1)
                 qq = q[b, h * G:(h + 1) * G]

@@ -87,6 +87,7 @@ class Workload:
     group_v: int = 128
     window_layers: int = 0  # number of sliding-window layers (the first ones)
     window: int = 0
+    sinks: int = 0          # attention-sink positions kept besides a window layer's ring
     zero_groups: tuple = field(default=())
 
     def layer_window(self, layer):
@@ -110,6 +111,9 @@ WORKLOADS = {
     5: Workload(5, "ctx128k-b1-gqa4", layers=32, batch=1, q_heads=32, kv_heads=8,
                 head_dim=128, context=131072, append=False,
                 outlier_channels=round(0.02 * 128)),
+    6: Workload(6, "llama3-8b-window4k-sinks4-b8", layers=32, batch=8, q_heads=32, kv_heads=8,
+                head_dim=128, context=8192, append=True,
+                outlier_channels=round(0.02 * 128), window_layers=32, window=4096, sinks=4),
 }
 
 
