@@ -21,6 +21,14 @@ attention sinks ([KV-opt] §3.2: every position also sees the first
 first n_sink columns for rows i < n_sink, positions after i that a decode step does
 not have yet, so at decode the sinks stop at ``len``.  Everything is fp64; the
 dequantized values passed in are exact (``q * s`` in fp64).
+
+Recent tokens in FP16 ([INT4-SM] section 8.3, first way of cutting memory: INT4 for
+the older tokens' K/V, FP16 kept for the recent ones).  The page fixes neither the
+size of the recent span nor when a token changes form.  Reading: the span is the last
+R positions of the sequence, ``[max(0, len - R), len)``, read at their fp16 values;
+every older position is read at its INT4 dequantized value.  A token is quantized when
+it arrives and also kept in fp16 while it is among the last R, so nothing is
+re-quantized when it leaves the span.
 """
 
 import numpy as np
@@ -38,6 +46,21 @@ def attended_positions(length, window, sinks=0):
     if window > 0 and sinks > 0:
         return np.concatenate([np.arange(0, min(sinks, lo)), np.arange(lo, length)])
     return np.arange(lo, length)
+
+
+def recent_fp16_rows(x_hat, x16, lens, recent):
+    """Rows a decode step reads when the last ``recent`` positions stay in fp16
+    ([INT4-SM] section 8.3): for sequence b, positions ``[max(0, len_b - recent),
+    len_b)`` take their fp16 values from ``x16``, older positions their dequantized
+    values from ``x_hat``.  x_hat, x16: [B, Hkv, N, D] indexed by position.  Returns
+    fp64 [B, Hkv, N, D] (rows at or past len_b copied from x_hat; never attended)."""
+    if recent < 0:
+        raise ValueError("recent must be non-negative")
+    out = np.array(x_hat, dtype=np.float64, copy=True)
+    for b, length in enumerate(lens):
+        lo = max(0, int(length) - recent)
+        out[b, :, lo:int(length)] = np.asarray(x16[b, :, lo:int(length)], dtype=np.float64)
+    return out
 
 
 def decode_attention(q, k_hat, v_hat, lens, window=0, scale=None, sinks=0):

@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.attention import attended_positions, decode_attention
+from oracle import quant
+from oracle.attention import attended_positions, decode_attention, recent_fp16_rows
 
 
 def _rand(rng, B=2, Hq=4, Hkv=2, N=37, D=16):
@@ -121,3 +122,74 @@ def test_sinks_match_torch_sdpa_with_the_pages_mask(lens, window, sinks):
         qt = torch.from_numpy(q[b])[:, None, :]
         ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask[None, None, :])[:, 0]
         assert np.allclose(o[b], ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ---- recent tokens in fp16 ("LLM长上下文推理优化：用INT4状态机管理KV Cache",
+# pwwt.cn/news/4219524, section 8.3: older tokens' K/V in INT4, recent ones in FP16)
+
+def _fp16_and_int4(rng, B=2, H=2, N=40, D=64):
+    x16 = (rng.standard_normal((B, H, N, D)) * 1.5).astype(np.float16)
+    c, s = quant.quantize_int4(x16, 32)
+    return x16, quant.dequantize_int4_exact(c, s, 32)
+
+
+def _sdpa(q, K, V):
+    """torch's scaled_dot_product_attention in float64, one query over rows K, V."""
+    qt = torch.from_numpy(np.asarray(q, dtype=np.float64))[None, None, None, :]
+    kt = torch.from_numpy(np.asarray(K, dtype=np.float64))[None, None]
+    vt = torch.from_numpy(np.asarray(V, dtype=np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, 0, 0].numpy()
+
+
+@pytest.mark.parametrize("lens,recent,window", [([40, 17], 8, 0), ([40, 5], 8, 0), ([33, 40], 1, 0),
+                                                ([40, 29], 12, 20), ([40, 40], 30, 10)])
+def test_recent_rows_match_sdpa_over_the_two_forms(lens, recent, window):
+    """The attended rows split at len - R: INT4 dequantized values before, fp16 values
+    from there on; torch's attention over exactly those rows, built by slicing."""
+    rng = np.random.default_rng(21)
+    k16, kh = _fp16_and_int4(rng)
+    v16, vh = _fp16_and_int4(rng)
+    q = rng.standard_normal((2, 4, 64))
+    o = decode_attention(q, recent_fp16_rows(kh, k16, lens, recent),
+                         recent_fp16_rows(vh, v16, lens, recent), lens, window=window)
+    for b, L in enumerate(lens):
+        lo = max(0, L - window) if window else 0
+        cut = max(lo, L - recent)
+        K = np.concatenate([kh[b, :, lo:cut], k16[b, :, cut:L].astype(np.float64)], axis=1)
+        V = np.concatenate([vh[b, :, lo:cut], v16[b, :, cut:L].astype(np.float64)], axis=1)
+        for h in range(4):
+            assert np.allclose(o[b, h], _sdpa(q[b, h], K[h // 2], V[h // 2]), rtol=1e-12, atol=1e-13)
+
+
+def test_recent_span_covering_the_sequence_is_plain_fp16_attention():
+    rng = np.random.default_rng(22)
+    k16, kh = _fp16_and_int4(rng)
+    v16, vh = _fp16_and_int4(rng)
+    q = rng.standard_normal((2, 4, 64))
+    lens = [40, 9]
+    o = decode_attention(q, recent_fp16_rows(kh, k16, lens, 64), recent_fp16_rows(vh, v16, lens, 64), lens)
+    ref = decode_attention(q, k16.astype(np.float64), v16.astype(np.float64), lens)
+    assert np.array_equal(o, ref)
+    # and the INT4 form alone differs (the two forms are not the same values)
+    assert not np.allclose(o, decode_attention(q, kh, vh, lens))
+
+
+def test_recent_reads_each_position_from_one_form_only():
+    """Planting garbage in the form a position is not read from changes nothing; planting
+    it in the form it is read from changes the output."""
+    rng = np.random.default_rng(23)
+    k16, kh = _fp16_and_int4(rng)
+    v16, vh = _fp16_and_int4(rng)
+    q = rng.standard_normal((2, 4, 64))
+    lens, R = [40, 23], 10
+    base = decode_attention(q, recent_fp16_rows(kh, k16, lens, R), recent_fp16_rows(vh, v16, lens, R), lens)
+    kh2, k162 = kh.copy(), k16.copy()
+    for b, L in enumerate(lens):
+        kh2[b, :, L - R:L] = 50.0                      # INT4 form of the recent rows
+        k162[b, :, :L - R] = 50.0                      # fp16 form of the older rows
+    same = decode_attention(q, recent_fp16_rows(kh2, k162, lens, R), recent_fp16_rows(vh, v16, lens, R), lens)
+    assert np.array_equal(base, same)
+    k163 = k16.copy()
+    k163[1, :, 23 - R] = 50.0                          # the first recent position of sequence 1
+    moved = decode_attention(q, recent_fp16_rows(kh, k163, lens, R), recent_fp16_rows(vh, v16, lens, R), lens)
+    assert not np.allclose(base[1], moved[1]) and np.array_equal(base[0], moved[0])
