@@ -19,6 +19,8 @@
  *   [INT4-SM]  "LLM长上下文推理优化：用INT4状态机管理KV Cache" (pwwt.cn/news/4219524),
  *              section 5 step 5: attention reads the INT4 data and dequantizes it
  *              inside the operator.
+ *              Section 8.3, first way to cut memory: INT4 for older tokens' K/V,
+ *              FP16 kept for the recent ones.
  *   [LARQL]    "长上下文内存大瘦身：LARQL 四大 KV 缓存引擎原理与横向对比"
  *              (pwwt.cn/news/5725003): window engine (keep only rows inside the
  *              attention horizon) and codec engine (per-head Walsh-Hadamard rotation
@@ -50,6 +52,11 @@
  *   Position p of a sequence lives in slot p when p < S (S = sinks, the first
  *   positions kept for attention sinks, [KV-opt] §3.2), else in slot
  *   S + (p - S) mod (C - S): a ring of C - S slots (S = 0: slot p mod C).
+ * Recent fp16 rows ([INT4-SM] §8.3; INT4 caches with recent = R > 0):
+ *   k_recent, v_recent  [B, Hkv, R, D] fp16, position p in row p mod R.  Every position
+ *   is still quantized into the INT4 buffers when it arrives; the fp16 ring keeps the
+ *   last R positions written, and decode reads positions [len - R, len) from it (and
+ *   older ones from the INT4 codes).
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -61,7 +68,7 @@
 extern "C" {
 #endif
 
-#define KVQ_VERSION 3
+#define KVQ_VERSION 4
 /* Largest batch the decode/append calls accept (per-sequence lengths and positions
  * travel in the kernel argument block). */
 #define KVQ_MAX_BATCH 256
@@ -70,6 +77,8 @@ extern "C" {
  * (KVQ_ERR_UNSUPPORTED otherwise).  They must read zero when a decode call starts;
  * every decode call leaves them zero again. */
 #define KVQ_WS_COUNTER_BYTES 65536
+/* Largest recent fp16 span (kvq_cache_desc.recent). */
+#define KVQ_MAX_RECENT 1024
 
 typedef enum {
   KVQ_INT4_G = 0,      /* group-wise symmetric INT4 ([KV-4bit] §2.1) */
@@ -96,6 +105,9 @@ typedef struct {
   int32_t group_k;   /* INT4 only: K group size (default 64); power of two, 32 <= g <= D */
   int32_t group_v;   /* INT4 only: V group size (default 128); same rule */
   int32_t sinks;     /* S: leading positions kept outside the ring, 0 <= S < C (0: none) */
+  int32_t recent;    /* R: last positions also kept in fp16 and read from there at
+                        decode, 0 <= R <= KVQ_MAX_RECENT (0: none).  INT4 format and
+                        S = 0 only (KVQ_ERR_UNSUPPORTED otherwise). */
 } kvq_cache_desc;
 
 /* Device pointers of one layer's cache (layout above). */
@@ -104,6 +116,8 @@ typedef struct {
   void* k_scales;
   void* v_codes;
   void* v_scales;
+  void* k_recent;    /* R > 0: [B, Hkv, R, D] fp16 rings (kvq_recent_bytes each); */
+  void* v_recent;    /*        R = 0: ignored */
 } kvq_cache;
 
 /* A hipStream_t, passed as an opaque pointer; NULL is the null stream. */
@@ -125,6 +139,9 @@ int32_t kvq_check_desc(const kvq_cache_desc* desc);
  * B*Hkv*C*(D/g)*4; INT8: B*Hkv*C*D and B*Hkv*C*4; codec: B*Hkv*C*D/2 and B*Hkv*C*4. */
 size_t kvq_codes_bytes(const kvq_cache_desc* desc, int32_t kv);
 size_t kvq_scales_bytes(const kvq_cache_desc* desc, int32_t kv);
+/* Bytes of each recent fp16 ring (K and V alike): B*Hkv*R*D*2; 0 if the descriptor is
+ * invalid or R = 0. */
+size_t kvq_recent_bytes(const kvq_cache_desc* desc);
 
 /* Number of sequence splits kvq_decode_attn uses when called with num_splits = 0 for
  * a longest attended span of `span` positions and `q_heads` query heads; 0 if invalid. */
@@ -133,8 +150,8 @@ int32_t kvq_plan_splits(const kvq_cache_desc* desc, int32_t q_heads, int32_t spa
 /* Workspace bytes kvq_decode_attn / kvq_append_decode_attn need for these arguments
  * (num_splits = 0: the library's own plan for the longest attended span at max_len:
  * max_len, or window + min(S, max_len - window) when 0 < window < max_len); 0 if
- * invalid.  Equal to KVQ_WS_COUNTER_BYTES + B * q_heads * nsplit *
- * (D + 2) * 4. */
+ * invalid.  Equal to KVQ_WS_COUNTER_BYTES + B * q_heads * (nsplit + E) * (D + 2) * 4,
+ * where E = ceil(R / 256) partials of the recent fp16 rows (0 without them). */
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t q_heads,
                                   int32_t max_len, int32_t window, int32_t num_splits);
 
@@ -152,7 +169,9 @@ int32_t kvq_codec_codebook(float* levels16, float* thresholds15);
  *   rows than ring slots would overwrite each other within one call).
  * INT4: per group, s = fl32(amax/7) (1 if 0), code = clamp(rne(fl32(x/s)), -7, 7).
  * INT8: s = max(fl32(amax/127), 1e-8), code = clamp(rne(fl32(x/s)), -128, 127).
- * Codec: y = H x / sqrt(D), s = ||x||_2 / sqrt(D), index = #{thresholds < y/s}. */
+ * Codec: y = H x / sqrt(D), s = ||x||_2 / sqrt(D), index = #{thresholds < y/s}.
+ * With recent fp16 rows (R > 0) the positions among the call's last R,
+ * [start_pos + n - R, start_pos + n), are also copied unchanged into the fp16 rings. */
 int32_t kvq_quantize_prefill(const kvq_cache_desc* desc, const kvq_cache* cache,
                              const void* k_f16, const void* v_f16,
                              int32_t start_pos, int32_t n, kvq_stream stream);
@@ -161,7 +180,8 @@ int32_t kvq_quantize_prefill(const kvq_cache_desc* desc, const kvq_cache* cache,
  * ([KV-4bit] §1.1 decode step: append the new token's K/V to the cache).
  *   k_f16, v_f16: device, [B, Hkv, D] fp16 contiguous.
  *   pos: host, [B] positions, each >= 0.
- * Same arithmetic as kvq_quantize_prefill. */
+ * Same arithmetic as kvq_quantize_prefill; with R > 0 the fp16 rows also go to ring row
+ * pos[b] mod R. */
 int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
                    const void* k_f16, const void* v_f16, const int32_t* pos,
                    kvq_stream stream);
@@ -171,7 +191,8 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
  *   out[b, h] = sum_t softmax_t(scale * q[b,h] . x_K[b,kv,t]) * x_V[b,kv,t]
  * with kv = h / (q_heads / Hkv) (GQA), t over [max(0, len_b - window), len_b) and,
  * with a window, the attention sinks [0, min(S, len_b - window)) as well (window = 0:
- * [0, len_b)), x = the dequantized cache values.
+ * [0, len_b)), x = the dequantized cache values; with R > 0, x = the fp16 ring rows for
+ * t >= len_b - R (so they must hold the last R positions written).
  *   q_f16: device, [B, q_heads, D] fp16.  q_heads must be a multiple of Hkv with
  *          q_heads / Hkv in {1, 2, 4, 8}.
  *   lens: host, [B], 1 <= len_b; positions 0..len_b-1 must be in the cache
@@ -188,9 +209,11 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
  *              time need separate workspaces.
  * Split-K: each split writes an unnormalized partial (running max, sum, weighted V) to
  * the workspace; the partials are merged with the log-sum-exp rule by the last split to
- * finish (no second launch) on the matrix-core kernels (INT4 with head_dim 128, V group
- * 128 and no sinks; INT8 with head_dim 128) and, up to 32 splits, on the split-K kernel
- * (every other case); above that by a second kernel. */
+ * finish (no second launch) on the matrix-core kernels (INT4 with head_dim 128 and V
+ * group 128; INT8 with head_dim 128) and, up to 32 splits, on the split-K kernel (every
+ * other case); above that by a second kernel.  R > 0 runs on the INT4 matrix-core kernel
+ * only (KVQ_ERR_UNSUPPORTED for other shapes): E extra workgroups per (b, kv head)
+ * attend the fp16 rows and publish partials like the splits; num_splits + E <= 1024. */
 int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
                         const void* q_f16, int32_t q_heads, const int32_t* lens,
                         int32_t window, float softmax_scale, int32_t num_splits,
@@ -202,9 +225,10 @@ int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
  *   k_f16, v_f16: device, [B, Hkv, D] fp16, the new token's rows (position lens[b] - 1).
  * Every other argument, the workspace rule and the errors are those of kvq_decode_attn
  * (KVQ_ERR_ARG also for null k_f16 / v_f16).  On the INT4 matrix-core kernel (head_dim
- * 128, V group 128, no sinks) and for the codec, the new row is quantized inside the
- * attention kernel, which writes it to the cache and adds it to the softmax without
- * reading it back (one launch per step); the other cases run the append kernel first. */
+ * 128, V group 128) and for the codec, the new row is quantized inside the attention
+ * kernel, which writes it to the cache (and, with R > 0, its fp16 row to the ring) and
+ * adds it to the softmax without reading it back (one launch per step); the other
+ * cases run the append kernel first. */
 int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
                                const void* k_f16, const void* v_f16, const void* q_f16,
                                int32_t q_heads, const int32_t* lens, int32_t window,
@@ -214,7 +238,8 @@ int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cach
 /* Dequantize positions [start_pos, start_pos + n) of K (kv = 0) or V (kv = 1)
  * ([KV-4bit] §2.1 dequantize_4bit_group: code * scale; codec: s * H c[idx] / sqrt(D)).
  *   out: device, [B, Hkv, n, D] fp32.  Requires start_pos >= 0, n >= 1 and at most C - S
- *   of the positions at or after S (the rows must be distinct slots). */
+ *   of the positions at or after S (the rows must be distinct slots).  Reads the INT4
+ *   codes also where recent fp16 rows exist. */
 int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t kv,
                     int32_t start_pos, int32_t n, float* out, kvq_stream stream);
 

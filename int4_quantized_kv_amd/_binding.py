@@ -30,10 +30,12 @@ KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, K
     0, -1, -2, -3, -4, -5
 KVQ_MAX_BATCH = 256
 KVQ_WS_COUNTER_BYTES = 65536
+KVQ_MAX_RECENT = 1024
 
 # Every symbol include/kvq.h declares.
 EXPORTS = (
     "kvq_version", "kvq_status_str", "kvq_check_desc", "kvq_codes_bytes", "kvq_scales_bytes",
+    "kvq_recent_bytes",
     "kvq_plan_splits", "kvq_decode_workspace_bytes", "kvq_codec_codebook",
     "kvq_quantize_prefill", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
     "kvq_dequant",
@@ -44,12 +46,14 @@ class kvq_cache_desc(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("group_k", ctypes.c_int32),
-                ("group_v", ctypes.c_int32), ("sinks", ctypes.c_int32)]
+                ("group_v", ctypes.c_int32), ("sinks", ctypes.c_int32),
+                ("recent", ctypes.c_int32)]
 
 
 class kvq_cache(ctypes.Structure):
     _fields_ = [("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
-                ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p)]
+                ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+                ("k_recent", ctypes.c_void_p), ("v_recent", ctypes.c_void_p)]
 
 
 class KvqError(RuntimeError):
@@ -73,6 +77,7 @@ def _load():
         "kvq_check_desc": (i32, [D]),
         "kvq_codes_bytes": (sz, [D, i32]),
         "kvq_scales_bytes": (sz, [D, i32]),
+        "kvq_recent_bytes": (sz, [D]),
         "kvq_plan_splits": (i32, [D, i32, i32]),
         "kvq_decode_workspace_bytes": (sz, [D, i32, i32, i32, i32]),
         "kvq_codec_codebook": (i32, [P(f32), P(f32)]),
@@ -105,9 +110,10 @@ def _check(status, where):
     return status
 
 
-def make_desc(fmt, batch, kv_heads, head_dim, capacity, group_k=64, group_v=128, sinks=0):
+def make_desc(fmt, batch, kv_heads, head_dim, capacity, group_k=64, group_v=128, sinks=0,
+              recent=0):
     f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
-    return kvq_cache_desc(f, batch, kv_heads, head_dim, capacity, group_k, group_v, sinks)
+    return kvq_cache_desc(f, batch, kv_heads, head_dim, capacity, group_k, group_v, sinks, recent)
 
 
 def _ptr(t, dtype=None, name="tensor"):
@@ -153,6 +159,10 @@ def kvq_codes_bytes(desc, kv):
 
 def kvq_scales_bytes(desc, kv):
     return LIB.kvq_scales_bytes(ctypes.byref(desc), kv)
+
+
+def kvq_recent_bytes(desc):
+    return LIB.kvq_recent_bytes(ctypes.byref(desc))
 
 
 def kvq_plan_splits(desc, q_heads, span):
@@ -245,10 +255,17 @@ class DeviceCache:
         self.k_scales = torch.zeros(nb[1] // 4, dtype=torch.float32, device=device)
         self.v_codes = torch.zeros(nb[2], dtype=torch.uint8, device=device)
         self.v_scales = torch.zeros(nb[3] // 4, dtype=torch.float32, device=device)
+        # recent fp16 rings (INT4 caches with desc.recent > 0), else absent
+        nr = kvq_recent_bytes(desc) // 2
+        self.k_recent = torch.zeros(nr, dtype=torch.float16, device=device) if nr else None
+        self.v_recent = torch.zeros(nr, dtype=torch.float16, device=device) if nr else None
         self.c = kvq_cache(self.k_codes.data_ptr(), self.k_scales.data_ptr(),
-                           self.v_codes.data_ptr(), self.v_scales.data_ptr())
+                           self.v_codes.data_ptr(), self.v_scales.data_ptr(),
+                           self.k_recent.data_ptr() if nr else None,
+                           self.v_recent.data_ptr() if nr else None)
 
     @property
     def nbytes(self):
         return sum(t.numel() * t.element_size()
-                   for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales))
+                   for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales,
+                             self.k_recent, self.v_recent) if t is not None)

@@ -16,7 +16,10 @@ int32_t check_desc(const kvq_cache_desc* d) {
   if (d->format < KVQ_INT4_G || d->format > KVQ_WHT_LM4) return KVQ_ERR_ARG;
   if (d->batch < 1 || d->kv_heads < 1 || d->head_dim < 1 || d->capacity < 1)
     return KVQ_ERR_ARG;
-  if (d->sinks < 0 || d->sinks >= d->capacity) return KVQ_ERR_ARG;
+  if (d->sinks < 0 || d->sinks >= d->capacity || d->recent < 0) return KVQ_ERR_ARG;
+  // recent fp16 rows: INT4 only, without sinks, at most KVQ_MAX_RECENT
+  if (d->recent > 0 && (d->format != KVQ_INT4_G || d->sinks > 0 || d->recent > KVQ_MAX_RECENT))
+    return KVQ_ERR_UNSUPPORTED;
   if (d->batch > KVQ_MAX_BATCH) return KVQ_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   if (d->format == KVQ_INT4_G) {
@@ -31,9 +34,13 @@ int32_t check_desc(const kvq_cache_desc* d) {
   return KVQ_OK;
 }
 
-bool cache_ok(const kvq_cache* c) {
-  return c && c->k_codes && c->k_scales && c->v_codes && c->v_scales;
+bool cache_ok(const kvq_cache_desc* d, const kvq_cache* c) {
+  return c && c->k_codes && c->k_scales && c->v_codes && c->v_scales &&
+         (d->recent == 0 || (c->k_recent && c->v_recent));
 }
+
+// Workgroups per (b, kv head) that attend the recent fp16 rows (up to 256 rows each).
+int32_t recent_workgroups(const kvq_cache_desc* d) { return (d->recent + 255) / 256; }
 
 int32_t scales_per_row(const kvq_cache_desc* d, int32_t kv) {
   if (d->format == KVQ_INT4_G) return d->head_dim / (kv ? d->group_v : d->group_k);
@@ -59,6 +66,11 @@ int32_t quant_common(const kvq_cache_desc* desc, const kvq_cache* cache, const v
   a.gv = desc->group_v;
   a.rows = desc->batch * desc->kv_heads * n;
   a.map = map;
+  if (desc->recent > 0) {
+    a.k_recent = static_cast<uint16_t*>(cache->k_recent);
+    a.v_recent = static_cast<uint16_t*>(cache->v_recent);
+    a.recent = desc->recent;
+  }
   if (desc->format == KVQ_WHT_LM4) {
     float lv[16];
     codec_codebook(lv, a.thr);
@@ -138,6 +150,11 @@ size_t kvq_scales_bytes(const kvq_cache_desc* d, int32_t kv) {
   return rows * scales_per_row(d, kv) * sizeof(float);
 }
 
+size_t kvq_recent_bytes(const kvq_cache_desc* d) {
+  if (check_desc(d) != KVQ_OK) return 0;
+  return (size_t)d->batch * d->kv_heads * d->recent * d->head_dim * sizeof(uint16_t);
+}
+
 int32_t kvq_plan_splits(const kvq_cache_desc* d, int32_t q_heads, int32_t span) {
   if (check_desc(d) != KVQ_OK || q_heads < 1 || q_heads % d->kv_heads || span < 1) return 0;
   return plan_splits(d, q_heads / d->kv_heads, span);
@@ -150,7 +167,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* d, int32_t q_heads, int3
     return 0;
   const int32_t span = attended_span(max_len, window, d->sinks);
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(d, q_heads, span);
-  return partials_offset() + partials_bytes(d->batch, q_heads, ns, d->head_dim);
+  return partials_offset() + partials_bytes(d->batch, q_heads, ns + recent_workgroups(d), d->head_dim);
 }
 
 int32_t kvq_codec_codebook(float* levels16, float* thresholds15) {
@@ -164,7 +181,7 @@ int32_t kvq_quantize_prefill(const kvq_cache_desc* desc, const kvq_cache* cache,
                              int32_t n, kvq_stream stream) {
   const int32_t st = check_desc(desc);
   if (st != KVQ_OK) return st;
-  if (!cache_ok(cache) || !k_f16 || !v_f16 || start_pos < 0 || n < 1) return KVQ_ERR_ARG;
+  if (!cache_ok(desc, cache) || !k_f16 || !v_f16 || start_pos < 0 || n < 1) return KVQ_ERR_ARG;
   if (!rows_fit(desc, start_pos, n)) return KVQ_ERR_CAPACITY;
   if ((uint64_t)desc->batch * desc->kv_heads * n * (desc->head_dim / 8) >= (1ull << 31))
     return KVQ_ERR_UNSUPPORTED;
@@ -183,7 +200,7 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache, const voi
                    const void* v_f16, const int32_t* pos, kvq_stream stream) {
   const int32_t st = check_desc(desc);
   if (st != KVQ_OK) return st;
-  if (!cache_ok(cache) || !k_f16 || !v_f16 || !pos) return KVQ_ERR_ARG;
+  if (!cache_ok(desc, cache) || !k_f16 || !v_f16 || !pos) return KVQ_ERR_ARG;
   SlotMap map;
   std::memset(&map, 0, sizeof(map));
   for (int32_t b = 0; b < desc->batch; ++b) {
@@ -208,7 +225,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
                       hipStream_t stream) {
   const int32_t st = check_desc(desc);
   if (st != KVQ_OK) return st;
-  if (!cache_ok(cache) || !q_f16 || !lens || !out || window < 0 || num_splits < 0 ||
+  if (!cache_ok(desc, cache) || !q_f16 || !lens || !out || window < 0 || num_splits < 0 ||
       q_heads < 1 || !std::isfinite(softmax_scale) || softmax_scale < 0.0f)
     return KVQ_ERR_ARG;
   if (q_heads % desc->kv_heads) return KVQ_ERR_ARG;
@@ -217,9 +234,14 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   if ((int64_t)desc->batch * desc->kv_heads > max_units()) return KVQ_ERR_UNSUPPORTED;
   const int32_t span = check_lens(desc, lens, window);
   if (span < 0) return span;
+  // recent fp16 rows: the INT4 matrix-core kernel only (its extra workgroups attend them)
+  if (desc->recent > 0 && !mfma_int4_eligible(desc->head_dim, desc->group_k, desc->group_v,
+                                              desc->capacity, G))
+    return KVQ_ERR_UNSUPPORTED;
+  const int32_t E = recent_workgroups(desc);
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(desc, q_heads, span);
-  if (ns < 1 || ns > MAX_SPLITS) return KVQ_ERR_ARG;
-  const size_t need = partials_offset() + partials_bytes(desc->batch, q_heads, ns, desc->head_dim);
+  if (ns < 1 || ns + E > MAX_SPLITS) return KVQ_ERR_ARG;
+  const size_t need = partials_offset() + partials_bytes(desc->batch, q_heads, ns + E, desc->head_dim);
   if (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16)
     return KVQ_ERR_WORKSPACE;
 
@@ -232,7 +254,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   a.q = static_cast<const uint16_t*>(q_f16);
   a.counters = static_cast<uint32_t*>(workspace);
   a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + partials_offset());
-  a.ws_ml = a.ws_acc + (size_t)desc->batch * q_heads * ns * desc->head_dim;
+  a.ws_ml = a.ws_acc + (size_t)desc->batch * q_heads * (ns + E) * desc->head_dim;
   a.out = out;
   a.B = desc->batch;
   a.Hkv = desc->kv_heads;
@@ -244,6 +266,12 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   a.window = window;
   a.nsplit = ns;
   a.sinks = desc->sinks;
+  if (desc->recent > 0) {
+    a.k_recent = static_cast<uint16_t*>(cache->k_recent);
+    a.v_recent = static_cast<uint16_t*>(cache->v_recent);
+    a.recent = desc->recent;
+    a.recent_wg = E;
+  }
   const float scale = softmax_scale != 0.0f ? softmax_scale
                                             : 1.0f / std::sqrt((float)desc->head_dim);
   a.qscale = scale * 1.4426950408889634f;  // log2(e): scores in base-2 units
@@ -296,7 +324,7 @@ int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t 
                     int32_t start_pos, int32_t n, float* out, kvq_stream stream) {
   const int32_t st = check_desc(desc);
   if (st != KVQ_OK) return st;
-  if (!cache_ok(cache) || !out || (kv != 0 && kv != 1) || start_pos < 0 || n < 1)
+  if (!cache_ok(desc, cache) || !out || (kv != 0 && kv != 1) || start_pos < 0 || n < 1)
     return KVQ_ERR_ARG;
   if (!rows_fit(desc, start_pos, n)) return KVQ_ERR_CAPACITY;
   if ((uint64_t)desc->batch * desc->kv_heads * n * (desc->head_dim / 8) >= (1ull << 31))

@@ -910,7 +910,95 @@ __device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewLds*
 // both carrying the whole q; 16-position tiles, one position set).
 // SK: the cache keeps attention-sink slots ahead of its ring (a separate instance, so
 // that the common case carries no sink arithmetic).
-template <int G, int NGK, bool I8, bool SK>
+// ---------------------------------------------------------------------------------------
+// Recent fp16 rows ("LLM长上下文推理优化：用INT4状态机管理KV Cache", pwwt.cn/news/4219524,
+// section 8.3: older tokens in INT4, recent ones in FP16).  Positions [rlo, len),
+// rlo = max(window start, len - recent), are read from the fp16 rings instead of the
+// codes, by recent_wg extra workgroups per (b, kv head) after the splits: workgroup rw
+// takes a chunk of them and its wave w the rows t = w, w + WAVES, ... of the chunk.
+// Lane l holds dims 2l, 2l + 1 of a row; a row's G scores are wave sums (DPP), so each
+// head's running (max, sum) is wave-uniform and the lane keeps its two dims of the
+// weighted V sum.  The result is the wave's combine entry, in the same form as a tile
+// wave's (max in base-2 units), so the combine, the partial, the arrival and the merge
+// are the splits' own.  With the append fused, position len - 1 is the new token's row
+// (read from the caller's buffer), which the first extra workgroup also stores into its
+// ring row (no workgroup of the launch reads that row of the ring: the attended
+// positions before len - 1 are the recent - 1 others).
+template <int G>
+__device__ __forceinline__ void recent_entry(const DecodeArgs& a, int unit, int len, int lo_pos,
+                                             int rw, int wave, int lane, bool fused,
+                                             const uint8_t* s_q, float* s_o, float* s_m,
+                                             float* s_l, int ors, int ne) {
+  const int R = a.recent;
+  const int rlo = max(lo_pos, len - R);
+  const int nrow = len - rlo;
+  const int rchunk = (nrow + a.recent_wg - 1) / a.recent_wg;
+  const int r0 = rlo + rw * rchunk, r1 = min(len, r0 + rchunk);
+  const uint32_t* kring = reinterpret_cast<const uint32_t*>(a.k_recent) + (size_t)unit * R * (HD / 2) + lane;
+  const uint32_t* vring = reinterpret_cast<const uint32_t*>(a.v_recent) + (size_t)unit * R * (HD / 2) + lane;
+  const uint32_t* knew = reinterpret_cast<const uint32_t*>(a.k_new) + (size_t)unit * (HD / 2) + lane;
+  const uint32_t* vnew = reinterpret_cast<const uint32_t*>(a.v_new) + (size_t)unit * (HD / 2) + lane;
+  if (fused && rw == 0 && wave == 0) {
+    const size_t o = (size_t)((len - 1) % R) * (HD / 2);
+    const uint32_t kw = *knew, vw = *vnew;
+    reinterpret_cast<uint32_t*>(a.k_recent)[(size_t)unit * R * (HD / 2) + o + lane] = kw;
+    reinterpret_cast<uint32_t*>(a.v_recent)[(size_t)unit * R * (HD / 2) + o + lane] = vw;
+  }
+  float q0[G], q1[G], m[G], l[G], o0[G], o1[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const f16x2 qq = __builtin_bit_cast(f16x2, reinterpret_cast<const uint32_t*>(s_q + h * 2 * HD)[lane]);
+    q0[h] = (float)qq[0];
+    q1[h] = (float)qq[1];
+    m[h] = empty_max(a.qscale) * a.qscale;
+    l[h] = 0.0f;
+    o0[h] = 0.0f;
+    o1[h] = 0.0f;
+  }
+  constexpr int RB = 4;   // rows per wave whose loads are issued together
+  for (int t0 = r0 + wave; t0 < r1; t0 += RB * WAVES) {
+    uint32_t kw[RB], vw[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int t = t0 + i * WAVES;
+      if (t < r1) {   // (uniform)
+        const bool nw = fused && t == len - 1;
+        const size_t o = (size_t)(t % R) * (HD / 2);
+        kw[i] = nw ? *knew : kring[o];
+        vw[i] = nw ? *vnew : vring[o];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if (t0 + i * WAVES >= r1) break;   // (uniform)
+      const f16x2 kk = __builtin_bit_cast(f16x2, kw[i]), vv = __builtin_bit_cast(f16x2, vw[i]);
+      const float k0 = (float)kk[0], k1 = (float)kk[1], v0 = (float)vv[0], v1 = (float)vv[1];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float part = lane_group_sum<32>(__builtin_fmaf(q0[h], k0, q1[h] * k1));
+        const float z = (readlane_f(part, 0) + readlane_f(part, 32)) * a.qscale;
+        const float mn = fmaxf(m[h], z);
+        const float f = fast_exp2(m[h] - mn), p = fast_exp2(z - mn);
+        l[h] = __builtin_fmaf(l[h], f, p);
+        o0[h] = __builtin_fmaf(o0[h], f, p * v0);
+        o1[h] = __builtin_fmaf(o1[h], f, p * v1);
+        m[h] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int d = 2 * lane;
+    s_o[h * ors + d + (d >> 5)] = o0[h];
+    s_o[h * ors + d + 1 + ((d + 1) >> 5)] = o1[h];
+    if (lane == 0) {
+      s_m[h * ne + wave] = m[h];
+      s_l[h * ne + wave] = l[h];
+    }
+  }
+}
+
+template <int G, int NGK, bool I8, bool SK, bool RC = false>
 __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   using L = std::conditional_t<I8, Slot8, Slot<NGK>>;
   constexpr int TL = I8 ? TILE8 : TILE;       // positions per tile
@@ -960,7 +1048,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // (INT4 only: the INT8 step is appended by the quantize kernel first)
   const bool fused = !I8 && a.k_new != nullptr;
   const bool appender = fused && sp == 0;
-  const int pt = fused ? len - 1 : len;                 // tiles cover [lo_pos, pt)
+  // tiles cover [lo_pos, pt); with recent fp16 rows, only the positions before them
+  const int pt = RC ? max(lo_pos, len - a.recent) : (fused ? len - 1 : len);
 
   // ---- tile schedule: split sp covers positions [ps, pe) of [lo_pos, pt), nts tiles
   // of 32 positions.  Wave w starts with tiles w and w + WAVES; every further tile is
@@ -1207,7 +1296,12 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     l_run = __builtin_fmaf(l_run, f0, lo_run * f1);
     st.m = mx;
   }
-  if (rr < G * NGK && qgrp == 0 && cset == 0) {
+  const bool recent_wg = RC && sp >= a.nsplit;   // (this workgroup attends the fp16 rows)
+  if (recent_wg) {
+    if constexpr (RC)
+      recent_entry<G>(a, unit, len, lo_pos, sp - a.nsplit, wave, lane, fused, qstage, s_o, s_m,
+                      s_l, ORS, NE);
+  } else if (rr < G * NGK && qgrp == 0 && cset == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
@@ -1219,7 +1313,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  const int nps = a.nsplit;                                     // partials per query head
+  const int nps = a.nsplit + (RC ? a.recent_wg : 0);           // partials per query head
   const size_t pbase = (size_t)(b * a.Hq + kvh * G) * nps;     // slot of (head 0, split 0)
   for (int idx = threadIdx.x; idx < G * HD; idx += NT) {
     const int h = idx / HD, d = idx % HD;
@@ -1240,8 +1334,9 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < NE; ++w)   // entry w: wave w's, in that wave's ring
       ow[w] = reinterpret_cast<const float*>(smem + w * NB * L::BYTES)[h * ORS + opad(d)];
-    const float mn = appender ? s_new.m[h] : NEG_INF;
-    const float on = appender ? s_new.o[d] : 0.0f;
+    // (with recent fp16 rows the new row is attended among them, not here)
+    const float mn = appender && !RC ? s_new.m[h] : NEG_INF;
+    const float on = appender && !RC ? s_new.o[d] : 0.0f;
     float M = mn;
 #pragma unroll
     for (int w = 0; w < NE; ++w) M = fmaxf(M, mw[w]);
@@ -1282,7 +1377,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   if (threadIdx.x == 0)
     s_last = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  const int np = a.nsplit;                               // partials to merge
+  const int np = nps;                                    // partials to merge
   if (s_last != np - 1) return;
 
   // ---- the last arrival merges the np partials of its G heads with the log-sum-exp
@@ -1375,22 +1470,24 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int G, bool SK>
+template <int G, bool SK, bool RC>
 hipError_t launch_gs(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.nsplit, a.Hkv, a.B);
+  const dim3 grid(a.nsplit + (RC ? a.recent_wg : 0), a.Hkv, a.B);
   switch (HD / a.gk) {
-    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1, false, SK>, grid, dim3(NT), a, s);
-    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2, false, SK>, grid, dim3(NT), a, s);
+    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1, false, SK, RC>, grid, dim3(NT), a, s);
+    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2, false, SK, RC>, grid, dim3(NT), a, s);
     case 4:
-      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4, false, SK>, grid, dim3(NT), a, s);
+      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4, false, SK, RC>, grid, dim3(NT), a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
+// (sinks and recent fp16 rows are not combined: the library rejects such caches)
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  return a.sinks ? launch_gs<G, true>(a, s) : launch_gs<G, false>(a, s);
+  if (a.recent) return a.sinks ? hipErrorInvalidValue : launch_gs<G, false, true>(a, s);
+  return a.sinks ? launch_gs<G, true, false>(a, s) : launch_gs<G, false, false>(a, s);
 }
 
 template <bool SK>

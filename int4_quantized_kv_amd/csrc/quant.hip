@@ -84,6 +84,13 @@ __device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
         if (slot >= cap) slot -= cap;
       }
       const size_t drow = row0 + slot;
+      if (!INT8 && a.recent) {   // (uniform) the call's last `recent` positions also
+        const int p = p0 + t;    // go to the fp16 ring, row p mod recent, unchanged
+        if (p >= p0 + a.map.n - a.recent) {
+          uint4* ring = reinterpret_cast<uint4*>(isv ? a.v_recent : a.k_recent);
+          ring[(((size_t)bh * a.recent + p % a.recent) << lsh) + c] = raw[u];
+        }
+      }
       if (INT8) {
         uint32_t w0 = 0, w1 = 0;
 #pragma unroll

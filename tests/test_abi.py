@@ -23,14 +23,14 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(kvq.EXPORTS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (kvq_\w+)", out))
     for n in names:
         assert n in exported, n
-    assert kvq.kvq_version() == 3
+    assert kvq.kvq_version() == 4
 
 
 def test_status_strings():
@@ -160,6 +160,43 @@ def test_sinks_validation_and_workspace():
     assert ws == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * kvq.kvq_plan_splits(d, 8, span) * 130 * 4
     _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_decode_attn, d, c, FAKE, 8, [30, 10], 17, 0.0, 0, FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_decode_attn, d, c, FAKE, 8, [30, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
+
+
+def test_recent_validation_and_workspace():
+    """Recent fp16 rows: INT4 only, not with sinks, at most KVQ_MAX_RECENT; the rings are
+    required when R > 0; decode needs the matrix-core INT4 kernel; the workspace holds
+    ceil(R / 256) more partials per query head."""
+    ok = kvq.make_desc("int4", 2, 4, 128, 64, recent=128)
+    assert kvq.kvq_check_desc(ok) == 0
+    assert kvq.kvq_recent_bytes(ok) == 2 * 4 * 128 * 128 * 2
+    assert kvq.kvq_recent_bytes(kvq.make_desc("int4", 2, 4, 128, 64)) == 0
+    assert kvq.kvq_check_desc(kvq.make_desc("int4", 2, 4, 128, 64, recent=-1)) == kvq.KVQ_ERR_ARG
+    for bad in (kvq.make_desc("int4", 2, 4, 128, 64, recent=kvq.KVQ_MAX_RECENT + 1),
+                kvq.make_desc("int8", 2, 4, 128, 64, recent=16),
+                kvq.make_desc("codec", 2, 4, 128, 64, recent=16),
+                kvq.make_desc("int4", 2, 4, 128, 64, sinks=4, recent=16)):
+        assert kvq.kvq_check_desc(bad) == kvq.KVQ_ERR_UNSUPPORTED
+        assert kvq.kvq_recent_bytes(bad) == 0
+    assert kvq.kvq_check_desc(kvq.make_desc("int4", 2, 4, 128, 64, recent=kvq.KVQ_MAX_RECENT)) == 0
+    for R, E in ((1, 1), (128, 1), (256, 1), (257, 2), (1024, 4)):
+        d = kvq.make_desc("int4", 2, 4, 128, 64, recent=R)
+        ns = kvq.kvq_plan_splits(d, 8, 60)
+        assert kvq.kvq_decode_workspace_bytes(d, 8, 60, 0) == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * (ns + E) * 130 * 4
+        assert kvq.kvq_decode_workspace_bytes(d, 8, 60, 0, 7) == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * (7 + E) * 130 * 4
+    no_rings = _cache()
+    rings = kvq.kvq_cache(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_quantize_prefill, ok, no_rings, FAKE, FAKE, 0, 10, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_append, ok, no_rings, FAKE, FAKE, [3, 4], 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, ok, no_rings, FAKE, 8, [30, 10], 0, 0.0, 0, FAKE, FAKE, 1 << 30, 0)
+    # shapes the matrix-core kernel does not take
+    for d, hq in ((kvq.make_desc("int4", 2, 4, 64, 64, 32, 64, recent=16), 8),
+                  (kvq.make_desc("int4", 2, 4, 128, 64, 64, 64, recent=16), 8),
+                  (kvq.make_desc("int4", 2, 4, 128, 64, 32, 128, recent=16), 32)):
+        _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_decode_attn, d, rings, FAKE, hq, [30, 10], 0, 0.0, 0, FAKE,
+                FAKE, 1 << 30, 0)
+    # splits plus the recent workgroups stay within 1024 partials
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, ok, rings, FAKE, 8, [30, 10], 0, 0.0, 1024, FAKE, FAKE,
+            1 << 30, 0)
 
 
 def test_split_plan():
