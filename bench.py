@@ -24,6 +24,8 @@ the same form; the default run is the headline above):
                  1024-row window ring, 5 global), append at position 4096 then attend
   llama8b-sinks  the headline shape with every layer windowed: a 4096-row ring plus 4
                  attention-sink positions, append at position 8192 then attend 4100 rows
+  llama8b-recent the headline step with the last 128 positions also kept, and read, in
+                 fp16 (8065 rows from the INT4 codes, 128 from the fp16 rings)
   dequant        kvq_dequant of K and V of 8 Llama-3-8B-shaped layer caches to fp32
 """
 import argparse
@@ -55,6 +57,7 @@ OTHER_TRAFFIC = {
     "gemma-codec": ("profiles/decode_splitk_codec_gemma3_4b_b4_traffic.md",
                     ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
     "llama8b-sinks": ("profiles/decode_int4_mfma_llama8b_window4k_sinks4_traffic.md", KERNEL_SOURCES),
+    "llama8b-recent": ("profiles/decode_int4_mfma_llama8b_ctx8k_recent128_traffic.md", KERNEL_SOURCES),
 }
 
 
@@ -63,7 +66,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--workload", default="llama8b",
                    choices=["llama8b", "mha7b-prefill", "mha7b-decode", "ctx128k-int4",
-                            "ctx128k-int8", "gemma-codec", "llama8b-sinks", "dequant"])
+                            "ctx128k-int8", "gemma-codec", "llama8b-sinks", "llama8b-recent",
+                            "dequant"])
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=None, help="override the layer count (debug only)")
@@ -446,6 +450,7 @@ DECODE_MODES = {   # workload id, cache format
     "ctx128k-int8": (5, "int8"),
     "gemma-codec": (4, "codec"),
     "llama8b-sinks": (6, "int4"),
+    "llama8b-recent": (7, "int4"),
 }
 
 
@@ -480,7 +485,7 @@ def bench_decode(args):
         lay.W = w.layer_window(li)
         ns = w.sinks if lay.W else 0
         cap = lay.W + ns if lay.W else L
-        lay.desc = kvq.make_desc(fmt, B, Hkv, D, cap, w.group_k, w.group_v, sinks=ns)
+        lay.desc = kvq.make_desc(fmt, B, Hkv, D, cap, w.group_k, w.group_v, sinks=ns, recent=w.recent)
         k, v, q, kn, vn = synth.layer_inputs(w, li, dev)
         lay.dc = kvq.DeviceCache(lay.desc, dev)
         if ns:                        # the sink positions, in their own slots
@@ -499,11 +504,18 @@ def bench_decode(args):
         # The attention call alone (for the roofline) reads every row of the horizon.
         rows = attended_rows(L, lay.W, ns)
         qo = B * Hq * D * 2 + B * Hq * D * 4
-        attend_bytes += B * Hkv * rows * rb + qo
-        if w.append:
-            step_bytes += B * Hkv * ((rows - 1) * rb + rb + 2 * D * 2) + qo
+        # rows read in fp16 (recent) cost 2 * D * 2 bytes each instead of rb; the
+        # appended row is quantized (rb written) and, with recent rows, also written in
+        # fp16 to its ring row
+        nr = min(rows, w.recent)
+        f16row = 2 * D * 2
+        attend_bytes += B * Hkv * ((rows - nr) * rb + nr * f16row) + qo
+        if w.append and nr:   # nr - 1 ring rows and the new row read; rb + f16row written
+            step_bytes += B * Hkv * ((rows - nr) * rb + nr * f16row + rb + f16row) + qo
+        elif w.append:        # rows - 1 cached rows and the new row read; rb written
+            step_bytes += B * Hkv * ((rows - 1) * rb + f16row + rb) + qo
         else:
-            step_bytes += B * Hkv * rows * rb + qo
+            step_bytes += B * Hkv * ((rows - nr) * rb + nr * f16row) + qo
         layers.append(lay)
     torch.cuda.synchronize()
     ws = torch.zeros(ws_need // 4 + 4, dtype=torch.float32, device=dev)
@@ -534,6 +546,9 @@ def bench_decode(args):
         kern = "kvq_decode_attn: decode_int4_mfma_kernel (splits merged in-kernel)"
         if w.sinks and w.window_layers:
             kern = "kvq_decode_attn: decode_int4_mfma_kernel, sink instance (splits merged in-kernel)"
+        if w.recent:
+            kern = ("kvq_decode_attn: decode_int4_mfma_kernel, recent-row instance (splits and the "
+                    "fp16-row workgroup merged in-kernel)")
     elif fmt == "int8" and D == 128:
         kern = "kvq_decode_attn: decode_int4_mfma_kernel, INT8 tiles (splits merged in-kernel)"
     else:
@@ -543,6 +558,7 @@ def bench_decode(args):
     cfg = {"workload": w.name, "format": fmt, "layers": nl, "batch": B, "q_heads": Hq,
            "kv_heads": Hkv, "head_dim": D, "context": L, "append": w.append,
            "window_layers": min(nl, w.window_layers), "window": w.window, "sinks": w.sinks,
+           "recent_fp16": w.recent,
            "launch": "eager" if args.eager else "hip-graph",
            "num_splits": kvq.kvq_plan_splits(layers[-1].desc, Hq,
                                              attended_rows(L, layers[-1].W, layers[-1].desc.sinks))}
@@ -550,7 +566,8 @@ def bench_decode(args):
     names = {"mha7b-decode": "MHA-7B shape, 20K ctx, B 8", "ctx128k-int4": "128K ctx, B 1, INT4",
              "ctx128k-int8": "128K ctx, B 1, INT8 per-token",
              "gemma-codec": "Gemma-3-4B shape, WHT+Lloyd-Max codec, window 1024 x29 + global x5",
-             "llama8b-sinks": "Llama-3-8B shape, 8K ctx, B 8, window 4096 + 4 sinks"}
+             "llama8b-sinks": "Llama-3-8B shape, 8K ctx, B 8, window 4096 + 4 sinks",
+             "llama8b-recent": "Llama-3-8B shape, 8K ctx, B 8, last 128 positions in fp16"}
     return _line(args, f"decode step: effective KV GB/s ({names[args.workload]})", gbs, ms_step, cfg,
                  roof, cpu, {"tok_per_s": round(B / (ms_step * 1e-3), 1), "bytes_per_step": step_bytes,
                              "wall_s_timed": round(wall, 4)})
@@ -636,6 +653,7 @@ def bench_dequant(args):
 
 OTHER = {"mha7b-prefill": bench_prefill, "mha7b-decode": bench_decode, "ctx128k-int4": bench_decode,
          "ctx128k-int8": bench_decode, "gemma-codec": bench_decode, "llama8b-sinks": bench_decode,
+         "llama8b-recent": bench_decode,
          "dequant": bench_dequant}
 
 
@@ -693,10 +711,19 @@ def cpu_baseline_decode(w, fmt, seconds, L):
                             _oracle_rows(fmt, vn[b, h][None], w.group_k, w.group_v, 1)
                         kh = np.concatenate([kh, nkdq(nkc)])
                         vh = np.concatenate([vh, nvdq(nvc)])
+                    if w.recent:   # the last positions are read at their fp16 values
+                        k16 = np.concatenate([kr, kn[b, h][None]]) if w.append else kr
+                        v16 = np.concatenate([vr, vn[b, h][None]]) if w.append else vr
+                        kh = attention.recent_fp16_rows(kh[None, None], k16[None, None], [kh.shape[0]], w.recent)[0, 0]
+                        vh = attention.recent_fp16_rows(vh[None, None], v16[None, None], [vh.shape[0]], w.recent)[0, 0]
                     attention.decode_attention(qq[None], kh[None, None], vh[None, None], [kh.shape[0]])
                     dt += time.perf_counter() - t0
                 units += 1
-                nbytes += rows * rb + G * D * 6 + (4 * D if w.append else 0)
+                nr = min(rows, w.recent)     # rows read in fp16 (4 D bytes each)
+                if w.append and nr:
+                    nbytes += (rows - nr) * rb + nr * 4 * D + rb + 4 * D + G * D * 6
+                else:
+                    nbytes += rows * rb + G * D * 6 + (4 * D if w.append else 0)
         layer += 1
         del k, v
     full = w.batch * w.kv_heads * w.layers

@@ -150,8 +150,8 @@ int32_t kvq_plan_splits(const kvq_cache_desc* desc, int32_t q_heads, int32_t spa
 /* Workspace bytes kvq_decode_attn / kvq_append_decode_attn need for these arguments
  * (num_splits = 0: the library's own plan for the longest attended span at max_len:
  * max_len, or window + min(S, max_len - window) when 0 < window < max_len); 0 if
- * invalid.  Equal to KVQ_WS_COUNTER_BYTES + B * q_heads * (nsplit + E) * (D + 2) * 4,
- * where E = ceil(R / 256) partials of the recent fp16 rows (0 without them). */
+ * invalid.  Equal to KVQ_WS_COUNTER_BYTES + B * q_heads * nsplit *
+ * (D + 2) * 4. */
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t q_heads,
                                   int32_t max_len, int32_t window, int32_t num_splits);
 
@@ -212,8 +212,8 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
  * finish (no second launch) on the matrix-core kernels (INT4 with head_dim 128 and V
  * group 128; INT8 with head_dim 128) and, up to 32 splits, on the split-K kernel (every
  * other case); above that by a second kernel.  R > 0 runs on the INT4 matrix-core kernel
- * only (KVQ_ERR_UNSUPPORTED for other shapes): E extra workgroups per (b, kv head)
- * attend the fp16 rows and publish partials like the splits; num_splits + E <= 1024. */
+ * only (KVQ_ERR_UNSUPPORTED for other shapes), whose splits each attend a share of the
+ * fp16 rows besides their share of the codes. */
 int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
                         const void* q_f16, int32_t q_heads, const int32_t* lens,
                         int32_t window, float softmax_scale, int32_t num_splits,

@@ -39,9 +39,6 @@ bool cache_ok(const kvq_cache_desc* d, const kvq_cache* c) {
          (d->recent == 0 || (c->k_recent && c->v_recent));
 }
 
-// Workgroups per (b, kv head) that attend the recent fp16 rows (up to 256 rows each).
-int32_t recent_workgroups(const kvq_cache_desc* d) { return (d->recent + 255) / 256; }
-
 int32_t scales_per_row(const kvq_cache_desc* d, int32_t kv) {
   if (d->format == KVQ_INT4_G) return d->head_dim / (kv ? d->group_v : d->group_k);
   return 1;
@@ -167,7 +164,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* d, int32_t q_heads, int3
     return 0;
   const int32_t span = attended_span(max_len, window, d->sinks);
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(d, q_heads, span);
-  return partials_offset() + partials_bytes(d->batch, q_heads, ns + recent_workgroups(d), d->head_dim);
+  return partials_offset() + partials_bytes(d->batch, q_heads, ns, d->head_dim);
 }
 
 int32_t kvq_codec_codebook(float* levels16, float* thresholds15) {
@@ -234,14 +231,13 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   if ((int64_t)desc->batch * desc->kv_heads > max_units()) return KVQ_ERR_UNSUPPORTED;
   const int32_t span = check_lens(desc, lens, window);
   if (span < 0) return span;
-  // recent fp16 rows: the INT4 matrix-core kernel only (its extra workgroups attend them)
+  // recent fp16 rows: the INT4 matrix-core kernel only (its splits share them out)
   if (desc->recent > 0 && !mfma_int4_eligible(desc->head_dim, desc->group_k, desc->group_v,
                                               desc->capacity, G))
     return KVQ_ERR_UNSUPPORTED;
-  const int32_t E = recent_workgroups(desc);
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(desc, q_heads, span);
-  if (ns < 1 || ns + E > MAX_SPLITS) return KVQ_ERR_ARG;
-  const size_t need = partials_offset() + partials_bytes(desc->batch, q_heads, ns + E, desc->head_dim);
+  if (ns < 1 || ns > MAX_SPLITS) return KVQ_ERR_ARG;
+  const size_t need = partials_offset() + partials_bytes(desc->batch, q_heads, ns, desc->head_dim);
   if (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16)
     return KVQ_ERR_WORKSPACE;
 
@@ -254,7 +250,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   a.q = static_cast<const uint16_t*>(q_f16);
   a.counters = static_cast<uint32_t*>(workspace);
   a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + partials_offset());
-  a.ws_ml = a.ws_acc + (size_t)desc->batch * q_heads * (ns + E) * desc->head_dim;
+  a.ws_ml = a.ws_acc + (size_t)desc->batch * q_heads * ns * desc->head_dim;
   a.out = out;
   a.B = desc->batch;
   a.Hkv = desc->kv_heads;
@@ -270,7 +266,6 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
     a.k_recent = static_cast<uint16_t*>(cache->k_recent);
     a.v_recent = static_cast<uint16_t*>(cache->v_recent);
     a.recent = desc->recent;
-    a.recent_wg = E;
   }
   const float scale = softmax_scale != 0.0f ? softmax_scale
                                             : 1.0f / std::sqrt((float)desc->head_dim);

@@ -914,36 +914,78 @@ __device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewLds*
 // Recent fp16 rows ("LLM长上下文推理优化：用INT4状态机管理KV Cache", pwwt.cn/news/4219524,
 // section 8.3: older tokens in INT4, recent ones in FP16).  Positions [rlo, len),
 // rlo = max(window start, len - recent), are read from the fp16 rings instead of the
-// codes, by recent_wg extra workgroups per (b, kv head) after the splits: workgroup rw
-// takes a chunk of them and its wave w the rows t = w, w + WAVES, ... of the chunk.
-// Lane l holds dims 2l, 2l + 1 of a row; a row's G scores are wave sums (DPP), so each
-// head's running (max, sum) is wave-uniform and the lane keeps its two dims of the
-// weighted V sum.  The result is the wave's combine entry, in the same form as a tile
-// wave's (max in base-2 units), so the combine, the partial, the arrival and the merge
-// are the splits' own.  With the append fused, position len - 1 is the new token's row
-// (read from the caller's buffer), which the first extra workgroup also stores into its
-// ring row (no workgroup of the launch reads that row of the ring: the attended
-// positions before len - 1 are the recent - 1 others).
-template <int G>
-__device__ __forceinline__ void recent_entry(const DecodeArgs& a, int unit, int len, int lo_pos,
-                                             int rw, int wave, int lane, bool fused,
-                                             const uint8_t* s_q, float* s_o, float* s_m,
-                                             float* s_l, int ors, int ne) {
-  const int R = a.recent;
-  const int rlo = max(lo_pos, len - R);
-  const int nrow = len - rlo;
-  const int rchunk = (nrow + a.recent_wg - 1) / a.recent_wg;
-  const int r0 = rlo + rw * rchunk, r1 = min(len, r0 + rchunk);
-  const uint32_t* kring = reinterpret_cast<const uint32_t*>(a.k_recent) + (size_t)unit * R * (HD / 2) + lane;
-  const uint32_t* vring = reinterpret_cast<const uint32_t*>(a.v_recent) + (size_t)unit * R * (HD / 2) + lane;
-  const uint32_t* knew = reinterpret_cast<const uint32_t*>(a.k_new) + (size_t)unit * (HD / 2) + lane;
-  const uint32_t* vnew = reinterpret_cast<const uint32_t*>(a.v_new) + (size_t)unit * (HD / 2) + lane;
-  if (fused && rw == 0 && wave == 0) {
-    const size_t o = (size_t)((len - 1) % R) * (HD / 2);
-    const uint32_t kw = *knew, vw = *vnew;
-    reinterpret_cast<uint32_t*>(a.k_recent)[(size_t)unit * R * (HD / 2) + o + lane] = kw;
-    reinterpret_cast<uint32_t*>(a.v_recent)[(size_t)unit * R * (HD / 2) + o + lane] = vw;
+// codes.  Every split workgroup takes a chunk of them (extra workgroups would not be
+// resident with the splits: the plan gives each CU one), and its wave w the rows
+// t = r0 + w, r0 + w + WAVES, ... of the chunk, RPW at a time.  A wave issues the loads
+// of its first RPW rows right after the q barrier, behind its first two tiles, so their
+// latency passes under the tile stream (up to RPRE rows; any further ones are loaded
+// after the loop, RPW at a time), and attends the rows after its tile loop.
+// Lane l holds dims 2l, 2l + 1 of a row.  A batch's G * RPW scores are wave sums (DPP),
+// reduced stage by stage over the whole batch so that the independent sums overlap;
+// the batch then updates each head's running (max, sum) once (max over the batch
+// first, then independent exponentials), and the lane keeps its two dims of the
+// weighted V sum.  The result is a second combine entry of the wave (entry WAVES + w),
+// in the same form as a tile entry (max in base-2 units), so the combine, the partial,
+// the arrival and the merge are unchanged.  With the append fused, position len - 1 is
+// the new token's row (read from the caller's buffer); the appending wave stores it
+// into its ring row from LDS before the loop (no workgroup of the launch reads that row
+// of the ring: the attended positions before len - 1 are the recent - 1 others).
+constexpr int RPW = 4;            // rows per wave and batch
+constexpr int RPRE = 16;          // rows per wave loaded before the tile loop
+
+struct RecentBatch {
+  uint32_t kw[RPW], vw[RPW];      // the lane's two fp16 of K and of V of RPW rows
+};
+struct RecentRows {
+  int t0, r1;                     // this wave's first row and the chunk's end (stride WAVES)
+  RecentBatch b[RPRE / RPW];
+};
+
+// rows t0, t0 + WAVES, ... (RPW of them; zero past r1)
+__device__ __forceinline__ void recent_load(const DecodeArgs& a, int unit, int len, bool fused,
+                                            int lane, int t0, int r1, RecentBatch& rb) {
+  const size_t base = (size_t)unit * a.recent * (HD / 2) + lane;
+  const uint32_t* kring = reinterpret_cast<const uint32_t*>(a.k_recent) + base;
+  const uint32_t* vring = reinterpret_cast<const uint32_t*>(a.v_recent) + base;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int t = t0 + i * WAVES;
+    if (t < r1) {   // (uniform)
+      if (fused && t == len - 1) {   // (uniform) the new token's row
+        rb.kw[i] = reinterpret_cast<const uint32_t*>(a.k_new)[(size_t)unit * (HD / 2) + lane];
+        rb.vw[i] = reinterpret_cast<const uint32_t*>(a.v_new)[(size_t)unit * (HD / 2) + lane];
+      } else {
+        const size_t o = (size_t)(t % a.recent) * (HD / 2);
+        rb.kw[i] = kring[o];
+        rb.vw[i] = vring[o];
+      }
+    } else {
+      rb.kw[i] = 0u;
+      rb.vw[i] = 0u;
+    }
   }
+}
+
+__device__ __forceinline__ RecentRows recent_preload(const DecodeArgs& a, int unit, int len,
+                                                     int lo_pos, int rw, int nwg, int wave,
+                                                     int lane, bool fused) {
+  RecentRows rr;
+  const int rlo = max(lo_pos, len - a.recent);
+  const int rchunk = (len - rlo + nwg - 1) / nwg;
+  const int r0 = rlo + rw * rchunk;
+  rr.r1 = min(len, r0 + rchunk);
+  rr.t0 = r0 + wave;
+#pragma unroll
+  for (int bi = 0; bi < RPRE / RPW; ++bi)
+    recent_load(a, unit, len, fused, lane, rr.t0 + bi * RPW * WAVES, rr.r1, rr.b[bi]);
+  return rr;
+}
+
+template <int G>
+__device__ __forceinline__ void recent_entry(const DecodeArgs& a, int unit, int len, int lane,
+                                             bool fused, const RecentRows& rr,
+                                             const uint8_t* s_q, float* s_o, float* s_m,
+                                             float* s_l, int ors, int ne, int slot) {
   float q0[G], q1[G], m[G], l[G], o0[G], o1[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -955,36 +997,72 @@ __device__ __forceinline__ void recent_entry(const DecodeArgs& a, int unit, int 
     o0[h] = 0.0f;
     o1[h] = 0.0f;
   }
-  constexpr int RB = 4;   // rows per wave whose loads are issued together
-  for (int t0 = r0 + wave; t0 < r1; t0 += RB * WAVES) {
-    uint32_t kw[RB], vw[RB];
+  // one batch of RPW rows starting at row t0 (the rows past the chunk score -inf)
+  auto batch = [&](int t0, const RecentBatch& rb) {
+    float v0[RPW], v1[RPW], z[RPW][G];
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int t = t0 + i * WAVES;
-      if (t < r1) {   // (uniform)
-        const bool nw = fused && t == len - 1;
-        const size_t o = (size_t)(t % R) * (HD / 2);
-        kw[i] = nw ? *knew : kring[o];
-        vw[i] = nw ? *vnew : vring[o];
-      }
+    for (int i = 0; i < RPW; ++i) {
+      const f16x2 kk = __builtin_bit_cast(f16x2, rb.kw[i]), vv = __builtin_bit_cast(f16x2, rb.vw[i]);
+      v0[i] = (float)vv[0];
+      v1[i] = (float)vv[1];
+#pragma unroll
+      for (int h = 0; h < G; ++h) z[i][h] = __builtin_fmaf(q0[h], (float)kk[0], q1[h] * (float)kk[1]);
     }
+    // the wave sums, one reduction stage at a time over the batch
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      if (t0 + i * WAVES >= r1) break;   // (uniform)
-      const f16x2 kk = __builtin_bit_cast(f16x2, kw[i]), vv = __builtin_bit_cast(f16x2, vw[i]);
-      const float k0 = (float)kk[0], k1 = (float)kk[1], v0 = (float)vv[0], v1 = (float)vv[1];
+    for (int i = 0; i < RPW; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float part = lane_group_sum<32>(__builtin_fmaf(q0[h], k0, q1[h] * k1));
-        const float z = (readlane_f(part, 0) + readlane_f(part, 32)) * a.qscale;
-        const float mn = fmaxf(m[h], z);
-        const float f = fast_exp2(m[h] - mn), p = fast_exp2(z - mn);
-        l[h] = __builtin_fmaf(l[h], f, p);
-        o0[h] = __builtin_fmaf(o0[h], f, p * v0);
-        o1[h] = __builtin_fmaf(o1[h], f, p * v1);
-        m[h] = mn;
+      for (int h = 0; h < G; ++h) z[i][h] = dpp_add<0xB1>(z[i][h]);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) z[i][h] = dpp_add<0x4E>(z[i][h]);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) z[i][h] = dpp_add<0x141>(z[i][h]);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) z[i][h] = dpp_add<0x140>(z[i][h]);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {   // each 16-lane row's sum is in all its lanes
+        const float lo16 = readlane_f(z[i][h], 0) + readlane_f(z[i][h], 16);
+        const float hi16 = readlane_f(z[i][h], 32) + readlane_f(z[i][h], 48);
+        const bool in = t0 + i * WAVES < rr.r1;   // (uniform)
+        z[i][h] = in ? (lo16 + hi16) * a.qscale : NEG_INF;
       }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mb = m[h];
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) mb = fmaxf(mb, z[i][h]);
+      const float f = fast_exp2(m[h] - mb);
+      float ls = l[h] * f, a0 = o0[h] * f, a1 = o1[h] * f;
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const float p = fast_exp2(z[i][h] - mb);   // 0 for a row past the chunk
+        ls += p;
+        a0 = __builtin_fmaf(p, v0[i], a0);
+        a1 = __builtin_fmaf(p, v1[i], a1);
+      }
+      m[h] = mb;
+      l[h] = ls;
+      o0[h] = a0;
+      o1[h] = a1;
     }
+  };
+#pragma unroll
+  for (int bi = 0; bi < RPRE / RPW; ++bi) {   // the preloaded rows
+    const int t0 = rr.t0 + bi * RPW * WAVES;
+    if (t0 < rr.r1) batch(t0, rr.b[bi]);   // (uniform)
+  }
+  for (int t0 = rr.t0 + RPRE * WAVES; t0 < rr.r1; t0 += RPW * WAVES) {   // any further ones
+    RecentBatch nb;
+    recent_load(a, unit, len, fused, lane, t0, rr.r1, nb);
+    batch(t0, nb);
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -992,8 +1070,8 @@ __device__ __forceinline__ void recent_entry(const DecodeArgs& a, int unit, int 
     s_o[h * ors + d + (d >> 5)] = o0[h];
     s_o[h * ors + d + 1 + ((d + 1) >> 5)] = o1[h];
     if (lane == 0) {
-      s_m[h * ne + wave] = m[h];
-      s_l[h * ne + wave] = l[h];
+      s_m[h * ne + slot] = m[h];
+      s_l[h * ne + slot] = l[h];
     }
   }
 }
@@ -1008,7 +1086,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) NewLds s_new;
   __shared__ int s_last;
   __shared__ uint32_t s_claim;
-  __shared__ __attribute__((aligned(16))) float s_mlc[2 * WAVES * G];   // combine max / sum
+  constexpr int NE = RC ? 2 * WAVES : WAVES;   // combine entries (a second per wave: recent rows)
+  __shared__ __attribute__((aligned(16))) float s_mlc[2 * NE * G];      // combine max / sum
   __shared__ __attribute__((aligned(16))) uint8_t s_q[G * 2 * HD];      // the G query rows
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -1133,6 +1212,9 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     else wait_vmcnt<0>();
   }
   lds_barrier();
+  // (recent fp16 rows: the first batch's loads go out behind the first tiles)
+  [[maybe_unused]] RecentRows rrows;
+  if constexpr (RC) rrows = recent_preload(a, unit, len, lo_pos, sp, a.nsplit, wave, lane, fused);
   // q into MFMA layout (and the appending wave's quantization of the new row) while
   // tiles 0 and 1 are in flight (asm reads: plain reads would make the compiler wait
   // for the first tiles as well)
@@ -1213,6 +1295,13 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) s_new.m[h] = nr.z[h] * a.qscale;
     }
+    if constexpr (RC) {   // the new row's fp16 K (lanes 0-15) / V (16-31) to its ring row
+      const int c = lane & 15;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>((lane >= 16 ? s_new.v : s_new.k) + 8 * c);
+      uint16_t* rrow = (lane >= 16 ? a.v_recent : a.k_recent) +
+                       ((size_t)unit * a.recent + (len - 1) % a.recent) * HD;
+      reinterpret_cast<u32x4*>(rrow)[c] = raw;
+    }
   }
 
   for (int k = 0; cur != NONE; ++k) {
@@ -1251,10 +1340,10 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // Entry rows of 132 words (a pad word after every 32 dims): one write instruction
   // stores dims 32j + const of up to 8 (entry, head) rows, which then fall in 32 distinct
   // banks (unpadded they all share one bank)
-  constexpr int NE = WAVES;                                     // combine entries
   constexpr int ORS = HD + HD / 32;                             // padded row stride
   auto opad = [](int d) { return d + (d >> 5); };
-  static_assert(G * ORS * sizeof(float) <= NB * L::BYTES, "a wave's entry fits its ring");
+  static_assert((NE / WAVES) * G * ORS * sizeof(float) <= NB * L::BYTES,
+                "a wave's entries fit its ring");
   float* s_o = reinterpret_cast<float*>(ring);                 // this wave's [G][ORS]
   float* s_m = s_mlc;                                           // [G][NE]
   float* s_l = s_mlc + NE * G;                                  // [G][NE]
@@ -1296,12 +1385,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     l_run = __builtin_fmaf(l_run, f0, lo_run * f1);
     st.m = mx;
   }
-  const bool recent_wg = RC && sp >= a.nsplit;   // (this workgroup attends the fp16 rows)
-  if (recent_wg) {
-    if constexpr (RC)
-      recent_entry<G>(a, unit, len, lo_pos, sp - a.nsplit, wave, lane, fused, qstage, s_o, s_m,
-                      s_l, ORS, NE);
-  } else if (rr < G * NGK && qgrp == 0 && cset == 0) {
+  if (rr < G * NGK && qgrp == 0 && cset == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
@@ -1312,8 +1396,11 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       s_l[qhead * NE + wave] = l_run;
     }
   }
+  if constexpr (RC)
+    recent_entry<G>(a, unit, len, lane, fused, rrows, qstage, s_o + G * ORS, s_m, s_l,
+                    ORS, NE, WAVES + wave);
   __syncthreads();
-  const int nps = a.nsplit + (RC ? a.recent_wg : 0);           // partials per query head
+  const int nps = a.nsplit;                                     // partials per query head
   const size_t pbase = (size_t)(b * a.Hq + kvh * G) * nps;     // slot of (head 0, split 0)
   for (int idx = threadIdx.x; idx < G * HD; idx += NT) {
     const int h = idx / HD, d = idx % HD;
@@ -1332,8 +1419,9 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int w = 0; w < NE; ++w)   // entry w: wave w's, in that wave's ring
-      ow[w] = reinterpret_cast<const float*>(smem + w * NB * L::BYTES)[h * ORS + opad(d)];
+    for (int w = 0; w < NE; ++w)   // entry w: wave w % WAVES's, in that wave's ring
+      ow[w] = reinterpret_cast<const float*>(smem + (w % WAVES) * NB * L::BYTES)[(w / WAVES) * G * ORS +
+                                                                                h * ORS + opad(d)];
     // (with recent fp16 rows the new row is attended among them, not here)
     const float mn = appender && !RC ? s_new.m[h] : NEG_INF;
     const float on = appender && !RC ? s_new.o[d] : 0.0f;
@@ -1472,7 +1560,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 
 template <int G, bool SK, bool RC>
 hipError_t launch_gs(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.nsplit + (RC ? a.recent_wg : 0), a.Hkv, a.B);
+  const dim3 grid(a.nsplit, a.Hkv, a.B);
   switch (HD / a.gk) {
     case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1, false, SK, RC>, grid, dim3(NT), a, s);
     case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2, false, SK, RC>, grid, dim3(NT), a, s);

@@ -59,8 +59,8 @@ struct DecodeArgs {
   const void* v_codes;
   const float* v_scales;
   const uint16_t* q;     // [B, Hq, D] fp16
-  float* ws_acc;         // [B, Hq, nsplit + recent_wg, D]
-  float* ws_ml;          // [B, Hq, nsplit + recent_wg, 2] (running max in log2 units, sum)
+  float* ws_acc;         // [B, Hq, nsplit, D]
+  float* ws_ml;          // [B, Hq, nsplit, 2] (running max in log2 units, sum)
   float* out;            // [B, Hq, D]
   uint32_t* counters;    // [B, Hkv] split arrival counters (zero between calls)
   const uint16_t* k_new; // [B, Hkv, D] fp16 rows appended at position lens[b] - 1, or null
@@ -74,9 +74,8 @@ struct DecodeArgs {
   int32_t merge_inline;  // split-K kernel: the last split of a unit merges (no merge kernel)
   uint16_t* k_recent;    // fp16 rings [B, Hkv, recent, D], position p in row p % recent
   uint16_t* v_recent;    // (INT4 matrix-core kernel with recent > 0), else null
-  int32_t recent;        // positions [len - recent, len) are read from the rings
-  int32_t recent_wg;     // workgroups per (b, kv head) attending them, after the nsplit
-                         // splits; their partials follow the splits'
+  int32_t recent;        // positions [len - recent, len) are read from the rings (each
+                         // split takes a share of them)
   int32_t lens[KVQ_MAX_BATCH];
 };
 

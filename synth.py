@@ -88,6 +88,7 @@ class Workload:
     window_layers: int = 0  # number of sliding-window layers (the first ones)
     window: int = 0
     sinks: int = 0          # attention-sink positions kept besides a window layer's ring
+    recent: int = 0         # last positions also kept (and read) in fp16
     zero_groups: tuple = field(default=())
 
     def layer_window(self, layer):
@@ -114,6 +115,9 @@ WORKLOADS = {
     6: Workload(6, "llama3-8b-window4k-sinks4-b8", layers=32, batch=8, q_heads=32, kv_heads=8,
                 head_dim=128, context=8192, append=True,
                 outlier_channels=round(0.02 * 128), window_layers=32, window=4096, sinks=4),
+    7: Workload(7, "llama3-8b-gqa4-ctx8k-b8-recent128", layers=32, batch=8, q_heads=32,
+                kv_heads=8, head_dim=128, context=8192, append=True,
+                outlier_channels=round(0.02 * 128), recent=128),
 }
 
 

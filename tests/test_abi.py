@@ -164,8 +164,8 @@ def test_sinks_validation_and_workspace():
 
 def test_recent_validation_and_workspace():
     """Recent fp16 rows: INT4 only, not with sinks, at most KVQ_MAX_RECENT; the rings are
-    required when R > 0; decode needs the matrix-core INT4 kernel; the workspace holds
-    ceil(R / 256) more partials per query head."""
+    required when R > 0; decode needs the matrix-core INT4 kernel; the workspace is the
+    splits' alone."""
     ok = kvq.make_desc("int4", 2, 4, 128, 64, recent=128)
     assert kvq.kvq_check_desc(ok) == 0
     assert kvq.kvq_recent_bytes(ok) == 2 * 4 * 128 * 128 * 2
@@ -178,11 +178,11 @@ def test_recent_validation_and_workspace():
         assert kvq.kvq_check_desc(bad) == kvq.KVQ_ERR_UNSUPPORTED
         assert kvq.kvq_recent_bytes(bad) == 0
     assert kvq.kvq_check_desc(kvq.make_desc("int4", 2, 4, 128, 64, recent=kvq.KVQ_MAX_RECENT)) == 0
-    for R, E in ((1, 1), (128, 1), (256, 1), (257, 2), (1024, 4)):
+    for R in (1, 128, 1024):
         d = kvq.make_desc("int4", 2, 4, 128, 64, recent=R)
         ns = kvq.kvq_plan_splits(d, 8, 60)
-        assert kvq.kvq_decode_workspace_bytes(d, 8, 60, 0) == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * (ns + E) * 130 * 4
-        assert kvq.kvq_decode_workspace_bytes(d, 8, 60, 0, 7) == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * (7 + E) * 130 * 4
+        assert kvq.kvq_decode_workspace_bytes(d, 8, 60, 0) == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * ns * 130 * 4
+        assert kvq.kvq_decode_workspace_bytes(d, 8, 60, 0, 7) == kvq.KVQ_WS_COUNTER_BYTES + 2 * 8 * 7 * 130 * 4
     no_rings = _cache()
     rings = kvq.kvq_cache(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_quantize_prefill, ok, no_rings, FAKE, FAKE, 0, 10, 0)
@@ -194,8 +194,7 @@ def test_recent_validation_and_workspace():
                   (kvq.make_desc("int4", 2, 4, 128, 64, 32, 128, recent=16), 32)):
         _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_decode_attn, d, rings, FAKE, hq, [30, 10], 0, 0.0, 0, FAKE,
                 FAKE, 1 << 30, 0)
-    # splits plus the recent workgroups stay within 1024 partials
-    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, ok, rings, FAKE, 8, [30, 10], 0, 0.0, 1024, FAKE, FAKE,
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, ok, rings, FAKE, 8, [30, 10], 0, 0.0, 1025, FAKE, FAKE,
             1 << 30, 0)
 
 

@@ -83,12 +83,13 @@ CASES = [
     (4, 64, 128, [1000, 700], 0, 0),
     (4, 64, 128, [1000, 50], 0, 0),          # sequence 1 shorter than the recent span
     (1, 128, 1, [900, 333], 0, 0),           # one fp16 row: the last position only
-    (2, 32, 300, [1200, 301], 0, 5),         # two recent workgroups
-    (8, 64, 64, [800, 640], 0, 1),           # one split besides the recent workgroup
-    (8, 128, 1024, [1500, 1024], 0, 0),      # four recent workgroups; 1024 = len
+    (2, 32, 300, [1200, 301], 0, 5),         # 5 splits share the 300 fp16 rows
+    (8, 64, 64, [800, 640], 0, 1),           # one split takes every row
+    (8, 128, 1024, [1500, 1024], 0, 0),      # 1024 = len: sequence 1 all fp16
     (4, 32, 256, [1100, 900], 500, 0),       # window longer than the recent span
     (2, 64, 300, [1000, 777], 200, 0),       # recent span longer than the window
-    (4, 64, 100, [1000, 640], 0, 40),        # 40 splits + 1 recent partial, merged in-kernel
+    (4, 64, 100, [1000, 640], 0, 40),        # 40 splits, 3 fp16 rows each, merged in-kernel
+    (4, 64, 3, [1000, 640], 0, 16),          # more splits than fp16 rows
 ]
 
 
