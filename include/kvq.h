@@ -49,6 +49,10 @@
  *   KVQ_WHT_LM4   codes  [B, Hkv, C, D/2] uint8, unsigned 4-bit Lloyd-Max indices
  *                        (0..15) of the rotated row, same nibble order as INT4;
  *                 scales [B, Hkv, C] fp32 (the row's RMS).
+ *   KVQ_WHT_LM3   codes  [B, Hkv, C, 3, D/8] uint8: the 3-bit indices (0..7) as three
+ *                        bit-planes; byte c of plane p holds bit p of the indices
+ *                        8c .. 8c+7 (index 8c+j in bit j);
+ *                 scales [B, Hkv, C] fp32, as for KVQ_WHT_LM4.
  *   Position p of a sequence lives in slot p when p < S (S = sinks, the first
  *   positions kept for attention sinks, [KV-opt] §3.2), else in slot
  *   S + (p - S) mod (C - S): a ring of C - S slots (S = 0: slot p mod C).
@@ -68,7 +72,7 @@
 extern "C" {
 #endif
 
-#define KVQ_VERSION 4
+#define KVQ_VERSION 5
 /* Largest batch the decode/append calls accept (per-sequence lengths and positions
  * travel in the kernel argument block). */
 #define KVQ_MAX_BATCH 256
@@ -83,7 +87,8 @@ extern "C" {
 typedef enum {
   KVQ_INT4_G = 0,      /* group-wise symmetric INT4 ([KV-4bit] §2.1) */
   KVQ_INT8_TOKEN = 1,  /* per-token symmetric INT8 ([KV-opt] §3.1) */
-  KVQ_WHT_LM4 = 2      /* Walsh-Hadamard rotation + 4-bit Lloyd-Max codec ([LARQL]) */
+  KVQ_WHT_LM4 = 2,     /* Walsh-Hadamard rotation + 4-bit Lloyd-Max codec ([LARQL]) */
+  KVQ_WHT_LM3 = 3      /* the same codec at 3 bits ([LARQL]: 3 or 4 bits) */
 } kvq_format;
 
 typedef enum {
@@ -136,7 +141,8 @@ int32_t kvq_check_desc(const kvq_cache_desc* desc);
 
 /* Bytes of the codes (or scales) buffer of K (kv = 0) or V (kv = 1) for `desc`;
  * 0 if the descriptor is invalid or kv is not 0/1.  INT4: B*Hkv*C*D/2 and
- * B*Hkv*C*(D/g)*4; INT8: B*Hkv*C*D and B*Hkv*C*4; codec: B*Hkv*C*D/2 and B*Hkv*C*4. */
+ * B*Hkv*C*(D/g)*4; INT8: B*Hkv*C*D and B*Hkv*C*4; codec: B*Hkv*C*D/2 (3-bit:
+ * B*Hkv*C*3D/8) and B*Hkv*C*4. */
 size_t kvq_codes_bytes(const kvq_cache_desc* desc, int32_t kv);
 size_t kvq_scales_bytes(const kvq_cache_desc* desc, int32_t kv);
 /* Bytes of each recent fp16 ring (K and V alike): B*Hkv*R*D*2; 0 if the descriptor is
@@ -160,6 +166,10 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t q_heads,
  * fp32 from a double-precision fixed-point iteration.  Host pointers.  KVQ_ERR_ARG on
  * null. */
 int32_t kvq_codec_codebook(float* levels16, float* thresholds15);
+
+/* The same at `bits` = 3 or 4: 2^bits levels and 2^bits - 1 thresholds into the host
+ * arrays.  KVQ_ERR_ARG on null or another bit count. */
+int32_t kvq_codec_codebook_bits(int32_t bits, float* levels, float* thresholds);
 
 /* Bulk quantize `n` consecutive positions [start_pos, start_pos + n) of every
  * (b, kv head) into the cache ([KV-4bit] §2.1 applied to the prefill rows).

@@ -24,8 +24,8 @@ import torch  # noqa: F401  (must precede the CDLL below: one HIP runtime per pr
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-KVQ_INT4_G, KVQ_INT8_TOKEN, KVQ_WHT_LM4 = 0, 1, 2
-FORMATS = {"int4": KVQ_INT4_G, "int8": KVQ_INT8_TOKEN, "codec": KVQ_WHT_LM4}
+KVQ_INT4_G, KVQ_INT8_TOKEN, KVQ_WHT_LM4, KVQ_WHT_LM3 = 0, 1, 2, 3
+FORMATS = {"int4": KVQ_INT4_G, "int8": KVQ_INT8_TOKEN, "codec": KVQ_WHT_LM4, "codec3": KVQ_WHT_LM3}
 KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = \
     0, -1, -2, -3, -4, -5
 KVQ_MAX_BATCH = 256
@@ -36,7 +36,7 @@ KVQ_MAX_RECENT = 1024
 EXPORTS = (
     "kvq_version", "kvq_status_str", "kvq_check_desc", "kvq_codes_bytes", "kvq_scales_bytes",
     "kvq_recent_bytes",
-    "kvq_plan_splits", "kvq_decode_workspace_bytes", "kvq_codec_codebook",
+    "kvq_plan_splits", "kvq_decode_workspace_bytes", "kvq_codec_codebook", "kvq_codec_codebook_bits",
     "kvq_quantize_prefill", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
     "kvq_dequant",
 )
@@ -81,6 +81,7 @@ def _load():
         "kvq_plan_splits": (i32, [D, i32, i32]),
         "kvq_decode_workspace_bytes": (sz, [D, i32, i32, i32, i32]),
         "kvq_codec_codebook": (i32, [P(f32), P(f32)]),
+        "kvq_codec_codebook_bits": (i32, [i32, P(f32), P(f32)]),
         "kvq_quantize_prefill": (i32, [D, C, vp, vp, i32, i32, vp]),
         "kvq_append": (i32, [D, C, vp, vp, P(i32), vp]),
         "kvq_decode_attn": (i32, [D, C, vp, i32, P(i32), i32, f32, i32, vp, vp, sz, vp]),
@@ -178,6 +179,13 @@ def kvq_codec_codebook():
     th = (ctypes.c_float * 15)()
     _check(LIB.kvq_codec_codebook(lv, th), "kvq_codec_codebook")
     return list(lv), list(th)
+
+
+def kvq_codec_codebook_bits(bits):
+    lv = (ctypes.c_float * 16)()
+    th = (ctypes.c_float * 15)()
+    _check(LIB.kvq_codec_codebook_bits(int(bits), lv, th), "kvq_codec_codebook_bits")
+    return list(lv)[: 1 << bits], list(th)[: (1 << bits) - 1]
 
 
 def kvq_quantize_prefill(desc, cache, k, v, start_pos, n, stream=None):

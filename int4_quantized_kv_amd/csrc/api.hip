@@ -13,7 +13,7 @@ bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int32_t check_desc(const kvq_cache_desc* d) {
   if (!d) return KVQ_ERR_ARG;
-  if (d->format < KVQ_INT4_G || d->format > KVQ_WHT_LM4) return KVQ_ERR_ARG;
+  if (d->format < KVQ_INT4_G || d->format > KVQ_WHT_LM3) return KVQ_ERR_ARG;
   if (d->batch < 1 || d->kv_heads < 1 || d->head_dim < 1 || d->capacity < 1)
     return KVQ_ERR_ARG;
   if (d->sinks < 0 || d->sinks >= d->capacity || d->recent < 0) return KVQ_ERR_ARG;
@@ -68,10 +68,10 @@ int32_t quant_common(const kvq_cache_desc* desc, const kvq_cache* cache, const v
     a.v_recent = static_cast<uint16_t*>(cache->v_recent);
     a.recent = desc->recent;
   }
-  if (desc->format == KVQ_WHT_LM4) {
+  if (is_codec(desc->format)) {
     float lv[16];
-    codec_codebook(lv, a.thr);
-    return launch_status(launch_codec_encode(a, stream));
+    codec_codebook(codec_bits(desc->format), lv, a.thr);
+    return launch_status(launch_codec_encode(codec_bits(desc->format), a, stream));
   }
   return launch_status(launch_quant_intq(desc->format, a, stream));
 }
@@ -138,7 +138,9 @@ int32_t kvq_check_desc(const kvq_cache_desc* desc) { return check_desc(desc); }
 size_t kvq_codes_bytes(const kvq_cache_desc* d, int32_t kv) {
   if (check_desc(d) != KVQ_OK || (kv != 0 && kv != 1)) return 0;
   const size_t rows = (size_t)d->batch * d->kv_heads * d->capacity;
-  return d->format == KVQ_INT8_TOKEN ? rows * d->head_dim : rows * (d->head_dim / 2);
+  if (d->format == KVQ_INT8_TOKEN) return rows * d->head_dim;
+  if (d->format == KVQ_WHT_LM3) return rows * (3 * d->head_dim / 8);
+  return rows * (d->head_dim / 2);
 }
 
 size_t kvq_scales_bytes(const kvq_cache_desc* d, int32_t kv) {
@@ -169,7 +171,16 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* d, int32_t q_heads, int3
 
 int32_t kvq_codec_codebook(float* levels16, float* thresholds15) {
   if (!levels16 || !thresholds15) return KVQ_ERR_ARG;
-  codec_codebook(levels16, thresholds15);
+  codec_codebook(4, levels16, thresholds15);
+  return KVQ_OK;
+}
+
+int32_t kvq_codec_codebook_bits(int32_t bits, float* levels, float* thresholds) {
+  if (!levels || !thresholds || (bits != 3 && bits != 4)) return KVQ_ERR_ARG;
+  float lv[16], th[15];
+  codec_codebook(bits, lv, th);
+  for (int32_t j = 0; j < (1 << bits); ++j) levels[j] = lv[j];
+  for (int32_t j = 0; j + 1 < (1 << bits); ++j) thresholds[j] = th[j];
   return KVQ_OK;
 }
 
@@ -270,7 +281,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   const float scale = softmax_scale != 0.0f ? softmax_scale
                                             : 1.0f / std::sqrt((float)desc->head_dim);
   a.qscale = scale * 1.4426950408889634f;  // log2(e): scores in base-2 units
-  if (desc->format == KVQ_WHT_LM4) codec_codebook(a.levels, a.thr);
+  if (is_codec(desc->format)) codec_codebook(codec_bits(desc->format), a.levels, a.thr);
   for (int32_t b = 0; b < desc->batch; ++b) a.lens[b] = lens[b];
 
   if (k_new) {
@@ -338,10 +349,10 @@ int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t 
   a.n = n;
   a.sinks = desc->sinks;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (desc->format == KVQ_WHT_LM4) {
+  if (is_codec(desc->format)) {
     float thr[15];
-    codec_codebook(a.levels, thr);
-    return launch_status(launch_codec_dequant(a, s));
+    codec_codebook(codec_bits(desc->format), a.levels, thr);
+    return launch_status(launch_codec_dequant(codec_bits(desc->format), a, s));
   }
   return launch_status(launch_dequant_intq(desc->format, a, s));
 }

@@ -1,5 +1,5 @@
-// codec.hip -- Walsh-Hadamard rotation + 4-bit Lloyd-Max KV codec: encode (prefill and
-// append), dequantize, and the library's own codebook.
+// codec.hip -- Walsh-Hadamard rotation + 4-bit or 3-bit Lloyd-Max KV codec: encode
+// (prefill and append), dequantize, and the library's own codebooks.
 //
 // Page: "长上下文内存大瘦身：LARQL 四大 KV 缓存引擎原理与横向对比" (pwwt.cn/news/5725003),
 // engine three (codec): every K/V row is coded per head by a Walsh-Hadamard rotation
@@ -10,7 +10,9 @@
 // strictly below y / s (a zero row is coded as y / 1), decode x = s * H c[index] / sqrt(D).
 //
 // Mapping: as for INT4, a row of D elements spans D/8 lanes of 8 elements; three
-// butterfly stages run inside a lane, log2(D/8) across lanes with xor shuffles.
+// butterfly stages run inside a lane, log2(D/8) across lanes with xor shuffles.  4-bit
+// rows are D/2 bytes of nibbles; 3-bit rows three bit-planes of D/8 bytes (see
+// store_planes).  The 3-bit coder is the 4-bit one with thresholds 7 .. 14 set to +inf.
 #include <cmath>
 
 #include "kvq_device.h"
@@ -19,12 +21,12 @@
 namespace kvq {
 namespace {
 
-template <int D>
+template <int D, int BITS>
 __global__ void __launch_bounds__(256) codec_encode_kernel(QuantArgs a) {
   constexpr int LPR = D / 8;
   const int isv = blockIdx.y;
   const uint16_t* src = isv ? a.v : a.k;
-  uint32_t* codes = reinterpret_cast<uint32_t*>(isv ? a.v_codes : a.k_codes);
+  void* codes = isv ? a.v_codes : a.k_codes;
   float* scales = isv ? a.v_scales : a.k_scales;
   const uint32_t total = (uint32_t)a.rows * LPR;
   const uint32_t stride = gridDim.x * blockDim.x;
@@ -42,18 +44,18 @@ __global__ void __launch_bounds__(256) codec_encode_kernel(QuantArgs a) {
     const int b = (int)(bh / (uint32_t)a.Hkv);
     const int p = a.map.append ? a.map.pos[b] : a.map.start + t;
     const size_t drow = (size_t)bh * a.map.cap + cache_slot(p, a.map.cap, a.map.sinks);
-    codes[drow * LPR + c] = w;
+    if (BITS == 4) static_cast<uint32_t*>(codes)[drow * LPR + c] = w;
+    else store_planes<LPR>(static_cast<uint8_t*>(codes) + drow * 3 * LPR, c, w);
     if (c == 0) scales[drow] = s;
   }
 }
 
-template <int D>
+template <int D, int BITS>
 __global__ void __launch_bounds__(256) codec_dequant_kernel(DequantArgs a) {
   constexpr int LPR = D / 8;
   __shared__ float lv[16];
   if (threadIdx.x < 16) lv[threadIdx.x] = a.levels[threadIdx.x];
   __syncthreads();
-  const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.codes);
   const uint32_t total = (uint32_t)a.B * a.Hkv * a.n * LPR;
   const uint32_t stride = gridDim.x * blockDim.x;
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
@@ -65,7 +67,8 @@ __global__ void __launch_bounds__(256) codec_dequant_kernel(DequantArgs a) {
     const uint32_t bh = row / (uint32_t)a.n;
     const int t = (int)(row - bh * a.n);
     const size_t drow = (size_t)bh * a.cap + cache_slot(a.start + t, a.cap, a.sinks);
-    const uint32_t w = codes[drow * LPR + c];
+    const uint32_t w = BITS == 4 ? static_cast<const uint32_t*>(a.codes)[drow * LPR + c]
+                                 : load_planes<LPR>(static_cast<const uint8_t*>(a.codes) + drow * 3 * LPR, c);
     const float s = a.scales[drow];
     float v[8];
 #pragma unroll
@@ -85,8 +88,8 @@ inline int grid_for(uint64_t lanes) {
 }
 
 struct Book {
-  float levels[16];
-  float thresholds[15];
+  float levels[16];        // 2^bits used
+  float thresholds[15];    // 2^bits - 1 used
 };
 
 double phi(double t) { return std::exp(-0.5 * t * t) / std::sqrt(2.0 * M_PI); }
@@ -95,18 +98,18 @@ double Phi(double t) { return 0.5 * std::erfc(-t / std::sqrt(2.0)); }
 // Lloyd's two optimality conditions for N(0,1), iterated to a fixed point in double:
 // thresholds are midpoints of adjacent levels; each level is the mean of its cell,
 // (phi(lo) - phi(hi)) / (Phi(hi) - Phi(lo)).
-Book compute_book() {
+Book compute_book(int n) {   // n = 2^bits levels
   double c[16];
-  for (int i = 0; i < 16; ++i) c[i] = -2.5 + 5.0 * i / 15.0;
+  for (int i = 0; i < n; ++i) c[i] = -2.5 + 5.0 * i / (n - 1);
   for (int it = 0; it < 200000; ++it) {
     double t[15];
-    for (int j = 0; j < 15; ++j) t[j] = 0.5 * (c[j] + c[j + 1]);
+    for (int j = 0; j < n - 1; ++j) t[j] = 0.5 * (c[j] + c[j + 1]);
     double delta = 0.0;
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < n; ++j) {
       const double plo = j == 0 ? 0.0 : phi(t[j - 1]);
-      const double phi_hi = j == 15 ? 0.0 : phi(t[j]);
+      const double phi_hi = j == n - 1 ? 0.0 : phi(t[j]);
       const double Plo = j == 0 ? 0.0 : Phi(t[j - 1]);
-      const double Phi_hi = j == 15 ? 1.0 : Phi(t[j]);
+      const double Phi_hi = j == n - 1 ? 1.0 : Phi(t[j]);
       const double cn = (plo - phi_hi) / (Phi_hi - Plo);
       delta = std::fmax(delta, std::fabs(cn - c[j]));
       c[j] = cn;
@@ -116,42 +119,53 @@ Book compute_book() {
   // N(0,1) is symmetric, so is its optimal quantizer: make the levels exactly odd so
   // that the middle threshold is exactly 0
   double cs[16];
-  for (int j = 0; j < 16; ++j) cs[j] = 0.5 * (c[j] - c[15 - j]);
-  for (int j = 0; j < 16; ++j) c[j] = cs[j];
+  for (int j = 0; j < n; ++j) cs[j] = 0.5 * (c[j] - c[n - 1 - j]);
   Book b;
-  for (int j = 0; j < 16; ++j) b.levels[j] = (float)c[j];
-  for (int j = 0; j < 15; ++j) b.thresholds[j] = (float)(0.5 * (c[j] + c[j + 1]));
+  for (int j = 0; j < 16; ++j) b.levels[j] = j < n ? (float)cs[j] : 0.0f;
+  for (int j = 0; j < 15; ++j)
+    b.thresholds[j] = j < n - 1 ? (float)(0.5 * (cs[j] + cs[j + 1])) : __builtin_huge_valf();
   return b;
 }
 
 }  // namespace
 
-void codec_codebook(float levels[16], float thresholds[15]) {
-  static const Book book = compute_book();  // computed once, constant afterwards
+void codec_codebook(int32_t bits, float levels[16], float thresholds[15]) {
+  static const Book book4 = compute_book(16), book3 = compute_book(8);   // computed once
+  const Book& book = bits == 3 ? book3 : book4;
   for (int j = 0; j < 16; ++j) levels[j] = book.levels[j];
   for (int j = 0; j < 15; ++j) thresholds[j] = book.thresholds[j];
 }
 
-hipError_t launch_codec_encode(const QuantArgs& a, hipStream_t s) {
-  const uint64_t lanes = (uint64_t)a.rows * (a.D / 8);
-  dim3 grid(grid_for(lanes), 2);
+template <int BITS>
+hipError_t encode_bits(const QuantArgs& a, dim3 grid, hipStream_t s) {
   switch (a.D) {
-    case 64: return launch_kernel(codec_encode_kernel<64>, grid, dim3(256), a, s);
-    case 128: return launch_kernel(codec_encode_kernel<128>, grid, dim3(256), a, s);
-    case 256: return launch_kernel(codec_encode_kernel<256>, grid, dim3(256), a, s);
+    case 64: return launch_kernel(codec_encode_kernel<64, BITS>, grid, dim3(256), a, s);
+    case 128: return launch_kernel(codec_encode_kernel<128, BITS>, grid, dim3(256), a, s);
+    case 256: return launch_kernel(codec_encode_kernel<256, BITS>, grid, dim3(256), a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_codec_dequant(const DequantArgs& a, hipStream_t s) {
-  const uint64_t lanes = (uint64_t)a.B * a.Hkv * a.n * (a.D / 8);
-  const dim3 grid(grid_for(lanes));
+template <int BITS>
+hipError_t dequant_bits(const DequantArgs& a, dim3 grid, hipStream_t s) {
   switch (a.D) {
-    case 64: return launch_kernel(codec_dequant_kernel<64>, grid, dim3(256), a, s);
-    case 128: return launch_kernel(codec_dequant_kernel<128>, grid, dim3(256), a, s);
-    case 256: return launch_kernel(codec_dequant_kernel<256>, grid, dim3(256), a, s);
+    case 64: return launch_kernel(codec_dequant_kernel<64, BITS>, grid, dim3(256), a, s);
+    case 128: return launch_kernel(codec_dequant_kernel<128, BITS>, grid, dim3(256), a, s);
+    case 256: return launch_kernel(codec_dequant_kernel<256, BITS>, grid, dim3(256), a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_codec_encode(int32_t bits, const QuantArgs& a, hipStream_t s) {
+  const uint64_t lanes = (uint64_t)a.rows * (a.D / 8);
+  const dim3 grid(grid_for(lanes), 2);
+  return bits == 3 ? encode_bits<3>(a, grid, s) : encode_bits<4>(a, grid, s);
+}
+
+hipError_t launch_codec_dequant(int32_t bits, const DequantArgs& a, hipStream_t s) {
+  const uint64_t lanes = (uint64_t)a.B * a.Hkv * a.n * (a.D / 8);
+  const dim3 grid(grid_for(lanes));
+  return bits == 3 ? dequant_bits<3>(a, grid, s) : dequant_bits<4>(a, grid, s);
 }
 
 }  // namespace kvq

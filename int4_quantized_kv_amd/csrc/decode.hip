@@ -63,6 +63,12 @@ __device__ __forceinline__ RawRow load_raw(const DecodeArgs& a, size_t row, int 
     r.k[0] = kw.x; r.k[1] = kw.y; r.v[0] = vw.x; r.v[1] = vw.y;
     r.sk = a.k_scales[row];
     r.sv = a.v_scales[row];
+  } else if (FMT == KVQ_WHT_LM3) {   // three plane bytes per lane, as a nibble word
+    r.k[0] = load_planes<LPR>(static_cast<const uint8_t*>(a.k_codes) + row * 3 * LPR, c);
+    r.v[0] = load_planes<LPR>(static_cast<const uint8_t*>(a.v_codes) + row * 3 * LPR, c);
+    r.k[1] = r.v[1] = 0u;
+    r.sk = a.k_scales[row];
+    r.sv = a.v_scales[row];
   } else {
     r.k[0] = reinterpret_cast<const uint32_t*>(a.k_codes)[row * LPR + c];
     r.v[0] = reinterpret_cast<const uint32_t*>(a.v_codes)[row * LPR + c];
@@ -111,12 +117,13 @@ constexpr int MERGE_INLINE_MAX = 32;
 
 template <int D, int G, int FMT>
 __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
+  constexpr bool CODEC = FMT == KVQ_WHT_LM4 || FMT == KVQ_WHT_LM3;
   constexpr int LPR = D / 8;
   constexpr int NGRP = 256 / LPR;
   __shared__ float s_m[NGRP][G];
   __shared__ float s_l[NGRP][G];
   __shared__ float s_acc[NGRP][G][D];
-  __shared__ float2 lv2[FMT == KVQ_WHT_LM4 ? 256 : 1];   // codec: the levels of a byte's nibbles
+  __shared__ float2 lv2[CODEC ? 256 : 1];   // codec: the levels of a byte's nibbles
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, grp = tid / LPR, c = tid % LPR;
@@ -125,7 +132,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   // codec with the append fused: position len - 1 is the new row, coded in this kernel
   // and attended from registers by the last split, which (when there are several) has
   // no other rows: the other splits cover [lo, len - 1)
-  const bool fused = FMT == KVQ_WHT_LM4 && a.k_new != nullptr;
+  const bool fused = CODEC && a.k_new != nullptr;
   const bool app_split = fused && sp == a.nsplit - 1;
   const int nrs = fused && a.nsplit > 1 ? a.nsplit - 1 : a.nsplit;   // splits with rows
   const int pt = fused ? len - 1 : len;
@@ -185,7 +192,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     f16x8_unpack(qraw[h], q[h]);
-    if (FMT == KVQ_WHT_LM4) {
+    if (CODEC) {
       wht_row<LPR>(q[h], c);
 #pragma unroll
       for (int j = 0; j < 8; ++j) q[h][j] *= 1.0f / sqrtf((float)D);
@@ -205,7 +212,9 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     codec_encode_row<LPR>(x, c, thr, w, sc);
     if (grp < 2) {
       const size_t row = bh * a.cap + cache_slot(len - 1, a.cap, a.sinks);
-      static_cast<uint32_t*>(const_cast<void*>(grp ? a.v_codes : a.k_codes))[row * LPR + c] = w;
+      void* codes = const_cast<void*>(grp ? a.v_codes : a.k_codes);
+      if (FMT == KVQ_WHT_LM3) store_planes<LPR>(static_cast<uint8_t*>(codes) + row * 3 * LPR, c, w);
+      else static_cast<uint32_t*>(codes)[row * LPR + c] = w;
       if (c == 0) const_cast<float*>(grp ? a.v_scales : a.k_scales)[row] = sc;
     }
     // group 0 takes the V row's word and scale from the lane LPR above it
@@ -217,7 +226,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     nr.k[1] = nr.v[1] = 0u;
   }
 
-  if (FMT == KVQ_WHT_LM4) {   // the codebook levels (the barrier comes after the loads above)
+  if (CODEC) {   // the codebook levels (the barrier comes after the loads above)
     lv2[tid] = make_float2(a.levels[tid & 15], a.levels[tid >> 4]);
     __syncthreads();
   }
@@ -434,11 +443,11 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
           if (s0 + t < np) A = __builtin_fmaf(x[t], wh[s0 + t], A);
       }
       const float o = A / s_L[h];
-      if (FMT == KVQ_WHT_LM4) s_out[h * D + d] = o;
+      if (CODEC) s_out[h * D + d] = o;
       else a.out[(size_t)(b * a.Hq + kvh * G + h) * D + d] = o;
     }
   }
-  if (FMT == KVQ_WHT_LM4) {   // back from the rotated domain: H o / sqrt(D), a row group per head
+  if (CODEC) {   // back from the rotated domain: H o / sqrt(D), a row group per head
     __syncthreads();
     if (grp < G) {
       float v[8];
@@ -571,7 +580,8 @@ hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || k.merge_inline) return e;
-  return launch_kernel(merge_kernel<D, FMT == KVQ_WHT_LM4>, dim3(a.Hq, a.B), dim3(D), k, s);
+  return launch_kernel(merge_kernel<D, FMT == KVQ_WHT_LM4 || FMT == KVQ_WHT_LM3>, dim3(a.Hq, a.B),
+                       dim3(D), k, s);
 }
 
 template <int D>
@@ -580,6 +590,7 @@ hipError_t launch_fmt(int32_t format, const DecodeArgs& a, int G, hipStream_t s)
     case KVQ_INT4_G: return launch_d<D, KVQ_INT4_G>(a, G, s);
     case KVQ_INT8_TOKEN: return launch_d<D, KVQ_INT8_TOKEN>(a, G, s);
     case KVQ_WHT_LM4: return launch_d<D, KVQ_WHT_LM4>(a, G, s);
+    case KVQ_WHT_LM3: return launch_d<D, KVQ_WHT_LM3>(a, G, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -596,7 +607,7 @@ int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
     return plan_splits_mfma(units, span);
   // the codec keeps one more split for the new row when its append is fused (planned
   // for every codec call, so that the workspace query does not depend on the call)
-  const int32_t extra = d->format == KVQ_WHT_LM4 ? 1 : 0;
+  const int32_t extra = is_codec(d->format) ? 1 : 0;
   const int32_t target = 1024;       // workgroups: 4 per CU on 256 CUs (all resident)
   const int32_t min_rows = 64;       // positions per split worth a workgroup (short
                                      // contexts need many splits to fill the chip)

@@ -1610,7 +1610,7 @@ int32_t plan_splits_mfma(int32_t units, int32_t span) {
 }
 
 bool fused_append_supported(const kvq_cache_desc* d, int32_t q_group) {
-  if (d->format == KVQ_WHT_LM4) return true;   // the codec's split-K kernel codes the row
+  if (is_codec(d->format)) return true;   // the codec's split-K kernel codes the row
   return d->format == KVQ_INT4_G &&
          mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group);
 }

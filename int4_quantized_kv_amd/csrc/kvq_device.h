@@ -176,6 +176,37 @@ __device__ __forceinline__ void codec_encode_row(float x[8], int c, const Thresh
   for (int j = 0; j < 8; ++j) w |= (uint32_t)count_below15(thr, x[j] * inv) << (4 * j);
 }
 
+// 3-bit codec rows are three bit-planes of D/8 bytes: byte c of plane p holds bit p of
+// the indices 8c .. 8c + 7 (index 8c + j in bit j).  A lane owning those 8 indices works
+// on them as the 4-bit codec's nibble word (index j in nibble j, values 0..7), so the
+// level lookups are shared; these convert between the word and its three plane bytes.
+__device__ __forceinline__ uint32_t spread_bits8(uint32_t x) {   // bit j -> bit 4j
+  x &= 0xFFu;
+  x = (x | (x << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  return (x | (x << 3)) & 0x11111111u;
+}
+__device__ __forceinline__ uint32_t gather_bits8(uint32_t x) {   // bit 4j -> bit j
+  x &= 0x11111111u;
+  x = (x | (x >> 3)) & 0x03030303u;
+  x = (x | (x >> 6)) & 0x000F000Fu;
+  return (x | (x >> 12)) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t planes_to_nibbles(uint32_t b0, uint32_t b1, uint32_t b2) {
+  return spread_bits8(b0) | (spread_bits8(b1) << 1) | (spread_bits8(b2) << 2);
+}
+// lane c of a row: its 8 indices (nibble word w) into the row's planes at `row`
+template <int LPR>
+__device__ __forceinline__ void store_planes(uint8_t* row, int c, uint32_t w) {
+  row[c] = (uint8_t)gather_bits8(w);
+  row[LPR + c] = (uint8_t)gather_bits8(w >> 1);
+  row[2 * LPR + c] = (uint8_t)gather_bits8(w >> 2);
+}
+template <int LPR>
+__device__ __forceinline__ uint32_t load_planes(const uint8_t* row, int c) {
+  return planes_to_nibbles(row[c], row[LPR + c], row[2 * LPR + c]);
+}
+
 // Sum over aligned groups of LANES (2, 4, 8, 16 or 32) lanes, left in every lane of the
 // group, without an LDS round trip: quad swaps for partners 1 and 2, the half-row and
 // row mirrors (each pairs a lane with one in the other half of its group of 8 / 16)

@@ -81,8 +81,8 @@ struct DecodeArgs {
 
 hipError_t launch_quant_intq(int32_t format, const QuantArgs& a, hipStream_t s);
 hipError_t launch_dequant_intq(int32_t format, const DequantArgs& a, hipStream_t s);
-hipError_t launch_codec_encode(const QuantArgs& a, hipStream_t s);
-hipError_t launch_codec_dequant(const DequantArgs& a, hipStream_t s);
+hipError_t launch_codec_encode(int32_t bits, const QuantArgs& a, hipStream_t s);
+hipError_t launch_codec_dequant(int32_t bits, const DequantArgs& a, hipStream_t s);
 // Decode attention.  When the matrix-core kernel applies, the splits are merged inside
 // it (a.counters must then point at zeroed counters).  a.k_new / a.v_new, if set, fuse
 // the append of position lens[b] - 1 into the INT4 matrix-core kernel and into the
@@ -109,8 +109,12 @@ hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int32_t q_group, hipStre
 // split in LDS).
 constexpr int32_t MAX_SPLITS = 1024;
 
-// The library's own 4-bit Lloyd-Max codebook of N(0,1) (computed once, then constant).
-void codec_codebook(float levels[16], float thresholds[15]);
+// The library's own Lloyd-Max codebooks of N(0,1) at 4 or 3 bits (computed once, then
+// constant): 2^bits levels (the rest 0) and 2^bits - 1 thresholds (the rest +inf, so
+// that a count of the thresholds below a value stays below 2^bits).
+void codec_codebook(int32_t bits, float levels[16], float thresholds[15]);
+inline bool is_codec(int32_t format) { return format == KVQ_WHT_LM4 || format == KVQ_WHT_LM3; }
+inline int32_t codec_bits(int32_t format) { return format == KVQ_WHT_LM3 ? 3 : 4; }
 
 }  // namespace kvq
 

@@ -22,7 +22,7 @@ def cache_arrays(dc, fmt):
     d = dc.desc
     B, H, C, D = d.batch, d.kv_heads, d.capacity, d.head_dim
     torch.cuda.synchronize()
-    row = D if fmt == "int8" else D // 2
+    row = D if fmt == "int8" else (3 * D // 8 if fmt == "codec3" else D // 2)
     kc = dc.k_codes.cpu().numpy().reshape(B, H, C, row)
     vc = dc.v_codes.cpu().numpy().reshape(B, H, C, row)
     if fmt == "int8":

@@ -23,14 +23,14 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     assert sorted(kvq.EXPORTS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (kvq_\w+)", out))
     for n in names:
         assert n in exported, n
-    assert kvq.kvq_version() == 4
+    assert kvq.kvq_version() == 5
 
 
 def test_status_strings():
@@ -40,7 +40,7 @@ def test_status_strings():
 
 
 def test_size_queries_match_closed_forms():
-    for fmt in ("int4", "int8", "codec"):
+    for fmt in ("int4", "int8", "codec", "codec3"):
         for (B, H, D, C, gk, gv) in [(8, 8, 128, 8193, 64, 128), (1, 4, 256, 1024, 64, 128),
                                      (3, 2, 64, 17, 32, 64)]:
             d = kvq.make_desc(fmt, B, H, D, C, gk, gv)
@@ -53,8 +53,11 @@ def test_size_queries_match_closed_forms():
             elif fmt == "int8":
                 assert kvq.kvq_codes_bytes(d, 0) == B * H * C * D
                 assert kvq.kvq_scales_bytes(d, 1) == B * H * C * 4
-            else:
+            elif fmt == "codec":
                 assert kvq.kvq_codes_bytes(d, 1) == B * H * C * D // 2
+                assert kvq.kvq_scales_bytes(d, 0) == B * H * C * 4
+            else:                                   # three bit-planes of D/8 bytes
+                assert kvq.kvq_codes_bytes(d, 1) == B * H * C * 3 * D // 8
                 assert kvq.kvq_scales_bytes(d, 0) == B * H * C * 4
             assert kvq.kvq_codes_bytes(d, 2) == 0
     # effective bits with fp32 scales: K (g=64) 4.5 bits, V (g=128) 4.25 bits per element
@@ -215,6 +218,14 @@ def test_library_codebook_matches_oracle():
     c, t, _ = codec.codebook(4)
     assert np.allclose(lv, c, atol=1e-6) and np.allclose(th, t, atol=1e-6)
     assert th[7] == 0.0 and lv[7] == -lv[8]
+    assert kvq.kvq_codec_codebook_bits(4) == (lv, th)
+    lv3, th3 = kvq.kvq_codec_codebook_bits(3)
+    c3, t3, _ = codec.codebook(3)
+    assert len(lv3) == 8 and len(th3) == 7
+    assert np.allclose(lv3, c3, atol=1e-6) and np.allclose(th3, t3, atol=1e-6)
+    assert th3[3] == 0.0 and lv3[3] == -lv3[4] and np.all(np.diff(th3) > 0)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_codec_codebook_bits(2)
     # the kernels code a value by binary search over the thresholds: they must ascend
     assert np.all(np.diff(th) > 0)
 

@@ -110,3 +110,20 @@ def test_codec_row_cosine_matches_page():
     levels, _, mse = codec.codebook(4)
     err = (u - levels[idx]) ** 2
     assert abs(err.mean() - mse) < 4e-4
+
+
+def test_codec_3bit_distortion_and_cosine():
+    """At 3 bits (the page's other width) the rotated-domain MSE of Gaussian rows sits at
+    the 8-level Lloyd-Max distortion (0.03454 in Max's 1960 table), and the row cosine
+    follows from it: with centroid levels the coded row is the projection of the row,
+    so cos^2 = 1 - mse (to first order in the scale's spread)."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((4000, 256)).astype(np.float16)
+    idx, s, u = codec.encode(x, bits=3)
+    assert idx.max() == 7 and idx.min() == 0
+    levels, _, mse = codec.codebook(3)
+    assert abs(mse - 0.03454) < 2e-5
+    err = (u - levels[idx]) ** 2
+    assert abs(err.mean() - mse) < 6e-4
+    cos = codec.row_cosine(x.astype(np.float64), codec.decode(idx, s, bits=3)).mean()
+    assert abs(cos - np.sqrt(1.0 - mse)) < 2e-3, cos
