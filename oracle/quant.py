@@ -52,6 +52,29 @@ def quantize_int4(x16, group):
     return q.astype(np.int8).reshape(x.shape), s
 
 
+def quantize_int4_fp16_scale(x16, group):
+    """INT4 group quantization with fp16 scales: the page's ``quantize_4bit_group`` run
+    in the tensor's own fp16 ([KV-4bit] §2.1; the fp16 storage is the 16-bit scale its
+    §2.2 accounting assumes, 4 + 16/g bits per element).
+
+      s = fl16(a / 7), replaced by 1 when it is 0;  q = clamp(rne(fl16(x / s)), -7, 7).
+
+    Each quotient is formed in fp64 and rounded once to fp16: the correctly rounded fp16
+    quotient.  Returns (codes int8 [..., D], scales float16 [..., D // group]).
+    """
+    x = np.asarray(x16, dtype=np.float16).astype(np.float64)   # exact widening
+    D = x.shape[-1]
+    if D % group != 0:
+        raise ValueError("head_dim must be a multiple of the group size")
+    xg = x.reshape(x.shape[:-1] + (D // group, group))
+    a = np.max(np.abs(xg), axis=-1)
+    s = (a / 7.0).astype(np.float16)                            # fl16(a / 7)
+    s = np.where(s == 0, np.float16(1.0), s).astype(np.float16)
+    y = (xg / s.astype(np.float64)[..., None]).astype(np.float16)   # fl16(x / s)
+    q = np.clip(np.rint(y.astype(np.float64)), -7, 7)
+    return q.astype(np.int8).reshape(x.shape), s
+
+
 def dequantize_int4(codes, scales, group):
     """``x_hat = fl32(q * s)`` per group ([KV-4bit] §2.1, ``dequantize_4bit_group``)."""
     q = np.asarray(codes).astype(F32)

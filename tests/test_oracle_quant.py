@@ -8,7 +8,8 @@ round-half-to-even and fp32 scales.  The INT8 rule ([KV-opt] bxzpzcl.cn/news/287
 import numpy as np
 import pytest
 
-from oracle import quant
+from oracle import memory, quant
+import torch
 
 F16_ALL = np.arange(1 << 16, dtype=np.uint16).view(np.float16)
 F16_FINITE = F16_ALL[np.isfinite(F16_ALL)]
@@ -177,3 +178,51 @@ def test_int8_rules():
     assert st[0] == np.float32(1e-8) and qt[0, 0] == 6
     dq = quant.dequantize_int8(q, s)
     assert np.array_equal(dq, quant.dequantize_int8_exact(q, s).astype(np.float32))
+
+
+
+# ---- INT4 with fp16 scales (lpnh.cn/news/2042373 §2.1 computed in fp16; §2.2's 16-bit
+# scale accounting)
+
+def _page_fp16(x16, group):
+    """The page's quantize_4bit_group as torch fp16 operations on the CPU."""
+    x = torch.from_numpy(np.ascontiguousarray(x16)).reshape(-1, group)
+    scale = x.abs().amax(dim=-1, keepdim=True) / 7
+    scale = torch.where(scale == 0, torch.ones_like(scale), scale)
+    q = torch.round(x / scale).clamp(-7, 7)
+    return q.to(torch.int8).reshape(x16.shape).numpy(), scale.reshape(x16.shape[:-1] + (-1,)).numpy()
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_fp16_scale_quantizer_equals_the_pages_fp16_code(group):
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((64, 128)) * np.exp(rng.uniform(-12, 6, (64, 1)))).astype(np.float16)
+    x[3] = 0                                               # all-zero groups
+    x[5, :group] = np.float16(6e-8)                        # amax / 7 underflows to 0 in fp16
+    x[7, 0] = np.float16(65504.0)                          # the largest fp16
+    q, s = quant.quantize_int4_fp16_scale(x, group)
+    qp, sp = _page_fp16(x, group)
+    assert s.dtype == np.float16
+    assert np.array_equal(s.view(np.uint16), sp.view(np.uint16))
+    assert np.array_equal(q, qp)
+    assert np.all(s[3] == 1.0) and np.all(q[3] == 0) and s[5, 0] == 1.0
+
+
+def test_fp16_scale_quotient_rounds_in_fp16():
+    """amax 4.176 (fp16 0x442D) gives s = fl16(amax / 7) = 0.5967; x = 3.281 (0x4290)
+    then has x / s = 5.49918..., which is 5.5 in fp16 and rounds half to even to 6,
+    where rounding the fp32 quotient would give 5: the codes follow the fp16 quotient."""
+    x = np.zeros(32, dtype=np.float16)
+    x[0] = np.array(0x442D, dtype=np.uint16).view(np.float16)
+    x[1] = np.array(0x4290, dtype=np.uint16).view(np.float16)
+    q, sc = quant.quantize_int4_fp16_scale(x, 32)
+    assert np.float32(x[1]) / np.float32(sc[0]) < 5.5
+    assert q[1] == 6 and q[0] == 7
+    qp, _ = _page_fp16(x, 32)
+    assert np.array_equal(q, qp)
+
+
+def test_fp16_scale_storage_matches_the_pages_bits():
+    """fp16 scales give the page's 4 + 16/g bits: 4.25 (K, g 64) and 4.125 (V, g 128)."""
+    assert memory.int4_cache_bytes(1, 1, 1, 128, 64, scale_bytes=2) * 8 / 128 == memory.effective_bits(64)
+    assert memory.effective_bits(64) == 4.25 and memory.effective_bits(128) == 4.125
