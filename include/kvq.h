@@ -45,6 +45,8 @@
  *                        i, element 2i+1 in the high nibble, 4-bit two's complement
  *                        (values -7..7);
  *                 scales [B, Hkv, C, D/g] fp32, g = group_k for K and group_v for V.
+ *   KVQ_INT4_G16  as KVQ_INT4_G with fp16 scales [B, Hkv, C, D/g] (4 + 16/g bits per
+ *                 element, the 16-bit scale of [KV-4bit] §2.2's accounting).
  *   KVQ_INT8_TOKEN codes [B, Hkv, C, D] int8; scales [B, Hkv, C] fp32.
  *   KVQ_WHT_LM4   codes  [B, Hkv, C, D/2] uint8, unsigned 4-bit Lloyd-Max indices
  *                        (0..15) of the rotated row, same nibble order as INT4;
@@ -88,7 +90,8 @@ typedef enum {
   KVQ_INT4_G = 0,      /* group-wise symmetric INT4 ([KV-4bit] §2.1) */
   KVQ_INT8_TOKEN = 1,  /* per-token symmetric INT8 ([KV-opt] §3.1) */
   KVQ_WHT_LM4 = 2,     /* Walsh-Hadamard rotation + 4-bit Lloyd-Max codec ([LARQL]) */
-  KVQ_WHT_LM3 = 3      /* the same codec at 3 bits ([LARQL]: 3 or 4 bits) */
+  KVQ_WHT_LM3 = 3,     /* the same codec at 3 bits ([LARQL]: 3 or 4 bits) */
+  KVQ_INT4_G16 = 4     /* group-wise INT4 with fp16 scales ([KV-4bit] §2.1 in fp16) */
 } kvq_format;
 
 typedef enum {
@@ -107,7 +110,7 @@ typedef struct {
   int32_t kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;  /* D: 64, 128 or 256 */
   int32_t capacity;  /* C: slots per (b, kv head) >= 1 */
-  int32_t group_k;   /* INT4 only: K group size (default 64); power of two, 32 <= g <= D */
+  int32_t group_k;   /* INT4 formats: K group size (default 64); power of two, 32 <= g <= D */
   int32_t group_v;   /* INT4 only: V group size (default 128); same rule */
   int32_t sinks;     /* S: leading positions kept outside the ring, 0 <= S < C (0: none) */
   int32_t recent;    /* R: last positions also kept in fp16 and read from there at
@@ -141,7 +144,7 @@ int32_t kvq_check_desc(const kvq_cache_desc* desc);
 
 /* Bytes of the codes (or scales) buffer of K (kv = 0) or V (kv = 1) for `desc`;
  * 0 if the descriptor is invalid or kv is not 0/1.  INT4: B*Hkv*C*D/2 and
- * B*Hkv*C*(D/g)*4; INT8: B*Hkv*C*D and B*Hkv*C*4; codec: B*Hkv*C*D/2 (3-bit:
+ * B*Hkv*C*(D/g)*4 (fp16 scales: *2); INT8: B*Hkv*C*D and B*Hkv*C*4; codec: B*Hkv*C*D/2 (3-bit:
  * B*Hkv*C*3D/8) and B*Hkv*C*4. */
 size_t kvq_codes_bytes(const kvq_cache_desc* desc, int32_t kv);
 size_t kvq_scales_bytes(const kvq_cache_desc* desc, int32_t kv);
@@ -178,6 +181,7 @@ int32_t kvq_codec_codebook_bits(int32_t bits, float* levels, float* thresholds);
  *   at most C - S of the positions at or after S (KVQ_ERR_CAPACITY otherwise: more
  *   rows than ring slots would overwrite each other within one call).
  * INT4: per group, s = fl32(amax/7) (1 if 0), code = clamp(rne(fl32(x/s)), -7, 7).
+ * INT4 with fp16 scales: s = fl16(amax/7) (1 if 0), code = clamp(rne(fl16(x/s)), -7, 7).
  * INT8: s = max(fl32(amax/127), 1e-8), code = clamp(rne(fl32(x/s)), -128, 127).
  * Codec: y = H x / sqrt(D), s = ||x||_2 / sqrt(D), index = #{thresholds < y/s}.
  * With recent fp16 rows (R > 0) the positions among the call's last R,

@@ -24,8 +24,9 @@ import torch  # noqa: F401  (must precede the CDLL below: one HIP runtime per pr
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-KVQ_INT4_G, KVQ_INT8_TOKEN, KVQ_WHT_LM4, KVQ_WHT_LM3 = 0, 1, 2, 3
-FORMATS = {"int4": KVQ_INT4_G, "int8": KVQ_INT8_TOKEN, "codec": KVQ_WHT_LM4, "codec3": KVQ_WHT_LM3}
+KVQ_INT4_G, KVQ_INT8_TOKEN, KVQ_WHT_LM4, KVQ_WHT_LM3, KVQ_INT4_G16 = 0, 1, 2, 3, 4
+FORMATS = {"int4": KVQ_INT4_G, "int8": KVQ_INT8_TOKEN, "codec": KVQ_WHT_LM4, "codec3": KVQ_WHT_LM3,
+           "int4h": KVQ_INT4_G16}
 KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = \
     0, -1, -2, -3, -4, -5
 KVQ_MAX_BATCH = 256
@@ -260,9 +261,10 @@ class DeviceCache:
         if min(nb) == 0:
             raise KvqError(kvq_check_desc(desc), "DeviceCache")
         self.k_codes = torch.zeros(nb[0], dtype=torch.uint8, device=device)
-        self.k_scales = torch.zeros(nb[1] // 4, dtype=torch.float32, device=device)
+        # (fp32 elements covering the byte size: fp16 scales may be an odd count)
+        self.k_scales = torch.zeros((nb[1] + 3) // 4, dtype=torch.float32, device=device)
         self.v_codes = torch.zeros(nb[2], dtype=torch.uint8, device=device)
-        self.v_scales = torch.zeros(nb[3] // 4, dtype=torch.float32, device=device)
+        self.v_scales = torch.zeros((nb[3] + 3) // 4, dtype=torch.float32, device=device)
         # recent fp16 rings (INT4 caches with desc.recent > 0), else absent
         nr = kvq_recent_bytes(desc) // 2
         self.k_recent = torch.zeros(nr, dtype=torch.float16, device=device) if nr else None

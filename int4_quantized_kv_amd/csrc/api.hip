@@ -13,7 +13,7 @@ bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int32_t check_desc(const kvq_cache_desc* d) {
   if (!d) return KVQ_ERR_ARG;
-  if (d->format < KVQ_INT4_G || d->format > KVQ_WHT_LM3) return KVQ_ERR_ARG;
+  if (d->format < KVQ_INT4_G || d->format > KVQ_INT4_G16) return KVQ_ERR_ARG;
   if (d->batch < 1 || d->kv_heads < 1 || d->head_dim < 1 || d->capacity < 1)
     return KVQ_ERR_ARG;
   if (d->sinks < 0 || d->sinks >= d->capacity || d->recent < 0) return KVQ_ERR_ARG;
@@ -22,7 +22,7 @@ int32_t check_desc(const kvq_cache_desc* d) {
     return KVQ_ERR_UNSUPPORTED;
   if (d->batch > KVQ_MAX_BATCH) return KVQ_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
-  if (d->format == KVQ_INT4_G) {
+  if (d->format == KVQ_INT4_G || d->format == KVQ_INT4_G16) {
     for (int32_t g : {d->group_k, d->group_v}) {
       if (g < 1) return KVQ_ERR_ARG;
       if (!pow2(g) || g < 32 || g > d->head_dim) return KVQ_ERR_UNSUPPORTED;
@@ -40,7 +40,8 @@ bool cache_ok(const kvq_cache_desc* d, const kvq_cache* c) {
 }
 
 int32_t scales_per_row(const kvq_cache_desc* d, int32_t kv) {
-  if (d->format == KVQ_INT4_G) return d->head_dim / (kv ? d->group_v : d->group_k);
+  if (d->format == KVQ_INT4_G || d->format == KVQ_INT4_G16)
+    return d->head_dim / (kv ? d->group_v : d->group_k);
   return 1;
 }
 
@@ -146,7 +147,7 @@ size_t kvq_codes_bytes(const kvq_cache_desc* d, int32_t kv) {
 size_t kvq_scales_bytes(const kvq_cache_desc* d, int32_t kv) {
   if (check_desc(d) != KVQ_OK || (kv != 0 && kv != 1)) return 0;
   const size_t rows = (size_t)d->batch * d->kv_heads * d->capacity;
-  return rows * scales_per_row(d, kv) * sizeof(float);
+  return rows * scales_per_row(d, kv) * (d->format == KVQ_INT4_G16 ? sizeof(uint16_t) : sizeof(float));
 }
 
 size_t kvq_recent_bytes(const kvq_cache_desc* d) {

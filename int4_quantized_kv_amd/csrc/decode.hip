@@ -76,6 +76,9 @@ __device__ __forceinline__ RawRow load_raw(const DecodeArgs& a, size_t row, int 
     if (FMT == KVQ_INT4_G) {
       r.sk = a.k_scales[row * (D / a.gk) + (8 * c) / a.gk];
       r.sv = a.v_scales[row * (D / a.gv) + (8 * c) / a.gv];
+    } else if (FMT == KVQ_INT4_G16) {   // fp16 scales
+      r.sk = (float)reinterpret_cast<const _Float16*>(a.k_scales)[row * (D / a.gk) + (8 * c) / a.gk];
+      r.sv = (float)reinterpret_cast<const _Float16*>(a.v_scales)[row * (D / a.gv) + (8 * c) / a.gv];
     } else {
       r.sk = a.k_scales[row];
       r.sv = a.v_scales[row];
@@ -89,7 +92,7 @@ __device__ __forceinline__ RawRow load_raw(const DecodeArgs& a, size_t row, int 
 // are powers of two of at least 32), which is applied once per dot product instead.
 template <int FMT>
 __device__ __forceinline__ void codes_f32(const uint32_t w[2], const float2* lv2, float x[8]) {
-  if (FMT == KVQ_INT4_G) {
+  if (FMT == KVQ_INT4_G || FMT == KVQ_INT4_G16) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = (float)nib_s(w[0], j);
   } else if (FMT == KVQ_INT8_TOKEN) {
@@ -591,6 +594,7 @@ hipError_t launch_fmt(int32_t format, const DecodeArgs& a, int G, hipStream_t s)
     case KVQ_INT8_TOKEN: return launch_d<D, KVQ_INT8_TOKEN>(a, G, s);
     case KVQ_WHT_LM4: return launch_d<D, KVQ_WHT_LM4>(a, G, s);
     case KVQ_WHT_LM3: return launch_d<D, KVQ_WHT_LM3>(a, G, s);
+    case KVQ_INT4_G16: return launch_d<D, KVQ_INT4_G16>(a, G, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -5,7 +5,11 @@
 // and V groups of 128 from its section 2.2.  INT8 rule: bxzpzcl.cn/news/2871434
 // section 3.1 (per token and head: s = max(amax/127, 1e-8), q = clamp(round(x/s),
 // -128, 127)).  Scales are fp32; x/s is rounded to fp32, clamped and then rounded
-// half-to-even (clamping first is the same for integer bounds).
+// half-to-even (clamping first is the same for integer bounds).  INT4 with fp16 scales
+// runs the INT4 rule in fp16, as the page's code does on fp16 tensors: s = fl16(amax/7)
+// (1 if 0), code = rne(fl16(x/s)); each quotient is the correctly rounded fp32 division
+// rounded once more to fp16, which equals the correctly rounded fp16 quotient (fp32
+// carries more than 2 * 11 + 2 significand bits).
 //
 // Mapping: one lane owns 8 consecutive fp16 of a row (one 16-byte load); a row of
 // D elements spans D/8 consecutive lanes, a group of g elements g/8 lanes, so the
@@ -33,7 +37,7 @@ namespace {
 __device__ __forceinline__ int log2i(int x) { return 31 - __builtin_clz(x); }
 
 
-template <bool INT8>
+template <bool INT8, bool H16 = false>
 __device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
   const int isv = blockIdx.y;
   const int b = bh / a.Hkv;
@@ -74,7 +78,13 @@ __device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
         case 16: am = lane_group_max<16>(am); break;
         default: am = lane_group_max<32>(am); break;
       }
-      const float sc = INT8 ? kvq_int8_scale(am) : kvq_int4_scale(am);
+      float sc;
+      if (H16) {
+        const float s16 = (float)(_Float16)(am / 7.0f);
+        sc = s16 == 0.0f ? 1.0f : s16;
+      } else {
+        sc = INT8 ? kvq_int8_scale(am) : kvq_int4_scale(am);
+      }
       const float r = 1.0f / sc;
       int slot;
       if (sinks) {   // (uniform) sink slots ahead of the ring
@@ -103,10 +113,15 @@ __device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
       } else {
         uint32_t w = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          w |= (kvq_round_bits(fminf(fmaxf(kvq_div_exact(x[j], sc, r), -7.0f), 7.0f)) & 15u) << (4 * j);
+        for (int j = 0; j < 8; ++j) {
+          const float y = H16 ? (float)(_Float16)(x[j] / sc) : kvq_div_exact(x[j], sc, r);
+          w |= (kvq_round_bits(fminf(fmaxf(y, -7.0f), 7.0f)) & 15u) << (4 * j);
+        }
         reinterpret_cast<uint32_t*>(isv ? a.v_codes : a.k_codes)[(drow << lsh) + c] = w;
-        if ((c & (lpg - 1)) == 0) scales[(drow << gprsh) + (c >> gsh)] = sc;
+        if ((c & (lpg - 1)) == 0) {
+          if (H16) reinterpret_cast<_Float16*>(scales)[(drow << gprsh) + (c >> gsh)] = (_Float16)sc;
+          else scales[(drow << gprsh) + (c >> gsh)] = sc;
+        }
       }
     }
   }
@@ -118,6 +133,9 @@ __global__ void __launch_bounds__(256) quant_int4_kernel(QuantArgs a) {
 __global__ void __launch_bounds__(256) quant_int8_kernel(QuantArgs a) {
   for (int bh = blockIdx.z; bh < a.B * a.Hkv; bh += gridDim.z) quant_pair<true>(a, bh);
 }
+__global__ void __launch_bounds__(256) quant_int4h_kernel(QuantArgs a) {
+  for (int bh = blockIdx.z; bh < a.B * a.Hkv; bh += gridDim.z) quant_pair<false, true>(a, bh);
+}
 
 // out[b, h, t, :] = fl32(code * scale) for positions start + t, t < n; one (b, h) pair
 // per blockIdx.z, mapped as the quantizers except that a lane owns half of a code
@@ -126,7 +144,7 @@ __global__ void __launch_bounds__(256) quant_int8_kernel(QuantArgs a) {
 // (owning whole chunks, a lane's two 16-byte stores leave every other 16 bytes of a
 // 2 KiB span to the other store).
 constexpr int UD = 1;   // half-chunks per lane per iteration (more gave less: see the launch)
-template <bool INT8>
+template <bool INT8, bool H16 = false>
 __device__ __forceinline__ void dequant_pair(const DequantArgs& a, int bh) {
   const int g = INT8 ? a.D : a.g;
   const int lpr = a.D >> 3, lsh = log2i(lpr), gsh = log2i(g >> 3), gprsh = log2i(a.D / g);
@@ -158,7 +176,8 @@ __device__ __forceinline__ void dequant_pair(const DequantArgs& a, int bh) {
           sr[u] = a.scales[drow];
         } else {
           wr[u] = reinterpret_cast<const uint32_t*>(a.codes)[(drow << lsh) + c] >> (16 * (k & 1));
-          sr[u] = a.scales[(drow << gprsh) + (c >> gsh)];
+          sr[u] = H16 ? (float)reinterpret_cast<const _Float16*>(a.scales)[(drow << gprsh) + (c >> gsh)]
+                      : a.scales[(drow << gprsh) + (c >> gsh)];
         }
       }
     }
@@ -182,6 +201,9 @@ __global__ void __launch_bounds__(256) dequant_int4_kernel(DequantArgs a) {
 __global__ void __launch_bounds__(256) dequant_int8_kernel(DequantArgs a) {
   for (int bh = blockIdx.z; bh < a.B * a.Hkv; bh += gridDim.z) dequant_pair<true>(a, bh);
 }
+__global__ void __launch_bounds__(256) dequant_int4h_kernel(DequantArgs a) {
+  for (int bh = blockIdx.z; bh < a.B * a.Hkv; bh += gridDim.z) dequant_pair<false, true>(a, bh);
+}
 
 // Chunk blocks per (b, h) pair: about `target` workgroups in all, at least one per
 // pair, no more than a pair's chunks need.
@@ -199,8 +221,10 @@ hipError_t launch_quant_intq(int32_t format, const QuantArgs& a, hipStream_t s) 
   // about 4096 workgroups (16 per CU)
   const dim3 grid(blocks_per_pair(2 * pairs, (uint64_t)a.map.n * (a.D / 8), 4096), 2,
                   (uint32_t)(pairs < 65535 ? pairs : 65535));
-  return launch_kernel(format == KVQ_INT4_G ? quant_int4_kernel : quant_int8_kernel, grid,
-                       dim3(256), a, s);
+  return launch_kernel(format == KVQ_INT4_G     ? quant_int4_kernel
+                       : format == KVQ_INT4_G16 ? quant_int4h_kernel
+                                                : quant_int8_kernel,
+                       grid, dim3(256), a, s);
 }
 
 hipError_t launch_dequant_intq(int32_t format, const DequantArgs& a, hipStream_t s) {
@@ -210,8 +234,10 @@ hipError_t launch_dequant_intq(int32_t format, const DequantArgs& a, hipStream_t
   // workgroups with 2 - 16 half-chunks per iteration
   const dim3 grid(blocks_per_pair(pairs, (uint64_t)a.n * (a.D / 4), 16384), 1,
                   (uint32_t)(pairs < 65535 ? pairs : 65535));
-  return launch_kernel(format == KVQ_INT4_G ? dequant_int4_kernel : dequant_int8_kernel, grid,
-                       dim3(256), a, s);
+  return launch_kernel(format == KVQ_INT4_G     ? dequant_int4_kernel
+                       : format == KVQ_INT4_G16 ? dequant_int4h_kernel
+                                                : dequant_int8_kernel,
+                       grid, dim3(256), a, s);
 }
 
 }  // namespace kvq

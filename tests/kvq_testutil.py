@@ -28,8 +28,12 @@ def cache_arrays(dc, fmt):
     if fmt == "int8":
         kc = kc.view(np.int8)
         vc = vc.view(np.int8)
-    ks = dc.k_scales.cpu().numpy().reshape(B, H, C, -1)
-    vs = dc.v_scales.cpu().numpy().reshape(B, H, C, -1)
+    if fmt == "int4h":   # fp16 scales, D / g per row
+        ks = dc.k_scales.cpu().numpy().view(np.float16)[:B * H * C * (D // d.group_k)].reshape(B, H, C, -1)
+        vs = dc.v_scales.cpu().numpy().view(np.float16)[:B * H * C * (D // d.group_v)].reshape(B, H, C, -1)
+    else:
+        ks = dc.k_scales.cpu().numpy().reshape(B, H, C, -1)
+        vs = dc.v_scales.cpu().numpy().reshape(B, H, C, -1)
     return kc, ks, vc, vs
 
 

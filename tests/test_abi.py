@@ -40,16 +40,17 @@ def test_status_strings():
 
 
 def test_size_queries_match_closed_forms():
-    for fmt in ("int4", "int8", "codec", "codec3"):
+    for fmt in ("int4", "int8", "codec", "codec3", "int4h"):
         for (B, H, D, C, gk, gv) in [(8, 8, 128, 8193, 64, 128), (1, 4, 256, 1024, 64, 128),
                                      (3, 2, 64, 17, 32, 64)]:
             d = kvq.make_desc(fmt, B, H, D, C, gk, gv)
             assert kvq.kvq_check_desc(d) == 0
-            if fmt == "int4":
+            if fmt in ("int4", "int4h"):
+                sb = 4 if fmt == "int4" else 2
                 assert kvq.kvq_codes_bytes(d, 0) + kvq.kvq_scales_bytes(d, 0) == \
-                    memory.int4_cache_bytes(B, H, C, D, gk)
+                    memory.int4_cache_bytes(B, H, C, D, gk, scale_bytes=sb)
                 assert kvq.kvq_codes_bytes(d, 1) + kvq.kvq_scales_bytes(d, 1) == \
-                    memory.int4_cache_bytes(B, H, C, D, gv)
+                    memory.int4_cache_bytes(B, H, C, D, gv, scale_bytes=sb)
             elif fmt == "int8":
                 assert kvq.kvq_codes_bytes(d, 0) == B * H * C * D
                 assert kvq.kvq_scales_bytes(d, 1) == B * H * C * 4
