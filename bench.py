@@ -25,6 +25,7 @@ the same form; the default run is the headline above):
   llama8b-sinks  the headline shape with every layer windowed: a 4096-row ring plus 4
                  attention-sink positions, append at position 8192 then attend 4100 rows
   gemma-codec3   the gemma-codec step with the 3-bit codec
+  llama8b-int4h  the headline step on INT4 with fp16 scales (split-K kernel)
   llama8b-recent the headline step with the last 128 positions also kept, and read, in
                  fp16 (8065 rows from the INT4 codes, 128 from the fp16 rings)
   dequant        kvq_dequant of K and V of 8 Llama-3-8B-shaped layer caches to fp32
@@ -61,6 +62,8 @@ OTHER_TRAFFIC = {
     "llama8b-recent": ("profiles/decode_int4_mfma_llama8b_ctx8k_recent128_traffic.md", KERNEL_SOURCES),
     "gemma-codec3": ("profiles/decode_splitk_codec3_gemma3_4b_b4_traffic.md",
                      ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
+    "llama8b-int4h": ("profiles/decode_splitk_int4h_llama8b_ctx8k_b8_traffic.md",
+                      ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
 }
 
 
@@ -70,6 +73,7 @@ def parse():
     p.add_argument("--workload", default="llama8b",
                    choices=["llama8b", "mha7b-prefill", "mha7b-decode", "ctx128k-int4",
                             "ctx128k-int8", "gemma-codec", "gemma-codec3", "llama8b-sinks", "llama8b-recent",
+                            "llama8b-int4h",
                             "dequant"])
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
@@ -385,8 +389,9 @@ def cpu_baseline(w, seconds, L):
 
 def row_bytes(fmt, D, gk, gv):
     """Bytes of K + V codes and scales per (position, kv head)."""
-    if fmt == "int4":
-        return (D // 2 + 4 * (D // gk)) + (D // 2 + 4 * (D // gv))
+    if fmt in ("int4", "int4h"):
+        sb = 4 if fmt == "int4" else 2
+        return (D // 2 + sb * (D // gk)) + (D // 2 + sb * (D // gv))
     if fmt == "int8":
         return 2 * (D + 4)
     if fmt == "codec3":
@@ -455,6 +460,7 @@ DECODE_MODES = {   # workload id, cache format
     "ctx128k-int8": (5, "int8"),
     "gemma-codec": (4, "codec"),
     "gemma-codec3": (8, "codec3"),
+    "llama8b-int4h": (9, "int4h"),
     "llama8b-sinks": (6, "int4"),
     "llama8b-recent": (7, "int4"),
 }
@@ -573,6 +579,7 @@ def bench_decode(args):
              "ctx128k-int8": "128K ctx, B 1, INT8 per-token",
              "gemma-codec": "Gemma-3-4B shape, WHT+Lloyd-Max codec, window 1024 x29 + global x5",
              "gemma-codec3": "Gemma-3-4B shape, WHT+Lloyd-Max 3-bit codec, window 1024 x29 + global x5",
+             "llama8b-int4h": "Llama-3-8B shape, 8K ctx, B 8, INT4 with fp16 scales",
              "llama8b-sinks": "Llama-3-8B shape, 8K ctx, B 8, window 4096 + 4 sinks",
              "llama8b-recent": "Llama-3-8B shape, 8K ctx, B 8, last 128 positions in fp16"}
     return _line(args, f"decode step: effective KV GB/s ({names[args.workload]})", gbs, ms_step, cfg,
@@ -660,16 +667,16 @@ def bench_dequant(args):
 
 OTHER = {"mha7b-prefill": bench_prefill, "mha7b-decode": bench_decode, "ctx128k-int4": bench_decode,
          "ctx128k-int8": bench_decode, "gemma-codec": bench_decode, "llama8b-sinks": bench_decode,
-         "llama8b-recent": bench_decode, "gemma-codec3": bench_decode,
+         "llama8b-recent": bench_decode, "gemma-codec3": bench_decode, "llama8b-int4h": bench_decode,
          "dequant": bench_dequant}
 
 
 def _oracle_rows(fmt, x16, gk, gv, kv):
     """Oracle quantization of rows [N, D] and their exact dequantization (fp64)."""
     from oracle import codec, quant
-    if fmt == "int4":
+    if fmt in ("int4", "int4h"):
         g = gk if kv == 0 else gv
-        c, s = quant.quantize_int4(x16, g)
+        c, s = (quant.quantize_int4 if fmt == "int4" else quant.quantize_int4_fp16_scale)(x16, g)
         return (c, s), lambda cs: quant.dequantize_int4_exact(cs[0], cs[1], g)
     if fmt == "int8":
         return quant.quantize_int8(x16), lambda cs: quant.dequantize_int8_exact(cs[0], cs[1])

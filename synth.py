@@ -82,7 +82,7 @@ class Workload:
     outlier_channels: int = 0
     outlier_mult: float = 20.0
     head_scale_range: tuple = None
-    fmt: str = "int4"        # "int4", "int8", "codec", "codec3"
+    fmt: str = "int4"        # "int4", "int4h" (fp16 scales), "int8", "codec", "codec3"
     group_k: int = 64
     group_v: int = 128
     window_layers: int = 0  # number of sliding-window layers (the first ones)
@@ -121,6 +121,9 @@ WORKLOADS = {
     8: Workload(8, "gemma3-4b-window-codec3-b4", layers=34, batch=4, q_heads=8, kv_heads=4,
                 head_dim=256, context=4096, append=True, fmt="codec3",
                 window_layers=29, window=1024),
+    9: Workload(9, "llama3-8b-gqa4-ctx8k-b8-int4h", layers=32, batch=8, q_heads=32, kv_heads=8,
+                head_dim=128, context=8192, append=True, fmt="int4h",
+                outlier_channels=round(0.02 * 128)),
 }
 
 
