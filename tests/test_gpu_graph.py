@@ -3,8 +3,9 @@
 A captured ``kvq_append_decode_attn`` call replays to the eager result, replay after
 replay, with eager library work and synchronizations in between, and leaves the split
 arrival counters at zero each time.  Paths: the INT4 matrix-core kernel (in-kernel
-merge, append fused in the prologue), the codec's split-K kernel with the in-kernel
-merge, and the codec's split-K kernel followed by the merge kernel.  The eager result
+merge, append fused in the prologue) and its instances for attention sinks and for
+recent fp16 rows, the codec's split-K kernel with the in-kernel merge, and the codec's
+split-K kernel followed by the merge kernel.  The eager result
 is itself checked against the oracle ("长上下文内存大瘦身" engine three for the codec;
 lpnh.cn/news/2042373 section 2.1 and the plain softmax definition for INT4).
 """
@@ -21,15 +22,18 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 CASES = [
-    # fmt, head_dim, q heads per kv head, num_splits (0: planned)
-    ("int4", 128, 4, 0),     # matrix-core kernel, 4 splits merged in-kernel
-    ("codec", 256, 2, 0),    # split-K, in-kernel merge (append in a split of its own)
-    ("codec", 256, 2, 40),   # split-K + merge kernel
+    # fmt, head_dim, q heads per kv head, num_splits (0: planned), sinks, recent, window
+    ("int4", 128, 4, 0, 0, 0, 0),     # matrix-core kernel, 4 splits merged in-kernel
+    ("codec", 256, 2, 0, 0, 0, 0),    # split-K, in-kernel merge (append in a split of its own)
+    ("codec", 256, 2, 40, 0, 0, 0),   # split-K + merge kernel
+    ("int4", 128, 4, 0, 4, 0, 256),   # matrix-core sink instance, window 256 + 4 sinks
+    ("int4", 128, 4, 0, 0, 64, 0),    # matrix-core recent-row instance, 64 fp16 rows
 ]
 
 
-@pytest.mark.parametrize("fmt,D,G,ns", CASES, ids=[f"{c[0]}-{c[1]}-ns{c[3]}" for c in CASES])
-def test_graph_replay_matches_eager(fmt, D, G, ns):
+@pytest.mark.parametrize("fmt,D,G,ns,S,R,W", CASES,
+                         ids=[f"{c[0]}-{c[1]}-ns{c[3]}-s{c[4]}-r{c[5]}" for c in CASES])
+def test_graph_replay_matches_eager(fmt, D, G, ns, S, R, W):
     B, Hkv, P = 2, 2, 700
     L = P + 1
     Hq = Hkv * G
@@ -37,17 +41,17 @@ def test_graph_replay_matches_eager(fmt, D, G, ns):
     v = synth.kv_source((B, Hkv, L, D), 62, DEV, outlier_channels=2)
     q = synth.query((B, Hq, D), 63, DEV)
     q2 = synth.query((B, Hq, D), 64, DEV)
-    desc = kvq.make_desc(fmt, B, Hkv, D, L, min(64, D), min(128, D))
+    desc = kvq.make_desc(fmt, B, Hkv, D, L, min(64, D), min(128, D), sinks=S, recent=R)
     dc = kvq.DeviceCache(desc, DEV)
     kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, :P].contiguous(), v[:, :, :P].contiguous(), 0, P)
     kn, vn = k[:, :, P].contiguous(), v[:, :, P].contiguous()
-    ws = kvq.decode_workspace(desc, Hq, L, 0, ns, DEV)
+    ws = kvq.decode_workspace(desc, Hq, L, W, ns, DEV)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
     other = torch.empty_like(out)
     lens = [L, L]
 
     def step():
-        kvq.kvq_append_decode_attn(desc, dc.c, kn, vn, q, Hq, lens, 0, 0.0, ns, out, ws)
+        kvq.kvq_append_decode_attn(desc, dc.c, kn, vn, q, Hq, lens, W, 0.0, ns, out, ws)
 
     step()
     torch.cuda.synchronize()
@@ -61,8 +65,11 @@ def test_graph_replay_matches_eager(fmt, D, G, ns):
     else:
         qk, sk = quant.quantize_int4(np16(k), 64)
         qv, sv = quant.quantize_int4(np16(v), 128)
-        ref = attention.decode_attention(np16(q), quant.dequantize_int4_exact(qk, sk, 64),
-                                         quant.dequantize_int4_exact(qv, sv, 128), lens)
+        kh, vh = quant.dequantize_int4_exact(qk, sk, 64), quant.dequantize_int4_exact(qv, sv, 128)
+        if R:
+            kh = attention.recent_fp16_rows(kh, np16(k), lens, R)
+            vh = attention.recent_fp16_rows(vh, np16(v), lens, R)
+        ref = attention.decode_attention(np16(q), kh, vh, lens, W, sinks=S)
         assert_attn_close(eager.cpu().numpy(), ref, f"{fmt} eager")
 
     g = torch.cuda.CUDAGraph()
@@ -81,7 +88,7 @@ def test_graph_replay_matches_eager(fmt, D, G, ns):
         assert torch.allclose(out, eager, rtol=1e-4, atol=1e-5), f"replay {r}"
         assert int(counters.abs().sum()) == 0, f"split counters after replay {r}"
         # eager work between replays, through the same workspace
-        kvq.kvq_decode_attn(desc, dc.c, q2, Hq, lens, 0, 0.0, ns, other, ws)
+        kvq.kvq_decode_attn(desc, dc.c, q2, Hq, lens, W, 0.0, ns, other, ws)
         torch.cuda.synchronize()
         assert int(counters.abs().sum()) == 0, f"split counters after eager call {r}"
         assert torch.isfinite(other).all()
