@@ -239,8 +239,8 @@ int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
  *   k_f16, v_f16: device, [B, Hkv, D] fp16, the new token's rows (position lens[b] - 1).
  * Every other argument, the workspace rule and the errors are those of kvq_decode_attn
  * (KVQ_ERR_ARG also for null k_f16 / v_f16).  On the INT4 matrix-core kernel (head_dim
- * 128, V group 128) and for the codec, the new row is quantized inside the attention
- * kernel, which writes it to the cache (and, with R > 0, its fp16 row to the ring) and
+ * 128, V group 128), for the codecs and for INT4 with fp16 scales, the new row is
+ * quantized inside the attention kernel, which writes it to the cache (and, with R > 0, its fp16 row to the ring) and
  * adds it to the softmax without reading it back (one launch per step); the other
  * cases run the append kernel first. */
 int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,

@@ -24,6 +24,7 @@
 // registers.
 #include <cmath>
 
+#include "kvq_arith.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -132,10 +133,10 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, grp = tid / LPR, c = tid % LPR;
   const int len = a.lens[b];
   const int lo = a.window > 0 ? max(0, len - a.window) : 0;
-  // codec with the append fused: position len - 1 is the new row, coded in this kernel
-  // and attended from registers by the last split, which (when there are several) has
-  // no other rows: the other splits cover [lo, len - 1)
-  const bool fused = CODEC && a.k_new != nullptr;
+  // codec or INT4 with fp16 scales, with the append fused: position len - 1 is the new
+  // row, coded in this kernel and attended from registers by the last split, which
+  // (when there are several) has no other rows: the other splits cover [lo, len - 1)
+  const bool fused = (CODEC || FMT == KVQ_INT4_G16) && a.k_new != nullptr;
   const bool app_split = fused && sp == a.nsplit - 1;
   const int nrs = fused && a.nsplit > 1 ? a.nsplit - 1 : a.nsplit;   // splits with rows
   const int pt = fused ? len - 1 : len;
@@ -188,7 +189,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   Thresholds thr;
   if (app_wave) {
     if (grp < 2) newx = *reinterpret_cast<const uint4*>((grp ? a.v_new : a.k_new) + bh * D + 8 * c);
-    thr = load_thresholds(a.thr);
+    if (CODEC) thr = load_thresholds(a.thr);
   }
 
   float q[G][8];
@@ -212,13 +213,43 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     f16x8_unpack(newx, x);
     uint32_t w;
     float sc;
-    codec_encode_row<LPR>(x, c, thr, w, sc);
+    if constexpr (CODEC) {
+      codec_encode_row<LPR>(x, c, thr, w, sc);
+    } else {   // INT4 with fp16 scales: the quantize kernel's arithmetic, group amax by DPP
+      float am = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+      auto group_max = [](float v, int lanes) {   // (uniform switch)
+        switch (lanes) {
+          case 4: return lane_group_max<4>(v);
+          case 8: return lane_group_max<8>(v);
+          case 16: return lane_group_max<16>(v);
+          default: return lane_group_max<32>(v);
+        }
+      };
+      const float amk = group_max(am, a.gk >> 3), amv = group_max(am, a.gv >> 3);
+      const float s16 = (float)(_Float16)((grp == 1 ? amv : amk) / 7.0f);
+      sc = s16 == 0.0f ? 1.0f : s16;
+      w = 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float y = (float)(_Float16)(x[j] / sc);
+        w |= (kvq_round_bits(fminf(fmaxf(y, -7.0f), 7.0f)) & 15u) << (4 * j);
+      }
+    }
     if (grp < 2) {
       const size_t row = bh * a.cap + cache_slot(len - 1, a.cap, a.sinks);
       void* codes = const_cast<void*>(grp ? a.v_codes : a.k_codes);
       if (FMT == KVQ_WHT_LM3) store_planes<LPR>(static_cast<uint8_t*>(codes) + row * 3 * LPR, c, w);
       else static_cast<uint32_t*>(codes)[row * LPR + c] = w;
-      if (c == 0) const_cast<float*>(grp ? a.v_scales : a.k_scales)[row] = sc;
+      if (FMT == KVQ_INT4_G16) {   // the group's fp16 scale, from its first lane
+        const int g = grp ? a.gv : a.gk;
+        if ((8 * c) % g == 0)
+          reinterpret_cast<_Float16*>(const_cast<float*>(grp ? a.v_scales : a.k_scales))[row * (D / g) + (8 * c) / g] =
+              (_Float16)sc;
+      } else if (c == 0) {
+        const_cast<float*>(grp ? a.v_scales : a.k_scales)[row] = sc;
+      }
     }
     // group 0 takes the V row's word and scale from the lane LPR above it
     const int src = ((tid + LPR) & 63) << 2;
@@ -609,9 +640,10 @@ int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
     return plan_splits_mfma(units, span);
   if (d->format == KVQ_INT8_TOKEN && mfma_int8_eligible(d->head_dim, d->capacity, q_group))
     return plan_splits_mfma(units, span);
-  // the codec keeps one more split for the new row when its append is fused (planned
-  // for every codec call, so that the workspace query does not depend on the call)
-  const int32_t extra = is_codec(d->format) ? 1 : 0;
+  // the codecs and INT4 with fp16 scales keep one more split for the new row when the
+  // append is fused (planned for every call of those formats, so that the workspace
+  // query does not depend on the call)
+  const int32_t extra = is_codec(d->format) || d->format == KVQ_INT4_G16 ? 1 : 0;
   const int32_t target = 1024;       // workgroups: 4 per CU on 256 CUs (all resident)
   const int32_t min_rows = 64;       // positions per split worth a workgroup (short
                                      // contexts need many splits to fill the chip)

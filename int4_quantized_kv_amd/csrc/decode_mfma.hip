@@ -1610,7 +1610,8 @@ int32_t plan_splits_mfma(int32_t units, int32_t span) {
 }
 
 bool fused_append_supported(const kvq_cache_desc* d, int32_t q_group) {
-  if (is_codec(d->format)) return true;   // the codec's split-K kernel codes the row
+  // the split-K kernel codes the row for the codecs and INT4 with fp16 scales
+  if (is_codec(d->format) || d->format == KVQ_INT4_G16) return true;
   return d->format == KVQ_INT4_G &&
          mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group);
 }

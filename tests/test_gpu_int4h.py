@@ -79,17 +79,27 @@ def test_decode_attention(case):
     assert_attn_close(out.cpu().numpy(), ref, f"{case}")
 
 
-def test_append_decode_step():
-    B, H, G, D, L = 2, 2, 4, 128, 800
+@pytest.mark.parametrize("D,G,gk,gv", [(128, 4, 64, 128), (64, 8, 32, 64), (256, 2, 128, 256), (128, 1, 32, 32)])
+def test_append_decode_step(D, G, gk, gv):
+    B, H, L = 2, 2, 800
     k = synth.kv_source((B, H, L, D), 201, DEV)
     v = synth.kv_source((B, H, L, D), 202, DEV)
     q = synth.query((B, H * G, D), 203, DEV)
-    desc = kvq.make_desc("int4h", B, H, D, L)
-    dc = kvq.DeviceCache(desc, DEV)
-    kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, :L - 1].contiguous(), v[:, :, :L - 1].contiguous(), 0, L - 1)
-    out = append_decode(desc, dc, k[:, :, L - 1].contiguous(), v[:, :, L - 1].contiguous(), q, H * G, [L, L])
-    qk, sk = quant.quantize_int4_fp16_scale(np16(k), 64)
-    qv, sv = quant.quantize_int4_fp16_scale(np16(v), 128)
-    ref = attention.decode_attention(np16(q), quant.dequantize_int4_exact(qk, sk, 64),
-                                     quant.dequantize_int4_exact(qv, sv, 128), [L, L])
-    assert_attn_close(out.cpu().numpy(), ref, "int4h append + decode")
+    desc = kvq.make_desc("int4h", B, H, D, L, gk, gv)
+    dc, du = kvq.DeviceCache(desc, DEV), kvq.DeviceCache(desc, DEV)
+    for c_ in (dc, du):
+        kvq.kvq_quantize_prefill(desc, c_.c, k[:, :, :L - 1].contiguous(), v[:, :, :L - 1].contiguous(), 0, L - 1)
+    kn, vn = k[:, :, L - 1].contiguous(), v[:, :, L - 1].contiguous()
+    out = append_decode(desc, dc, kn, vn, q, H * G, [L, L])
+    # the fused step (the split-K kernel codes the new row) leaves the cache bytes of the
+    # append kernel
+    kvq.kvq_append(desc, du.c, kn, vn, [L - 1, L - 1])
+    torch.cuda.synchronize()
+    for x, y in ((dc.k_codes, du.k_codes), (dc.k_scales, du.k_scales), (dc.v_codes, du.v_codes),
+                 (dc.v_scales, du.v_scales)):
+        assert torch.equal(x, y)
+    qk, sk = quant.quantize_int4_fp16_scale(np16(k), gk)
+    qv, sv = quant.quantize_int4_fp16_scale(np16(v), gv)
+    ref = attention.decode_attention(np16(q), quant.dequantize_int4_exact(qk, sk, gk),
+                                     quant.dequantize_int4_exact(qv, sv, gv), [L, L])
+    assert_attn_close(out.cpu().numpy(), ref, f"int4h append + decode D={D} G={G}")
