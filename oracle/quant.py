@@ -13,7 +13,8 @@ Pages cited
 Readings taken where the text is silent or garbled:
   * Groups are ``g`` contiguous elements of the last axis (head_dim): the page
     reshapes "the last dim" into groups of ``group_size``.
-  * The extraction dropped ``=`` and ``==``: ``scale = torch.where(scale == 0, 1, scale)``.
+  * The page's zero-group rule lost its comparison operator in the text: read as a
+    scale that is exactly zero (a group of zeros) being replaced by 1.
   * Scales are fp32 and every step is fp32: ``s = fl32(amax / 7)``, then the
     quotient ``fl32(x / s)`` is rounded to fp32 *before* rounding to an integer.
   * Rounding is half-to-even (``torch.round`` semantics).

@@ -150,6 +150,67 @@ def test_dequant_is_fl32_of_exact_product():
     assert exact[0, 0] == float(q[0, 0]) * float(s[0, 0])
 
 
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_dequant_error_bound_every_group(g):
+    """|x - dequant(quant(x))| <= s/2 element by element, with the bound taken per group
+    from the dequantized output itself ([KV-4bit] §2.1: round to the nearest multiple of
+    the group's scale).  Adjacent groups get scales four decades apart, so a dequantizer
+    that applied one group's scale to another group would break the bound by orders of
+    magnitude."""
+    rng = np.random.default_rng(11)
+    D = 128
+    ng = D // g
+    x = rng.standard_normal((400, D))
+    mag = 10.0 ** (4 * (np.arange(ng) % 2) - 2)            # 1e-2, 1e2, 1e-2, ...
+    x = (x.reshape(400, ng, g) * mag[None, :, None]).reshape(400, D).astype(np.float16)
+    q, s = quant.quantize_int4(x, g)
+    xd = x.astype(np.float64).reshape(400, ng, g)
+    bound = s.astype(np.float64)[..., None] * (0.5 + 2.0 ** -21)
+    for deq in (quant.dequantize_int4(q, s, g).astype(np.float64),
+                quant.dequantize_int4_exact(q, s, g)):
+        err = np.abs(xd - deq.reshape(400, ng, g))
+        # fl32 of the product adds at most half an ulp of |q s| <= 7 s
+        assert np.all(err <= bound + 7 * s.astype(np.float64)[..., None] * 2.0 ** -24)
+        # the groups' outputs really live at their own scale
+        assert np.all(np.abs(deq.reshape(400, ng, g)).max(-1) <= 7 * s.astype(np.float64) * (1 + 2.0 ** -23))
+
+
+def test_dequant_hand_case_two_groups():
+    """By hand, D = 128, g = 64.  Group 0 holds 7, 3.5, 0: amax 7, s = 1, codes 7, 4
+    (half to even), 0 -> 7, 4, 0.  Group 1 holds -1400, 700, 350: amax 1400, s = 200,
+    codes -7, 4 (3.5 to even), 2 (1.75) -> -1400, 800, 400."""
+    x = np.zeros((1, 128), np.float16)
+    x[0, :3] = [7.0, 3.5, 0.0]
+    x[0, 64:67] = [-1400.0, 700.0, 350.0]
+    q, s = quant.quantize_int4(x, 64)
+    assert list(s[0]) == [1.0, 200.0]
+    for deq in (quant.dequantize_int4(q, s, 64), quant.dequantize_int4_exact(q, s, 64)):
+        assert list(deq[0, :3]) == [7.0, 4.0, 0.0]
+        assert list(deq[0, 64:67]) == [-1400.0, 800.0, 400.0]
+        assert not deq[0, 3:64].any() and not deq[0, 67:].any()
+
+
+def test_int8_dequant_bound_and_hand_case():
+    """Per-token INT8 ([KV-opt] §3.1): |x - dequant(quant(x))| <= s/2 per row, with rows
+    of very different magnitude; by hand, row 0 = (127, 63.5): s = 1, codes 127, 64 (to
+    even) -> 127, 64; row 1 = (-254, 1): s = 2, codes -127, 0 (0.5 to even) -> -254, 0."""
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((300, 128)) * 10.0 ** rng.integers(-3, 4, (300, 1))).astype(np.float16)
+    q, s = quant.quantize_int8(x)
+    sd = s.astype(np.float64)[:, None]
+    for deq in (quant.dequantize_int8(q, s).astype(np.float64), quant.dequantize_int8_exact(q, s)):
+        err = np.abs(x.astype(np.float64) - deq)
+        assert np.all(err <= sd * (0.5 + 2.0 ** -17) + 127 * sd * 2.0 ** -24)
+    h = np.zeros((2, 128), np.float16)
+    h[0, :2] = [127.0, 63.5]
+    h[1, :2] = [-254.0, 1.0]
+    qh, sh = quant.quantize_int8(h)
+    assert list(sh) == [1.0, 2.0]
+    for deq in (quant.dequantize_int8(qh, sh), quant.dequantize_int8_exact(qh, sh)):
+        assert list(deq[0, :2]) == [127.0, 64.0] and list(deq[1, :2]) == [-254.0, 0.0]
+        assert not deq[:, 2:].any()
+
+
 # ---------------------------------------------------------------- INT8 per-token
 
 
