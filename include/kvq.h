@@ -31,7 +31,9 @@
  *     calling thread; host pointers are ordinary CPU memory read before the call
  *     returns.  The caller owns every buffer.  The library allocates nothing,
  *     keeps no pointer after returning and has no mutable global state (it is
- *     re-entrant; calls on different streams touching different buffers may overlap).
+ *     re-entrant; calls on different streams touching different buffers may overlap),
+ *     with one exception: kvq_append_decode_attn_noalloc uses a scratch array the
+ *     library holds on each GPU (see there).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
  *     stream).  Nothing synchronizes the host.
  *   - Every argument is validated before any work is enqueued.  On error a negative
@@ -74,7 +76,7 @@
 extern "C" {
 #endif
 
-#define KVQ_VERSION 5
+#define KVQ_VERSION 6
 /* Largest batch the decode/append calls accept (per-sequence lengths and positions
  * travel in the kernel argument block). */
 #define KVQ_MAX_BATCH 256
@@ -85,6 +87,9 @@ extern "C" {
 #define KVQ_WS_COUNTER_BYTES 65536
 /* Largest recent fp16 span (kvq_cache_desc.recent). */
 #define KVQ_MAX_RECENT 1024
+/* Bytes of the per-GPU scratch array behind kvq_append_decode_attn_noalloc (its split
+ * counters and partials; the same layout as a decode workspace). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 typedef enum {
   KVQ_INT4_G = 0,      /* group-wise symmetric INT4 ([KV-4bit] §2.1) */
@@ -248,6 +253,27 @@ int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cach
                                int32_t q_heads, const int32_t* lens, int32_t window,
                                float softmax_scale, int32_t num_splits, float* out,
                                void* workspace, size_t ws_bytes, kvq_stream stream);
+
+/* kvq_append_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step, arguments, result and errors, without the workspace arguments.  The split
+ * counters and partials live instead in a scratch array of KVQ_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends (a static
+ * device array; nothing is allocated, by this call or any other).
+ *   - KVQ_ERR_WORKSPACE, before any launch, when the call needs more than the array
+ *     holds: kvq_decode_workspace_bytes(desc, q_heads, max(lens), window, num_splits)
+ *     > KVQ_NOALLOC_SCRATCH_BYTES.
+ *   - Every call on a GPU shares that GPU's array, and each leaves its counters zero:
+ *     calls that may overlap in time on one GPU (other streams, concurrent graph
+ *     replays) race on it and give wrong results.  Serialize them (one stream).
+ *   - The first call on a device looks the array's address up once
+ *     (hipGetSymbolAddress; KVQ_ERR_LAUNCH if that fails) and enqueues a small kernel
+ *     on `stream` that zeroes the counters. */
+int32_t kvq_append_decode_attn_noalloc(const kvq_cache_desc* desc, const kvq_cache* cache,
+                                       const void* k_f16, const void* v_f16, const void* q_f16,
+                                       int32_t q_heads, const int32_t* lens, int32_t window,
+                                       float softmax_scale, int32_t num_splits, float* out,
+                                       kvq_stream stream);
 
 /* Dequantize positions [start_pos, start_pos + n) of K (kv = 0) or V (kv = 1)
  * ([KV-4bit] §2.1 dequantize_4bit_group: code * scale; codec: s * H c[idx] / sqrt(D)).

@@ -32,6 +32,7 @@ KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, K
 KVQ_MAX_BATCH = 256
 KVQ_WS_COUNTER_BYTES = 65536
 KVQ_MAX_RECENT = 1024
+KVQ_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 # Every symbol include/kvq.h declares.
 EXPORTS = (
@@ -39,7 +40,7 @@ EXPORTS = (
     "kvq_recent_bytes",
     "kvq_plan_splits", "kvq_decode_workspace_bytes", "kvq_codec_codebook", "kvq_codec_codebook_bits",
     "kvq_quantize_prefill", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
-    "kvq_dequant",
+    "kvq_append_decode_attn_noalloc", "kvq_dequant",
 )
 
 
@@ -88,6 +89,8 @@ def _load():
         "kvq_decode_attn": (i32, [D, C, vp, i32, P(i32), i32, f32, i32, vp, vp, sz, vp]),
         "kvq_append_decode_attn": (i32, [D, C, vp, vp, vp, i32, P(i32), i32, f32, i32, vp, vp,
                                          sz, vp]),
+        "kvq_append_decode_attn_noalloc": (i32, [D, C, vp, vp, vp, i32, P(i32), i32, f32, i32, vp,
+                                                 vp]),
         "kvq_dequant": (i32, [D, C, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -228,6 +231,17 @@ def kvq_append_decode_attn(desc, cache, k, v, q, q_heads, lens, window, softmax_
         _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"), int(ws_bytes),
         _stream(stream))
     return _check(st, "kvq_append_decode_attn")
+
+
+def kvq_append_decode_attn_noalloc(desc, cache, k, v, q, q_heads, lens, window, softmax_scale,
+                                   num_splits, out, stream=None):
+    import torch
+    st = LIB.kvq_append_decode_attn_noalloc(
+        ctypes.byref(desc), ctypes.byref(cache), _ptr(k, torch.float16, "k"),
+        _ptr(v, torch.float16, "v"), _ptr(q, torch.float16, "q"), int(q_heads),
+        _i32_array(lens), int(window), float(softmax_scale), int(num_splits),
+        _ptr(out, torch.float32, "out"), _stream(stream))
+    return _check(st, "kvq_append_decode_attn_noalloc")
 
 
 def decode_workspace(desc, q_heads, max_len, window=0, num_splits=0, device="cuda"):

@@ -2,6 +2,7 @@
 // split planning and kernel dispatch.  Every check runs before anything is enqueued.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "kvq_internal.h"
 
@@ -223,6 +224,47 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache, const voi
   return quant_common(desc, cache, k_f16, v_f16, map, 1, static_cast<hipStream_t>(stream));
 }
 
+// ---- the scratch of kvq_append_decode_attn_noalloc: the split counters and partials in
+// a static device array (one copy per GPU, held until the process ends) instead of a
+// caller workspace.
+namespace {
+
+__device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::once_flag scratch_once[MAX_DEVICES];
+void* scratch_addr[MAX_DEVICES];   // the array's device address on each GPU (set once)
+
+__global__ void zero_words(uint32_t* p, int32_t n) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The array's address on the current device, looked up once per device (in host code
+// the array's name is only a stand-in; kernels get this address).  The first lookup also
+// zeroes the counters with a fill kernel on `stream` (the array starts zeroed when the
+// code object loads; this makes that explicit, with no memset node under capture).
+void* scratch_on_current_device(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::call_once(scratch_once[dev], [&] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return;
+    const int32_t words = KVQ_WS_COUNTER_BYTES / 4;
+    hipLaunchKernelGGL(zero_words, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(p), words);
+    if (hipGetLastError() != hipSuccess) return;
+    scratch_addr[dev] = p;
+  });
+  return scratch_addr[dev];
+}
+
+// Workspace argument of decode_common that selects the scratch array.
+char scratch_tag;
+void* const USE_SCRATCH = &scratch_tag;
+
+}  // namespace
+
 namespace {
 
 // Shared by kvq_decode_attn and kvq_append_decode_attn: validate, then append (when
@@ -250,6 +292,12 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   const int32_t ns = num_splits ? num_splits : kvq_plan_splits(desc, q_heads, span);
   if (ns < 1 || ns > MAX_SPLITS) return KVQ_ERR_ARG;
   const size_t need = partials_offset() + partials_bytes(desc->batch, q_heads, ns, desc->head_dim);
+  if (workspace == USE_SCRATCH) {   // kvq_append_decode_attn_noalloc, all else checked
+    if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+    workspace = scratch_on_current_device(stream);
+    if (!workspace) return KVQ_ERR_LAUNCH;
+    ws_bytes = KVQ_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16)
     return KVQ_ERR_WORKSPACE;
 
@@ -325,6 +373,16 @@ int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cach
   return decode_common(desc, cache, k_f16, v_f16, q_f16, q_heads, lens, window,
                        softmax_scale, num_splits, out, workspace, ws_bytes,
                        static_cast<hipStream_t>(stream));
+}
+
+int32_t kvq_append_decode_attn_noalloc(const kvq_cache_desc* desc, const kvq_cache* cache,
+                                       const void* k_f16, const void* v_f16, const void* q_f16,
+                                       int32_t q_heads, const int32_t* lens, int32_t window,
+                                       float softmax_scale, int32_t num_splits, float* out,
+                                       kvq_stream stream) {
+  if (!k_f16 || !v_f16) return KVQ_ERR_ARG;
+  return decode_common(desc, cache, k_f16, v_f16, q_f16, q_heads, lens, window, softmax_scale,
+                       num_splits, out, USE_SCRATCH, 0, static_cast<hipStream_t>(stream));
 }
 
 int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t kv,

@@ -23,14 +23,14 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     assert sorted(kvq.EXPORTS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (kvq_\w+)", out))
     for n in names:
         assert n in exported, n
-    assert kvq.kvq_version() == 5
+    assert kvq.kvq_version() == 6
 
 
 def test_status_strings():
@@ -136,6 +136,14 @@ def test_error_paths_enqueue_nothing():
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_append_decode_attn, d, c, FAKE, 0, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_append_decode_attn, d, c, FAKE, FAKE, FAKE, 8, [65, 10], 0, 0.0, 0, FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_append_decode_attn, d, c, FAKE, FAKE, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, FAKE, ws - 1, 0)
+    # the no-allocation step: the same checks, and calls whose counters and partials
+    # exceed the library's scratch array are rejected before anything is enqueued
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_append_decode_attn_noalloc, d, c, 0, FAKE, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_append_decode_attn_noalloc, d, c, FAKE, FAKE, FAKE, 8, [65, 10], 0, 0.0, 0, FAKE, 0)
+    wide = kvq.make_desc("int4", 64, 8, 128, 64)
+    need = kvq.kvq_decode_workspace_bytes(wide, 64, 64, 0, 8)
+    assert need > kvq.KVQ_NOALLOC_SCRATCH_BYTES
+    _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_append_decode_attn_noalloc, wide, c, FAKE, FAKE, FAKE, 64, [64] * 64, 0, 0.0, 8, FAKE, 0)
     # the split counters bound batch * kv_heads
     big = kvq.make_desc("int4", 256, 128, 128, 64)
     _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_decode_attn, big, c, FAKE, 128, [10] * 256, 0, 0.0, 1, FAKE, FAKE, 1 << 40, 0)
