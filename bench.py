@@ -86,7 +86,17 @@ def parse():
                    help="timed CPU work of the oracle baseline (whole (batch, kv head) units)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="time a plain 1 GiB device copy and a 1 GiB read-only reduction instead "
-                        "(attainable bandwidth; the known-size reference for the HBM counters)")
+                        "(the known-size reference for the HBM counters)")
+    p.add_argument("--calibrate-read", action="store_true",
+                   help="sweep the streaming-read kernel (libkvq_bench.so) over launch shapes on "
+                        "4 GiB and print the table (the attainable read rate every line reports)")
+    p.add_argument("--timeline", action="store_true",
+                   help="phase timeline of the headline step's kernel from the probe build "
+                        "libkvq_timeline.so (python -m int4_quantized_kv_amd.build --timeline)")
+    p.add_argument("--no-attainable", action="store_true",
+                   help="leave out the attainable-read measurement of the line")
+    p.add_argument("--cpu-workers", type=int, default=None,
+                   help="processes of the all-core oracle leg (default: the affinity set, at most 16)")
     return p.parse_args()
 
 
@@ -105,6 +115,12 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args)
         return
+    if args.calibrate_read:
+        calibrate_read(args)
+        return
+    if args.timeline:
+        timeline(args)
+        return
     import int4_quantized_kv_amd as kvq
     import synth
 
@@ -113,6 +129,7 @@ def main():
     if args.workload != "llama8b":
         line = OTHER[args.workload](args)
         line["roofline"]["traffic"] = recorded_traffic(*OTHER_TRAFFIC[args.workload])
+        add_attainable(args, line)
         print(json.dumps(line), flush=True)
         return
     w = synth.WORKLOADS[2]
@@ -276,8 +293,10 @@ def main():
         "cpu_baseline": None,
     }
 
+    del layers, ws
+    add_attainable(args, result)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, L)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, L, args.cpu_workers)
 
     print(json.dumps(result), flush=True)
 
@@ -337,7 +356,211 @@ def calibrate_copy(args):
     print(json.dumps({"calibration": res, "steps": args.steps}), flush=True)
 
 
-def cpu_baseline(w, seconds, L):
+# ---------------------------------------------------------------------------------------
+# Attainable read rate: the hand-written streaming-read kernel of libkvq_bench.so
+# (csrc/stream_read.hip) over 4 GiB, 16-byte loads, `unroll` in flight per lane.
+
+READ_BYTES = 4 << 30
+# launch shapes every line tries (workgroups of 256 lanes, loads in flight per lane,
+# non-temporal); the best median of them is the line's attainable read rate
+READ_CONFIGS = [(2048, 8, 0), (4096, 8, 0), (8192, 4, 0), (4096, 8, 1), (16384, 4, 0)]
+
+
+def _bench_lib():
+    lib = ctypes.CDLL(os.path.join(ROOT, "int4_quantized_kv_amd", "libkvq_bench.so"))
+    fn = lib.kvqb_stream_read
+    fn.restype = ctypes.c_int32
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    return fn
+
+
+def _read_rate(fn, buf, sink, grid, unroll, nt, reps):
+    """Median GB/s of `reps` event-timed launches of the streaming read."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        st = fn(buf.data_ptr(), READ_BYTES, grid, unroll, nt, sink.data_ptr(), ctypes.c_void_p(stream))
+        if st:
+            raise RuntimeError(f"kvqb_stream_read failed ({st})")
+
+    launch()
+    torch.cuda.synchronize()
+    rates = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        launch()
+        e1.record()
+        torch.cuda.synchronize()
+        rates.append(READ_BYTES / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    rates.sort()
+    return rates[len(rates) // 2]
+
+
+def attainable_read(configs=READ_CONFIGS, reps=7):
+    """(best median GB/s, its config) of the streaming read over a 4 GiB buffer."""
+    import torch
+    fn = _bench_lib()
+    buf = torch.ones(READ_BYTES // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.empty(max(c[0] for c in configs), dtype=torch.int32, device="cuda:0")
+    best = (0.0, None)
+    table = []
+    for grid, unroll, nt in configs:
+        r = _read_rate(fn, buf, sink, grid, unroll, nt, reps)
+        table.append({"workgroups": grid, "loads_in_flight": unroll, "nontemporal": bool(nt),
+                      "GBps": round(r, 1)})
+        if r > best[0]:
+            best = (r, table[-1])
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best[0], best[1], table
+
+
+def add_attainable(args, line):
+    """Put the attainable read rate into the line, and the roofline kernel's share of it."""
+    if args.no_attainable:
+        return
+    rate, cfg, _ = attainable_read()
+    line["attainable_read_GBps"] = round(rate, 1)
+    line["attainable_read_config"] = dict(cfg, bytes=READ_BYTES,
+                                          kernel="libkvq_bench.so: stream_read_kernel")
+    roof = line.get("roofline")
+    if roof and roof.get("unit") == "GB/s":
+        roof["frac_of_attainable"] = round(roof["achieved"] / rate, 4)
+
+
+def calibrate_read(args):
+    configs = [(g, u, nt) for g in (1024, 2048, 4096, 8192, 16384, 32768)
+               for u in (2, 4, 8, 16) for nt in (0, 1)]
+    rate, cfg, table = attainable_read(configs, reps=max(5, args.steps // 2))
+    print(json.dumps({"stream_read": table, "best": cfg, "bytes": READ_BYTES}), flush=True)
+
+
+def timeline(args):
+    """Per-phase timeline of the headline step's matrix-core kernel, from the probe build
+    (libkvq_timeline.so: the same sources with -DKVQ_TIMELINE, each workgroup recording
+    the 100 MHz real-time counter at its phase points).  The 32 layers of the step run
+    from a HIP graph as in the timed bench; the stamps of the last replay are read back.
+    Prints one JSON line: per phase, the median over layers of (min, median, max) over
+    the layer's workgroups (waves for loop ends), in microseconds from the layer's first
+    workgroup entry, plus the gap from each layer's last exit to the next layer's first
+    entry and the loop-end medians per XCD."""
+    import numpy as np
+    import torch
+    import int4_quantized_kv_amd as kvq
+    from int4_quantized_kv_amd import _binding
+    import synth
+    lib = _binding._load(os.path.join(ROOT, "int4_quantized_kv_amd", "libkvq_timeline.so"))
+    dev = "cuda:0"
+    w = synth.WORKLOADS[2]
+    nl = args.layers or w.layers
+    B, Hq, Hkv, D, S = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.context
+    L = S + 1
+    desc = kvq.make_desc("int4", B, Hkv, D, L, w.group_k, w.group_v)
+    ns = kvq.kvq_plan_splits(desc, Hq, L)
+    need = kvq.kvq_decode_workspace_bytes(desc, Hq, L)
+    nwg = ns * Hkv * B
+    tl_off = (need + 255) // 256 * 256
+    layers = []
+    for li in range(nl):
+        k, v, q, kn, vn = synth.layer_inputs(w, li, dev)
+        lay = Layer()
+        lay.dc = kvq.DeviceCache(desc, dev)
+        kvq.kvq_quantize_prefill(desc, lay.dc.c, k, v, 0, S)
+        del k, v
+        lay.q, lay.kn, lay.vn = q, kn, vn
+        lay.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        lay.ws = torch.zeros((tl_off + nwg * 128) // 4, dtype=torch.float32, device=dev)
+        lay.cref = ctypes.byref(lay.dc.c)
+        layers.append(lay)
+    torch.cuda.synchronize()
+    lens = (ctypes.c_int32 * B)(*([L] * B))
+    dref = ctypes.byref(desc)
+
+    def step(stream):
+        sp = ctypes.c_void_p(stream)
+        for lay in layers:
+            st = lib.kvq_append_decode_attn(dref, lay.cref, lay.kn.data_ptr(), lay.vn.data_ptr(),
+                                            lay.q.data_ptr(), Hq, lens, 0, 0.0, 0, lay.out.data_ptr(),
+                                            lay.ws.data_ptr(), lay.ws.numel() * 4, sp)
+            if st:
+                raise kvq.KvqError(st, "kvq_append_decode_attn (timeline build)")
+
+    run = _runner(args, step)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    stamps = [lay.ws.view(torch.int64)[tl_off // 8: tl_off // 8 + nwg * 16].cpu().numpy()
+              .reshape(nwg, 16).astype(np.int64) for lay in layers]
+    us = lambda t: t / 100.0   # noqa: E731  (100 MHz counter)
+    per = {k: [] for k in ("entry", "q_in_lds", "loop_start", "loop_end", "published", "arrived", "exit")}
+    gaps, xcc_end, tiles = [], {}, []
+    for li, st in enumerate(stamps):
+        t0 = st[:, 0].min()
+        rel = lambda col: us(st[:, col] - t0)   # noqa: E731
+        per["entry"].append(np.percentile(rel(0), [0, 50, 100]))
+        per["q_in_lds"].append(np.percentile(rel(2), [0, 50, 100]))
+        per["loop_start"].append(np.percentile(rel(3), [0, 50, 100]))
+        ends = us(st[:, 4:12] - t0).ravel()
+        per["loop_end"].append(np.percentile(ends, [0, 50, 100]))
+        per["published"].append(np.percentile(rel(12), [0, 50, 100]))
+        per["arrived"].append(np.percentile(rel(13), [0, 50, 100]))
+        per["exit"].append(np.percentile(rel(14), [0, 50, 100]))
+        if li + 1 < len(stamps):
+            gaps.append(us(stamps[li + 1][:, 0].min() - st[:, 14].max()))
+        xcc = (st[:, 1] >> 32) & 0xF
+        for x in np.unique(xcc):
+            xcc_end.setdefault(int(x), []).append(float(np.median(us(st[xcc == x][:, 4:12] - t0))))
+        t = st[:, 15]
+        tiles.extend(((t >> (8 * wv)) & 255).tolist() for wv in range(8))
+    tl = np.array(tiles).ravel()
+    out = {"timeline_us": {k: [round(float(x), 2) for x in np.median(np.array(v), axis=0)]
+                           for k, v in per.items()},
+           "columns": ["min", "median", "max"],
+           "gap_to_next_layer_us": [round(float(x), 2) for x in np.percentile(gaps, [0, 50, 100])] if gaps else None,
+           "loop_end_median_by_xcc_us": {k: round(float(np.median(v)), 2) for k, v in sorted(xcc_end.items())},
+           "tiles_per_wave": [int(tl.min()), float(np.median(tl)), int(tl.max())],
+           "workgroups": nwg, "layers": nl, "num_splits": ns,
+           "workload": w.name, "entry": "kvq_append_decode_attn (timeline probe build)"}
+    print(json.dumps(out), flush=True)
+
+
+def _blas_threads():
+    from threadpoolctl import threadpool_info
+    return max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
+
+
+def _cpu_meta(workers_used):
+    return {"os_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas_threads_default": _blas_threads(), "blas_threads_used": 1,
+            "threads_used": workers_used}
+
+
+def _allcore_unit(task):
+    """One worker of the all-core leg: `reps` headline units (append the new row,
+    exact dequantization of 8193 rows, fp64 attention for the unit's query heads) over
+    the unit's arrays, on one core; returns (start, end) wall times of its timed work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention, quant
+    k, v, kn, vn, qq, L, reps = task
+    (ck, sk), (cv, sv) = quant.quantize_int4(k, 64), quant.quantize_int4(v, 128)
+    with threadpool_limits(1):
+        t0 = time.time()
+        for _ in range(reps):
+            nk, nsk = quant.quantize_int4(kn[None], 64)
+            nv, nsv = quant.quantize_int4(vn[None], 128)
+            kh = quant.dequantize_int4_exact(np.concatenate([ck, nk]), np.concatenate([sk, nsk]), 64)
+            vh = quant.dequantize_int4_exact(np.concatenate([cv, nv]), np.concatenate([sv, nsv]), 128)
+            attention.decode_attention(qq[None], kh[None, None], vh[None, None], [L])
+        t1 = time.time()
+    return t0, t1
+
+
+def cpu_baseline(w, seconds, L, workers=None):
     """The oracle (never tuned) timed on host cores, one (batch, kv head) unit of a layer
     at a time, layer after layer, until `seconds` of timed work: quantize the new row,
     dequantize the cache exactly, fp64 softmax attention for the unit's G query heads.
@@ -377,11 +600,33 @@ def cpu_baseline(w, seconds, L):
     row = 140
     unit_bytes = S * row + row + 2 * 128 * 2 + G * 128 * 2 + G * 128 * 4
     full = w.batch * w.kv_heads * w.layers
-    return {"value": round(units * unit_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{units} of the step's {full} (layer, batch, kv head) units "
-                      f"(append + exact dequant + fp64 attention over {L} positions), "
-                      f"{dt:.2f} s timed; a full step extrapolates to {dt * full / units:.1f} s"}
+    res = {"value": round(units * unit_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "kind": "oracle",
+           "sample": f"{units} of the step's {full} (layer, batch, kv head) units "
+                     f"(append + exact dequant + fp64 attention over {L} positions), "
+                     f"{dt:.2f} s timed on one core; a full step extrapolates to "
+                     f"{dt * full / units:.1f} s"}
+    res.update(_cpu_meta(1))
+    # ---- all-core leg: one process per core of the affinity set (at most 16), each
+    # running whole units of the first layer over its own arrays for ~seconds / 2
+    import multiprocessing as mp
+    nw = workers or min(16, len(os.sched_getaffinity(0)))
+    reps = max(1, int(0.5 * seconds / (dt / units)))
+    k, v, q, kn, vn = (t.cpu().numpy() for t in synth.layer_inputs(w, 0, "cuda:0"))
+    tasks = []
+    for i in range(nw):
+        b, h = divmod(i % (w.batch * w.kv_heads), w.kv_heads)
+        tasks.append((k[b, h], v[b, h], kn[b, h], vn[b, h], q[b, h * G:(h + 1) * G], L, reps))
+    del k, v
+    with mp.get_context("spawn").Pool(nw) as pool:
+        spans = pool.map(_allcore_unit, tasks)
+    wall = max(e for _, e in spans) - min(b0 for b0, _ in spans)
+    res["all_cores"] = {"value": round(nw * reps * unit_bytes / wall / 1e9, 4), "unit": "GB/s",
+                        "cores": nw, "processes": nw,
+                        "sample": f"{nw} processes x {reps} units each (append + exact dequant + "
+                                  f"fp64 attention over {L} positions), {wall:.2f} s wall, one "
+                                  f"BLAS thread per process"}
+    return res
 
 
 # ---------------------------------------------------------------------------------------
@@ -574,6 +819,9 @@ def bench_decode(args):
            "launch": "eager" if args.eager else "hip-graph",
            "num_splits": kvq.kvq_plan_splits(layers[-1].desc, Hq,
                                              attended_rows(L, layers[-1].W, layers[-1].desc.sinks))}
+    extra = {}
+    if fmt in ("codec", "codec3"):
+        extra["row_cosine"] = codec_row_cosine(w, fmt, layers, nl, dev)
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(w, fmt, args.cpu_seconds, L)
     names = {"mha7b-decode": "MHA-7B shape, 20K ctx, B 8", "ctx128k-int4": "128K ctx, B 1, INT4",
              "ctx128k-int8": "128K ctx, B 1, INT8 per-token",
@@ -583,8 +831,36 @@ def bench_decode(args):
              "llama8b-sinks": "Llama-3-8B shape, 8K ctx, B 8, window 4096 + 4 sinks",
              "llama8b-recent": "Llama-3-8B shape, 8K ctx, B 8, last 128 positions in fp16"}
     return _line(args, f"decode step: effective KV GB/s ({names[args.workload]})", gbs, ms_step, cfg,
-                 roof, cpu, {"tok_per_s": round(B / (ms_step * 1e-3), 1), "bytes_per_step": step_bytes,
-                             "wall_s_timed": round(wall, 4)})
+                 roof, cpu, dict({"tok_per_s": round(B / (ms_step * 1e-3), 1), "bytes_per_step": step_bytes,
+                                  "wall_s_timed": round(wall, 4)}, **extra))
+
+
+def codec_row_cosine(w, fmt, layers, nl, dev):
+    """Cosine between each fp16 source row and its codec reconstruction (kvq_dequant of
+    the cached codes), over the prefilled rows a window layer's ring and a global layer
+    hold: layers 0 and nl - 1, K and V, every (batch, kv head)."""
+    import torch
+    import int4_quantized_kv_amd as kvq
+    import synth
+    cos = []
+    for li in sorted({0, nl - 1}):
+        lay = layers[li]
+        k, v, _, _, _ = synth.layer_inputs(w, li, dev)
+        S = w.context
+        cap = lay.desc.capacity
+        # (a window layer's ring slot of position S - cap now holds the appended row S)
+        lo = max(0, S - cap + 1) if lay.W else 0
+        for kv, src in ((0, k), (1, v)):
+            out = torch.empty((w.batch, w.kv_heads, S - lo, w.head_dim), dtype=torch.float32, device=dev)
+            kvq.kvq_dequant(lay.desc, lay.dc.c, kv, lo, S - lo, out)
+            x = src[:, :, lo:S].double()
+            y = out.double()
+            cos.append(((x * y).sum(-1) / (x.norm(dim=-1) * y.norm(dim=-1))).flatten())
+        del k, v
+    c = torch.cat(cos)
+    return {"mean": round(float(c.mean()), 5), "min": round(float(c.min()), 5), "rows": int(c.numel()),
+            "layers": sorted({0, nl - 1}), "page_figure_4bit": 0.9954,
+            "what": "cosine of fp16 source row vs its dequantized codec row (kvq_dequant)"}
 
 
 def bench_prefill(args):
@@ -742,10 +1018,10 @@ def cpu_baseline_decode(w, fmt, seconds, L):
         layer += 1
         del k, v
     full = w.batch * w.kv_heads * w.layers
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return dict({"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{units} of the step's {full} (layer, batch, kv head) units "
                       f"({'append + ' if w.append else ''}exact dequant + fp64 attention), "
-                      f"{dt:.2f} s timed"}
+                      f"{dt:.2f} s timed"}, **_cpu_meta(1))
 
 
 def cpu_baseline_prefill(w, seconds):
@@ -769,9 +1045,9 @@ def cpu_baseline_prefill(w, seconds):
                 dt += time.perf_counter() - t0
             units += 1
     nbytes = units * S * (2 * D * 2 + row_bytes("int4", D, w.group_k, w.group_v))
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return dict({"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{units} of the layer's {w.batch * w.kv_heads} (batch, kv head) units "
-                      f"({S} K and V rows each), {dt:.2f} s timed"}
+                      f"({S} K and V rows each), {dt:.2f} s timed"}, **_cpu_meta(1))
 
 
 def cpu_baseline_dequant(w, seconds):
@@ -796,9 +1072,9 @@ def cpu_baseline_dequant(w, seconds):
                 dt += time.perf_counter() - t0
             units += 1
     per = S * ((D // 2 + 4 * (D // w.group_k) + 4 * D) + (D // 2 + 4 * (D // w.group_v) + 4 * D))
-    return {"value": round(units * per / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return dict({"value": round(units * per / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{units} of a layer's {w.batch * w.kv_heads} (batch, kv head) units "
-                      f"({S} K and V rows each), {dt:.2f} s timed"}
+                      f"({S} K and V rows each), {dt:.2f} s timed"}, **_cpu_meta(1))
 
 
 if __name__ == "__main__":

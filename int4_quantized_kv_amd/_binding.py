@@ -64,12 +64,13 @@ class KvqError(RuntimeError):
         super().__init__(f"{where}: {status_str(status)} ({status})")
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
+def _load(path=LIB_PATH):
+    """Open the library at `path` (the timeline probe build has the same C ABI)."""
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build the HIP library first "
+            f"{path} is missing: build the HIP library first "
             "(python -m int4_quantized_kv_amd.build)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     i32, sz, vp, f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
     D, C = P(kvq_cache_desc), P(kvq_cache)

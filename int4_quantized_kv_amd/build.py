@@ -11,6 +11,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvq.so")
+# the benchmark's streaming-read reference (not part of the library's ABI)
+BENCH_OUT = os.path.join(HERE, "libkvq_bench.so")
+BENCH_SOURCES = ["stream_read.hip"]
 BUILD_DIR = os.path.join(HERE, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
@@ -37,17 +40,24 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# The timeline probe: the same sources built with -DKVQ_TIMELINE, where the matrix-core
+# decode kernel records the real-time counter at its phase points (bench.py --timeline).
+# Built on request only (python -m int4_quantized_kv_amd.build --timeline).
+TIMELINE_OUT = os.path.join(HERE, "libkvq_timeline.so")
+
+
+def build(verbose=False, timeline=False):
+    bdir = os.path.join(BUILD_DIR, "timeline") if timeline else BUILD_DIR
+    os.makedirs(bdir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         if not os.path.exists(path):
             continue
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, "-c", path, "-o", obj]
+        cmd = [HIPCC, *FLAGS, *(["-DKVQ_TIMELINE"] if timeline else []), "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -63,15 +73,32 @@ def build(verbose=False):
             print("\n".join(noisy))
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    tmp = OUT + ".tmp"
+    if timeline:
+        _link(objs, TIMELINE_OUT)
+        return TIMELINE_OUT
+    _link(objs, OUT)
+    bench_objs = []
+    for src in BENCH_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        r = subprocess.run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj],
+                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout.decode(errors="replace"))
+            raise RuntimeError("hipcc failed for: " + src)
+        bench_objs.append(obj)
+    _link(bench_objs, BENCH_OUT)
+    return OUT
+
+
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
         sys.stderr.write(r.stdout.decode(errors="replace"))
-        raise RuntimeError("link of libkvq.so failed")
-    os.replace(tmp, OUT)
-    return OUT
+        raise RuntimeError("link of " + os.path.basename(out) + " failed")
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, timeline="--timeline" in sys.argv))

@@ -186,11 +186,17 @@ struct Slot {
   static constexpr int DMA = 4 + (NGK <= 2 ? 1 : 2) + 1;   // transfers per tile
 };
 
+// Cache policy of the tile transfers: non-temporal ("nt"), since every cache byte is read
+// once per step.  A plain streaming-read kernel on this machine moves ~12% more bytes per
+// second with nt loads than with plain ones (6.2 -> 7.0 TB/s at its best launch shape).
+constexpr int CPOL_NT = 2;
+template <int AUX = 0>
 __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds((gbl_vptr)g, (lds_vptr)l, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gbl_vptr)g, (lds_vptr)l, 16, 0, AUX);
 }
+template <int AUX = 0>
 __device__ __forceinline__ void dma4(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds((gbl_vptr)g, (lds_vptr)l, 4, 0, 0);
+  __builtin_amdgcn_global_load_lds((gbl_vptr)g, (lds_vptr)l, 4, 0, AUX);
 }
 
 template <int N>
@@ -204,6 +210,25 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// ---------------------------------------------------------------------------------------
+// Timeline probe (a separate build, -DKVQ_TIMELINE: libkvq_timeline.so; the library itself
+// is built without it).  Each workgroup records the 100 MHz real-time counter at its phase
+// points into a.stamps[workgroup * 16 + i]:
+//   0 entry (wave 0)   1 XCC id << 32 | HW_ID   2 q in LDS (after the prologue barrier)
+//   3 wave 0's loop start   4 .. 11 loop end of waves 0 .. 7
+//   12 partial published (thread 0)   13 arrival counted (thread 0)
+//   14 exit (thread 0: after the merge in the last workgroup of a unit)
+//   15 tiles processed by waves 0 .. 7, 8 bits each
+#ifdef KVQ_TIMELINE
+__device__ __forceinline__ uint64_t tl_now() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ void tl_put(const DecodeArgs& a, int i, uint64_t v) {
+  if (a.stamps) {
+    const size_t wg = blockIdx.x + (size_t)gridDim.x * (blockIdx.y + (size_t)gridDim.y * blockIdx.z);
+    a.stamps[wg * 16 + i] = v;
+  }
+}
+#endif
 
 // Per-lane byte offsets of the transfers, fixed for the whole kernel: lane l fills LDS
 // row position P = l / 4, chunk slot l % 4 with chunk (l % 4) ^ f(P) of tile row
@@ -255,12 +280,12 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int
     const uint8_t* vsb = vs + rb * 4;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      dma16(kb + o.kv[T], lb + L::K_OFF + 1024 * T);
-      dma16(vb + o.kv[T], lb + L::V_OFF + 1024 * T);
+      dma16<CPOL_NT>(kb + o.kv[T], lb + L::K_OFF + 1024 * T);
+      dma16<CPOL_NT>(vb + o.kv[T], lb + L::V_OFF + 1024 * T);
     }
 #pragma unroll
-    for (int h = 0; h < (NGK <= 2 ? 1 : 2); ++h) dma4(ksb + o.sk[h], lb + L::SK_OFF + 256 * h);
-    dma4(vsb + o.sv, lb + L::SV_OFF);
+    for (int h = 0; h < (NGK <= 2 ? 1 : 2); ++h) dma4<CPOL_NT>(ksb + o.sk[h], lb + L::SK_OFF + 256 * h);
+    dma4<CPOL_NT>(vsb + o.sv, lb + L::SV_OFF);
     return;
   }
   auto row_of = [&](int rho) -> size_t {
@@ -277,14 +302,14 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
     const size_t row = row_of(o.rho[T]);
-    dma16(kc + row * (HD / 2) + o.kap16, lb + L::K_OFF + 1024 * T);
-    dma16(vc + row * (HD / 2) + o.kap16, lb + L::V_OFF + 1024 * T);
+    dma16<CPOL_NT>(kc + row * (HD / 2) + o.kap16, lb + L::K_OFF + 1024 * T);
+    dma16<CPOL_NT>(vc + row * (HD / 2) + o.kap16, lb + L::V_OFF + 1024 * T);
   }
   const size_t srow = row_of(lane & 31);
 #pragma unroll
   for (int h = 0; h < (NGK <= 2 ? 1 : 2); ++h)
-    dma4(ks + srow * (NGK * 4) + (o.sk[h] - (lane & 31) * NGK * 4), lb + L::SK_OFF + 256 * h);
-  dma4(vs + srow * 4, lb + L::SV_OFF);
+    dma4<CPOL_NT>(ks + srow * (NGK * 4) + (o.sk[h] - (lane & 31) * NGK * 4), lb + L::SK_OFF + 256 * h);
+  dma4<CPOL_NT>(vs + srow * 4, lb + L::SV_OFF);
 }
 
 // Position sets.  A head's q.K needs G * NGK of the 16 MFMA columns.  When that is at
@@ -299,10 +324,58 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int
 __host__ __device__ constexpr int position_sets(int g, int ngk) { return g * ngk <= 8 ? 2 : 1; }
 
 // Online-softmax state of one wave (per lane: query head of column r).
+// P' = p * sV enters P.V as fp16 hi + lo parts; with small V scales (a head whose values
+// are ~1e-3) the lo part would fall below fp16's normal range and lose its low bits.  So
+// the wave carries a power-of-two normalizer 2^lvs of the V scales (wave-uniform): the
+// exponent takes it as an added integer, so p~ = p * 2^lvs and l, oacc hold 2^lvs times
+// their plain values; the combine entry's maximum subtracts lvs again, which cancels it.
+// lvs moves (and l, oacc by the same exact power of two) only when a tile's largest V
+// scale times 2^lvs leaves [1/16, 16]; it then puts that product in [1, 2).
 struct State {
   floatx4 oacc[8];
   float m, l;
+  int lvs;
 };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// fp32 pair -> fp16 pair, round to nearest even (one v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pk_f16_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
+// P' = p~ * sV as fp16 hi (round to nearest) + lo (the exact fp32 remainder, rounded to
+// nearest): ~22 significant bits while p~ * sV stays within fp16's normal range.
+__device__ __forceinline__ void split_hi_lo(float q0, float q1, uint32_t& hi, uint32_t& lo) {
+  hi = pk_f16_rne(q0, q1);
+  const f16x2 h = __builtin_bit_cast(f16x2, hi);
+  lo = pk_f16_rne(__builtin_fmaf((float)h.x, -1.0f, q0), __builtin_fmaf((float)h.y, -1.0f, q1));
+}
+
+// The softmax / V-scale update of one tile.  `mx` is the tile's score maximum of the
+// lane's column (over the 4 lanes j) and `svmax` the largest V scale among the rows the
+// lane holds.  Returns mq = m * scale - lvs, the exponent offset of this tile's p~.
+__device__ __forceinline__ float tile_update(State& st, float mx, float svmax, float qscale) {
+  const float m_new = fmaxf(st.m, mx);
+  // V-scale band, by ballots: some lane above 16, or every lane below 1/16
+  const float x = __builtin_amdgcn_ldexpf(svmax, st.lvs);
+  const bool vmove = __any(x > 16.0f) || !__any(x >= 0.0625f);
+  if (__any(m_new > st.m) || vmove) {
+    int nl = st.lvs;
+    if (vmove) {   // (rare) the wave's largest V scale of the tile
+      float t = max_over_j(svmax);
+      t = fmaxf(t, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                       0, __builtin_bit_cast(int, t), 0x128, 0xF, 0xF, false)));   // lane r ^ 8
+      t = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t)));
+      nl = 1 - __builtin_amdgcn_frexp_expf(t);   // t * 2^nl in [1, 2)
+    }
+    const float corr = fast_exp2(__builtin_fmaf(st.m - m_new, qscale, (float)(nl - st.lvs)));
+    st.l *= corr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.oacc[e] *= corr;
+    st.m = m_new;
+    st.lvs = nl;
+  }
+  return __builtin_fmaf(st.m, qscale, -(float)st.lvs);
+}
 
 // Per-lane LDS offsets, fixed for the whole kernel (see position_sets).
 struct LaneOffs {
@@ -444,17 +517,18 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
   if (NTB == 2) mx = fmaxf(mx, fmaxf(fmaxf(z[NTB - 1][0], z[NTB - 1][1]),
                                      fmaxf(z[NTB - 1][2], z[NTB - 1][3])));
   mx = max_over_j(mx);
-  const float m_new = fmaxf(st.m, mx);
-  if (__any(m_new > st.m)) {
-    const float corr = fast_exp2((st.m - m_new) * qscale);
-    st.l *= corr;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.oacc[e] *= corr;
-    st.m = m_new;
+  float svmax;
+  {
+    const floatx4 v0 = __builtin_bit_cast(floatx4, td.sv[0]);
+    svmax = fmaxf(fmaxf(v0[0], v0[1]), fmaxf(v0[2], v0[3]));
+    if (NTB == 2) {
+      const floatx4 v1 = __builtin_bit_cast(floatx4, td.sv[NTB - 1]);
+      svmax = fmaxf(svmax, fmaxf(fmaxf(v1[0], v1[1]), fmaxf(v1[2], v1[3])));
+    }
   }
-  const float mq = st.m * qscale;
+  const float mq = tile_update(st, mx, svmax, qscale);
 
-  // ---- P' = P * sV as fp16 hi + lo, in the B layout: k slot 4T + i (S = 1) or
+  // ---- P' = p~ * sV as fp16 hi + lo, in the B layout: k slot 4T + i (S = 1) or
   // 4 * set + i (S = 2, zeros in the other set's four slots)
   H8 phi, plo;
 #pragma unroll
@@ -465,13 +539,7 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
       const float p0 = fast_exp2(__builtin_fmaf(z[T][i], qscale, -mq));
       const float p1 = fast_exp2(__builtin_fmaf(z[T][i + 1], qscale, -mq));
       st.l += p0 + p1;
-      const float q0 = p0 * sv[i];
-      const float q1 = p1 * sv[i + 1];
-      const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(q0, q1));
-      const float r0 = __builtin_fmaf((float)h.x, -1.0f, q0);
-      const float r1 = __builtin_fmaf((float)h.y, -1.0f, q1);
-      phi.u[2 * T + i / 2] = __builtin_bit_cast(uint32_t, h);
-      plo.u[2 * T + i / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+      split_hi_lo(p0 * sv[i], p1 * sv[i + 1], phi.u[2 * T + i / 2], plo.u[2 * T + i / 2]);
     }
   }
   // S = 2: the lane's two dwords go to its set's slots (the other two are zero)
@@ -605,11 +673,11 @@ __device__ __forceinline__ void issue_tile8(const DecodeArgs& a, size_t row0, in
     const size_t rb = row0 + (size_t)sbase;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      dma16(kc + rb * HD + o.kv[T], lb + L::K_OFF + 1024 * T);
-      dma16(vc + rb * HD + o.kv[T], lb + L::V_OFF + 1024 * T);
+      dma16<CPOL_NT>(kc + rb * HD + o.kv[T], lb + L::K_OFF + 1024 * T);
+      dma16<CPOL_NT>(vc + rb * HD + o.kv[T], lb + L::V_OFF + 1024 * T);
     }
     const float* sc = o.sv ? a.v_scales : a.k_scales;
-    dma4(sc + rb + o.srow, lb + L::SK_OFF);
+    dma4<CPOL_NT>(sc + rb + o.srow, lb + L::SK_OFF);
     return;
   }
   auto row_of = [&](int rho) -> size_t {
@@ -626,11 +694,11 @@ __device__ __forceinline__ void issue_tile8(const DecodeArgs& a, size_t row0, in
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
     const size_t row = row_of(o.rho[T]);
-    dma16(kc + row * HD + o.ch16[T], lb + L::K_OFF + 1024 * T);
-    dma16(vc + row * HD + o.ch16[T], lb + L::V_OFF + 1024 * T);
+    dma16<CPOL_NT>(kc + row * HD + o.ch16[T], lb + L::K_OFF + 1024 * T);
+    dma16<CPOL_NT>(vc + row * HD + o.ch16[T], lb + L::V_OFF + 1024 * T);
   }
   const float* sc = o.sv ? a.v_scales : a.k_scales;
-  dma4(sc + row_of(o.srow), lb + L::SK_OFF);
+  dma4<CPOL_NT>(sc + row_of(o.srow), lb + L::SK_OFF);
 }
 
 struct LaneOffs8 {
@@ -737,31 +805,18 @@ __device__ __forceinline__ void process_tile8(const uint8_t* lb, const LaneOffs8
   // ---- online softmax (the 4 lanes j of a column share a head)
   float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
   mx = max_over_j(mx);
-  const float m_new = fmaxf(st.m, mx);
-  if (__any(m_new > st.m)) {
-    const float corr = fast_exp2((st.m - m_new) * qscale);
-    st.l *= corr;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.oacc[e] *= corr;
-    st.m = m_new;
-  }
-  const float mq = st.m * qscale;
-
-  // ---- P' = P * sV as fp16 hi + lo; the column's part goes to B
   const floatx4 sv = __builtin_bit_cast(floatx4, td.sv);
+  const float mq = tile_update(st, mx, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), qscale);
+
+  // ---- P' = p~ * sV as fp16 hi + lo; the column's part goes to B
   H4 pb;
 #pragma unroll
   for (int i = 0; i < 4; i += 2) {
     const float p0 = fast_exp2(__builtin_fmaf(z[i], qscale, -mq));
     const float p1 = fast_exp2(__builtin_fmaf(z[i + 1], qscale, -mq));
     st.l += p0 + p1;
-    const float q0 = p0 * sv[i];
-    const float q1 = p1 * sv[i + 1];
-    const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(q0, q1));
-    const float r0 = __builtin_fmaf((float)h.x, -1.0f, q0);
-    const float r1 = __builtin_fmaf((float)h.y, -1.0f, q1);
-    const uint32_t hi = __builtin_bit_cast(uint32_t, h);
-    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    uint32_t hi, lo;
+    split_hi_lo(p0 * sv[i], p1 * sv[i + 1], hi, lo);
     pb.u[i / 2] = lo_col ? lo : hi;
   }
 
@@ -1089,7 +1144,13 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   constexpr int NE = RC ? 2 * WAVES : WAVES;   // combine entries (a second per wave: recent rows)
   __shared__ __attribute__((aligned(16))) float s_mlc[2 * NE * G];      // combine max / sum
   __shared__ __attribute__((aligned(16))) uint8_t s_q[G * 2 * HD];      // the G query rows
+#ifdef KVQ_TIMELINE
+  __shared__ uint32_t s_tl_tiles[WAVES];
+#endif
 
+#ifdef KVQ_TIMELINE
+  const uint64_t tl_entry = tl_now();
+#endif
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   // wave-uniform: keeps tile positions, ring addresses and base pointers in SGPRs
@@ -1190,6 +1251,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   for (int e = 0; e < 8; ++e) st.oacc[e] = (floatx4){0.f, 0.f, 0.f, 0.f};
   st.m = empty_max(a.qscale);
   st.l = 0.0f;
+  st.lvs = 0;
   half8 qb[4 * S];
   float qbias = 0.0f;
 
@@ -1212,6 +1274,9 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     else wait_vmcnt<0>();
   }
   lds_barrier();
+#ifdef KVQ_TIMELINE
+  const uint64_t tl_q = tl_now();
+#endif
   // (recent fp16 rows: the first batch's loads go out behind the first tiles)
   [[maybe_unused]] RecentRows rrows;
   if constexpr (RC) rrows = recent_preload(a, unit, len, lo_pos, sp, a.nsplit, wave, lane, fused);
@@ -1304,7 +1369,14 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     }
   }
 
+#ifdef KVQ_TIMELINE
+  const uint64_t tl_loop = tl_now();
+  int tl_tiles = 0;
+#endif
   for (int k = 0; cur != NONE; ++k) {
+#ifdef KVQ_TIMELINE
+    ++tl_tiles;
+#endif
     int nn = NONE;
     if (nxt != NONE) {
       const int id = 2 * WAVES + (int)lds_claim(&s_claim, lane);
@@ -1329,6 +1401,24 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     nxt = nn;
   }
   wait_vmcnt<0>();   // (also the q staging, when this wave had no tile)
+#ifdef KVQ_TIMELINE
+  {
+    const uint64_t tl_end = tl_now();
+    if (lane == 0) {
+      tl_put(a, 4 + wave, tl_end);
+      s_tl_tiles[wave] = (uint32_t)tl_tiles;
+      if (wave == 0) {
+        uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | 20);   // HW_REG_XCC_ID
+        uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);     // HW_REG_HW_ID
+        tl_put(a, 0, tl_entry);
+        tl_put(a, 1, ((uint64_t)xcc << 32) | hw);
+        tl_put(a, 2, tl_q);
+        tl_put(a, 3, tl_loop);
+      }
+    }
+    wait_vmcnt<0>();
+  }
+#endif
 
   // ---- combine the waves' column sets (and, in the appending workgroup, the new row)
   // through LDS: lane (r, j) holds O[column r][8(4j + i) + e] in oacc[e][i]; a head sits
@@ -1391,8 +1481,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         s_o[qhead * ORS + opad(8 * (4 * j + i) + e)] = st.oacc[e][i];
-    if (j == 0) {
-      s_m[qhead * NE + wave] = st.m * a.qscale;   // base-2 units
+    if (j == 0) {   // base-2 units; - lvs cancels the V-scale normalizer in l and o
+      s_m[qhead * NE + wave] = __builtin_fmaf(st.m, a.qscale, -(float)st.lvs);
       s_l[qhead * NE + wave] = l_run;
     }
   }
@@ -1460,12 +1550,26 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     store_new_row<NGK>(a, &s_new, row0 + (size_t)(SK ? cache_slot(len - 1, a.cap, a.sinks)
                                                        : (len - 1) % a.cap), lane);
   uint32_t* cnt = a.counters + unit;
+#ifdef KVQ_TIMELINE
+  const uint64_t tl_pub = tl_now();
+#endif
   wait_vmcnt<0>();
   __syncthreads();
   if (threadIdx.x == 0)
     s_last = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int np = nps;                                    // partials to merge
+#ifdef KVQ_TIMELINE
+  const uint64_t tl_arr = tl_now();
+  if (threadIdx.x == 0) {
+    uint64_t packed = 0;
+    for (int w = 0; w < WAVES; ++w) packed |= (uint64_t)(s_tl_tiles[w] & 255u) << (8 * w);
+    tl_put(a, 12, tl_pub);
+    tl_put(a, 13, tl_arr);
+    tl_put(a, 15, packed);
+    if (s_last != np - 1) tl_put(a, 14, tl_now());
+  }
+#endif
   if (s_last != np - 1) return;
 
   // ---- the last arrival merges the np partials of its G heads with the log-sum-exp
@@ -1556,6 +1660,9 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     }
   }
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#ifdef KVQ_TIMELINE
+  if (threadIdx.x == 0) tl_put(a, 14, tl_now());
+#endif
 }
 
 template <int G, bool SK, bool RC>

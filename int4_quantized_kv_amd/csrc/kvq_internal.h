@@ -76,6 +76,8 @@ struct DecodeArgs {
   uint16_t* v_recent;    // (INT4 matrix-core kernel with recent > 0), else null
   int32_t recent;        // positions [len - recent, len) are read from the rings (each
                          // split takes a share of them)
+  uint64_t* stamps;      // timeline probe builds only (-DKVQ_TIMELINE): phase timestamps
+                         // of each workgroup of the matrix-core kernel, else null
   int32_t lens[KVQ_MAX_BATCH];
 };
 

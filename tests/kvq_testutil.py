@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 import int4_quantized_kv_amd as kvq
+from oracle import attention, codec, quant
 
 # Attention tolerance against the fp64 oracle over the same dequantized values.
 ATTN_MAX_ABS = 2e-3
@@ -73,3 +74,83 @@ def append_decode(desc, dc, k_new, v_new, q, q_heads, lens, window=0, scale=0.0,
                                num_splits, out, ws)
     torch.cuda.synchronize()
     return out
+
+
+# ----------------------------------------------------------------------------- codec rows
+
+def pack_planes(idx):
+    """3-bit indices [..., D] (0..7) -> the library's rows [..., 3 * D / 8] uint8: byte c of
+    plane p holds bit p of indices 8c .. 8c + 7 (index 8c + j in bit j)."""
+    idx = np.asarray(idx, dtype=np.uint8)
+    D = idx.shape[-1]
+    bits = idx.reshape(*idx.shape[:-1], D // 8, 8)
+    planes = [np.packbits((bits >> p) & 1, axis=-1, bitorder="little")[..., 0] for p in range(3)]
+    return np.concatenate(planes, axis=-1)
+
+
+def unpack_planes(rows):
+    rows = np.asarray(rows, dtype=np.uint8)
+    n = rows.shape[-1] // 3
+    out = 0
+    for p in range(3):
+        bits = np.unpackbits(rows[..., p * n:(p + 1) * n, None], axis=-1, bitorder="little")
+        out = out + (bits.astype(np.uint8) << p)
+    return out.reshape(*rows.shape[:-1], 8 * n)
+
+
+def codec_indices(codes, fmt):
+    """Stored codec rows -> indices [..., D]."""
+    if fmt == "codec3":
+        return unpack_planes(codes)
+    return quant.unpack_nibbles(codes, signed=False)
+
+
+def check_codec_rows(got_idx, got_scale, x16, bits):
+    """The codec's GPU rule: scales within 1e-5 relative of the oracle's, and an index
+    may differ from the oracle's only where the oracle's normalized rotated value lies
+    within 1e-5 of a decision threshold.  Returns the number of differing indices."""
+    idx, s, u = codec.encode(x16, bits=bits)
+    assert np.allclose(got_scale, s, rtol=1e-5, atol=0), "codec row scales differ"
+    mism = got_idx != idx
+    if mism.any():
+        _, thr, _ = codec.codebook(bits)
+        d = np.min(np.abs(u[mism][:, None] - thr[None, :]), axis=1)
+        assert np.all(d <= 1e-5), f"{int((d > 1e-5).sum())} codes differ away from a threshold"
+    return int(mism.sum())
+
+
+def slot_of(p, cap, sinks=0):
+    """Slot of position p: p below the sinks, else the ring of cap - sinks slots."""
+    return p if p < sinks else sinks + (p - sinks) % (cap - sinks)
+
+
+def codec_hat_from_device(dc, fmt, k16, v16, lens, window=0):
+    """Rows attention is checked over, for a codec cache coded on the GPU.
+
+    k16, v16: fp16 [B, Hkv, N, D] source rows indexed by position (N >= max(lens)).
+    Every position a decode at ``lens`` attends is read back from its slot in the
+    device cache and held to the codec rule of ``check_codec_rows`` against the
+    oracle's own encoding of the same fp16 row; the oracle then decodes those indices
+    (where the rule leaves two indices correct, the one the GPU stored is used, so both
+    sides attend over identical values).  Positions not attended keep the oracle's
+    codes.  Returns (k_hat, v_hat) fp64 [B, Hkv, N, D] and the number of indices that
+    differ from the oracle's.
+    """
+    d = dc.desc
+    bits = 3 if fmt == "codec3" else 4
+    kc, ks, vc, vs = cache_arrays(dc, fmt)
+    out = []
+    nmis = 0
+    for x16, codes, scales in ((k16, kc, ks), (v16, vc, vs)):
+        idx, sc, _ = codec.encode(x16, bits=bits)
+        idx, sc = idx.copy(), sc.copy()
+        for b, ln in enumerate(lens):
+            pos = attention.attended_positions(int(ln), window, d.sinks)
+            slots = np.array([slot_of(int(p), d.capacity, d.sinks) for p in pos])
+            g_idx = codec_indices(codes[b][:, slots], fmt)
+            g_sc = scales[b][:, slots, 0]
+            nmis += check_codec_rows(g_idx, g_sc, x16[b][:, pos], bits)
+            idx[b][:, pos] = g_idx
+            sc[b][:, pos] = g_sc
+        out.append(codec.decode(idx, sc, bits=bits))
+    return out[0], out[1], nmis

@@ -13,29 +13,11 @@ import torch
 import int4_quantized_kv_amd as kvq
 import synth
 from oracle import attention, codec
-from tests.kvq_testutil import append_decode, assert_attn_close, cache_arrays, decode, np16
+from tests.kvq_testutil import (append_decode, assert_attn_close, cache_arrays, codec_hat_from_device,
+                                decode, np16, pack_planes, unpack_planes)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-
-
-def pack_planes(idx):
-    """Indices [..., D] (0..7) -> the library's rows [..., 3 * D / 8] uint8."""
-    idx = np.asarray(idx, dtype=np.uint8)
-    D = idx.shape[-1]
-    bits = idx.reshape(*idx.shape[:-1], D // 8, 8)
-    planes = [np.packbits((bits >> p) & 1, axis=-1, bitorder="little")[..., 0] for p in range(3)]
-    return np.concatenate(planes, axis=-1)
-
-
-def unpack_planes(rows):
-    rows = np.asarray(rows, dtype=np.uint8)
-    n = rows.shape[-1] // 3
-    out = 0
-    for p in range(3):
-        bits = np.unpackbits(rows[..., p * n:(p + 1) * n, None], axis=-1, bitorder="little")
-        out = out + (bits.astype(np.uint8) << p)
-    return out.reshape(*rows.shape[:-1], 8 * n)
 
 
 def test_plane_helpers_round_trip():
@@ -153,9 +135,7 @@ def test_fused_append_decode_3bit(D, G, window):
                  (dc.v_scales, du.v_scales)):
         assert torch.equal(x, y)
     assert_attn_close(out.cpu().numpy(), out_u.cpu().numpy().astype(np.float64), "fused vs unfused")
-    kidx, ks, _ = codec.encode(np16(k), bits=3)
-    vidx, vs, _ = codec.encode(np16(v), bits=3)
-    ref = attention.decode_attention(np16(q), codec.decode(kidx, ks, bits=3), codec.decode(vidx, vs, bits=3),
-                                     [L, L], window)
-    rel = np.linalg.norm(out.cpu().numpy() - ref) / np.linalg.norm(ref)
-    assert rel < 1e-3, rel   # a code that flips at a threshold moves one value by a level gap
+    # the oracle over the rows the fused call stored (each held to the codec rule first)
+    kh, vh, _ = codec_hat_from_device(dc, "codec3", np16(k), np16(v), [L, L], window)
+    ref = attention.decode_attention(np16(q), kh, vh, [L, L], window)
+    assert_attn_close(out.cpu().numpy(), ref, f"codec3 fused D={D} w={window}")

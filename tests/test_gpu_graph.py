@@ -16,7 +16,7 @@ import torch
 import int4_quantized_kv_amd as kvq
 import synth
 from oracle import attention, codec, quant
-from tests.kvq_testutil import assert_attn_close, np16
+from tests.kvq_testutil import assert_attn_close, codec_hat_from_device, np16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -56,12 +56,10 @@ def test_graph_replay_matches_eager(fmt, D, G, ns, S, R, W):
     step()
     torch.cuda.synchronize()
     eager = out.clone()
-    if fmt == "codec":   # a code that flips at a threshold moves one value by a level gap
-        kidx, ksc, _ = codec.encode(np16(k))
-        vidx, vsc, _ = codec.encode(np16(v))
-        ref = attention.decode_attention(np16(q), codec.decode(kidx, ksc), codec.decode(vidx, vsc), lens)
-        rel = np.linalg.norm(eager.cpu().numpy() - ref) / np.linalg.norm(ref)
-        assert rel < 1e-3, rel
+    if fmt == "codec":   # over the rows the GPU coded (each held to the codec rule)
+        kh, vh, _ = codec_hat_from_device(dc, fmt, np16(k), np16(v), lens, W)
+        ref = attention.decode_attention(np16(q), kh, vh, lens, W)
+        assert_attn_close(eager.cpu().numpy(), ref, f"{fmt} eager")
     else:
         qk, sk = quant.quantize_int4(np16(k), 64)
         qv, sv = quant.quantize_int4(np16(v), 128)
