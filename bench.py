@@ -473,7 +473,7 @@ def timeline(args):
         del k, v
         lay.q, lay.kn, lay.vn = q, kn, vn
         lay.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-        lay.ws = torch.zeros((tl_off + nwg * 128) // 4, dtype=torch.float32, device=dev)
+        lay.ws = torch.zeros((tl_off + nwg * 256) // 4, dtype=torch.float32, device=dev)
         lay.cref = ctypes.byref(lay.dc.c)
         layers.append(lay)
     torch.cuda.synchronize()
@@ -493,16 +493,19 @@ def timeline(args):
     for _ in range(3):
         run()
     torch.cuda.synchronize()
-    stamps = [lay.ws.view(torch.int64)[tl_off // 8: tl_off // 8 + nwg * 16].cpu().numpy()
-              .reshape(nwg, 16).astype(np.int64) for lay in layers]
+    stamps = [lay.ws.view(torch.int64)[tl_off // 8: tl_off // 8 + nwg * 32].cpu().numpy()
+              .reshape(nwg, 32).astype(np.int64) for lay in layers]
     us = lambda t: t / 100.0   # noqa: E731  (100 MHz counter)
-    per = {k: [] for k in ("entry", "q_in_lds", "loop_start", "loop_end", "published", "arrived", "exit")}
+    per = {k: [] for k in ("entry", "kernel_args", "q_in_lds", "first_tile", "loop_start", "loop_end",
+                           "published", "arrived", "exit")}
     gaps, xcc_end, tiles = [], {}, []
     for li, st in enumerate(stamps):
         t0 = st[:, 0].min()
         rel = lambda col: us(st[:, col] - t0)   # noqa: E731
         per["entry"].append(np.percentile(rel(0), [0, 50, 100]))
+        per["kernel_args"].append(np.percentile(rel(16), [0, 50, 100]))
         per["q_in_lds"].append(np.percentile(rel(2), [0, 50, 100]))
+        per["first_tile"].append(np.percentile(rel(17), [0, 50, 100]))
         per["loop_start"].append(np.percentile(rel(3), [0, 50, 100]))
         ends = us(st[:, 4:12] - t0).ravel()
         per["loop_end"].append(np.percentile(ends, [0, 50, 100]))
@@ -517,8 +520,24 @@ def timeline(args):
         t = st[:, 15]
         tiles.extend(((t >> (8 * wv)) & 255).tolist() for wv in range(8))
     tl = np.array(tiles).ravel()
+    # where the loop-end spread comes from: per workgroup, its last wave's loop end
+    # (relative to the layer's first entry), by split index; the spread inside a
+    # workgroup; and whether late workgroups started late
+    by_sp, intra, corr = {}, [], []
+    for st in stamps:
+        t0 = st[:, 0].min()
+        wg_end = us(st[:, 4:12].max(1) - t0)
+        intra.extend(us(st[:, 4:12].max(1) - st[:, 4:12].min(1)).tolist())
+        for sp in range(ns):
+            by_sp.setdefault(sp, []).extend(wg_end[sp::ns].tolist())
+        corr.append(float(np.corrcoef(us(st[:, 0] - t0), wg_end)[0, 1]))
+    out_extra = {"wg_last_loop_end_by_split_us": {sp: [round(float(x), 2) for x in np.percentile(v, [0, 50, 100])]
+                                                 for sp, v in by_sp.items()},
+                 "loop_end_spread_inside_wg_us": [round(float(x), 2) for x in np.percentile(intra, [0, 50, 90, 100])],
+                 "corr_entry_vs_wg_end": round(float(np.median(corr)), 3)}
     out = {"timeline_us": {k: [round(float(x), 2) for x in np.median(np.array(v), axis=0)]
                            for k, v in per.items()},
+           **out_extra,
            "columns": ["min", "median", "max"],
            "gap_to_next_layer_us": [round(float(x), 2) for x in np.percentile(gaps, [0, 50, 100])] if gaps else None,
            "loop_end_median_by_xcc_us": {k: round(float(np.median(v)), 2) for k, v in sorted(xcc_end.items())},

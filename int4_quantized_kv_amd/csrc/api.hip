@@ -301,10 +301,10 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   if (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16)
     return KVQ_ERR_WORKSPACE;
 #ifdef KVQ_TIMELINE
-  // the probe build: 16 timestamps per workgroup after the partials, when the
+  // the probe build: 32 timestamp slots per workgroup after the partials, when the
   // workspace has room for them
   const size_t tl_off = (need + 255) & ~(size_t)255;
-  const size_t tl_bytes = (size_t)ns * desc->kv_heads * desc->batch * 16 * sizeof(uint64_t);
+  const size_t tl_bytes = (size_t)ns * desc->kv_heads * desc->batch * 32 * sizeof(uint64_t);
   uint64_t* stamps = ws_bytes >= tl_off + tl_bytes
                          ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + tl_off)
                          : nullptr;
@@ -330,6 +330,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   a.gv = desc->group_v;
   a.window = window;
   a.nsplit = ns;
+
 #ifdef KVQ_TIMELINE
   a.stamps = stamps;
 #endif

@@ -170,6 +170,7 @@ typedef __attribute__((address_space(1))) void* gbl_vptr;
 // free of bank conflicts for 32- and for 64-bank LDS.  K scales are stored group-major
 // ([g][32 rows]) so a lane reads its 4 rows of its group with one ds_read_b128.
 constexpr int NB = 3;
+constexpr int DEPTH = NB - 1;   // tiles in flight behind the one being processed
 
 __device__ __forceinline__ int rowinv(int rho) { return 4 * (rho >> 2) + ((rho + (rho >> 2)) & 3); }
 __device__ __forceinline__ int rowperm(int P) { return 4 * (P >> 2) + (((P & 3) - (P >> 2)) & 3); }
@@ -203,6 +204,16 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Wait until at most n tiles' transfers (DMA each) are outstanding, n in 0 .. D <= 3
+// (uniform; the immediate must be a constant, hence the cases).
+template <int DMA, int D>
+__device__ __forceinline__ void wait_vmcnt_tiles(int n) {
+  static_assert(D >= 1 && D <= 3, "pipeline depth");
+  if (D >= 3 && n >= 3) wait_vmcnt<3 * DMA>();
+  else if (D >= 2 && n == 2) wait_vmcnt<2 * DMA>();
+  else if (n == 1) wait_vmcnt<DMA>();
+  else wait_vmcnt<0>();
+}
 
 // Workgroup barrier over LDS data: waits for this wave's LDS operations only.
 // __syncthreads()'s fence also waits for every outstanding global load (vmcnt 0), here
@@ -214,18 +225,20 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------------------------------
 // Timeline probe (a separate build, -DKVQ_TIMELINE: libkvq_timeline.so; the library itself
 // is built without it).  Each workgroup records the 100 MHz real-time counter at its phase
-// points into a.stamps[workgroup * 16 + i]:
+// points into a.stamps[workgroup * TL_SLOTS + i]:
 //   0 entry (wave 0)   1 XCC id << 32 | HW_ID   2 q in LDS (after the prologue barrier)
 //   3 wave 0's loop start   4 .. 11 loop end of waves 0 .. 7
 //   12 partial published (thread 0)   13 arrival counted (thread 0)
 //   14 exit (thread 0: after the merge in the last workgroup of a unit)
 //   15 tiles processed by waves 0 .. 7, 8 bits each
+//   16 kernel arguments read (wave 0)   17 wave 0's first tile landed
 #ifdef KVQ_TIMELINE
+constexpr int TL_SLOTS = 32;
 __device__ __forceinline__ uint64_t tl_now() { return __builtin_amdgcn_s_memrealtime(); }
 __device__ __forceinline__ void tl_put(const DecodeArgs& a, int i, uint64_t v) {
   if (a.stamps) {
     const size_t wg = blockIdx.x + (size_t)gridDim.x * (blockIdx.y + (size_t)gridDim.y * blockIdx.z);
-    a.stamps[wg * 16 + i] = v;
+    a.stamps[wg * TL_SLOTS + i] = v;
   }
 }
 #endif
@@ -1163,6 +1176,11 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // wherever it reuses those registers; a load before the loop would make it wait ahead
   // of every transfer.)
   uint8_t* qstage = s_q;
+#ifdef KVQ_TIMELINE
+  // (an empty asm that consumes the q pointer: the stamp follows its kernel-argument load)
+  asm volatile("" ::"s"(a.q), "s"(a.k_codes));
+  const uint64_t tl_karg = tl_now();
+#endif
   if (wave == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -1255,24 +1273,27 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   half8 qb[4 * S];
   float qbias = 0.0f;
 
-  // The pipeline: the first two tiles start before the loop; step k claims tile k + 2,
-  // starts it into slot (k + 2) % NB and processes tile k from slot k % NB, so two tiles
-  // stay in flight behind the one being processed.  `cur` / `nxt` are the tiles of
-  // steps k and k + 1 (NONE past the end; claims only grow, so once a claim is past the
-  // end every later one is too).
+  // The pipeline: the first DEPTH tiles start before the loop; step k claims tile
+  // k + DEPTH, starts it into slot (k + DEPTH) % NB and processes tile k from slot k % NB,
+  // so DEPTH tiles stay in flight behind the one being processed.  tq[i] is the tile of
+  // step k + i (NONE past the end; claims only grow, so once a claim is past the end
+  // every later one is too).
   constexpr int NONE = -1;
-  int cur = wave < nts ? wave : NONE;
-  int nxt = wave + WAVES < nts ? wave + WAVES : NONE;
-  if (cur != NONE) issue(ps + TL * cur, ring);
-  if (nxt != NONE) issue(ps + TL * nxt, ring + L::BYTES);
+  int tq[DEPTH];
+  int nq = 0;   // tiles started (the first NONE ends them)
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) {
+    const int id = wave + i * WAVES;
+    tq[i] = id < nts ? id : NONE;
+    if (tq[i] != NONE) {
+      issue(ps + TL * tq[i], ring + i * L::BYTES);
+      ++nq;
+    }
+  }
 
   // wave 0 waits for its q (and new-row) transfers alone, which are older than its
   // tiles'; the barrier then publishes them (and the zeroed claim counter) to every wave
-  if (wave == 0) {
-    if (nxt != NONE) wait_vmcnt<2 * DMA>();
-    else if (cur != NONE) wait_vmcnt<DMA>();
-    else wait_vmcnt<0>();
-  }
+  if (wave == 0) wait_vmcnt_tiles<DMA, DEPTH>(nq);
   lds_barrier();
 #ifdef KVQ_TIMELINE
   const uint64_t tl_q = tl_now();
@@ -1372,33 +1393,39 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 #ifdef KVQ_TIMELINE
   const uint64_t tl_loop = tl_now();
   int tl_tiles = 0;
+  uint64_t tl_first = 0;
 #endif
-  for (int k = 0; cur != NONE; ++k) {
+  for (int k = 0; tq[0] != NONE; ++k) {
 #ifdef KVQ_TIMELINE
     ++tl_tiles;
 #endif
     int nn = NONE;
-    if (nxt != NONE) {
-      const int id = 2 * WAVES + (int)lds_claim(&s_claim, lane);
+    if (tq[DEPTH - 1] != NONE) {
+      const int id = DEPTH * WAVES + (int)lds_claim(&s_claim, lane);
       nn = id < nts ? id : NONE;
     }
     if (nn != NONE) {
-      issue(ps + TL * nn, ring + ((k + 2) % NB) * L::BYTES);
-      wait_vmcnt<2 * DMA>();   // after tile k: the transfers of tiles k + 1 and k + 2
-    } else if (nxt != NONE) {
-      wait_vmcnt<DMA>();
+      issue(ps + TL * nn, ring + ((k + DEPTH) % NB) * L::BYTES);
+      wait_vmcnt<DEPTH * DMA>();   // after tile k: the transfers of tiles k + 1 .. k + DEPTH
     } else {
-      wait_vmcnt<0>();
+      int later = 0;   // tiles still in flight behind tile k
+#pragma unroll
+      for (int i = 1; i < DEPTH; ++i) later += tq[i] != NONE;
+      wait_vmcnt_tiles<DMA, DEPTH>(later);
     }
-    const int t0 = ps + TL * cur;
+#ifdef KVQ_TIMELINE
+    if (k == 0) tl_first = tl_now();
+#endif
+    const int t0 = ps + TL * tq[0];
     if constexpr (I8)
       process_tile8<G>(ring + (k % NB) * L::BYTES, lo, st, qb, t0, pe, j, a.qscale, lo_col,
                        t0 + TL > pe);
     else
       process_tile<G, NGK, S>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j,
                               a.qscale, lo_col, 16 * cset, t0 + TL > pe);
-    cur = nxt;
-    nxt = nn;
+#pragma unroll
+    for (int i = 0; i + 1 < DEPTH; ++i) tq[i] = tq[i + 1];
+    tq[DEPTH - 1] = nn;
   }
   wait_vmcnt<0>();   // (also the q staging, when this wave had no tile)
 #ifdef KVQ_TIMELINE
@@ -1414,6 +1441,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
         tl_put(a, 1, ((uint64_t)xcc << 32) | hw);
         tl_put(a, 2, tl_q);
         tl_put(a, 3, tl_loop);
+        tl_put(a, 16, tl_karg);
+        tl_put(a, 17, tl_first);
       }
     }
     wait_vmcnt<0>();

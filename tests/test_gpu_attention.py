@@ -444,3 +444,68 @@ def test_matrix_core_small_and_mixed_value_scales(case):
     kh, vh = _oracle_hat(fmt, np16(k), np16(v))
     ref = attention.decode_attention(np16(q), kh, vh, lens)
     assert_attn_close(out.cpu().numpy(), ref, f"{fmt} {kind} G={G}")
+
+
+MANY_SPLIT_CASES = [
+    # fmt, gk, G, lens, nsplit, window, cap, sinks, recent, fused
+    ("int4", 64, 4, [6000, 4100], 3, 0, None, 0, 0, False),   # ragged units
+    ("int4", 32, 8, [5000], 2, 0, None, 0, 0, False),         # 16 columns (one position set)
+    ("int4", 64, 4, [20000], 8, 0, None, 0, 0, False),        # many splits
+    ("int4", 64, 2, [50000], 2, 0, None, 0, 0, False),        # long splits
+    ("int8", 64, 4, [9000, 3000], 4, 0, None, 0, 0, False),   # 16-position tiles
+    ("int8", 64, 1, [60000], 32, 0, None, 0, 0, False),       # INT8, many splits
+    ("int4", 64, 4, [9000, 9000], 2, 4000, 4096, 0, 0, False),   # window ring
+    ("int4", 64, 4, [9000, 5000], 2, 4000, 4100, 4, 0, False),   # sinks + window ring
+    ("int4", 64, 4, [7000, 7000], 3, 0, None, 0, 64, False),     # recent fp16 rows
+    ("int4", 64, 4, [6001, 6001], 3, 0, None, 0, 0, True),       # fused append
+    ("int4", 128, 2, [8193, 8193, 8193, 8193], 0, 0, None, 0, 0, True),   # planned splits
+]
+
+
+@pytest.mark.parametrize("case", MANY_SPLIT_CASES, ids=[f"splits{i}" for i in range(len(MANY_SPLIT_CASES))])
+def test_matrix_core_long_contexts_many_splits(case):
+    """Long contexts cut into 2 .. 32 splits per (sequence, KV head), ragged units,
+    16-position (INT8) and 32-position tiles, window rings, sinks, recent fp16 rows and
+    the fused append: every position attended exactly once across the splits."""
+    fmt, gk, G, lens, ns, W, cap, S, R, fused = case
+    B, Hkv, D = len(lens), 2, 128
+    L = max(lens)
+    C = cap or L
+    k = synth.kv_source((B, Hkv, L, D), 1700 + L + ns, DEV, outlier_channels=3)
+    v = synth.kv_source((B, Hkv, L, D), 1800 + L + ns, DEV, outlier_channels=3)
+    q = synth.query((B, Hkv * G, D), 1900 + L + ns, DEV)
+    desc = kvq.make_desc(fmt, B, Hkv, D, C, gk, 128, sinks=S, recent=R)
+    dc = kvq.DeviceCache(desc, DEV)
+    P = L - 1 if fused else L        # positions written before the call
+    if S:
+        kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, :S].contiguous(), v[:, :, :S].contiguous(), 0, S)
+    first = max(S, P - (C - S))      # the rows the ring still holds
+    for start in range(first, P, C - S):
+        n = min(C - S, P - start)
+        kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, start:start + n].contiguous(),
+                                 v[:, :, start:start + n].contiguous(), start, n)
+    # a shorter sequence's own window: its last rows back into its ring (see fused tests)
+    one = kvq.make_desc(fmt, 1, Hkv, D, C, gk, 128, sinks=S, recent=R)
+    for b, ln in enumerate(lens):
+        end = ln - 1 if fused else ln
+        lo = max(S, end - (C - S))
+        if ln < L and C < L and end > lo:
+            sub = kvq.kvq_cache(*[t.view(B, -1)[b].data_ptr() for t in
+                                  (dc.k_codes, dc.k_scales, dc.v_codes, dc.v_scales)],
+                                *([t.view(B, -1)[b].data_ptr() for t in (dc.k_recent, dc.v_recent)]
+                                  if R else []))
+            kvq.kvq_quantize_prefill(one, sub, k[b:b + 1, :, lo:end].contiguous(),
+                                     v[b:b + 1, :, lo:end].contiguous(), lo, end - lo)
+    if fused:
+        idx = torch.tensor([ln - 1 for ln in lens], device=DEV)
+        ar = torch.arange(B, device=DEV)
+        out = append_decode(desc, dc, k[ar, :, idx].contiguous(), v[ar, :, idx].contiguous(), q,
+                            Hkv * G, lens, W, 0.0, ns)
+    else:
+        out = decode(desc, dc, q, Hkv * G, lens, W, 0.0, ns)
+    kh, vh = _oracle_hat(fmt, np16(k), np16(v), gk, 128)
+    if R:
+        kh = attention.recent_fp16_rows(kh, np16(k), lens, R)
+        vh = attention.recent_fp16_rows(vh, np16(v), lens, R)
+    ref = attention.decode_attention(np16(q), kh, vh, lens, W, sinks=S)
+    assert_attn_close(out.cpu().numpy(), ref, f"splits {case}")
