@@ -28,6 +28,8 @@ the same form; the default run is the headline above):
   llama8b-int4h  the headline step on INT4 with fp16 scales (split-K kernel)
   llama8b-recent the headline step with the last 128 positions also kept, and read, in
                  fp16 (8065 rows from the INT4 codes, 128 from the fp16 rings)
+  llama8b-paged  the headline step on the paged layout: pages of 16 positions, each
+                 sequence's pages shuffled over the pool by a seeded block table
   dequant        kvq_dequant of K and V of 8 Llama-3-8B-shaped layer caches to fp32
 """
 import argparse
@@ -64,6 +66,7 @@ OTHER_TRAFFIC = {
                      ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
     "llama8b-int4h": ("profiles/decode_splitk_int4h_llama8b_ctx8k_b8_traffic.md",
                       ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
+    "llama8b-paged": ("profiles/decode_int4_mfma_llama8b_ctx8k_paged16_traffic.md", KERNEL_SOURCES),
 }
 
 
@@ -73,7 +76,7 @@ def parse():
     p.add_argument("--workload", default="llama8b",
                    choices=["llama8b", "mha7b-prefill", "mha7b-decode", "ctx128k-int4",
                             "ctx128k-int8", "gemma-codec", "gemma-codec3", "llama8b-sinks", "llama8b-recent",
-                            "llama8b-int4h",
+                            "llama8b-int4h", "llama8b-paged",
                             "dequant"])
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
@@ -727,6 +730,7 @@ DECODE_MODES = {   # workload id, cache format
     "llama8b-int4h": (9, "int4h"),
     "llama8b-sinks": (6, "int4"),
     "llama8b-recent": (7, "int4"),
+    "llama8b-paged": (10, "int4"),
 }
 
 
@@ -761,9 +765,18 @@ def bench_decode(args):
         lay.W = w.layer_window(li)
         ns = w.sinks if lay.W else 0
         cap = lay.W + ns if lay.W else L
-        lay.desc = kvq.make_desc(fmt, B, Hkv, D, cap, w.group_k, w.group_v, sinks=ns, recent=w.recent)
+        if w.page_size:   # paged layout: shuffled pages from a pool of exactly enough
+            P = w.page_size
+            cap = (L + P - 1) // P * P
+            table, npages = synth.block_table(B, cap, P, synth.seed_of(w.wid, li, 5))
+            lay.desc = kvq.make_desc(fmt, B, Hkv, D, cap, w.group_k, w.group_v, page_size=P,
+                                     num_pages=npages)
+            lay.table = table.to(dev)
+        else:
+            lay.desc = kvq.make_desc(fmt, B, Hkv, D, cap, w.group_k, w.group_v, sinks=ns, recent=w.recent)
+            lay.table = None
         k, v, q, kn, vn = synth.layer_inputs(w, li, dev)
-        lay.dc = kvq.DeviceCache(lay.desc, dev)
+        lay.dc = kvq.DeviceCache(lay.desc, dev, block_table=lay.table)
         if ns:                        # the sink positions, in their own slots
             kvq.kvq_quantize_prefill(lay.desc, lay.dc.c, k[:, :, :ns].contiguous(),
                                      v[:, :, :ns].contiguous(), 0, ns)
@@ -820,6 +833,9 @@ def bench_decode(args):
         attn_ms = ms_step
     if fmt == "int4" and D == 128 and w.group_v == 128:
         kern = "kvq_decode_attn: decode_int4_mfma_kernel (splits merged in-kernel)"
+        if w.page_size:
+            kern = (f"kvq_decode_attn: decode_int4_mfma_kernel, paged instance (pages of "
+                    f"{w.page_size}, splits merged in-kernel)")
         if w.sinks and w.window_layers:
             kern = "kvq_decode_attn: decode_int4_mfma_kernel, sink instance (splits merged in-kernel)"
         if w.recent:
@@ -834,7 +850,7 @@ def bench_decode(args):
     cfg = {"workload": w.name, "format": fmt, "layers": nl, "batch": B, "q_heads": Hq,
            "kv_heads": Hkv, "head_dim": D, "context": L, "append": w.append,
            "window_layers": min(nl, w.window_layers), "window": w.window, "sinks": w.sinks,
-           "recent_fp16": w.recent,
+           "recent_fp16": w.recent, "page_size": w.page_size,
            "launch": "eager" if args.eager else "hip-graph",
            "num_splits": kvq.kvq_plan_splits(layers[-1].desc, Hq,
                                              attended_rows(L, layers[-1].W, layers[-1].desc.sinks))}
@@ -848,7 +864,8 @@ def bench_decode(args):
              "gemma-codec3": "Gemma-3-4B shape, WHT+Lloyd-Max 3-bit codec, window 1024 x29 + global x5",
              "llama8b-int4h": "Llama-3-8B shape, 8K ctx, B 8, INT4 with fp16 scales",
              "llama8b-sinks": "Llama-3-8B shape, 8K ctx, B 8, window 4096 + 4 sinks",
-             "llama8b-recent": "Llama-3-8B shape, 8K ctx, B 8, last 128 positions in fp16"}
+             "llama8b-recent": "Llama-3-8B shape, 8K ctx, B 8, last 128 positions in fp16",
+             "llama8b-paged": "Llama-3-8B shape, 8K ctx, B 8, pages of 16 positions, shuffled block table"}
     return _line(args, f"decode step: effective KV GB/s ({names[args.workload]})", gbs, ms_step, cfg,
                  roof, cpu, dict({"tok_per_s": round(B / (ms_step * 1e-3), 1), "bytes_per_step": step_bytes,
                                   "wall_s_timed": round(wall, 4)}, **extra))
@@ -963,6 +980,7 @@ def bench_dequant(args):
 OTHER = {"mha7b-prefill": bench_prefill, "mha7b-decode": bench_decode, "ctx128k-int4": bench_decode,
          "ctx128k-int8": bench_decode, "gemma-codec": bench_decode, "llama8b-sinks": bench_decode,
          "llama8b-recent": bench_decode, "gemma-codec3": bench_decode, "llama8b-int4h": bench_decode,
+         "llama8b-paged": bench_decode,
          "dequant": bench_dequant}
 
 

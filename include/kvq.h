@@ -60,6 +60,18 @@
  *   Position p of a sequence lives in slot p when p < S (S = sinks, the first
  *   positions kept for attention sinks, [KV-opt] §3.2), else in slot
  *   S + (p - S) mod (C - S): a ring of C - S slots (S = 0: slot p mod C).
+ * Paged layout ([KV-opt] §3.1 KVCacheManager: the cache handed out in fixed pages of
+ * page_size tokens from a pool of max_pages; §4: 16-64 token pages in practice), when
+ * page_size = P > 0: every buffer above is a pool of num_pages pages, page n holding P
+ * positions of one sequence for every kv head,
+ *   codes  [num_pages, Hkv, P, row bytes], scales [num_pages, Hkv, P, D/g (or 1)],
+ * and kvq_cache.block_table, device int32 [B, C / P], maps page j of sequence b (its
+ * positions jP .. jP + P - 1) to its pool page: position p of sequence b, kv head h is
+ * row ((table[b][p / P] * Hkv + h) * P + p mod P).  Capacity C is then the positions a
+ * sequence may hold (a multiple of P); there is no ring (every position below C has
+ * its own row), and sinks and recent rows are not combined with pages.  Table entries
+ * must lie in [0, num_pages): the kernels clamp any other entry into that range, so a
+ * wrong entry reads or writes the wrong page rather than outside the pool.
  * Recent fp16 rows ([INT4-SM] §8.3; INT4 caches with recent = R > 0):
  *   k_recent, v_recent  [B, Hkv, R, D] fp16, position p in row p mod R.  Every position
  *   is still quantized into the INT4 buffers when it arrives; the fp16 ring keeps the
@@ -76,7 +88,7 @@
 extern "C" {
 #endif
 
-#define KVQ_VERSION 6
+#define KVQ_VERSION 7
 /* Largest batch the decode/append calls accept (per-sequence lengths and positions
  * travel in the kernel argument block). */
 #define KVQ_MAX_BATCH 256
@@ -121,6 +133,10 @@ typedef struct {
   int32_t recent;    /* R: last positions also kept in fp16 and read from there at
                         decode, 0 <= R <= KVQ_MAX_RECENT (0: none).  INT4 format and
                         S = 0 only (KVQ_ERR_UNSUPPORTED otherwise). */
+  int32_t page_size; /* P: 0 = contiguous [B, Hkv, C, .] buffers; else the paged layout
+                        (a power of two, 16 <= P <= 256, C % P == 0, S = R = 0;
+                        KVQ_ERR_UNSUPPORTED otherwise) */
+  int32_t num_pages; /* paged layout: pages in the pool (>= 1); ignored when P = 0 */
 } kvq_cache_desc;
 
 /* Device pointers of one layer's cache (layout above). */
@@ -131,6 +147,8 @@ typedef struct {
   void* v_scales;
   void* k_recent;    /* R > 0: [B, Hkv, R, D] fp16 rings (kvq_recent_bytes each); */
   void* v_recent;    /*        R = 0: ignored */
+  const int32_t* block_table;   /* P > 0: device int32 [B, C / P] (paged layout above);
+                                   P = 0: ignored */
 } kvq_cache;
 
 /* A hipStream_t, passed as an opaque pointer; NULL is the null stream. */
@@ -150,7 +168,7 @@ int32_t kvq_check_desc(const kvq_cache_desc* desc);
 /* Bytes of the codes (or scales) buffer of K (kv = 0) or V (kv = 1) for `desc`;
  * 0 if the descriptor is invalid or kv is not 0/1.  INT4: B*Hkv*C*D/2 and
  * B*Hkv*C*(D/g)*4 (fp16 scales: *2); INT8: B*Hkv*C*D and B*Hkv*C*4; codec: B*Hkv*C*D/2 (3-bit:
- * B*Hkv*C*3D/8) and B*Hkv*C*4. */
+ * B*Hkv*C*3D/8) and B*Hkv*C*4.  Paged layout: num_pages*P in place of B*C. */
 size_t kvq_codes_bytes(const kvq_cache_desc* desc, int32_t kv);
 size_t kvq_scales_bytes(const kvq_cache_desc* desc, int32_t kv);
 /* Bytes of each recent fp16 ring (K and V alike): B*Hkv*R*D*2; 0 if the descriptor is

@@ -49,13 +49,15 @@ class kvq_cache_desc(ctypes.Structure):
                 ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("group_k", ctypes.c_int32),
                 ("group_v", ctypes.c_int32), ("sinks", ctypes.c_int32),
-                ("recent", ctypes.c_int32)]
+                ("recent", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
 
 
 class kvq_cache(ctypes.Structure):
     _fields_ = [("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
                 ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
-                ("k_recent", ctypes.c_void_p), ("v_recent", ctypes.c_void_p)]
+                ("k_recent", ctypes.c_void_p), ("v_recent", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p)]
 
 
 class KvqError(RuntimeError):
@@ -117,9 +119,10 @@ def _check(status, where):
 
 
 def make_desc(fmt, batch, kv_heads, head_dim, capacity, group_k=64, group_v=128, sinks=0,
-              recent=0):
+              recent=0, page_size=0, num_pages=0):
     f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
-    return kvq_cache_desc(f, batch, kv_heads, head_dim, capacity, group_k, group_v, sinks, recent)
+    return kvq_cache_desc(f, batch, kv_heads, head_dim, capacity, group_k, group_v, sinks, recent,
+                          page_size, num_pages)
 
 
 def _ptr(t, dtype=None, name="tensor"):
@@ -266,9 +269,11 @@ def kvq_dequant(desc, cache, kv, start_pos, n, out, stream=None):
 
 class DeviceCache:
     """torch-owned device buffers of one layer's cache, sized by the library's own size
-    queries, plus the ``kvq_cache`` struct pointing at them."""
+    queries, plus the ``kvq_cache`` struct pointing at them.  A paged descriptor
+    (page_size > 0) takes its block table, a device int32 tensor [batch, capacity /
+    page_size], as ``block_table``."""
 
-    def __init__(self, desc, device="cuda"):
+    def __init__(self, desc, device="cuda", block_table=None):
         import torch
         self.desc = desc
         nb = [kvq_codes_bytes(desc, 0), kvq_scales_bytes(desc, 0),
@@ -284,10 +289,18 @@ class DeviceCache:
         nr = kvq_recent_bytes(desc) // 2
         self.k_recent = torch.zeros(nr, dtype=torch.float16, device=device) if nr else None
         self.v_recent = torch.zeros(nr, dtype=torch.float16, device=device) if nr else None
+        if desc.page_size > 0:
+            import torch
+            if block_table is None or block_table.dtype != torch.int32 or not block_table.is_contiguous():
+                raise ValueError("a paged cache needs a contiguous int32 block table")
+            if tuple(block_table.shape) != (desc.batch, desc.capacity // desc.page_size):
+                raise ValueError("block table must be [batch, capacity / page_size]")
+        self.block_table = block_table
         self.c = kvq_cache(self.k_codes.data_ptr(), self.k_scales.data_ptr(),
                            self.v_codes.data_ptr(), self.v_scales.data_ptr(),
                            self.k_recent.data_ptr() if nr else None,
-                           self.v_recent.data_ptr() if nr else None)
+                           self.v_recent.data_ptr() if nr else None,
+                           block_table.data_ptr() if block_table is not None else None)
 
     @property
     def nbytes(self):

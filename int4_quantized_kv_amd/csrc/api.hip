@@ -17,7 +17,13 @@ int32_t check_desc(const kvq_cache_desc* d) {
   if (d->format < KVQ_INT4_G || d->format > KVQ_INT4_G16) return KVQ_ERR_ARG;
   if (d->batch < 1 || d->kv_heads < 1 || d->head_dim < 1 || d->capacity < 1)
     return KVQ_ERR_ARG;
-  if (d->sinks < 0 || d->sinks >= d->capacity || d->recent < 0) return KVQ_ERR_ARG;
+  if (d->sinks < 0 || d->sinks >= d->capacity || d->recent < 0 || d->page_size < 0) return KVQ_ERR_ARG;
+  if (d->page_size > 0) {   // paged layout: pages of 16 .. 256 positions, no ring
+    if (d->num_pages < 1) return KVQ_ERR_ARG;
+    if (!pow2(d->page_size) || d->page_size < 16 || d->page_size > 256 ||
+        d->capacity % d->page_size != 0 || d->sinks > 0 || d->recent > 0)
+      return KVQ_ERR_UNSUPPORTED;
+  }
   // recent fp16 rows: INT4 only, without sinks, at most KVQ_MAX_RECENT
   if (d->recent > 0 && (d->format != KVQ_INT4_G || d->sinks > 0 || d->recent > KVQ_MAX_RECENT))
     return KVQ_ERR_UNSUPPORTED;
@@ -30,14 +36,36 @@ int32_t check_desc(const kvq_cache_desc* d) {
     }
   }
   // 32-bit lane indexing inside the kernels
-  const uint64_t rows = (uint64_t)d->batch * d->kv_heads * d->capacity;
+  const uint64_t rows = d->page_size > 0
+                            ? (uint64_t)d->num_pages * d->kv_heads * d->page_size
+                            : (uint64_t)d->batch * d->kv_heads * d->capacity;
   if (rows * (uint64_t)(d->head_dim / 8) >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
 bool cache_ok(const kvq_cache_desc* d, const kvq_cache* c) {
   return c && c->k_codes && c->k_scales && c->v_codes && c->v_scales &&
-         (d->recent == 0 || (c->k_recent && c->v_recent));
+         (d->recent == 0 || (c->k_recent && c->v_recent)) &&
+         (d->page_size == 0 || c->block_table);
+}
+
+// Rows of each codes / scales buffer: the pool's pages, or B * Hkv * C.
+size_t cache_rows(const kvq_cache_desc* d) {
+  return d->page_size > 0 ? (size_t)d->num_pages * d->kv_heads * d->page_size
+                          : (size_t)d->batch * d->kv_heads * d->capacity;
+}
+
+Pages make_pages(const kvq_cache_desc* d, const kvq_cache* c) {
+  Pages p;
+  std::memset(&p, 0, sizeof(p));
+  if (d->page_size > 0) {
+    p.table = c->block_table;
+    p.size = d->page_size;
+    p.shift = __builtin_ctz((unsigned)d->page_size);
+    p.pps = d->capacity / d->page_size;
+    p.count = d->num_pages;
+  }
+  return p;
 }
 
 int32_t scales_per_row(const kvq_cache_desc* d, int32_t kv) {
@@ -65,6 +93,7 @@ int32_t quant_common(const kvq_cache_desc* desc, const kvq_cache* cache, const v
   a.gv = desc->group_v;
   a.rows = desc->batch * desc->kv_heads * n;
   a.map = map;
+  a.pages = make_pages(desc, cache);
   if (desc->recent > 0) {
     a.k_recent = static_cast<uint16_t*>(cache->k_recent);
     a.v_recent = static_cast<uint16_t*>(cache->v_recent);
@@ -100,7 +129,7 @@ int32_t check_lens(const kvq_cache_desc* d, const int32_t* lens, int32_t window)
   for (int32_t b = 0; b < d->batch; ++b) {
     const int32_t L = lens[b];
     if (L < 1) return KVQ_ERR_ARG;
-    if (window == 0) {
+    if (window == 0 || d->page_size > 0) {   // (a paged cache has no ring)
       if (L > d->capacity) return KVQ_ERR_CAPACITY;
     } else if (L > d->capacity && window > d->capacity - d->sinks) {
       return KVQ_ERR_CAPACITY;   // the window's rows would not all be in the ring
@@ -111,8 +140,10 @@ int32_t check_lens(const kvq_cache_desc* d, const int32_t* lens, int32_t window)
   return span;
 }
 
-// Positions [start, start + n) map to distinct slots: at most C - S of them at or after S.
+// Positions [start, start + n) map to distinct slots: at most C - S of them at or after S
+// (paged: all of them below C).
 bool rows_fit(const kvq_cache_desc* d, int32_t start, int32_t n) {
+  if (d->page_size > 0) return (int64_t)start + n <= d->capacity;
   const int64_t first_ring = start > d->sinks ? start : d->sinks;
   return (int64_t)start + n - first_ring <= d->capacity - d->sinks;
 }
@@ -139,7 +170,7 @@ int32_t kvq_check_desc(const kvq_cache_desc* desc) { return check_desc(desc); }
 
 size_t kvq_codes_bytes(const kvq_cache_desc* d, int32_t kv) {
   if (check_desc(d) != KVQ_OK || (kv != 0 && kv != 1)) return 0;
-  const size_t rows = (size_t)d->batch * d->kv_heads * d->capacity;
+  const size_t rows = cache_rows(d);
   if (d->format == KVQ_INT8_TOKEN) return rows * d->head_dim;
   if (d->format == KVQ_WHT_LM3) return rows * (3 * d->head_dim / 8);
   return rows * (d->head_dim / 2);
@@ -147,7 +178,7 @@ size_t kvq_codes_bytes(const kvq_cache_desc* d, int32_t kv) {
 
 size_t kvq_scales_bytes(const kvq_cache_desc* d, int32_t kv) {
   if (check_desc(d) != KVQ_OK || (kv != 0 && kv != 1)) return 0;
-  const size_t rows = (size_t)d->batch * d->kv_heads * d->capacity;
+  const size_t rows = cache_rows(d);
   return rows * scales_per_row(d, kv) * (d->format == KVQ_INT4_G16 ? sizeof(uint16_t) : sizeof(float));
 }
 
@@ -215,6 +246,7 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache, const voi
   std::memset(&map, 0, sizeof(map));
   for (int32_t b = 0; b < desc->batch; ++b) {
     if (pos[b] < 0) return KVQ_ERR_ARG;
+    if (desc->page_size > 0 && pos[b] >= desc->capacity) return KVQ_ERR_CAPACITY;
     map.pos[b] = pos[b];
   }
   map.append = 1;
@@ -330,6 +362,7 @@ int32_t decode_common(const kvq_cache_desc* desc, const kvq_cache* cache, const 
   a.gv = desc->group_v;
   a.window = window;
   a.nsplit = ns;
+  a.pages = make_pages(desc, cache);
 
 #ifdef KVQ_TIMELINE
   a.stamps = stamps;
@@ -420,6 +453,7 @@ int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t 
   a.start = start_pos;
   a.n = n;
   a.sinks = desc->sinks;
+  a.pages = make_pages(desc, cache);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (is_codec(desc->format)) {
     float thr[15];

@@ -43,7 +43,8 @@ __global__ void __launch_bounds__(256) codec_encode_kernel(QuantArgs a) {
     const int t = (int)(row - bh * a.map.n);
     const int b = (int)(bh / (uint32_t)a.Hkv);
     const int p = a.map.append ? a.map.pos[b] : a.map.start + t;
-    const size_t drow = (size_t)bh * a.map.cap + cache_slot(p, a.map.cap, a.map.sinks);
+    const size_t drow = a.pages.size ? paged_row(a.pages, a.Hkv, b, (int)(bh - b * a.Hkv), p)
+                                     : (size_t)bh * a.map.cap + cache_slot(p, a.map.cap, a.map.sinks);
     if (BITS == 4) static_cast<uint32_t*>(codes)[drow * LPR + c] = w;
     else store_planes<LPR>(static_cast<uint8_t*>(codes) + drow * 3 * LPR, c, w);
     if (c == 0) scales[drow] = s;
@@ -66,7 +67,9 @@ __global__ void __launch_bounds__(256) codec_dequant_kernel(DequantArgs a) {
     const int c = (int)(i - row * LPR);
     const uint32_t bh = row / (uint32_t)a.n;
     const int t = (int)(row - bh * a.n);
-    const size_t drow = (size_t)bh * a.cap + cache_slot(a.start + t, a.cap, a.sinks);
+    const int b = (int)(bh / (uint32_t)a.Hkv);
+    const size_t drow = a.pages.size ? paged_row(a.pages, a.Hkv, b, (int)(bh - b * a.Hkv), a.start + t)
+                                     : (size_t)bh * a.cap + cache_slot(a.start + t, a.cap, a.sinks);
     const uint32_t w = BITS == 4 ? static_cast<const uint32_t*>(a.codes)[drow * LPR + c]
                                  : load_planes<LPR>(static_cast<const uint8_t*>(a.codes) + drow * 3 * LPR, c);
     const float s = a.scales[drow];

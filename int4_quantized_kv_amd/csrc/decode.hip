@@ -157,7 +157,13 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   constexpr int SR = U * NGRP;   // rows per step (all groups)
   const size_t bh = (size_t)b * a.Hkv + kvh;
   auto load_step = [&](int t0, RawRow (&raw)[U]) {
-    if (a.sinks == 0) {   // (uniform) one ring: slot t mod cap
+    if (a.pages.size) {   // (uniform) paged layout: each row through the block table
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = min(t0 + u * NGRP, pe - 1);
+        raw[u] = load_raw<D, FMT>(a, paged_row(a.pages, a.Hkv, b, kvh, t), c);
+      }
+    } else if (a.sinks == 0) {   // (uniform) one ring: slot t mod cap
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = min(t0 + u * NGRP, pe - 1);
@@ -238,7 +244,8 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
       }
     }
     if (grp < 2) {
-      const size_t row = bh * a.cap + cache_slot(len - 1, a.cap, a.sinks);
+      const size_t row = a.pages.size ? paged_row(a.pages, a.Hkv, b, kvh, len - 1)
+                                      : bh * a.cap + cache_slot(len - 1, a.cap, a.sinks);
       void* codes = const_cast<void*>(grp ? a.v_codes : a.k_codes);
       if (FMT == KVQ_WHT_LM3) store_planes<LPR>(static_cast<uint8_t*>(codes) + row * 3 * LPR, c, w);
       else static_cast<uint32_t*>(codes)[row * LPR + c] = w;

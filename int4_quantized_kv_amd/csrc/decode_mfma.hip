@@ -325,6 +325,74 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int
   dma4<CPOL_NT>(vs + srow * 4, lb + L::SV_OFF);
 }
 
+// ---------------------------------------------------------------------------------------
+// Paged layout (include/kvq.h; "AI 推理性能调优：KV Cache 优化与显存管理的工程实践",
+// bxzpzcl.cn/news/2871434, section 3.1 KVCacheManager: fixed pages from a pool).  The
+// paged instance aligns its tiles to TL positions, so a tile lies in one page (P >= TL)
+// or in two (P = 16 with 32-position tiles, one page per 16-row half).  Page ids are
+// read with scalar loads written in asm: a vector load would join the tile transfers'
+// vmcnt count, which the pipeline's waits assume holds transfers only.
+__device__ __forceinline__ uint32_t page_id(const Pages& pg, int b, int e) {
+  const int32_t* p = pg.table + (size_t)b * pg.pps + e;
+  uint32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return min(v, (uint32_t)(pg.count - 1));   // an entry outside the pool stays inside it
+}
+
+// The rows of a tile [t0, t0 + TL) in the paged layout: positions below pb or at pe and
+// beyond are clamped into [pb, pe) (their scores are masked), which keeps them in the
+// tile's page(s).
+struct PageRows {
+  uint32_t id0, id1;   // pages of positions t0 .. and t0 + 16 .. (P = 16)
+  int e0;
+  __device__ __forceinline__ size_t row(const Pages& pg, int Hkv, int h, int p) const {
+    const uint32_t id = (p >> pg.shift) == e0 ? id0 : id1;
+    return ((size_t)id * Hkv + h) * pg.size + (p & (pg.size - 1));
+  }
+};
+template <int TLN>
+__device__ __forceinline__ PageRows page_rows(const DecodeArgs& a, int b, int t0, int pe) {
+  PageRows r;
+  r.e0 = t0 >> a.pages.shift;
+  r.id0 = page_id(a.pages, b, r.e0);
+  r.id1 = (a.pages.size < TLN && t0 + 16 < pe) ? page_id(a.pages, b, r.e0 + 1) : r.id0;
+  return r;
+}
+
+template <int NGK>
+__device__ __forceinline__ void issue_tile_pg(const DecodeArgs& a, int b, int h, int t0, int pb,
+                                              int pe, uint8_t* lb, int lane, const DmaOffs& o) {
+  using L = Slot<NGK>;
+  const uint8_t* kc = static_cast<const uint8_t*>(a.k_codes);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.v_codes);
+  const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k_scales);
+  const uint8_t* vs = reinterpret_cast<const uint8_t*>(a.v_scales);
+  const PageRows pr = page_rows<TILE>(a, b, t0, pe);
+  auto row_of = [&](int rho) -> size_t {   // tile row -> cache row, clamped into [pb, pe)
+    return pr.row(a.pages, a.Hkv, h, min(max(t0 + rho, pb), pe - 1));
+  };
+  if (t0 >= pb && t0 + TILE <= pe) {   // (uniform) every row in range: one base per half
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const size_t rb = pr.row(a.pages, a.Hkv, h, t0 + 16 * T);   // rows 16 T .. 16 T + 15
+      dma16<CPOL_NT>(kc + rb * (HD / 2) + o.kv[T] - 16 * T * (HD / 2), lb + L::K_OFF + 1024 * T);
+      dma16<CPOL_NT>(vc + rb * (HD / 2) + o.kv[T] - 16 * T * (HD / 2), lb + L::V_OFF + 1024 * T);
+    }
+  } else {
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const size_t row = row_of(o.rho[T]);
+      dma16<CPOL_NT>(kc + row * (HD / 2) + o.kap16, lb + L::K_OFF + 1024 * T);
+      dma16<CPOL_NT>(vc + row * (HD / 2) + o.kap16, lb + L::V_OFF + 1024 * T);
+    }
+  }
+  const size_t srow = row_of(lane & 31);
+#pragma unroll
+  for (int hh = 0; hh < (NGK <= 2 ? 1 : 2); ++hh)
+    dma4<CPOL_NT>(ks + srow * (NGK * 4) + (o.sk[hh] - (lane & 31) * NGK * 4), lb + L::SK_OFF + 256 * hh);
+  dma4<CPOL_NT>(vs + srow * 4, lb + L::SV_OFF);
+}
+
 // Position sets.  A head's q.K needs G * NGK of the 16 MFMA columns.  When that is at
 // most 8 (S = 2), the other 8 columns score the second 16-position half of the tile in
 // the same MFMAs: A row r then carries position r of half 0 in the k slots of lane
@@ -484,14 +552,15 @@ __device__ __forceinline__ TileData read_tile(const uint8_t* lb, const LaneOffs&
 // (softmax scale * log2 e) is positive, p = 2^(scale * (z - m)).
 // S = 1: the lane's scores are positions 16T + 4j + i (T = 0, 1); S = 2: positions
 // soff + 4j + i, soff = 16 * (the half of the lane's column set), see position_sets.
-// masked (uniform): the tile reaches past pe (a split's last tile); those positions get
+// masked (uniform): the tile reaches past pe (a split's last tile) or, in the paged
+// layout, starts below pmin (the first tile of an aligned plan); those positions get
 // score -inf.  One code path serves both kinds of tile, and the masking only rewrites
 // the scores in place: with two instances of the tile in the loop, the compiler gave
 // the accumulators of each its own registers and copied all 32 of them twice per tile.
 template <int G, int NGK, int S>
 __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& lo, State& st,
                                              const half8 (&qb)[4 * S], float qbias, int t0,
-                                             int pe, int j, float qscale, bool lo_col,
+                                             int pmin, int pe, int j, float qscale, bool lo_col,
                                              int soff, bool masked) {
   constexpr int NTB = 2 / S;   // 16-row blocks of q.K results per lane
   const TileData td = read_tile<NGK, S>(lb, lo);
@@ -522,7 +591,8 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
     for (int T = 0; T < NTB; ++T)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (t0 + 16 * T + soff + 4 * j + i >= pe) z[T][i] = NEG_INF;
+        if (t0 + 16 * T + soff + 4 * j + i >= pe || t0 + 16 * T + soff + 4 * j + i < pmin)
+          z[T][i] = NEG_INF;
   }
 
   // ---- online softmax (the 4 lanes j of a column share a head)
@@ -714,6 +784,35 @@ __device__ __forceinline__ void issue_tile8(const DecodeArgs& a, size_t row0, in
   dma4<CPOL_NT>(sc + row_of(o.srow), lb + L::SK_OFF);
 }
 
+// The paged layout's INT8 tile: 16 positions from a multiple of 16, so one page.
+__device__ __forceinline__ void issue_tile8_pg(const DecodeArgs& a, int b, int h, int t0, int pb,
+                                               int pe, uint8_t* lb, const DmaOffs8& o) {
+  using L = Slot8;
+  const uint8_t* kc = static_cast<const uint8_t*>(a.k_codes);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.v_codes);
+  const PageRows pr = page_rows<TILE8>(a, b, t0, pe);
+  auto row_of = [&](int rho) -> size_t {
+    return pr.row(a.pages, a.Hkv, h, min(max(t0 + rho, pb), pe - 1));
+  };
+  if (t0 >= pb && t0 + TILE8 <= pe) {   // (uniform) 16 consecutive rows of one page
+    const size_t rb = pr.row(a.pages, a.Hkv, h, t0);
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      dma16<CPOL_NT>(kc + rb * HD + o.kv[T], lb + L::K_OFF + 1024 * T);
+      dma16<CPOL_NT>(vc + rb * HD + o.kv[T], lb + L::V_OFF + 1024 * T);
+    }
+  } else {
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const size_t row = row_of(o.rho[T]);
+      dma16<CPOL_NT>(kc + row * HD + o.ch16[T], lb + L::K_OFF + 1024 * T);
+      dma16<CPOL_NT>(vc + row * HD + o.ch16[T], lb + L::V_OFF + 1024 * T);
+    }
+  }
+  const float* sc = o.sv ? a.v_scales : a.k_scales;
+  dma4<CPOL_NT>(sc + row_of(o.srow), lb + L::SK_OFF);
+}
+
 struct LaneOffs8 {
   int k[2];     // chunks 2j, 2j + 1 of row r
   int v[4];     // bytes 8r .. 8r + 7 of rows 4j + i
@@ -788,8 +887,8 @@ __device__ __forceinline__ uint32_t v8_pair(uint32_t w0, uint32_t w1, uint32_t s
 
 template <int G>
 __device__ __forceinline__ void process_tile8(const uint8_t* lb, const LaneOffs8& lo, State& st,
-                                              const half8 (&qb)[4], int t0, int pe, int j,
-                                              float qscale, bool lo_col, bool masked) {
+                                              const half8 (&qb)[4], int t0, int pmin, int pe,
+                                              int j, float qscale, bool lo_col, bool masked) {
   const TileData8 td = read_tile8(lb, lo);
   // ---- q.K: the lane's 32 dims in 4 MFMAs, 8 dims each
   const uint32_t kw[8] = {td.k[0].x, td.k[0].y, td.k[0].z, td.k[0].w,
@@ -812,7 +911,7 @@ __device__ __forceinline__ void process_tile8(const uint8_t* lb, const LaneOffs8
   if (masked) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (t0 + 4 * j + i >= pe) z[i] = NEG_INF;
+      if (t0 + 4 * j + i >= pe || t0 + 4 * j + i < pmin) z[i] = NEG_INF;
   }
 
   // ---- online softmax (the 4 lanes j of a column share a head)
@@ -1144,7 +1243,9 @@ __device__ __forceinline__ void recent_entry(const DecodeArgs& a, int unit, int 
   }
 }
 
-template <int G, int NGK, bool I8, bool SK, bool RC = false>
+// PG: the paged layout (page-aligned tiles, rows through the block table; a separate
+// instance, so that the contiguous case carries none of it).
+template <int G, int NGK, bool I8, bool SK, bool RC = false, bool PG = false>
 __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   using L = std::conditional_t<I8, Slot8, Slot<NGK>>;
   constexpr int TL = I8 ? TILE8 : TILE;       // positions per tile
@@ -1219,10 +1320,15 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // virtual range [vlo, pt), where u in [vlo, lo_pos) stands for position u - vlo
   const int nsk = SK && a.window > 0 ? min(a.sinks, lo_pos) : 0;
   const int vlo = lo_pos - nsk;
-  const int span = pt - vlo;
-  const int chunk = span > 0 ? (span + a.nsplit - 1) / a.nsplit : 0;
-  const int ps = min(pt, vlo + sp * chunk);
+  // paged layout: tiles start at multiples of TL (so each lies in one page, or two of 16),
+  // from the multiple of TL below the horizon; positions below it are masked
+  const int vbase = PG ? (vlo & ~(TL - 1)) : vlo;
+  const int span = pt - vbase;
+  int chunk = span > 0 ? (span + a.nsplit - 1) / a.nsplit : 0;
+  if (PG) chunk = (chunk + TL - 1) & ~(TL - 1);
+  const int ps = min(pt, vbase + sp * chunk);
   const int pe = min(pt, ps + chunk);
+  const int pb = PG ? vlo : -2147483647;   // positions below are masked (paged plan)
   const int nts = (pe - ps + TL - 1) / TL;
   const size_t row0 = (size_t)unit * a.cap;
   uint8_t* ring = smem + wave * NB * L::BYTES;
@@ -1231,8 +1337,13 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     else return dma_offsets<NGK>(lane);
   }();
   auto issue = [&](int t0, uint8_t* lb) {
-    if constexpr (I8) issue_tile8<SK>(a, row0, t0, pe, lo_pos, vlo, lb, dof);
-    else issue_tile<NGK, SK>(a, row0, t0, pe, lo_pos, vlo, lb, lane, dof);
+    if constexpr (PG) {
+      if constexpr (I8) issue_tile8_pg(a, b, kvh, t0, pb, pe, lb, dof);
+      else issue_tile_pg<NGK>(a, b, kvh, t0, pb, pe, lb, lane, dof);
+    } else {
+      if constexpr (I8) issue_tile8<SK>(a, row0, t0, pe, lo_pos, vlo, lb, dof);
+      else issue_tile<NGK, SK>(a, row0, t0, pe, lo_pos, vlo, lb, lane, dof);
+    }
   };
   if (threadIdx.x == 0) s_claim = 0;   // ordered before the first claim by the q barrier
 
@@ -1417,12 +1528,13 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     if (k == 0) tl_first = tl_now();
 #endif
     const int t0 = ps + TL * tq[0];
+    const bool masked = t0 + TL > pe || (PG && t0 < pb);
     if constexpr (I8)
-      process_tile8<G>(ring + (k % NB) * L::BYTES, lo, st, qb, t0, pe, j, a.qscale, lo_col,
-                       t0 + TL > pe);
+      process_tile8<G>(ring + (k % NB) * L::BYTES, lo, st, qb, t0, pb, pe, j, a.qscale, lo_col,
+                       masked);
     else
-      process_tile<G, NGK, S>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pe, j,
-                              a.qscale, lo_col, 16 * cset, t0 + TL > pe);
+      process_tile<G, NGK, S>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pb, pe, j,
+                              a.qscale, lo_col, 16 * cset, masked);
 #pragma unroll
     for (int i = 0; i + 1 < DEPTH; ++i) tq[i] = tq[i + 1];
     tq[DEPTH - 1] = nn;
@@ -1575,9 +1687,12 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // the new row's codes and scales go to the cache here, so that the wait below covers
   // them together with the partials (a barrier right after the loop would wait for them
   // alone); no tile of this step reads that row
-  if (app_wave && lane < 32)
-    store_new_row<NGK>(a, &s_new, row0 + (size_t)(SK ? cache_slot(len - 1, a.cap, a.sinks)
-                                                       : (len - 1) % a.cap), lane);
+  if (app_wave && lane < 32) {
+    size_t nrow;
+    if constexpr (PG) nrow = page_rows<TL>(a, b, len - 1, len).row(a.pages, a.Hkv, kvh, len - 1);
+    else nrow = row0 + (size_t)(SK ? cache_slot(len - 1, a.cap, a.sinks) : (len - 1) % a.cap);
+    store_new_row<NGK>(a, &s_new, nrow, lane);
+  }
   uint32_t* cnt = a.counters + unit;
 #ifdef KVQ_TIMELINE
   const uint64_t tl_pub = tl_now();
@@ -1694,34 +1809,35 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 #endif
 }
 
-template <int G, bool SK, bool RC>
+template <int G, bool SK, bool RC, bool PG = false>
 hipError_t launch_gs(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   switch (HD / a.gk) {
-    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1, false, SK, RC>, grid, dim3(NT), a, s);
-    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2, false, SK, RC>, grid, dim3(NT), a, s);
+    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1, false, SK, RC, PG>, grid, dim3(NT), a, s);
+    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2, false, SK, RC, PG>, grid, dim3(NT), a, s);
     case 4:
-      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4, false, SK, RC>, grid, dim3(NT), a, s);
+      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4, false, SK, RC, PG>, grid, dim3(NT), a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
-// (sinks and recent fp16 rows are not combined: the library rejects such caches)
+// (sinks, recent fp16 rows and pages are not combined: the library rejects such caches)
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
+  if (a.pages.size) return a.sinks || a.recent ? hipErrorInvalidValue : launch_gs<G, false, false, true>(a, s);
   if (a.recent) return a.sinks ? hipErrorInvalidValue : launch_gs<G, false, true>(a, s);
   return a.sinks ? launch_gs<G, true, false>(a, s) : launch_gs<G, false, false>(a, s);
 }
 
-template <bool SK>
+template <bool SK, bool PG = false>
 hipError_t launch_i8(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   switch (q_group) {
-    case 1: return launch_kernel(decode_int4_mfma_kernel<1, 2, true, SK>, grid, dim3(NT), a, s);
-    case 2: return launch_kernel(decode_int4_mfma_kernel<2, 2, true, SK>, grid, dim3(NT), a, s);
-    case 4: return launch_kernel(decode_int4_mfma_kernel<4, 2, true, SK>, grid, dim3(NT), a, s);
-    case 8: return launch_kernel(decode_int4_mfma_kernel<8, 2, true, SK>, grid, dim3(NT), a, s);
+    case 1: return launch_kernel(decode_int4_mfma_kernel<1, 2, true, SK, false, PG>, grid, dim3(NT), a, s);
+    case 2: return launch_kernel(decode_int4_mfma_kernel<2, 2, true, SK, false, PG>, grid, dim3(NT), a, s);
+    case 4: return launch_kernel(decode_int4_mfma_kernel<4, 2, true, SK, false, PG>, grid, dim3(NT), a, s);
+    case 8: return launch_kernel(decode_int4_mfma_kernel<8, 2, true, SK, false, PG>, grid, dim3(NT), a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1768,6 +1884,7 @@ bool mfma_int8_eligible(int32_t head_dim, int32_t cap, int32_t q_group) {
 }
 
 hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
+  if (a.pages.size) return a.sinks ? hipErrorInvalidValue : launch_i8<false, true>(a, q_group, s);
   return a.sinks ? launch_i8<true>(a, q_group, s) : launch_i8<false>(a, q_group, s);
 }
 

@@ -19,6 +19,22 @@ __host__ __device__ inline int32_t cache_slot(int32_t p, int32_t cap, int32_t si
   return p < sinks ? p : sinks + (p - sinks) % (cap - sinks);
 }
 
+// The paged layout (include/kvq.h): the row of position p of sequence b, kv head h,
+// through the block table; an entry outside the pool is clamped into it.
+struct Pages {
+  const int32_t* table;  // [B, pps] (device), or null: contiguous layout
+  int32_t size;          // page size P (a power of two), 0 when contiguous
+  int32_t shift;         // log2(P)
+  int32_t pps;           // pages per sequence (table row length) = capacity / P
+  int32_t count;         // pages in the pool
+};
+__device__ inline size_t paged_row(const Pages& pg, int32_t Hkv, int32_t b, int32_t h,
+                                   int32_t p) {
+  const uint32_t id = min((uint32_t)pg.table[(size_t)b * pg.pps + (p >> pg.shift)],
+                          (uint32_t)(pg.count - 1));
+  return ((size_t)id * Hkv + h) * pg.size + (p & (pg.size - 1));
+}
+
 struct SlotMap {
   int32_t append;   // 0: prefill, 1: append
   int32_t start;
@@ -41,6 +57,7 @@ struct QuantArgs {
   uint16_t* k_recent;    // fp16 rings [B, Hkv, recent, D] (INT4 with recent > 0), else null
   uint16_t* v_recent;
   int32_t recent;
+  Pages pages;
   SlotMap map;
 };
 
@@ -50,6 +67,7 @@ struct DequantArgs {
   float* out;            // [B, Hkv, n, D]
   int32_t B, Hkv, D, g, cap, start, n;
   int32_t sinks;         // slots ahead of the ring (cache_slot)
+  Pages pages;
   float levels[16];      // codec output levels (codec format only)
 };
 
@@ -76,6 +94,7 @@ struct DecodeArgs {
   uint16_t* v_recent;    // (INT4 matrix-core kernel with recent > 0), else null
   int32_t recent;        // positions [len - recent, len) are read from the rings (each
                          // split takes a share of them)
+  Pages pages;           // paged layout (pages.size > 0), else contiguous [B, Hkv, cap, .]
   uint64_t* stamps;      // timeline probe builds only (-DKVQ_TIMELINE): phase timestamps
                          // of each workgroup of the matrix-core kernel, else null
   int32_t lens[KVQ_MAX_BATCH];

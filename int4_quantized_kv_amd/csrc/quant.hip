@@ -86,14 +86,19 @@ __device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
         sc = INT8 ? kvq_int8_scale(am) : kvq_int4_scale(am);
       }
       const float r = 1.0f / sc;
-      int slot;
-      if (sinks) {   // (uniform) sink slots ahead of the ring
-        slot = cache_slot(p0 + t, cap, sinks);
+      size_t drow;
+      if (a.pages.size) {   // (uniform) paged layout: the page of position p0 + t
+        drow = paged_row(a.pages, a.Hkv, b, bh - b * a.Hkv, p0 + t);
       } else {
-        slot = base + t;
-        if (slot >= cap) slot -= cap;
+        int slot;
+        if (sinks) {   // (uniform) sink slots ahead of the ring
+          slot = cache_slot(p0 + t, cap, sinks);
+        } else {
+          slot = base + t;
+          if (slot >= cap) slot -= cap;
+        }
+        drow = row0 + slot;
       }
-      const size_t drow = row0 + slot;
       if (!INT8 && a.recent) {   // (uniform) the call's last `recent` positions also
         const int p = p0 + t;    // go to the fp16 ring, row p mod recent, unchanged
         if (p >= p0 + a.map.n - a.recent) {
@@ -163,14 +168,20 @@ __device__ __forceinline__ void dequant_pair(const DequantArgs& a, int bh) {
       if (k < nhalf) {
         const uint32_t i = k >> 1;
         const int t = (int)(i >> lsh), c = (int)(i & (lpr - 1));
-        int slot;
-        if (sinks) {   // (uniform) sink slots ahead of the ring
-          slot = cache_slot(a.start + t, cap, sinks);
+        size_t drow;
+        if (a.pages.size) {   // (uniform) paged layout
+          const int b = bh / a.Hkv;
+          drow = paged_row(a.pages, a.Hkv, b, bh - b * a.Hkv, a.start + t);
         } else {
-          slot = base + t;
-          if (slot >= cap) slot -= cap;
+          int slot;
+          if (sinks) {   // (uniform) sink slots ahead of the ring
+            slot = cache_slot(a.start + t, cap, sinks);
+          } else {
+            slot = base + t;
+            if (slot >= cap) slot -= cap;
+          }
+          drow = row0 + slot;
         }
-        const size_t drow = row0 + slot;
         if (INT8) {   // the half's 4 bytes
           wr[u] = reinterpret_cast<const uint32_t*>(a.codes)[2 * ((drow << lsh) + c) + (k & 1)];
           sr[u] = a.scales[drow];

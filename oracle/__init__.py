@@ -16,10 +16,11 @@ Modules
   attention  plain softmax decode attention with GQA and a sliding-window horizon
   codec      Walsh-Hadamard rotation + Lloyd-Max 4-bit codec
   memory     KV-cache size and effective-bit closed forms
+  paged      the paged layout: the page allocation policy, pool rows, fragmentation
 
 Pinning status: every public function is pinned by ``tests/test_oracle_*.py``
 against values printed on the pages (``tests/golden``), closed forms, textbook
 tables, library routines or brute force.  No function is "parity unpinned".
 """
 
-from . import quant, attention, codec, memory  # noqa: F401
+from . import quant, attention, codec, memory, paged  # noqa: F401

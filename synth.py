@@ -90,6 +90,7 @@ class Workload:
     sinks: int = 0          # attention-sink positions kept besides a window layer's ring
     recent: int = 0         # last positions also kept (and read) in fp16
     zero_groups: tuple = field(default=())
+    page_size: int = 0      # paged layout: positions per page (0 = contiguous buffers)
 
     def layer_window(self, layer):
         return self.window if layer < self.window_layers else 0
@@ -124,7 +125,23 @@ WORKLOADS = {
     9: Workload(9, "llama3-8b-gqa4-ctx8k-b8-int4h", layers=32, batch=8, q_heads=32, kv_heads=8,
                 head_dim=128, context=8192, append=True, fmt="int4h",
                 outlier_channels=round(0.02 * 128)),
+    10: Workload(10, "llama3-8b-gqa4-ctx8k-b8-paged16", layers=32, batch=8, q_heads=32, kv_heads=8,
+                 head_dim=128, context=8192, append=True, outlier_channels=round(0.02 * 128),
+                 page_size=16),
 }
+
+
+def block_table(batch, positions, page_size, seed, spare=0):
+    """A seeded block table [batch, ceil(positions / page_size)] (int32, CPU) over a
+    pool of exactly the pages the sequences need plus `spare`: page ids in a shuffled
+    order, so that consecutive pages of a sequence lie anywhere in the pool.  Returns
+    (table, pages in the pool)."""
+    pps = (positions + page_size - 1) // page_size
+    pages = batch * pps + spare
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + 9_000_000)
+    perm = torch.randperm(pages, generator=g)[:batch * pps]
+    return perm.view(batch, pps).to(torch.int32).contiguous(), pages
 
 
 def layer_inputs(w, layer, device, context=None, batch=None):

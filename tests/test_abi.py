@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     exported = set(re.findall(r" T (kvq_\w+)", out))
     for n in names:
         assert n in exported, n
-    assert kvq.kvq_version() == 6
+    assert kvq.kvq_version() == 7
 
 
 def test_status_strings():
@@ -250,3 +250,39 @@ def test_quantizer_arithmetic_exhaustive_on_host(tmp_path, rule):
     assert r.returncode == 0, r.stdout
     assert "quotient_mismatches=0" in r.stdout and "scale_mismatches=0" in r.stdout
     assert "code_mismatches=0" in r.stdout
+
+
+def test_paged_validation_and_sizes():
+    """Paged layout (bxzpzcl.cn/news/2871434 section 3.1 pages; section 4 sizes): page
+    sizes 16 .. 256 (powers of two), capacity a multiple of the page, no sinks or recent
+    rows; buffers sized by the pool; positions beyond the capacity rejected."""
+    ok = kvq.make_desc("int4", 2, 8, 128, 1024, page_size=16, num_pages=100)
+    assert kvq.kvq_check_desc(ok) == kvq.KVQ_OK
+    assert kvq.kvq_codes_bytes(ok, 0) == 100 * 8 * 16 * 64
+    assert kvq.kvq_scales_bytes(ok, 0) == 100 * 8 * 16 * 2 * 4
+    assert kvq.kvq_scales_bytes(ok, 1) == 100 * 8 * 16 * 1 * 4
+    i8 = kvq.make_desc("int8", 2, 8, 128, 1024, page_size=64, num_pages=7)
+    assert kvq.kvq_codes_bytes(i8, 1) == 7 * 8 * 64 * 128
+    for fields, status in [
+        (dict(page_size=8, num_pages=10), kvq.KVQ_ERR_UNSUPPORTED),      # below 16
+        (dict(page_size=48, num_pages=10), kvq.KVQ_ERR_UNSUPPORTED),     # not a power of two
+        (dict(page_size=512, num_pages=10), kvq.KVQ_ERR_UNSUPPORTED),    # above 256
+        (dict(page_size=16, num_pages=0), kvq.KVQ_ERR_ARG),              # empty pool
+        (dict(page_size=-16, num_pages=10), kvq.KVQ_ERR_ARG),
+        (dict(page_size=16, num_pages=10, sinks=4), kvq.KVQ_ERR_UNSUPPORTED),
+        (dict(page_size=16, num_pages=10, recent=16), kvq.KVQ_ERR_UNSUPPORTED),
+    ]:
+        d = kvq.make_desc("int4", 2, 8, 128, 1024, **fields)
+        assert kvq.kvq_check_desc(d) == status, fields
+    odd = kvq.make_desc("int4", 2, 8, 128, 1000, page_size=16, num_pages=10)   # C % P != 0
+    assert kvq.kvq_check_desc(odd) == kvq.KVQ_ERR_UNSUPPORTED
+    c = kvq.kvq_cache(FAKE, FAKE, FAKE, FAKE, 0, 0, FAKE)
+    no_table = kvq.kvq_cache(FAKE, FAKE, FAKE, FAKE)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_quantize_prefill, ok, no_table, FAKE, FAKE, 0, 4, 0)
+    # no ring: positions at or past the capacity are rejected, windowed or not
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_quantize_prefill, ok, c, FAKE, FAKE, 1000, 25, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_append, ok, c, FAKE, FAKE, [1024, 3], 0)
+    ws = kvq.kvq_decode_workspace_bytes(ok, 32, 1024)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_decode_attn, ok, c, FAKE, 32, [1025, 10], 512, 0.0, 0,
+            FAKE, FAKE, ws, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_dequant, ok, c, 0, 1020, 5, FAKE, 0)
