@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define KVQ_VERSION 7
+#define KVQ_VERSION 8
 /* Largest batch the decode/append calls accept (per-sequence lengths and positions
  * travel in the kernel argument block). */
 #define KVQ_MAX_BATCH 256
@@ -292,6 +292,24 @@ int32_t kvq_append_decode_attn_noalloc(const kvq_cache_desc* desc, const kvq_cac
                                        int32_t q_heads, const int32_t* lens, int32_t window,
                                        float softmax_scale, int32_t num_splits, float* out,
                                        kvq_stream stream);
+
+/* Chunked-prefill attention over the packed cache ([KV-4bit] §1.1: the prefill computes
+ * every position of the prompt at once, where decode computes one): n_query tokens per
+ * sequence, at positions [len_b - n_query, len_b), whose K/V rows are already in the
+ * cache (kvq_quantize_prefill of the chunk), attend causally:
+ *   out[b, h, i] = sum_t softmax_t(scale * q[b,h,i] . x_K[b,kv,t]) * x_V[b,kv,t],
+ *   t over [lo, len_b - n_query + i], lo = max(0, len_b - n_query + i - window + 1) with
+ *   a window (window > 0), else 0; kv = h / (q_heads / Hkv); x = dequantized values.
+ *   q_f16: device, [B, q_heads, n_query, D] fp16; out: device, [B, q_heads, n_query, D]
+ *   fp32.  lens: host, [B], n_query <= len_b; len_b <= C, or (a window ring, contiguous
+ *   layout) window > 0 and window + n_query - 1 <= C - S.  softmax_scale as in
+ *   kvq_decode_attn.
+ * INT4 format with head_dim 128, V group 128 and K group 64 or 128, q_heads / Hkv in
+ * {1, 2, 4, 8}, no sinks or recent rows (KVQ_ERR_UNSUPPORTED otherwise); contiguous or
+ * paged.  Runs on the matrix cores; needs no workspace. */
+int32_t kvq_prefill_attn(const kvq_cache_desc* desc, const kvq_cache* cache, const void* q_f16,
+                         int32_t q_heads, int32_t n_query, const int32_t* lens, int32_t window,
+                         float softmax_scale, float* out, kvq_stream stream);
 
 /* Dequantize positions [start_pos, start_pos + n) of K (kv = 0) or V (kv = 1)
  * ([KV-4bit] §2.1 dequantize_4bit_group: code * scale; codec: s * H c[idx] / sqrt(D)).

@@ -10,6 +10,6 @@ from ._binding import (  # noqa: F401
     KVQ_MAX_RECENT, KVQ_NOALLOC_SCRATCH_BYTES, KVQ_WS_COUNTER_BYTES, LIB, LIB_PATH, DeviceCache, KvqError, decode_workspace, kvq_append,
     kvq_append_decode_attn, kvq_append_decode_attn_noalloc, kvq_cache, kvq_cache_desc, kvq_check_desc,
     kvq_codec_codebook, kvq_codec_codebook_bits, kvq_codes_bytes, kvq_decode_attn, kvq_decode_workspace_bytes,
-    kvq_dequant, kvq_plan_splits, kvq_quantize_prefill, kvq_scales_bytes, kvq_recent_bytes, kvq_version,
+    kvq_dequant, kvq_plan_splits, kvq_prefill_attn, kvq_quantize_prefill, kvq_scales_bytes, kvq_recent_bytes, kvq_version,
     make_desc, status_str,
 )

@@ -40,7 +40,7 @@ EXPORTS = (
     "kvq_recent_bytes",
     "kvq_plan_splits", "kvq_decode_workspace_bytes", "kvq_codec_codebook", "kvq_codec_codebook_bits",
     "kvq_quantize_prefill", "kvq_append", "kvq_decode_attn", "kvq_append_decode_attn",
-    "kvq_append_decode_attn_noalloc", "kvq_dequant",
+    "kvq_append_decode_attn_noalloc", "kvq_prefill_attn", "kvq_dequant",
 )
 
 
@@ -94,6 +94,7 @@ def _load(path=LIB_PATH):
                                          sz, vp]),
         "kvq_append_decode_attn_noalloc": (i32, [D, C, vp, vp, vp, i32, P(i32), i32, f32, i32, vp,
                                                  vp]),
+        "kvq_prefill_attn": (i32, [D, C, vp, i32, i32, P(i32), i32, f32, vp, vp]),
         "kvq_dequant": (i32, [D, C, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -246,6 +247,15 @@ def kvq_append_decode_attn_noalloc(desc, cache, k, v, q, q_heads, lens, window, 
         _i32_array(lens), int(window), float(softmax_scale), int(num_splits),
         _ptr(out, torch.float32, "out"), _stream(stream))
     return _check(st, "kvq_append_decode_attn_noalloc")
+
+
+def kvq_prefill_attn(desc, cache, q, q_heads, n_query, lens, window, softmax_scale, out,
+                     stream=None):
+    import torch
+    st = LIB.kvq_prefill_attn(ctypes.byref(desc), ctypes.byref(cache), _ptr(q, torch.float16, "q"),
+                              int(q_heads), int(n_query), _i32_array(lens), int(window),
+                              float(softmax_scale), _ptr(out, torch.float32, "out"), _stream(stream))
+    return _check(st, "kvq_prefill_attn")
 
 
 def decode_workspace(desc, q_heads, max_len, window=0, num_splits=0, device="cuda"):

@@ -431,6 +431,55 @@ int32_t kvq_append_decode_attn_noalloc(const kvq_cache_desc* desc, const kvq_cac
                        num_splits, out, USE_SCRATCH, 0, static_cast<hipStream_t>(stream));
 }
 
+int32_t kvq_prefill_attn(const kvq_cache_desc* desc, const kvq_cache* cache, const void* q_f16,
+                         int32_t q_heads, int32_t n_query, const int32_t* lens, int32_t window,
+                         float softmax_scale, float* out, kvq_stream stream) {
+  const int32_t st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (!cache_ok(desc, cache) || !q_f16 || !lens || !out || window < 0 || n_query < 1 ||
+      q_heads < 1 || !std::isfinite(softmax_scale) || softmax_scale < 0.0f)
+    return KVQ_ERR_ARG;
+  if (q_heads % desc->kv_heads) return KVQ_ERR_ARG;
+  const int32_t G = q_heads / desc->kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
+  if (desc->format != KVQ_INT4_G || desc->head_dim != 128 || desc->group_v != 128 ||
+      (desc->group_k != 64 && desc->group_k != 128) || desc->sinks > 0 || desc->recent > 0 ||
+      desc->capacity < 32)
+    return KVQ_ERR_UNSUPPORTED;
+  for (int32_t b = 0; b < desc->batch; ++b) {
+    const int32_t L = lens[b];
+    if (L < n_query) return KVQ_ERR_ARG;
+    if (L > desc->capacity) {   // a window ring must hold every position the chunk attends
+      if (desc->page_size > 0 || window == 0 || (int64_t)window + n_query - 1 > desc->capacity)
+        return KVQ_ERR_CAPACITY;
+    }
+  }
+  if ((uint64_t)desc->batch * q_heads * n_query * 128 >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k_codes = cache->k_codes;
+  a.k_scales = static_cast<const float*>(cache->k_scales);
+  a.v_codes = cache->v_codes;
+  a.v_scales = static_cast<const float*>(cache->v_scales);
+  a.q = static_cast<const uint16_t*>(q_f16);
+  a.out = out;
+  a.B = desc->batch;
+  a.Hkv = desc->kv_heads;
+  a.Hq = q_heads;
+  a.D = desc->head_dim;
+  a.cap = desc->capacity;
+  a.gk = desc->group_k;
+  a.gv = desc->group_v;
+  a.window = window;
+  a.nq = n_query;
+  a.pages = make_pages(desc, cache);
+  const float scale = softmax_scale != 0.0f ? softmax_scale
+                                            : 1.0f / std::sqrt((float)desc->head_dim);
+  a.qscale = scale * 1.4426950408889634f;
+  for (int32_t b = 0; b < desc->batch; ++b) a.lens[b] = lens[b];
+  return launch_status(launch_prefill_int4_mfma(a, G, static_cast<hipStream_t>(stream)));
+}
+
 int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t kv,
                     int32_t start_pos, int32_t n, float* out, kvq_stream stream) {
   const int32_t st = check_desc(desc);

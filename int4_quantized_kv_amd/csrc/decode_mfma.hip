@@ -1830,6 +1830,334 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   return a.sinks ? launch_gs<G, true, false>(a, s) : launch_gs<G, false, false>(a, s);
 }
 
+// ---------------------------------------------------------------------------------------
+// Chunked prefill: multi-query causal attention over the INT4 cache
+// (lpnh.cn/news/2042373 section 1.1: the prefill computes every position of a prompt
+// at once, where decode computes one).  A chunk of nq new tokens per sequence, whose
+// K/V rows are already in the cache at positions [len - nq, len), attends causally:
+// query i, at position len - nq + i, sees positions [lo_i, len - nq + i] with
+// lo_i = max(0, len - nq + i - window + 1) under a window, else 0.  Every cached row now
+// meets G * nq query rows, so the work is a dense contraction and the matrix cores bound
+// it, not HBM.
+//
+// Workgroup: (query block, KV head, sequence), PF_WAVES waves.  Wave w owns NCB column
+// blocks of 16 query rows: column c of block cb is head c % G of query
+// qb0 + (w * NCB + cb) * 16 / G + c / G.  All waves walk the same K/V tiles (the decode
+// kernel's 32-position LDS tile layout and transfers): tile t is staged by wave
+// t % PF_WAVES into slot t % NB of one ring, and one barrier per tile both publishes it
+// (its wave waited for its transfers first) and frees the slot the next transfer reuses.
+//   q.K   per tile half T and K group g (64 dims): A = the half's 16 K rows, k = 32 dims
+//         of group g (lane quarter j: dims 64 g + 16 j + 8 c2 + 0..7, c2 = 0, 1),
+//         B = q of the block's 16 columns at the same dims; two MFMAs per (T, g), whose
+//         sum is scaled by the group's K scale: z = sum_g sK(g) (q . codes_g).  (With
+//         one K group of 128 the scale slot holds the same scale twice.)
+//   P.V   as in decode: A = V codes (rows = 16 dims, k = 32 positions), B = the lane's
+//         own 8 values of P' = p~ * sV as fp16 hi and lo, in two MFMAs per dim group
+//         (every column is a query row, so the parts cannot share one MFMA here).
+// The online softmax, the V-scale normalizer and the masks are the decode kernel's, with
+// each column's own horizon.
+constexpr int PF_WAVES = 4;
+constexpr int PF_NT = PF_WAVES * 64;
+constexpr int PF_NCB = 2;   // column blocks (16 query rows each) per wave
+
+struct TileDataPF {
+  u32x2 k[2][2];     // [T][g]: dims 64 g + 16 j .. + 15 of tile row r of half T
+  u32x4 sk[2][2];    // [T][g]: K scales of rows 16 T + 4 j .. + 3, group g
+  uint32_t v[2][4];  // [T][i]: dword r of V row 16 T + 4 j + i
+  u32x4 sv[2];       // [T]: V scales of rows 16 T + 4 j .. + 3
+};
+
+struct LaneOffsPF {
+  int k[2];          // group g's 8-byte piece of row r (half 0; + 1024 for half 1)
+  int v[4];
+};
+
+// The 18 LDS reads of a tile for one lane, in one asm statement that waits for them
+// (for the reason given at read_tile).
+template <int NGK>
+__device__ __forceinline__ TileDataPF read_tile_pf(const uint8_t* lb, const LaneOffsPF& lo, int j) {
+  using L = Slot<NGK>;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_vptr)lb;
+  const uint32_t ak0 = base + L::K_OFF + lo.k[0], ak1 = base + L::K_OFF + lo.k[1];
+  const uint32_t ask = base + L::SK_OFF + 16 * j, asv = base + L::SV_OFF + 16 * j;
+  const uint32_t av0 = base + L::V_OFF + lo.v[0], av1 = base + L::V_OFF + lo.v[1];
+  const uint32_t av2 = base + L::V_OFF + lo.v[2], av3 = base + L::V_OFF + lo.v[3];
+  TileDataPF d;
+  asm volatile(
+      "ds_read_b64 %0, %18\n\t"
+      "ds_read_b64 %1, %19\n\t"
+      "ds_read_b64 %2, %18 offset:1024\n\t"
+      "ds_read_b64 %3, %19 offset:1024\n\t"
+      "ds_read_b128 %4, %20\n\t"
+      "ds_read_b128 %5, %20 offset:128\n\t"
+      "ds_read_b128 %6, %20 offset:64\n\t"
+      "ds_read_b128 %7, %20 offset:192\n\t"
+      "ds_read_b32 %8, %22\n\t"
+      "ds_read_b32 %9, %23\n\t"
+      "ds_read_b32 %10, %24\n\t"
+      "ds_read_b32 %11, %25\n\t"
+      "ds_read_b32 %12, %22 offset:1024\n\t"
+      "ds_read_b32 %13, %23 offset:1024\n\t"
+      "ds_read_b32 %14, %24 offset:1024\n\t"
+      "ds_read_b32 %15, %25 offset:1024\n\t"
+      "ds_read_b128 %16, %21\n\t"
+      "ds_read_b128 %17, %21 offset:64\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d.k[0][0]), "=&v"(d.k[0][1]), "=&v"(d.k[1][0]), "=&v"(d.k[1][1]),
+        "=&v"(d.sk[0][0]), "=&v"(d.sk[0][1]), "=&v"(d.sk[1][0]), "=&v"(d.sk[1][1]),
+        "=&v"(d.v[0][0]), "=&v"(d.v[0][1]), "=&v"(d.v[0][2]), "=&v"(d.v[0][3]),
+        "=&v"(d.v[1][0]), "=&v"(d.v[1][1]), "=&v"(d.v[1][2]), "=&v"(d.v[1][3]),
+        "=&v"(d.sv[0]), "=&v"(d.sv[1])
+      : "v"(ak0), "v"(ak1), "v"(ask), "v"(asv), "v"(av0), "v"(av1), "v"(av2), "v"(av3)
+      : "memory");
+  return d;
+}
+
+template <int G, int NGK, int NCB, bool PG>
+__global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) {
+  using L = Slot<NGK>;
+  constexpr int QPC = 16 / G;                  // queries per column block
+  constexpr int QWG = PF_WAVES * NCB * QPC;    // queries per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NB * L::BYTES];
+
+  const int qb0 = blockIdx.x * QWG, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int len = a.lens[b];
+  const int nq = a.nq;
+  const int p0 = len - nq;                     // position of query 0
+  const int W = a.window;
+  // the workgroup's queries [qb0, qe) and the positions they attend
+  const int qe = min(nq, qb0 + QWG);
+  const int hi_last = p0 + qe - 1;
+  const int lo_first = W > 0 ? max(0, p0 + qb0 - W + 1) : 0;
+  const int min_hi = p0 + qb0;                 // the first query's position
+  const int max_lo = W > 0 ? max(0, hi_last - W + 1) : 0;
+  const int tbase = lo_first & ~(TILE - 1);    // tiles from a multiple of 32 (paged layout)
+  const int pe = hi_last + 1;
+  const int ntiles = (pe - tbase + TILE - 1) / TILE;
+  const size_t row0 = (size_t)(b * a.Hkv + kvh) * a.cap;
+  const auto dof = dma_offsets<NGK>(lane);
+  auto issue = [&](int t) {
+    uint8_t* lb = ring + (t % NB) * L::BYTES;
+    const int t0 = tbase + TILE * t;
+    if constexpr (PG) issue_tile_pg<NGK>(a, b, kvh, t0, lo_first, pe, lb, lane, dof);
+    else issue_tile<NGK, false>(a, row0, t0, pe, 0, 0, lb, lane, dof);
+  };
+
+  // ---- the columns: q as the B operands of the four (g, c2) MFMAs, -8 * (sum of each
+  // group's q) for the nibble bias, and each column's horizon [clo, chi]
+  half8 qop[NCB][4];
+  float qbias[NCB][2];
+  int chi[NCB], clo[NCB], cq[NCB];
+  const int hh = r % G;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int qi = qb0 + (wave * NCB + cb) * QPC + r / G;
+    const bool live = qi < qe;
+    cq[cb] = live ? qi : -1;
+    const int pq = p0 + qi;
+    chi[cb] = live ? pq : -1;                  // (a junk column attends nothing)
+    clo[cb] = W > 0 ? max(0, pq - W + 1) : 0;
+    const uint16_t* qrow = a.q + (((size_t)b * a.Hq + kvh * G + hh) * nq + (live ? qi : 0)) * HD;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float qs = 0.0f;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const u32x4 raw = live ? *reinterpret_cast<const u32x4*>(qrow + 64 * g + 16 * j + 8 * c2)
+                               : (u32x4){0u, 0u, 0u, 0u};
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        H8 o;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {   // slot 2p: element p, slot 2p + 1: element p + 4
+          const uint32_t lo16 = (w[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
+          const uint32_t hi16 = (w[2 + (p >> 1)] >> (16 * (p & 1))) & 0xFFFFu;
+          o.u[p] = lo16 | (hi16 << 16);
+          f16x2 h2 = __builtin_bit_cast(f16x2, o.u[p]);
+          const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+          qs = __builtin_amdgcn_fdot2(h2, one2, qs, false);
+          if (p & 1) {   // slots of nibbles taken at bits 4..7 (16 times larger): q / 16
+            const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+            h2 = h2 * sixteenth;
+            o.u[p] = __builtin_bit_cast(uint32_t, h2);
+          }
+        }
+        qop[cb][2 * g + c2] = o.h;
+      }
+      qbias[cb][g] = -8.0f * sum_over_j(qs);
+    }
+  }
+
+  // per-lane LDS offsets: K rows r (group g's 8-byte piece), V dwords r of rows 4 j + i
+  LaneOffsPF lo;
+  {
+    const int P = rowinv(r);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) lo.k[g] = P * 64 + 16 * ((2 * g + (j >> 1)) ^ chunk_swz(P)) + 8 * (j & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int Pv = rowinv(4 * j + i);
+      lo.v[i] = Pv * 64 + 16 * ((r >> 2) ^ chunk_swz(Pv)) + 4 * (r & 3);
+    }
+  }
+
+  State st[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st[cb].oacc[e] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    st[cb].m = empty_max(a.qscale);
+    st[cb].l = 0.0f;
+    st[cb].lvs = 0;
+  }
+
+  // ---- the tile loop: tile t staged by wave t % PF_WAVES, two tiles ahead
+  if (wave == 0 && ntiles > 0) issue(0);
+  if (wave == 1 && ntiles > 1) issue(1);
+  for (int k = 0; k < ntiles; ++k) {
+    // a wave has at most one tile in flight (its tiles are PF_WAVES apart and it waits
+    // for each before the next is issued), so vmcnt(0) waits for exactly tile k
+    if (wave == k % PF_WAVES) wait_vmcnt<0>();
+    lds_barrier();   // tile k visible to every wave; every wave done with tile k - 1
+    if (k + 2 < ntiles && wave == (k + 2) % PF_WAVES) issue(k + 2);   // into tile k - 1's slot
+    const int t0 = tbase + TILE * k;
+    const TileDataPF td = read_tile_pf<NGK>(ring + (k % NB) * L::BYTES, lo, j);
+    // K operands of the tile (shared by the column blocks): [T][g][c2]
+    half8 ka[2][2][2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        ka[T][g][0] = unpack_word_u(td.k[T][g].x);
+        ka[T][g][1] = unpack_word_u(td.k[T][g].y);
+      }
+    // V operands: byte halves of two rows' dwords give the (row, row + 1) pairs of 4 dims
+    half8 va[8];
+    {
+      uint32_t xlo[4], xhi[4];
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const int T = pr >> 1, i = 2 * (pr & 1);
+        xlo[pr] = __builtin_amdgcn_perm(td.v[T][i + 1], td.v[T][i], 0x05040100u);
+        xhi[pr] = __builtin_amdgcn_perm(td.v[T][i + 1], td.v[T][i], 0x07060302u);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        H8 v;
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          const uint32_t x = e < 4 ? xlo[pr] : xhi[pr];
+          const uint32_t x8 = x >> 8;
+          switch (e & 3) {
+            case 0: v.u[pr] = v_pair_f16<0>(x, x8); break;
+            case 1: v.u[pr] = v_pair_f16<1>(x, x8); break;
+            case 2: v.u[pr] = v_pair_f16<2>(x, x8); break;
+            default: v.u[pr] = v_pair_f16<3>(x, x8); break;
+          }
+        }
+        va[e] = v.h;
+      }
+    }
+    const floatx4 sk00 = __builtin_bit_cast(floatx4, td.sk[0][0]), sk01 = __builtin_bit_cast(floatx4, td.sk[0][1]);
+    const floatx4 sk10 = __builtin_bit_cast(floatx4, td.sk[1][0]), sk11 = __builtin_bit_cast(floatx4, td.sk[1][1]);
+    const floatx4 sv0 = __builtin_bit_cast(floatx4, td.sv[0]), sv1 = __builtin_bit_cast(floatx4, td.sv[1]);
+    float svmax = fmaxf(fmaxf(fmaxf(sv0[0], sv0[1]), fmaxf(sv0[2], sv0[3])),
+                        fmaxf(fmaxf(sv1[0], sv1[1]), fmaxf(sv1[2], sv1[3])));
+    // (uniform) positions past the earliest query or before the latest window start
+    const bool masked = t0 + TILE - 1 > min_hi || t0 < max_lo;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      float z[2][4];
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        floatx4 c0 = (floatx4){0.f, 0.f, 0.f, 0.f}, c1 = c0;
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[T][0][0], qop[cb][0], c0, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[T][0][1], qop[cb][1], c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[T][1][0], qop[cb][2], c1, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[T][1][1], qop[cb][3], c1, 0, 0, 0);
+        const floatx4 s0 = T ? sk10 : sk00, s1 = T ? sk11 : sk01;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          z[T][i] = __builtin_fmaf(__builtin_fmaf(c0[i], 16777216.0f, qbias[cb][0]), s0[i],
+                                   __builtin_fmaf(c1[i], 16777216.0f, qbias[cb][1]) * s1[i]);
+      }
+      if (masked) {
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int p = t0 + 16 * T + 4 * j + i;
+            if (p > chi[cb] || p < clo[cb]) z[T][i] = NEG_INF;
+          }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                       fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+      mx = max_over_j(mx);
+      const float mq = tile_update(st[cb], mx, svmax, a.qscale);
+      H8 phi, plo;
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const floatx4 sv = T ? sv1 : sv0;
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float pa = fast_exp2(__builtin_fmaf(z[T][i], a.qscale, -mq));
+          const float pb = fast_exp2(__builtin_fmaf(z[T][i + 1], a.qscale, -mq));
+          st[cb].l += pa + pb;
+          split_hi_lo(pa * sv[i], pb * sv[i + 1], phi.u[2 * T + i / 2], plo.u[2 * T + i / 2]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        st[cb].oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[e], phi.h, st[cb].oacc[e], 0, 0, 0);
+        st[cb].oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[e], plo.h, st[cb].oacc[e], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- outputs: lane (column r, j) holds dims 8 (4 j + i) + e of its column
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+    for (int e = 1; e < 8; e += 2) st[cb].oacc[e] *= 0.0625f;   // see v_pair_f16
+    const float inv = 1.0f / sum_over_j(st[cb].l);
+    if (cq[cb] >= 0) {
+      float* orow = a.out + (((size_t)b * a.Hq + kvh * G + hh) * nq + cq[cb]) * HD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4* dst = reinterpret_cast<float4*>(orow + 8 * (4 * j + i));
+        dst[0] = make_float4(st[cb].oacc[0][i] * inv, st[cb].oacc[1][i] * inv,
+                             st[cb].oacc[2][i] * inv, st[cb].oacc[3][i] * inv);
+        dst[1] = make_float4(st[cb].oacc[4][i] * inv, st[cb].oacc[5][i] * inv,
+                             st[cb].oacc[6][i] * inv, st[cb].oacc[7][i] * inv);
+      }
+    }
+  }
+}
+
+template <int G, int NCB, bool PG>
+hipError_t launch_pf_g(const DecodeArgs& a, hipStream_t s) {
+  constexpr int QWG = PF_WAVES * NCB * (16 / G);
+  const dim3 grid((a.nq + QWG - 1) / QWG, a.Hkv, a.B);
+  switch (HD / a.gk) {
+    case 1: return launch_kernel(prefill_int4_mfma_kernel<G, 1, NCB, PG>, grid, dim3(PF_NT), a, s);
+    case 2: return launch_kernel(prefill_int4_mfma_kernel<G, 2, NCB, PG>, grid, dim3(PF_NT), a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool PG>
+hipError_t launch_pf(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
+  switch (q_group) {
+    case 1: return launch_pf_g<1, PF_NCB, PG>(a, s);
+    case 2: return launch_pf_g<2, PF_NCB, PG>(a, s);
+    case 4: return launch_pf_g<4, PF_NCB, PG>(a, s);
+    case 8: return launch_pf_g<8, PF_NCB, PG>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <bool SK, bool PG = false>
 hipError_t launch_i8(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
@@ -1881,6 +2209,10 @@ hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStre
 bool mfma_int8_eligible(int32_t head_dim, int32_t cap, int32_t q_group) {
   return head_dim == HD && cap >= TILE8 &&
          (q_group == 1 || q_group == 2 || q_group == 4 || q_group == 8);
+}
+
+hipError_t launch_prefill_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
+  return a.pages.size ? launch_pf<true>(a, q_group, s) : launch_pf<false>(a, q_group, s);
 }
 
 hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s) {

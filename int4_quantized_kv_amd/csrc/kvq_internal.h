@@ -95,6 +95,7 @@ struct DecodeArgs {
   int32_t recent;        // positions [len - recent, len) are read from the rings (each
                          // split takes a share of them)
   Pages pages;           // paged layout (pages.size > 0), else contiguous [B, Hkv, cap, .]
+  int32_t nq;            // chunked prefill: queries per sequence (q [B, Hq, nq, D])
   uint64_t* stamps;      // timeline probe builds only (-DKVQ_TIMELINE): phase timestamps
                          // of each workgroup of the matrix-core kernel, else null
   int32_t lens[KVQ_MAX_BATCH];
@@ -122,6 +123,10 @@ bool mfma_int4_eligible(int32_t head_dim, int32_t group_k, int32_t group_v, int3
 int32_t plan_splits_mfma(int32_t units, int32_t span);
 bool fused_append_supported(const kvq_cache_desc* d, int32_t q_group);
 hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
+// Chunked-prefill (multi-query causal) attention over the INT4 cache on the matrix cores
+// (head_dim 128, V group 128, K group 64 or 128): a.q [B, Hq, nq, D], a.out the same in
+// fp32; no workspace.
+hipError_t launch_prefill_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
 // The same kernel for the INT8 per-token format (head_dim 128, capacity >= 16).
 bool mfma_int8_eligible(int32_t head_dim, int32_t cap, int32_t q_group);
 hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);

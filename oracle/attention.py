@@ -95,3 +95,21 @@ def decode_attention(q, k_hat, v_hat, lens, window=0, scale=None, sinks=0):
             p = e / e.sum()
             out[b, h] = p @ V
     return out
+
+
+def prefill_attention(q, k_hat, v_hat, lens, window=0, scale=None):
+    """Chunked-prefill attention: the chunk's nq queries of each sequence, at positions
+    [len_b - nq, len_b), each attend causally ([KV-4bit] §1.1: the prefill processes every
+    position of the prompt, each seeing the positions up to its own): query i is a decode
+    query at length len_b - nq + i + 1 (the same horizon, window and GQA rule).
+
+    q:     [B, Hq, nq, D];  k_hat, v_hat: [B, Hkv, N, D] by position;  lens: [B].
+    Returns fp64 [B, Hq, nq, D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, nq, D = q.shape
+    out = np.zeros((B, Hq, nq, D), dtype=np.float64)
+    for i in range(nq):
+        lens_i = [int(ln) - nq + i + 1 for ln in lens]
+        out[:, :, i] = decode_attention(q[:, :, i], k_hat, v_hat, lens_i, window, scale)
+    return out

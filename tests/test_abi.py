@@ -23,14 +23,14 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(kvq.EXPORTS) == names
     out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (kvq_\w+)", out))
     for n in names:
         assert n in exported, n
-    assert kvq.kvq_version() == 7
+    assert kvq.kvq_version() == 8
 
 
 def test_status_strings():
@@ -286,3 +286,20 @@ def test_paged_validation_and_sizes():
     _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_decode_attn, ok, c, FAKE, 32, [1025, 10], 512, 0.0, 0,
             FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_dequant, ok, c, 0, 1020, 5, FAKE, 0)
+
+
+def test_prefill_attn_validation():
+    """kvq_prefill_attn: INT4 with head_dim 128, V group 128 and K group 64 or 128 only;
+    chunk within each sequence; a ring must hold the chunk's window."""
+    d = kvq.make_desc("int4", 2, 8, 128, 4096)
+    c = _cache()
+    out = FAKE
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_prefill_attn, d, c, FAKE, 32, 0, [100, 100], 0, 0.0, out, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_prefill_attn, d, c, FAKE, 32, 200, [100, 300], 0, 0.0, out, 0)
+    _expect(kvq.KVQ_ERR_ARG, kvq.kvq_prefill_attn, d, c, FAKE, 30, 16, [100, 300], 0, 0.0, out, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_prefill_attn, d, c, FAKE, 32, 16, [5000, 300], 0, 0.0, out, 0)
+    _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_prefill_attn, d, c, FAKE, 32, 16, [5000, 300], 4090, 0.0, out, 0)
+    for bad in (kvq.make_desc("int8", 2, 8, 128, 4096), kvq.make_desc("int4", 2, 8, 64, 4096),
+                kvq.make_desc("int4", 2, 8, 128, 4096, 32, 128), kvq.make_desc("int4", 2, 8, 128, 4096, 64, 64),
+                kvq.make_desc("codec", 2, 8, 128, 4096)):
+        _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_prefill_attn, bad, c, FAKE, 32, 16, [100, 100], 0, 0.0, out, 0)

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import quant
+from oracle import attention, quant
 from oracle.attention import attended_positions, decode_attention, recent_fp16_rows
 
 
@@ -193,3 +193,49 @@ def test_recent_reads_each_position_from_one_form_only():
     k163[1, :, 23 - R] = 50.0                          # the first recent position of sequence 1
     moved = decode_attention(q, recent_fp16_rows(kh, k163, lens, R), recent_fp16_rows(vh, v16, lens, R), lens)
     assert not np.allclose(base[1], moved[1]) and np.array_equal(base[0], moved[0])
+
+
+def test_prefill_attention_matches_torch_causal_sdpa():
+    """The chunk's queries against torch's scaled_dot_product_attention with a causal
+    mask aligned to the end of the key range (query i sees keys 0 .. len - nq + i), in
+    fp64 on the CPU, for GQA 4:1 (the KV heads repeated per query head) and a window
+    (the mask also drops keys before len - nq + i - W + 1)."""
+    import torch
+    rng = np.random.default_rng(21)
+    B, Hkv, G, D, nq = 2, 2, 4, 16, 7
+    lens = [40, 29]
+    N = max(lens)
+    q = rng.standard_normal((B, Hkv * G, nq, D))
+    k = rng.standard_normal((B, Hkv, N, D))
+    v = rng.standard_normal((B, Hkv, N, D))
+    for W in (0, 9):
+        got = attention.prefill_attention(q, k, v, lens, W)
+        for b, ln in enumerate(lens):
+            kk = torch.from_numpy(k[b:b + 1, :, :ln]).repeat_interleave(G, dim=1)
+            vv = torch.from_numpy(v[b:b + 1, :, :ln]).repeat_interleave(G, dim=1)
+            pos_q = torch.arange(ln - nq, ln)[:, None]
+            pos_k = torch.arange(ln)[None, :]
+            mask = pos_k <= pos_q
+            if W:
+                mask &= pos_k > pos_q - W
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b:b + 1]), kk, vv, attn_mask=mask).numpy()
+            assert np.allclose(got[b:b + 1], ref, rtol=1e-12, atol=1e-12), (W, b)
+
+
+def test_prefill_last_query_is_the_decode_query():
+    """The chunk's last query attends exactly like a decode step at the full length; a
+    one-token chunk is a decode step."""
+    rng = np.random.default_rng(22)
+    B, H, D, nq = 2, 3, 8, 5
+    lens = [12, 30]
+    q = rng.standard_normal((B, H, nq, D))
+    k = rng.standard_normal((B, H, 30, D))
+    v = rng.standard_normal((B, H, 30, D))
+    out = attention.prefill_attention(q, k, v, lens, 6)
+    assert np.array_equal(out[:, :, -1], attention.decode_attention(q[:, :, -1], k, v, lens, 6))
+    one = attention.prefill_attention(q[:, :, :1], k, v, lens)
+    assert np.array_equal(one[:, :, 0], attention.decode_attention(q[:, :, 0], k, v, lens))
+    # the first query of a chunk that starts the sequence sees only position 0
+    first = attention.prefill_attention(q, k, v, [nq, nq])
+    assert np.allclose(first[:, :, 0], v[:, :, 0])
