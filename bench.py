@@ -31,6 +31,9 @@ the same form; the default run is the headline above):
   llama8b-paged  the headline step on the paged layout: pages of 16 positions, each
                  sequence's pages shuffled over the pool by a seeded block table
   dequant        kvq_dequant of K and V of 8 Llama-3-8B-shaped layer caches to fp32
+  llama8b-prefill-chunk  chunked prefill on the Llama-3-8B shape: per layer, quantize a
+                 512-token chunk into positions 7680 .. 8191 and attend it causally
+                 (kvq_prefill_attn); TFLOP/s against the fp16 matrix-core peak
 """
 import argparse
 import ctypes
@@ -43,6 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+MFMA_F16_PEAK_TFS = 2500.0   # MI355X dense fp16 matrix-core peak, published
 # Sources of the dominant kernel (and its build flags): HBM-traffic counters recorded in
 # profiles/ are reported only while these files hash to the value recorded with them.
 _COMMON = ["int4_quantized_kv_amd/csrc/kvq_device.h", "int4_quantized_kv_amd/csrc/kvq_internal.h",
@@ -76,7 +80,7 @@ def parse():
     p.add_argument("--workload", default="llama8b",
                    choices=["llama8b", "mha7b-prefill", "mha7b-decode", "ctx128k-int4",
                             "ctx128k-int8", "gemma-codec", "gemma-codec3", "llama8b-sinks", "llama8b-recent",
-                            "llama8b-int4h", "llama8b-paged",
+                            "llama8b-int4h", "llama8b-paged", "llama8b-prefill-chunk",
                             "dequant"])
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
@@ -131,7 +135,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload != "llama8b":
         line = OTHER[args.workload](args)
-        line["roofline"]["traffic"] = recorded_traffic(*OTHER_TRAFFIC[args.workload])
+        if args.workload in OTHER_TRAFFIC:
+            line["roofline"]["traffic"] = recorded_traffic(*OTHER_TRAFFIC[args.workload])
         add_attainable(args, line)
         print(json.dumps(line), flush=True)
         return
@@ -977,7 +982,117 @@ def bench_dequant(args):
                  {"bytes_per_step": nbytes, "wall_s_timed": round(wall, 4)})
 
 
-OTHER = {"mha7b-prefill": bench_prefill, "mha7b-decode": bench_decode, "ctx128k-int4": bench_decode,
+def bench_prefill_chunk(args):
+    """Chunked prefill on the Llama-3-8B shape: the last 512 tokens of an 8192-token prompt
+    as one chunk per layer.  A step = for each of the 32 layers (distinct caches holding
+    positions 0 .. 7679), kvq_quantize_prefill of the chunk's K/V into positions
+    7680 .. 8191, then kvq_prefill_attn of its 512 queries (causal).  The attention is a
+    dense contraction (G * 512 query rows per cached row), so its roofline is the matrix
+    cores' fp16 peak; flops are the algorithmic 4 * head_dim per (query row, attended
+    position) (q.K and P.V, 2 flops per multiply-add)."""
+    import torch
+    import int4_quantized_kv_amd as kvq
+    import synth
+    w = synth.WORKLOADS[2]
+    dev = "cuda:0"
+    nl = args.layers or w.layers
+    B, Hq, Hkv, D = w.batch, w.q_heads, w.kv_heads, w.head_dim
+    NQ, L = 512, w.context
+    P0 = L - NQ
+    desc = kvq.make_desc("int4", B, Hkv, D, L, w.group_k, w.group_v)
+    dref = ctypes.byref(desc)
+    LIB = kvq.LIB
+    layers = []
+    for li in range(nl):
+        k, v, _, _, _ = synth.layer_inputs(w, li, dev)
+        lay = Layer()
+        lay.dc = kvq.DeviceCache(desc, dev)
+        kvq.kvq_quantize_prefill(desc, lay.dc.c, k[:, :, :P0].contiguous(), v[:, :, :P0].contiguous(), 0, P0)
+        lay.kc, lay.vc = k[:, :, P0:].contiguous(), v[:, :, P0:].contiguous()
+        del k, v
+        lay.q = synth.query((B, Hq, NQ, D), synth.seed_of(w.wid, li, 6), dev)
+        lay.out = torch.empty((B, Hq, NQ, D), dtype=torch.float32, device=dev)
+        lay.cref = ctypes.byref(lay.dc.c)
+        layers.append(lay)
+    torch.cuda.synchronize()
+    lens = (ctypes.c_int32 * B)(*([L] * B))
+
+    def step(stream, attend_only=False):
+        sp = ctypes.c_void_p(stream)
+        for lay in layers:
+            if not attend_only:
+                st = LIB.kvq_quantize_prefill(dref, lay.cref, lay.kc.data_ptr(), lay.vc.data_ptr(), P0, NQ, sp)
+                if st:
+                    raise kvq.KvqError(st, "kvq_quantize_prefill")
+            st = LIB.kvq_prefill_attn(dref, lay.cref, lay.q.data_ptr(), Hq, NQ, lens, 0, 0.0,
+                                      lay.out.data_ptr(), sp)
+            if st:
+                raise kvq.KvqError(st, "kvq_prefill_attn")
+
+    run = _runner(args, step)
+    ms_step, wall = _timed(run, args.steps)
+    attn = _runner(args, lambda st: step(st, attend_only=True))
+    attn_ms, _ = _timed(attn, args.steps)
+    pairs = B * Hq * (NQ * P0 + NQ * (NQ + 1) // 2)   # (query row, attended position) pairs
+    flops = 4 * D * pairs                              # per layer
+    tfs = nl * flops / (ms_step * 1e-3) / 1e12
+    kern_tfs = flops / (attn_ms * 1e-3 / nl) / 1e12
+    roof = {"kernel": "kvq_prefill_attn: prefill_int4_mfma_kernel", "bound": "mfma",
+            "achieved": round(kern_tfs, 1), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": round(kern_tfs / MFMA_F16_PEAK_TFS, 4), "traffic": None,
+            "flops_per_launch": flops, "avg_launch_us": round(attn_ms * 1e3 / nl, 2)}
+    cfg = {"workload": w.name + "-prefill-chunk512", "format": "int4", "layers": nl, "batch": B,
+           "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "chunk": NQ, "chunk_start": P0,
+           "context": L, "launch": "eager" if args.eager else "hip-graph"}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill_chunk(w, args.cpu_seconds, NQ, L)
+    out = {"metric": "chunked prefill attention over the INT4 cache: TFLOP/s (Llama-3-8B shape, "
+                     "512-token chunk at 8K)",
+           "value": round(tfs, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16 MFMA, f32 accumulate",
+           "data": "synthetic", "config": cfg,
+           "prefill_tok_per_s": round(B * NQ / (ms_step * 1e-3), 1),
+           "flops_per_step": nl * flops, "wall_s_timed": round(wall, 4)}
+    out["roofline"] = roof
+    out["cpu_baseline"] = cpu
+    return out
+
+
+def cpu_baseline_prefill_chunk(w, seconds, NQ, L):
+    """The oracle's prefill attention (never tuned) on one host core: one (batch, kv
+    head) unit of layer 0 at a time (the G query heads' 512 chunk queries over their
+    causal horizons, exact dequantization included) until `seconds` of timed work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import synth
+    from oracle import attention, quant
+    G = w.q_heads // w.kv_heads
+    D = w.head_dim
+    k, v, _, _, _ = synth.layer_inputs(w, 0, "cuda:0")
+    k, v = k.cpu().numpy(), v.cpu().numpy()
+    units, dt, pairs = 0, 0.0, 0
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            if dt >= seconds:
+                break
+            q = synth.query((1, G, NQ, D), synth.seed_of(w.wid, 0, 6) + units, "cpu").numpy()
+            with threadpool_limits(1):
+                t0 = time.perf_counter()
+                qk, sk = quant.quantize_int4(k[b, h][None, None], 64)
+                qv, sv = quant.quantize_int4(v[b, h][None, None], 128)
+                kh = quant.dequantize_int4_exact(qk, sk, 64)
+                vh = quant.dequantize_int4_exact(qv, sv, 128)
+                attention.prefill_attention(q, kh, vh, [L])
+                dt += time.perf_counter() - t0
+            units += 1
+            pairs += G * (NQ * (L - NQ) + NQ * (NQ + 1) // 2)
+    return dict({"value": round(4 * D * pairs / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                 "kind": "oracle",
+                 "sample": f"{units} of layer 0's {w.batch * w.kv_heads} (batch, kv head) units "
+                           f"({G} heads x {NQ} chunk queries, fp64), {dt:.2f} s timed"}, **_cpu_meta(1))
+
+
+OTHER = {"mha7b-prefill": bench_prefill, "llama8b-prefill-chunk": bench_prefill_chunk, "mha7b-decode": bench_decode, "ctx128k-int4": bench_decode,
          "ctx128k-int8": bench_decode, "gemma-codec": bench_decode, "llama8b-sinks": bench_decode,
          "llama8b-recent": bench_decode, "gemma-codec3": bench_decode, "llama8b-int4h": bench_decode,
          "llama8b-paged": bench_decode,

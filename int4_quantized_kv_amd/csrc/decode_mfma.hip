@@ -1858,7 +1858,8 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
 // each column's own horizon.
 constexpr int PF_WAVES = 4;
 constexpr int PF_NT = PF_WAVES * 64;
-constexpr int PF_NCB = 2;   // column blocks (16 query rows each) per wave
+constexpr int PF_NCB = 1;   // column blocks (16 query rows each) per wave: 2 measured
+                            // 365 vs 458 TFLOP/s (261 VGPRs, one wave per SIMD)
 
 struct TileDataPF {
   u32x2 k[2][2];     // [T][g]: dims 64 g + 16 j .. + 15 of tile row r of half T
