@@ -71,6 +71,7 @@ OTHER_TRAFFIC = {
     "llama8b-int4h": ("profiles/decode_splitk_int4h_llama8b_ctx8k_b8_traffic.md",
                       ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
     "llama8b-paged": ("profiles/decode_int4_mfma_llama8b_ctx8k_paged16_traffic.md", KERNEL_SOURCES),
+    "llama8b-prefill-chunk": ("profiles/prefill_int4_mfma_llama8b_chunk512_ctx8k_traffic.md", KERNEL_SOURCES),
 }
 
 
