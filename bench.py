@@ -68,8 +68,7 @@ OTHER_TRAFFIC = {
     "llama8b-recent": ("profiles/decode_int4_mfma_llama8b_ctx8k_recent128_traffic.md", KERNEL_SOURCES),
     "gemma-codec3": ("profiles/decode_splitk_codec3_gemma3_4b_b4_traffic.md",
                      ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
-    "llama8b-int4h": ("profiles/decode_splitk_int4h_llama8b_ctx8k_b8_traffic.md",
-                      ["int4_quantized_kv_amd/csrc/decode.hip"] + _COMMON),
+    "llama8b-int4h": ("profiles/decode_int4_mfma_int4h_llama8b_ctx8k_b8_traffic.md", KERNEL_SOURCES),
     "llama8b-paged": ("profiles/decode_int4_mfma_llama8b_ctx8k_paged16_traffic.md", KERNEL_SOURCES),
     "llama8b-prefill-chunk": ("profiles/prefill_int4_mfma_llama8b_chunk512_ctx8k_traffic.md", KERNEL_SOURCES),
 }
@@ -837,8 +836,11 @@ def bench_decode(args):
         attn_ms, _ = _timed(attn, args.steps)
     else:
         attn_ms = ms_step
-    if fmt == "int4" and D == 128 and w.group_v == 128:
+    if fmt in ("int4", "int4h") and D == 128 and w.group_v == 128:
         kern = "kvq_decode_attn: decode_int4_mfma_kernel (splits merged in-kernel)"
+        if fmt == "int4h":
+            kern = ("kvq_decode_attn: decode_int4_mfma_kernel, fp16-scale instance (splits merged "
+                    "in-kernel)")
         if w.page_size:
             kern = (f"kvq_decode_attn: decode_int4_mfma_kernel, paged instance (pages of "
                     f"{w.page_size}, splits merged in-kernel)")

@@ -606,6 +606,8 @@ hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
   hipError_t e;
   if (FMT == KVQ_INT4_G && mfma_int4_eligible(D, a.gk, a.gv, a.cap, G))
     return launch_decode_int4_mfma(a, G, s);   // merges the splits itself
+  if (FMT == KVQ_INT4_G16 && a.sinks == 0 && a.recent == 0 && mfma_int4_eligible(D, a.gk, a.gv, a.cap, G))
+    return launch_decode_int4h_mfma(a, G, s);
   if (FMT == KVQ_INT8_TOKEN && mfma_int8_eligible(D, a.cap, G))
     return launch_decode_int8_mfma(a, G, s);
   // up to MERGE_INLINE_MAX splits the last split of a unit merges inside the kernel
@@ -647,6 +649,7 @@ int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
     return plan_splits_mfma(units, span);
   if (d->format == KVQ_INT8_TOKEN && mfma_int8_eligible(d->head_dim, d->capacity, q_group))
     return plan_splits_mfma(units, span);
+  if (mfma_int4h_eligible(d, q_group)) return plan_splits_mfma(units, span);
   // the codecs and INT4 with fp16 scales keep one more split for the new row when the
   // append is fused (planned for every call of those formats, so that the workspace
   // query does not depend on the call)

@@ -199,6 +199,18 @@ template <int AUX = 0>
 __device__ __forceinline__ void dma4(const void* g, uint8_t* l) {
   __builtin_amdgcn_global_load_lds((gbl_vptr)g, (lds_vptr)l, 4, 0, AUX);
 }
+// The transfer of one scale per lane into one LDS dword per lane.  fp32 scales: a
+// 4-byte transfer.  fp16 scales (H16): a 2-byte transfer, which lands zero-extended in
+// the low half of the lane's dword (lane stride 4 bytes, checked on gfx950), so the
+// LDS tile layout and its reads are the same for both and the reader converts.
+template <bool H16>
+__device__ __forceinline__ void dma_scale(const uint8_t* g, uint8_t* l) {
+  if constexpr (H16) __builtin_amdgcn_global_load_lds((gbl_vptr)g, (lds_vptr)l, 2, 0, CPOL_NT);
+  else __builtin_amdgcn_global_load_lds((gbl_vptr)g, (lds_vptr)l, 4, 0, CPOL_NT);
+}
+// bytes of one stored scale, and the shift from a 4-byte scale offset to the stored one
+template <bool H16> constexpr int SCB = H16 ? 2 : 4;
+template <bool H16> constexpr int SCSH = H16 ? 1 : 0;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -274,7 +286,7 @@ __device__ __forceinline__ DmaOffs dma_offsets(int lane) {
 // the LDS slot `lb`.  A full tile whose 32 slots are contiguous is addressed from one
 // scalar base row plus the fixed lane offsets; otherwise each row is clamped to pe - 1
 // (masked positions read a valid row) and wrapped around the ring.
-template <int NGK, bool SK>
+template <int NGK, bool SK, bool H16 = false>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int t0, int pe,
                                            int lo, int vlo, uint8_t* lb, int lane,
                                            const DmaOffs& o) {
@@ -289,16 +301,17 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int
     const size_t rb = row0 + (size_t)sbase;
     const uint8_t* kb = kc + rb * (HD / 2);
     const uint8_t* vb = vc + rb * (HD / 2);
-    const uint8_t* ksb = ks + rb * (NGK * 4);
-    const uint8_t* vsb = vs + rb * 4;
+    const uint8_t* ksb = ks + rb * (NGK * SCB<H16>);
+    const uint8_t* vsb = vs + rb * SCB<H16>;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       dma16<CPOL_NT>(kb + o.kv[T], lb + L::K_OFF + 1024 * T);
       dma16<CPOL_NT>(vb + o.kv[T], lb + L::V_OFF + 1024 * T);
     }
 #pragma unroll
-    for (int h = 0; h < (NGK <= 2 ? 1 : 2); ++h) dma4<CPOL_NT>(ksb + o.sk[h], lb + L::SK_OFF + 256 * h);
-    dma4<CPOL_NT>(vsb + o.sv, lb + L::SV_OFF);
+    for (int h = 0; h < (NGK <= 2 ? 1 : 2); ++h)
+      dma_scale<H16>(ksb + (o.sk[h] >> SCSH<H16>), lb + L::SK_OFF + 256 * h);
+    dma_scale<H16>(vsb + (o.sv >> SCSH<H16>), lb + L::SV_OFF);
     return;
   }
   auto row_of = [&](int rho) -> size_t {
@@ -321,8 +334,9 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int
   const size_t srow = row_of(lane & 31);
 #pragma unroll
   for (int h = 0; h < (NGK <= 2 ? 1 : 2); ++h)
-    dma4<CPOL_NT>(ks + srow * (NGK * 4) + (o.sk[h] - (lane & 31) * NGK * 4), lb + L::SK_OFF + 256 * h);
-  dma4<CPOL_NT>(vs + srow * 4, lb + L::SV_OFF);
+    dma_scale<H16>(ks + (srow * (NGK * 4) + (o.sk[h] - (lane & 31) * NGK * 4)) / (4 / SCB<H16>),
+                   lb + L::SK_OFF + 256 * h);
+  dma_scale<H16>(vs + srow * SCB<H16>, lb + L::SV_OFF);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -359,7 +373,7 @@ __device__ __forceinline__ PageRows page_rows(const DecodeArgs& a, int b, int t0
   return r;
 }
 
-template <int NGK>
+template <int NGK, bool H16 = false>
 __device__ __forceinline__ void issue_tile_pg(const DecodeArgs& a, int b, int h, int t0, int pb,
                                               int pe, uint8_t* lb, int lane, const DmaOffs& o) {
   using L = Slot<NGK>;
@@ -389,8 +403,9 @@ __device__ __forceinline__ void issue_tile_pg(const DecodeArgs& a, int b, int h,
   const size_t srow = row_of(lane & 31);
 #pragma unroll
   for (int hh = 0; hh < (NGK <= 2 ? 1 : 2); ++hh)
-    dma4<CPOL_NT>(ks + srow * (NGK * 4) + (o.sk[hh] - (lane & 31) * NGK * 4), lb + L::SK_OFF + 256 * hh);
-  dma4<CPOL_NT>(vs + srow * 4, lb + L::SV_OFF);
+    dma_scale<H16>(ks + (srow * (NGK * 4) + (o.sk[hh] - (lane & 31) * NGK * 4)) / (4 / SCB<H16>),
+                   lb + L::SK_OFF + 256 * hh);
+  dma_scale<H16>(vs + srow * SCB<H16>, lb + L::SV_OFF);
 }
 
 // Position sets.  A head's q.K needs G * NGK of the 16 MFMA columns.  When that is at
@@ -429,6 +444,15 @@ __device__ __forceinline__ void split_hi_lo(float q0, float q1, uint32_t& hi, ui
   hi = pk_f16_rne(q0, q1);
   const f16x2 h = __builtin_bit_cast(f16x2, hi);
   lo = pk_f16_rne(__builtin_fmaf((float)h.x, -1.0f, q0), __builtin_fmaf((float)h.y, -1.0f, q1));
+}
+
+// Four scales stored as fp16 in the low halves of four dwords -> their fp32 values (exact).
+__device__ __forceinline__ u32x4 f16lo_to_f32(const u32x4& w) {
+  const floatx4 f = {(float)__builtin_bit_cast(_Float16, (uint16_t)w.x),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)w.y),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)w.z),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)w.w)};
+  return __builtin_bit_cast(u32x4, f);
 }
 
 // The softmax / V-scale update of one tile.  `mx` is the tile's score maximum of the
@@ -557,13 +581,20 @@ __device__ __forceinline__ TileData read_tile(const uint8_t* lb, const LaneOffs&
 // score -inf.  One code path serves both kinds of tile, and the masking only rewrites
 // the scores in place: with two instances of the tile in the loop, the compiler gave
 // the accumulators of each its own registers and copied all 32 of them twice per tile.
-template <int G, int NGK, int S>
+template <int G, int NGK, int S, bool H16 = false>
 __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& lo, State& st,
                                              const half8 (&qb)[4 * S], float qbias, int t0,
                                              int pmin, int pe, int j, float qscale, bool lo_col,
                                              int soff, bool masked) {
   constexpr int NTB = 2 / S;   // 16-row blocks of q.K results per lane
-  const TileData td = read_tile<NGK, S>(lb, lo);
+  TileData td = read_tile<NGK, S>(lb, lo);
+  if constexpr (H16) {   // fp16 scales sit in the low halves of their dwords (dma_scale)
+#pragma unroll
+    for (int T = 0; T < NTB; ++T) {
+      td.sk[T] = f16lo_to_f32(td.sk[T]);
+      td.sv[T] = f16lo_to_f32(td.sv[T]);
+    }
+  }
   // ---- q.K: lane (r, j) gets rows 4j + i of block T for column r = (set, head, group)
   const uint32_t kw8[8] = {td.k[0].x, td.k[0].y, td.k[0].z, td.k[0].w,
                            td.k[1].x, td.k[1].y, td.k[1].z, td.k[1].w};
@@ -1009,7 +1040,9 @@ __device__ __forceinline__ float row_reduce(float x) {
   return x;
 }
 
-template <int G, int NGK>
+// H16: the fp16-scale format's arithmetic (the append kernel's): scale fl16(amax / 7),
+// 1 when that is 0, and each quotient rounded to fp16 before it is rounded to an integer.
+template <int G, int NGK, bool H16 = false>
 __device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds* s,
                                              const uint8_t* qrows, int lane) {
   NewRow nr;
@@ -1023,13 +1056,20 @@ __device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds* 
   for (int jj = 0; jj < 8; ++jj) am = fmaxf(am, fabsf(x[jj]));
   const float am_row = row_reduce<true, 16>(am);
   am = isv ? am_row : row_reduce<true, LPG_K>(am);
-  const float sc = kvq_int4_scale(am);
+  float sc;
+  if constexpr (H16) {
+    const float s16 = (float)(_Float16)(am / 7.0f);
+    sc = s16 == 0.0f ? 1.0f : s16;
+  } else {
+    sc = kvq_int4_scale(am);
+  }
   const float rc = 1.0f / sc;
   uint32_t w = 0;
   float code[8];
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    const float q = fminf(fmaxf(rintf(kvq_div_exact(x[jj], sc, rc)), -7.0f), 7.0f);
+    const float y = H16 ? (float)(_Float16)(x[jj] / sc) : kvq_div_exact(x[jj], sc, rc);
+    const float q = fminf(fmaxf(rintf(y), -7.0f), 7.0f);
     code[jj] = q;
     w |= ((uint32_t)(int)q & 15u) << (4 * jj);
   }
@@ -1056,20 +1096,24 @@ __device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds* 
 }
 
 // Write the new row's codes and scales (kept in LDS by lanes 0..31) to cache row `row`.
-template <int NGK>
+template <int NGK, bool H16 = false>
 __device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewLds* s, size_t row,
                                               int lane) {
   const bool isv = lane >= 16;
   const int c = lane & 15;
   const uint32_t w = s->w[lane];
   const float sc = s->sc[lane];
+  auto put = [](const float* base, size_t i, float v) {   // (fp16 scales: v is exact in fp16)
+    if constexpr (H16) reinterpret_cast<_Float16*>(const_cast<float*>(base))[i] = (_Float16)v;
+    else const_cast<float*>(base)[i] = v;
+  };
   if (isv) {
     static_cast<uint32_t*>(const_cast<void*>(a.v_codes))[row * (HD / 8) + c] = w;
-    if (c == 0) const_cast<float*>(a.v_scales)[row] = sc;
+    if (c == 0) put(a.v_scales, row, sc);
   } else {
     const int lpg = a.gk >> 3;
     static_cast<uint32_t*>(const_cast<void*>(a.k_codes))[row * (HD / 8) + c] = w;
-    if ((c & (lpg - 1)) == 0) const_cast<float*>(a.k_scales)[row * NGK + c / lpg] = sc;
+    if ((c & (lpg - 1)) == 0) put(a.k_scales, row * NGK + c / lpg, sc);
   }
 }
 
@@ -1245,7 +1289,10 @@ __device__ __forceinline__ void recent_entry(const DecodeArgs& a, int unit, int 
 
 // PG: the paged layout (page-aligned tiles, rows through the block table; a separate
 // instance, so that the contiguous case carries none of it).
-template <int G, int NGK, bool I8, bool SK, bool RC = false, bool PG = false>
+// H16: INT4 with fp16 scales (KVQ_INT4_G16): 2-byte scale transfers into the same tile
+// layout, converted after the LDS reads; the fused append codes the new row with the
+// format's fp16 arithmetic.
+template <int G, int NGK, bool I8, bool SK, bool RC = false, bool PG = false, bool H16 = false>
 __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   using L = std::conditional_t<I8, Slot8, Slot<NGK>>;
   constexpr int TL = I8 ? TILE8 : TILE;       // positions per tile
@@ -1339,10 +1386,10 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   auto issue = [&](int t0, uint8_t* lb) {
     if constexpr (PG) {
       if constexpr (I8) issue_tile8_pg(a, b, kvh, t0, pb, pe, lb, dof);
-      else issue_tile_pg<NGK>(a, b, kvh, t0, pb, pe, lb, lane, dof);
+      else issue_tile_pg<NGK, H16>(a, b, kvh, t0, pb, pe, lb, lane, dof);
     } else {
       if constexpr (I8) issue_tile8<SK>(a, row0, t0, pe, lo_pos, vlo, lb, dof);
-      else issue_tile<NGK, SK>(a, row0, t0, pe, lo_pos, vlo, lb, lane, dof);
+      else issue_tile<NGK, SK, H16>(a, row0, t0, pe, lo_pos, vlo, lb, lane, dof);
     }
   };
   if (threadIdx.x == 0) s_claim = 0;   // ordered before the first claim by the q barrier
@@ -1482,7 +1529,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   qbias = -8.0f * sum_over_j(qs);
   }
   if constexpr (!I8) if (app_wave && lane < 32) {
-    const NewRow nr = append_row<G, NGK>(a, &s_new, qstage, lane);
+    const NewRow nr = append_row<G, NGK, H16>(a, &s_new, qstage, lane);
     s_new.w[lane] = nr.w;
     s_new.sc[lane] = nr.sc;
     if (lane >= 16) {
@@ -1533,7 +1580,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       process_tile8<G>(ring + (k % NB) * L::BYTES, lo, st, qb, t0, pb, pe, j, a.qscale, lo_col,
                        masked);
     else
-      process_tile<G, NGK, S>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pb, pe, j,
+      process_tile<G, NGK, S, H16>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pb, pe, j,
                               a.qscale, lo_col, 16 * cset, masked);
 #pragma unroll
     for (int i = 0; i + 1 < DEPTH; ++i) tq[i] = tq[i + 1];
@@ -1691,7 +1738,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     size_t nrow;
     if constexpr (PG) nrow = page_rows<TL>(a, b, len - 1, len).row(a.pages, a.Hkv, kvh, len - 1);
     else nrow = row0 + (size_t)(SK ? cache_slot(len - 1, a.cap, a.sinks) : (len - 1) % a.cap);
-    store_new_row<NGK>(a, &s_new, nrow, lane);
+    store_new_row<NGK, H16>(a, &s_new, nrow, lane);
   }
   uint32_t* cnt = a.counters + unit;
 #ifdef KVQ_TIMELINE
@@ -1809,25 +1856,33 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 #endif
 }
 
-template <int G, bool SK, bool RC, bool PG = false>
+template <int G, bool SK, bool RC, bool PG = false, bool H16 = false>
 hipError_t launch_gs(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.nsplit, a.Hkv, a.B);
   switch (HD / a.gk) {
-    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1, false, SK, RC, PG>, grid, dim3(NT), a, s);
-    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2, false, SK, RC, PG>, grid, dim3(NT), a, s);
+    case 1: return launch_kernel(decode_int4_mfma_kernel<G, 1, false, SK, RC, PG, H16>, grid, dim3(NT), a, s);
+    case 2: return launch_kernel(decode_int4_mfma_kernel<G, 2, false, SK, RC, PG, H16>, grid, dim3(NT), a, s);
     case 4:
-      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4, false, SK, RC, PG>, grid, dim3(NT), a, s);
+      if constexpr (G <= 4) return launch_kernel(decode_int4_mfma_kernel<G, 4, false, SK, RC, PG, H16>, grid, dim3(NT), a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
-// (sinks, recent fp16 rows and pages are not combined: the library rejects such caches)
+// (sinks, recent fp16 rows and pages are not combined: the library rejects such caches;
+// fp16 scales take the contiguous and the paged instances, a cache with sinks the
+// split-K kernel)
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   if (a.pages.size) return a.sinks || a.recent ? hipErrorInvalidValue : launch_gs<G, false, false, true>(a, s);
   if (a.recent) return a.sinks ? hipErrorInvalidValue : launch_gs<G, false, true>(a, s);
   return a.sinks ? launch_gs<G, true, false>(a, s) : launch_gs<G, false, false>(a, s);
+}
+template <int G>
+hipError_t launch_g16(const DecodeArgs& a, hipStream_t s) {
+  if (a.sinks || a.recent) return hipErrorInvalidValue;
+  return a.pages.size ? launch_gs<G, false, false, true, true>(a, s)
+                      : launch_gs<G, false, false, false, true>(a, s);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1921,7 +1976,18 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
   constexpr int QWG = PF_WAVES * NCB * QPC;    // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t ring[NB * L::BYTES];
 
-  const int qb0 = blockIdx.x * QWG, kvh = blockIdx.y, b = blockIdx.z;
+  // Workgroups reach the 8 XCDs in turn, in dispatch order (x fastest).  They are
+  // renumbered so that each XCD runs whole (sequence, KV head) units, all query blocks of
+  // a unit side by side: those walk the same K/V tiles at about the same pace, so a tile
+  // comes from HBM into that XCD's L2 once rather than once per XCD.  (Any order is
+  // correct; this one only saves traffic.)
+  const int nqb = gridDim.x;
+  const int nwg = nqb * gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + nqb * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int xcd = lin & 7, per = nwg >> 3, rem = nwg & 7;
+  const int vid = xcd * per + min(xcd, rem) + (lin >> 3);
+  const int unit = vid / nqb;
+  const int qb0 = (vid - unit * nqb) * QWG, kvh = unit % a.Hkv, b = unit / a.Hkv;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, j = lane >> 4;
@@ -2190,8 +2256,14 @@ int32_t plan_splits_mfma(int32_t units, int32_t span) {
   return n < 1 ? 1 : n;
 }
 
+bool mfma_int4h_eligible(const kvq_cache_desc* d, int32_t q_group) {
+  return d->format == KVQ_INT4_G16 && d->sinks == 0 && d->recent == 0 &&
+         mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group);
+}
+
 bool fused_append_supported(const kvq_cache_desc* d, int32_t q_group) {
-  // the split-K kernel codes the row for the codecs and INT4 with fp16 scales
+  // the matrix-core kernel codes the row for INT4 (either scale type); the split-K
+  // kernel for the codecs and for INT4 with fp16 scales beside sinks or other shapes
   if (is_codec(d->format) || d->format == KVQ_INT4_G16) return true;
   return d->format == KVQ_INT4_G &&
          mfma_int4_eligible(d->head_dim, d->group_k, d->group_v, d->capacity, q_group);
@@ -2203,6 +2275,16 @@ hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStre
     case 2: return launch_g<2>(a, s);
     case 4: return launch_g<4>(a, s);
     case 8: return launch_g<8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_int4h_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
+  switch (q_group) {
+    case 1: return launch_g16<1>(a, s);
+    case 2: return launch_g16<2>(a, s);
+    case 4: return launch_g16<4>(a, s);
+    case 8: return launch_g16<8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -122,7 +122,10 @@ bool mfma_int4_eligible(int32_t head_dim, int32_t group_k, int32_t group_v, int3
                         int32_t q_group);
 int32_t plan_splits_mfma(int32_t units, int32_t span);
 bool fused_append_supported(const kvq_cache_desc* d, int32_t q_group);
+// INT4 with fp16 scales on the matrix-core kernel: its shapes, without sinks
+bool mfma_int4h_eligible(const kvq_cache_desc* d, int32_t q_group);
 hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
+hipError_t launch_decode_int4h_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
 // Chunked-prefill (multi-query causal) attention over the INT4 cache on the matrix cores
 // (head_dim 128, V group 128, K group 64 or 128): a.q [B, Hq, nq, D], a.out the same in
 // fp32; no workspace.

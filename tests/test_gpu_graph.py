@@ -3,8 +3,8 @@
 A captured ``kvq_append_decode_attn`` call replays to the eager result, replay after
 replay, with eager library work and synchronizations in between, and leaves the split
 arrival counters at zero each time.  Paths: the INT4 matrix-core kernel (in-kernel
-merge, append fused in the prologue) and its instances for attention sinks and for
-recent fp16 rows, the codec's split-K kernel with the in-kernel merge, and the codec's
+merge, append fused in the prologue) and its instances for attention sinks, for
+recent fp16 rows and for fp16 scales, the codec's split-K kernel with the in-kernel merge, and the codec's
 split-K kernel followed by the merge kernel.  The eager result
 is itself checked against the oracle ("长上下文内存大瘦身" engine three for the codec;
 lpnh.cn/news/2042373 section 2.1 and the plain softmax definition for INT4).
@@ -28,6 +28,7 @@ CASES = [
     ("codec", 256, 2, 40, 0, 0, 0),   # split-K + merge kernel
     ("int4", 128, 4, 0, 4, 0, 256),   # matrix-core sink instance, window 256 + 4 sinks
     ("int4", 128, 4, 0, 0, 64, 0),    # matrix-core recent-row instance, 64 fp16 rows
+    ("int4h", 128, 4, 0, 0, 0, 0),    # matrix-core fp16-scale instance
 ]
 
 
@@ -61,8 +62,9 @@ def test_graph_replay_matches_eager(fmt, D, G, ns, S, R, W):
         ref = attention.decode_attention(np16(q), kh, vh, lens, W)
         assert_attn_close(eager.cpu().numpy(), ref, f"{fmt} eager")
     else:
-        qk, sk = quant.quantize_int4(np16(k), 64)
-        qv, sv = quant.quantize_int4(np16(v), 128)
+        quantize = quant.quantize_int4_fp16_scale if fmt == "int4h" else quant.quantize_int4
+        qk, sk = quantize(np16(k), 64)
+        qv, sv = quantize(np16(v), 128)
         kh, vh = quant.dequantize_int4_exact(qk, sk, 64), quant.dequantize_int4_exact(qv, sv, 128)
         if R:
             kh = attention.recent_fp16_rows(kh, np16(k), lens, R)

@@ -193,7 +193,9 @@ DECODE_CASES = [
     ("int8", 128, 4, 64, 16, [3000, 1234], 0, 0, False),    # INT8 tiles
     ("int8", 128, 2, 64, 64, [2500, 2500], 900, 4, False),
     ("codec", 256, 2, 64, 32, [2000, 600], 512, 0, True),   # codec split-K, fused
-    ("int4h", 128, 4, 64, 16, [1800, 900], 0, 0, True),     # fp16 scales, split-K, fused
+    ("int4h", 128, 4, 64, 16, [1800, 900], 0, 0, True),     # fp16 scales, matrix-core, fused
+    ("int4h", 128, 2, 64, 32, [2000, 1300], 600, 3, False),  # fp16 scales, matrix-core, window
+    ("int4h", 64, 4, 32, 16, [900, 400], 0, 0, True),       # fp16 scales, split-K, fused
     ("int4", 64, 4, 64, 16, [1200, 300], 0, 40, False),     # head_dim 64 split-K + merge kernel
 ]
 
