@@ -370,8 +370,10 @@ def calibrate_copy(args):
 
 READ_BYTES = 4 << 30
 # launch shapes every line tries (workgroups of 256 lanes, loads in flight per lane,
-# non-temporal); the best median of them is the line's attainable read rate
-READ_CONFIGS = [(2048, 8, 0), (4096, 8, 0), (8192, 4, 0), (4096, 8, 1), (16384, 4, 0)]
+# non-temporal): the five fastest of the 48-shape sweep of --calibrate-read (1K-32K
+# workgroups, 2-16 loads in flight, plain and non-temporal; all five non-temporal).
+# The best median of them is the line's attainable read rate.
+READ_CONFIGS = [(32768, 16, 1), (32768, 8, 1), (16384, 16, 1), (1024, 2, 1), (16384, 8, 1)]
 
 
 def _bench_lib():
