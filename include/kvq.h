@@ -53,9 +53,9 @@
  *   KVQ_WHT_LM4   codes  [B, Hkv, C, D/2] uint8, unsigned 4-bit Lloyd-Max indices
  *                        (0..15) of the rotated row, same nibble order as INT4;
  *                 scales [B, Hkv, C] fp32 (the row's RMS).
- *   KVQ_WHT_LM3   codes  [B, Hkv, C, 3, D/8] uint8: the 3-bit indices (0..7) as three
- *                        bit-planes; byte c of plane p holds bit p of the indices
- *                        8c .. 8c+7 (index 8c+j in bit j);
+ *   KVQ_WHT_LM3   codes  [B, Hkv, C, 3*D/8] uint8: the 3-bit indices (0..7) packed
+ *                        back to back, index i in bits 3i .. 3i+2 of the row read as a
+ *                        little-endian bit string;
  *                 scales [B, Hkv, C] fp32, as for KVQ_WHT_LM4.
  *   Position p of a sequence lives in slot p when p < S (S = sinks, the first
  *   positions kept for attention sinks, [KV-opt] §3.2), else in slot

@@ -11,8 +11,9 @@
 //
 // Mapping: as for INT4, a row of D elements spans D/8 lanes of 8 elements; three
 // butterfly stages run inside a lane, log2(D/8) across lanes with xor shuffles.  4-bit
-// rows are D/2 bytes of nibbles; 3-bit rows three bit-planes of D/8 bytes (see
-// store_planes).  The 3-bit coder is the 4-bit one with thresholds 7 .. 14 set to +inf.
+// rows are D/2 bytes of nibbles; 3-bit rows the indices packed back to back in 3D/8
+// bytes (see store_packed3).  The 3-bit coder is the 4-bit one with thresholds 7 .. 14
+// set to +inf.
 #include <cmath>
 
 #include "kvq_device.h"
@@ -46,7 +47,7 @@ __global__ void __launch_bounds__(256) codec_encode_kernel(QuantArgs a) {
     const size_t drow = a.pages.size ? paged_row(a.pages, a.Hkv, b, (int)(bh - b * a.Hkv), p)
                                      : (size_t)bh * a.map.cap + cache_slot(p, a.map.cap, a.map.sinks);
     if (BITS == 4) static_cast<uint32_t*>(codes)[drow * LPR + c] = w;
-    else store_planes<LPR>(static_cast<uint8_t*>(codes) + drow * 3 * LPR, c, w);
+    else store_packed3<LPR>(static_cast<uint8_t*>(codes) + drow * 3 * LPR, c, w);
     if (c == 0) scales[drow] = s;
   }
 }
@@ -71,7 +72,7 @@ __global__ void __launch_bounds__(256) codec_dequant_kernel(DequantArgs a) {
     const size_t drow = a.pages.size ? paged_row(a.pages, a.Hkv, b, (int)(bh - b * a.Hkv), a.start + t)
                                      : (size_t)bh * a.cap + cache_slot(a.start + t, a.cap, a.sinks);
     const uint32_t w = BITS == 4 ? static_cast<const uint32_t*>(a.codes)[drow * LPR + c]
-                                 : load_planes<LPR>(static_cast<const uint8_t*>(a.codes) + drow * 3 * LPR, c);
+                                 : load_packed3<LPR>(static_cast<const uint8_t*>(a.codes) + drow * 3 * LPR, c);
     const float s = a.scales[drow];
     float v[8];
 #pragma unroll

@@ -64,9 +64,10 @@ __device__ __forceinline__ RawRow load_raw(const DecodeArgs& a, size_t row, int 
     r.k[0] = kw.x; r.k[1] = kw.y; r.v[0] = vw.x; r.v[1] = vw.y;
     r.sk = a.k_scales[row];
     r.sv = a.v_scales[row];
-  } else if (FMT == KVQ_WHT_LM3) {   // three plane bytes per lane, as a nibble word
-    r.k[0] = load_planes<LPR>(static_cast<const uint8_t*>(a.k_codes) + row * 3 * LPR, c);
-    r.v[0] = load_planes<LPR>(static_cast<const uint8_t*>(a.v_codes) + row * 3 * LPR, c);
+  } else if (FMT == KVQ_WHT_LM3) {   // one aligned dword of the packed row per lane
+    // (its 24 bits are assembled where the row is used: packed3_bits)
+    r.k[0] = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.k_codes) + row * 3 * LPR)[packed3_dword(c)];
+    r.v[0] = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.v_codes) + row * 3 * LPR)[packed3_dword(c)];
     r.k[1] = r.v[1] = 0u;
     r.sk = a.k_scales[row];
     r.sv = a.v_scales[row];
@@ -101,6 +102,13 @@ __device__ __forceinline__ void codes_f32(const uint32_t w[2], const float2* lv2
     for (int j = 0; j < 4; ++j) {
       x[j] = (float)(int8_t)((w[0] >> (8 * j)) & 255u);
       x[j + 4] = (float)(int8_t)((w[1] >> (8 * j)) & 255u);
+    }
+  } else if (FMT == KVQ_WHT_LM3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // w[0]: the lane's 24 bits; one lookup per index pair
+      const float2 p = lv2[(w[0] >> (6 * i)) & 63u];
+      x[2 * i] = p.x;
+      x[2 * i + 1] = p.y;
     }
   } else {
 #pragma unroll
@@ -247,7 +255,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
       const size_t row = a.pages.size ? paged_row(a.pages, a.Hkv, b, kvh, len - 1)
                                       : bh * a.cap + cache_slot(len - 1, a.cap, a.sinks);
       void* codes = const_cast<void*>(grp ? a.v_codes : a.k_codes);
-      if (FMT == KVQ_WHT_LM3) store_planes<LPR>(static_cast<uint8_t*>(codes) + row * 3 * LPR, c, w);
+      if (FMT == KVQ_WHT_LM3) store_packed3<LPR>(static_cast<uint8_t*>(codes) + row * 3 * LPR, c, w);
       else static_cast<uint32_t*>(codes)[row * LPR + c] = w;
       if (FMT == KVQ_INT4_G16) {   // the group's fp16 scale, from its first lane
         const int g = grp ? a.gv : a.gk;
@@ -258,7 +266,9 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
         const_cast<float*>(grp ? a.v_scales : a.k_scales)[row] = sc;
       }
     }
-    // group 0 takes the V row's word and scale from the lane LPR above it
+    // group 0 takes the V row's word and scale from the lane LPR above it (3 bits: the
+    // word as the lane's 24 packed bits, the form the row loop looks levels up from)
+    if (FMT == KVQ_WHT_LM3) w = packed3_of_nibbles(w);
     const int src = ((tid + LPR) & 63) << 2;
     nr.k[0] = w;
     nr.sk = sc;
@@ -267,8 +277,10 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     nr.k[1] = nr.v[1] = 0u;
   }
 
-  if (CODEC) {   // the codebook levels (the barrier comes after the loads above)
-    lv2[tid] = make_float2(a.levels[tid & 15], a.levels[tid >> 4]);
+  if (CODEC) {   // the codebook levels (the barrier comes after the loads above): the
+    // two levels of a byte (4 bits) or of a 6-bit index pair (3 bits)
+    lv2[tid] = FMT == KVQ_WHT_LM3 ? make_float2(a.levels[tid & 7], a.levels[(tid >> 3) & 7])
+                                  : make_float2(a.levels[tid & 15], a.levels[tid >> 4]);
     __syncthreads();
   }
 
@@ -288,12 +300,22 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   // (last step only) are loaded clamped to pe - 1 and scored -inf; they are the same
   // rows for the LPR lanes of a row, and every lane of a row takes part in the row's
   // lane sums.
-  auto do_step = [&](const RawRow (&raw)[U], int nvalid) {
+  // (3 bits: a cached row's words are the lane's aligned dwords of the packed row, whose
+  // 24 bits packed3_bits assembles here, where the row is used, so that the row loads
+  // stay in flight until then; the fused append's row arrives assembled)
+  const int quad = c & 3;
+  auto bits_of = [&](const uint32_t (&w)[2], bool assembled, uint32_t (&o)[2]) {
+    o[0] = FMT == KVQ_WHT_LM3 && !assembled ? packed3_bits(w[0], quad) : w[0];
+    o[1] = w[1];
+  };
+  auto do_step = [&](const RawRow (&raw)[U], int nvalid, bool assembled = false) {
     float z[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kc[8];
-      codes_f32<FMT>(raw[u].k, lv2, kc);
+      uint32_t kw[2];
+      bits_of(raw[u].k, assembled, kw);
+      codes_f32<FMT>(kw, lv2, kc);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.0f;
@@ -318,7 +340,9 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float vc[8];
-      codes_f32<FMT>(raw[u].v, lv2, vc);
+      uint32_t vw[2];
+      bits_of(raw[u].v, assembled, vw);
+      codes_f32<FMT>(vw, lv2, vc);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float p = fast_exp2(z[u][h] - m[h]);
@@ -348,7 +372,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   }
   if (app_grp) {   // the new row: one more row of this group's softmax
     const RawRow raw[U] = {nr, nr, nr, nr};
-    do_step(raw, 1);
+    do_step(raw, 1, true);
   }
 
   if (c == 0) {

@@ -176,35 +176,46 @@ __device__ __forceinline__ void codec_encode_row(float x[8], int c, const Thresh
   for (int j = 0; j < 8; ++j) w |= (uint32_t)count_below15(thr, x[j] * inv) << (4 * j);
 }
 
-// 3-bit codec rows are three bit-planes of D/8 bytes: byte c of plane p holds bit p of
-// the indices 8c .. 8c + 7 (index 8c + j in bit j).  A lane owning those 8 indices works
-// on them as the 4-bit codec's nibble word (index j in nibble j, values 0..7), so the
-// level lookups are shared; these convert between the word and its three plane bytes.
-__device__ __forceinline__ uint32_t spread_bits8(uint32_t x) {   // bit j -> bit 4j
-  x &= 0xFFu;
-  x = (x | (x << 12)) & 0x000F000Fu;
-  x = (x | (x << 6)) & 0x03030303u;
-  return (x | (x << 3)) & 0x11111111u;
+// 3-bit codec rows: the D indices packed back to back, index i in bits 3i .. 3i + 2 of
+// the row read as a little-endian bit string (3D/8 bytes).  Lane c owns indices
+// 8c .. 8c + 7, i.e. the 24 bits of bytes 3c .. 3c + 2.  The encoder, the dequantizer
+// and the fused append convert between those 24 bits and the 4-bit codec's nibble word
+// (index j in nibble j, values 0..7), so the coder and the level lookups are shared.
+__device__ __forceinline__ uint32_t packed3_of_nibbles(uint32_t w) {   // nibble j -> bits 3j
+  w &= 0x77777777u;
+  w = (w & 0x07070707u) | ((w >> 1) & 0x38383838u);   // byte k: indices 2k, 2k+1 in 6 bits
+  w = (w & 0x003F003Fu) | ((w >> 2) & 0x0FC00FC0u);   // half h: indices 4h .. 4h+3 in 12 bits
+  return (w & 0x00000FFFu) | ((w >> 4) & 0x00FFF000u);
 }
-__device__ __forceinline__ uint32_t gather_bits8(uint32_t x) {   // bit 4j -> bit j
-  x &= 0x11111111u;
-  x = (x | (x >> 3)) & 0x03030303u;
-  x = (x | (x >> 6)) & 0x000F000Fu;
-  return (x | (x >> 12)) & 0xFFu;
+__device__ __forceinline__ uint32_t nibbles_of_packed3(uint32_t t) {   // bits 3j -> nibble j
+  t = (t & 0x00000FFFu) | ((t & 0x00FFF000u) << 4);
+  t = (t & 0x003F003Fu) | ((t & 0x0FC00FC0u) << 2);
+  return (t & 0x07070707u) | ((t & 0x38383838u) << 1);
 }
-__device__ __forceinline__ uint32_t planes_to_nibbles(uint32_t b0, uint32_t b1, uint32_t b2) {
-  return spread_bits8(b0) | (spread_bits8(b1) << 1) | (spread_bits8(b2) << 2);
-}
-// lane c of a row: its 8 indices (nibble word w) into the row's planes at `row`
+// lane c's 24 bits by byte accesses (encode, dequant, append: off the decode loop)
 template <int LPR>
-__device__ __forceinline__ void store_planes(uint8_t* row, int c, uint32_t w) {
-  row[c] = (uint8_t)gather_bits8(w);
-  row[LPR + c] = (uint8_t)gather_bits8(w >> 1);
-  row[2 * LPR + c] = (uint8_t)gather_bits8(w >> 2);
+__device__ __forceinline__ void store_packed3(uint8_t* row, int c, uint32_t w) {
+  const uint32_t t = packed3_of_nibbles(w);
+  row[3 * c] = (uint8_t)t;
+  row[3 * c + 1] = (uint8_t)(t >> 8);
+  row[3 * c + 2] = (uint8_t)(t >> 16);
 }
 template <int LPR>
-__device__ __forceinline__ uint32_t load_planes(const uint8_t* row, int c) {
-  return planes_to_nibbles(row[c], row[LPR + c], row[2 * LPR + c]);
+__device__ __forceinline__ uint32_t load_packed3(const uint8_t* row, int c) {
+  return nibbles_of_packed3((uint32_t)row[3 * c] | ((uint32_t)row[3 * c + 1] << 8) |
+                            ((uint32_t)row[3 * c + 2] << 16));
+}
+// The decode loop fetches a row with one aligned dword per lane: lane 4m + i loads
+// dword 3m + min(i, 2) of the row (its quad's 12 bytes; lanes 4m + 2 and 4m + 3 load the
+// same dword), and packed3_bits later assembles its 24 bits from its own dword and the
+// one of lane 4m + i - 1 (a quad DPP): i = 0: bytes 0-2 of its own; 1: the last byte of
+// lane 4m's and the first two of its own; 2: the last two of lane 4m + 1's and the first
+// of its own; 3: bytes 1-3 of its own.  Every lane of the quad must be active.
+__device__ __forceinline__ int packed3_dword(int c) { return 3 * (c >> 2) + min(c & 3, 2); }
+__device__ __forceinline__ uint32_t packed3_bits(uint32_t own, int i) {
+  const uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0x90, 0xF, 0xF, false);   // quad_perm [0, 0, 1, 2]
+  const uint32_t lo = (i == 1 || i == 2) ? prev : own;
+  return __builtin_amdgcn_alignbyte(own, lo, (uint32_t)((4 - i) & 3));
 }
 
 // Sum over aligned groups of LANES (2, 4, 8, 16 or 32) lanes, left in every lane of the

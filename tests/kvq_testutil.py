@@ -78,30 +78,24 @@ def append_decode(desc, dc, k_new, v_new, q, q_heads, lens, window=0, scale=0.0,
 
 # ----------------------------------------------------------------------------- codec rows
 
-def pack_planes(idx):
-    """3-bit indices [..., D] (0..7) -> the library's rows [..., 3 * D / 8] uint8: byte c of
-    plane p holds bit p of indices 8c .. 8c + 7 (index 8c + j in bit j)."""
+def pack3(idx):
+    """3-bit indices [..., D] (0..7) -> the library's rows [..., 3 * D / 8] uint8: index i in
+    bits 3i .. 3i + 2 of the row read as a little-endian bit string."""
     idx = np.asarray(idx, dtype=np.uint8)
-    D = idx.shape[-1]
-    bits = idx.reshape(*idx.shape[:-1], D // 8, 8)
-    planes = [np.packbits((bits >> p) & 1, axis=-1, bitorder="little")[..., 0] for p in range(3)]
-    return np.concatenate(planes, axis=-1)
+    bits = ((idx[..., None] >> np.arange(3, dtype=np.uint8)) & 1).reshape(*idx.shape[:-1], -1)
+    return np.packbits(bits, axis=-1, bitorder="little")
 
 
-def unpack_planes(rows):
+def unpack3(rows):
     rows = np.asarray(rows, dtype=np.uint8)
-    n = rows.shape[-1] // 3
-    out = 0
-    for p in range(3):
-        bits = np.unpackbits(rows[..., p * n:(p + 1) * n, None], axis=-1, bitorder="little")
-        out = out + (bits.astype(np.uint8) << p)
-    return out.reshape(*rows.shape[:-1], 8 * n)
+    bits = np.unpackbits(rows, axis=-1, bitorder="little").reshape(*rows.shape[:-1], -1, 3)
+    return (bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2)).astype(np.uint8)
 
 
 def codec_indices(codes, fmt):
     """Stored codec rows -> indices [..., D]."""
     if fmt == "codec3":
-        return unpack_planes(codes)
+        return unpack3(codes)
     return quant.unpack_nibbles(codes, signed=False)
 
 

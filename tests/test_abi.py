@@ -57,7 +57,7 @@ def test_size_queries_match_closed_forms():
             elif fmt == "codec":
                 assert kvq.kvq_codes_bytes(d, 1) == B * H * C * D // 2
                 assert kvq.kvq_scales_bytes(d, 0) == B * H * C * 4
-            else:                                   # three bit-planes of D/8 bytes
+            else:                                   # 3-bit indices packed: 3D/8 bytes
                 assert kvq.kvq_codes_bytes(d, 1) == B * H * C * 3 * D // 8
                 assert kvq.kvq_scales_bytes(d, 0) == B * H * C * 4
             assert kvq.kvq_codes_bytes(d, 2) == 0

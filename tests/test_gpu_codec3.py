@@ -1,8 +1,8 @@
 """GPU parity of the WHT + Lloyd-Max codec at 3 bits ("长上下文内存大瘦身：LARQL 四大 KV 缓存
 引擎原理与横向对比", pwwt.cn/news/5725003, engine three: 3 or 4 bits) against the oracle.
 
-Rows hold the 3-bit indices as three bit-planes of D/8 bytes (byte c of plane p: bit p
-of indices 8c .. 8c + 7).  Bar as for the 4-bit codec: index mismatches only where y/s
+Rows hold the 3-bit indices packed back to back (index i in bits 3i .. 3i + 2 of the row
+as a little-endian bit string, 3D/8 bytes).  Bar as for the 4-bit codec: index mismatches only where y/s
 lies within 1e-5 of a decision threshold; scales and decoded values within 1e-5
 relative; attention over the same codes within max abs 2e-3 and relative L2 1e-4.
 """
@@ -14,22 +14,24 @@ import int4_quantized_kv_amd as kvq
 import synth
 from oracle import attention, codec
 from tests.kvq_testutil import (append_decode, assert_attn_close, cache_arrays, codec_hat_from_device,
-                                decode, np16, pack_planes, unpack_planes)
+                                decode, np16, pack3, unpack3)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def test_plane_helpers_round_trip():
+def test_packed3_helpers_round_trip():
     rng = np.random.default_rng(3)
     idx = rng.integers(0, 8, size=(3, 5, 64))
-    rows = pack_planes(idx)
+    rows = pack3(idx)
     assert rows.shape == (3, 5, 24)
-    assert np.array_equal(unpack_planes(rows), idx)
+    assert np.array_equal(unpack3(rows), idx)
     one = np.zeros(16, dtype=np.uint8)
-    one[9] = 5                         # index 8 + 1 of chunk 1: bits 0 and 2
-    r = pack_planes(one)
-    assert list(r) == [0, 2, 0, 0, 0, 2]
+    one[0] = 7                         # bits 0, 1, 2
+    one[9] = 5                         # 0b101 at bits 27 .. 29: bits 27 and 29 (byte 3: 8 + 32)
+    one[15] = 6                        # 0b110 at bits 45 .. 47: bits 46 and 47 (byte 5: 64 + 128)
+    r = pack3(one)
+    assert list(r) == [7, 0, 0, 40, 0, 192]
 
 
 def _encode(k, v, cap=None):
@@ -42,7 +44,7 @@ def _encode(k, v, cap=None):
 
 def _check_codes(got_codes, got_scales, x16):
     idx, s, u = codec.encode(x16, bits=3)
-    g_idx = unpack_planes(got_codes)
+    g_idx = unpack3(got_codes)
     assert np.allclose(got_scales[..., 0], s, rtol=1e-5, atol=0)
     mism = g_idx != idx
     if mism.any():
@@ -73,7 +75,7 @@ def test_dequant_3bit():
     out = torch.empty((2, 4, 100, D), dtype=torch.float32, device=DEV)
     kvq.kvq_dequant(desc, dc.c, 0, 0, 100, out)
     torch.cuda.synchronize()
-    ref = codec.decode(unpack_planes(kc), ks[..., 0], bits=3)
+    ref = codec.decode(unpack3(kc), ks[..., 0], bits=3)
     got = out.cpu().numpy()
     assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
     # coarser than the 4-bit codec's ~0.9954, as the 3-bit distortion is larger
@@ -82,8 +84,8 @@ def test_dequant_3bit():
 
 
 def _inject(dc, kidx, ks, vidx, vs):
-    dc.k_codes.copy_(torch.from_numpy(pack_planes(kidx).reshape(-1)).to(DEV))
-    dc.v_codes.copy_(torch.from_numpy(pack_planes(vidx).reshape(-1)).to(DEV))
+    dc.k_codes.copy_(torch.from_numpy(pack3(kidx).reshape(-1)).to(DEV))
+    dc.v_codes.copy_(torch.from_numpy(pack3(vidx).reshape(-1)).to(DEV))
     dc.k_scales.copy_(torch.from_numpy(np.ascontiguousarray(ks).reshape(-1)).to(DEV))
     dc.v_scales.copy_(torch.from_numpy(np.ascontiguousarray(vs).reshape(-1)).to(DEV))
 
@@ -113,7 +115,7 @@ def test_attention_over_oracle_codes_3bit(window, L, cap, D, G, ns):
 
 @pytest.mark.parametrize("D,G,window", [(256, 2, 0), (128, 4, 512)])
 def test_fused_append_decode_3bit(D, G, window):
-    """The split-K kernel codes the new row (as the encode kernel does), stores its planes
+    """The split-K kernel codes the new row (as the encode kernel does), stores its packed bits
     and attends it; against the oracle and against the unfused pair."""
     B, H, L = 2, 2, 1500
     cap = window or L
