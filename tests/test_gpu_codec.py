@@ -12,7 +12,8 @@ import torch
 import int4_quantized_kv_amd as kvq
 import synth
 from oracle import attention, codec, quant
-from tests.kvq_testutil import assert_attn_close, cache_arrays, codec_hat_from_device, decode, np16
+from tests.kvq_testutil import (append_decode, assert_attn_close, cache_arrays, codec_hat_from_device,
+                                decode, np16)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -99,28 +100,47 @@ def test_attention_over_oracle_codes(window, L, cap):
     assert_attn_close(out.cpu().numpy(), ref, f"codec w={window}")
 
 
-def test_gemma_shape_end_to_end_window_and_global():
-    """Gemma-3-4B-shaped codec decode step (batch 4, 4 KV heads x 256, 8 query heads):
-    one sliding-window layer (ring of 1024 rows) and one global layer, each prefilled to
-    4096 positions then appended at position 4096, encoded and attended on the GPU."""
-    w = synth.WORKLOADS[4]
+@pytest.mark.parametrize("fmt,wid", [("codec", 4), ("codec3", 8)])
+def test_gemma_shape_end_to_end_window_and_global(fmt, wid):
+    """The Gemma-3-4B-shaped codec decode step as the benchmark runs it (batch 4, 4 KV
+    heads x 256, 8 query heads; the library's split plan): one sliding-window layer (ring
+    of 1024 rows) and one global layer, each prefilled to 4096 positions, then the one-launch
+    kvq_append_decode_attn of position 4096 (the kernel codes the new row), eager and
+    replayed from a HIP graph.  The new row's bytes equal those kvq_append stores."""
+    w = synth.WORKLOADS[wid]
     for layer in (0, w.layers - 1):
         W = w.layer_window(layer)
         k, v, q, kn, vn = synth.layer_inputs(w, layer, DEV)
         L = w.context + 1
         cap = W if W else L
-        desc = kvq.make_desc("codec", w.batch, w.kv_heads, w.head_dim, cap)
-        dc = kvq.DeviceCache(desc, DEV)
+        desc = kvq.make_desc(fmt, w.batch, w.kv_heads, w.head_dim, cap)
+        dc, du = kvq.DeviceCache(desc, DEV), kvq.DeviceCache(desc, DEV)
         for start in range(0, w.context, cap):
             n = min(cap, w.context - start)
-            kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, start:start + n].contiguous(),
-                                     v[:, :, start:start + n].contiguous(), start, n)
-        kvq.kvq_append(desc, dc.c, kn, vn, [w.context] * w.batch)
-        out = decode(desc, dc, q, w.q_heads, [L] * w.batch, W).cpu().numpy()
+            for c_ in (dc, du):
+                kvq.kvq_quantize_prefill(desc, c_.c, k[:, :, start:start + n].contiguous(),
+                                         v[:, :, start:start + n].contiguous(), start, n)
+        ws = kvq.decode_workspace(desc, w.q_heads, L, W, device=DEV)
+        out = append_decode(desc, dc, kn, vn, q, w.q_heads, [L] * w.batch, W, ws=ws).cpu().numpy()
+        kvq.kvq_append(desc, du.c, kn, vn, [w.context] * w.batch)
+        torch.cuda.synchronize()
+        for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
+            assert torch.equal(getattr(dc, name), getattr(du, name)), name
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        replayed = torch.full((w.batch, w.q_heads, w.head_dim), float("nan"), device=DEV)
+        with torch.cuda.graph(g, stream=st):   # (re-appends the same row: same bytes)
+            kvq.kvq_append_decode_attn(desc, dc.c, kn, vn, q, w.q_heads, [L] * w.batch, W, 0.0, 0,
+                                       replayed, ws)
+        g.replay()
+        g.replay()
+        torch.cuda.synchronize()
         kall = np.concatenate([np16(k), np16(kn)[:, :, None]], axis=2)
         vall = np.concatenate([np16(v), np16(vn)[:, :, None]], axis=2)
         # every attended row read back from the cache and held to the codec rule, then
         # the oracle's attention over those rows
-        kh, vh, _ = codec_hat_from_device(dc, "codec", kall, vall, [L] * w.batch, W)
+        kh, vh, _ = codec_hat_from_device(dc, fmt, kall, vall, [L] * w.batch, W)
         ref = attention.decode_attention(np16(q), kh, vh, [L] * w.batch, W)
-        assert_attn_close(out, ref, f"gemma layer {layer}")
+        assert_attn_close(out, ref, f"gemma {fmt} layer {layer}")
+        assert_attn_close(replayed.cpu().numpy(), ref, f"gemma {fmt} layer {layer}, graph")

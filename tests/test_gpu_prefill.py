@@ -93,3 +93,48 @@ def test_prefill_then_decode_agree():
     kvq.kvq_decode_attn(desc, dc.c, q, Hkv * G, lens, 0, 0.0, 0, dec, ws)
     torch.cuda.synchronize()
     assert_attn_close(out[:, :, 0].cpu().numpy(), dec.cpu().numpy().astype(np.float64), "prefill vs decode")
+
+
+def test_benched_chunk_full_size_sampled():
+    """The chunk the benchmark times, at full size: the Llama-3-8B-shaped layer (8
+    sequences, 8 KV heads, 32 query heads) prefilled to 7680 positions, the 512-token chunk
+    quantized into positions 7680 .. 8191, then kvq_prefill_attn of its 512 queries, eager
+    and replayed from a HIP graph.  The oracle checks sampled outputs one by one (a query
+    of the chunk is the decode query at its own length): first, middle and last queries of
+    corner (sequence, head) pairs."""
+    w = synth.WORKLOADS[2]
+    B, Hq, Hkv, D, L, NQ = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.context, 512
+    P0 = L - NQ
+    k, v, _, _, _ = synth.layer_inputs(w, 1, DEV)
+    q = synth.query((B, Hq, NQ, D), synth.seed_of(w.wid, 1, 6), DEV)
+    desc = kvq.make_desc("int4", B, Hkv, D, L, w.group_k, w.group_v)
+    dc = kvq.DeviceCache(desc, DEV)
+    kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, :P0].contiguous(), v[:, :, :P0].contiguous(), 0, P0)
+    kvq.kvq_quantize_prefill(desc, dc.c, k[:, :, P0:].contiguous(), v[:, :, P0:].contiguous(), P0, NQ)
+    out = torch.full((B, Hq, NQ, D), float("nan"), dtype=torch.float32, device=DEV)
+    kvq.kvq_prefill_attn(desc, dc.c, q, Hq, NQ, [L] * B, 0, 0.0, out)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    replayed = torch.full_like(out, float("nan"))
+    with torch.cuda.graph(g, stream=s):
+        kvq.kvq_prefill_attn(desc, dc.c, q, Hq, NQ, [L] * B, 0, 0.0, replayed)
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.equal(out, replayed)
+    got = out.cpu().numpy()
+    q16 = np16(q)
+    for b in (0, B - 1):
+        kh_b, vh_b = {}, {}
+        for h in (0, 5, Hq - 1):
+            kvh = h // (Hq // Hkv)
+            if kvh not in kh_b:
+                qk, sk = quant.quantize_int4(np16(k[b:b + 1, kvh:kvh + 1]), w.group_k)
+                qv, sv = quant.quantize_int4(np16(v[b:b + 1, kvh:kvh + 1]), w.group_v)
+                kh_b[kvh] = quant.dequantize_int4_exact(qk, sk, w.group_k)
+                vh_b[kvh] = quant.dequantize_int4_exact(qv, sv, w.group_v)
+            for i in (0, 1, 255, NQ - 1):
+                ref = attention.prefill_attention(q16[b:b + 1, h:h + 1, i:i + 1], kh_b[kvh], vh_b[kvh],
+                                                  [P0 + i + 1])
+                assert_attn_close(got[b:b + 1, h:h + 1, i:i + 1], ref, f"chunk b={b} h={h} query {i}")
