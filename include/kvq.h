@@ -304,9 +304,9 @@ int32_t kvq_append_decode_attn_noalloc(const kvq_cache_desc* desc, const kvq_cac
  *   fp32.  lens: host, [B], n_query <= len_b; len_b <= C, or (a window ring, contiguous
  *   layout) window > 0 and window + n_query - 1 <= C - S.  softmax_scale as in
  *   kvq_decode_attn.
- * INT4 format with head_dim 128, V group 128 and K group 64 or 128, q_heads / Hkv in
- * {1, 2, 4, 8}, no sinks or recent rows (KVQ_ERR_UNSUPPORTED otherwise); contiguous or
- * paged.  Runs on the matrix cores; needs no workspace. */
+ * INT4 formats (fp32 or fp16 scales) with head_dim 128, V group 128 and K group 64 or
+ * 128, q_heads / Hkv in {1, 2, 4, 8}, no sinks or recent rows (KVQ_ERR_UNSUPPORTED
+ * otherwise); contiguous or paged.  Runs on the matrix cores; needs no workspace. */
 int32_t kvq_prefill_attn(const kvq_cache_desc* desc, const kvq_cache* cache, const void* q_f16,
                          int32_t q_heads, int32_t n_query, const int32_t* lens, int32_t window,
                          float softmax_scale, float* out, kvq_stream stream);

@@ -442,7 +442,8 @@ int32_t kvq_prefill_attn(const kvq_cache_desc* desc, const kvq_cache* cache, con
   if (q_heads % desc->kv_heads) return KVQ_ERR_ARG;
   const int32_t G = q_heads / desc->kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
-  if (desc->format != KVQ_INT4_G || desc->head_dim != 128 || desc->group_v != 128 ||
+  if ((desc->format != KVQ_INT4_G && desc->format != KVQ_INT4_G16) || desc->head_dim != 128 ||
+      desc->group_v != 128 ||
       (desc->group_k != 64 && desc->group_k != 128) || desc->sinks > 0 || desc->recent > 0 ||
       desc->capacity < 32)
     return KVQ_ERR_UNSUPPORTED;
@@ -477,7 +478,7 @@ int32_t kvq_prefill_attn(const kvq_cache_desc* desc, const kvq_cache* cache, con
                                             : 1.0f / std::sqrt((float)desc->head_dim);
   a.qscale = scale * 1.4426950408889634f;
   for (int32_t b = 0; b < desc->batch; ++b) a.lens[b] = lens[b];
-  return launch_status(launch_prefill_int4_mfma(a, G, static_cast<hipStream_t>(stream)));
+  return launch_status(launch_prefill_int4_mfma(a, G, desc->format == KVQ_INT4_G16, static_cast<hipStream_t>(stream)));
 }
 
 int32_t kvq_dequant(const kvq_cache_desc* desc, const kvq_cache* cache, int32_t kv,

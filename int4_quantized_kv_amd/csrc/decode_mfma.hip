@@ -1969,7 +1969,8 @@ __device__ __forceinline__ TileDataPF read_tile_pf(const uint8_t* lb, const Lane
   return d;
 }
 
-template <int G, int NGK, int NCB, bool PG>
+// H16: fp16 scales (KVQ_INT4_G16), transferred and converted as in the decode kernel.
+template <int G, int NGK, int NCB, bool PG, bool H16 = false>
 __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) {
   using L = Slot<NGK>;
   constexpr int QPC = 16 / G;                  // queries per column block
@@ -2009,8 +2010,8 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
   auto issue = [&](int t) {
     uint8_t* lb = ring + (t % NB) * L::BYTES;
     const int t0 = tbase + TILE * t;
-    if constexpr (PG) issue_tile_pg<NGK>(a, b, kvh, t0, lo_first, pe, lb, lane, dof);
-    else issue_tile<NGK, false>(a, row0, t0, pe, 0, 0, lb, lane, dof);
+    if constexpr (PG) issue_tile_pg<NGK, H16>(a, b, kvh, t0, lo_first, pe, lb, lane, dof);
+    else issue_tile<NGK, false, H16>(a, row0, t0, pe, 0, 0, lb, lane, dof);
   };
 
   // ---- the columns: q as the B operands of the four (g, c2) MFMAs, -8 * (sum of each
@@ -2090,7 +2091,15 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
     lds_barrier();   // tile k visible to every wave; every wave done with tile k - 1
     if (k + 2 < ntiles && wave == (k + 2) % PF_WAVES) issue(k + 2);   // into tile k - 1's slot
     const int t0 = tbase + TILE * k;
-    const TileDataPF td = read_tile_pf<NGK>(ring + (k % NB) * L::BYTES, lo, j);
+    TileDataPF td = read_tile_pf<NGK>(ring + (k % NB) * L::BYTES, lo, j);
+    if constexpr (H16) {   // fp16 scales in the low halves of their dwords (dma_scale)
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        td.sk[T][0] = f16lo_to_f32(td.sk[T][0]);
+        td.sk[T][1] = f16lo_to_f32(td.sk[T][1]);
+        td.sv[T] = f16lo_to_f32(td.sv[T]);
+      }
+    }
     // K operands of the tile (shared by the column blocks): [T][g][c2]
     half8 ka[2][2][2];
 #pragma unroll
@@ -2203,24 +2212,24 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
   }
 }
 
-template <int G, int NCB, bool PG>
+template <int G, int NCB, bool PG, bool H16>
 hipError_t launch_pf_g(const DecodeArgs& a, hipStream_t s) {
   constexpr int QWG = PF_WAVES * NCB * (16 / G);
   const dim3 grid((a.nq + QWG - 1) / QWG, a.Hkv, a.B);
   switch (HD / a.gk) {
-    case 1: return launch_kernel(prefill_int4_mfma_kernel<G, 1, NCB, PG>, grid, dim3(PF_NT), a, s);
-    case 2: return launch_kernel(prefill_int4_mfma_kernel<G, 2, NCB, PG>, grid, dim3(PF_NT), a, s);
+    case 1: return launch_kernel(prefill_int4_mfma_kernel<G, 1, NCB, PG, H16>, grid, dim3(PF_NT), a, s);
+    case 2: return launch_kernel(prefill_int4_mfma_kernel<G, 2, NCB, PG, H16>, grid, dim3(PF_NT), a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool PG>
+template <bool PG, bool H16>
 hipError_t launch_pf(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
   switch (q_group) {
-    case 1: return launch_pf_g<1, PF_NCB, PG>(a, s);
-    case 2: return launch_pf_g<2, PF_NCB, PG>(a, s);
-    case 4: return launch_pf_g<4, PF_NCB, PG>(a, s);
-    case 8: return launch_pf_g<8, PF_NCB, PG>(a, s);
+    case 1: return launch_pf_g<1, PF_NCB, PG, H16>(a, s);
+    case 2: return launch_pf_g<2, PF_NCB, PG, H16>(a, s);
+    case 4: return launch_pf_g<4, PF_NCB, PG, H16>(a, s);
+    case 8: return launch_pf_g<8, PF_NCB, PG, H16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -2294,8 +2303,11 @@ bool mfma_int8_eligible(int32_t head_dim, int32_t cap, int32_t q_group) {
          (q_group == 1 || q_group == 2 || q_group == 4 || q_group == 8);
 }
 
-hipError_t launch_prefill_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s) {
-  return a.pages.size ? launch_pf<true>(a, q_group, s) : launch_pf<false>(a, q_group, s);
+hipError_t launch_prefill_int4_mfma(const DecodeArgs& a, int32_t q_group, bool fp16_scales,
+                                    hipStream_t s) {
+  if (fp16_scales)
+    return a.pages.size ? launch_pf<true, true>(a, q_group, s) : launch_pf<false, true>(a, q_group, s);
+  return a.pages.size ? launch_pf<true, false>(a, q_group, s) : launch_pf<false, false>(a, q_group, s);
 }
 
 hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s) {

@@ -127,9 +127,10 @@ bool mfma_int4h_eligible(const kvq_cache_desc* d, int32_t q_group);
 hipError_t launch_decode_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
 hipError_t launch_decode_int4h_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
 // Chunked-prefill (multi-query causal) attention over the INT4 cache on the matrix cores
-// (head_dim 128, V group 128, K group 64 or 128): a.q [B, Hq, nq, D], a.out the same in
-// fp32; no workspace.
-hipError_t launch_prefill_int4_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);
+// (head_dim 128, V group 128, K group 64 or 128; fp32 or fp16 scales): a.q [B, Hq, nq, D],
+// a.out the same in fp32; no workspace.
+hipError_t launch_prefill_int4_mfma(const DecodeArgs& a, int32_t q_group, bool fp16_scales,
+                                    hipStream_t s);
 // The same kernel for the INT8 per-token format (head_dim 128, capacity >= 16).
 bool mfma_int8_eligible(int32_t head_dim, int32_t cap, int32_t q_group);
 hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int32_t q_group, hipStream_t s);

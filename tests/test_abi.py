@@ -289,8 +289,8 @@ def test_paged_validation_and_sizes():
 
 
 def test_prefill_attn_validation():
-    """kvq_prefill_attn: INT4 with head_dim 128, V group 128 and K group 64 or 128 only;
-    chunk within each sequence; a ring must hold the chunk's window."""
+    """kvq_prefill_attn: INT4 (fp32 or fp16 scales) with head_dim 128, V group 128 and K
+    group 64 or 128 only; chunk within each sequence; a ring must hold the chunk's window."""
     d = kvq.make_desc("int4", 2, 8, 128, 4096)
     c = _cache()
     out = FAKE
@@ -301,5 +301,6 @@ def test_prefill_attn_validation():
     _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_prefill_attn, d, c, FAKE, 32, 16, [5000, 300], 4090, 0.0, out, 0)
     for bad in (kvq.make_desc("int8", 2, 8, 128, 4096), kvq.make_desc("int4", 2, 8, 64, 4096),
                 kvq.make_desc("int4", 2, 8, 128, 4096, 32, 128), kvq.make_desc("int4", 2, 8, 128, 4096, 64, 64),
-                kvq.make_desc("codec", 2, 8, 128, 4096)):
+                kvq.make_desc("codec", 2, 8, 128, 4096), kvq.make_desc("int4h", 2, 8, 128, 4096, 32, 128),
+                kvq.make_desc("codec3", 2, 8, 128, 4096)):
         _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_prefill_attn, bad, c, FAKE, 32, 16, [100, 100], 0, 0.0, out, 0)

@@ -75,6 +75,47 @@ def test_prefill_attention(case):
     assert_attn_close(out.cpu().numpy(), ref, f"prefill {case}")
 
 
+H16_CASES = [
+    # G, gk, nq, lens, window, cap, page size
+    (4, 64, 100, [1000, 1000], 0, None, 0),
+    (2, 128, 333, [2000, 700], 0, None, 0),
+    (8, 64, 64, [1500, 1200], 256, None, 0),
+    (4, 64, 48, [1999, 777], 0, None, 16),
+]
+
+
+@pytest.mark.parametrize("case", H16_CASES, ids=[f"h16_{i}" for i in range(len(H16_CASES))])
+def test_prefill_attention_fp16_scales(case):
+    """The same chunked prefill over an INT4 cache with fp16 scales (the kernel's 2-byte
+    scale transfers), against the oracle over the fp16-scale format's dequantized values."""
+    G, gk, nq, lens, W, cap, P = case
+    B, Hkv, D = len(lens), 2, 128
+    L = max(lens)
+    k = synth.kv_source((B, Hkv, L, D), 4700 + nq, DEV, outlier_channels=3)
+    v = synth.kv_source((B, Hkv, L, D), 4800 + nq, DEV, outlier_channels=3)
+    q = synth.query((B, Hkv * G, nq, D), 4900 + nq, DEV)
+    if P:
+        C = (L + P - 1) // P * P
+        table, pages = synth.block_table(B, C, P, 5000 + nq)
+        desc = kvq.make_desc("int4h", B, Hkv, D, C, gk, 128, page_size=P, num_pages=pages)
+        dc = kvq.DeviceCache(desc, DEV, block_table=table.to(DEV))
+    else:
+        C = cap or L
+        desc = kvq.make_desc("int4h", B, Hkv, D, C, gk, 128)
+        dc = kvq.DeviceCache(desc, DEV)
+    _fill(desc, dc, k, v, L, C)
+    out = torch.full((B, Hkv * G, nq, D), float("nan"), dtype=torch.float32, device=DEV)
+    kvq.kvq_prefill_attn(desc, dc.c, q, Hkv * G, nq, lens, W, 0.0, out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all(), "an output was not written"
+    qk, sk = quant.quantize_int4_fp16_scale(np16(k), gk)
+    qv, sv = quant.quantize_int4_fp16_scale(np16(v), 128)
+    kh = quant.dequantize_int4_exact(qk, sk, gk)
+    vh = quant.dequantize_int4_exact(qv, sv, 128)
+    ref = attention.prefill_attention(np16(q), kh, vh, lens, W)
+    assert_attn_close(out.cpu().numpy(), ref, f"prefill fp16 scales {case}")
+
+
 def test_prefill_then_decode_agree():
     """A one-token chunk is the decode step: kvq_prefill_attn with n_query = 1 and
     kvq_decode_attn give the same output within the bar."""
