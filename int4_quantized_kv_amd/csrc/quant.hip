@@ -35,6 +35,8 @@ namespace {
 // (base + t) mod cap with base < cap and t < n <= cap: one conditional subtract
 // (cache_slot when the cache keeps sink slots ahead of its ring).
 __device__ __forceinline__ int log2i(int x) { return 31 - __builtin_clz(x); }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 
 template <bool INT8, bool H16 = false>
@@ -59,7 +61,10 @@ __device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t i = i0 + u * stride;
-      if (i < npair) raw[u] = srcp[i];
+      if (i < npair) {   // non-temporal: every source byte is read once (+6% on a 3.4 GB layer)
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(srcp) + i);
+        raw[u] = make_uint4(t.x, t.y, t.z, t.w);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -122,7 +127,7 @@ __device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
           const float y = H16 ? (float)(_Float16)(x[j] / sc) : kvq_div_exact(x[j], sc, r);
           w |= (kvq_round_bits(fminf(fmaxf(y, -7.0f), 7.0f)) & 15u) << (4 * j);
         }
-        reinterpret_cast<uint32_t*>(isv ? a.v_codes : a.k_codes)[(drow << lsh) + c] = w;
+        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(isv ? a.v_codes : a.k_codes) + (drow << lsh) + c);
         if ((c & (lpg - 1)) == 0) {
           if (H16) reinterpret_cast<_Float16*>(scales)[(drow << gprsh) + (c >> gsh)] = (_Float16)sc;
           else scales[(drow << gprsh) + (c >> gsh)] = sc;
@@ -201,7 +206,7 @@ __device__ __forceinline__ void dequant_pair(const DequantArgs& a, int bh) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         v[j] = (INT8 ? (float)(int8_t)((wr[u] >> (8 * j)) & 255u) : (float)nib_s(wr[u], j)) * s;
-      outp[k] = make_float4(v[0], v[1], v[2], v[3]);
+      __builtin_nontemporal_store((floatx4){v[0], v[1], v[2], v[3]}, reinterpret_cast<floatx4*>(outp) + k);
     }
   }
 }
