@@ -1913,8 +1913,9 @@ hipError_t launch_g16(const DecodeArgs& a, hipStream_t s) {
 // each column's own horizon.
 constexpr int PF_WAVES = 4;
 constexpr int PF_NT = PF_WAVES * 64;
-constexpr int PF_NCB = 1;   // column blocks (16 query rows each) per wave: 2 measured
-                            // 365 vs 458 TFLOP/s (261 VGPRs, one wave per SIMD)
+constexpr int PF_NCB = 2;   // column blocks (16 query rows each) per wave: each wave's
+                            // K and V operand conversions serve 32 columns (232 VGPRs, two
+                            // waves per SIMD): 508 vs 454 TFLOP/s with one block
 
 struct TileDataPF {
   u32x2 k[2][2];     // [T][g]: dims 64 g + 16 j .. + 15 of tile row r of half T
@@ -2109,33 +2110,6 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
         ka[T][g][0] = unpack_word_u(td.k[T][g].x);
         ka[T][g][1] = unpack_word_u(td.k[T][g].y);
       }
-    // V operands: byte halves of two rows' dwords give the (row, row + 1) pairs of 4 dims
-    half8 va[8];
-    {
-      uint32_t xlo[4], xhi[4];
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        const int T = pr >> 1, i = 2 * (pr & 1);
-        xlo[pr] = __builtin_amdgcn_perm(td.v[T][i + 1], td.v[T][i], 0x05040100u);
-        xhi[pr] = __builtin_amdgcn_perm(td.v[T][i + 1], td.v[T][i], 0x07060302u);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        H8 v;
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const uint32_t x = e < 4 ? xlo[pr] : xhi[pr];
-          const uint32_t x8 = x >> 8;
-          switch (e & 3) {
-            case 0: v.u[pr] = v_pair_f16<0>(x, x8); break;
-            case 1: v.u[pr] = v_pair_f16<1>(x, x8); break;
-            case 2: v.u[pr] = v_pair_f16<2>(x, x8); break;
-            default: v.u[pr] = v_pair_f16<3>(x, x8); break;
-          }
-        }
-        va[e] = v.h;
-      }
-    }
     const floatx4 sk00 = __builtin_bit_cast(floatx4, td.sk[0][0]), sk01 = __builtin_bit_cast(floatx4, td.sk[0][1]);
     const floatx4 sk10 = __builtin_bit_cast(floatx4, td.sk[1][0]), sk11 = __builtin_bit_cast(floatx4, td.sk[1][1]);
     const floatx4 sv0 = __builtin_bit_cast(floatx4, td.sv[0]), sv1 = __builtin_bit_cast(floatx4, td.sv[1]);
@@ -2143,6 +2117,7 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
                         fmaxf(fmaxf(sv1[0], sv1[1]), fmaxf(sv1[2], sv1[3])));
     // (uniform) positions past the earliest query or before the latest window start
     const bool masked = t0 + TILE - 1 > min_hi || t0 < max_lo;
+    H8 phi[NCB], plo[NCB];   // each column block's P' (fp16 hi and lo parts), B operands of P.V
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       float z[2][4];
@@ -2172,7 +2147,6 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
                        fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
       mx = max_over_j(mx);
       const float mq = tile_update(st[cb], mx, svmax, a.qscale);
-      H8 phi, plo;
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         const floatx4 sv = T ? sv1 : sv0;
@@ -2181,13 +2155,38 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
           const float pa = fast_exp2(__builtin_fmaf(z[T][i], a.qscale, -mq));
           const float pb = fast_exp2(__builtin_fmaf(z[T][i + 1], a.qscale, -mq));
           st[cb].l += pa + pb;
-          split_hi_lo(pa * sv[i], pb * sv[i + 1], phi.u[2 * T + i / 2], plo.u[2 * T + i / 2]);
+          split_hi_lo(pa * sv[i], pb * sv[i + 1], phi[cb].u[2 * T + i / 2], plo[cb].u[2 * T + i / 2]);
+        }
+      }
+    }
+    // ---- P.V, one dim group at a time (its V operand converted just before its MFMAs,
+    // so that only one group's operand is live): byte halves of two rows' dwords give the
+    // (row, row + 1) pairs of 4 dims
+    uint32_t xlo[4], xhi[4];
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      const int T = pr >> 1, i = 2 * (pr & 1);
+      xlo[pr] = __builtin_amdgcn_perm(td.v[T][i + 1], td.v[T][i], 0x05040100u);
+      xhi[pr] = __builtin_amdgcn_perm(td.v[T][i + 1], td.v[T][i], 0x07060302u);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      H8 v;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const uint32_t x = e < 4 ? xlo[pr] : xhi[pr];
+        const uint32_t x8 = x >> 8;
+        switch (e & 3) {
+          case 0: v.u[pr] = v_pair_f16<0>(x, x8); break;
+          case 1: v.u[pr] = v_pair_f16<1>(x, x8); break;
+          case 2: v.u[pr] = v_pair_f16<2>(x, x8); break;
+          default: v.u[pr] = v_pair_f16<3>(x, x8); break;
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        st[cb].oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[e], phi.h, st[cb].oacc[e], 0, 0, 0);
-        st[cb].oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[e], plo.h, st[cb].oacc[e], 0, 0, 0);
+      for (int cb = 0; cb < NCB; ++cb) {
+        st[cb].oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v.h, phi[cb].h, st[cb].oacc[e], 0, 0, 0);
+        st[cb].oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v.h, plo[cb].h, st[cb].oacc[e], 0, 0, 0);
       }
     }
   }
