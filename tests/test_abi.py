@@ -128,6 +128,10 @@ def test_error_paths_enqueue_nothing():
     _expect(kvq.KVQ_ERR_CAPACITY, kvq.kvq_decode_attn, d, c, FAKE, 8, [100, 10], 65, 0.0, 0, FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, FAKE, ws - 1, 0)
     _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, 0, ws, 0)
+    # more (sequence, KV head) units than the workspace's 16384 split counters
+    big = kvq.make_desc("int4", 256, 65, 128, 64)
+    _expect(kvq.KVQ_ERR_UNSUPPORTED, kvq.kvq_decode_attn, big, c, FAKE, 65, [10] * 256, 0, 0.0, 0, FAKE, FAKE,
+            1 << 30, 0)
     _expect(kvq.KVQ_ERR_WORKSPACE, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, 0.0, 0, FAKE, FAKE + 8, ws, 0)
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], -1, 0.0, 0, FAKE, FAKE, ws, 0)
     _expect(kvq.KVQ_ERR_ARG, kvq.kvq_decode_attn, d, c, FAKE, 8, [64, 10], 0, float("nan"), 0, FAKE, FAKE, ws, 0)

@@ -509,3 +509,30 @@ def test_matrix_core_long_contexts_many_splits(case):
         vh = attention.recent_fp16_rows(vh, np16(v), lens, R)
     ref = attention.decode_attention(np16(q), kh, vh, lens, W, sinks=S)
     assert_attn_close(out.cpu().numpy(), ref, f"splits {case}")
+
+
+@pytest.mark.parametrize("fmt", ["int4", "codec"])
+def test_maximum_units_fused_step(fmt):
+    """The largest call the library takes: 256 sequences (KVQ_MAX_BATCH) x 64 KV heads =
+    16384 (sequence, KV head) units, one split counter each in the workspace, with ragged
+    lengths 1 .. 48 (lengths 1 and 2 included), GQA 2, the fused append + decode step;
+    every unit against the oracle."""
+    B, Hkv, G, D, C = 256, 64, 2, 128, 48
+    lens = [1 + (b * 7) % C for b in range(B)]
+    lens[0], lens[1] = 1, 2
+    k = synth.kv_source((B, Hkv, C, D), 5100, DEV, outlier_channels=2)
+    v = synth.kv_source((B, Hkv, C, D), 5101, DEV)
+    q = synth.query((B, Hkv * G, D), 5102, DEV)
+    desc = kvq.make_desc(fmt, B, Hkv, D, C)
+    dc = kvq.DeviceCache(desc, DEV)
+    kvq.kvq_quantize_prefill(desc, dc.c, k, v, 0, C)   # every slot; each sequence attends its own lens
+    idx = torch.tensor([ln - 1 for ln in lens], device=DEV)
+    ar = torch.arange(B, device=DEV)
+    kn, vn = k[ar, :, idx].contiguous(), v[ar, :, idx].contiguous()
+    out = append_decode(desc, dc, kn, vn, q, Hkv * G, lens)
+    if fmt == "codec":
+        kh, vh, _ = codec_hat_from_device(dc, fmt, np16(k), np16(v), lens)
+    else:
+        kh, vh = _oracle_hat(fmt, np16(k), np16(v))
+    ref = attention.decode_attention(np16(q), kh, vh, lens)
+    assert_attn_close(out.cpu().numpy(), ref, f"{fmt} at 16384 units")
