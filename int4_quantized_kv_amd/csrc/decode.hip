@@ -127,11 +127,20 @@ __device__ __forceinline__ void codes_f32(const uint32_t w[2], const float2* lv2
 // otherwise they store and exit.)
 constexpr int MERGE_INLINE_MAX = 32;
 
+// Threads per workgroup: 512 for the codecs at D = 256 (16 row groups of 32 lanes: a
+// split of 128 rows is two row steps, and half as many splits write and merge partials
+// as with 256 threads and 64-row splits), 256 otherwise.
+__host__ __device__ constexpr int splitk_threads(int D, int FMT) {
+  return (FMT == KVQ_WHT_LM4 || FMT == KVQ_WHT_LM3) && D == 256 ? 512 : 256;
+}
+
 template <int D, int G, int FMT>
-__global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(DecodeArgs a) {
   constexpr bool CODEC = FMT == KVQ_WHT_LM4 || FMT == KVQ_WHT_LM3;
+  constexpr int NT = splitk_threads(D, FMT);
+  constexpr int NW = NT / 64;   // waves
   constexpr int LPR = D / 8;
-  constexpr int NGRP = 256 / LPR;
+  constexpr int NGRP = NT / LPR;
   __shared__ float s_m[NGRP][G];
   __shared__ float s_l[NGRP][G];
   __shared__ float s_acc[NGRP][G][D];
@@ -279,8 +288,9 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
 
   if (CODEC) {   // the codebook levels (the barrier comes after the loads above): the
     // two levels of a byte (4 bits) or of a 6-bit index pair (3 bits)
-    lv2[tid] = FMT == KVQ_WHT_LM3 ? make_float2(a.levels[tid & 7], a.levels[(tid >> 3) & 7])
-                                  : make_float2(a.levels[tid & 15], a.levels[tid >> 4]);
+    if (tid < 256)
+      lv2[tid] = FMT == KVQ_WHT_LM3 ? make_float2(a.levels[tid & 7], a.levels[(tid >> 3) & 7])
+                                    : make_float2(a.levels[tid & 15], a.levels[tid >> 4]);
     __syncthreads();
   }
 
@@ -388,7 +398,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
     for (int j = 0; j < 8; ++j) s_acc[grp][h][8 * c + j] = acc[h][j];
   __syncthreads();
 
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D, d = idx % D;
     float M = NEG_INF;
 #pragma unroll
@@ -442,12 +452,12 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   // splits are one round trip; the partial loads go in groups of 8 under a uniform test,
   // the split index clamped to np - 1 inside a group (their weight is 0) and the output
   // index to the last output
-  constexpr int OPT = (G * D + 255) / 256;                 // outputs per thread
+  constexpr int OPT = (G * D + NT - 1) / NT;               // outputs per thread
   constexpr int PF = OPT <= 2 ? 32 : 64 / OPT;             // partials prefetched per output
   float pre[OPT][PF];
 #pragma unroll
   for (int u = 0; u < OPT; ++u) {
-    const int idx = min(tid + 256 * u, G * D - 1), h = idx / D, d = idx % D;
+    const int idx = min(tid + NT * u, G * D - 1), h = idx / D, d = idx % D;
     const float* src = a.ws_acc + (pbase + (size_t)h * np) * D + d;
 #pragma unroll
     for (int t8 = 0; t8 < PF; t8 += 8) {
@@ -460,11 +470,11 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
       }
     }
   }
-  constexpr int HPW = (G + 3) / 4;                         // heads per wave
+  constexpr int HPW = (G + NW - 1) / NW;                   // heads per wave
   float mt[HPW], lt[HPW];
 #pragma unroll
   for (int k = 0; k < HPW; ++k) {
-    const int h = wave + 4 * k;
+    const int h = wave + NW * k;
     mt[k] = NEG_INF;
     lt[k] = 0.0f;
     if (h < G && lane < np) {
@@ -477,7 +487,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   // and 32 (by every lane: the half sums must be formed in both lanes)
 #pragma unroll
   for (int k = 0; k < HPW; ++k) {
-    const int h = wave + 4 * k;
+    const int h = wave + NW * k;
     if (h < G) {   // wave-uniform
       const float mh = lane_group_max<32>(mt[k]);
       const float M = fmaxf(readlane_f(mh, 0), readlane_f(mh, 32));
@@ -491,7 +501,7 @@ __global__ void __launch_bounds__(256) decode_splitk_kernel(DecodeArgs a) {
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < OPT; ++u) {
-    const int idx = tid + 256 * u;
+    const int idx = tid + NT * u;
     if (idx < G * D) {
       const int h = idx / D, d = idx % D;
       const float* wh = s_w + h * 64;
@@ -640,10 +650,10 @@ hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t s) {
   DecodeArgs k = a;
   k.merge_inline = a.nsplit <= MERGE_INLINE_MAX;
   switch (G) {
-    case 1: e = launch_kernel(decode_splitk_kernel<D, 1, FMT>, grid, dim3(256), k, s); break;
-    case 2: e = launch_kernel(decode_splitk_kernel<D, 2, FMT>, grid, dim3(256), k, s); break;
-    case 4: e = launch_kernel(decode_splitk_kernel<D, 4, FMT>, grid, dim3(256), k, s); break;
-    case 8: e = launch_kernel(decode_splitk_kernel<D, 8, FMT>, grid, dim3(256), k, s); break;
+    case 1: e = launch_kernel(decode_splitk_kernel<D, 1, FMT>, grid, dim3(splitk_threads(D, FMT)), k, s); break;
+    case 2: e = launch_kernel(decode_splitk_kernel<D, 2, FMT>, grid, dim3(splitk_threads(D, FMT)), k, s); break;
+    case 4: e = launch_kernel(decode_splitk_kernel<D, 4, FMT>, grid, dim3(splitk_threads(D, FMT)), k, s); break;
+    case 8: e = launch_kernel(decode_splitk_kernel<D, 8, FMT>, grid, dim3(splitk_threads(D, FMT)), k, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || k.merge_inline) return e;
@@ -678,9 +688,12 @@ int32_t plan_splits(const kvq_cache_desc* d, int32_t q_group, int32_t span) {
   // append is fused (planned for every call of those formats, so that the workspace
   // query does not depend on the call)
   const int32_t extra = is_codec(d->format) || d->format == KVQ_INT4_G16 ? 1 : 0;
-  const int32_t target = 1024;       // workgroups: 4 per CU on 256 CUs (all resident)
-  const int32_t min_rows = 64;       // positions per split worth a workgroup (short
-                                     // contexts need many splits to fill the chip)
+  // workgroups: 4 per CU on 256 CUs (all resident), and positions per split worth a
+  // workgroup (short contexts need many splits to fill the chip); the codecs at D = 256
+  // run 512-thread workgroups (splitk_threads): half the workgroups, twice the rows
+  const bool wide = is_codec(d->format) && d->head_dim == 256;
+  const int32_t target = wide ? 512 : 1024;
+  const int32_t min_rows = wide ? 128 : 64;
   int32_t n = (target + units - 1) / units - extra;
   const int32_t by_span = (span + min_rows - 1) / min_rows;
   if (n > by_span) n = by_span;
