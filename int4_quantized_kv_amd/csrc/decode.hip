@@ -432,7 +432,11 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
   // ---- in-kernel merge (few splits): every wave waits for its partial stores, the
   // workgroup counts itself in with a device-scope atomic, and the last split of the
   // (b, kv head) merges the partials with the log-sum-exp rule (the codec's output is
-  // rotated back), then resets the counter for the next call
+  // rotated back), then resets the counter for the next call.  The order rests on the
+  // same hardware properties as the matrix-core kernel's merge (decode_mfma.hip,
+  // "arrivals"): acknowledged device-scope stores are visible to device-scope loads on
+  // every XCD, increments follow their workgroup's acknowledgements, and the merging
+  // workgroup's loads follow its increment's return.
   __shared__ int s_last;
   uint32_t* cnt = a.counters + (size_t)b * a.Hkv + kvh;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

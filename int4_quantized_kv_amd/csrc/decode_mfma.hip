@@ -1730,7 +1730,15 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // where every XCD sees them); each wave waits until its own have completed before the
   // barrier, so when the counting thread bumps the (device-scope) arrival counter the
   // whole partial is visible.  This avoids a release fence, which on this chip writes
-  // back the XCD's whole L2 and costs microseconds per workgroup.
+  // back the XCD's whole L2 and costs microseconds per workgroup.  Ordering: (1) an
+  // acknowledged device-scope store has been performed where every XCD's device-scope
+  // loads see it; (2) each workgroup's increment comes after its acknowledgements; (3)
+  // the increments of one counter are totally ordered, so the workgroup that reads
+  // count - 1 comes after every other workgroup's stores; (4) it issues its
+  // device-scope partial loads only once its increment has returned (they depend on
+  // the returned value through the branch below).  These are properties of the hardware
+  // rather than of the C++ memory model, in which relaxed atomics order nothing; an
+  // acquire on the increment adds a cache invalidation costing 2-3% per decode step.
   // the new row's codes and scales go to the cache here, so that the wait below covers
   // them together with the partials (a barrier right after the loop would wait for them
   // alone); no tile of this step reads that row
