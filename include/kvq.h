@@ -246,9 +246,10 @@ int32_t kvq_append(const kvq_cache_desc* desc, const kvq_cache* cache,
  *              time need separate workspaces.
  * Split-K: each split writes an unnormalized partial (running max, sum, weighted V) to
  * the workspace; the partials are merged with the log-sum-exp rule by the last split to
- * finish (no second launch) on the matrix-core kernels (INT4 with head_dim 128 and V
- * group 128; INT8 with head_dim 128) and, up to 32 splits, on the split-K kernel (every
- * other case); above that by a second kernel.  R > 0 runs on the INT4 matrix-core kernel
+ * finish (no second launch) on the matrix-core kernels (INT4, with fp32 or fp16 scales,
+ * at head_dim 128 and V group 128, fp16 scales without sinks; INT8 with head_dim 128)
+ * and, up to 32 splits, on the split-K kernel (every other case); above that by a second
+ * kernel.  R > 0 runs on the INT4 matrix-core kernel
  * only (KVQ_ERR_UNSUPPORTED for other shapes), whose splits each attend a share of the
  * fp16 rows besides their share of the codes. */
 int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
@@ -262,10 +263,11 @@ int32_t kvq_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
  *   k_f16, v_f16: device, [B, Hkv, D] fp16, the new token's rows (position lens[b] - 1).
  * Every other argument, the workspace rule and the errors are those of kvq_decode_attn
  * (KVQ_ERR_ARG also for null k_f16 / v_f16).  On the INT4 matrix-core kernel (head_dim
- * 128, V group 128), for the codecs and for INT4 with fp16 scales, the new row is
- * quantized inside the attention kernel, which writes it to the cache (and, with R > 0, its fp16 row to the ring) and
- * adds it to the softmax without reading it back (one launch per step); the other
- * cases run the append kernel first. */
+ * 128, V group 128, either scale type), for the codecs and for INT4 with fp16 scales at
+ * other shapes, the new row is quantized inside the attention kernel, which writes it
+ * to the cache (and, with R > 0, its fp16 row to the ring) and adds it to the softmax
+ * without reading it back (one launch per step); the other cases (INT8) run the append
+ * kernel first. */
 int32_t kvq_append_decode_attn(const kvq_cache_desc* desc, const kvq_cache* cache,
                                const void* k_f16, const void* v_f16, const void* q_f16,
                                int32_t q_heads, const int32_t* lens, int32_t window,
