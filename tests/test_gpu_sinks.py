@@ -48,6 +48,12 @@ def _hat(fmt, k16, v16):
         qk, sk = quant.quantize_int8(k16)
         qv, sv = quant.quantize_int8(v16)
         return quant.dequantize_int8_exact(qk, sk), quant.dequantize_int8_exact(qv, sv)
+    if fmt == "int4h":
+        D = k16.shape[-1]
+        gk, gv = min(64, D), min(128, D)
+        qk, sk = quant.quantize_int4_fp16_scale(k16, gk)
+        qv, sv = quant.quantize_int4_fp16_scale(v16, gv)
+        return quant.dequantize_int4_exact(qk, sk, gk), quant.dequantize_int4_exact(qv, sv, gv)
     kidx, ksc, _ = codec.encode(k16)
     vidx, vsc, _ = codec.encode(v16)
     return codec.decode(kidx, ksc), codec.decode(vidx, vsc)
@@ -85,6 +91,7 @@ CASES = [
     ("int4", 64, 2, 16, 96, 96, [500, 140], 0),
     ("codec", 256, 2, 4, 256, 256, [1500, 600], 0),
     ("codec", 128, 4, 8, 128, 100, [700, 20], 40),      # merge kernel; a short sequence
+    ("int4h", 128, 4, 4, 256, 200, [1000, 700], 0),     # fp16 scales with sinks: split-K kernel
 ]
 
 
@@ -119,7 +126,7 @@ def test_decode_window_with_sinks(case):
     assert_attn_close(out.cpu().numpy(), ref, f"{case}")
 
 
-@pytest.mark.parametrize("fmt,D,G", [("int4", 128, 4), ("codec", 256, 2)])
+@pytest.mark.parametrize("fmt,D,G", [("int4", 128, 4), ("codec", 256, 2), ("int4h", 128, 4)])
 def test_append_decode_with_sinks(fmt, D, G):
     """The step's new row (position len - 1) lands in its ring slot and is attended."""
     B, Hkv, S, R, W, L = 2, 2, 4, 128, 128, 700
@@ -140,8 +147,9 @@ def test_append_decode_with_sinks(fmt, D, G):
     ref_cache = _fill_ring(desc, k, v, L)
     slot = S + (L - 1 - S) % R
     torch.cuda.synchronize()
+    sc = (lambda t: t.view(torch.float16)) if fmt == "int4h" else (lambda t: t)   # fp16 scales
     for x, y in ((dc.k_codes, ref_cache.k_codes), (dc.v_codes, ref_cache.v_codes),
-                 (dc.k_scales, ref_cache.k_scales), (dc.v_scales, ref_cache.v_scales)):
+                 (sc(dc.k_scales), sc(ref_cache.k_scales)), (sc(dc.v_scales), sc(ref_cache.v_scales))):
         xs = x.view(B, Hkv, S + R, -1)[:, :, slot]
         ys = y.view(B, Hkv, S + R, -1)[:, :, slot]
         assert torch.equal(xs, ys)
