@@ -2,6 +2,8 @@
 
 No arithmetic of the method lives here; expected values come from ``oracle/`` only.
 """
+import os
+
 import numpy as np
 import torch
 
@@ -48,6 +50,10 @@ def attn_errors(got, ref):
 
 def assert_attn_close(got, ref, what=""):
     max_abs, rel = attn_errors(got, ref)
+    log = os.environ.get("KVQ_TEST_METRICS")   # optional: one line per check, for margins
+    if log:
+        with open(log, "a") as f:
+            f.write(f"{max_abs:.3e} {rel:.3e} {what}\n")
     assert max_abs <= ATTN_MAX_ABS and rel <= ATTN_REL_L2, \
         f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
     return max_abs, rel
