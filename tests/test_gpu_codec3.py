@@ -20,20 +20,6 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def test_packed3_helpers_round_trip():
-    rng = np.random.default_rng(3)
-    idx = rng.integers(0, 8, size=(3, 5, 64))
-    rows = pack3(idx)
-    assert rows.shape == (3, 5, 24)
-    assert np.array_equal(unpack3(rows), idx)
-    one = np.zeros(16, dtype=np.uint8)
-    one[0] = 7                         # bits 0, 1, 2
-    one[9] = 5                         # 0b101 at bits 27 .. 29: bits 27 and 29 (byte 3: 8 + 32)
-    one[15] = 6                        # 0b110 at bits 45 .. 47: bits 46 and 47 (byte 5: 64 + 128)
-    r = pack3(one)
-    assert list(r) == [7, 0, 0, 40, 0, 192]
-
-
 def _encode(k, v, cap=None):
     B, H, S, D = k.shape
     desc = kvq.make_desc("codec3", B, H, D, cap or S)
