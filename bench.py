@@ -541,10 +541,42 @@ def timeline(args):
         for sp in range(ns):
             by_sp.setdefault(sp, []).extend(wg_end[sp::ns].tolist())
         corr.append(float(np.corrcoef(us(st[:, 0] - t0), wg_end)[0, 1]))
+    # what makes a workgroup late: its first tile's arrival, its compute unit (the same
+    # CU late in every layer), or its (b, kv head) unit's data (the unit's other splits
+    # late with it); lateness = last loop end minus the layer's median
+    corr_first, corr_unit, late_by_cu, unit_bound = [], [], {}, []
+    for st in stamps:
+        t0 = st[:, 0].min()
+        wg_end = us(st[:, 4:12].max(1) - t0)
+        late = wg_end - np.median(wg_end)
+        # the last loop end if each (b, kv head) unit's splits shared its tiles perfectly
+        # (every split ending at the mean of their ends), against the actual last one
+        unit_bound.append((float(wg_end.mean()), float(wg_end.reshape(-1, ns).mean(1).max()),
+                           *np.percentile(wg_end, [50, 90, 99, 100]).tolist()))
+        corr_first.append(float(np.corrcoef(us(st[:, 17] - t0), wg_end)[0, 1]))
+        per_unit = late.reshape(-1, ns)
+        others = (per_unit.sum(1, keepdims=True) - per_unit) / max(ns - 1, 1)
+        if ns > 1:
+            corr_unit.append(float(np.corrcoef(per_unit.ravel(), others.ravel())[0, 1]))
+        cu = ((st[:, 1] >> 32) & 0xF) * 256 + ((st[:, 1] >> 8) & 0xFF)
+        for c, x in zip(cu.tolist(), late.tolist()):
+            late_by_cu.setdefault(c, []).append(x)
+    cu_mean = np.array([np.mean(v) for v in late_by_cu.values() if len(v) > 1])
+    all_late = np.concatenate([np.array(v) for v in late_by_cu.values()])
     out_extra = {"wg_last_loop_end_by_split_us": {sp: [round(float(x), 2) for x in np.percentile(v, [0, 50, 100])]
                                                  for sp, v in by_sp.items()},
                  "loop_end_spread_inside_wg_us": [round(float(x), 2) for x in np.percentile(intra, [0, 50, 90, 100])],
-                 "corr_entry_vs_wg_end": round(float(np.median(corr)), 3)}
+                 "corr_entry_vs_wg_end": round(float(np.median(corr)), 3),
+                 "corr_first_tile_vs_wg_end": round(float(np.median(corr_first)), 3),
+                 "corr_wg_vs_unit_siblings_lateness": round(float(np.median(corr_unit)), 3) if corr_unit else None,
+                 # (mean over all workgroups, max over units of their mean, percentiles
+                 # 50 / 90 / 99 / 100 over workgroups)
+                 "wg_last_loop_end_mean_unitmax_p50_p90_p99_max_us": [round(float(x), 2)
+                                                               for x in np.median(np.array(unit_bound), axis=0)],
+                 "compute_units_seen": len(late_by_cu),
+                 "lateness_sd_us": round(float(all_late.std()), 3),
+                 "per_cu_mean_lateness_sd_us": round(float(cu_mean.std()), 3) if cu_mean.size else None,
+                 "per_cu_mean_lateness_max_us": round(float(cu_mean.max()), 3) if cu_mean.size else None}
     out = {"timeline_us": {k: [round(float(x), 2) for x in np.median(np.array(v), axis=0)]
                            for k, v in per.items()},
            **out_extra,

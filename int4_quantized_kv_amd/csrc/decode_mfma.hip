@@ -141,15 +141,6 @@ __device__ __forceinline__ float sum_over_j(float x) {
   swap32(c, d);
   return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
 }
-// x + x[lane ^ 1] / x[lane ^ 2] within quads (DPP, one VALU op each).
-__device__ __forceinline__ float add_xor1(float x) {
-  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                 0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float add_xor2(float x) {
-  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                 0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-}
 
 typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
 typedef __attribute__((address_space(3))) void* lds_vptr;
@@ -286,32 +277,58 @@ __device__ __forceinline__ DmaOffs dma_offsets(int lane) {
 // the LDS slot `lb`.  A full tile whose 32 slots are contiguous is addressed from one
 // scalar base row plus the fixed lane offsets; otherwise each row is clamped to pe - 1
 // (masked positions read a valid row) and wrapped around the ring.
+// The unit's four streams as buffer resources (base at the unit's first row), so that a
+// full tile's transfers take a scalar byte offset plus the fixed lane offsets and need no
+// per-lane address arithmetic.  Word 3 is the gfx9 raw-buffer configuration; the record
+// count is the unit's bytes (used only for units below 4 GiB per stream: cap <= 2^26).
+struct UnitBufs {
+  __amdgpu_buffer_rsrc_t kc, vc, ks, vs;
+};
+constexpr int BUF_CFG = 0x00020000;
+constexpr int BUF_MAX_CAP = 1 << 26;
+template <int NGK, bool H16>
+__device__ __forceinline__ UnitBufs unit_bufs(const DecodeArgs& a, size_t row0) {
+  const uint32_t cap = (uint32_t)min(a.cap, BUF_MAX_CAP);
+  auto mk = [&](const void* base, size_t row_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(base) + row0 * row_bytes), (short)0,
+        (int)(cap * row_bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)(cap * row_bytes)), BUF_CFG);
+  };
+  return {mk(a.k_codes, HD / 2), mk(a.v_codes, HD / 2), mk(a.k_scales, NGK * SCB<H16>),
+          mk(a.v_scales, SCB<H16>)};
+}
+template <int SIZE>
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                        uint8_t* l) {
+  static_assert(SIZE == 16 || SIZE == 4 || SIZE == 2, "transfer size");
+  if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)l, 16, voff, soff, 0, CPOL_NT);
+  else if constexpr (SIZE == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)l, 4, voff, soff, 0, CPOL_NT);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)l, 2, voff, soff, 0, CPOL_NT);
+}
+
 template <int NGK, bool SK, bool H16 = false>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int t0, int pe,
                                            int lo, int vlo, uint8_t* lb, int lane,
-                                           const DmaOffs& o) {
+                                           const DmaOffs& o, const UnitBufs& ub) {
   using L = Slot<NGK>;
   const int cap = a.cap;
-  const int sbase = t0 % cap;
+  const int sbase = t0 < cap ? t0 : t0 % cap;
   const uint8_t* kc = static_cast<const uint8_t*>(a.k_codes);
   const uint8_t* vc = static_cast<const uint8_t*>(a.v_codes);
   const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k_scales);
   const uint8_t* vs = reinterpret_cast<const uint8_t*>(a.v_scales);
-  if (!SK && t0 + TILE <= pe && sbase + TILE <= cap) {
-    const size_t rb = row0 + (size_t)sbase;
-    const uint8_t* kb = kc + rb * (HD / 2);
-    const uint8_t* vb = vc + rb * (HD / 2);
-    const uint8_t* ksb = ks + rb * (NGK * SCB<H16>);
-    const uint8_t* vsb = vs + rb * SCB<H16>;
+  if (!SK && t0 + TILE <= pe && sbase + TILE <= cap && cap <= BUF_MAX_CAP) {
+    const uint32_t sb = (uint32_t)sbase;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      dma16<CPOL_NT>(kb + o.kv[T], lb + L::K_OFF + 1024 * T);
-      dma16<CPOL_NT>(vb + o.kv[T], lb + L::V_OFF + 1024 * T);
+      dma_buf<16>(ub.kc, (uint32_t)o.kv[T], sb * (HD / 2), lb + L::K_OFF + 1024 * T);
+      dma_buf<16>(ub.vc, (uint32_t)o.kv[T], sb * (HD / 2), lb + L::V_OFF + 1024 * T);
     }
 #pragma unroll
     for (int h = 0; h < (NGK <= 2 ? 1 : 2); ++h)
-      dma_scale<H16>(ksb + (o.sk[h] >> SCSH<H16>), lb + L::SK_OFF + 256 * h);
-    dma_scale<H16>(vsb + (o.sv >> SCSH<H16>), lb + L::SV_OFF);
+      dma_buf<SCB<H16>>(ub.ks, (uint32_t)(o.sk[h] >> SCSH<H16>), sb * (NGK * SCB<H16>),
+                        lb + L::SK_OFF + 256 * h);
+    dma_buf<SCB<H16>>(ub.vs, (uint32_t)(o.sv >> SCSH<H16>), sb * SCB<H16>, lb + L::SV_OFF);
     return;
   }
   auto row_of = [&](int rho) -> size_t {
@@ -511,62 +528,74 @@ struct TileData {
   uint32_t v[2][4];
 };
 
+// A lane's read addresses in slot 0 of its wave's ring, computed once before the loop;
+// the loop is unrolled over the ring's slots, so a slot's offset is an immediate of the
+// read instructions and a tile costs no address arithmetic.
+struct TileAddr {
+  uint32_t k0, k1, sk, sv, v0, v1, v2, v3;
+};
+template <int NGK>
+__device__ __forceinline__ TileAddr tile_addr(const uint8_t* ring, const LaneOffs& lo) {
+  using L = Slot<NGK>;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_vptr)ring;
+  return {base + L::K_OFF + lo.k[0], base + L::K_OFF + lo.k[1], base + L::SK_OFF + lo.sk,
+          base + L::SV_OFF + lo.sv,  base + L::V_OFF + lo.v[0], base + L::V_OFF + lo.v[1],
+          base + L::V_OFF + lo.v[2], base + L::V_OFF + lo.v[3]};
+}
+
 // All 14 (S = 2: 12) reads are issued in one asm statement that ends by waiting for them.  Written
 // this way the compiler sees no LDS read here, so it does not add a wait for every
 // transfer in flight before the tile (it cannot tell which LDS bytes a global->LDS
 // transfer writes); the caller's vmcnt wait is what orders this tile's own transfers
-// before the reads.
-template <int NGK, int S>
-__device__ __forceinline__ TileData read_tile(const uint8_t* lb, const LaneOffs& lo) {
-  using L = Slot<NGK>;
-  const uint32_t base = (uint32_t)(uintptr_t)(lds_vptr)lb;
-  const uint32_t ak0 = base + L::K_OFF + lo.k[0], ak1 = base + L::K_OFF + lo.k[1];
-  const uint32_t ask = base + L::SK_OFF + lo.sk, asv = base + L::SV_OFF + lo.sv;
-  const uint32_t av0 = base + L::V_OFF + lo.v[0], av1 = base + L::V_OFF + lo.v[1];
-  const uint32_t av2 = base + L::V_OFF + lo.v[2], av3 = base + L::V_OFF + lo.v[3];
+// before the reads.  OFF: the byte offset of the tile's slot in the ring.
+template <int NGK, int S, int OFF>
+__device__ __forceinline__ TileData read_tile(const TileAddr& ad) {
+  static_assert(OFF + 1024 + 64 < 65536, "the slot offset fits the reads' immediate");
   TileData d;
   if (S == 1) {
     asm volatile(
-        "ds_read_b128 %0, %14\n\t"
-        "ds_read_b128 %1, %15\n\t"
-        "ds_read_b128 %2, %16\n\t"
-        "ds_read_b128 %3, %16 offset:64\n\t"
-        "ds_read_b128 %4, %17\n\t"
-        "ds_read_b128 %5, %17 offset:64\n\t"
-        "ds_read_b32 %6, %18\n\t"
-        "ds_read_b32 %7, %19\n\t"
-        "ds_read_b32 %8, %20\n\t"
-        "ds_read_b32 %9, %21\n\t"
-        "ds_read_b32 %10, %18 offset:1024\n\t"
-        "ds_read_b32 %11, %19 offset:1024\n\t"
-        "ds_read_b32 %12, %20 offset:1024\n\t"
-        "ds_read_b32 %13, %21 offset:1024\n\t"
+        "ds_read_b128 %0, %14 offset:%22\n\t"
+        "ds_read_b128 %1, %15 offset:%22\n\t"
+        "ds_read_b128 %2, %16 offset:%22\n\t"
+        "ds_read_b128 %3, %16 offset:%23\n\t"
+        "ds_read_b128 %4, %17 offset:%22\n\t"
+        "ds_read_b128 %5, %17 offset:%23\n\t"
+        "ds_read_b32 %6, %18 offset:%22\n\t"
+        "ds_read_b32 %7, %19 offset:%22\n\t"
+        "ds_read_b32 %8, %20 offset:%22\n\t"
+        "ds_read_b32 %9, %21 offset:%22\n\t"
+        "ds_read_b32 %10, %18 offset:%24\n\t"
+        "ds_read_b32 %11, %19 offset:%24\n\t"
+        "ds_read_b32 %12, %20 offset:%24\n\t"
+        "ds_read_b32 %13, %21 offset:%24\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(d.k[0]), "=&v"(d.k[1]), "=&v"(d.sk[0]), "=&v"(d.sk[1]), "=&v"(d.sv[0]),
           "=&v"(d.sv[1]), "=&v"(d.v[0][0]), "=&v"(d.v[0][1]), "=&v"(d.v[0][2]),
           "=&v"(d.v[0][3]), "=&v"(d.v[1][0]), "=&v"(d.v[1][1]), "=&v"(d.v[1][2]),
           "=&v"(d.v[1][3])
-        : "v"(ak0), "v"(ak1), "v"(ask), "v"(asv), "v"(av0), "v"(av1), "v"(av2), "v"(av3)
+        : "v"(ad.k0), "v"(ad.k1), "v"(ad.sk), "v"(ad.sv), "v"(ad.v0), "v"(ad.v1), "v"(ad.v2),
+          "v"(ad.v3), "n"(OFF), "n"(OFF + 64), "n"(OFF + 1024)
         : "memory");
   } else {
     asm volatile(
-        "ds_read_b128 %0, %12\n\t"
-        "ds_read_b128 %1, %13\n\t"
-        "ds_read_b128 %2, %14\n\t"
-        "ds_read_b128 %3, %15\n\t"
-        "ds_read_b32 %4, %16\n\t"
-        "ds_read_b32 %5, %17\n\t"
-        "ds_read_b32 %6, %18\n\t"
-        "ds_read_b32 %7, %19\n\t"
-        "ds_read_b32 %8, %16 offset:1024\n\t"
-        "ds_read_b32 %9, %17 offset:1024\n\t"
-        "ds_read_b32 %10, %18 offset:1024\n\t"
-        "ds_read_b32 %11, %19 offset:1024\n\t"
+        "ds_read_b128 %0, %12 offset:%20\n\t"
+        "ds_read_b128 %1, %13 offset:%20\n\t"
+        "ds_read_b128 %2, %14 offset:%20\n\t"
+        "ds_read_b128 %3, %15 offset:%20\n\t"
+        "ds_read_b32 %4, %16 offset:%20\n\t"
+        "ds_read_b32 %5, %17 offset:%20\n\t"
+        "ds_read_b32 %6, %18 offset:%20\n\t"
+        "ds_read_b32 %7, %19 offset:%20\n\t"
+        "ds_read_b32 %8, %16 offset:%21\n\t"
+        "ds_read_b32 %9, %17 offset:%21\n\t"
+        "ds_read_b32 %10, %18 offset:%21\n\t"
+        "ds_read_b32 %11, %19 offset:%21\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(d.k[0]), "=&v"(d.k[1]), "=&v"(d.sk[0]), "=&v"(d.sv[0]), "=&v"(d.v[0][0]),
           "=&v"(d.v[0][1]), "=&v"(d.v[0][2]), "=&v"(d.v[0][3]), "=&v"(d.v[1][0]),
           "=&v"(d.v[1][1]), "=&v"(d.v[1][2]), "=&v"(d.v[1][3])
-        : "v"(ak0), "v"(ak1), "v"(ask), "v"(asv), "v"(av0), "v"(av1), "v"(av2), "v"(av3)
+        : "v"(ad.k0), "v"(ad.k1), "v"(ad.sk), "v"(ad.sv), "v"(ad.v0), "v"(ad.v1), "v"(ad.v2),
+          "v"(ad.v3), "n"(OFF), "n"(OFF + 1024)
         : "memory");
   }
   return d;
@@ -581,13 +610,13 @@ __device__ __forceinline__ TileData read_tile(const uint8_t* lb, const LaneOffs&
 // score -inf.  One code path serves both kinds of tile, and the masking only rewrites
 // the scores in place: with two instances of the tile in the loop, the compiler gave
 // the accumulators of each its own registers and copied all 32 of them twice per tile.
-template <int G, int NGK, int S, bool H16 = false>
-__device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& lo, State& st,
+template <int G, int NGK, int S, bool H16, int OFF>
+__device__ __forceinline__ void process_tile(const TileAddr& ad, State& st,
                                              const half8 (&qb)[4 * S], float qbias, int t0,
                                              int pmin, int pe, int j, float qscale, bool lo_col,
                                              int soff, bool masked) {
   constexpr int NTB = 2 / S;   // 16-row blocks of q.K results per lane
-  TileData td = read_tile<NGK, S>(lb, lo);
+  TileData td = read_tile<NGK, S, OFF>(ad);
   if constexpr (H16) {   // fp16 scales sit in the low halves of their dwords (dma_scale)
 #pragma unroll
     for (int T = 0; T < NTB; ++T) {
@@ -607,15 +636,32 @@ __device__ __forceinline__ void process_tile(const uint8_t* lb, const LaneOffs& 
     for (int c = 0; c < 4 * S; ++c)
       cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_word_u(kw8[4 * S * T + c]), qb[c], cg,
                                                   0, 0, 0);
+    // q . codes_g = 2^24 C - 8 sum_g(q); then the group scale
+    float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // q . codes_g = 2^24 C - 8 sum_g(q); then the group scale
-      float sc = __builtin_fmaf(cg[i], 16777216.0f, qbias) * sk[i];
-      // the NGK columns of a head are adjacent (column = head * NGK + group)
-      if (NGK >= 2) sc = add_xor1(sc);
-      if (NGK >= 4) sc = add_xor2(sc);
-      z[T][i] = sc;
-    }
+    for (int i = 0; i < 4; ++i) sc[i] = __builtin_fmaf(cg[i], 16777216.0f, qbias) * sk[i];
+    // the NGK columns of a head are adjacent (column = head * NGK + group): DPP adds over
+    // lane pairs (and quads), in assembly so that each is one instruction (from the
+    // builtin the compiler formed a DPP move and recomputed the product into it); each
+    // block starts with the two wait states a DPP read needs after a VALU write
+    if constexpr (NGK >= 2)
+      asm volatile(
+          "s_nop 1\n\t"
+          "v_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_add_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_add_f32_dpp %2, %2, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+          "v_add_f32_dpp %3, %3, %3 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+          : "+v"(sc[0]), "+v"(sc[1]), "+v"(sc[2]), "+v"(sc[3]));
+    if constexpr (NGK >= 4)
+      asm volatile(
+          "s_nop 1\n\t"
+          "v_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "v_add_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "v_add_f32_dpp %2, %2, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+          "v_add_f32_dpp %3, %3, %3 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+          : "+v"(sc[0]), "+v"(sc[1]), "+v"(sc[2]), "+v"(sc[3]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[T][i] = sc[i];
   }
   if (masked) {
 #pragma unroll
@@ -1383,13 +1429,16 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     if constexpr (I8) return dma_offsets8(lane);
     else return dma_offsets<NGK>(lane);
   }();
+  // (contiguous INT4 layout: the unit's streams as buffer resources)
+  [[maybe_unused]] UnitBufs ubufs;
+  if constexpr (!I8 && !PG) ubufs = unit_bufs<NGK, H16>(a, row0);
   auto issue = [&](int t0, uint8_t* lb) {
     if constexpr (PG) {
       if constexpr (I8) issue_tile8_pg(a, b, kvh, t0, pb, pe, lb, dof);
       else issue_tile_pg<NGK, H16>(a, b, kvh, t0, pb, pe, lb, lane, dof);
     } else {
       if constexpr (I8) issue_tile8<SK>(a, row0, t0, pe, lo_pos, vlo, lb, dof);
-      else issue_tile<NGK, SK, H16>(a, row0, t0, pe, lo_pos, vlo, lb, lane, dof);
+      else issue_tile<NGK, SK, H16>(a, row0, t0, pe, lo_pos, vlo, lb, lane, dof, ubufs);
     }
   };
   if (threadIdx.x == 0) s_claim = 0;   // ordered before the first claim by the q barrier
@@ -1553,7 +1602,14 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   int tl_tiles = 0;
   uint64_t tl_first = 0;
 #endif
-  for (int k = 0; tq[0] != NONE; ++k) {
+  // lane read addresses of slot 0 (INT4 tiles; the INT8 reader forms its own)
+  [[maybe_unused]] TileAddr tad;
+  if constexpr (!I8) tad = tile_addr<NGK>(ring, lo);
+  // step k: processes slot k % NB, so the loop is unrolled NB times with the slot a
+  // compile-time constant (SL)
+  static_assert(NB == 3, "the loop below is unrolled over a 3-slot ring");
+  auto step = [&](auto slot) {
+    constexpr int SL = decltype(slot)::value;
 #ifdef KVQ_TIMELINE
     ++tl_tiles;
 #endif
@@ -1563,7 +1619,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       nn = id < nts ? id : NONE;
     }
     if (nn != NONE) {
-      issue(ps + TL * nn, ring + ((k + DEPTH) % NB) * L::BYTES);
+      issue(ps + TL * nn, ring + ((SL + DEPTH) % NB) * L::BYTES);
       wait_vmcnt<DEPTH * DMA>();   // after tile k: the transfers of tiles k + 1 .. k + DEPTH
     } else {
       int later = 0;   // tiles still in flight behind tile k
@@ -1572,19 +1628,25 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
       wait_vmcnt_tiles<DMA, DEPTH>(later);
     }
 #ifdef KVQ_TIMELINE
-    if (k == 0) tl_first = tl_now();
+    if (tl_tiles == 1) tl_first = tl_now();
 #endif
     const int t0 = ps + TL * tq[0];
     const bool masked = t0 + TL > pe || (PG && t0 < pb);
     if constexpr (I8)
-      process_tile8<G>(ring + (k % NB) * L::BYTES, lo, st, qb, t0, pb, pe, j, a.qscale, lo_col,
-                       masked);
+      process_tile8<G>(ring + SL * L::BYTES, lo, st, qb, t0, pb, pe, j, a.qscale, lo_col, masked);
     else
-      process_tile<G, NGK, S, H16>(ring + (k % NB) * L::BYTES, lo, st, qb, qbias, t0, pb, pe, j,
-                              a.qscale, lo_col, 16 * cset, masked);
+      process_tile<G, NGK, S, H16, SL * L::BYTES>(tad, st, qb, qbias, t0, pb, pe, j, a.qscale,
+                                                  lo_col, 16 * cset, masked);
 #pragma unroll
     for (int i = 0; i + 1 < DEPTH; ++i) tq[i] = tq[i + 1];
     tq[DEPTH - 1] = nn;
+  };
+  while (tq[0] != NONE) {
+    step(std::integral_constant<int, 0>{});
+    if (tq[0] == NONE) break;
+    step(std::integral_constant<int, 1>{});
+    if (tq[0] == NONE) break;
+    step(std::integral_constant<int, 2>{});
   }
   wait_vmcnt<0>();   // (also the q staging, when this wave had no tile)
 #ifdef KVQ_TIMELINE
@@ -2017,11 +2079,13 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
   const int ntiles = (pe - tbase + TILE - 1) / TILE;
   const size_t row0 = (size_t)(b * a.Hkv + kvh) * a.cap;
   const auto dof = dma_offsets<NGK>(lane);
+  [[maybe_unused]] UnitBufs ubufs;
+  if constexpr (!PG) ubufs = unit_bufs<NGK, H16>(a, row0);
   auto issue = [&](int t) {
     uint8_t* lb = ring + (t % NB) * L::BYTES;
     const int t0 = tbase + TILE * t;
     if constexpr (PG) issue_tile_pg<NGK, H16>(a, b, kvh, t0, lo_first, pe, lb, lane, dof);
-    else issue_tile<NGK, false, H16>(a, row0, t0, pe, 0, 0, lb, lane, dof);
+    else issue_tile<NGK, false, H16>(a, row0, t0, pe, 0, 0, lb, lane, dof, ubufs);
   };
 
   // ---- the columns: q as the B operands of the four (g, c2) MFMAs, -8 * (sum of each
