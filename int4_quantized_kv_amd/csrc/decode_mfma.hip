@@ -123,14 +123,27 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 __device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+// Maxima of scores and scales, none of which is ever NaN: the hardware max, one
+// instruction (fmaxf also quiets signalling NaNs first, an extra max of each operand
+// with itself).
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float max_over_j(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   swap16(a, b);
-  uint32_t c = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, a),
-                                                  __builtin_bit_cast(float, b)));
+  uint32_t c = __builtin_bit_cast(uint32_t, max_raw(__builtin_bit_cast(float, a),
+                                                    __builtin_bit_cast(float, b)));
   uint32_t d = c;
   swap32(c, d);
-  return fmaxf(__builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
+  return max_raw(__builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
 }
 __device__ __forceinline__ float sum_over_j(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
@@ -476,7 +489,7 @@ __device__ __forceinline__ u32x4 f16lo_to_f32(const u32x4& w) {
 // lane's column (over the 4 lanes j) and `svmax` the largest V scale among the rows the
 // lane holds.  Returns mq = m * scale - lvs, the exponent offset of this tile's p~.
 __device__ __forceinline__ float tile_update(State& st, float mx, float svmax, float qscale) {
-  const float m_new = fmaxf(st.m, mx);
+  const float m_new = max_raw(st.m, mx);
   // V-scale band, by ballots: some lane above 16, or every lane below 1/16
   const float x = __builtin_amdgcn_ldexpf(svmax, st.lvs);
   const bool vmove = __any(x > 16.0f) || !__any(x >= 0.0625f);
@@ -673,17 +686,17 @@ __device__ __forceinline__ void process_tile(const TileAddr& ad, State& st,
   }
 
   // ---- online softmax (the 4 lanes j of a column share a head)
-  float mx = fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3]));
-  if (NTB == 2) mx = fmaxf(mx, fmaxf(fmaxf(z[NTB - 1][0], z[NTB - 1][1]),
-                                     fmaxf(z[NTB - 1][2], z[NTB - 1][3])));
+  float mx = max3_raw(z[0][0], z[0][1], max_raw(z[0][2], z[0][3]));
+  if (NTB == 2) mx = max3_raw(mx, max_raw(z[NTB - 1][0], z[NTB - 1][1]),
+                              max_raw(z[NTB - 1][2], z[NTB - 1][3]));
   mx = max_over_j(mx);
   float svmax;
   {
     const floatx4 v0 = __builtin_bit_cast(floatx4, td.sv[0]);
-    svmax = fmaxf(fmaxf(v0[0], v0[1]), fmaxf(v0[2], v0[3]));
+    svmax = max3_raw(v0[0], v0[1], max_raw(v0[2], v0[3]));
     if (NTB == 2) {
       const floatx4 v1 = __builtin_bit_cast(floatx4, td.sv[NTB - 1]);
-      svmax = fmaxf(svmax, fmaxf(fmaxf(v1[0], v1[1]), fmaxf(v1[2], v1[3])));
+      svmax = max3_raw(svmax, max_raw(v1[0], v1[1]), max_raw(v1[2], v1[3]));
     }
   }
   const float mq = tile_update(st, mx, svmax, qscale);
@@ -992,10 +1005,10 @@ __device__ __forceinline__ void process_tile8(const uint8_t* lb, const LaneOffs8
   }
 
   // ---- online softmax (the 4 lanes j of a column share a head)
-  float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+  float mx = max3_raw(z[0], z[1], max_raw(z[2], z[3]));
   mx = max_over_j(mx);
   const floatx4 sv = __builtin_bit_cast(floatx4, td.sv);
-  const float mq = tile_update(st, mx, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), qscale);
+  const float mq = tile_update(st, mx, max3_raw(sv[0], sv[1], max_raw(sv[2], sv[3])), qscale);
 
   // ---- P' = p~ * sV as fp16 hi + lo; the column's part goes to B
   H4 pb;
@@ -1835,11 +1848,51 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 
   // ---- the last arrival merges the np partials of its G heads with the log-sum-exp
   // rule (device-scope loads: the partials come from other XCDs) and resets the arrival
-  // counter.  Each thread first issues the loads of its outputs' first PF partials, so
+  // counter.
+  constexpr int OPT = (G * HD + NT - 1) / NT;           // outputs per thread
+  // Up to SM splits: every thread loads its outputs' partials and the (max, sum) pairs of
+  // their heads (repeated across a head's threads: one request per wave) in one round
+  // trip and forms the weights itself, with no LDS staging and no barrier.
+  constexpr int SM = 8;
+  if (np <= SM) {
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int idx = threadIdx.x + NT * u;
+      const int ic = min(idx, G * HD - 1);
+      const int h = ic / HD, d = ic % HD;
+      const size_t o0 = pbase + (size_t)h * nps;
+      // (branch-free: the split index clamped to np - 1, its weight zeroed below)
+      float pv[SM];
+      uint64_t ml[SM];
+#pragma unroll
+      for (int sI = 0; sI < SM; ++sI) {
+        const size_t o = o0 + (size_t)min(sI, np - 1);
+        pv[sI] = fetch(a.ws_acc + o * HD + d);
+        ml[sI] = fetch_pair(a.ws_ml + 2 * o);
+      }
+      float M = NEG_INF;
+#pragma unroll
+      for (int sI = 0; sI < SM; ++sI) M = max_raw(M, __builtin_bit_cast(float, (uint32_t)ml[sI]));
+      float A = 0.0f, L = 0.0f;
+#pragma unroll
+      for (int sI = 0; sI < SM; ++sI) {
+        const float ms = __builtin_bit_cast(float, (uint32_t)ml[sI]);
+        const float w = sI < np && ms != NEG_INF ? fast_exp2(ms - M) : 0.0f;
+        A = __builtin_fmaf(pv[sI], w, A);
+        L = __builtin_fmaf(__builtin_bit_cast(float, (uint32_t)(ml[sI] >> 32)), w, L);
+      }
+      if (idx < G * HD) a.out[(size_t)(b * a.Hq + kvh * G + h) * HD + d] = A / L;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#ifdef KVQ_TIMELINE
+    if (threadIdx.x == 0) tl_put(a, 14, tl_now());
+#endif
+    return;
+  }
+  // More splits: each thread first issues the loads of its outputs' first PF partials, so
   // their latency overlaps the maxima's (32: a 128K-position sequence's 32 splits in one
   // round trip, 2% on that step over 16; plans with fewer splits issue fewer loads).
   constexpr int PF = 32;
-  constexpr int OPT = (G * HD + NT - 1) / NT;           // outputs per thread
   // (branch-free: the loads go in groups of 4 under a uniform test, the split index
   // clamped to np - 1 inside a group and the output index to the last output)
   float pre[OPT][PF];
@@ -2186,8 +2239,8 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
     const floatx4 sk00 = __builtin_bit_cast(floatx4, td.sk[0][0]), sk01 = __builtin_bit_cast(floatx4, td.sk[0][1]);
     const floatx4 sk10 = __builtin_bit_cast(floatx4, td.sk[1][0]), sk11 = __builtin_bit_cast(floatx4, td.sk[1][1]);
     const floatx4 sv0 = __builtin_bit_cast(floatx4, td.sv[0]), sv1 = __builtin_bit_cast(floatx4, td.sv[1]);
-    float svmax = fmaxf(fmaxf(fmaxf(sv0[0], sv0[1]), fmaxf(sv0[2], sv0[3])),
-                        fmaxf(fmaxf(sv1[0], sv1[1]), fmaxf(sv1[2], sv1[3])));
+    float svmax = max3_raw(max3_raw(sv0[0], sv0[1], sv0[2]), max3_raw(sv0[3], sv1[0], sv1[1]),
+                           max_raw(sv1[2], sv1[3]));
     // (uniform) positions past the earliest query or before the latest window start
     const bool masked = t0 + TILE - 1 > min_hi || t0 < max_lo;
     H8 phi[NCB], plo[NCB];   // each column block's P' (fp16 hi and lo parts), B operands of P.V
@@ -2216,8 +2269,8 @@ __global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) 
             if (p > chi[cb] || p < clo[cb]) z[T][i] = NEG_INF;
           }
       }
-      float mx = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
-                       fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+      float mx = max3_raw(max3_raw(z[0][0], z[0][1], z[0][2]), max3_raw(z[0][3], z[1][0], z[1][1]),
+                          max_raw(z[1][2], z[1][3]));
       mx = max_over_j(mx);
       const float mq = tile_update(st[cb], mx, svmax, a.qscale);
 #pragma unroll
