@@ -2096,7 +2096,8 @@ __device__ __forceinline__ TileDataPF read_tile_pf(const uint8_t* lb, const Lane
 
 // H16: fp16 scales (KVQ_INT4_G16), transferred and converted as in the decode kernel.
 template <int G, int NGK, int NCB, bool PG, bool H16 = false>
-__global__ void __launch_bounds__(PF_NT) prefill_int4_mfma_kernel(DecodeArgs a) {
+// (at least two workgroups per CU: at most 256 registers per lane, two waves per SIMD)
+__global__ void __launch_bounds__(PF_NT, 2) prefill_int4_mfma_kernel(DecodeArgs a) {
   using L = Slot<NGK>;
   constexpr int QPC = 16 / G;                  // queries per column block
   constexpr int QWG = PF_WAVES * NCB * QPC;    // queries per workgroup
