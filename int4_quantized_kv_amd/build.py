@@ -5,6 +5,7 @@ Every HIP translation unit under ``csrc/`` is compiled for gfx950 only and linke
 one shared library next to this file, where the Python binding loads it.
 """
 import os
+import re
 import subprocess
 import sys
 
@@ -40,6 +41,27 @@ FLAGS = [
 ]
 
 
+# Sources whose kernels count their own global->LDS transfers with explicit vmcnt waits:
+# a register spill there would put scratch loads and stores into the same counter and
+# break those waits, so the build reports every kernel's scratch use and fails on any.
+NO_SCRATCH = {"decode_mfma.hip"}
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+
+
+def _scratch_users(text):
+    """Kernels with a nonzero scratch size in the compiler's resource-usage remarks."""
+    users, name = [], None
+    for ln in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", ln)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", ln)
+        if m and int(m.group(1)) > 0:
+            users.append(f"{name} ({m.group(1)} bytes/lane)")
+    return users
+
+
 # The timeline probe: the same sources built with -DKVQ_TIMELINE, where the matrix-core
 # decode kernel records the real-time counter at its phase points (bench.py --timeline).
 # Built on request only (python -m int4_quantized_kv_amd.build --timeline).
@@ -57,7 +79,8 @@ def build(verbose=False, timeline=False):
             continue
         obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, *(["-DKVQ_TIMELINE"] if timeline else []), "-c", path, "-o", obj]
+        cmd = [HIPCC, *FLAGS, *(["-DKVQ_TIMELINE"] if timeline else []),
+               *(RESOURCE_REMARKS if src in NO_SCRATCH else []), "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -65,12 +88,19 @@ def build(verbose=False, timeline=False):
     for src, p in procs:
         out, _ = p.communicate()
         text = out.decode(errors="replace")
-        noisy = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
+        noisy = [ln for ln in text.splitlines()
+                 if "packed-fp32-ops" not in ln and "kernel-resource-usage" not in ln]
         if p.returncode != 0:
             failed.append(src)
             sys.stderr.write("\n".join(noisy) + "\n")
-        elif verbose and noisy:
+            continue
+        if verbose and noisy:
             print("\n".join(noisy))
+        if src in NO_SCRATCH:
+            users = _scratch_users(text)
+            if users:
+                failed.append(src)
+                sys.stderr.write(src + ": kernels using scratch memory:\n  " + "\n  ".join(users) + "\n")
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
     if timeline:

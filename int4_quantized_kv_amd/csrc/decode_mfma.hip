@@ -1620,7 +1620,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   if constexpr (!I8) tad = tile_addr<NGK>(ring, lo);
   // step k: processes slot k % NB, so the loop is unrolled NB times with the slot a
   // compile-time constant (SL)
-  static_assert(NB == 3, "the loop below is unrolled over a 3-slot ring");
+  static_assert(NB == 2 || NB == 3, "the loop below is unrolled over a 2- or 3-slot ring");
   auto step = [&](auto slot) {
     constexpr int SL = decltype(slot)::value;
 #ifdef KVQ_TIMELINE
@@ -1658,8 +1658,10 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     step(std::integral_constant<int, 0>{});
     if (tq[0] == NONE) break;
     step(std::integral_constant<int, 1>{});
-    if (tq[0] == NONE) break;
-    step(std::integral_constant<int, 2>{});
+    if constexpr (NB == 3) {
+      if (tq[0] == NONE) break;
+      step(std::integral_constant<int, 2>{});
+    }
   }
   wait_vmcnt<0>();   // (also the q staging, when this wave had no tile)
 #ifdef KVQ_TIMELINE
