@@ -301,12 +301,55 @@ def main():
         "cpu_baseline": None,
     }
 
+    # ---- after the timed region: the step's access pattern alone, on the same caches
+    if not args.no_attainable:
+        pat_gbs, pat_us = tile_pattern_rate(args, [lay.dc for lay in layers], B * Hkv, L,
+                                            4 * (D // w.group_k), nsplit, S)
+        result["pattern_read_GBps"] = round(pat_gbs, 1)
+        result["pattern_read_config"] = {
+            "kernel": "libkvq_bench.so: tile_pattern_kernel", "launches": nl,
+            "bytes_per_launch": B * Hkv * S * row_bytes, "avg_launch_us": round(pat_us, 2)}
+        result["roofline"]["frac_of_pattern"] = round(kern_gbs / pat_gbs, 4)
     del layers, ws
     add_attainable(args, result)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, L, args.cpu_workers)
 
     print(json.dumps(result), flush=True)
+
+
+def tile_pattern_rate(args, caches, units, cap, kscale_bytes, nsplit, rows):
+    """The decode step's transfers with no arithmetic (libkvq_bench.so kvqb_tile_pattern):
+    each cache's first `rows` rows per (b, kv head) unit, in the decode kernel's 32-row
+    tiles, split plan and per-wave ring, one launch per cache replayed as a HIP graph like
+    the timed step.  Returns (GB/s of the tile bytes, microseconds per launch)."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "int4_quantized_kv_amd", "libkvq_bench.so"))
+    fn = lib.kvqb_tile_pattern
+    fn.restype = ctypes.c_int32
+    fn.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int32] * 5 + [ctypes.c_void_p]
+    tps = rows // (32 * nsplit)
+
+    def step(stream):
+        for c in caches:
+            st = fn(c.k_codes.data_ptr(), c.k_scales.data_ptr(), c.v_codes.data_ptr(),
+                    c.v_scales.data_ptr(), units, cap, kscale_bytes, nsplit, tps,
+                    ctypes.c_void_p(stream))
+            if st:
+                raise RuntimeError(f"kvqb_tile_pattern failed ({st})")
+
+    run = _runner(args, step)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (args.steps * len(caches))
+    tile_bytes = units * nsplit * tps * 32 * (128 + kscale_bytes + 4)
+    return tile_bytes / (us * 1e-6) / 1e9, us
 
 
 def kernel_source_hash(sources=None):

@@ -52,9 +52,91 @@ hipError_t launch(const void* buf, size_t bytes, int grid, uint32_t* sink, hipSt
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// The decode step's own access pattern with no arithmetic: the attainable rate of exactly
+// the transfers the matrix-core INT4 decode issues.  Each (b, kv head) unit's rows are
+// cut into nsplit ranges of 32-row tiles; a workgroup of 8 waves takes one range, wave w
+// tiles w, w + 8, ..., each tile four 1 KB pieces of K and V codes plus the tile's K and
+// V scales moved global -> LDS, two tiles in flight behind the one being waited for (the
+// decode kernel's 3-slot ring).  The tiles are never read: only the transfers are timed.
+constexpr int PT_WAVES = 8, PT_SLOT = 4608, PT_TILE = 32;
+typedef __attribute__((address_space(3))) void* pt_lds_ptr;
+typedef __attribute__((address_space(1))) void* pt_gbl_ptr;
+
+template <int N>
+__device__ __forceinline__ void pt_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int SIZE>
+__device__ __forceinline__ void pt_dma(const uint8_t* g, uint8_t* l) {
+  // non-temporal, as the decode kernel's transfers
+  if constexpr (SIZE == 16) __builtin_amdgcn_global_load_lds((pt_gbl_ptr)g, (pt_lds_ptr)l, 16, 0, 2);
+  else __builtin_amdgcn_global_load_lds((pt_gbl_ptr)g, (pt_lds_ptr)l, 4, 0, 2);
+}
+
+// k_codes / v_codes: [units][cap][64] bytes; k_scales: [units][cap][ksb]; v_scales:
+// [units][cap][4]; tiles per split `nt`, rows per split nt * 32 from row 0.
+__global__ void __launch_bounds__(PT_WAVES * 64) tile_pattern_kernel(
+    const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc,
+    const uint8_t* __restrict__ vs, int cap, int ksb, int nt) {
+  constexpr int DMA = 6;   // transfers per tile
+  __shared__ __attribute__((aligned(16))) uint8_t ring[PT_WAVES * 3 * PT_SLOT];
+  const int sp = blockIdx.x, unit = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* wr = ring + wave * 3 * PT_SLOT;
+  const size_t row0 = (size_t)unit * cap + (size_t)sp * nt * PT_TILE;
+  auto issue = [&](int t, int slot) {
+    const size_t r = row0 + (size_t)t * PT_TILE;
+    uint8_t* lb = wr + slot * PT_SLOT;
+    pt_dma<16>(kc + r * 64 + 16 * lane, lb);
+    pt_dma<16>(kc + r * 64 + 1024 + 16 * lane, lb + 1024);
+    pt_dma<16>(vc + r * 64 + 16 * lane, lb + 2048);
+    pt_dma<16>(vc + r * 64 + 1024 + 16 * lane, lb + 3072);
+    pt_dma<4>(ks + r * ksb + (4 * lane) % (PT_TILE * ksb), lb + 4096);   // the tile's K scales
+    pt_dma<4>(vs + r * 4 + 4 * (lane & 31), lb + 4352);                  // and its V scales
+  };
+  int t0 = wave, t1 = wave + PT_WAVES;
+  if (t0 < nt) issue(t0, 0);
+  if (t1 < nt) issue(t1, 1);
+  for (int k = 0; t0 < nt; ++k) {
+    const int t2 = t1 + PT_WAVES;
+    if (t1 < nt && t2 < nt) {
+      issue(t2, (k + 2) % 3);
+      pt_wait<2 * DMA>();   // tile t0 in LDS; t1 and t2 in flight
+    } else if (t1 < nt) {
+      pt_wait<DMA>();
+    } else {
+      pt_wait<0>();
+    }
+    t0 = t1;
+    t1 = t1 < nt ? t2 : nt;
+  }
+  pt_wait<0>();
+}
+
 }  // namespace
 
 extern "C" {
+
+// The decode access pattern over one layer's INT4 cache: `units` (b, kv head) units of
+// `cap` rows, K codes / V codes 64 bytes per row (head_dim 128), K scales `kscale_bytes`
+// (4 to 64, a multiple of 4) and V scales 4 bytes per row, each unit's first
+// nsplit * tiles_per_split * 32 rows (<= cap) read as nsplit workgroups of 8 waves.
+// Returns 0, -1 for invalid arguments, -5 for a launch error.  Asynchronous on `stream`.
+int32_t kvqb_tile_pattern(const void* k_codes, const void* k_scales, const void* v_codes,
+                          const void* v_scales, int32_t units, int32_t cap, int32_t kscale_bytes,
+                          int32_t nsplit, int32_t tiles_per_split, void* stream) {
+  if (!k_codes || !k_scales || !v_codes || !v_scales || units < 1 || nsplit < 1 ||
+      tiles_per_split < 1 || kscale_bytes < 4 || kscale_bytes > 64 || kscale_bytes % 4 ||
+      (int64_t)nsplit * tiles_per_split * PT_TILE > cap || units > 65535)
+    return -1;
+  hipLaunchKernelGGL(tile_pattern_kernel, dim3(nsplit, units), dim3(PT_WAVES * 64), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(k_codes),
+                     static_cast<const uint8_t*>(k_scales), static_cast<const uint8_t*>(v_codes),
+                     static_cast<const uint8_t*>(v_scales), cap, kscale_bytes, tiles_per_split);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // Read `bytes` (a multiple of 16; buffer 16-byte aligned) of device memory at `buf`
 // once with `grid` workgroups of 256 lanes, `unroll` (1, 2, 4, 8 or 16) 16-byte loads
