@@ -1497,18 +1497,21 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // k + DEPTH, starts it into slot (k + DEPTH) % NB and processes tile k from slot k % NB,
   // so DEPTH tiles stay in flight behind the one being processed.  tq[i] is the tile of
   // step k + i (NONE past the end; claims only grow, so once a claim is past the end
-  // every later one is too).
+  // every later one is too).  Only the first tile starts here, behind q; the others
+  // start after the q barrier: an opening burst of one tile per wave (9 MB over the
+  // chip on the Llama-3-8B step instead of 18) brings q and the first tiles in sooner
+  // (step 2% faster, same-box A/B; starting a third tile early instead was 2% slower).
   constexpr int NONE = -1;
   int tq[DEPTH];
-  int nq = 0;   // tiles started (the first NONE ends them)
+  int nq = 0;   // tiles started before the q barrier (0 or 1)
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
     const int id = wave + i * WAVES;
     tq[i] = id < nts ? id : NONE;
-    if (tq[i] != NONE) {
-      issue(ps + TL * tq[i], ring + i * L::BYTES);
-      ++nq;
-    }
+  }
+  if (tq[0] != NONE) {
+    issue(ps + TL * tq[0], ring);
+    ++nq;
   }
 
   // wave 0 waits for its q (and new-row) transfers alone, which are older than its
@@ -1518,6 +1521,9 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
 #ifdef KVQ_TIMELINE
   const uint64_t tl_q = tl_now();
 #endif
+#pragma unroll
+  for (int i = 1; i < DEPTH; ++i)
+    if (tq[i] != NONE) issue(ps + TL * tq[i], ring + i * L::BYTES);
   // (recent fp16 rows: the first batch's loads go out behind the first tiles)
   [[maybe_unused]] RecentRows rrows;
   if constexpr (RC) rrows = recent_preload(a, unit, len, lo_pos, sp, a.nsplit, wave, lane, fused);
