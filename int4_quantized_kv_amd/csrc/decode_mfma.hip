@@ -162,9 +162,15 @@ typedef __attribute__((address_space(1))) void* gbl_vptr;
 // ---------------------------------------------------------------------------------------
 // LDS staging.  Each wave owns a ring of NB tile slots and keeps NB - 1 tiles in flight:
 // tiles arrive by global_load_lds (HBM -> LDS without passing through VGPRs), so the
-// prefetch depth does not cost registers.  The compiler does not track these transfers,
-// so the pipeline waits on them explicitly with s_waitcnt vmcnt (every tile issues the
-// same number of transfers, and no other vector-memory load is issued inside the loop).
+// prefetch depth does not cost registers.  The decode kernel keeps one tile in flight
+// behind the one being processed (8 per CU, ~9 MB over the chip): the same transfers
+// with no arithmetic stream equally fast at one, two or three tiles per wave, and with
+// the arithmetic one is the fastest (Llama-3-8B step 2-3% faster than two, which was
+// 3-4% faster than three), since fewer requests queued ahead of each tile shorten its
+// latency.  The chunked prefill keeps its own three-slot ring (PF_NB).  The compiler
+// does not track these transfers, so the pipeline waits on them explicitly with
+// s_waitcnt vmcnt (every tile issues the same number of transfers, and no other
+// vector-memory load is issued inside the loop).
 //
 // Slot layout (bytes): K codes [0, 2048), V codes [2048, 4096), K scales [4096, +SKB),
 // V scales [.., +256).  A 16-row half of K or V is 1 KB: LDS row position P holds tile
@@ -173,7 +179,7 @@ typedef __attribute__((address_space(1))) void* gbl_vptr;
 // r, ds_read_b128) and the P.V reads (lane (r, j): dword r of row 4j + i, ds_read_b32)
 // free of bank conflicts for 32- and for 64-bank LDS.  K scales are stored group-major
 // ([g][32 rows]) so a lane reads its 4 rows of its group with one ds_read_b128.
-constexpr int NB = 3;
+constexpr int NB = 2;
 constexpr int DEPTH = NB - 1;   // tiles in flight behind the one being processed
 
 __device__ __forceinline__ int rowinv(int rho) { return 4 * (rho >> 2) + ((rho + (rho >> 2)) & 3); }
@@ -1187,7 +1193,7 @@ __device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewLds*
 // codes.  Every split workgroup takes a chunk of them (extra workgroups would not be
 // resident with the splits: the plan gives each CU one), and its wave w the rows
 // t = r0 + w, r0 + w + WAVES, ... of the chunk, RPW at a time.  A wave issues the loads
-// of its first RPW rows right after the q barrier, behind its first two tiles, so their
+// of its first RPW rows right after the q barrier, behind its first tile, so their
 // latency passes under the tile stream (up to RPRE rows; any further ones are loaded
 // after the loop, RPW at a time), and attends the rows after its tile loop.
 // Lane l holds dims 2l, 2l + 1 of a row.  A batch's G * RPW scores are wave sums (DPP),
@@ -1357,7 +1363,10 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   constexpr int TL = I8 ? TILE8 : TILE;       // positions per tile
   constexpr int S = I8 ? 1 : position_sets(G, NGK);
   constexpr int DMA = L::DMA;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[WAVES * NB * L::BYTES];
+  // the wave rings; after the loop, the merge's staging of up to MAX_SPLITS partials
+  constexpr int RING_BYTES = WAVES * NB * L::BYTES;
+  constexpr int MERGE_BYTES = (3 * G * MAX_SPLITS + G) * (int)sizeof(float);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES];
   __shared__ __attribute__((aligned(16))) NewLds s_new;
   __shared__ int s_last;
   __shared__ uint32_t s_claim;
@@ -1497,10 +1506,11 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   // k + DEPTH, starts it into slot (k + DEPTH) % NB and processes tile k from slot k % NB,
   // so DEPTH tiles stay in flight behind the one being processed.  tq[i] is the tile of
   // step k + i (NONE past the end; claims only grow, so once a claim is past the end
-  // every later one is too).  Only the first tile starts here, behind q; the others
-  // start after the q barrier: an opening burst of one tile per wave (9 MB over the
-  // chip on the Llama-3-8B step instead of 18) brings q and the first tiles in sooner
-  // (step 2% faster, same-box A/B; starting a third tile early instead was 2% slower).
+  // every later one is too).  Only the first tile starts here, behind q; with a deeper
+  // ring the others start after the q barrier: an opening burst of one tile per wave
+  // brings q and the first tiles in sooner (with two tiles in flight, starting the
+  // second after the barrier made the Llama-3-8B step 2% faster; a third tile started
+  // early made it 2% slower).
   constexpr int NONE = -1;
   int tq[DEPTH];
   int nq = 0;   // tiles started before the q barrier (0 or 1)
@@ -1920,7 +1930,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
     }
   }
   const int sws = np > PF ? (np + 3) & ~3 : PF;         // weight row stride (>= PF)
-  static_assert((3 * G * MAX_SPLITS + G) * sizeof(float) <= sizeof(smem),
+  static_assert(MERGE_BYTES <= sizeof(smem),
                 "the merge stages up to MAX_SPLITS partials per head in the tile rings");
   float* s_mx = reinterpret_cast<float*>(smem);          // [G][np] split maxima
   float* s_ls = s_mx + G * np;                           // [G][np] split sums
@@ -2031,7 +2041,7 @@ hipError_t launch_g16(const DecodeArgs& a, hipStream_t s) {
 // blocks of 16 query rows: column c of block cb is head c % G of query
 // qb0 + (w * NCB + cb) * 16 / G + c / G.  All waves walk the same K/V tiles (the decode
 // kernel's 32-position LDS tile layout and transfers): tile t is staged by wave
-// t % PF_WAVES into slot t % NB of one ring, and one barrier per tile both publishes it
+// t % PF_WAVES into slot t % PF_NB of one ring, and one barrier per tile both publishes it
 // (its wave waited for its transfers first) and frees the slot the next transfer reuses.
 //   q.K   per tile half T and K group g (64 dims): A = the half's 16 K rows, k = 32 dims
 //         of group g (lane quarter j: dims 64 g + 16 j + 8 c2 + 0..7, c2 = 0, 1),
@@ -2044,6 +2054,7 @@ hipError_t launch_g16(const DecodeArgs& a, hipStream_t s) {
 // The online softmax, the V-scale normalizer and the masks are the decode kernel's, with
 // each column's own horizon.
 constexpr int PF_WAVES = 4;
+constexpr int PF_NB = 3;      // the prefill's ring: two tiles ahead of the one in use
 constexpr int PF_NT = PF_WAVES * 64;
 constexpr int PF_NCB = 2;   // column blocks (16 query rows each) per wave: each wave's
                             // K and V operand conversions serve 32 columns (232 VGPRs, two
@@ -2109,7 +2120,7 @@ __global__ void __launch_bounds__(PF_NT, 2) prefill_int4_mfma_kernel(DecodeArgs 
   using L = Slot<NGK>;
   constexpr int QPC = 16 / G;                  // queries per column block
   constexpr int QWG = PF_WAVES * NCB * QPC;    // queries per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NB * L::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[PF_NB * L::BYTES];
 
   // Workgroups reach the 8 XCDs in turn, in dispatch order (x fastest).  They are
   // renumbered so that each XCD runs whole (sequence, KV head) units, all query blocks of
@@ -2144,7 +2155,7 @@ __global__ void __launch_bounds__(PF_NT, 2) prefill_int4_mfma_kernel(DecodeArgs 
   [[maybe_unused]] UnitBufs ubufs;
   if constexpr (!PG) ubufs = unit_bufs<NGK, H16>(a, row0);
   auto issue = [&](int t) {
-    uint8_t* lb = ring + (t % NB) * L::BYTES;
+    uint8_t* lb = ring + (t % PF_NB) * L::BYTES;
     const int t0 = tbase + TILE * t;
     if constexpr (PG) issue_tile_pg<NGK, H16>(a, b, kvh, t0, lo_first, pe, lb, lane, dof);
     else issue_tile<NGK, false, H16>(a, row0, t0, pe, 0, 0, lb, lane, dof, ubufs);
@@ -2227,7 +2238,7 @@ __global__ void __launch_bounds__(PF_NT, 2) prefill_int4_mfma_kernel(DecodeArgs 
     lds_barrier();   // tile k visible to every wave; every wave done with tile k - 1
     if (k + 2 < ntiles && wave == (k + 2) % PF_WAVES) issue(k + 2);   // into tile k - 1's slot
     const int t0 = tbase + TILE * k;
-    TileDataPF td = read_tile_pf<NGK>(ring + (k % NB) * L::BYTES, lo, j);
+    TileDataPF td = read_tile_pf<NGK>(ring + (k % PF_NB) * L::BYTES, lo, j);
     if constexpr (H16) {   // fp16 scales in the low halves of their dwords (dma_scale)
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
