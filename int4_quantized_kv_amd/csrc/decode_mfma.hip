@@ -167,7 +167,7 @@ typedef __attribute__((address_space(1))) void* gbl_vptr;
 // with no arithmetic stream equally fast at one, two or three tiles per wave, and with
 // the arithmetic one is the fastest (Llama-3-8B step 2-3% faster than two, which was
 // 3-4% faster than three), since fewer requests queued ahead of each tile shorten its
-// latency.  The chunked prefill keeps its own three-slot ring (PF_NB).  The compiler
+// latency.  The chunked prefill has a ring of its own (PF_NB), shared by its waves.  The compiler
 // does not track these transfers, so the pipeline waits on them explicitly with
 // s_waitcnt vmcnt (every tile issues the same number of transfers, and no other
 // vector-memory load is issued inside the loop).
@@ -2054,7 +2054,7 @@ hipError_t launch_g16(const DecodeArgs& a, hipStream_t s) {
 // The online softmax, the V-scale normalizer and the masks are the decode kernel's, with
 // each column's own horizon.
 constexpr int PF_WAVES = 4;
-constexpr int PF_NB = 3;      // the prefill's ring: two tiles ahead of the one in use
+constexpr int PF_NB = 2;      // the prefill's ring: one tile ahead of the one in use
 constexpr int PF_NT = PF_WAVES * 64;
 constexpr int PF_NCB = 2;   // column blocks (16 query rows each) per wave: each wave's
                             // K and V operand conversions serve 32 columns (232 VGPRs, two
@@ -2228,15 +2228,15 @@ __global__ void __launch_bounds__(PF_NT, 2) prefill_int4_mfma_kernel(DecodeArgs 
     st[cb].lvs = 0;
   }
 
-  // ---- the tile loop: tile t staged by wave t % PF_WAVES, two tiles ahead
+  // ---- the tile loop: tile t staged by wave t % PF_WAVES, one tile ahead (two ahead, in a
+  // 3-slot ring, was 1.7% slower)
   if (wave == 0 && ntiles > 0) issue(0);
-  if (wave == 1 && ntiles > 1) issue(1);
   for (int k = 0; k < ntiles; ++k) {
     // a wave has at most one tile in flight (its tiles are PF_WAVES apart and it waits
     // for each before the next is issued), so vmcnt(0) waits for exactly tile k
     if (wave == k % PF_WAVES) wait_vmcnt<0>();
     lds_barrier();   // tile k visible to every wave; every wave done with tile k - 1
-    if (k + 2 < ntiles && wave == (k + 2) % PF_WAVES) issue(k + 2);   // into tile k - 1's slot
+    if (k + 1 < ntiles && wave == (k + 1) % PF_WAVES) issue(k + 1);   // into tile k - 1's slot
     const int t0 = tbase + TILE * k;
     TileDataPF td = read_tile_pf<NGK>(ring + (k % PF_NB) * L::BYTES, lo, j);
     if constexpr (H16) {   // fp16 scales in the low halves of their dwords (dma_scale)
