@@ -1426,7 +1426,7 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   const int pt = RC ? max(lo_pos, len - a.recent) : (fused ? len - 1 : len);
 
   // ---- tile schedule: split sp covers positions [ps, pe) of [lo_pos, pt), nts tiles
-  // of 32 positions.  Wave w starts with tiles w and w + WAVES; every further tile is
+  // of 32 positions.  Wave w starts with tile w; every further tile is
   // claimed from the workgroup's LDS counter, so faster waves take more tiles.  One
   // workgroup of 8 waves per CU: with two workgroups of 4 waves sharing a CU, one of the
   // pair was measured to lag the other by up to a third of the kernel, a split no LDS
@@ -1538,8 +1538,8 @@ __global__ void __launch_bounds__(NT) decode_int4_mfma_kernel(DecodeArgs a) {
   [[maybe_unused]] RecentRows rrows;
   if constexpr (RC) rrows = recent_preload(a, unit, len, lo_pos, sp, a.nsplit, wave, lane, fused);
   // q into MFMA layout (and the appending wave's quantization of the new row) while
-  // tiles 0 and 1 are in flight (asm reads: plain reads would make the compiler wait
-  // for the first tiles as well)
+  // the first tiles are in flight (asm reads: plain reads would make the compiler wait
+  // for them as well)
   // the chunk of q feeding MFMA c: S = 1: chunk j (all c); S = 2: chunk j % 2 + 2 (c / 4)
   u32x4 qraw[4 * S];
   {

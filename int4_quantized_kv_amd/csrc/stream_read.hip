@@ -57,8 +57,8 @@ hipError_t launch(const void* buf, size_t bytes, int grid, uint32_t* sink, hipSt
 // the transfers the matrix-core INT4 decode issues.  Each (b, kv head) unit's rows are
 // cut into nsplit ranges of 32-row tiles; a workgroup of 8 waves takes one range, wave w
 // tiles w, w + 8, ..., each tile four 1 KB pieces of K and V codes plus the tile's K and
-// V scales moved global -> LDS, two tiles in flight behind the one being waited for (the
-// decode kernel's 3-slot ring).  The tiles are never read: only the transfers are timed.
+// V scales moved global -> LDS, one tile in flight behind the one being waited for (the
+// decode kernel's 2-slot ring).  The tiles are never read: only the transfers are timed.
 constexpr int PT_WAVES = 8, PT_SLOT = 4608, PT_TILE = 32;
 typedef __attribute__((address_space(3))) void* pt_lds_ptr;
 typedef __attribute__((address_space(1))) void* pt_gbl_ptr;
@@ -80,11 +80,11 @@ __global__ void __launch_bounds__(PT_WAVES * 64) tile_pattern_kernel(
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc,
     const uint8_t* __restrict__ vs, int cap, int ksb, int nt) {
   constexpr int DMA = 6;   // transfers per tile
-  __shared__ __attribute__((aligned(16))) uint8_t ring[PT_WAVES * 3 * PT_SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[PT_WAVES * 2 * PT_SLOT];
   const int sp = blockIdx.x, unit = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint8_t* wr = ring + wave * 3 * PT_SLOT;
+  uint8_t* wr = ring + wave * 2 * PT_SLOT;
   const size_t row0 = (size_t)unit * cap + (size_t)sp * nt * PT_TILE;
   auto issue = [&](int t, int slot) {
     const size_t r = row0 + (size_t)t * PT_TILE;
@@ -96,21 +96,17 @@ __global__ void __launch_bounds__(PT_WAVES * 64) tile_pattern_kernel(
     pt_dma<4>(ks + r * ksb + (4 * lane) % (PT_TILE * ksb), lb + 4096);   // the tile's K scales
     pt_dma<4>(vs + r * 4 + 4 * (lane & 31), lb + 4352);                  // and its V scales
   };
-  int t0 = wave, t1 = wave + PT_WAVES;
+  int t0 = wave;
   if (t0 < nt) issue(t0, 0);
-  if (t1 < nt) issue(t1, 1);
   for (int k = 0; t0 < nt; ++k) {
-    const int t2 = t1 + PT_WAVES;
-    if (t1 < nt && t2 < nt) {
-      issue(t2, (k + 2) % 3);
-      pt_wait<2 * DMA>();   // tile t0 in LDS; t1 and t2 in flight
-    } else if (t1 < nt) {
-      pt_wait<DMA>();
+    const int t1 = t0 + PT_WAVES;
+    if (t1 < nt) {
+      issue(t1, (k + 1) & 1);
+      pt_wait<DMA>();   // tile t0 in LDS; t1 in flight
     } else {
       pt_wait<0>();
     }
     t0 = t1;
-    t1 = t1 < nt ? t2 : nt;
   }
   pt_wait<0>();
 }
