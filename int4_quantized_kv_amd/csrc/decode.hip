@@ -239,9 +239,7 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
     if constexpr (CODEC) {
       codec_encode_row<LPR>(x, c, thr, w, sc);
     } else {   // INT4 with fp16 scales: the quantize kernel's arithmetic, group amax by DPP
-      float am = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+      float am = abs_max8(x);
       auto group_max = [](float v, int lanes) {   // (uniform switch)
         switch (lanes) {
           case 4: return lane_group_max<4>(v);

@@ -1116,9 +1116,7 @@ __device__ __forceinline__ NewRow append_row(const DecodeArgs& a, const NewLds* 
   constexpr int LPG_K = 16 / NGK;                       // lanes per K group (V: 16)
   float x[8];
   f16x8_to_f32(*reinterpret_cast<const u32x4*>((isv ? s->v : s->k) + 8 * c), x);
-  float am = 0.0f;
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) am = fmaxf(am, fabsf(x[jj]));
+  float am = abs_max8(x);
   const float am_row = row_reduce<true, 16>(am);
   am = isv ? am_row : row_reduce<true, LPG_K>(am);
   float sc;

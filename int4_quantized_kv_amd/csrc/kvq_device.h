@@ -248,11 +248,25 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
-// Maximum over aligned groups of LANES lanes, by the same lane pairings.
+// Maximum over aligned groups of LANES lanes, by the same lane pairings: one
+// v_max_f32_dpp per stage, in asm (fmaxf would first quiet signalling NaNs with a max of
+// each operand with itself, and the builtin DPP move is not folded into the max; the
+// values reduced here are never NaN).  Each stage starts with the two wait states a DPP
+// read needs after a VALU write.
 template <int CTRL>
 __device__ __forceinline__ float dpp_max(float x) {
-  return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                      0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false)));
+  float r;
+  if constexpr (CTRL == 0xB1)
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  else if constexpr (CTRL == 0x4E)
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  else if constexpr (CTRL == 0x141)
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  else {
+    static_assert(CTRL == 0x140, "lane pairing");
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_mirror row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  }
+  return r;
 }
 template <int LANES>
 __device__ __forceinline__ float lane_group_max(float x) {
@@ -263,9 +277,20 @@ __device__ __forceinline__ float lane_group_max(float x) {
   if (LANES >= 32) {
     uint32_t p = __builtin_bit_cast(uint32_t, x), q = p;
     asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(p), "+v"(q));
-    x = fmaxf(__builtin_bit_cast(float, p), __builtin_bit_cast(float, q));
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(p), "v"(q));
+    x = r;
   }
   return x;
+}
+// max(|x[0]|, ..., |x[7]|): four v_max3_f32 with absolute-value source modifiers.
+__device__ __forceinline__ float abs_max8(const float (&x)[8]) {
+  float m;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m) : "v"(x[0]), "v"(x[1]), "v"(x[2]));
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(m) : "v"(m), "v"(x[3]), "v"(x[4]));
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(m) : "v"(m), "v"(x[5]), "v"(x[6]));
+  asm("v_max_f32 %0, %1, |%2|" : "=v"(m) : "v"(m), "v"(x[7]));
+  return m;
 }
 
 // Enqueue `kernel(args)` and return the runtime's status for this launch only (the

@@ -73,9 +73,7 @@ __device__ __forceinline__ void quant_pair(const QuantArgs& a, int bh) {
       const int t = (int)(i >> lsh), c = (int)(i & (lpr - 1));
       float x[8];
       f16x8_unpack(raw[u], x);
-      float am = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+      float am = abs_max8(x);
       // a group is lpg aligned consecutive lanes, all of which take this chunk
       switch (lpg) {   // (uniform)
         case 4: am = lane_group_max<4>(am); break;
