@@ -331,12 +331,16 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, size_t row0, int
                                            const DmaOffs& o, const UnitBufs& ub) {
   using L = Slot<NGK>;
   const int cap = a.cap;
-  const int sbase = t0 < cap ? t0 : t0 % cap;
+  // the tile's first slot; with sinks, a tile at or past the window start holds
+  // positions t0 .. t0 + 31 themselves, in consecutive ring slots unless it wraps
+  // (tiles below the window start, which hold sinks, take the general path)
+  const int sbase = SK ? (t0 >= lo ? cache_slot(t0, cap, a.sinks) : cap)
+                       : (t0 < cap ? t0 : t0 % cap);
   const uint8_t* kc = static_cast<const uint8_t*>(a.k_codes);
   const uint8_t* vc = static_cast<const uint8_t*>(a.v_codes);
   const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k_scales);
   const uint8_t* vs = reinterpret_cast<const uint8_t*>(a.v_scales);
-  if (!SK && t0 + TILE <= pe && sbase + TILE <= cap && cap <= BUF_MAX_CAP) {
+  if (t0 + TILE <= pe && sbase + TILE <= cap && cap <= BUF_MAX_CAP) {
     const uint32_t sb = (uint32_t)sbase;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
