@@ -15,13 +15,13 @@
 // the rows are combined through LDS and the workgroup writes one unnormalized partial
 // (max, sum, weighted V) per query head.
 // Stage 2: out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i, inside stage 1 by the
-// last split of a (b, kv head) when there are at most 16 splits, otherwise by
+// last split of a (b, kv head) when there are at most 32 splits, otherwise by
 // merge_kernel (one workgroup per query head).
 // Codec: keys/values stay in the rotated domain.  Since H/sqrt(D) is orthonormal and
 // symmetric, q . x_hat = (H q / sqrt(D)) . (s c[idx]); q is rotated once per workgroup
-// and the merged output is rotated back once per (b, h).  With the append fused, split
-// 0 codes the new row (the same row encoder as the append kernel) and attends it from
-// registers.
+// and the merged output is rotated back once per (b, h).  With the append fused, the
+// last split codes the new row (the same row encoder as the append kernel) and attends
+// it from registers.
 #include <cmath>
 
 #include "kvq_arith.h"
