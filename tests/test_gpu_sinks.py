@@ -92,6 +92,12 @@ CASES = [
     ("codec", 256, 2, 4, 256, 256, [1500, 600], 0),
     ("codec", 128, 4, 8, 128, 100, [700, 20], 40),      # merge kernel; a short sequence
     ("int4h", 128, 4, 4, 256, 200, [1000, 700], 0),     # fp16 scales with sinks: split-K kernel
+    # one split, so its 32-position tiles start at lo - 4 (sequence 0: lo = 792): the first
+    # holds the sinks, the next ones lie past the window start in consecutive ring slots,
+    # and the one at 1012 wraps the ring (slots 244 .. 259, then 4 ..); in sequence 1
+    # (lo = 712) the tile at 740 ends exactly at the last slot (228 .. 259)
+    ("int4", 128, 4, 4, 256, 256, [1048, 968], 1),
+    ("int4", 128, 4, 4, 256, 256, [1048, 968], 3),
 ]
 
 
