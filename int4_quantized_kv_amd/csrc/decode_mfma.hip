@@ -161,16 +161,17 @@ typedef __attribute__((address_space(1))) void* gbl_vptr;
 
 // ---------------------------------------------------------------------------------------
 // LDS staging.  Each wave owns a ring of NB tile slots and keeps NB - 1 tiles in flight:
-// tiles arrive by global_load_lds (HBM -> LDS without passing through VGPRs), so the
-// prefetch depth does not cost registers.  The decode kernel keeps one tile in flight
-// behind the one being processed (8 per CU, ~9 MB over the chip): the same transfers
-// with no arithmetic stream equally fast at one, two or three tiles per wave, and with
-// the arithmetic one is the fastest (Llama-3-8B step 2-3% faster than two, which was
-// 3-4% faster than three), since fewer requests queued ahead of each tile shorten its
-// latency.  The chunked prefill has a ring of its own (PF_NB), shared by its waves.  The compiler
-// does not track these transfers, so the pipeline waits on them explicitly with
-// s_waitcnt vmcnt (every tile issues the same number of transfers, and no other
-// vector-memory load is issued inside the loop).
+// tiles arrive by direct HBM -> LDS transfers (buffer loads into LDS for full tiles,
+// global_load_lds otherwise) that do not pass through VGPRs, so the prefetch depth does
+// not cost registers.  The decode kernel keeps one tile in flight behind the one being
+// processed (8 per CU, ~9 MB over the chip): the same transfers with no arithmetic
+// stream equally fast at one, two or three tiles per wave, and with the arithmetic one
+// is the fastest (Llama-3-8B step 2-3% faster than two, which was 3-4% faster than
+// three), since fewer requests queued ahead of each tile shorten its latency.  The
+// chunked prefill has a ring of its own (PF_NB), shared by its waves.  The compiler does
+// not track these transfers, so the pipeline waits on them explicitly with s_waitcnt
+// vmcnt (every tile issues the same number of transfers, and no other vector-memory
+// load is issued inside the loop).
 //
 // Slot layout (bytes): K codes [0, 2048), V codes [2048, 4096), K scales [4096, +SKB),
 // V scales [.., +256).  A 16-row half of K or V is 1 KB: LDS row position P holds tile
