@@ -194,11 +194,18 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
       }
     }
   };
-  // q first (it is needed first), then the rows
+  // q first (it is needed first), then the codebook levels, then the rows
   uint4 qraw[G];
 #pragma unroll
   for (int h = 0; h < G; ++h)
     qraw[h] = *reinterpret_cast<const uint4*>(a.q + ((size_t)(b * a.Hq + kvh * G + h) * D + 8 * c));
+  // codec: this thread's entry of the level table, the two levels of a byte (4 bits) or of
+  // a 6-bit index pair (3 bits); requested here, the loads overlap q's (requested after
+  // q's rotation they were a round trip of their own before the first row step)
+  [[maybe_unused]] float2 lvv;
+  if (CODEC && tid < 256)
+    lvv = FMT == KVQ_WHT_LM3 ? make_float2(a.levels[tid & 7], a.levels[(tid >> 3) & 7])
+                             : make_float2(a.levels[tid & 15], a.levels[tid >> 4]);
   int t0 = ps + grp;
   RawRow cur[U], nxt[U];
   if (t0 < pe) load_step(t0, cur);
@@ -215,6 +222,8 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
     if (CODEC) thr = load_thresholds(a.thr);
   }
 
+  // (the levels arrive with q: stored now, they hold no registers through q's rotation)
+  if (CODEC && tid < 256) lv2[tid] = lvv;
   float q[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -284,13 +293,7 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
     nr.k[1] = nr.v[1] = 0u;
   }
 
-  if (CODEC) {   // the codebook levels (the barrier comes after the loads above): the
-    // two levels of a byte (4 bits) or of a 6-bit index pair (3 bits)
-    if (tid < 256)
-      lv2[tid] = FMT == KVQ_WHT_LM3 ? make_float2(a.levels[tid & 7], a.levels[(tid >> 3) & 7])
-                                    : make_float2(a.levels[tid & 15], a.levels[tid >> 4]);
-    __syncthreads();
-  }
+  if (CODEC) __syncthreads();   // the level table (stored above) is complete
 
   float m[G], l[G], acc[G][8];
 #pragma unroll
