@@ -145,6 +145,7 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
   __shared__ float s_l[NGRP][G];
   __shared__ float s_acc[NGRP][G][D];
   __shared__ float2 lv2[CODEC ? 256 : 1];   // codec: the levels of a byte's nibbles
+  __shared__ float s_q[CODEC ? G * D : 1];   // codec: q rotated and scaled, [G][D]
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, grp = tid / LPR, c = tid % LPR;
@@ -194,11 +195,21 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
       }
     }
   };
-  // q first (it is needed first), then the codebook levels, then the rows
-  uint4 qraw[G];
+  // q first (it is needed first), then the codebook levels, then the rows.  The codec
+  // rotates q once per workgroup: row group NGRP - G + h (the last ones, which never
+  // code the fused append's row) loads, rotates and scales head h and stages it in LDS;
+  // every thread reads its dims of each head after the barrier below.  (Rotated by
+  // every row group, the transform held every wave for ~0.7 us before the first row.)
+  uint4 qraw[CODEC ? 1 : G];
+  [[maybe_unused]] const int hq = grp - (NGRP - G);   // codec: the head this group rotates
+  if constexpr (CODEC) {
+    if (hq >= 0)
+      qraw[0] = *reinterpret_cast<const uint4*>(a.q + ((size_t)(b * a.Hq + kvh * G + hq) * D + 8 * c));
+  } else {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-    qraw[h] = *reinterpret_cast<const uint4*>(a.q + ((size_t)(b * a.Hq + kvh * G + h) * D + 8 * c));
+    for (int h = 0; h < G; ++h)
+      qraw[h] = *reinterpret_cast<const uint4*>(a.q + ((size_t)(b * a.Hq + kvh * G + h) * D + 8 * c));
+  }
   // codec: this thread's entry of the level table, the two levels of a byte (4 bits) or of
   // a 6-bit index pair (3 bits); requested here, the loads overlap q's (requested after
   // q's rotation they were a round trip of their own before the first row step)
@@ -225,16 +236,25 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
   // (the levels arrive with q: stored now, they hold no registers through q's rotation)
   if (CODEC && tid < 256) lv2[tid] = lvv;
   float q[G][8];
+  if constexpr (CODEC) {
+    if (hq >= 0) {   // (whole row groups: the transform's lane exchanges stay inside)
+      float x[8];
+      f16x8_unpack(qraw[0], x);
+      wht_row<LPR>(x, c);
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    f16x8_unpack(qraw[h], q[h]);
-    if (CODEC) {
-      wht_row<LPR>(q[h], c);
+      for (int j = 0; j < 8; ++j) x[j] *= 1.0f / sqrtf((float)D);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[h][j] *= 1.0f / sqrtf((float)D);
+      for (int j = 0; j < 8; ++j) x[j] *= a.qscale;
+      *reinterpret_cast<float4*>(s_q + hq * D + 8 * c) = make_float4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<float4*>(s_q + hq * D + 8 * c + 4) = make_float4(x[4], x[5], x[6], x[7]);
     }
+  } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[h][j] *= a.qscale;
+    for (int h = 0; h < G; ++h) {
+      f16x8_unpack(qraw[h], q[h]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[h][j] *= a.qscale;
+    }
   }
   RawRow nr;
   if (app_wave) {
@@ -293,7 +313,16 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
     nr.k[1] = nr.v[1] = 0u;
   }
 
-  if (CODEC) __syncthreads();   // the level table (stored above) is complete
+  if constexpr (CODEC) {   // the level table and the rotated q (stored above) are complete
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float4 lo4 = *reinterpret_cast<const float4*>(s_q + h * D + 8 * c);
+      const float4 hi4 = *reinterpret_cast<const float4*>(s_q + h * D + 8 * c + 4);
+      q[h][0] = lo4.x; q[h][1] = lo4.y; q[h][2] = lo4.z; q[h][3] = lo4.w;
+      q[h][4] = hi4.x; q[h][5] = hi4.y; q[h][6] = hi4.z; q[h][7] = hi4.w;
+    }
+  }
 
   float m[G], l[G], acc[G][8];
 #pragma unroll
