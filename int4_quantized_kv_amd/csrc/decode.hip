@@ -145,7 +145,8 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
   __shared__ float s_l[NGRP][G];
   __shared__ float s_acc[NGRP][G][D];
   __shared__ float2 lv2[CODEC ? 256 : 1];   // codec: the levels of a byte's nibbles
-  __shared__ float s_q[CODEC ? G * D : 1];   // codec: q rotated and scaled, [G][D]
+  // codec: q rotated and scaled, [G][D] (read and written as float4)
+  __shared__ __attribute__((aligned(16))) float s_q[CODEC ? G * D : 1];
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, grp = tid / LPR, c = tid % LPR;
@@ -222,8 +223,9 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
   if (t0 < pe) load_step(t0, cur);
   if (t0 + SR < pe) load_step(t0 + SR, nxt);
   // the append split: row group 0 codes the new K row and row group 1 the new V row,
-  // side by side in wave 0 (fp16 rows requested here, coded once q is ready); group 0
-  // then attends the new row (after its cached rows, if the split has any)
+  // side by side in wave 0 (fp16 rows requested here and coded as soon as they arrive;
+  // wave 0 takes no part in q's rotation); group 0 then attends the new row (after its
+  // cached rows, if the split has any)
   const bool app_wave = app_split && tid < 64;   // wave-uniform
   const bool app_grp = app_wave && grp == 0;
   uint4 newx = make_uint4(0u, 0u, 0u, 0u);
