@@ -150,6 +150,22 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, grp = tid / LPR, c = tid % LPR;
+  // q first: its load heads the critical path.  The codec rotates q once per workgroup:
+  // row group NGRP - G + h (the last ones, which never code the fused append's row)
+  // loads, rotates and scales head h and stages it in LDS; every thread reads its dims
+  // of each head after the barrier below.  (Rotated by every row group, the transform
+  // held every wave for ~0.7 us before the first row.)  Issued here, ahead of the split
+  // bounds, the load follows the first read of the argument block; placed after them, it
+  // waited for a second one.
+  const uint16_t* qb = a.q + (size_t)(b * a.Hq + kvh * G) * D;   // head 0 of this KV head
+  uint4 qraw[CODEC ? 1 : G];
+  [[maybe_unused]] const int hq = grp - (NGRP - G);   // codec: the head this group rotates
+  if constexpr (CODEC) {
+    if (hq >= 0) qraw[0] = *reinterpret_cast<const uint4*>(qb + (size_t)hq * D + 8 * c);
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) qraw[h] = *reinterpret_cast<const uint4*>(qb + (size_t)h * D + 8 * c);
+  }
   const int len = a.lens[b];
   const int lo = a.window > 0 ? max(0, len - a.window) : 0;
   // codec or INT4 with fp16 scales, with the append fused: position len - 1 is the new
@@ -196,21 +212,7 @@ __global__ void __launch_bounds__(splitk_threads(D, FMT)) decode_splitk_kernel(D
       }
     }
   };
-  // q first (it is needed first), then the codebook levels, then the rows.  The codec
-  // rotates q once per workgroup: row group NGRP - G + h (the last ones, which never
-  // code the fused append's row) loads, rotates and scales head h and stages it in LDS;
-  // every thread reads its dims of each head after the barrier below.  (Rotated by
-  // every row group, the transform held every wave for ~0.7 us before the first row.)
-  uint4 qraw[CODEC ? 1 : G];
-  [[maybe_unused]] const int hq = grp - (NGRP - G);   // codec: the head this group rotates
-  if constexpr (CODEC) {
-    if (hq >= 0)
-      qraw[0] = *reinterpret_cast<const uint4*>(a.q + ((size_t)(b * a.Hq + kvh * G + hq) * D + 8 * c));
-  } else {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      qraw[h] = *reinterpret_cast<const uint4*>(a.q + ((size_t)(b * a.Hq + kvh * G + h) * D + 8 * c));
-  }
+  // then the codebook levels, then the rows
   // codec: this thread's entry of the level table, the two levels of a byte (4 bits) or of
   // a 6-bit index pair (3 bits); requested here, the loads overlap q's (requested after
   // q's rotation they were a round trip of their own before the first row step)
