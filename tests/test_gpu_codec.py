@@ -100,6 +100,26 @@ def test_attention_over_oracle_codes(window, L, cap):
     assert_attn_close(out.cpu().numpy(), ref, f"codec w={window}")
 
 
+@pytest.mark.parametrize("D,G", [(64, 8), (128, 1), (128, 4), (256, 4), (256, 8)])
+def test_attention_over_oracle_codes_head_shapes(D, G):
+    """The same check over head dims and GQA groups: q is rotated once per workgroup by
+    the last G row groups, whose placement depends on D (lanes per row) and G."""
+    B, H, L = 2, 2, 300
+    k = synth.kv_source((B, H, L, D), 70 + D + G, DEV)
+    v = synth.kv_source((B, H, L, D), 71 + D + G, DEV)
+    q = synth.query((B, H * G, D), 72 + D + G, DEV)
+    kn, vn = np16(k), np16(v)
+    kidx, ks, _ = codec.encode(kn)
+    vidx, vs, _ = codec.encode(vn)
+    desc = kvq.make_desc("codec", B, H, D, L)
+    dc = kvq.DeviceCache(desc, DEV)
+    _inject(dc, kidx, ks, vidx, vs)
+    out = decode(desc, dc, q, H * G, [L, L - 37], 0)
+    ref = attention.decode_attention(np16(q), codec.decode(kidx, ks), codec.decode(vidx, vs),
+                                     [L, L - 37], 0)
+    assert_attn_close(out.cpu().numpy(), ref, f"codec D={D} G={G}")
+
+
 @pytest.mark.parametrize("fmt,wid", [("codec", 4), ("codec3", 8)])
 def test_gemma_shape_end_to_end_window_and_global(fmt, wid):
     """The Gemma-3-4B-shaped codec decode step as the benchmark runs it (batch 4, 4 KV
